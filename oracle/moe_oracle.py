@@ -1,0 +1,229 @@
+"""Plain fp32 CPU oracle of one GPU's share of an MoE layer.
+
+TEST INFRASTRUCTURE ONLY (see oracle/__init__.py): imported by tests/,
+__graft_entry__.smoke() and bench.py's cpu_baseline leg, never by the product.
+
+The layer, as the pages state it:
+  1. router: logits = x W_r (+ per-expert bias), top-k per token with scores
+     ("Lower latency and higher throughput with multi-node DeepSeek deployment",
+     MoE Router section);
+  2. dispatch: count tokens per expert, give each token a unique index in its
+     expert's list, copy tokens into per-expert buffers ("CuTeDSL at
+     Perplexity", MoE Dispatch/Combine, local kernel);
+  3. grouped expert FFN with SwiGLU: silu(x W_gate^T) * (x W_up^T), then the
+     down projection (Qwen3.5-397B on Ironwood, section 4.2.2, GMM v2 with fused
+     SwiGLU);
+  4. combine: weighted accumulation of the expert outputs back in token order
+     ("CuTeDSL at Perplexity", local combine); a shared expert's output is added
+     (DeepSeek-deployment page, Expert parallelism section).
+
+Readings where the pages are silent (each also listed in the design doc):
+  - top-k selects on fp32 logits; ties go to the lower expert index; +0 and -0
+    tie; slots are ordered best first.
+  - weights: softmax over the selected logits (equal to full softmax
+    renormalised over the selected experts).
+  - rows inside an expert group are token-ascending; groups are unpadded.
+  - shared expert = group E, rows T*k + t, weight 1, added after the routed sum.
+  - fp8 layers: x and h are quantised per row per 128 channels (scale = amax/448).
+
+Parity status (pins in tests/test_oracle_*.py):
+  router_logits  pinned (exact on small-integer inputs; W_r = 0 special case)
+  topk_softmax   pinned (brute-force sorted() on tiny inputs, ties, +-0, fp64 softmax)
+  counting_sort  pinned (brute-force loops, bijection / scan invariants)
+  expert_ffn     pinned (closed-form SwiGLU values, fp64 brute force per token)
+  combine        pinned (one-hot routing = inverse permutation, identical experts)
+  forward        pinned on tiny and random micro shapes against an fp64
+                 per-token brute force; at the large sizes it rests on those pins.
+"""
+import numpy as np
+
+from .fp8_e4m3 import (quantize_groups_128, dequantize_groups_128,
+                       dequantize_blocks_128x128)
+
+F32 = np.float32
+
+
+def bf16_bits_to_f32(u16: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns (uint16) to fp32."""
+    return (np.asarray(u16).astype(np.uint32) << 16).view(np.float32)
+
+
+# ---------------------------------------------------------------- router ----
+def router_logits(x: np.ndarray, w_router: np.ndarray, bias=None) -> np.ndarray:
+    """logits[t, e] = sum_h x[t, h] W_r[h, e] (+ b[e]), fp32.
+
+    The router's input to top-k (DeepSeek-deployment page, MoE Router).
+    """
+    l = np.matmul(x.astype(F32), w_router.astype(F32), dtype=F32)
+    if bias is not None:
+        l = (l + bias.astype(F32)[None, :]).astype(F32)
+    return l
+
+
+def topk_softmax(logits: np.ndarray, k: int):
+    """Top-k experts per token and their renormalised softmax weights.
+
+    DeepSeek-deployment page, MoE Router: a sort that tracks indices, giving
+    the top-k indices and scores per token.  A stable sort of -logits puts the
+    lower expert index first among equal logits (and treats -0 == +0 as equal).
+    Weights: w_j = exp(l_j - l_0) / sum_j' exp(l_j' - l_0) over the selected.
+    """
+    assert np.all(np.isfinite(logits)), "router logits must be finite"
+    T, E = logits.shape
+    assert 1 <= k <= E
+    order = np.argsort(-logits, axis=1, kind="stable")[:, :k]
+    sel = np.take_along_axis(logits, order, axis=1).astype(F32)
+    ex = np.exp((sel - sel[:, :1]).astype(F32)).astype(F32)
+    w = (ex / ex.sum(axis=1, keepdims=True, dtype=F32)).astype(F32)
+    return order.astype(np.int32), w
+
+
+# -------------------------------------------------------------- dispatch ----
+def counting_sort(topk_idx: np.ndarray, E: int, n_shared: int = 0):
+    """Per-expert counts, offsets and each (token, slot)'s row in the permuted matrix.
+
+    "CuTeDSL at Perplexity", MoE Dispatch/Combine, local kernel: count the
+    tokens of each expert, give each token a unique index within its expert,
+    then copy.  Unique index = number of earlier tokens routed to the same
+    expert (token-ascending, unpadded groups).  The shared expert is group E
+    holding every token in order.
+
+    Returns counts [E+ns], offsets [E+ns+1], dest [T, k], src_row [R] (int32).
+    """
+    T, k = topk_idx.shape
+    flat = topk_idx.reshape(-1).astype(np.int64)
+    counts = np.bincount(flat, minlength=E).astype(np.int64)
+    assert counts.shape[0] == E, "expert index out of range"
+    if n_shared:
+        counts = np.concatenate([counts, np.full(n_shared, T, dtype=np.int64)])
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    # A stable sort by expert keeps (token, slot) order, i.e. token order
+    # within each expert since a token picks an expert at most once.
+    order = np.argsort(flat, kind="stable")
+    dest_flat = np.empty(T * k, dtype=np.int64)
+    dest_flat[order] = np.arange(T * k)
+    dest = dest_flat.reshape(T, k)
+    R = int(offsets[-1])
+    src_row = np.empty(R, dtype=np.int64)
+    src_row[dest_flat] = np.repeat(np.arange(T), k)
+    for s in range(n_shared):
+        base = int(offsets[E + s])
+        src_row[base:base + T] = np.arange(T)
+    return (counts.astype(np.int32), offsets.astype(np.int32),
+            dest.astype(np.int32), src_row.astype(np.int32))
+
+
+def permute_rows(x: np.ndarray, src_row: np.ndarray) -> np.ndarray:
+    """x_perm[r] = x[src_row[r]]: the dispatch copy into expert-contiguous groups."""
+    return x[src_row]
+
+
+# ------------------------------------------------------------ expert FFN ----
+def expert_weights_f32(inputs: dict, e: int):
+    """fp32 values of expert e's (W_gate [I,H], W_up [I,H], W_down [H,I]).
+
+    bf16 weights widen exactly; fp8 weights are code value * block scale
+    (DeepSeek-deployment page, Quantization: one scale per 128x128 block).
+    """
+    if inputs["wdtype"] == "fp8":
+        return (dequantize_blocks_128x128(inputs["w_gate"][e], inputs["s_gate"][e]),
+                dequantize_blocks_128x128(inputs["w_up"][e], inputs["s_up"][e]),
+                dequantize_blocks_128x128(inputs["w_down"][e], inputs["s_down"][e]))
+    return (bf16_bits_to_f32(inputs["w_gate"][e]), bf16_bits_to_f32(inputs["w_up"][e]),
+            bf16_bits_to_f32(inputs["w_down"][e]))
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """silu(z) = z * sigmoid(z) = z / (1 + exp(-z)), fp32."""
+    with np.errstate(over="ignore"):
+        return (z / (F32(1.0) + np.exp(-z))).astype(F32)
+
+
+def expert_ffn(X: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray,
+               quantize_h: bool = False) -> np.ndarray:
+    """One expert on its rows: h = silu(X Wg^T) * (X Wu^T); y = h Wd^T (fp32).
+
+    SwiGLU as fused into the grouped matmul (Qwen3.5-397B on Ironwood, section
+    4.2.2: gate and up projections, then swiglu(gate, up)).  For fp8 layers h
+    is quantised per row per 128 channels before the down projection, as the
+    DeepSeek-deployment page's SiLU kernel block-quantises its output
+    (Quantization section).
+    """
+    G = np.matmul(X, wg.T, dtype=F32)
+    U = np.matmul(X, wu.T, dtype=F32)
+    h = (silu(G) * U).astype(F32)
+    if quantize_h:
+        codes, scales = quantize_groups_128(h)
+        h = dequantize_groups_128(codes, scales)
+    return np.matmul(h, wd.T, dtype=F32)
+
+
+def grouped_ffn(x_perm: np.ndarray, offsets: np.ndarray, inputs: dict) -> np.ndarray:
+    """y_perm[rows of e] = expert_ffn_e(x_perm[rows of e]) for every non-empty group."""
+    R = x_perm.shape[0]
+    H = inputs["w_down"].shape[1]
+    y = np.zeros((R, H), dtype=F32)
+    n_groups = offsets.shape[0] - 1
+    for e in range(n_groups):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        wg, wu, wd = expert_weights_f32(inputs, e)
+        y[lo:hi] = expert_ffn(x_perm[lo:hi], wg, wu, wd,
+                              quantize_h=inputs["wdtype"] == "fp8")
+    return y
+
+
+# --------------------------------------------------------------- combine ----
+def combine(y_perm: np.ndarray, dest: np.ndarray, w: np.ndarray, n_shared: int = 0) -> np.ndarray:
+    """out[t] = sum_{j ascending} w[t,j] * y_perm[dest[t,j]] (+ shared rows), fp32.
+
+    "CuTeDSL at Perplexity", local combine: weighted accumulation using the
+    offsets dispatch computed.  The shared expert's output (rows T*k + t) is
+    added with weight 1 after the routed sum (DeepSeek-deployment page, Expert
+    parallelism section).  Each step is one fp32 product then one fp32 add.
+    """
+    T, k = dest.shape
+    out = np.zeros((T, y_perm.shape[1]), dtype=F32)
+    for j in range(k):
+        out = (out + (w[:, j:j + 1].astype(F32) * y_perm[dest[:, j]]).astype(F32)).astype(F32)
+    for s in range(n_shared):
+        out = (out + y_perm[T * k + s * T + np.arange(T)]).astype(F32)
+    return out
+
+
+# --------------------------------------------------------------- forward ----
+class OracleResult(dict):
+    """Intermediates of one oracle forward (attribute access for convenience)."""
+    __getattr__ = dict.__getitem__
+
+
+def forward(inputs: dict, logits_override=None) -> OracleResult:
+    """The whole layer on the CPU.
+
+    inputs: dict from synth.to_numpy_inputs (bf16 as uint16 bit patterns).
+    logits_override: route from these fp32 logits instead of recomputing them
+    (used to evaluate the layer under the GPU's own routing at near-ties).
+    """
+    x = bf16_bits_to_f32(inputs["x_bf16"])
+    T, H = x.shape
+    E = inputs["w_router"].shape[1]
+    k, ns = inputs["k"], inputs["n_shared"]
+    logits = (router_logits(x, inputs["w_router"], inputs.get("router_bias"))
+              if logits_override is None else np.asarray(logits_override, dtype=F32))
+    idx, w = topk_softmax(logits, k)
+    counts, offsets, dest, src_row = counting_sort(idx, E, ns)
+    if inputs["wdtype"] == "fp8":
+        # Activations quantised on the fly per token per 128 channels
+        # (DeepSeek-deployment page, Quantization section).
+        xc, xs = quantize_groups_128(x)
+        x_perm_codes, x_perm_scales = xc[src_row], xs[src_row]
+        x_perm = dequantize_groups_128(x_perm_codes, x_perm_scales)
+    else:
+        x_perm_codes = x_perm_scales = None
+        x_perm = permute_rows(x, src_row)
+    y_perm = grouped_ffn(x_perm, offsets, inputs)
+    out = combine(y_perm, dest, w, ns)
+    return OracleResult(logits=logits, topk_idx=idx, topk_w=w, counts=counts, offsets=offsets,
+                        dest=dest, src_row=src_row, x_perm=x_perm, x_perm_codes=x_perm_codes,
+                        x_perm_scales=x_perm_scales, y_perm=y_perm, out=out)

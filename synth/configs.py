@@ -1,0 +1,59 @@
+"""The five seeded synthetic layer shapes used for parity and measurement.
+
+Shapes and distributions:
+- Qwen3-235B-like: 128 experts, top-8 ("Hosting Qwen on Blackwell", Prefillers
+  section: 6000 * 8 / 128 tokens per expert); hidden 4096, intermediate 1536.
+- Qwen3.5-397B-like: hidden 4096 (xxmr.cn Qwen3.5-397B on Ironwood, section
+  1.1), 512 experts (section 3.1), top-10 over 1024 tokens (the [1024,10]
+  routing tensors of section 3.2.1); intermediate 1024; router logits carry a
+  Zipf(1.1) per-expert popularity term.
+- DeepSeek-V3-like: 256 routed experts + 1 shared expert, top-8, shared output
+  added ("Lower latency and higher throughput with multi-node DeepSeek
+  deployment", Expert parallelism section); FP8 with 128-element activation
+  groups and 128x128 weight blocks (same page, Quantization section).
+"""
+from dataclasses import dataclass
+from typing import Optional
+
+
+@dataclass(frozen=True)
+class MoeConfig:
+    name: str
+    seed: int
+    T: int          # tokens
+    H: int          # hidden size (GEMM K of gate/up, N of down)
+    E: int          # routed experts
+    k: int          # experts per token
+    I: int          # SwiGLU intermediate size
+    n_shared: int = 0           # always-on shared experts (0 or 1)
+    wdtype: str = "bf16"        # "bf16" or "fp8" (e4m3fn codes + fp32 128x128 block scales)
+    zipf_s: Optional[float] = None  # Zipf exponent of the per-expert router-logit bias
+    w_std: float = 0.02
+    router_std: float = 0.02
+    regime: str = ""            # which roofline binds: "launch", "hbm", "mfma"
+
+    @property
+    def R(self) -> int:
+        """Rows of the permuted activation matrix (routed + shared)."""
+        return self.T * self.k + self.T * self.n_shared
+
+    @property
+    def n_groups(self) -> int:
+        return self.E + self.n_shared
+
+
+CONFIGS = [
+    MoeConfig("tiny", 0, T=64, H=256, E=8, k=2, I=512, regime="launch"),
+    MoeConfig("qwen3_235b_decode", 1, T=64, H=4096, E=128, k=8, I=1536, regime="hbm"),
+    MoeConfig("qwen3_235b_prefill", 2, T=8192, H=4096, E=128, k=8, I=1536, regime="mfma"),
+    MoeConfig("qwen35_397b_zipf", 3, T=1024, H=4096, E=512, k=10, I=1024, zipf_s=1.1, regime="hbm"),
+    MoeConfig("deepseek_v3_fp8", 4, T=4096, H=7168, E=256, k=8, I=2048, n_shared=1,
+              wdtype="fp8", regime="hbm"),
+]
+
+
+def config_by_name(name: str) -> MoeConfig:
+    for c in CONFIGS:
+        if c.name == name:
+            return c
+    raise KeyError(f"unknown config {name!r}; known: {[c.name for c in CONFIGS]}")
