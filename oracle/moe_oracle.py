@@ -50,11 +50,11 @@ def bf16_bits_to_f32(u16: np.ndarray) -> np.ndarray:
 
 # ---------------------------------------------------------------- router ----
 def router_logits(x: np.ndarray, w_router: np.ndarray, bias=None) -> np.ndarray:
-    """logits[t, e] = sum_h x[t, h] W_r[h, e] (+ b[e]), fp32.
+    """logits[t, e] = sum_h x[t, h] W_r[e, h] (+ b[e]), fp32; W_r is [E, H].
 
     The router's input to top-k (DeepSeek-deployment page, MoE Router).
     """
-    l = np.matmul(x.astype(F32), w_router.astype(F32), dtype=F32)
+    l = np.matmul(x.astype(F32), w_router.astype(F32).T, dtype=F32)
     if bias is not None:
         l = (l + bias.astype(F32)[None, :]).astype(F32)
     return l
@@ -207,7 +207,7 @@ def forward(inputs: dict, logits_override=None) -> OracleResult:
     """
     x = bf16_bits_to_f32(inputs["x_bf16"])
     T, H = x.shape
-    E = inputs["w_router"].shape[1]
+    E = inputs["w_router"].shape[0]
     k, ns = inputs["k"], inputs["n_shared"]
     logits = (router_logits(x, inputs["w_router"], inputs.get("router_bias"))
               if logits_override is None else np.asarray(logits_override, dtype=F32))
@@ -227,3 +227,41 @@ def forward(inputs: dict, logits_override=None) -> OracleResult:
     return OracleResult(logits=logits, topk_idx=idx, topk_w=w, counts=counts, offsets=offsets,
                         dest=dest, src_row=src_row, x_perm=x_perm, x_perm_codes=x_perm_codes,
                         x_perm_scales=x_perm_scales, y_perm=y_perm, out=out)
+
+
+
+def forward_tokens(inputs: dict, tokens, logits_override=None) -> OracleResult:
+    """The layer's output for a sample of tokens, evaluated one token at a time.
+
+    Each token's output depends only on its own row: its router logits, its
+    top-k and weights, and its experts' FFN of its own (for fp8: own quantised)
+    row, combined in slot order with the shared expert added last.  This is
+    the combine of "CuTeDSL at Perplexity" (local combine) written per token,
+    without the permutation, so the large workloads can be checked on sampled
+    outputs.  `logits_override` holds the logits of the sampled tokens only.
+    """
+    tokens = np.asarray(tokens, dtype=np.int64)
+    n = len(tokens)
+    x = bf16_bits_to_f32(inputs["x_bf16"][tokens])
+    k, ns = inputs["k"], inputs["n_shared"]
+    E = inputs["w_router"].shape[0]
+    logits = (router_logits(x, inputs["w_router"], inputs.get("router_bias"))
+              if logits_override is None else np.asarray(logits_override, dtype=F32))
+    idx, w = topk_softmax(logits, k)
+    fp8 = inputs["wdtype"] == "fp8"
+    if fp8:
+        xc, xs = quantize_groups_128(x)
+        x = dequantize_groups_128(xc, xs)
+    H = x.shape[1]
+    y = np.zeros((n, k + ns, H), dtype=F32)       # expert output of each (token, slot)
+    for e in sorted(set(idx.ravel().tolist())):
+        rows, slots = np.nonzero(idx == e)
+        y[rows, slots] = expert_ffn(x[rows], *expert_weights_f32(inputs, e), quantize_h=fp8)
+    for s_ in range(ns):
+        y[:, k + s_] = expert_ffn(x, *expert_weights_f32(inputs, E + s_), quantize_h=fp8)
+    out = np.zeros((n, H), dtype=F32)
+    for j in range(k):
+        out = (out + (w[:, j:j + 1] * y[:, j]).astype(F32)).astype(F32)
+    for s_ in range(ns):
+        out = (out + y[:, k + s_]).astype(F32)
+    return OracleResult(tokens=tokens, logits=logits, topk_idx=idx, topk_w=w, out=out)

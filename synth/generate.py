@@ -2,7 +2,7 @@
 
 Recipe (per config):
 - x ~ N(0, 1), cast fp32 -> bf16 (round to nearest even, torch's cast).
-- router weight W_r [H, E] ~ N(0, router_std), kept fp32.
+- router weight W_r [E, H] (torch Linear layout) ~ N(0, router_std), kept fp32.
 - optional Zipf(s) popularity term b [E]: b_e = -s * ln(rho_e), rho a seeded
   permutation of 1..E, added to the router logits by the layer.
 - expert weights per expert e (keyed separately so any single expert can be
@@ -36,7 +36,7 @@ def _gen(device, seed: int, tensor_id: int, expert_id: int = 0) -> torch.Generat
 class LayerInputs:
     cfg: MoeConfig
     x: torch.Tensor                       # [T, H] bf16
-    w_router: torch.Tensor                # [H, E] fp32
+    w_router: torch.Tensor                # [E, H] fp32
     router_bias: Optional[torch.Tensor]   # [E] fp32 or None
     w_gate: torch.Tensor                  # [G, I, H] bf16 | uint8 e4m3fn codes
     w_up: torch.Tensor                    # [G, I, H]
@@ -77,7 +77,7 @@ def generate_layer(cfg: MoeConfig, device="cpu") -> LayerInputs:
     G = cfg.n_groups
     x = torch.randn((T, H), generator=_gen(device, cfg.seed, 0), device=device,
                     dtype=torch.float32).to(torch.bfloat16)
-    w_router = torch.randn((H, E), generator=_gen(device, cfg.seed, 1), device=device,
+    w_router = torch.randn((E, H), generator=_gen(device, cfg.seed, 1), device=device,
                            dtype=torch.float32) * cfg.router_std
     bias = None
     if cfg.zipf_s is not None:

@@ -43,10 +43,10 @@ def layer_bruteforce(inp):
     """Returns (out [T,H] float64, topk_idx [T,k], logits float64, boundary gap per token)."""
     x = _bf16_to_f64(inp["x_bf16"])
     T, H = x.shape
-    Wr = inp["w_router"].astype(np.float64)
-    E = Wr.shape[1]
+    Wr = inp["w_router"].astype(np.float64)          # [E, H]
+    E = Wr.shape[0]
     k, ns, fp8 = inp["k"], inp["n_shared"], inp["wdtype"] == "fp8"
-    logits = x @ Wr
+    logits = x @ Wr.T
     if inp.get("router_bias") is not None:
         logits = logits + inp["router_bias"].astype(np.float64)
     xin = _quant_dequant_rows_torch(x) if fp8 else x

@@ -91,9 +91,35 @@ def test_single_expert_is_dense_mlp():
 
 def test_logits_override_routes_from_given_logits():
     inp = to_numpy_inputs(generate_layer(CONFIGS[0]))
-    T, E = inp["x_bf16"].shape[0], inp["w_router"].shape[1]
+    T, E = inp["x_bf16"].shape[0], inp["w_router"].shape[0]
     forced = np.zeros((T, E), np.float32)
     forced[:, 5] = 1.0
     forced[:, 2] = 0.5
     res = forward(inp, logits_override=forced)
     assert np.all(res.topk_idx == np.array([5, 2])) and res.counts.tolist() == [0, 0, T, 0, 0, T, 0, 0]
+
+
+@pytest.mark.parametrize("ci", [0, 3])
+def test_forward_tokens_matches_full_forward(ci):
+    """The per-token evaluation equals the permuted evaluation on every token."""
+    from synth.configs import MoeConfig as C
+    base = CONFIGS[ci]
+    cfg = C(base.name + "_small", base.seed, T=48, H=256, E=min(base.E, 64), k=min(base.k, 6),
+            I=256, n_shared=base.n_shared, wdtype=base.wdtype, zipf_s=base.zipf_s)
+    inp = to_numpy_inputs(generate_layer(cfg))
+    full = forward(inp)
+    toks = np.array([0, 5, 17, 47, 3])
+    part = oracle.forward_tokens(inp, toks)
+    assert np.array_equal(part.topk_idx, full.topk_idx[toks])
+    assert _rel_inf(part.out, full.out[toks]) <= 1e-5
+
+
+def test_forward_tokens_fp8_shared_vs_bruteforce():
+    cfg = MoeConfig("fp8s", 11, T=20, H=256, E=9, k=3, I=256, n_shared=1, wdtype="fp8")
+    inp = to_numpy_inputs(generate_layer(cfg))
+    ref, ref_idx, _, gap = layer_bruteforce(inp)
+    toks = np.arange(20)
+    part = oracle.forward_tokens(inp, toks)
+    ok = gap > 1e-5
+    assert np.array_equal(part.topk_idx[ok], ref_idx[ok])
+    assert _rel_inf(part.out[ok], ref[ok]) <= 2e-2

@@ -39,7 +39,7 @@ def test_zero_router_weight_ties_everything():
     rng = np.random.default_rng(0)
     T, H, E, k = 17, 64, 12, 5
     x = rng.standard_normal((T, H)).astype(np.float32)
-    l = router_logits(x, np.zeros((H, E), np.float32))
+    l = router_logits(x, np.zeros((E, H), np.float32))
     idx, w = topk_softmax(l, k)
     assert np.all(idx == np.arange(k)[None, :])
     assert np.all(w == np.float32(1.0) / np.float32(k))
@@ -50,10 +50,10 @@ def test_router_logits_exact_on_integer_inputs():
     rng = np.random.default_rng(1)
     T, H, E = 7, 40, 9                       # H != E: a transposed operand would not even fit
     x = rng.integers(-4, 5, (T, H)).astype(np.float32)
-    W = rng.integers(-3, 4, (H, E)).astype(np.float32)
+    W = rng.integers(-3, 4, (E, H)).astype(np.float32)
     b = rng.integers(-2, 3, (E,)).astype(np.float32)
     l = router_logits(x, W, b)
-    ref = [[sum(int(x[t, h]) * int(W[h, e]) for h in range(H)) + int(b[e]) for e in range(E)]
+    ref = [[sum(int(x[t, h]) * int(W[e, h]) for h in range(H)) + int(b[e]) for e in range(E)]
            for t in range(T)]
     assert np.array_equal(l, np.array(ref, np.float32))
 
