@@ -1,0 +1,276 @@
+// C ABI of libmoe.so (declared in include/moe.h): argument validation,
+// workspace layout and the launch sequence of each entry point.  Everything
+// here runs on the host; all arithmetic of the layer is in the kernels.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+
+#include "../../include/moe.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MOE_OK;
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define MOE_NEED_PTR(p)                                                                   \
+  do {                                                                                    \
+    if ((p) == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s: %s is NULL", fn, #p);       \
+    if (!aligned16(p)) return fail(MOE_ERR_INVALID_ARG, "%s: %s not 16-byte aligned", fn, #p); \
+  } while (0)
+
+// Shape checks shared by every entry point.
+int check_shape(const char* fn, const moe_shape* s, bool need_ffn_dims) {
+  if (s == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s: shape is NULL", fn);
+  if (s->wdtype != MOE_BF16 && s->wdtype != MOE_FP8_E4M3_BLOCK128)
+    return fail(MOE_ERR_INVALID_ARG, "%s: unknown wdtype %d", fn, s->wdtype);
+  if (s->T < 0) return fail(MOE_ERR_UNSUPPORTED, "%s: T=%d < 0", fn, s->T);
+  if (s->E < 1 || s->E > 1024) return fail(MOE_ERR_UNSUPPORTED, "%s: E=%d not in [1,1024]", fn, s->E);
+  if (s->k < 1 || s->k > 16 || s->k > s->E)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: k=%d not in [1, min(E,16)]", fn, s->k);
+  if (s->n_shared != 0 && s->n_shared != 1)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: n_shared=%d not 0 or 1", fn, s->n_shared);
+  if ((long long)s->T * (s->k + s->n_shared) >= (1LL << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: T*(k+n_shared) >= 2^31", fn);
+  if (s->H < 128 || s->H % 128)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: H=%d not a positive multiple of 128", fn, s->H);
+  if (need_ffn_dims && (s->I < 128 || s->I % 128))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: I=%d not a positive multiple of 128", fn, s->I);
+  return MOE_OK;
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+// moe_forward workspace: routing, dispatch and expert intermediates.
+struct FwdLayout {
+  size_t logits, idx, w, counts, offsets, dest, src_row, x_perm, x_scale, y_perm, ffn, total;
+};
+
+FwdLayout fwd_layout(const moe_shape* s) {
+  const bool fp8 = s->wdtype == MOE_FP8_E4M3_BLOCK128;
+  const size_t T = s->T, H = s->H, E = s->E, k = s->k, G = s->E + s->n_shared;
+  const size_t R = T * (k + s->n_shared);
+  FwdLayout L{};
+  size_t off = 0;
+  L.logits = off;  off += align256(T * E * 4);
+  L.idx = off;     off += align256(T * k * 4);
+  L.w = off;       off += align256(T * k * 4);
+  L.counts = off;  off += align256(G * 4);
+  L.offsets = off; off += align256((G + 1) * 4);
+  L.dest = off;    off += align256(T * k * 4);
+  L.src_row = off; off += align256(R * 4);
+  L.x_perm = off;  off += align256(R * H * (fp8 ? 1 : 2));
+  L.x_scale = off; off += fp8 ? align256(R * (H / 128) * 4) : 0;
+  L.y_perm = off;  off += align256(R * H * 2);
+  L.ffn = off;
+  off += moe::ffn_workspace_bytes(s->T, s->H, s->E, s->k, s->I, s->n_shared, fp8);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err; }
+
+int moe_abi_version(void) { return 1; }
+
+size_t moe_forward_workspace_bytes(const moe_shape* shape) {
+  if (check_shape("moe_forward_workspace_bytes", shape, true) != MOE_OK) return 0;
+  return fwd_layout(shape).total;
+}
+
+size_t moe_ffn_workspace_bytes(const moe_shape* shape) {
+  if (check_shape("moe_ffn_workspace_bytes", shape, true) != MOE_OK) return 0;
+  return moe::ffn_workspace_bytes(shape->T, shape->H, shape->E, shape->k, shape->I,
+                                  shape->n_shared, shape->wdtype == MOE_FP8_E4M3_BLOCK128);
+}
+
+int moe_route(const moe_shape* shape, const void* x, const float* w_router,
+              const float* router_bias, float* logits, int32_t* topk_idx, float* topk_w,
+              void* stream) {
+  const char* fn = "moe_route";
+  if (int rc = check_shape(fn, shape, false)) return rc;
+  if (shape->T == 0) return MOE_OK;
+  MOE_NEED_PTR(x);
+  MOE_NEED_PTR(w_router);
+  MOE_NEED_PTR(logits);
+  MOE_NEED_PTR(topk_idx);
+  MOE_NEED_PTR(topk_w);
+  if (router_bias && !aligned16(router_bias))
+    return fail(MOE_ERR_INVALID_ARG, "%s: router_bias not 16-byte aligned", fn);
+  hipError_t e = moe::launch_router_gemm(static_cast<const uint16_t*>(x), w_router, router_bias,
+                                         logits, shape->T, shape->H, shape->E, as_stream(stream));
+  if (e == hipSuccess)
+    e = moe::launch_topk(logits, topk_idx, topk_w, shape->T, shape->E, shape->k, as_stream(stream));
+  return hip_status(e, fn);
+}
+
+int moe_route_from_logits(const moe_shape* shape, const float* logits, int32_t* topk_idx,
+                          float* topk_w, void* stream) {
+  const char* fn = "moe_route_from_logits";
+  if (shape == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s: shape is NULL", fn);
+  if (shape->T < 0) return fail(MOE_ERR_UNSUPPORTED, "%s: T < 0", fn);
+  if (shape->E < 1 || shape->E > 1024) return fail(MOE_ERR_UNSUPPORTED, "%s: E not in [1,1024]", fn);
+  if (shape->k < 1 || shape->k > 16 || shape->k > shape->E)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: k not in [1, min(E,16)]", fn);
+  if (shape->T == 0) return MOE_OK;
+  MOE_NEED_PTR(logits);
+  MOE_NEED_PTR(topk_idx);
+  MOE_NEED_PTR(topk_w);
+  return hip_status(moe::launch_topk(logits, topk_idx, topk_w, shape->T, shape->E, shape->k,
+                                     as_stream(stream)), fn);
+}
+
+int moe_permute(const moe_shape* shape, const int32_t* topk_idx, const void* x, int32_t* counts,
+                int32_t* offsets, int32_t* dest, int32_t* src_row, void* x_perm,
+                float* x_perm_scale, void* stream) {
+  const char* fn = "moe_permute";
+  if (int rc = check_shape(fn, shape, false)) return rc;
+  const bool fp8 = shape->wdtype == MOE_FP8_E4M3_BLOCK128;
+  MOE_NEED_PTR(counts);
+  MOE_NEED_PTR(offsets);
+  if (shape->T > 0) {
+    MOE_NEED_PTR(topk_idx);
+    MOE_NEED_PTR(x);
+    MOE_NEED_PTR(dest);
+    MOE_NEED_PTR(src_row);
+    MOE_NEED_PTR(x_perm);
+    if (fp8) MOE_NEED_PTR(x_perm_scale);
+  }
+  return hip_status(moe::launch_permute(topk_idx, static_cast<const uint16_t*>(x), counts, offsets,
+                                        dest, src_row, x_perm, x_perm_scale, shape->T, shape->H,
+                                        shape->E, shape->k, shape->n_shared, fp8,
+                                        as_stream(stream)), fn);
+}
+
+int moe_grouped_ffn(const moe_shape* shape, const int32_t* offsets, const void* x_perm,
+                    const float* x_perm_scale, const void* w_gate, const void* w_up,
+                    const void* w_down, const float* s_gate, const float* s_up,
+                    const float* s_down, void* y_perm, void* workspace, size_t ws_bytes,
+                    void* stream) {
+  const char* fn = "moe_grouped_ffn";
+  if (int rc = check_shape(fn, shape, true)) return rc;
+  const bool fp8 = shape->wdtype == MOE_FP8_E4M3_BLOCK128;
+  if (shape->T == 0) return MOE_OK;
+  MOE_NEED_PTR(offsets);
+  MOE_NEED_PTR(x_perm);
+  MOE_NEED_PTR(w_gate);
+  MOE_NEED_PTR(w_up);
+  MOE_NEED_PTR(w_down);
+  MOE_NEED_PTR(y_perm);
+  if (fp8) {
+    MOE_NEED_PTR(x_perm_scale);
+    MOE_NEED_PTR(s_gate);
+    MOE_NEED_PTR(s_up);
+    MOE_NEED_PTR(s_down);
+  }
+  const size_t need = moe_ffn_workspace_bytes(shape);
+  if (workspace == nullptr || ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: workspace not 256-byte aligned", fn);
+  moe::FfnArgs a{shape->T, shape->H, shape->E, shape->k, shape->I, shape->n_shared, fp8,
+                 offsets, x_perm, x_perm_scale, w_gate, w_up, w_down, s_gate, s_up, s_down,
+                 y_perm, workspace};
+  return hip_status(moe::launch_grouped_ffn(a, as_stream(stream)), fn);
+}
+
+int moe_combine(const moe_shape* shape, const void* y_perm, const int32_t* dest,
+                const float* topk_w, void* out, void* stream) {
+  const char* fn = "moe_combine";
+  if (int rc = check_shape(fn, shape, false)) return rc;
+  if (shape->T == 0) return MOE_OK;
+  MOE_NEED_PTR(y_perm);
+  MOE_NEED_PTR(dest);
+  MOE_NEED_PTR(topk_w);
+  MOE_NEED_PTR(out);
+  return hip_status(moe::launch_combine(static_cast<const uint16_t*>(y_perm), dest, topk_w,
+                                        static_cast<uint16_t*>(out), shape->T, shape->H, shape->k,
+                                        shape->n_shared, as_stream(stream)), fn);
+}
+
+int moe_forward(const moe_shape* shape, const void* x, const float* w_router,
+                const float* router_bias, const void* w_gate, const void* w_up,
+                const void* w_down, const float* s_gate, const float* s_up, const float* s_down,
+                void* out, int32_t* topk_idx_out, float* topk_w_out, void* workspace,
+                size_t ws_bytes, void* stream) {
+  const char* fn = "moe_forward";
+  if (int rc = check_shape(fn, shape, true)) return rc;
+  const bool fp8 = shape->wdtype == MOE_FP8_E4M3_BLOCK128;
+  if (shape->T == 0) return MOE_OK;
+  MOE_NEED_PTR(x);
+  MOE_NEED_PTR(w_router);
+  MOE_NEED_PTR(w_gate);
+  MOE_NEED_PTR(w_up);
+  MOE_NEED_PTR(w_down);
+  MOE_NEED_PTR(out);
+  if (fp8) {
+    MOE_NEED_PTR(s_gate);
+    MOE_NEED_PTR(s_up);
+    MOE_NEED_PTR(s_down);
+  }
+  if (router_bias && !aligned16(router_bias))
+    return fail(MOE_ERR_INVALID_ARG, "%s: router_bias not 16-byte aligned", fn);
+  if (topk_idx_out && !aligned16(topk_idx_out))
+    return fail(MOE_ERR_INVALID_ARG, "%s: topk_idx_out not 16-byte aligned", fn);
+  if (topk_w_out && !aligned16(topk_w_out))
+    return fail(MOE_ERR_INVALID_ARG, "%s: topk_w_out not 16-byte aligned", fn);
+  const FwdLayout L = fwd_layout(shape);
+  if (workspace == nullptr || ws_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, L.total);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: workspace not 256-byte aligned", fn);
+
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* logits = reinterpret_cast<float*>(ws + L.logits);
+  int32_t* idx = topk_idx_out ? topk_idx_out : reinterpret_cast<int32_t*>(ws + L.idx);
+  float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + L.w);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  int32_t* dest = reinterpret_cast<int32_t*>(ws + L.dest);
+  int32_t* src_row = reinterpret_cast<int32_t*>(ws + L.src_row);
+  void* x_perm = ws + L.x_perm;
+  float* x_scale = fp8 ? reinterpret_cast<float*>(ws + L.x_scale) : nullptr;
+  void* y_perm = ws + L.y_perm;
+  hipStream_t s = as_stream(stream);
+
+  hipError_t e = moe::launch_router_gemm(static_cast<const uint16_t*>(x), w_router, router_bias,
+                                         logits, shape->T, shape->H, shape->E, s);
+  if (e == hipSuccess) e = moe::launch_topk(logits, idx, w, shape->T, shape->E, shape->k, s);
+  if (e == hipSuccess)
+    e = moe::launch_permute(idx, static_cast<const uint16_t*>(x), counts, offsets, dest, src_row,
+                            x_perm, x_scale, shape->T, shape->H, shape->E, shape->k,
+                            shape->n_shared, fp8, s);
+  if (e == hipSuccess) {
+    moe::FfnArgs a{shape->T, shape->H, shape->E, shape->k, shape->I, shape->n_shared, fp8,
+                   offsets, x_perm, x_scale, w_gate, w_up, w_down, s_gate, s_up, s_down,
+                   y_perm, ws + L.ffn};
+    e = moe::launch_grouped_ffn(a, s);
+  }
+  if (e == hipSuccess)
+    e = moe::launch_combine(static_cast<const uint16_t*>(y_perm), dest, w,
+                            static_cast<uint16_t*>(out), shape->T, shape->H, shape->k,
+                            shape->n_shared, s);
+  return hip_status(e, fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// Combine: out[t] = bf16( sum_j w[t,j] * y_perm[dest[t,j]] (+ y_perm[T*k + t]) )
+// ("CuTeDSL at Perplexity", local combine: vectorised weighted accumulation in
+// registers from the offsets the dispatch computed; the DeepSeek-deployment
+// page's shared expert is added after the routed sum).
+//
+// A gather, not a scatter: each token reads its k rows, so no atomics are
+// needed and the summation order (slot order, then the shared row) is fixed.
+// Contraction is disabled so each term is one rounded product and one rounded
+// add, which makes the result reproducible and checkable bit for bit.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+#pragma clang fp contract(off)
+
+template <int TPB>
+__global__ __launch_bounds__(TPB) void k_combine(const uint16_t* __restrict__ y_perm,
+                                                 const int32_t* __restrict__ dest,
+                                                 const float* __restrict__ topk_w,
+                                                 uint16_t* __restrict__ out, int T, int H, int k,
+                                                 int n_shared) {
+  const int t = blockIdx.x;
+  const int chunks = H / 8;
+  for (int c = threadIdx.x; c < chunks; c += TPB) {
+    float acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const float w = topk_w[(size_t)t * k + j];
+      const int row = dest[(size_t)t * k + j];
+      float v[8];
+      unpack_bf16x8(reinterpret_cast<const u32x4_t*>(y_perm + (size_t)row * H)[c], v);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = acc[q] + w * v[q];
+    }
+    if (n_shared) {
+      float v[8];
+      unpack_bf16x8(reinterpret_cast<const u32x4_t*>(y_perm + ((size_t)T * k + t) * H)[c], v);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = acc[q] + v[q];
+    }
+    reinterpret_cast<u32x4_t*>(out + (size_t)t * H)[c] = pack_bf16x8(acc);
+  }
+}
+
+hipError_t launch_combine(const uint16_t* y_perm, const int32_t* dest, const float* topk_w,
+                          uint16_t* out, int T, int H, int k, int n_shared, hipStream_t s) {
+  if (H / 8 <= 256)
+    hipLaunchKernelGGL((k_combine<64>), dim3(T), dim3(64), 0, s, y_perm, dest, topk_w, out, T, H,
+                       k, n_shared);
+  else
+    hipLaunchKernelGGL((k_combine<256>), dim3(T), dim3(256), 0, s, y_perm, dest, topk_w, out, T, H,
+                       k, n_shared);
+  return hipGetLastError();
+}
+
+}  // namespace moe

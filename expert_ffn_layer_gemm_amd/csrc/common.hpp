@@ -1,0 +1,103 @@
+// Shared device helpers for the gfx950 MoE kernels: vector types, bf16 and
+// e4m3fn conversions, MFMA wrappers and wave-level reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bf16 ----
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (inputs are finite here).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Unpack 8 bf16 values held in a 16-byte word.
+__device__ __forceinline__ void unpack_bf16x8(const u32x4_t v, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(v[i] << 16);
+    f[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+  }
+}
+
+__device__ __forceinline__ u32x4_t pack_bf16x8(const float* f) {
+  u32x4_t r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = f32_to_bf16_bits(f[2 * i]) | (f32_to_bf16_bits(f[2 * i + 1]) << 16);
+  return r;
+}
+
+// --------------------------------------------------------------- e4m3fn ----
+// Round-to-nearest-even encoding of a finite fp32 value with |v| <= 448 into
+// an OCP e4m3fn code (bias 7, 3 mantissa bits, subnormals below 2^-6).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  uint32_t b = __float_as_uint(v);
+  uint32_t sign = (b >> 24) & 0x80u;
+  uint32_t a = b & 0x7FFFFFFFu;
+  float af = __uint_as_float(a);
+  uint32_t code;
+  if (af < 0.015625f) {               // 2^-6: subnormal range, value m * 2^-9
+    code = (uint32_t)__builtin_rintf(af * 512.0f);   // exact scaling, ties to even
+  } else {
+    uint32_t e = a >> 23;             // biased fp32 exponent, 121..135
+    uint32_t m = (a & 0x7FFFFFu);
+    uint32_t r = m >> 20;             // top 3 mantissa bits
+    uint32_t rem = m & 0xFFFFFu;
+    r += (rem > 0x80000u) || (rem == 0x80000u && (r & 1u));
+    if (r == 8u) { r = 0u; ++e; }
+    code = ((e - 120u) << 3) | r;     // e - 127 + 7
+  }
+  return sign | code;
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  uint32_t ef = (c >> 3) & 0xFu, mf = c & 7u;
+  float mag = ef == 0 ? (float)mf * 0.001953125f
+                      : __uint_as_float(((ef + 120u) << 23) | (mf << 20));
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// ----------------------------------------------------------------- MFMA ----
+// D(16x16 fp32) += A(16x32 bf16) * B(32x16 bf16).  Lane l supplies row l%16
+// of A and column l%16 of B, 8 consecutive k each; lane l receives
+// D[4*(l/16) + i][l%16], i = 0..3.
+__device__ __forceinline__ f32x4_t mfma_bf16_16x16x32(const u32x4_t a, const u32x4_t b,
+                                                     f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// D(16x16 fp32) += A(16x128 e4m3) * B(128x16 e4m3), unit scales.  Lane l
+// supplies 32 codes of row l%16 of A and of column l%16 of B.
+__device__ __forceinline__ f32x4_t mfma_fp8_16x16x128(const i32x8_t a, const i32x8_t b,
+                                                     f32x4_t c) {
+  // cbsz = blgp = 0 selects e4m3 for both operands; scale 127 = 2^0 (e8m0).
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// ------------------------------------------------------- wave reductions ----
+__device__ __forceinline__ float wave_max_xor(float v, int lanes) {
+  for (int m = 1; m < lanes; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+
+__host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace moe

@@ -1,0 +1,671 @@
+// Grouped expert FFN: for every non-empty group g (rows [offsets[g],
+// offsets[g+1]) of the permuted matrix)
+//     h = silu(X W_gate[g]^T) * (X W_up[g]^T)      (gate/up GEMM, SwiGLU epilogue)
+//     y = h W_down[g]^T                            (down GEMM)
+// with fp32 accumulation on the MFMA units.  SwiGLU is fused into the gate/up
+// GEMM as in the Ironwood page's GMM v2 (section 4.2.2): the gate and up
+// weights are two B streams of the same workgroup, so each output element has
+// its gate and up sums in the same lane.  FP8 layers follow the DeepSeek
+// deployment page (Quantization): e4m3 operands, one fp32 scale per 128x128
+// weight block and per 128 activation channels, applied to the fp32
+// accumulator once per 128-wide K block; the SwiGLU epilogue re-quantises h
+// per row per 128 channels.
+//
+// Scheduling (DeepSeek-deployment page, Quantization and CUDA Graph
+// sections: kernels read the routed token counts on the device instead of
+// sizing work from the buffer's upper bound).  One small kernel reads
+// `offsets` and writes two work lists into the workspace:
+//   - skinny list: groups with 1..kSkinnyMax rows.  Decode-sized groups are
+//     bound by streaming their weights from HBM; the skinny kernel keeps the
+//     few activation rows in registers (straight from L2) and streams each
+//     weight byte exactly once, 16 bytes per lane, with the next K block's
+//     weight loads in flight while the current one is multiplied.
+//   - tile list: (group, first row) pairs covering groups with more rows, for
+//     an LDS-tiled MFMA kernel (prefill-sized groups, compute bound).
+// Both GEMM grids are sized on the host from upper bounds; workgroups past
+// the device-side list length exit at once.  No host synchronisation.
+#include <algorithm>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+constexpr int kSkinnyMax = 64;      // rows handled by the skinny kernel (4 MFMA row blocks)
+constexpr int kTileWaves = 8;       // tiled kernel: 4 (rows) x 2 (cols) waves
+constexpr int kTileFM = 2, kTileFN = 4;
+constexpr int kTileBM = 4 * 16 * kTileFM;   // 128 rows per tile
+constexpr int kTileBN = 2 * 16 * kTileFN;   // 128 output columns per tile
+constexpr int kLdsStride = 144;             // bytes per staged 128-byte K row (+16 pad)
+
+// Skinny groups are split into row classes (<= 16, <= 32, <= 64 rows) so each
+// class runs a kernel whose register use matches its row blocks.
+constexpr int kSkinnyClasses = 3;
+__host__ __device__ constexpr int skinny_class_rows(int c) { return 16 << c; }
+
+struct Sched {
+  int32_t* n_skinny;  // [kSkinnyClasses]
+  int32_t* n_tiles;
+  int32_t* skinny;    // [kSkinnyClasses][G] group ids
+  int32_t* tiles;     // [max_tiles][2] (group, first row)
+  int G;
+};
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.f + expf(-g)) * u; }
+
+// ------------------------------------------------------------------ plan ----
+__device__ __forceinline__ void block_scan_pair(int a, int b, int* wave_sum, int& excl_a,
+                                                int& total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int s = a + b;
+  int incl = s;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wave_sum[wave] = incl;
+  __syncthreads();
+  int before = 0, tot = 0;
+  for (int w = 0; w < 16; ++w) {
+    if (w < wave) before += wave_sum[w];
+    tot += wave_sum[w];
+  }
+  excl_a = before + incl - s;
+  total = tot;
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ offsets, Sched sc) {
+  __shared__ int wave_sum[16];
+  const int tid = threadIdx.x, G = sc.G;
+  int m[2], cls[2], nt[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int g = 2 * tid + q;
+    m[q] = g < G ? offsets[g + 1] - offsets[g] : 0;
+    cls[q] = -1;
+    if (m[q] > 0 && m[q] <= kSkinnyMax)
+      cls[q] = m[q] <= skinny_class_rows(0) ? 0 : (m[q] <= skinny_class_rows(1) ? 1 : 2);
+    nt[q] = m[q] > kSkinnyMax ? ceil_div(m[q], kTileBM) : 0;
+  }
+#pragma unroll
+  for (int c = 0; c < kSkinnyClasses; ++c) {
+    int pos, total;
+    block_scan_pair(cls[0] == c, cls[1] == c, wave_sum, pos, total);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      if (cls[q] == c) sc.skinny[c * G + pos++] = 2 * tid + q;
+    if (tid == 0) sc.n_skinny[c] = total;
+  }
+  int nt_pos, nt_total;
+  block_scan_pair(nt[0], nt[1], wave_sum, nt_pos, nt_total);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int g = 2 * tid + q;
+    for (int i = 0; i < nt[q]; ++i) {
+      sc.tiles[2 * nt_pos] = g;
+      sc.tiles[2 * nt_pos + 1] = i * kTileBM;
+      ++nt_pos;
+    }
+  }
+  if (tid == 0) *sc.n_tiles = nt_total;
+}
+
+// Operands of one grouped GEMM launch.  Row-major, K contiguous:
+// A [R, K] (x_perm or h), B0/B1 [G, N, K] (gate/up or down), out [R, N].
+struct GemmArgs {
+  Sched sc;
+  const int32_t* offsets;
+  const uint8_t* A;
+  const float* A_scale;    // [R, K/128] (fp8)
+  const uint8_t* B0;
+  const uint8_t* B1;       // up weights (dual) or unused
+  const float* s_B0;       // [G, N/128, K/128] (fp8)
+  const float* s_B1;
+  uint8_t* out;            // bf16 or e4m3 codes
+  float* out_scale;        // [R, N/128] (fp8 dual)
+  int K, N, n_ntile;
+};
+
+// ---------------------------------------------------------- skinny, bf16 ----
+// Workgroup = NW waves; wave w owns 16 output columns and all (<= 16*MB) rows
+// of the group.  Lane l: row/column l%16 of each 16x16 MFMA block, 8
+// consecutive k at offset 8*(l/16) of each 32-wide K step.
+template <bool DUAL, int NW, int MB>
+__global__ __launch_bounds__(64 * NW) void k_skinny_bf16(const GemmArgs p) {
+  constexpr int CLS = MB == 1 ? 0 : (MB == 2 ? 1 : 2);
+  const int slot = blockIdx.x / p.n_ntile, nt = blockIdx.x % p.n_ntile;
+  if (slot >= p.sc.n_skinny[CLS]) return;
+  const int g = p.sc.skinny[CLS * p.sc.G + slot];
+  const int row0 = p.offsets[g], m = p.offsets[g + 1] - row0;
+  const int nmb = ceil_div(m, 16);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, kq = (lane >> 4) * 8;
+  const int K = p.K, N = p.N;
+  const int n0 = (nt * NW + wave) * 16;
+
+  const uint16_t* b0 = reinterpret_cast<const uint16_t*>(p.B0) + ((size_t)g * N + n0 + r16) * K + kq;
+  const uint16_t* b1 = DUAL ? reinterpret_cast<const uint16_t*>(p.B1) + ((size_t)g * N + n0 + r16) * K + kq
+                            : nullptr;
+  const uint16_t* arow[MB];
+  bool aok[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int r = mb * 16 + r16;
+    aok[mb] = r < m;
+    arow[mb] = reinterpret_cast<const uint16_t*>(p.A) + (size_t)(row0 + (aok[mb] ? r : 0)) * K + kq;
+  }
+
+  f32x4_t acc0[MB], acc1[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc0[mb] = acc1[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  constexpr int U = 4;  // 32-wide K steps per iteration (128 of K)
+  u32x4_t cur0[U], cur1[U], nxt0[U], nxt1[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    cur0[u] = *reinterpret_cast<const u32x4_t*>(b0 + u * 32);
+    if (DUAL) cur1[u] = *reinterpret_cast<const u32x4_t*>(b1 + u * 32);
+  }
+  for (int k0 = 0; k0 < K; k0 += 32 * U) {
+    const bool more = k0 + 32 * U < K;
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        nxt0[u] = *reinterpret_cast<const u32x4_t*>(b0 + k0 + 32 * U + u * 32);
+        if (DUAL) nxt1[u] = *reinterpret_cast<const u32x4_t*>(b1 + k0 + 32 * U + u * 32);
+      }
+    }
+    u32x4_t a[MB][U];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      if (mb < nmb) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          a[mb][u] = aok[mb] ? *reinterpret_cast<const u32x4_t*>(arow[mb] + k0 + u * 32)
+                             : u32x4_t{0, 0, 0, 0};
+      }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        if (mb < nmb) {
+          acc0[mb] = mfma_bf16_16x16x32(a[mb][u], cur0[u], acc0[mb]);
+          if (DUAL) acc1[mb] = mfma_bf16_16x16x32(a[mb][u], cur1[u], acc1[mb]);
+        }
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        cur0[u] = nxt0[u];
+        if (DUAL) cur1[u] = nxt1[u];
+      }
+    }
+  }
+
+  uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+    if (mb < nmb) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = mb * 16 + (lane >> 4) * 4 + q;
+        if (r < m) {
+          const float v = DUAL ? silu_mul(acc0[mb][q], acc1[mb][q]) : acc0[mb][q];
+          out[(size_t)(row0 + r) * N + n0 + r16] = (uint16_t)f32_to_bf16_bits(v);
+        }
+      }
+    }
+}
+
+// ----------------------------------------------------------- skinny, fp8 ----
+// Same scheme with the e4m3 16x16x128 MFMA: one MFMA per 128-wide K block;
+// lane l supplies 32 codes at K offset 32*(l/16).  The block partial is scaled
+// by (activation scale of its row) * (weight block scale) into fp32.
+// DUAL needs NW = 8 so a workgroup covers one 128-column group of h, whose
+// row maxima are combined across waves through LDS.
+template <bool DUAL, int NW, int MB>
+__global__ __launch_bounds__(64 * NW) void k_skinny_fp8(const GemmArgs p) {
+  constexpr int CLS = MB == 1 ? 0 : (MB == 2 ? 1 : 2);
+  __shared__ float row_amax[NW][16 * MB];
+  const int slot = blockIdx.x / p.n_ntile, nt = blockIdx.x % p.n_ntile;
+  if (slot >= p.sc.n_skinny[CLS]) return;
+  const int g = p.sc.skinny[CLS * p.sc.G + slot];
+  const int row0 = p.offsets[g], m = p.offsets[g + 1] - row0;
+  const int nmb = ceil_div(m, 16);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, kq = (lane >> 4) * 32;
+  const int K = p.K, N = p.N, KB = K / 128;
+  const int n0 = (nt * NW + wave) * 16;
+  const int nblk = n0 / 128;
+
+  const uint8_t* b0 = p.B0 + ((size_t)g * N + n0 + r16) * K + kq;
+  const uint8_t* b1 = DUAL ? p.B1 + ((size_t)g * N + n0 + r16) * K + kq : nullptr;
+  const float* sb0 = p.s_B0 + ((size_t)g * (N / 128) + nblk) * KB;
+  const float* sb1 = DUAL ? p.s_B1 + ((size_t)g * (N / 128) + nblk) * KB : nullptr;
+  const uint8_t* arow[MB];
+  bool aok[MB];
+  const float* srow[MB][4];
+  bool sok[MB][4];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int r = mb * 16 + r16;
+    aok[mb] = r < m;
+    arow[mb] = p.A + (size_t)(row0 + (aok[mb] ? r : 0)) * K + kq;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int rr = mb * 16 + (lane >> 4) * 4 + q;
+      sok[mb][q] = rr < m;
+      srow[mb][q] = p.A_scale + (size_t)(row0 + (sok[mb][q] ? rr : 0)) * KB;
+    }
+  }
+  f32x4_t acc0[MB], acc1[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc0[mb] = acc1[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  i32x8_t cur0 = *reinterpret_cast<const i32x8_t*>(b0), cur1{};
+  if (DUAL) cur1 = *reinterpret_cast<const i32x8_t*>(b1);
+  for (int kb = 0; kb < KB; ++kb) {
+    const bool more = kb + 1 < KB;
+    i32x8_t nxt0{}, nxt1{};
+    if (more) {
+      nxt0 = *reinterpret_cast<const i32x8_t*>(b0 + (kb + 1) * 128);
+      if (DUAL) nxt1 = *reinterpret_cast<const i32x8_t*>(b1 + (kb + 1) * 128);
+    }
+    const float s0 = sb0[kb], s1 = DUAL ? sb1[kb] : 0.f;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      if (mb < nmb) {
+        const i32x8_t a = aok[mb] ? *reinterpret_cast<const i32x8_t*>(arow[mb] + kb * 128) : i32x8_t{};
+        const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+        const f32x4_t p0 = mfma_fp8_16x16x128(a, cur0, z);
+        f32x4_t p1 = z;
+        if (DUAL) p1 = mfma_fp8_16x16x128(a, cur1, z);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float sa = sok[mb][q] ? srow[mb][q][kb] : 0.f;
+          acc0[mb][q] += p0[q] * (sa * s0);
+          if (DUAL) acc1[mb][q] += p1[q] * (sa * s1);
+        }
+      }
+    if (more) { cur0 = nxt0; if (DUAL) cur1 = nxt1; }
+  }
+
+  if constexpr (DUAL) {
+    // h = silu(g) * u, then per-row amax over the workgroup's 128 columns.
+    float hv[MB][4];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = mb * 16 + (lane >> 4) * 4 + q;
+        hv[mb][q] = (mb < nmb && r < m) ? silu_mul(acc0[mb][q], acc1[mb][q]) : 0.f;
+        const float am = wave_max_xor(fabsf(hv[mb][q]), 16);
+        if (r16 == 0) row_amax[wave][r] = am;
+      }
+    __syncthreads();
+    const int N128 = N / 128;
+    const int gcol = (nt * NW * 16) / 128;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      if (mb < nmb) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = mb * 16 + (lane >> 4) * 4 + q;
+          if (r < m) {
+            float am = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) am = fmaxf(am, row_amax[w][r]);
+            const float scale = am == 0.f ? 1.f : am / 448.f;
+            const float qv = fminf(fmaxf(hv[mb][q] / scale, -448.f), 448.f);
+            p.out[(size_t)(row0 + r) * N + n0 + r16] = (uint8_t)f32_to_e4m3(qv);
+            if (wave == 0 && r16 == 0) p.out_scale[(size_t)(row0 + r) * N128 + gcol] = scale;
+          }
+        }
+      }
+  } else {
+    uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      if (mb < nmb) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = mb * 16 + (lane >> 4) * 4 + q;
+          if (r < m) out[(size_t)(row0 + r) * N + n0 + r16] = (uint16_t)f32_to_bf16_bits(acc0[mb][q]);
+        }
+      }
+  }
+}
+
+// ------------------------------------------------------------- LDS tiled ----
+// Workgroup: 8 waves as 4 (rows) x 2 (columns); tile = 128 rows x 128 output
+// columns; each K iteration stages one 128-byte K chunk per row (64 bf16 or
+// 128 e4m3 values) of A (128 rows) and B (128 rows, or 256 for gate+up) in
+// LDS, double-buffered: the next chunk's global loads are issued into
+// registers before the current chunk is multiplied, and stored to the other
+// LDS buffer after it.  Rows are padded to 144 bytes so the 16-byte fragment
+// reads of 8 consecutive lanes (8 different rows) hit distinct banks.
+template <bool FP8, bool DUAL>
+struct TileCfg {
+  static constexpr int BROWS = DUAL ? 2 * kTileBN : kTileBN;
+  static constexpr int ROWS = kTileBM + BROWS;
+  static constexpr int CHUNKS = ROWS * 8;                       // 16-byte chunks per stage
+  static constexpr int PER_THREAD = CHUNKS / (64 * kTileWaves);
+  static constexpr int LDS_BYTES = 2 * ROWS * kLdsStride;
+};
+
+template <bool FP8, bool DUAL>
+__global__ __launch_bounds__(64 * kTileWaves) void k_tiled(const GemmArgs p) {
+  using C = TileCfg<FP8, DUAL>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS_BYTES];
+  const int slot = blockIdx.x / p.n_ntile, nt = blockIdx.x % p.n_ntile;
+  if (slot >= *p.sc.n_tiles) return;
+  const int g = p.sc.tiles[2 * slot], m0 = p.sc.tiles[2 * slot + 1];
+  const int row0 = p.offsets[g] + m0;
+  const int mrows = min(kTileBM, p.offsets[g + 1] - row0);
+  const int K = p.K, N = p.N;
+  const int Kbytes = FP8 ? K : 2 * K;
+  const int n0 = nt * kTileBN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r16 = lane & 15;
+
+  // Global source of each staged 16-byte chunk this thread moves.
+  const uint8_t* src[C::PER_THREAD];
+  bool ok[C::PER_THREAD];
+  int dst[C::PER_THREAD];
+#pragma unroll
+  for (int i = 0; i < C::PER_THREAD; ++i) {
+    const int c = tid + i * 64 * kTileWaves;
+    const int row = c >> 3, col = (c & 7) * 16;
+    dst[i] = row * kLdsStride + col;
+    if (row < kTileBM) {
+      ok[i] = row < mrows;
+      src[i] = p.A + (size_t)(row0 + (ok[i] ? row : 0)) * Kbytes + col;
+    } else {
+      const int br = row - kTileBM;
+      const bool up = DUAL && br >= kTileBN;
+      const int n = n0 + (up ? br - kTileBN : br);
+      ok[i] = true;
+      src[i] = (up ? p.B1 : p.B0) + ((size_t)g * N + n) * Kbytes + col;
+    }
+  }
+  u32x4_t stage[C::PER_THREAD];
+  auto load = [&](int kc) {
+#pragma unroll
+    for (int i = 0; i < C::PER_THREAD; ++i)
+      stage[i] = ok[i] ? *reinterpret_cast<const u32x4_t*>(src[i] + (size_t)kc * 128)
+                       : u32x4_t{0, 0, 0, 0};
+  };
+  auto store = [&](int buf) {
+    uint8_t* base = lds + buf * C::ROWS * kLdsStride;
+#pragma unroll
+    for (int i = 0; i < C::PER_THREAD; ++i) *reinterpret_cast<u32x4_t*>(base + dst[i]) = stage[i];
+  };
+
+  f32x4_t acc0[kTileFM][kTileFN], acc1[kTileFM][kTileFN];
+#pragma unroll
+  for (int i = 0; i < kTileFM; ++i)
+#pragma unroll
+    for (int j = 0; j < kTileFN; ++j) acc0[i][j] = acc1[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Rows of this wave's fragments inside the tile.
+  const int arow0 = wm * 16 * kTileFM;
+  const int bcol0 = wn * 16 * kTileFN;
+  const int nk = Kbytes / 128;
+  const int KB = K / 128;
+  const int nblk = n0 / 128;
+  const float* sb0 = FP8 ? p.s_B0 + ((size_t)g * (N / 128) + nblk) * KB : nullptr;
+  const float* sb1 = (FP8 && DUAL) ? p.s_B1 + ((size_t)g * (N / 128) + nblk) * KB : nullptr;
+  const bool wave_active = arow0 < mrows;
+
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int kc = 0; kc < nk; ++kc) {
+    const int buf = kc & 1;
+    if (kc + 1 < nk) load(kc + 1);
+    const uint8_t* As = lds + buf * C::ROWS * kLdsStride;
+    const uint8_t* Bs = As + kTileBM * kLdsStride;
+    if (wave_active) {
+      if constexpr (!FP8) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {   // two 32-wide K steps per 64-element chunk
+          const int off = ks * 64 + (lane >> 4) * 16;
+          u32x4_t a[kTileFM], b0[kTileFN], b1[kTileFN];
+#pragma unroll
+          for (int i = 0; i < kTileFM; ++i)
+            a[i] = *reinterpret_cast<const u32x4_t*>(As + (arow0 + i * 16 + r16) * kLdsStride + off);
+#pragma unroll
+          for (int j = 0; j < kTileFN; ++j) {
+            b0[j] = *reinterpret_cast<const u32x4_t*>(Bs + (bcol0 + j * 16 + r16) * kLdsStride + off);
+            if (DUAL)
+              b1[j] = *reinterpret_cast<const u32x4_t*>(Bs + (kTileBN + bcol0 + j * 16 + r16) * kLdsStride + off);
+          }
+#pragma unroll
+          for (int i = 0; i < kTileFM; ++i)
+#pragma unroll
+            for (int j = 0; j < kTileFN; ++j) {
+              acc0[i][j] = mfma_bf16_16x16x32(a[i], b0[j], acc0[i][j]);
+              if (DUAL) acc1[i][j] = mfma_bf16_16x16x32(a[i], b1[j], acc1[i][j]);
+            }
+        }
+      } else {
+        const int off = (lane >> 4) * 32;
+        i32x8_t a[kTileFM], b0[kTileFN], b1[kTileFN];
+#pragma unroll
+        for (int i = 0; i < kTileFM; ++i) {
+          const uint8_t* pa = As + (arow0 + i * 16 + r16) * kLdsStride + off;
+          const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(pa), hi = *reinterpret_cast<const u32x4_t*>(pa + 16);
+          a[i] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        }
+#pragma unroll
+        for (int j = 0; j < kTileFN; ++j) {
+          const uint8_t* pb = Bs + (bcol0 + j * 16 + r16) * kLdsStride + off;
+          const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(pb), hi = *reinterpret_cast<const u32x4_t*>(pb + 16);
+          b0[j] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+          if (DUAL) {
+            const uint8_t* pu = pb + kTileBN * kLdsStride;
+            const u32x4_t ulo = *reinterpret_cast<const u32x4_t*>(pu), uhi = *reinterpret_cast<const u32x4_t*>(pu + 16);
+            b1[j] = i32x8_t{(int)ulo[0], (int)ulo[1], (int)ulo[2], (int)ulo[3], (int)uhi[0], (int)uhi[1], (int)uhi[2], (int)uhi[3]};
+          }
+        }
+        const float s0 = sb0[kc], s1 = DUAL ? sb1[kc] : 0.f;
+#pragma unroll
+        for (int i = 0; i < kTileFM; ++i) {
+          float sa[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = arow0 + i * 16 + (lane >> 4) * 4 + q;
+            sa[q] = r < mrows ? p.A_scale[(size_t)(row0 + r) * KB + kc] : 0.f;
+          }
+#pragma unroll
+          for (int j = 0; j < kTileFN; ++j) {
+            const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+            const f32x4_t p0 = mfma_fp8_16x16x128(a[i], b0[j], z);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc0[i][j][q] += p0[q] * (sa[q] * s0);
+            if (DUAL) {
+              const f32x4_t p1 = mfma_fp8_16x16x128(a[i], b1[j], z);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) acc1[i][j][q] += p1[q] * (sa[q] * s1);
+            }
+          }
+        }
+      }
+    }
+    if (kc + 1 < nk) store(buf ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue.  Lane holds rows arow0 + 16 i + 4 (lane/16) + q, column
+  // n0 + bcol0 + 16 j + lane%16.
+  if constexpr (FP8 && DUAL) {
+    // Row maxima of |h| over the tile's 128 columns: 4 column blocks in the
+    // lane, 16 lanes, then the two column waves through LDS (reusing lds).
+    float* amax_s = reinterpret_cast<float*>(lds);   // [2][kTileBM]
+    float hv[kTileFM][kTileFN][4];
+#pragma unroll
+    for (int i = 0; i < kTileFM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = arow0 + i * 16 + (lane >> 4) * 4 + q;
+        float am = 0.f;
+#pragma unroll
+        for (int j = 0; j < kTileFN; ++j) {
+          hv[i][j][q] = r < mrows ? silu_mul(acc0[i][j][q], acc1[i][j][q]) : 0.f;
+          am = fmaxf(am, fabsf(hv[i][j][q]));
+        }
+        am = wave_max_xor(am, 16);
+        if (r16 == 0) amax_s[wn * kTileBM + r] = am;
+      }
+    __syncthreads();
+    const int N128 = N / 128;
+#pragma unroll
+    for (int i = 0; i < kTileFM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = arow0 + i * 16 + (lane >> 4) * 4 + q;
+        if (r < mrows) {
+          const float am = fmaxf(amax_s[r], amax_s[kTileBM + r]);
+          const float scale = am == 0.f ? 1.f : am / 448.f;
+#pragma unroll
+          for (int j = 0; j < kTileFN; ++j) {
+            const float qv = fminf(fmaxf(hv[i][j][q] / scale, -448.f), 448.f);
+            p.out[(size_t)(row0 + r) * N + n0 + bcol0 + j * 16 + r16] = (uint8_t)f32_to_e4m3(qv);
+          }
+          if (wn == 0 && r16 == 0) p.out_scale[(size_t)(row0 + r) * N128 + nblk] = scale;
+        }
+      }
+  } else {
+    uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
+#pragma unroll
+    for (int i = 0; i < kTileFM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = arow0 + i * 16 + (lane >> 4) * 4 + q;
+        if (r < mrows) {
+#pragma unroll
+          for (int j = 0; j < kTileFN; ++j) {
+            const float v = DUAL ? silu_mul(acc0[i][j][q], acc1[i][j][q]) : acc0[i][j][q];
+            out[(size_t)(row0 + r) * N + n0 + bcol0 + j * 16 + r16] = (uint16_t)f32_to_bf16_bits(v);
+          }
+        }
+      }
+  }
+}
+
+// ------------------------------------------------------------------- host ----
+namespace {
+size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+struct WsLayout {
+  size_t h, h_scale, n_skinny, n_tiles, skinny, tiles, total;
+  int max_tiles;
+};
+
+WsLayout ffn_layout(int T, int H, int E, int k, int I, int n_shared, bool fp8) {
+  (void)H;
+  WsLayout L{};
+  const long long R = (long long)T * (k + n_shared);
+  const int G = E + n_shared;
+  const long long big_groups = std::min<long long>(G, R / (kSkinnyMax + 1));
+  L.max_tiles = (int)(R / kTileBM + big_groups + 1);
+  size_t off = 0;
+  L.h = off;        off += align256((size_t)R * I * (fp8 ? 1 : 2));
+  L.h_scale = off;  off += fp8 ? align256((size_t)R * (I / 128) * 4) : 0;
+  L.n_skinny = off; off += 256;
+  L.n_tiles = off;  off += 256;
+  L.skinny = off;   off += align256((size_t)kSkinnyClasses * G * 4);
+  L.tiles = off;    off += align256((size_t)L.max_tiles * 8);
+  L.total = off;
+  return L;
+}
+}  // namespace
+
+size_t ffn_workspace_bytes(int T, int H, int E, int k, int I, int n_shared, bool fp8) {
+  return ffn_layout(T, H, E, k, I, n_shared, fp8).total;
+}
+
+template <typename Kern>
+static void launch_gemm(Kern kern, int threads, long long blocks, const GemmArgs& a, hipStream_t s) {
+  if (blocks > 0) hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(threads), 0, s, a);
+}
+
+hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
+  const WsLayout L = ffn_layout(f.T, f.H, f.E, f.k, f.I, f.n_shared, f.fp8);
+  uint8_t* ws = static_cast<uint8_t*>(f.workspace);
+  const int G = f.E + f.n_shared;
+  Sched sc{reinterpret_cast<int32_t*>(ws + L.n_skinny), reinterpret_cast<int32_t*>(ws + L.n_tiles),
+           reinterpret_cast<int32_t*>(ws + L.skinny), reinterpret_cast<int32_t*>(ws + L.tiles), G};
+  const long long R = (long long)f.T * (f.k + f.n_shared);
+  hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, f.offsets, sc);
+
+  uint8_t* h = ws + L.h;
+  float* h_scale = f.fp8 ? reinterpret_cast<float*>(ws + L.h_scale) : nullptr;
+  // Upper bound on the groups of each skinny class (a class-c group has more
+  // than 16 << (c-1) rows).
+  long long max_cls[kSkinnyClasses];
+  for (int c = 0; c < kSkinnyClasses; ++c)
+    max_cls[c] = std::min<long long>(G, c == 0 ? R : R / (skinny_class_rows(c - 1) + 1));
+
+  GemmArgs up{};
+  up.sc = sc;
+  up.offsets = f.offsets;
+  up.A = static_cast<const uint8_t*>(f.x_perm);
+  up.A_scale = f.x_perm_scale;
+  up.B0 = static_cast<const uint8_t*>(f.w_gate);
+  up.B1 = static_cast<const uint8_t*>(f.w_up);
+  up.s_B0 = f.s_gate;
+  up.s_B1 = f.s_up;
+  up.out = h;
+  up.out_scale = h_scale;
+  up.K = f.H;
+  up.N = f.I;
+
+  GemmArgs dn = up;
+  dn.A = h;
+  dn.A_scale = h_scale;
+  dn.B0 = static_cast<const uint8_t*>(f.w_down);
+  dn.B1 = nullptr;
+  dn.s_B0 = f.s_down;
+  dn.s_B1 = nullptr;
+  dn.out = static_cast<uint8_t*>(f.y_perm);
+  dn.out_scale = nullptr;
+  dn.K = f.I;
+  dn.N = f.H;
+
+  // gate/up + SwiGLU
+  if (f.fp8) {
+    up.n_ntile = f.I / (16 * 8);
+    launch_gemm(k_skinny_fp8<true, 8, 1>, 512, max_cls[0] * up.n_ntile, up, s);
+    launch_gemm(k_skinny_fp8<true, 8, 2>, 512, max_cls[1] * up.n_ntile, up, s);
+    launch_gemm(k_skinny_fp8<true, 8, 4>, 512, max_cls[2] * up.n_ntile, up, s);
+  } else {
+    up.n_ntile = f.I / (16 * 4);
+    launch_gemm(k_skinny_bf16<true, 4, 1>, 256, max_cls[0] * up.n_ntile, up, s);
+    launch_gemm(k_skinny_bf16<true, 4, 2>, 256, max_cls[1] * up.n_ntile, up, s);
+    launch_gemm(k_skinny_bf16<true, 4, 4>, 256, max_cls[2] * up.n_ntile, up, s);
+  }
+  up.n_ntile = f.I / kTileBN;
+  if (f.fp8) launch_gemm(k_tiled<true, true>, 512, (long long)L.max_tiles * up.n_ntile, up, s);
+  else launch_gemm(k_tiled<false, true>, 512, (long long)L.max_tiles * up.n_ntile, up, s);
+
+  // down
+  dn.n_ntile = f.H / (16 * 4);
+  if (f.fp8) {
+    launch_gemm(k_skinny_fp8<false, 4, 1>, 256, max_cls[0] * dn.n_ntile, dn, s);
+    launch_gemm(k_skinny_fp8<false, 4, 2>, 256, max_cls[1] * dn.n_ntile, dn, s);
+    launch_gemm(k_skinny_fp8<false, 4, 4>, 256, max_cls[2] * dn.n_ntile, dn, s);
+  } else {
+    launch_gemm(k_skinny_bf16<false, 4, 1>, 256, max_cls[0] * dn.n_ntile, dn, s);
+    launch_gemm(k_skinny_bf16<false, 4, 2>, 256, max_cls[1] * dn.n_ntile, dn, s);
+    launch_gemm(k_skinny_bf16<false, 4, 4>, 256, max_cls[2] * dn.n_ntile, dn, s);
+  }
+  dn.n_ntile = f.H / kTileBN;
+  if (f.fp8) launch_gemm(k_tiled<true, false>, 512, (long long)L.max_tiles * dn.n_ntile, dn, s);
+  else launch_gemm(k_tiled<false, false>, 512, (long long)L.max_tiles * dn.n_ntile, dn, s);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,46 @@
+// Host-side launchers of the MoE kernels (one per kernel family).  Each one
+// enqueues on the given stream and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// route.hip
+hipError_t launch_router_gemm(const uint16_t* x, const float* w, const float* bias, float* logits,
+                              int T, int H, int E, hipStream_t s);
+hipError_t launch_topk(const float* logits, int32_t* idx, float* w, int T, int E, int k,
+                       hipStream_t s);
+
+// permute.hip
+hipError_t launch_permute(const int32_t* topk_idx, const uint16_t* x, int32_t* counts,
+                          int32_t* offsets, int32_t* dest, int32_t* src_row, void* x_perm,
+                          float* x_perm_scale, int T, int H, int E, int k, int n_shared, bool fp8,
+                          hipStream_t s);
+
+// combine.hip
+hipError_t launch_combine(const uint16_t* y_perm, const int32_t* dest, const float* topk_w,
+                          uint16_t* out, int T, int H, int k, int n_shared, hipStream_t s);
+
+// ffn.hip: the on-device schedule and the grouped GEMMs.
+struct FfnArgs {
+  int T, H, E, k, I, n_shared;
+  bool fp8;
+  const int32_t* offsets;
+  const void* x_perm;
+  const float* x_perm_scale;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  const float* s_gate;
+  const float* s_up;
+  const float* s_down;
+  void* y_perm;
+  void* workspace;
+};
+size_t ffn_workspace_bytes(int T, int H, int E, int k, int I, int n_shared, bool fp8);
+hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s);
+
+}  // namespace moe

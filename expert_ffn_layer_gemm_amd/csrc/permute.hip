@@ -1,0 +1,162 @@
+// Dispatch: counting sort of (token, slot) pairs by expert and the row copy
+// into unpadded expert-contiguous groups ("CuTeDSL at Perplexity", MoE
+// Dispatch/Combine, local kernel: count per expert, a unique index per token
+// inside its expert's list, then a copy launched on many more blocks to use
+// the memory bandwidth).  The Ironwood page (section 4.2.1) makes the same
+// point for its ragged gather: no padded per-expert tensor is built in HBM.
+//
+// Differences from the page's kernel, for gfx950 and for determinism:
+//   - the unique index is the token-ascending rank, computed from LDS bit masks
+//     (one bit per token of a 256-token tile per expert) with popcounts, instead
+//     of atomically incremented counters, so dest / src_row / x_perm are
+//     identical from run to run;
+//   - three launches: one workgroup builds counts + offsets (LDS histogram and
+//     a wave-level prefix scan), a tile grid assigns ranks, and a wide grid
+//     gathers rows (x_perm[r] = x[src_row[r]], 16-byte lanes), quantising each
+//     128-channel group to e4m3fn on the way for fp8 layers.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+
+// Counts per group and their exclusive prefix sum; one workgroup of 1024.
+__global__ __launch_bounds__(1024) void k_hist_scan(const int32_t* __restrict__ idx,
+                                                    int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ offsets, int T, int E,
+                                                    int k, int n_shared) {
+  __shared__ int cnt[2048];
+  __shared__ int wave_sum[16];
+  const int tid = threadIdx.x, G = E + n_shared;
+  for (int i = tid; i < 2048; i += 1024) cnt[i] = 0;
+  __syncthreads();
+  const long long n = (long long)T * k;
+  for (long long i = tid; i < n; i += 1024) atomicAdd(&cnt[idx[i]], 1);
+  __syncthreads();
+  if (tid == 0 && n_shared) cnt[E] = T;
+  __syncthreads();
+  // Each thread owns entries 2*tid and 2*tid + 1.
+  const int a = cnt[2 * tid], b = cnt[2 * tid + 1];
+  int s = a + b, incl = s;
+  const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wave_sum[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += wave_sum[w];
+  const int excl = before + incl - s;
+  if (2 * tid < G) { offsets[2 * tid] = excl; counts[2 * tid] = a; }
+  if (2 * tid + 1 < G) { offsets[2 * tid + 1] = excl + a; counts[2 * tid + 1] = b; }
+  if (2 * tid == G) offsets[G] = excl;
+  if (2 * tid + 1 == G) offsets[G] = excl + a;
+}
+
+// Token-ascending rank of every (t, j) inside its expert's group.
+constexpr int kRankTile = 256;
+__global__ __launch_bounds__(kRankTile) void k_rank(const int32_t* __restrict__ idx,
+                                                    const int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ dest,
+                                                    int32_t* __restrict__ src_row, int T, int E,
+                                                    int k, int n_shared) {
+  __shared__ int base[1024];
+  __shared__ uint32_t mask[1024 * (kRankTile / 32)];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * kRankTile;
+  for (int i = tid; i < E; i += kRankTile) base[i] = 0;
+  for (int i = tid; i < E * (kRankTile / 32); i += kRankTile) mask[i] = 0u;
+  __syncthreads();
+  // Routings of every token before this tile.
+  const long long before = (long long)t0 * k;
+  for (long long i = tid; i < before; i += kRankTile) atomicAdd(&base[idx[i]], 1);
+  const int t = t0 + tid;
+  const bool valid = t < T;
+  const int word = tid >> 5;
+  const uint32_t bit = 1u << (tid & 31);
+  if (valid)
+    for (int j = 0; j < k; ++j) atomicOr(&mask[idx[(size_t)t * k + j] * (kRankTile / 32) + word], bit);
+  __syncthreads();
+  if (!valid) return;
+  for (int j = 0; j < k; ++j) {
+    const int e = idx[(size_t)t * k + j];
+    const uint32_t* m = mask + e * (kRankTile / 32);
+    int rank = __popc(m[word] & (bit - 1u));
+    for (int w = 0; w < word; ++w) rank += __popc(m[w]);
+    const int d = offsets[e] + base[e] + rank;
+    dest[(size_t)t * k + j] = d;
+    src_row[d] = t;
+  }
+  if (n_shared) src_row[offsets[E] + t] = t;
+}
+
+// x_perm[r] = x[src_row[r]] (bf16), 16 bytes per lane.
+constexpr int kGatherRows = 4;
+__global__ __launch_bounds__(256) void k_gather_bf16(const int32_t* __restrict__ src_row,
+                                                     const uint16_t* __restrict__ x,
+                                                     uint16_t* __restrict__ x_perm, int R, int H) {
+  const int chunks = H / 8;
+  for (int rr = 0; rr < kGatherRows; ++rr) {
+    const int r = blockIdx.x * kGatherRows + rr;
+    if (r >= R) return;
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + (size_t)src_row[r] * H);
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(x_perm + (size_t)r * H);
+    for (int c = threadIdx.x; c < chunks; c += 256) dst[c] = src[c];
+  }
+}
+
+// x_perm[r] = e4m3 codes of x[src_row[r]] per 128-channel group, scale = amax/448.
+// 16 lanes cover one group (8 bf16 each); the group max is a 16-lane xor reduction.
+__global__ __launch_bounds__(256) void k_gather_fp8(const int32_t* __restrict__ src_row,
+                                                    const uint16_t* __restrict__ x,
+                                                    uint8_t* __restrict__ x_perm,
+                                                    float* __restrict__ x_scale, int R, int H) {
+  const int chunks = H / 8;
+  for (int rr = 0; rr < kGatherRows; ++rr) {
+    const int r = blockIdx.x * kGatherRows + rr;
+    if (r >= R) return;
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + (size_t)src_row[r] * H);
+    for (int c = threadIdx.x; c < chunks; c += 256) {
+      float v[8];
+      unpack_bf16x8(src[c], v);
+      float amax = 0.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(v[q]));
+      amax = wave_max_xor(amax, 16);
+      const float scale = amax == 0.f ? 1.f : amax / 448.f;
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float qv = fminf(fmaxf(v[q] / scale, -448.f), 448.f);
+        const uint32_t code = f32_to_e4m3(qv);
+        if (q < 4) lo |= code << (8 * q); else hi |= code << (8 * (q - 4));
+      }
+      *reinterpret_cast<uint2*>(x_perm + (size_t)r * H + c * 8) = make_uint2(lo, hi);
+      if ((c & 15) == 0) x_scale[(size_t)r * (H / 128) + c / 16] = scale;
+    }
+  }
+}
+
+hipError_t launch_permute(const int32_t* topk_idx, const uint16_t* x, int32_t* counts,
+                          int32_t* offsets, int32_t* dest, int32_t* src_row, void* x_perm,
+                          float* x_perm_scale, int T, int H, int E, int k, int n_shared, bool fp8,
+                          hipStream_t s) {
+  hipLaunchKernelGGL(k_hist_scan, dim3(1), dim3(1024), 0, s, topk_idx, counts, offsets, T, E, k,
+                     n_shared);
+  if (T == 0) return hipGetLastError();
+  hipLaunchKernelGGL(k_rank, dim3(ceil_div(T, kRankTile)), dim3(kRankTile), 0, s, topk_idx, offsets,
+                     dest, src_row, T, E, k, n_shared);
+  const int R = T * (k + n_shared);
+  const dim3 grid(ceil_div(R, kGatherRows));
+  if (fp8)
+    hipLaunchKernelGGL(k_gather_fp8, grid, dim3(256), 0, s, src_row, x,
+                       static_cast<uint8_t*>(x_perm), x_perm_scale, R, H);
+  else
+    hipLaunchKernelGGL(k_gather_bf16, grid, dim3(256), 0, s, src_row, x,
+                       static_cast<uint16_t*>(x_perm), R, H);
+  return hipGetLastError();
+}
+
+}  // namespace moe

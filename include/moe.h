@@ -1,0 +1,192 @@
+/*
+ * moe.h - C ABI of libmoe.so, one GPU's share of a mixture-of-experts (MoE)
+ * layer of LLM inference on AMD Instinct MI355X (gfx950).
+ *
+ * The layer (router top-k -> dispatch into expert-contiguous groups ->
+ * grouped expert GEMM with SwiGLU -> weighted combine) as the source pages
+ * state it:
+ *   - router: "Lower latency and higher throughput with multi-node DeepSeek
+ *     deployment", section MoE Router (sort with index tracking, top-k indices
+ *     and scores per token);
+ *   - dispatch / combine: "CuTeDSL at Perplexity", section MoE Dispatch/Combine,
+ *     local (single-GPU) kernel: per-expert counts, a unique index per token in
+ *     its expert's list, a copy into per-expert buffers, then a weighted
+ *     accumulation in registers using the dispatch offsets;
+ *   - expert FFN: Qwen3.5-397B on Ironwood TPU v7x (xxmr.cn), section 4.2.2,
+ *     grouped matmul with SwiGLU fused into the loop (gate and up streams);
+ *   - FP8: DeepSeek-deployment page, section Quantization: weights with one
+ *     scale per 128x128 block, activations quantised on the fly per
+ *     128-element vector;
+ *   - group sizes read on the device, never synchronised back to the host:
+ *     DeepSeek-deployment page, Quantization (routing-aware persistent
+ *     kernels) and CUDA Graph sections.
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer argument is a DEVICE pointer unless stated otherwise; the
+ *     caller owns every buffer.  The library never allocates, frees or
+ *     synchronises; each call only enqueues kernels on `stream` (a
+ *     hipStream_t; NULL = the default stream) and returns.
+ *   - Row-major layouts; "[A, B]" means B is the contiguous dimension.
+ *   - bf16 = IEEE bfloat16 bit patterns (uint16); fp8 = OCP e4m3fn codes
+ *     (uint8, bias 7, max 448).  Device pointers must be 16-byte aligned.
+ *   - Return value: MOE_OK or a negative moe_status.  Argument errors are
+ *     detected on the host before anything is launched (nothing is written).
+ *     A launch failure returns MOE_ERR_HIP.  moe_last_error() then returns a
+ *     thread-local message.  No exception crosses the ABI.
+ *   - Supported shapes: 0 <= T, T*(k+n_shared) < 2^31, 1 <= k <= min(E, 16),
+ *     1 <= E <= 1024, n_shared in {0, 1}, H and I positive multiples of 128.
+ *     T == 0 is a valid no-op.  Other shapes return MOE_ERR_UNSUPPORTED.
+ *   - The library keeps no state between calls; calls on different streams
+ *     with disjoint buffers may run concurrently.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* NULL pointer, bad enum, misaligned pointer */
+  MOE_ERR_UNSUPPORTED = -2, /* shape outside the supported set */
+  MOE_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than required */
+  MOE_ERR_HIP = -4          /* a HIP launch failed; see moe_last_error() */
+} moe_status;
+
+typedef enum {
+  MOE_BF16 = 0,              /* bf16 activations and expert weights */
+  MOE_FP8_E4M3_BLOCK128 = 1  /* e4m3fn expert weights + fp32 scale per 128x128
+                                block; x and h quantised per row per 128 channels */
+} moe_wdtype;
+
+/* Shape of one layer call.  G = E + n_shared expert groups; R = T*(k + n_shared)
+   rows in the permuted (expert-contiguous) matrices. */
+typedef struct {
+  int32_t T;        /* tokens */
+  int32_t H;        /* hidden size */
+  int32_t E;        /* routed experts */
+  int32_t k;        /* experts chosen per token */
+  int32_t I;        /* SwiGLU intermediate size */
+  int32_t n_shared; /* always-on shared experts, 0 or 1 (group E) */
+  int32_t wdtype;   /* moe_wdtype */
+} moe_shape;
+
+/* Thread-local description of the last non-OK return on this thread. */
+const char* moe_last_error(void);
+
+/* Library ABI version (increments on any signature change). */
+int moe_abi_version(void);
+
+/* Bytes of device workspace moe_forward needs for `shape` (256-byte aligned
+   sub-buffers).  Returns 0 for an unsupported shape. */
+size_t moe_forward_workspace_bytes(const moe_shape* shape);
+
+/* Bytes of device workspace moe_grouped_ffn needs (h, its fp8 scales and the
+   on-device tile schedule).  Returns 0 for an unsupported shape. */
+size_t moe_ffn_workspace_bytes(const moe_shape* shape);
+
+/*
+ * Router: logits = x W_r^T (+ router_bias), then top-k and renormalised
+ * softmax weights (DeepSeek-deployment page, MoE Router).
+ *   x           [T, H] bf16
+ *   w_router    [E, H] fp32 (torch Linear layout)
+ *   router_bias [E] fp32 or NULL (added to every token's logits)
+ *   logits      [T, E] fp32, written (required: the top-k reads it back)
+ *   topk_idx    [T, k] int32, written: slot j holds the j-th largest logit;
+ *               equal logits (+0 == -0) go to the lower expert index
+ *   topk_w      [T, k] fp32, written: exp(l_j - l_0) / sum_j' exp(l_j' - l_0)
+ * Logits must be finite (a NaN logit gives unspecified routing).
+ */
+int moe_route(const moe_shape* shape, const void* x, const float* w_router,
+              const float* router_bias, float* logits, int32_t* topk_idx,
+              float* topk_w, void* stream);
+
+/* Top-k + weights alone, from caller-given fp32 logits [T, E] (same rules as
+   moe_route).  Only T, E and k of `shape` are read. */
+int moe_route_from_logits(const moe_shape* shape, const float* logits,
+                          int32_t* topk_idx, float* topk_w, void* stream);
+
+/*
+ * Dispatch ("CuTeDSL at Perplexity", MoE Dispatch/Combine, local kernel):
+ * counting sort of the (token, slot) pairs by expert into unpadded,
+ * expert-contiguous groups, token-ascending within a group, and the row copy.
+ *   topk_idx     [T, k] int32 in [0, E) (distinct per token)
+ *   x            [T, H] bf16
+ *   counts       [G] int32, written: rows per group (group E = shared, = T)
+ *   offsets      [G + 1] int32, written: exclusive prefix sum of counts
+ *   dest         [T, k] int32, written: row of (t, j) in the permuted matrix
+ *   src_row      [R] int32, written: token of each permuted row
+ *                (shared group: rows T*k + t hold token t)
+ *   x_perm       [R, H], written: bf16 copy of x[src_row[r]], or for
+ *                MOE_FP8_E4M3_BLOCK128 the e4m3fn codes of that row quantised
+ *                per 128 channels (scale = amax / 448, 1 for an all-zero group,
+ *                codes rounded to nearest even after clamping to +-448)
+ *   x_perm_scale [R, H/128] fp32, written for fp8 (NULL for bf16)
+ * Routing entries outside [0, E) make the results unspecified.
+ */
+int moe_permute(const moe_shape* shape, const int32_t* topk_idx, const void* x,
+                int32_t* counts, int32_t* offsets, int32_t* dest,
+                int32_t* src_row, void* x_perm, float* x_perm_scale,
+                void* stream);
+
+/*
+ * Grouped expert FFN over the permuted rows (Qwen3.5-397B on Ironwood, section
+ * 4.2.2): for every group g with rows [offsets[g], offsets[g+1]):
+ *   h = silu(X W_gate[g]^T) * (X W_up[g]^T)   (fp32 accumulation)
+ *   y_perm rows = h W_down[g]^T                (fp32 accumulation, bf16 out)
+ * bf16 layers keep h in bf16.  fp8 layers quantise h per row per 128
+ * channels like x_perm before the down projection.
+ *   offsets      [G + 1] int32 (device; read only on the device)
+ *   x_perm       [R, H] bf16 or e4m3fn codes; x_perm_scale [R, H/128] (fp8)
+ *   w_gate, w_up [G, I, H] bf16 or e4m3fn codes
+ *   w_down       [G, H, I] bf16 or e4m3fn codes
+ *   s_gate, s_up [G, I/128, H/128] fp32 block scales (fp8; NULL for bf16)
+ *   s_down       [G, H/128, I/128] fp32 block scales (fp8; NULL for bf16)
+ *   y_perm       [R, H] bf16, written (rows of empty groups untouched)
+ *   workspace    >= moe_ffn_workspace_bytes(shape) bytes of device memory
+ * Groups whose offsets are not non-decreasing within [0, R] give unspecified
+ * results.
+ */
+int moe_grouped_ffn(const moe_shape* shape, const int32_t* offsets,
+                    const void* x_perm, const float* x_perm_scale,
+                    const void* w_gate, const void* w_up, const void* w_down,
+                    const float* s_gate, const float* s_up, const float* s_down,
+                    void* y_perm, void* workspace, size_t ws_bytes,
+                    void* stream);
+
+/*
+ * Combine ("CuTeDSL at Perplexity", local combine; shared expert added as in
+ * the DeepSeek-deployment page, Expert parallelism section):
+ *   out[t] = bf16( sum_{j = 0..k-1} topk_w[t, j] * y_perm[dest[t, j]]
+ *                  + y_perm[T*k + t] if n_shared )
+ * summed in fp32 in that fixed order, one rounded product and one rounded add
+ * per term (no fused multiply-add), one round-to-nearest-even at the end.
+ * Deterministic, no atomics.
+ *   y_perm [R, H] bf16; dest [T, k] int32; topk_w [T, k] fp32; out [T, H] bf16
+ */
+int moe_combine(const moe_shape* shape, const void* y_perm, const int32_t* dest,
+                const float* topk_w, void* out, void* stream);
+
+/*
+ * The whole layer in one call: moe_route -> moe_permute -> moe_grouped_ffn ->
+ * moe_combine on `stream`, intermediates in `workspace`
+ * (>= moe_forward_workspace_bytes(shape)).  Arguments as above;
+ * topk_idx_out / topk_w_out may be NULL (then the routing lives in the
+ * workspace only).  out [T, H] bf16.
+ */
+int moe_forward(const moe_shape* shape, const void* x, const float* w_router,
+                const float* router_bias, const void* w_gate, const void* w_up,
+                const void* w_down, const float* s_gate, const float* s_up,
+                const float* s_down, void* out, int32_t* topk_idx_out,
+                float* topk_w_out, void* workspace, size_t ws_bytes,
+                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

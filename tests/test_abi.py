@@ -1,0 +1,109 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol,
+and rejects bad arguments on the host before any launch (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import expert_ffn_layer_gemm_amd as moe
+from expert_ffn_layer_gemm_amd._binding import SIGNATURES
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declarations_match_binding():
+    assert _declared_functions() == sorted(SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = moe.lib()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_shape_struct_matches_header():
+    fields = re.search(r"typedef struct \{(.*?)\} moe_shape;", open(HEADER).read(), re.S).group(1)
+    names = re.findall(r"int32_t (\w+);", fields)
+    assert names == [f for f, _ in moe.MoeShape._fields_]
+    assert ctypes.sizeof(moe.MoeShape) == 4 * len(names)
+
+
+def test_abi_version():
+    assert moe.moe_abi_version() == 1
+
+
+FAKE = 0x10000  # a non-NULL, aligned address; never dereferenced (validation fails first)
+
+
+def _call(fn, *args):
+    return getattr(moe.lib(), fn)(*args)
+
+
+def test_workspace_sizes_and_bad_shapes():
+    good = moe.make_shape(64, 4096, 128, 8, 1536)
+    assert moe.moe_forward_workspace_bytes(good) > moe.moe_ffn_workspace_bytes(good) > 64 * 8 * 1536 * 2
+    fp8 = moe.make_shape(4096, 7168, 256, 8, 2048, 1, "fp8")
+    assert moe.moe_ffn_workspace_bytes(fp8) >= 4096 * 9 * 2048
+    for bad in (moe.make_shape(64, 100, 128, 8, 1536), moe.make_shape(64, 4096, 128, 8, 100),
+                moe.make_shape(64, 4096, 4, 8, 1536), moe.make_shape(64, 4096, 2048, 8, 1536),
+                moe.make_shape(64, 4096, 128, 17, 1536), moe.make_shape(64, 4096, 128, 8, 1536, 2),
+                moe.make_shape(-1, 4096, 128, 8, 1536), moe.MoeShape(64, 4096, 128, 8, 1536, 0, 7)):
+        assert moe.moe_forward_workspace_bytes(bad) == 0
+        assert moe.moe_ffn_workspace_bytes(bad) == 0
+
+
+def test_error_codes_before_launch():
+    sh = moe.make_shape(64, 256, 8, 2, 512)
+    P = ctypes.byref
+    # NULL shape
+    assert _call("moe_route", None, FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    # NULL / misaligned pointers
+    assert _call("moe_route", P(sh), None, FAKE, None, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert "x is NULL" in moe.moe_last_error()
+    assert _call("moe_route", P(sh), FAKE + 2, FAKE, None, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert "aligned" in moe.moe_last_error()
+    # unsupported shapes
+    bad = moe.make_shape(64, 256, 8, 9, 512)
+    assert _call("moe_route", P(bad), FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert _call("moe_route_from_logits", P(bad), FAKE, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    bad_dt = moe.MoeShape(64, 256, 8, 2, 512, 0, 3)
+    assert _call("moe_combine", P(bad_dt), FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    # workspace too small / missing
+    need = moe.moe_forward_workspace_bytes(sh)
+    args = [P(sh), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None, None, FAKE, None, None]
+    assert _call("moe_forward", *args, FAKE, need - 1, None) == moe.MOE_ERR_WORKSPACE
+    assert _call("moe_forward", *args, None, need, None) == moe.MOE_ERR_WORKSPACE
+    assert _call("moe_forward", *args, FAKE + 16, need, None) == moe.MOE_ERR_INVALID_ARG
+    ffn_need = moe.moe_ffn_workspace_bytes(sh)
+    assert _call("moe_grouped_ffn", P(sh), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None, None,
+                 FAKE, FAKE, ffn_need - 256, None) == moe.MOE_ERR_WORKSPACE
+    # fp8 needs every scale pointer
+    s8 = moe.make_shape(64, 256, 8, 2, 512, 0, "fp8")
+    assert _call("moe_grouped_ffn", P(s8), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                 FAKE, FAKE, 1 << 30, None) == moe.MOE_ERR_INVALID_ARG
+    assert "x_perm_scale" in moe.moe_last_error()
+    assert _call("moe_permute", P(s8), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_zero_tokens_is_a_no_op():
+    sh = moe.make_shape(0, 256, 8, 2, 512)
+    P = ctypes.byref
+    assert _call("moe_route", P(sh), None, None, None, None, None, None, None) == moe.MOE_OK
+    assert _call("moe_combine", P(sh), None, None, None, None, None) == moe.MOE_OK
+    assert _call("moe_forward", P(sh), *([None] * 12), None, 0, None) == moe.MOE_OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import expert_ffn_layer_gemm_amd._binding as b
+    monkeypatch.setattr(b, "_lib", None)
+    monkeypatch.setattr(b, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        b.lib()

@@ -1,0 +1,276 @@
+"""GPU parity of every C-ABI entry point against the CPU oracle (MI355X).
+
+Bars: routing (top-k indices, counts, offsets, dest, src_row, permuted rows and
+fp8 codes/scales) bit-exact given the same fp32 logits; weights within 1e-6 of
+a float64 evaluation; combine bit-exact given the same y_perm; layer output
+within a per-token infinity-norm relative error of 2e-2 (bf16) / 5e-2 (fp8).
+"""
+import numpy as np
+import pytest
+import torch
+
+import expert_ffn_layer_gemm_amd as moe
+import oracle
+from synth import CONFIGS, MoeConfig, generate_layer, to_numpy_inputs
+from tests.gpu_helpers import (DEV, bf16_bits_np, bf16_np, layer, rel_inf, run_ffn, run_forward,
+                               run_permute, run_route, to_bf16_rne)
+
+pytestmark = pytest.mark.gpu
+TOL = {"bf16": 2e-2, "fp8": 5e-2}
+
+
+def _route_inputs(li):
+    return dict(x_bf16=bf16_bits_np(li.x), w_router=li.w_router.cpu().numpy(),
+                router_bias=None if li.router_bias is None else li.router_bias.cpu().numpy())
+
+
+# ------------------------------------------------------------------ top-k ----
+def _crafted_logits(rng, T, E):
+    one = np.float32(1.0)
+    up = np.nextafter(one, np.float32(2))
+    kinds = [
+        lambda: rng.standard_normal(E).astype(np.float32),
+        lambda: np.array([-1.0, -0.0, 0.0, 0.5, 1.0], np.float32)[rng.integers(0, 5, E)],
+        lambda: np.where(rng.random(E) < 0.5, one, up).astype(np.float32),
+        lambda: np.zeros(E, np.float32) * np.where(rng.random(E) < 0.5, -1, 1).astype(np.float32),
+        lambda: (rng.standard_normal(E) * 1e4).astype(np.float32),
+    ]
+    return np.stack([kinds[t % len(kinds)]() for t in range(T)])
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (37, 5), (128, 8), (512, 10), (1024, 16), (16, 16), (1, 1)])
+def test_topk_from_logits_bitexact(E, k):
+    rng = np.random.default_rng(E * 31 + k)
+    T = 203
+    lg = _crafted_logits(rng, T, E)
+    idx_ref, w_ref = oracle.topk_softmax(lg, k)
+    sh = moe.make_shape(T, 128, E, k, 128)
+    logits = torch.from_numpy(lg).to(DEV)
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    moe.moe_route_from_logits(sh, logits, idx, w)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    sel = np.take_along_axis(lg.astype(np.float64), idx_ref.astype(np.int64), 1)
+    p = np.exp(sel - sel[:, :1])
+    p /= p.sum(1, keepdims=True)
+    assert np.abs(w.cpu().numpy() - p).max() <= 1e-6
+    assert np.abs(w.cpu().numpy() - w_ref).max() <= 1e-6
+
+
+# ----------------------------------------------------------------- router ----
+@pytest.mark.parametrize("ci", range(len(CONFIGS)))
+def test_route_configs(ci):
+    cfg = CONFIGS[ci]
+    li = layer(cfg)
+    logits, idx, w = run_route(cfg, li)
+    inp = _route_inputs(li)
+    x = oracle.bf16_bits_to_f32(inp["x_bf16"])
+    ref = oracle.router_logits(x, inp["w_router"], inp["router_bias"])
+    lg = logits.cpu().numpy()
+    # fp32 dot-product error bound (Higham): |err| <= H u sum|x_h w_h|, u = 2^-24
+    mag = np.abs(x) @ np.abs(inp["w_router"]).T
+    if inp["router_bias"] is not None:
+        mag = mag + np.abs(inp["router_bias"])[None, :]
+    bound = (cfg.H + 2) * 2.0 ** -24 * mag
+    assert np.all(np.abs(lg - ref) <= bound)
+    delta = float(np.abs(lg - ref).max())
+    print(f"{cfg.name}: max |logit_gpu - logit_oracle| = {delta:.3e}")
+    # routing bit-exact on the GPU's own logits
+    idx_ref, w_ref = oracle.topk_softmax(lg, cfg.k)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    assert np.abs(w.cpu().numpy() - w_ref).max() <= 1e-6
+
+
+def test_route_zero_router_weight_ties():
+    cfg = MoeConfig("zero_router", 5, T=70, H=512, E=24, k=6, I=128)
+    li = generate_layer(cfg, DEV)
+    li.w_router.zero_()
+    logits, idx, w = run_route(cfg, li)
+    assert np.all(idx.cpu().numpy() == np.arange(6)[None, :])
+    assert np.all(w.cpu().numpy() == np.float32(1.0) / np.float32(6.0))
+
+
+# ---------------------------------------------------------------- permute ----
+def _check_permute(cfg, li, idx):
+    counts, offsets, dest, src, x_perm, x_scale = run_permute(cfg, idx, li.x)
+    c_ref, o_ref, d_ref, s_ref = oracle.counting_sort(idx.cpu().numpy(), cfg.E, cfg.n_shared)
+    assert np.array_equal(counts.cpu().numpy(), c_ref)
+    assert np.array_equal(offsets.cpu().numpy(), o_ref)
+    assert np.array_equal(dest.cpu().numpy(), d_ref)
+    assert np.array_equal(src.cpu().numpy(), s_ref)
+    xb = bf16_bits_np(li.x)
+    if cfg.wdtype == "fp8":
+        codes, scales = oracle.quantize_groups_128(oracle.bf16_bits_to_f32(xb))
+        assert np.array_equal(x_perm.cpu().numpy(), codes[s_ref])
+        assert np.array_equal(x_scale.cpu().numpy(), scales[s_ref])
+    else:
+        assert np.array_equal(bf16_bits_np(x_perm), xb[s_ref])
+
+
+@pytest.mark.parametrize("ci", range(len(CONFIGS)))
+def test_permute_configs(ci):
+    cfg = CONFIGS[ci]
+    li = layer(cfg)
+    _, idx, _ = run_route(cfg, li)
+    _check_permute(cfg, li, idx)
+
+
+@pytest.mark.parametrize("T,E,k,ns,fp8", [(1, 1, 1, 0, False), (257, 7, 3, 1, True),
+                                          (600, 1024, 16, 0, False), (513, 5, 5, 1, False)])
+def test_permute_ragged_shapes(T, E, k, ns, fp8):
+    cfg = MoeConfig("perm", 9, T=T, H=256, E=E, k=k, I=128, n_shared=ns,
+                    wdtype="fp8" if fp8 else "bf16")
+    rng = np.random.default_rng(T + E)
+    p = 1.0 / np.arange(1, E + 1) ** 1.2
+    p /= p.sum()
+    idx = np.stack([rng.choice(E, k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    li = generate_layer(cfg, DEV)
+    _check_permute(cfg, li, torch.from_numpy(idx).to(DEV))
+
+
+# ------------------------------------------------------------- grouped FFN ----
+def _ffn_case(cfg, sizes, seed):
+    """Random x_perm with crafted group sizes; returns GPU y_perm and oracle y_perm (fp32)."""
+    li = generate_layer(cfg, DEV)
+    rng = np.random.default_rng(seed)
+    G = cfg.n_groups
+    assert len(sizes) == G
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    R = int(offsets[-1])
+    xr = rng.standard_normal((R, cfg.H)).astype(np.float32)
+    inp = to_numpy_inputs(li)
+    if cfg.wdtype == "fp8":
+        codes, scales = oracle.quantize_groups_128(xr)
+        x_perm = torch.from_numpy(codes).to(DEV)
+        x_scale = torch.from_numpy(scales).to(DEV)
+        xo = oracle.fp8_e4m3.dequantize_groups_128(codes, scales)
+    else:
+        xt = torch.from_numpy(xr).to(torch.bfloat16)
+        x_perm, x_scale = xt.to(DEV), None
+        xo = xt.float().numpy()
+    sh = moe.make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.n_shared, cfg.wdtype)
+    assert R <= cfg.R
+    ws = torch.empty(moe.moe_ffn_workspace_bytes(sh), dtype=torch.uint8, device=DEV)
+    y = torch.zeros((cfg.R, cfg.H), dtype=torch.bfloat16, device=DEV)
+    moe.moe_grouped_ffn(sh, torch.from_numpy(offsets).to(DEV), x_perm, x_scale, li.w_gate, li.w_up,
+                        li.w_down, li.s_gate, li.s_up, li.s_down, y, ws)
+    torch.cuda.synchronize()
+    ref = oracle.grouped_ffn(xo, offsets, inp)
+    return bf16_np(y)[:R], ref
+
+
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8"])
+def test_grouped_ffn_group_size_boundaries(wdtype):
+    # sizes straddle the skinny row classes (16/32/64) and the 128-row tiles
+    sizes = [0, 1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 0, 200, 257, 3]
+    E = len(sizes)
+    cfg = MoeConfig("ffn_" + wdtype, 21, T=sum(sizes), H=384, E=E, k=1, I=256, wdtype=wdtype)
+    y, ref = _ffn_case(cfg, sizes, 1)
+    err = rel_inf(y, ref)
+    print(f"grouped ffn {wdtype}: per-row rel err {err:.3e}")
+    assert err <= TOL[wdtype]
+
+
+def test_grouped_ffn_fp8_shared_group():
+    sizes = [5, 0, 70, 9, 40]        # group 4 = shared expert
+    cfg = MoeConfig("ffn_fp8_shared", 22, T=40, H=256, E=4, k=2, I=384, n_shared=1, wdtype="fp8")
+    y, ref = _ffn_case(cfg, sizes, 2)
+    assert rel_inf(y, ref) <= TOL["fp8"]
+
+
+# ----------------------------------------------------------------- combine ----
+@pytest.mark.parametrize("T,H,k,ns", [(64, 4096, 8, 0), (33, 256, 2, 1), (1, 128, 1, 0), (700, 7168, 8, 1)])
+def test_combine_bitexact(T, H, k, ns):
+    rng = np.random.default_rng(T * 7 + k)
+    R = T * (k + ns)
+    y = torch.randn((R, H), generator=torch.Generator().manual_seed(T), dtype=torch.float32).to(torch.bfloat16)
+    perm = rng.permutation(T * k).astype(np.int32)
+    dest = perm.reshape(T, k)
+    w = rng.random((T, k)).astype(np.float32)
+    w /= w.sum(1, keepdims=True)
+    sh = moe.make_shape(T, H, max(k, 2), k, 128, ns)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    moe.moe_combine(sh, y.to(DEV), torch.from_numpy(dest).to(DEV), torch.from_numpy(w).to(DEV), out)
+    torch.cuda.synchronize()
+    ref = oracle.combine(y.float().numpy(), dest, w, ns)
+    assert np.array_equal(bf16_np(out), to_bf16_rne(ref))
+
+
+# ------------------------------------------------------------- end to end ----
+def _forward_check(cfg, li, sample=None):
+    out, idx, w = run_forward(cfg, li)
+    logits, idx2, _ = run_route(cfg, li)
+    assert np.array_equal(idx.cpu().numpy(), idx2.cpu().numpy())
+    lg = logits.cpu().numpy()
+    inp = to_numpy_inputs(li)
+    gpu_out = bf16_np(out)
+    if sample is None:
+        ref = oracle.forward(inp, logits_override=lg)
+        assert np.array_equal(idx.cpu().numpy(), ref.topk_idx)
+        err = rel_inf(gpu_out, ref.out)
+    else:
+        ref = oracle.forward_tokens(inp, sample, logits_override=lg[sample])
+        assert np.array_equal(idx.cpu().numpy()[sample], ref.topk_idx)
+        err = rel_inf(gpu_out[sample], ref.out)
+    # routing of the oracle's own logits: report near-tie flips (not a failure)
+    own = oracle.topk_softmax(oracle.router_logits(oracle.bf16_bits_to_f32(inp["x_bf16"]),
+                                                   inp["w_router"], inp["router_bias"]), cfg.k)[0]
+    flips = int((own != idx.cpu().numpy()).any(axis=1).sum())
+    print(f"{cfg.name}: per-token rel err {err:.3e}, routing flips vs oracle logits: {flips}")
+    assert err <= TOL[cfg.wdtype]
+    assert flips <= max(2, cfg.T // 500)
+    return out
+
+
+@pytest.mark.parametrize("ci", [0, 1, 3])
+def test_forward_configs_full(ci):
+    cfg = CONFIGS[ci]
+    _forward_check(cfg, layer(cfg))
+
+
+@pytest.mark.parametrize("ci", [2, 4])
+def test_forward_configs_sampled(ci):
+    cfg = CONFIGS[ci]
+    rng = np.random.default_rng(ci)
+    sample = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 14, replace=False)]))
+    _forward_check(cfg, layer(cfg), sample)
+
+
+@pytest.mark.parametrize("ci", range(len(CONFIGS)))
+def test_forward_deterministic(ci):
+    cfg = CONFIGS[ci]
+    li = layer(cfg)
+    a, ia, wa = run_forward(cfg, li)
+    b, ib, wb = run_forward(cfg, li)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(ia, ib) and torch.equal(wa, wb)
+
+
+@pytest.mark.parametrize("case", ["T1", "T3_ragged", "E1k1", "kE", "one_hot_expert", "fp8_small"])
+def test_forward_edge_cases(case):
+    cfgs = {
+        "T1": MoeConfig("T1", 30, T=1, H=256, E=8, k=2, I=256),
+        "T3_ragged": MoeConfig("T3", 31, T=3, H=384, E=16, k=4, I=128, n_shared=1),
+        "E1k1": MoeConfig("E1", 32, T=40, H=256, E=1, k=1, I=256),
+        "kE": MoeConfig("kE", 33, T=50, H=256, E=6, k=6, I=256),
+        "one_hot_expert": MoeConfig("hot", 34, T=300, H=256, E=8, k=1, I=384),
+        "fp8_small": MoeConfig("f8", 35, T=77, H=512, E=12, k=3, I=256, n_shared=1, wdtype="fp8"),
+    }
+    cfg = cfgs[case]
+    li = generate_layer(cfg, DEV)
+    if case == "one_hot_expert":
+        li.router_bias = torch.zeros(cfg.E, dtype=torch.float32, device=DEV)
+        li.router_bias[3] = 100.0          # every token -> expert 3: 300 rows, ragged tiles
+    _forward_check(cfg, li)
+
+
+def test_forward_zero_tokens():
+    cfg = MoeConfig("T0", 36, T=0, H=256, E=8, k=2, I=256)
+    sh = moe.shape_of(cfg)
+    moe.moe_forward(sh, None, None, None, None, None, None, None, None, None, None, None, None, None, 0)
+    counts = torch.full((8,), -1, dtype=torch.int32, device=DEV)
+    offsets = torch.full((9,), -1, dtype=torch.int32, device=DEV)
+    moe.moe_permute(sh, None, None, counts, offsets, None, None, None, None)
+    torch.cuda.synchronize()
+    assert counts.cpu().tolist() == [0] * 8 and offsets.cpu().tolist() == [0] * 9
