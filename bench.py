@@ -1,0 +1,195 @@
+"""Throughput of the MoE layer (moe_forward through the C ABI) on one MI355X.
+
+One step = one moe_forward call over one batch of seeded synthetic input:
+router GEMM + top-k, dispatch (counting sort + row gather), grouped gate/up
+GEMM with SwiGLU, grouped down GEMM, weighted combine.  Inputs and weights are
+resident in HBM before the timed region.  Prints ONE JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
+
+The default workload is the Qwen3-235B-like decode step (T=64 tokens, hidden
+4096, 128 experts, top-8, intermediate 1536, bf16).  The roofline object is
+for the kernel with the largest share of the step, timed with HIP events
+recorded by the library around that kernel's launch on the caller's stream
+during the timed steps.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec on 1 MI355X + % of HBM / MFMA roofline"
+
+
+def source_hash() -> str:
+    """Hash of the kernel sources, to tell whether stored counter data is stale."""
+    csrc = os.path.join(ROOT, "expert_ffn_layer_gemm_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(f.encode())
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str, kernel: str):
+    """HBM traffic of `kernel` from the committed rocprofv3 counter summary, or None
+    when there is none for this workload or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("kernel") != kernel or d.get("source_hash") != source_hash():
+        return None
+    return d.get("traffic_bytes")
+
+
+def cpu_baseline(cfg, li, n_tokens):
+    """The oracle, as it stands, on the first n_tokens tokens of the same workload."""
+    import numpy as np
+    import oracle
+    from synth import to_numpy_inputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    inp = to_numpy_inputs(li)
+    n = min(n_tokens, cfg.T)
+    inp["x_bf16"] = np.ascontiguousarray(inp["x_bf16"][:n])
+    t0 = time.perf_counter()
+    oracle.forward(inp)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"oracle.forward on the first {n} of {cfg.T} tokens of {cfg.name} "
+                      f"(seed {cfg.seed}), {dt:.2f} s, fp32 NumPy, OpenBLAS threads={threads}, "
+                      f"os.cpu_count()={os.cpu_count()}"}
+
+
+CPU_TOKENS = {"tiny": 64, "qwen3_235b_decode": 64, "qwen3_235b_prefill": 256,
+              "qwen35_397b_zipf": 128, "deepseek_v3_fp8": 16}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="qwen3_235b_decode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=None)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy 3 times (HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU's share of the MoE layer on one MI355X; "
+              "runs on more than one GPU are not part of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import expert_ffn_layer_gemm_amd as moe
+    from expert_ffn_layer_gemm_amd import accounting as acc
+    from synth import config_by_name, generate_layer
+
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": 1 << 30, "launches": 3}))
+        return
+
+    cfg = config_by_name(args.config)
+    li = generate_layer(cfg, dev)
+    shape = moe.shape_of(cfg)
+    ws = torch.empty(moe.moe_forward_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
+    idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
+    w = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        moe.moe_forward(shape, li.x, li.w_router, li.router_bias, li.w_gate, li.w_up, li.w_down,
+                        li.s_gate, li.s_up, li.s_down, out, idx, w, ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # One untimed step with events around every launch: find the dominant kernel.
+    moe.moe_profile_start(1, 0, 64)
+    step()
+    launches = [moe.moe_profile_read(i) for i in range(moe.moe_profile_count())]
+    moe.moe_profile_stop()
+    dom = int(np.argmax([ms for ms, _ in launches]))
+    dom_name = launches[dom][1]
+
+    # Timed region: K steps; the library records one event pair around the
+    # dominant kernel's launch in each step.
+    moe.moe_profile_start(2, dom, args.steps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    total_ms = e0.elapsed_time(e1)
+    kern_ms = [moe.moe_profile_read(i)[0] for i in range(moe.moe_profile_count())]
+    moe.moe_profile_stop()
+    ms_per_step = total_ms / args.steps
+    value = cfg.T * args.steps / (total_ms / 1e3)
+
+    counts = np.bincount(idx.cpu().numpy().ravel(), minlength=cfg.E)
+    if cfg.n_shared:
+        counts = np.concatenate([counts, [cfg.T] * cfg.n_shared])
+    dtype = "fp8" if cfg.wdtype == "fp8" else "bf16"
+    kern_s = float(np.mean(kern_ms)) / 1e3
+    if dom_name.startswith(("skinny_", "tiled_")):
+        work = acc.kernel_work(dom_name, counts, cfg.H, cfg.I, cfg.wdtype)
+    else:
+        work = None
+    roof = acc.roofline(work, kern_s, dtype) if work else None
+    if roof is not None:
+        roof.update({"kernel": dom_name, "kernel_ms": kern_s * 1e3,
+                     "algorithmic_bytes": work.bytes, "algorithmic_flops": work.flops,
+                     "traffic": stored_traffic(cfg.name, dom_name)})
+    layer = acc.layer_work(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.n_shared, cfg.wdtype, counts)
+    layer_roof = acc.roofline(layer, ms_per_step / 1e3, dtype)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, li, args.cpu_tokens or CPU_TOKENS.get(cfg.name, 64))
+
+    res = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "data": "synthetic (seeded; random-init weights of the layer's shape)",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k,
+                   "I": cfg.I, "n_shared": cfg.n_shared, "weights": cfg.wdtype,
+                   "touched_experts": int(layer.groups), "max_group_rows": int(counts.max()),
+                   "empty_experts": int((counts[:cfg.E] == 0).sum())},
+        "roofline": roof,
+        "layer_roofline": layer_roof,
+        "per_kernel_ms": {f"{i}:{n}": round(ms, 4) for i, (ms, n) in enumerate(launches)},
+        "wall_s_timed_region": t_wall,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -42,6 +42,11 @@ SIGNATURES = {
     "moe_grouped_ffn": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_combine": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P]),
     "moe_forward": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_profile_start": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int]),
+    "moe_profile_count": (ctypes.c_int, []),
+    "moe_profile_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_float),
+                                        ctypes.POINTER(ctypes.c_char_p)]),
+    "moe_profile_stop": (ctypes.c_int, []),
 }
 
 _lib = None
@@ -157,3 +162,27 @@ def moe_forward(shape, x, w_router, router_bias, w_gate, w_up, w_down, s_gate, s
                              _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(s_gate), _ptr(s_up),
                              _ptr(s_down), _ptr(out), _ptr(topk_idx_out), _ptr(topk_w_out),
                              _ptr(workspace), ws_bytes, _stream(stream)), "moe_forward")
+
+
+def moe_profile_start(mode: int, which: int = 0, capacity: int = 64) -> None:
+    rc = lib().moe_profile_start(mode, which, capacity)
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_profile_start failed")
+
+
+def moe_profile_count() -> int:
+    return lib().moe_profile_count()
+
+
+def moe_profile_read(i: int):
+    """(milliseconds, kernel name) of recorded event pair i (waits for it)."""
+    ms = ctypes.c_float()
+    name = ctypes.c_char_p()
+    rc = lib().moe_profile_read(i, ctypes.byref(ms), ctypes.byref(name))
+    if rc != MOE_OK:
+        raise MoeError(rc, f"moe_profile_read({i}) failed")
+    return ms.value, name.value.decode()
+
+
+def moe_profile_stop() -> None:
+    lib().moe_profile_stop()

@@ -1,0 +1,126 @@
+"""Algorithmic work of the MoE layer and of each kernel launch (host logic).
+
+Cost model of a grouped GEMM ("Lower latency and higher throughput with
+multi-node DeepSeek deployment", Roofline / GroupGEMM section): g groups of
+[m, k] x [k, n] cost 2*g*m*k*n FLOPs and move g*(m*k + n*k + m*n) elements.
+Here every group has its own m (the realised routing), and only groups with
+at least one row count: an expert that receives no token is never read,
+which is the point the same page makes about the number of activated experts.
+
+Bytes are ALGORITHMIC: what the step must read and write at least (weights
+of touched experts, activations in, results out), not what a kernel happens
+to move.
+"""
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+# MI355X published peaks (dense, no sparsity).
+PEAK_HBM_GBS = 8000.0
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp32": 157.3}
+
+# Row classes of the grouped-FFN schedule; the same thresholds as the C++
+# schedule in csrc/ffn.hip (skinny classes up to 16/32/64 rows, then 128-row
+# tiles).
+SKINNY_CLASS_ROWS = (16, 32, 64)
+TILE_ROWS = 128
+
+
+def tokens_per_expert(T: int, k: int, E: int) -> float:
+    """Mean rows per expert when T tokens each pick k of E experts."""
+    return T * k / E
+
+
+def ep_tokens_per_expert(batch: int, qlen: int, k: int, ep: int, E: int) -> float:
+    """Mean rows per expert under expert parallelism over `ep` GPUs holding E experts
+    with `batch` requests of `qlen` query tokens per GPU."""
+    return batch * qlen * k * ep / E
+
+
+def groupgemm_flops(g: int, m: int, k: int, n: int) -> int:
+    return 2 * g * m * k * n
+
+
+def groupgemm_io_elements(g: int, m: int, k: int, n: int) -> int:
+    return g * (m * k + n * k + m * n)
+
+
+def fp8_scale_shapes(M: int, K: int, N: int):
+    """Scale shapes of a block-quantised (M, K) x (K, N) product: activation scales
+    [M, ceil(K/128)] and weight scales [ceil(K/128), ceil(N/128)]."""
+    kb = math.ceil(K / 128)
+    return (M, kb), (kb, math.ceil(N / 128))
+
+
+@dataclass
+class Work:
+    bytes: float
+    flops: float
+    groups: int
+
+
+def _elt(wdtype: str) -> int:
+    return 1 if wdtype == "fp8" else 2
+
+
+def kernel_groups(kernel: str, counts: np.ndarray) -> np.ndarray:
+    """Group sizes a grouped-FFN launch processes, from its name."""
+    m = np.asarray(counts, dtype=np.int64)
+    m = m[m > 0]
+    if kernel.startswith("skinny_"):
+        c = int(kernel.rsplit("_r", 1)[1])
+        lo = {16: 0, 32: 16, 64: 32}[c]
+        return m[(m > lo) & (m <= c)]
+    if kernel.startswith("tiled_"):
+        return m[m > SKINNY_CLASS_ROWS[-1]]
+    raise ValueError(f"not a grouped-FFN kernel: {kernel}")
+
+
+def kernel_work(kernel: str, counts: np.ndarray, H: int, I: int, wdtype: str) -> Work:
+    """Algorithmic bytes and FLOPs of one launch of a grouped-FFN kernel."""
+    m = kernel_groups(kernel, counts).astype(np.float64)
+    e = _elt(wdtype)
+    fp8 = wdtype == "fp8"
+    rows = float(m.sum())
+    g = len(m)
+    if "_gateup_" in kernel:
+        w = g * 2 * I * H * e + (g * 2 * (I // 128) * (H // 128) * 4 if fp8 else 0)
+        a = rows * H * e + (rows * (H // 128) * 4 if fp8 else 0)
+        o = rows * I * e + (rows * (I // 128) * 4 if fp8 else 0)
+        return Work(w + a + o, 4.0 * rows * I * H, g)
+    if "_down_" in kernel:
+        w = g * H * I * e + (g * (H // 128) * (I // 128) * 4 if fp8 else 0)
+        a = rows * I * e + (rows * (I // 128) * 4 if fp8 else 0)
+        o = rows * H * 2
+        return Work(w + a + o, 2.0 * rows * H * I, g)
+    raise ValueError(f"not a grouped-FFN kernel: {kernel}")
+
+
+def layer_work(T: int, H: int, E: int, k: int, I: int, n_shared: int, wdtype: str,
+               counts: np.ndarray) -> Work:
+    """Algorithmic bytes / FLOPs of one layer call: weights of touched experts
+    (and their block scales), the router weight, x in and out."""
+    m = np.asarray(counts, dtype=np.int64)
+    touched = int((m > 0).sum())
+    e = _elt(wdtype)
+    wbytes = touched * 3 * H * I * e
+    if wdtype == "fp8":
+        wbytes += touched * 3 * (H // 128) * (I // 128) * 4
+    byts = wbytes + 4 * H * E + T * H * 2 + T * H * 2
+    R = T * (k + n_shared)
+    flops = 2 * T * H * E + 2 * R * 3 * H * I
+    return Work(float(byts), float(flops), touched)
+
+
+def roofline(work: Work, seconds: float, dtype: str):
+    """Binding roofline of a launch: HBM if its arithmetic intensity is below the ridge."""
+    ridge = PEAK_TFLOPS[dtype] * 1e12 / (PEAK_HBM_GBS * 1e9)
+    ai = work.flops / max(work.bytes, 1.0)
+    if ai < ridge:
+        ach = work.bytes / seconds / 1e9
+        return {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": ach / PEAK_HBM_GBS}
+    ach = work.flops / seconds / 1e12
+    return {"bound": "mfma", "achieved": ach, "peak": PEAK_TFLOPS[dtype], "unit": "TFLOP/s",
+            "frac": ach / PEAK_TFLOPS[dtype]}

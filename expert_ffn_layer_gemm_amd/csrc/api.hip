@@ -108,6 +108,7 @@ int moe_route(const moe_shape* shape, const void* x, const float* w_router,
               const float* router_bias, float* logits, int32_t* topk_idx, float* topk_w,
               void* stream) {
   const char* fn = "moe_route";
+  moe::prof_call_begin();
   if (int rc = check_shape(fn, shape, false)) return rc;
   if (shape->T == 0) return MOE_OK;
   MOE_NEED_PTR(x);
@@ -127,6 +128,7 @@ int moe_route(const moe_shape* shape, const void* x, const float* w_router,
 int moe_route_from_logits(const moe_shape* shape, const float* logits, int32_t* topk_idx,
                           float* topk_w, void* stream) {
   const char* fn = "moe_route_from_logits";
+  moe::prof_call_begin();
   if (shape == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s: shape is NULL", fn);
   if (shape->T < 0) return fail(MOE_ERR_UNSUPPORTED, "%s: T < 0", fn);
   if (shape->E < 1 || shape->E > 1024) return fail(MOE_ERR_UNSUPPORTED, "%s: E not in [1,1024]", fn);
@@ -144,6 +146,7 @@ int moe_permute(const moe_shape* shape, const int32_t* topk_idx, const void* x, 
                 int32_t* offsets, int32_t* dest, int32_t* src_row, void* x_perm,
                 float* x_perm_scale, void* stream) {
   const char* fn = "moe_permute";
+  moe::prof_call_begin();
   if (int rc = check_shape(fn, shape, false)) return rc;
   const bool fp8 = shape->wdtype == MOE_FP8_E4M3_BLOCK128;
   MOE_NEED_PTR(counts);
@@ -168,6 +171,7 @@ int moe_grouped_ffn(const moe_shape* shape, const int32_t* offsets, const void* 
                     const float* s_down, void* y_perm, void* workspace, size_t ws_bytes,
                     void* stream) {
   const char* fn = "moe_grouped_ffn";
+  moe::prof_call_begin();
   if (int rc = check_shape(fn, shape, true)) return rc;
   const bool fp8 = shape->wdtype == MOE_FP8_E4M3_BLOCK128;
   if (shape->T == 0) return MOE_OK;
@@ -197,6 +201,7 @@ int moe_grouped_ffn(const moe_shape* shape, const int32_t* offsets, const void* 
 int moe_combine(const moe_shape* shape, const void* y_perm, const int32_t* dest,
                 const float* topk_w, void* out, void* stream) {
   const char* fn = "moe_combine";
+  moe::prof_call_begin();
   if (int rc = check_shape(fn, shape, false)) return rc;
   if (shape->T == 0) return MOE_OK;
   MOE_NEED_PTR(y_perm);
@@ -214,6 +219,7 @@ int moe_forward(const moe_shape* shape, const void* x, const float* w_router,
                 void* out, int32_t* topk_idx_out, float* topk_w_out, void* workspace,
                 size_t ws_bytes, void* stream) {
   const char* fn = "moe_forward";
+  moe::prof_call_begin();
   if (int rc = check_shape(fn, shape, true)) return rc;
   const bool fp8 = shape->wdtype == MOE_FP8_E4M3_BLOCK128;
   if (shape->T == 0) return MOE_OK;

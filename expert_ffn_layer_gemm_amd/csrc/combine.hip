@@ -47,10 +47,10 @@ __global__ __launch_bounds__(TPB) void k_combine(const uint16_t* __restrict__ y_
 hipError_t launch_combine(const uint16_t* y_perm, const int32_t* dest, const float* topk_w,
                           uint16_t* out, int T, int H, int k, int n_shared, hipStream_t s) {
   if (H / 8 <= 256)
-    hipLaunchKernelGGL((k_combine<64>), dim3(T), dim3(64), 0, s, y_perm, dest, topk_w, out, T, H,
+    MOE_LAUNCH("combine", (k_combine<64>), dim3(T), dim3(64), 0, s, y_perm, dest, topk_w, out, T, H,
                        k, n_shared);
   else
-    hipLaunchKernelGGL((k_combine<256>), dim3(T), dim3(256), 0, s, y_perm, dest, topk_w, out, T, H,
+    MOE_LAUNCH("combine", (k_combine<256>), dim3(T), dim3(256), 0, s, y_perm, dest, topk_w, out, T, H,
                        k, n_shared);
   return hipGetLastError();
 }

@@ -588,8 +588,9 @@ size_t ffn_workspace_bytes(int T, int H, int E, int k, int I, int n_shared, bool
 }
 
 template <typename Kern>
-static void launch_gemm(Kern kern, int threads, long long blocks, const GemmArgs& a, hipStream_t s) {
-  if (blocks > 0) hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(threads), 0, s, a);
+static void launch_gemm(const char* name, Kern kern, int threads, long long blocks,
+                        const GemmArgs& a, hipStream_t s) {
+  if (blocks > 0) MOE_LAUNCH(name, kern, dim3((unsigned)blocks), dim3(threads), 0, s, a);
 }
 
 hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
@@ -599,7 +600,7 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
   Sched sc{reinterpret_cast<int32_t*>(ws + L.n_skinny), reinterpret_cast<int32_t*>(ws + L.n_tiles),
            reinterpret_cast<int32_t*>(ws + L.skinny), reinterpret_cast<int32_t*>(ws + L.tiles), G};
   const long long R = (long long)f.T * (f.k + f.n_shared);
-  hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, f.offsets, sc);
+  MOE_LAUNCH("plan", k_plan, dim3(1), dim3(1024), 0, s, f.offsets, sc);
 
   uint8_t* h = ws + L.h;
   float* h_scale = f.fp8 ? reinterpret_cast<float*>(ws + L.h_scale) : nullptr;
@@ -638,33 +639,33 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
   // gate/up + SwiGLU
   if (f.fp8) {
     up.n_ntile = f.I / (16 * 8);
-    launch_gemm(k_skinny_fp8<true, 8, 1>, 512, max_cls[0] * up.n_ntile, up, s);
-    launch_gemm(k_skinny_fp8<true, 8, 2>, 512, max_cls[1] * up.n_ntile, up, s);
-    launch_gemm(k_skinny_fp8<true, 8, 4>, 512, max_cls[2] * up.n_ntile, up, s);
+    launch_gemm("skinny_gateup_fp8_r16", k_skinny_fp8<true, 8, 1>, 512, max_cls[0] * up.n_ntile, up, s);
+    launch_gemm("skinny_gateup_fp8_r32", k_skinny_fp8<true, 8, 2>, 512, max_cls[1] * up.n_ntile, up, s);
+    launch_gemm("skinny_gateup_fp8_r64", k_skinny_fp8<true, 8, 4>, 512, max_cls[2] * up.n_ntile, up, s);
   } else {
     up.n_ntile = f.I / (16 * 4);
-    launch_gemm(k_skinny_bf16<true, 4, 1>, 256, max_cls[0] * up.n_ntile, up, s);
-    launch_gemm(k_skinny_bf16<true, 4, 2>, 256, max_cls[1] * up.n_ntile, up, s);
-    launch_gemm(k_skinny_bf16<true, 4, 4>, 256, max_cls[2] * up.n_ntile, up, s);
+    launch_gemm("skinny_gateup_bf16_r16", k_skinny_bf16<true, 4, 1>, 256, max_cls[0] * up.n_ntile, up, s);
+    launch_gemm("skinny_gateup_bf16_r32", k_skinny_bf16<true, 4, 2>, 256, max_cls[1] * up.n_ntile, up, s);
+    launch_gemm("skinny_gateup_bf16_r64", k_skinny_bf16<true, 4, 4>, 256, max_cls[2] * up.n_ntile, up, s);
   }
   up.n_ntile = f.I / kTileBN;
-  if (f.fp8) launch_gemm(k_tiled<true, true>, 512, (long long)L.max_tiles * up.n_ntile, up, s);
-  else launch_gemm(k_tiled<false, true>, 512, (long long)L.max_tiles * up.n_ntile, up, s);
+  if (f.fp8) launch_gemm("tiled_gateup_fp8", k_tiled<true, true>, 512, (long long)L.max_tiles * up.n_ntile, up, s);
+  else launch_gemm("tiled_gateup_bf16", k_tiled<false, true>, 512, (long long)L.max_tiles * up.n_ntile, up, s);
 
   // down
   dn.n_ntile = f.H / (16 * 4);
   if (f.fp8) {
-    launch_gemm(k_skinny_fp8<false, 4, 1>, 256, max_cls[0] * dn.n_ntile, dn, s);
-    launch_gemm(k_skinny_fp8<false, 4, 2>, 256, max_cls[1] * dn.n_ntile, dn, s);
-    launch_gemm(k_skinny_fp8<false, 4, 4>, 256, max_cls[2] * dn.n_ntile, dn, s);
+    launch_gemm("skinny_down_fp8_r16", k_skinny_fp8<false, 4, 1>, 256, max_cls[0] * dn.n_ntile, dn, s);
+    launch_gemm("skinny_down_fp8_r32", k_skinny_fp8<false, 4, 2>, 256, max_cls[1] * dn.n_ntile, dn, s);
+    launch_gemm("skinny_down_fp8_r64", k_skinny_fp8<false, 4, 4>, 256, max_cls[2] * dn.n_ntile, dn, s);
   } else {
-    launch_gemm(k_skinny_bf16<false, 4, 1>, 256, max_cls[0] * dn.n_ntile, dn, s);
-    launch_gemm(k_skinny_bf16<false, 4, 2>, 256, max_cls[1] * dn.n_ntile, dn, s);
-    launch_gemm(k_skinny_bf16<false, 4, 4>, 256, max_cls[2] * dn.n_ntile, dn, s);
+    launch_gemm("skinny_down_bf16_r16", k_skinny_bf16<false, 4, 1>, 256, max_cls[0] * dn.n_ntile, dn, s);
+    launch_gemm("skinny_down_bf16_r32", k_skinny_bf16<false, 4, 2>, 256, max_cls[1] * dn.n_ntile, dn, s);
+    launch_gemm("skinny_down_bf16_r64", k_skinny_bf16<false, 4, 4>, 256, max_cls[2] * dn.n_ntile, dn, s);
   }
   dn.n_ntile = f.H / kTileBN;
-  if (f.fp8) launch_gemm(k_tiled<true, false>, 512, (long long)L.max_tiles * dn.n_ntile, dn, s);
-  else launch_gemm(k_tiled<false, false>, 512, (long long)L.max_tiles * dn.n_ntile, dn, s);
+  if (f.fp8) launch_gemm("tiled_down_fp8", k_tiled<true, false>, 512, (long long)L.max_tiles * dn.n_ntile, dn, s);
+  else launch_gemm("tiled_down_bf16", k_tiled<false, false>, 512, (long long)L.max_tiles * dn.n_ntile, dn, s);
   return hipGetLastError();
 }
 

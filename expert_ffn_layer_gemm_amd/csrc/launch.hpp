@@ -8,6 +8,19 @@
 
 namespace moe {
 
+// prof.hip: measurement hook (events around launches when enabled).
+void prof_call_begin();
+void prof_before(const char* name, hipStream_t s);
+void prof_after(hipStream_t s);
+
+// Launch a kernel, bracketed by the measurement hook.
+#define MOE_LAUNCH(name, kernel, grid, block, shmem, stream, ...)          \
+  do {                                                                   \
+    ::moe::prof_before(name, stream);                                    \
+    hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__); \
+    ::moe::prof_after(stream);                                           \
+  } while (0)
+
 // route.hip
 hipError_t launch_router_gemm(const uint16_t* x, const float* w, const float* bias, float* logits,
                               int T, int H, int E, hipStream_t s);

@@ -143,18 +143,18 @@ hipError_t launch_permute(const int32_t* topk_idx, const uint16_t* x, int32_t* c
                           int32_t* offsets, int32_t* dest, int32_t* src_row, void* x_perm,
                           float* x_perm_scale, int T, int H, int E, int k, int n_shared, bool fp8,
                           hipStream_t s) {
-  hipLaunchKernelGGL(k_hist_scan, dim3(1), dim3(1024), 0, s, topk_idx, counts, offsets, T, E, k,
+  MOE_LAUNCH("hist_scan", k_hist_scan, dim3(1), dim3(1024), 0, s, topk_idx, counts, offsets, T, E, k,
                      n_shared);
   if (T == 0) return hipGetLastError();
-  hipLaunchKernelGGL(k_rank, dim3(ceil_div(T, kRankTile)), dim3(kRankTile), 0, s, topk_idx, offsets,
+  MOE_LAUNCH("rank", k_rank, dim3(ceil_div(T, kRankTile)), dim3(kRankTile), 0, s, topk_idx, offsets,
                      dest, src_row, T, E, k, n_shared);
   const int R = T * (k + n_shared);
   const dim3 grid(ceil_div(R, kGatherRows));
   if (fp8)
-    hipLaunchKernelGGL(k_gather_fp8, grid, dim3(256), 0, s, src_row, x,
+    MOE_LAUNCH("gather_fp8", k_gather_fp8, grid, dim3(256), 0, s, src_row, x,
                        static_cast<uint8_t*>(x_perm), x_perm_scale, R, H);
   else
-    hipLaunchKernelGGL(k_gather_bf16, grid, dim3(256), 0, s, src_row, x,
+    MOE_LAUNCH("gather_bf16", k_gather_bf16, grid, dim3(256), 0, s, src_row, x,
                        static_cast<uint16_t*>(x_perm), R, H);
   return hipGetLastError();
 }

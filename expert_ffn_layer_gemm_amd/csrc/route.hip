@@ -191,17 +191,17 @@ hipError_t launch_router_gemm(const uint16_t* x, const float* w, const float* bi
                               int T, int H, int E, hipStream_t s) {
   if (T <= 256) {
     dim3 grid(ceil_div(T, 16), ceil_div(E, 16));
-    hipLaunchKernelGGL((k_router_gemm<1, 1, 8>), grid, dim3(512), 0, s, x, w, bias, logits, T, H, E);
+    MOE_LAUNCH("router_gemm_t16x16_k8", (k_router_gemm<1, 1, 8>), grid, dim3(512), 0, s, x, w, bias, logits, T, H, E);
   } else {
     dim3 grid(ceil_div(T, 32), ceil_div(E, 64));
-    hipLaunchKernelGGL((k_router_gemm<2, 4, 2>), grid, dim3(128), 0, s, x, w, bias, logits, T, H, E);
+    MOE_LAUNCH("router_gemm_t32x64_k2", (k_router_gemm<2, 4, 2>), grid, dim3(128), 0, s, x, w, bias, logits, T, H, E);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_topk(const float* logits, int32_t* idx, float* w, int T, int E, int k,
                        hipStream_t s) {
-  hipLaunchKernelGGL(k_topk, dim3(ceil_div(T, 4)), dim3(256), 0, s, logits, idx, w, T, E, k);
+  MOE_LAUNCH("topk", k_topk, dim3(ceil_div(T, 4)), dim3(256), 0, s, logits, idx, w, T, E, k);
   return hipGetLastError();
 }
 

@@ -185,6 +185,24 @@ int moe_forward(const moe_shape* shape, const void* x, const float* w_router,
                 float* topk_w_out, void* workspace, size_t ws_bytes,
                 void* stream);
 
+/*
+ * Measurement hook (not a step of the layer).  After moe_profile_start, the
+ * entry-point calls made on this thread record a pair of HIP events on their
+ * stream around kernel launches:
+ *   mode 1: around every launch, in launch order, up to `capacity` pairs;
+ *   mode 2: around launch number `which` (0-based, counted from the start of
+ *           each entry-point call) only, up to `capacity` pairs.
+ * The events are created here (host objects; no device memory).
+ * moe_profile_count: pairs recorded so far.  moe_profile_read: waits for pair
+ * i, returns its elapsed milliseconds and the launched kernel's name (a static
+ * string).  moe_profile_stop: stop recording and destroy the events.
+ * Returns MOE_OK, MOE_ERR_INVALID_ARG (bad mode/index) or MOE_ERR_HIP.
+ */
+int moe_profile_start(int mode, int which, int capacity);
+int moe_profile_count(void);
+int moe_profile_read(int i, float* ms, const char** name);
+int moe_profile_stop(void);
+
 #ifdef __cplusplus
 }
 #endif

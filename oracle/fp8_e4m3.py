@@ -17,9 +17,9 @@ import numpy as np
 E4M3_MAX = np.float32(448.0)
 
 
-def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+def _decode_fields(c: np.ndarray) -> np.ndarray:
     """Value of each e4m3fn code, from its sign / exponent / mantissa fields."""
-    c = np.asarray(codes, dtype=np.uint8).astype(np.int32)
+    c = c.astype(np.int32)
     sign = np.where(c & 0x80, -1.0, 1.0)
     ef = (c >> 3) & 0xF
     mf = c & 0x7
@@ -28,9 +28,17 @@ def e4m3_decode(codes: np.ndarray) -> np.ndarray:
     return (sign * mag).astype(np.float32)
 
 
+_TABLE = _decode_fields(np.arange(256))
+
+
 def e4m3_table() -> np.ndarray:
     """The 256 decoded values, indexed by code."""
-    return e4m3_decode(np.arange(256, dtype=np.uint8))
+    return _TABLE.copy()
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """Value of each e4m3fn code (a lookup in the 256-entry table of field values)."""
+    return _TABLE[np.asarray(codes, dtype=np.uint8)]
 
 
 def e4m3_encode(v: np.ndarray) -> np.ndarray:

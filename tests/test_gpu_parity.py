@@ -173,7 +173,7 @@ def test_grouped_ffn_group_size_boundaries(wdtype):
 
 
 def test_grouped_ffn_fp8_shared_group():
-    sizes = [5, 0, 70, 9, 40]        # group 4 = shared expert
+    sizes = [5, 0, 66, 9, 40]        # routed rows sum to T*k = 80; group 4 = shared expert (T rows)
     cfg = MoeConfig("ffn_fp8_shared", 22, T=40, H=256, E=4, k=2, I=384, n_shared=1, wdtype="fp8")
     y, ref = _ffn_case(cfg, sizes, 2)
     assert rel_inf(y, ref) <= TOL["fp8"]
