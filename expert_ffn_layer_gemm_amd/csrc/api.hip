@@ -51,6 +51,10 @@ int check_shape(const char* fn, const moe_shape* s, bool need_ffn_dims) {
     return fail(MOE_ERR_UNSUPPORTED, "%s: H=%d not a positive multiple of 128", fn, s->H);
   if (need_ffn_dims && (s->I < 128 || s->I % 128))
     return fail(MOE_ERR_UNSUPPORTED, "%s: I=%d not a positive multiple of 128", fn, s->I);
+  // One expert matrix must stay below 4 GB (32-bit in-matrix offsets) and K
+  // below 131072 (fp8 block scales of a tile are staged in LDS).
+  if (need_ffn_dims && ((long long)s->H * s->I >= (1LL << 31) || s->H > 131072 || s->I > 131072))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: H*I=%lld too large", fn, (long long)s->H * s->I);
   return MOE_OK;
 }
 

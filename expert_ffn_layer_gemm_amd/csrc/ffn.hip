@@ -26,32 +26,9 @@
 // the device-side list length exit at once.  No host synchronisation.
 #include <algorithm>
 
-#include "common.hpp"
-#include "launch.hpp"
+#include "ffn.hpp"
 
 namespace moe {
-
-constexpr int kSkinnyMax = 64;      // rows handled by the skinny kernel (4 MFMA row blocks)
-constexpr int kTileWaves = 8;       // tiled kernel: 4 (rows) x 2 (cols) waves
-constexpr int kTileFM = 2, kTileFN = 4;
-constexpr int kTileBM = 4 * 16 * kTileFM;   // 128 rows per tile
-constexpr int kTileBN = 2 * 16 * kTileFN;   // 128 output columns per tile
-constexpr int kLdsStride = 144;             // bytes per staged 128-byte K row (+16 pad)
-
-// Skinny groups are split into row classes (<= 16, <= 32, <= 64 rows) so each
-// class runs a kernel whose register use matches its row blocks.
-constexpr int kSkinnyClasses = 3;
-__host__ __device__ constexpr int skinny_class_rows(int c) { return 16 << c; }
-
-struct Sched {
-  int32_t* n_skinny;  // [kSkinnyClasses]
-  int32_t* n_tiles;
-  int32_t* skinny;    // [kSkinnyClasses][G] group ids
-  int32_t* tiles;     // [max_tiles][2] (group, first row)
-  int G;
-};
-
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.f + expf(-g)) * u; }
 
 // ------------------------------------------------------------------ plan ----
 __device__ __forceinline__ void block_scan_pair(int a, int b, int* wave_sum, int& excl_a,
@@ -111,22 +88,6 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ offse
   }
   if (tid == 0) *sc.n_tiles = nt_total;
 }
-
-// Operands of one grouped GEMM launch.  Row-major, K contiguous:
-// A [R, K] (x_perm or h), B0/B1 [G, N, K] (gate/up or down), out [R, N].
-struct GemmArgs {
-  Sched sc;
-  const int32_t* offsets;
-  const uint8_t* A;
-  const float* A_scale;    // [R, K/128] (fp8)
-  const uint8_t* B0;
-  const uint8_t* B1;       // up weights (dual) or unused
-  const float* s_B0;       // [G, N/128, K/128] (fp8)
-  const float* s_B1;
-  uint8_t* out;            // bf16 or e4m3 codes
-  float* out_scale;        // [R, N/128] (fp8 dual)
-  int K, N, n_ntile;
-};
 
 // ---------------------------------------------------------- skinny, bf16 ----
 // Workgroup = NW waves; wave w owns 16 output columns and all (<= 16*MB) rows
@@ -337,224 +298,6 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_fp8(const GemmArgs p) {
   }
 }
 
-// ------------------------------------------------------------- LDS tiled ----
-// Workgroup: 8 waves as 4 (rows) x 2 (columns); tile = 128 rows x 128 output
-// columns; each K iteration stages one 128-byte K chunk per row (64 bf16 or
-// 128 e4m3 values) of A (128 rows) and B (128 rows, or 256 for gate+up) in
-// LDS, double-buffered: the next chunk's global loads are issued into
-// registers before the current chunk is multiplied, and stored to the other
-// LDS buffer after it.  Rows are padded to 144 bytes so the 16-byte fragment
-// reads of 8 consecutive lanes (8 different rows) hit distinct banks.
-template <bool FP8, bool DUAL>
-struct TileCfg {
-  static constexpr int BROWS = DUAL ? 2 * kTileBN : kTileBN;
-  static constexpr int ROWS = kTileBM + BROWS;
-  static constexpr int CHUNKS = ROWS * 8;                       // 16-byte chunks per stage
-  static constexpr int PER_THREAD = CHUNKS / (64 * kTileWaves);
-  static constexpr int LDS_BYTES = 2 * ROWS * kLdsStride;
-};
-
-template <bool FP8, bool DUAL>
-__global__ __launch_bounds__(64 * kTileWaves) void k_tiled(const GemmArgs p) {
-  using C = TileCfg<FP8, DUAL>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS_BYTES];
-  const int slot = blockIdx.x / p.n_ntile, nt = blockIdx.x % p.n_ntile;
-  if (slot >= *p.sc.n_tiles) return;
-  const int g = p.sc.tiles[2 * slot], m0 = p.sc.tiles[2 * slot + 1];
-  const int row0 = p.offsets[g] + m0;
-  const int mrows = min(kTileBM, p.offsets[g + 1] - row0);
-  const int K = p.K, N = p.N;
-  const int Kbytes = FP8 ? K : 2 * K;
-  const int n0 = nt * kTileBN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int r16 = lane & 15;
-
-  // Global source of each staged 16-byte chunk this thread moves.
-  const uint8_t* src[C::PER_THREAD];
-  bool ok[C::PER_THREAD];
-  int dst[C::PER_THREAD];
-#pragma unroll
-  for (int i = 0; i < C::PER_THREAD; ++i) {
-    const int c = tid + i * 64 * kTileWaves;
-    const int row = c >> 3, col = (c & 7) * 16;
-    dst[i] = row * kLdsStride + col;
-    if (row < kTileBM) {
-      ok[i] = row < mrows;
-      src[i] = p.A + (size_t)(row0 + (ok[i] ? row : 0)) * Kbytes + col;
-    } else {
-      const int br = row - kTileBM;
-      const bool up = DUAL && br >= kTileBN;
-      const int n = n0 + (up ? br - kTileBN : br);
-      ok[i] = true;
-      src[i] = (up ? p.B1 : p.B0) + ((size_t)g * N + n) * Kbytes + col;
-    }
-  }
-  u32x4_t stage[C::PER_THREAD];
-  auto load = [&](int kc) {
-#pragma unroll
-    for (int i = 0; i < C::PER_THREAD; ++i)
-      stage[i] = ok[i] ? *reinterpret_cast<const u32x4_t*>(src[i] + (size_t)kc * 128)
-                       : u32x4_t{0, 0, 0, 0};
-  };
-  auto store = [&](int buf) {
-    uint8_t* base = lds + buf * C::ROWS * kLdsStride;
-#pragma unroll
-    for (int i = 0; i < C::PER_THREAD; ++i) *reinterpret_cast<u32x4_t*>(base + dst[i]) = stage[i];
-  };
-
-  f32x4_t acc0[kTileFM][kTileFN], acc1[kTileFM][kTileFN];
-#pragma unroll
-  for (int i = 0; i < kTileFM; ++i)
-#pragma unroll
-    for (int j = 0; j < kTileFN; ++j) acc0[i][j] = acc1[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // Rows of this wave's fragments inside the tile.
-  const int arow0 = wm * 16 * kTileFM;
-  const int bcol0 = wn * 16 * kTileFN;
-  const int nk = Kbytes / 128;
-  const int KB = K / 128;
-  const int nblk = n0 / 128;
-  const float* sb0 = FP8 ? p.s_B0 + ((size_t)g * (N / 128) + nblk) * KB : nullptr;
-  const float* sb1 = (FP8 && DUAL) ? p.s_B1 + ((size_t)g * (N / 128) + nblk) * KB : nullptr;
-  const bool wave_active = arow0 < mrows;
-
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int kc = 0; kc < nk; ++kc) {
-    const int buf = kc & 1;
-    if (kc + 1 < nk) load(kc + 1);
-    const uint8_t* As = lds + buf * C::ROWS * kLdsStride;
-    const uint8_t* Bs = As + kTileBM * kLdsStride;
-    if (wave_active) {
-      if constexpr (!FP8) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {   // two 32-wide K steps per 64-element chunk
-          const int off = ks * 64 + (lane >> 4) * 16;
-          u32x4_t a[kTileFM], b0[kTileFN], b1[kTileFN];
-#pragma unroll
-          for (int i = 0; i < kTileFM; ++i)
-            a[i] = *reinterpret_cast<const u32x4_t*>(As + (arow0 + i * 16 + r16) * kLdsStride + off);
-#pragma unroll
-          for (int j = 0; j < kTileFN; ++j) {
-            b0[j] = *reinterpret_cast<const u32x4_t*>(Bs + (bcol0 + j * 16 + r16) * kLdsStride + off);
-            if (DUAL)
-              b1[j] = *reinterpret_cast<const u32x4_t*>(Bs + (kTileBN + bcol0 + j * 16 + r16) * kLdsStride + off);
-          }
-#pragma unroll
-          for (int i = 0; i < kTileFM; ++i)
-#pragma unroll
-            for (int j = 0; j < kTileFN; ++j) {
-              acc0[i][j] = mfma_bf16_16x16x32(a[i], b0[j], acc0[i][j]);
-              if (DUAL) acc1[i][j] = mfma_bf16_16x16x32(a[i], b1[j], acc1[i][j]);
-            }
-        }
-      } else {
-        const int off = (lane >> 4) * 32;
-        i32x8_t a[kTileFM], b0[kTileFN], b1[kTileFN];
-#pragma unroll
-        for (int i = 0; i < kTileFM; ++i) {
-          const uint8_t* pa = As + (arow0 + i * 16 + r16) * kLdsStride + off;
-          const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(pa), hi = *reinterpret_cast<const u32x4_t*>(pa + 16);
-          a[i] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        }
-#pragma unroll
-        for (int j = 0; j < kTileFN; ++j) {
-          const uint8_t* pb = Bs + (bcol0 + j * 16 + r16) * kLdsStride + off;
-          const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(pb), hi = *reinterpret_cast<const u32x4_t*>(pb + 16);
-          b0[j] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-          if (DUAL) {
-            const uint8_t* pu = pb + kTileBN * kLdsStride;
-            const u32x4_t ulo = *reinterpret_cast<const u32x4_t*>(pu), uhi = *reinterpret_cast<const u32x4_t*>(pu + 16);
-            b1[j] = i32x8_t{(int)ulo[0], (int)ulo[1], (int)ulo[2], (int)ulo[3], (int)uhi[0], (int)uhi[1], (int)uhi[2], (int)uhi[3]};
-          }
-        }
-        const float s0 = sb0[kc], s1 = DUAL ? sb1[kc] : 0.f;
-#pragma unroll
-        for (int i = 0; i < kTileFM; ++i) {
-          float sa[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int r = arow0 + i * 16 + (lane >> 4) * 4 + q;
-            sa[q] = r < mrows ? p.A_scale[(size_t)(row0 + r) * KB + kc] : 0.f;
-          }
-#pragma unroll
-          for (int j = 0; j < kTileFN; ++j) {
-            const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-            const f32x4_t p0 = mfma_fp8_16x16x128(a[i], b0[j], z);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) acc0[i][j][q] += p0[q] * (sa[q] * s0);
-            if (DUAL) {
-              const f32x4_t p1 = mfma_fp8_16x16x128(a[i], b1[j], z);
-#pragma unroll
-              for (int q = 0; q < 4; ++q) acc1[i][j][q] += p1[q] * (sa[q] * s1);
-            }
-          }
-        }
-      }
-    }
-    if (kc + 1 < nk) store(buf ^ 1);
-    __syncthreads();
-  }
-
-  // Epilogue.  Lane holds rows arow0 + 16 i + 4 (lane/16) + q, column
-  // n0 + bcol0 + 16 j + lane%16.
-  if constexpr (FP8 && DUAL) {
-    // Row maxima of |h| over the tile's 128 columns: 4 column blocks in the
-    // lane, 16 lanes, then the two column waves through LDS (reusing lds).
-    float* amax_s = reinterpret_cast<float*>(lds);   // [2][kTileBM]
-    float hv[kTileFM][kTileFN][4];
-#pragma unroll
-    for (int i = 0; i < kTileFM; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = arow0 + i * 16 + (lane >> 4) * 4 + q;
-        float am = 0.f;
-#pragma unroll
-        for (int j = 0; j < kTileFN; ++j) {
-          hv[i][j][q] = r < mrows ? silu_mul(acc0[i][j][q], acc1[i][j][q]) : 0.f;
-          am = fmaxf(am, fabsf(hv[i][j][q]));
-        }
-        am = wave_max_xor(am, 16);
-        if (r16 == 0) amax_s[wn * kTileBM + r] = am;
-      }
-    __syncthreads();
-    const int N128 = N / 128;
-#pragma unroll
-    for (int i = 0; i < kTileFM; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = arow0 + i * 16 + (lane >> 4) * 4 + q;
-        if (r < mrows) {
-          const float am = fmaxf(amax_s[r], amax_s[kTileBM + r]);
-          const float scale = am == 0.f ? 1.f : am / 448.f;
-#pragma unroll
-          for (int j = 0; j < kTileFN; ++j) {
-            const float qv = fminf(fmaxf(hv[i][j][q] / scale, -448.f), 448.f);
-            p.out[(size_t)(row0 + r) * N + n0 + bcol0 + j * 16 + r16] = (uint8_t)f32_to_e4m3(qv);
-          }
-          if (wn == 0 && r16 == 0) p.out_scale[(size_t)(row0 + r) * N128 + nblk] = scale;
-        }
-      }
-  } else {
-    uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
-#pragma unroll
-    for (int i = 0; i < kTileFM; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = arow0 + i * 16 + (lane >> 4) * 4 + q;
-        if (r < mrows) {
-#pragma unroll
-          for (int j = 0; j < kTileFN; ++j) {
-            const float v = DUAL ? silu_mul(acc0[i][j][q], acc1[i][j][q]) : acc0[i][j][q];
-            out[(size_t)(row0 + r) * N + n0 + bcol0 + j * 16 + r16] = (uint16_t)f32_to_bf16_bits(v);
-          }
-        }
-      }
-  }
-}
-
 // ------------------------------------------------------------------- host ----
 namespace {
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
@@ -648,9 +391,9 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
     launch_gemm("skinny_gateup_bf16_r32", k_skinny_bf16<true, 4, 2>, 256, max_cls[1] * up.n_ntile, up, s);
     launch_gemm("skinny_gateup_bf16_r64", k_skinny_bf16<true, 4, 4>, 256, max_cls[2] * up.n_ntile, up, s);
   }
-  up.n_ntile = f.I / kTileBN;
-  if (f.fp8) launch_gemm("tiled_gateup_fp8", k_tiled<true, true>, 512, (long long)L.max_tiles * up.n_ntile, up, s);
-  else launch_gemm("tiled_gateup_bf16", k_tiled<false, true>, 512, (long long)L.max_tiles * up.n_ntile, up, s);
+  up.n_ntile = f.I / 128;
+  launch_tiled(f.fp8 ? "tiled_gateup_fp8" : "tiled_gateup_bf16", f.fp8, true,
+               (long long)L.max_tiles * up.n_ntile, up, s);
 
   // down
   dn.n_ntile = f.H / (16 * 4);
@@ -663,9 +406,9 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
     launch_gemm("skinny_down_bf16_r32", k_skinny_bf16<false, 4, 2>, 256, max_cls[1] * dn.n_ntile, dn, s);
     launch_gemm("skinny_down_bf16_r64", k_skinny_bf16<false, 4, 4>, 256, max_cls[2] * dn.n_ntile, dn, s);
   }
-  dn.n_ntile = f.H / kTileBN;
-  if (f.fp8) launch_gemm("tiled_down_fp8", k_tiled<true, false>, 512, (long long)L.max_tiles * dn.n_ntile, dn, s);
-  else launch_gemm("tiled_down_bf16", k_tiled<false, false>, 512, (long long)L.max_tiles * dn.n_ntile, dn, s);
+  dn.n_ntile = ceil_div(f.H, 256);
+  launch_tiled(f.fp8 ? "tiled_down_fp8" : "tiled_down_bf16", f.fp8, false,
+               (long long)L.max_tiles * dn.n_ntile, dn, s);
   return hipGetLastError();
 }
 

@@ -1,0 +1,48 @@
+// Definitions shared by the grouped-FFN kernels (ffn.hip: schedule and
+// weight-streaming kernels; tiled.hip: LDS-pipelined tiled kernel).
+#pragma once
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+constexpr int kSkinnyMax = 64;      // rows handled by the skinny kernel (4 MFMA row blocks)
+constexpr int kTileBM = 256;        // rows per tile of the tiled kernel
+
+// Skinny groups are split into row classes (<= 16, <= 32, <= 64 rows) so each
+// class runs a kernel whose register use matches its row blocks.
+constexpr int kSkinnyClasses = 3;
+__host__ __device__ constexpr int skinny_class_rows(int c) { return 16 << c; }
+
+struct Sched {
+  int32_t* n_skinny;  // [kSkinnyClasses]
+  int32_t* n_tiles;
+  int32_t* skinny;    // [kSkinnyClasses][G] group ids
+  int32_t* tiles;     // [max_tiles][2] (group, first row)
+  int G;
+};
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.f + expf(-g)) * u; }
+
+// Operands of one grouped GEMM launch.  Row-major, K contiguous:
+// A [R, K] (x_perm or h), B0/B1 [G, N, K] (gate/up or down), out [R, N].
+struct GemmArgs {
+  Sched sc;
+  const int32_t* offsets;
+  const uint8_t* A;
+  const float* A_scale;    // [R, K/128] (fp8)
+  const uint8_t* B0;
+  const uint8_t* B1;       // up weights (dual) or unused
+  const float* s_B0;       // [G, N/128, K/128] (fp8)
+  const float* s_B1;
+  uint8_t* out;            // bf16 or e4m3 codes
+  float* out_scale;        // [R, N/128] (fp8 dual)
+  int K, N, n_ntile;
+};
+
+// Tiled kernel launch (tiled.hip).
+hipError_t launch_tiled(const char* name, bool fp8, bool dual, long long blocks, const GemmArgs& a,
+                        hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,355 @@
+// LDS-pipelined tiled grouped GEMM for groups with more than 64 rows
+// (prefill-sized groups, the shared expert, the hot experts of a skewed
+// routing).  Computes, per (group, 256-row tile, column tile):
+//   DUAL:   h = silu(X W_gate^T) * (X W_up^T)    128 h columns (256 B rows)
+//   single: y = h W_down^T                        256 output columns
+// with fp32 accumulation; fp8 layers apply the per-row activation scale and
+// the 128x128 weight-block scale to each 128-wide K block's MFMA partial
+// (DeepSeek-deployment page, Quantization), and the DUAL fp8 epilogue
+// re-quantises h per row per 128 channels.  SwiGLU in the epilogue follows the
+// Ironwood page's GMM v2 (section 4.2.2): gate and up are two B streams of
+// one workgroup.
+//
+// gfx950 design:
+//   - 256 x 256 tile (A 256 rows, B 256 rows), 4 waves, 64 MFMA 16x16 blocks
+//     (256 fp32 accumulators) per wave.  At 128 FLOP per staged byte (bf16)
+//     the operand stream from L2 / the Infinity Cache stays below what the
+//     MFMA rate needs; smaller tiles were bound by that stream.
+//   - Wave layout WM x WN: 2 x 2 (128 x 128 per wave, fewest LDS reads) for
+//     bf16; 1 x 4 (256 rows x 64 B rows per wave) for fp8, whose groups have
+//     ~128 rows, so that all four SIMDs have rows to multiply.
+//   - K is staged in 128-byte chunks (64 bf16 / 128 e4m3 per row) through a
+//     2-stage LDS ring filled by direct-to-LDS loads (global_load_lds_dwordx4):
+//     the next chunk (64 KB per CU) is in flight while this one is multiplied.
+//   - A direct-to-LDS instruction writes 1 KB contiguously (lane i at +16 i);
+//     each lane fetches global chunk c ^ (row & 7) of its row so row r's
+//     chunk c sits in slot c ^ (r & 7).  Fragment reads (16 lanes on 16
+//     consecutive rows, one chunk) with this slot map measured conflict-free
+//     on gfx950 (the row-XOR variant (r ^ r >> 3) & 7 tried first was not).
+//   - Blocks are renumbered so each XCD (own L2) takes a contiguous run of
+//     tiles: the column tiles of one row tile, and the row tiles of one
+//     group, run on the same L2 at the same time and share their operands.
+//   - Rows past the group's end are loaded from its last row (finite values)
+//     and never stored; 16-row blocks wholly past the end skip their MFMAs.
+#include "ffn.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kRB = 128;                          // bytes of K per staged row and chunk
+constexpr int kStages = 2;
+constexpr int kBM = kTileBM;                      // 256 rows per tile
+constexpr int kBRows = 256;                       // staged B rows per tile
+constexpr int kRows = kBM + kBRows;
+constexpr int kStageData = kRows * kRB;           // 64 KB
+constexpr int kMaxKB = 1024;                      // fp8: K <= 131072 (B scales kept in LDS)
+constexpr int kXcds = 8;
+
+static_assert(kBM == 256, "tile geometry below assumes 256 rows");
+
+// Slot of chunk c of staged row r.
+__device__ __forceinline__ int slot(int r, int c) { return c ^ (r & 7); }
+
+// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() would also
+// wait for every outstanding vector-memory operation, including the
+// direct-to-LDS loads of the next chunk, and drain the pipeline; completion of
+// the chunk about to be read is awaited explicitly with wait_vmcnt instead.
+// The memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ u32x4_t lds_read16(const uint8_t* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+// Direct-to-LDS loads of one K chunk into stage `st`: this wave's IPW
+// 1 KB blocks (wave-uniform base + per-lane offsets) and, for fp8, the row
+// scales of the chunk's K block.
+template <int IPW, bool FP8>
+__device__ __forceinline__ void dma_chunk(uint8_t* st, const uint8_t* kbase, const uint32_t (&soff)[IPW],
+                                          int wave, const float* sptr) {
+#pragma unroll
+  for (int j = 0; j < IPW; ++j)
+    __builtin_amdgcn_global_load_lds(kbase + soff[j], (lds_ptr_t)(st + (wave * IPW + j) * 1024), 16, 0, 0);
+  if constexpr (FP8)
+    __builtin_amdgcn_global_load_lds(sptr, (lds_ptr_t)(st + kStageData + wave * 256), 4, 0, 0);
+}
+
+// Staged B row of 16-column block j (lane row r16) for wave column wn.
+template <bool DUAL, int WN, int NB>
+__device__ __forceinline__ int b_row(int j, int wn, int r16) {
+  if constexpr (DUAL)
+    return (j < NB / 2 ? wn * (128 / WN) + j * 16 : 128 + wn * (128 / WN) + (j - NB / 2) * 16) + r16;
+  return wn * (256 / WN) + j * 16 + r16;
+}
+
+}  // namespace
+
+template <bool FP8, bool DUAL, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
+  // The body is device code only; the host pass needs just the launch stub.
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int NW = WM * WN;                     // waves per workgroup
+  constexpr int MB = kBM / WM / 16;               // 16-row blocks per wave
+  constexpr int NB = kBRows / WN / 16;            // 16-column blocks per wave
+  constexpr int IPW = kStageData / 1024 / NW;     // direct-to-LDS instructions per wave and stage
+  constexpr int SCALE_BYTES = FP8 ? NW * 256 : 0; // fp8 row scales (waves >= 4 load duplicates)
+  constexpr int STAGE = kStageData + SCALE_BYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * STAGE + (FP8 ? 2 * kMaxKB * 4 : 16)];
+
+  // XCD-contiguous renumbering of the valid (tile, column tile) pairs.
+  const int n_valid = *p.sc.n_tiles * p.n_ntile;
+  const int per_xcd = (n_valid + kXcds - 1) / kXcds;
+  const int bid = blockIdx.x;
+  const int logical = (bid % kXcds) * per_xcd + bid / kXcds;
+  if (bid >= kXcds * per_xcd || logical >= n_valid) return;
+  const int tslot = logical / p.n_ntile, nt = logical % p.n_ntile;
+  const int g = p.sc.tiles[2 * tslot], m0 = p.sc.tiles[2 * tslot + 1];
+  const int row0 = p.offsets[g] + m0;
+  const int mrows = min(kBM, p.offsets[g + 1] - row0);
+  const int K = p.K, N = p.N;
+  const size_t Kb = FP8 ? (size_t)K : 2 * (size_t)K;
+  const int nk = (int)(Kb / kRB);
+  const int KB = K / 128;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // Wave index as a scalar: keeps every per-wave condition a scalar branch.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int n0 = nt * (DUAL ? 128 : 256);
+  const int ncols = DUAL ? 128 : min(256, N - n0);
+  const int r16 = lane & 15;
+
+  // Sources of the 16-byte chunks this wave moves per stage: a wave-uniform
+  // base (its rows all lie in A, in B0 or in B1) plus a 32-bit lane offset.
+  const int wrow0 = wave * IPW * 8;                // first staged row of this wave
+  const uint8_t* wbase;
+  uint32_t soff[IPW];
+  if (wrow0 < kBM) {
+    wbase = p.A + (size_t)row0 * Kb;
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) {
+      const int row = wrow0 + j * 8 + (lane >> 3);
+      soff[j] = (uint32_t)min(row, mrows - 1) * (uint32_t)Kb + (uint32_t)(slot(row, lane & 7) * 16);
+    }
+  } else {
+    int bw = wrow0 - kBM;                          // first B row of this wave
+    const uint8_t* B = p.B0;
+    if (DUAL && bw >= 128) { B = p.B1; bw -= 128; }
+    // Rows past the matrix (ragged last column tile) re-read its last row.
+    wbase = B + (size_t)g * N * Kb;
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) {
+      const int row = wrow0 + j * 8 + (lane >> 3);
+      const int n = min(n0 + bw + j * 8 + (lane >> 3), N - 1);
+      soff[j] = (uint32_t)n * (uint32_t)Kb + (uint32_t)(slot(row, lane & 7) * 16);
+    }
+  }
+  const float* ssrc = nullptr;
+  float* bsc = reinterpret_cast<float*>(lds + kStages * STAGE);   // fp8: [2][KB] B block scales
+  if constexpr (FP8) {
+    ssrc = p.A_scale + (size_t)(row0 + min((wave & 3) * 64 + lane, mrows - 1)) * KB;
+    const int N128 = N / 128;
+    for (int i = tid; i < 2 * KB; i += 64 * NW) {
+      const int which = i / KB, kb = i % KB;
+      float v;
+      if (DUAL) v = (which ? p.s_B1 : p.s_B0)[((size_t)g * N128 + nt) * KB + kb];
+      else v = p.s_B0[((size_t)g * N128 + min(n0 / 128 + which, N128 - 1)) * KB + kb];
+      bsc[i] = v;
+    }
+  }
+
+
+  // 16-row blocks of the wave holding valid rows.
+  const int rbase = wm * (kBM / WM);
+  const int nmb = max(0, min(MB, ceil_div(mrows - rbase, 16)));
+  const bool has_cols = DUAL || wn * (256 / WN) < ncols;
+  const bool active = nmb > 0 && has_cols;
+
+  f32x4_t acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Multiply one staged chunk.  bf16: all fragments of a K step are read from
+  // LDS before its MFMAs, so the LDS latency is paid once per step.  FULL
+  // multiplies every row block (rows past the group's end hold finite copies
+  // of its last row and are never stored).
+  constexpr bool FULL = FP8;
+  dma_chunk<IPW, FP8>(lds, wbase, soff, wave, ssrc);
+  for (int kc = 0; kc < nk; ++kc) {
+    wait_vmcnt<0>();        // this wave's share of chunk kc has landed
+    lds_barrier();          // every wave's share, and every wave is done with chunk kc - 1
+    if (kc + 1 < nk)      // into the stage of chunk kc - 1
+      dma_chunk<IPW, FP8>(lds + ((kc + 1) % kStages) * STAGE, wbase + (size_t)(kc + 1) * kRB, soff,
+                          wave, FP8 ? ssrc + kc + 1 : nullptr);
+    if (!active) continue;
+    const uint8_t* As = lds + (kc % kStages) * STAGE;
+    const uint8_t* Bs = As + kBM * kRB;
+    // fp8 (memory-bound) multiplies every row block of an active wave, which
+    // keeps its code branch-free; bf16 skips the row blocks past the group's end.
+    if constexpr (!FP8) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int c = ks * 4 + (lane >> 4);
+        u32x4_t a[MB], b[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const int br = b_row<DUAL, WN, NB>(j, wn, r16);
+          b[j] = lds_read16(Bs + br * kRB + (slot(br, c) << 4));
+        }
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+          const int r = rbase + i * 16 + r16;
+          a[i] = lds_read16(As + r * kRB + (slot(r, c) << 4));
+        }
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+          if (FULL || i < nmb) {
+#pragma unroll
+            for (int j = 0; j < NB; ++j) acc[i][j] = mfma_bf16_16x16x32(a[i], b[j], acc[i][j]);
+          }
+      }
+    } else {
+      // A lane's 32 codes: K positions 16*(lane/16) .. +16 and 64 + 16*(lane/16) .. +16
+      // (the same positions for A and B, so the pairing inside the MFMA is right).
+      const int c0 = lane >> 4, c1 = 4 + (lane >> 4);
+      i32x8_t b[NB];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int br = b_row<DUAL, WN, NB>(j, wn, r16);
+        const uint8_t* rowp = Bs + br * kRB;
+        const u32x4_t lo = lds_read16(rowp + (slot(br, c0) << 4));
+        const u32x4_t hi = lds_read16(rowp + (slot(br, c1) << 4));
+        b[j] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                       (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
+      const float* ascale = reinterpret_cast<const float*>(As + kStageData);
+      const float sb_lo = DUAL ? bsc[kc] : bsc[(wn * (256 / WN)) / 128 * KB + kc];
+      const float sb_hi = DUAL ? bsc[KB + kc] : sb_lo;
+      // One A fragment at a time: the second wave of the SIMD covers its latency.
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+        if (FULL || i < nmb) {
+          const int r = rbase + i * 16 + r16;
+          const uint8_t* rowp = As + r * kRB;
+          const u32x4_t lo = lds_read16(rowp + (slot(r, c0) << 4));
+          const u32x4_t hi = lds_read16(rowp + (slot(r, c1) << 4));
+          const i32x8_t a = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                    (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+          float s_lo[4], s_hi[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float sa = ascale[rbase + i * 16 + (lane >> 4) * 4 + q];
+            s_lo[q] = sa * sb_lo;
+            s_hi[q] = sa * sb_hi;
+          }
+#pragma unroll
+          for (int j = 0; j < NB; ++j) {
+            const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+            const f32x4_t pr = mfma_fp8_16x16x128(a, b[j], z);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[i][j][q] += pr[q] * (j < NB / 2 ? s_lo[q] : s_hi[q]);
+          }
+        }
+    }
+  }
+
+  // Epilogue.  Lane holds rows rbase + 16 i + 4 (lane/16) + q of its blocks.
+  if constexpr (FP8 && DUAL) {
+    lds_barrier();                                    // stages are free: reuse for row maxima
+    float* amax_s = reinterpret_cast<float*>(lds);    // [WN][kBM]
+    constexpr int NH = NB / 2;                        // gate (= up) blocks per wave
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = rbase + i * 16 + (lane >> 4) * 4 + q;
+        float am = 0.f;
+#pragma unroll
+        for (int j = 0; j < NH; ++j) {
+          const float h = (i < nmb && r < mrows) ? silu_mul(acc[i][j][q], acc[i][j + NH][q]) : 0.f;
+          acc[i][j][q] = h;
+          am = fmaxf(am, fabsf(h));
+        }
+        am = wave_max_xor(am, 16);
+        if (r16 == 0) amax_s[wn * kBM + r] = am;
+      }
+    lds_barrier();
+    const int N128 = N / 128;
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+      if (i < nmb) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = rbase + i * 16 + (lane >> 4) * 4 + q;
+          if (r < mrows) {
+            float am = 0.f;
+#pragma unroll
+            for (int w = 0; w < WN; ++w) am = fmaxf(am, amax_s[w * kBM + r]);
+            const float scale = am == 0.f ? 1.f : am / 448.f;
+#pragma unroll
+            for (int j = 0; j < NH; ++j) {
+              const float qv = fminf(fmaxf(acc[i][j][q] / scale, -448.f), 448.f);
+              p.out[(size_t)(row0 + r) * N + n0 + wn * (128 / WN) + j * 16 + r16] =
+                  (uint8_t)f32_to_e4m3(qv);
+            }
+            if (wn == 0 && r16 == 0) p.out_scale[(size_t)(row0 + r) * N128 + nt] = scale;
+          }
+        }
+      }
+  } else {
+    if (!active) return;
+    uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+      if (i < nmb) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = rbase + i * 16 + (lane >> 4) * 4 + q;
+          if (r < mrows) {
+            uint16_t* orow = out + (size_t)(row0 + r) * N;
+            if constexpr (DUAL) {
+#pragma unroll
+              for (int j = 0; j < NB / 2; ++j)
+                orow[n0 + wn * (128 / WN) + j * 16 + r16] =
+                    (uint16_t)f32_to_bf16_bits(silu_mul(acc[i][j][q], acc[i][j + NB / 2][q]));
+            } else {
+#pragma unroll
+              for (int j = 0; j < NB; ++j) {
+                const int col = wn * (256 / WN) + j * 16 + r16;
+                if (col < ncols) orow[n0 + col] = (uint16_t)f32_to_bf16_bits(acc[i][j][q]);
+              }
+            }
+          }
+        }
+      }
+  }
+#else
+  (void)p;
+#endif
+}
+
+hipError_t launch_tiled(const char* name, bool fp8, bool dual, long long blocks, const GemmArgs& a,
+                        hipStream_t s) {
+  if (blocks <= 0) return hipSuccess;
+  // The XCD renumbering needs up to kXcds - 1 blocks past the valid ones.
+  const dim3 grid((unsigned)((blocks + 2 * kXcds - 1) / kXcds * kXcds));
+  if (fp8 && dual) MOE_LAUNCH(name, (k_tiled3<true, true, 2, 4>), grid, dim3(512), 0, s, a);
+  else if (fp8) MOE_LAUNCH(name, (k_tiled3<true, false, 2, 4>), grid, dim3(512), 0, s, a);
+  else if (dual) MOE_LAUNCH(name, (k_tiled3<false, true, 2, 2>), grid, dim3(256), 0, s, a);
+  else MOE_LAUNCH(name, (k_tiled3<false, false, 2, 2>), grid, dim3(256), 0, s, a);
+  return hipSuccess;
+}
+
+}  // namespace moe

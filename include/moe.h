@@ -34,7 +34,8 @@
  *     A launch failure returns MOE_ERR_HIP.  moe_last_error() then returns a
  *     thread-local message.  No exception crosses the ABI.
  *   - Supported shapes: 0 <= T, T*(k+n_shared) < 2^31, 1 <= k <= min(E, 16),
- *     1 <= E <= 1024, n_shared in {0, 1}, H and I positive multiples of 128.
+ *     1 <= E <= 1024, n_shared in {0, 1}, H and I positive multiples of 128,
+ *     H, I <= 131072 and H*I < 2^31.
  *     T == 0 is a valid no-op.  Other shapes return MOE_ERR_UNSUPPORTED.
  *   - The library keeps no state between calls; calls on different streams
  *     with disjoint buffers may run concurrently.
