@@ -347,8 +347,8 @@ hipError_t launch_tiled(const char* name, bool fp8, bool dual, long long blocks,
   const dim3 grid((unsigned)((blocks + 2 * kXcds - 1) / kXcds * kXcds));
   if (fp8 && dual) MOE_LAUNCH(name, (k_tiled3<true, true, 2, 4>), grid, dim3(512), 0, s, a);
   else if (fp8) MOE_LAUNCH(name, (k_tiled3<true, false, 2, 4>), grid, dim3(512), 0, s, a);
-  else if (dual) MOE_LAUNCH(name, (k_tiled3<false, true, 2, 2>), grid, dim3(256), 0, s, a);
-  else MOE_LAUNCH(name, (k_tiled3<false, false, 2, 2>), grid, dim3(256), 0, s, a);
+  else if (dual) MOE_LAUNCH(name, (k_tiled3<false, true, 2, 4>), grid, dim3(512), 0, s, a);
+  else MOE_LAUNCH(name, (k_tiled3<false, false, 2, 4>), grid, dim3(512), 0, s, a);
   return hipSuccess;
 }
 
