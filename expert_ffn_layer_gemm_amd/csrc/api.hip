@@ -62,9 +62,11 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
-// moe_forward workspace: routing, dispatch and expert intermediates.
+// moe_forward workspace: routing, dispatch and expert intermediates.  The
+// forward path never builds x_perm: the GEMMs gather their rows through
+// src_row from x (bf16) or from x quantised once per token (fp8: xq, xs).
 struct FwdLayout {
-  size_t logits, idx, w, counts, offsets, dest, src_row, x_perm, x_scale, y_perm, ffn, total;
+  size_t logits, idx, w, counts, offsets, dest, src_row, xq, xs, y_perm, ffn, total;
 };
 
 FwdLayout fwd_layout(const moe_shape* s) {
@@ -80,8 +82,8 @@ FwdLayout fwd_layout(const moe_shape* s) {
   L.offsets = off; off += align256((G + 1) * 4);
   L.dest = off;    off += align256(T * k * 4);
   L.src_row = off; off += align256(R * 4);
-  L.x_perm = off;  off += align256(R * H * (fp8 ? 1 : 2));
-  L.x_scale = off; off += fp8 ? align256(R * (H / 128) * 4) : 0;
+  L.xq = off;      off += fp8 ? align256(T * H) : 0;
+  L.xs = off;      off += fp8 ? align256(T * (H / 128) * 4) : 0;
   L.y_perm = off;  off += align256(R * H * 2);
   L.ffn = off;
   off += moe::ffn_workspace_bytes(s->T, s->H, s->E, s->k, s->I, s->n_shared, fp8);
@@ -197,8 +199,8 @@ int moe_grouped_ffn(const moe_shape* shape, const int32_t* offsets, const void* 
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return fail(MOE_ERR_INVALID_ARG, "%s: workspace not 256-byte aligned", fn);
   moe::FfnArgs a{shape->T, shape->H, shape->E, shape->k, shape->I, shape->n_shared, fp8,
-                 offsets, x_perm, x_perm_scale, w_gate, w_up, w_down, s_gate, s_up, s_down,
-                 y_perm, workspace};
+                 offsets, nullptr, x_perm, x_perm_scale, w_gate, w_up, w_down, s_gate, s_up,
+                 s_down, y_perm, workspace};
   return hip_status(moe::launch_grouped_ffn(a, as_stream(stream)), fn);
 }
 
@@ -225,6 +227,8 @@ int moe_forward(const moe_shape* shape, const void* x, const float* w_router,
   const char* fn = "moe_forward";
   moe::prof_call_begin();
   if (int rc = check_shape(fn, shape, true)) return rc;
+  if ((long long)shape->T * shape->H * 2 >= (1LL << 32))   // 32-bit row offsets into x
+    return fail(MOE_ERR_UNSUPPORTED, "%s: T*H*2 >= 2^32", fn);
   const bool fp8 = shape->wdtype == MOE_FP8_E4M3_BLOCK128;
   if (shape->T == 0) return MOE_OK;
   MOE_NEED_PTR(x);
@@ -258,22 +262,24 @@ int moe_forward(const moe_shape* shape, const void* x, const float* w_router,
   int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
   int32_t* dest = reinterpret_cast<int32_t*>(ws + L.dest);
   int32_t* src_row = reinterpret_cast<int32_t*>(ws + L.src_row);
-  void* x_perm = ws + L.x_perm;
-  float* x_scale = fp8 ? reinterpret_cast<float*>(ws + L.x_scale) : nullptr;
+  uint8_t* xq = fp8 ? ws + L.xq : nullptr;
+  float* xs = fp8 ? reinterpret_cast<float*>(ws + L.xs) : nullptr;
   void* y_perm = ws + L.y_perm;
   hipStream_t s = as_stream(stream);
 
   hipError_t e = moe::launch_router_gemm(static_cast<const uint16_t*>(x), w_router, router_bias,
                                          logits, shape->T, shape->H, shape->E, s);
   if (e == hipSuccess) e = moe::launch_topk(logits, idx, w, shape->T, shape->E, shape->k, s);
-  if (e == hipSuccess)
+  if (e == hipSuccess)   // routing tables only: no row copy
     e = moe::launch_permute(idx, static_cast<const uint16_t*>(x), counts, offsets, dest, src_row,
-                            x_perm, x_scale, shape->T, shape->H, shape->E, shape->k,
+                            nullptr, nullptr, shape->T, shape->H, shape->E, shape->k,
                             shape->n_shared, fp8, s);
+  if (e == hipSuccess && fp8)
+    e = moe::launch_quantize_rows(static_cast<const uint16_t*>(x), xq, xs, shape->T, shape->H, s);
   if (e == hipSuccess) {
     moe::FfnArgs a{shape->T, shape->H, shape->E, shape->k, shape->I, shape->n_shared, fp8,
-                   offsets, x_perm, x_scale, w_gate, w_up, w_down, s_gate, s_up, s_down,
-                   y_perm, ws + L.ffn};
+                   offsets, src_row, fp8 ? static_cast<const void*>(xq) : x, xs, w_gate, w_up,
+                   w_down, s_gate, s_up, s_down, y_perm, ws + L.ffn};
     e = moe::launch_grouped_ffn(a, s);
   }
   if (e == hipSuccess)

@@ -115,7 +115,8 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_bf16(const GemmArgs p) {
   for (int mb = 0; mb < MB; ++mb) {
     const int r = mb * 16 + r16;
     aok[mb] = r < m;
-    arow[mb] = reinterpret_cast<const uint16_t*>(p.A) + (size_t)(row0 + (aok[mb] ? r : 0)) * K + kq;
+    const int pr = row0 + (aok[mb] ? r : 0);
+    arow[mb] = reinterpret_cast<const uint16_t*>(p.A) + (size_t)(p.a_rows ? p.a_rows[pr] : pr) * K + kq;
   }
 
   f32x4_t acc0[MB], acc1[MB];
@@ -212,12 +213,14 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_fp8(const GemmArgs p) {
   for (int mb = 0; mb < MB; ++mb) {
     const int r = mb * 16 + r16;
     aok[mb] = r < m;
-    arow[mb] = p.A + (size_t)(row0 + (aok[mb] ? r : 0)) * K + kq;
+    const int pr = row0 + (aok[mb] ? r : 0);
+    arow[mb] = p.A + (size_t)(p.a_rows ? p.a_rows[pr] : pr) * K + kq;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int rr = mb * 16 + (lane >> 4) * 4 + q;
       sok[mb][q] = rr < m;
-      srow[mb][q] = p.A_scale + (size_t)(row0 + (sok[mb][q] ? rr : 0)) * KB;
+      const int ps = row0 + (sok[mb][q] ? rr : 0);
+      srow[mb][q] = p.A_scale + (size_t)(p.a_rows ? p.a_rows[ps] : ps) * KB;
     }
   }
   f32x4_t acc0[MB], acc1[MB];
@@ -356,6 +359,7 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
   GemmArgs up{};
   up.sc = sc;
   up.offsets = f.offsets;
+  up.a_rows = f.a_rows;
   up.A = static_cast<const uint8_t*>(f.x_perm);
   up.A_scale = f.x_perm_scale;
   up.B0 = static_cast<const uint8_t*>(f.w_gate);
@@ -368,6 +372,7 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
   up.N = f.I;
 
   GemmArgs dn = up;
+  dn.a_rows = nullptr;            // h is written in permuted row order
   dn.A = h;
   dn.A_scale = h_scale;
   dn.B0 = static_cast<const uint8_t*>(f.w_down);

@@ -30,6 +30,7 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.f + 
 struct GemmArgs {
   Sched sc;
   const int32_t* offsets;
+  const int32_t* a_rows;   // optional: A row of permuted row r is a_rows[r] (gather on load)
   const uint8_t* A;
   const float* A_scale;    // [R, K/128] (fp8)
   const uint8_t* B0;

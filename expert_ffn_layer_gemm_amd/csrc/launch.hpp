@@ -28,10 +28,15 @@ hipError_t launch_topk(const float* logits, int32_t* idx, float* w, int T, int E
                        hipStream_t s);
 
 // permute.hip
+// x_perm == nullptr skips the row copy (the GEMMs then gather rows through src_row).
 hipError_t launch_permute(const int32_t* topk_idx, const uint16_t* x, int32_t* counts,
                           int32_t* offsets, int32_t* dest, int32_t* src_row, void* x_perm,
                           float* x_perm_scale, int T, int H, int E, int k, int n_shared, bool fp8,
                           hipStream_t s);
+// Per-token e4m3 quantisation of x (128-channel groups): the rows the fp8
+// GEMMs gather through src_row.
+hipError_t launch_quantize_rows(const uint16_t* x, uint8_t* xq, float* xs, int T, int H,
+                                hipStream_t s);
 
 // combine.hip
 hipError_t launch_combine(const uint16_t* y_perm, const int32_t* dest, const float* topk_w,
@@ -42,6 +47,7 @@ struct FfnArgs {
   int T, H, E, k, I, n_shared;
   bool fp8;
   const int32_t* offsets;
+  const int32_t* a_rows;    // nullptr: x_perm holds the permuted rows; else rows of x_perm gathered
   const void* x_perm;
   const float* x_perm_scale;
   const void* w_gate;

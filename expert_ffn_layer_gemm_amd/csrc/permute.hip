@@ -107,8 +107,9 @@ __global__ __launch_bounds__(256) void k_gather_bf16(const int32_t* __restrict__
   }
 }
 
-// x_perm[r] = e4m3 codes of x[src_row[r]] per 128-channel group, scale = amax/448.
-// 16 lanes cover one group (8 bf16 each); the group max is a 16-lane xor reduction.
+// x_perm[r] = e4m3 codes of x[src_row[r]] (x[r] when src_row is null) per
+// 128-channel group, scale = amax/448.  16 lanes cover one group (8 bf16
+// each); the group max is a 16-lane xor reduction.
 __global__ __launch_bounds__(256) void k_gather_fp8(const int32_t* __restrict__ src_row,
                                                     const uint16_t* __restrict__ x,
                                                     uint8_t* __restrict__ x_perm,
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(256) void k_gather_fp8(const int32_t* __restrict__ 
   for (int rr = 0; rr < kGatherRows; ++rr) {
     const int r = blockIdx.x * kGatherRows + rr;
     if (r >= R) return;
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + (size_t)src_row[r] * H);
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + (size_t)(src_row ? src_row[r] : r) * H);
     for (int c = threadIdx.x; c < chunks; c += 256) {
       float v[8];
       unpack_bf16x8(src[c], v);
@@ -148,6 +149,7 @@ hipError_t launch_permute(const int32_t* topk_idx, const uint16_t* x, int32_t* c
   if (T == 0) return hipGetLastError();
   MOE_LAUNCH("rank", k_rank, dim3(ceil_div(T, kRankTile)), dim3(kRankTile), 0, s, topk_idx, offsets,
                      dest, src_row, T, E, k, n_shared);
+  if (x_perm == nullptr) return hipGetLastError();
   const int R = T * (k + n_shared);
   const dim3 grid(ceil_div(R, kGatherRows));
   if (fp8)
@@ -156,6 +158,14 @@ hipError_t launch_permute(const int32_t* topk_idx, const uint16_t* x, int32_t* c
   else
     MOE_LAUNCH("gather_bf16", k_gather_bf16, grid, dim3(256), 0, s, src_row, x,
                        static_cast<uint16_t*>(x_perm), R, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_rows(const uint16_t* x, uint8_t* xq, float* xs, int T, int H,
+                                hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  MOE_LAUNCH("quantize_rows_fp8", k_gather_fp8, dim3(ceil_div(T, kGatherRows)), dim3(256), 0, s,
+             static_cast<const int32_t*>(nullptr), x, xq, xs, T, H);
   return hipGetLastError();
 }
 

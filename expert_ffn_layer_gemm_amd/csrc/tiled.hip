@@ -77,10 +77,11 @@ __device__ __forceinline__ u32x4_t lds_read16(const uint8_t* p) {
 // scales of the chunk's K block.
 template <int IPW, bool FP8>
 __device__ __forceinline__ void dma_chunk(uint8_t* st, const uint8_t* kbase, const uint32_t (&soff)[IPW],
-                                          int wave, const float* sptr) {
+                                          int wave, const float* sptr, int nvalid) {
 #pragma unroll
   for (int j = 0; j < IPW; ++j)
-    __builtin_amdgcn_global_load_lds(kbase + soff[j], (lds_ptr_t)(st + (wave * IPW + j) * 1024), 16, 0, 0);
+    if (j < nvalid)
+      __builtin_amdgcn_global_load_lds(kbase + soff[j], (lds_ptr_t)(st + (wave * IPW + j) * 1024), 16, 0, 0);
   if constexpr (FP8)
     __builtin_amdgcn_global_load_lds(sptr, (lds_ptr_t)(st + kStageData + wave * 256), 4, 0, 0);
 }
@@ -134,12 +135,20 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
   const int wrow0 = wave * IPW * 8;                // first staged row of this wave
   const uint8_t* wbase;
   uint32_t soff[IPW];
+  // 1 KB instructions of this wave that carry valid rows (A rows past the
+  // group's end are not fetched: those LDS rows keep stale finite data from
+  // earlier chunks and their outputs are never stored).
+  int nvalid = IPW;
   if (wrow0 < kBM) {
-    wbase = p.A + (size_t)row0 * Kb;
+    nvalid = max(0, min(IPW, ceil_div(mrows - wrow0, 8)));
+    // With a_rows the tile's rows are gathered from the unpermuted matrix.
+    wbase = p.a_rows ? p.A : p.A + (size_t)row0 * Kb;
 #pragma unroll
     for (int j = 0; j < IPW; ++j) {
       const int row = wrow0 + j * 8 + (lane >> 3);
-      soff[j] = (uint32_t)min(row, mrows - 1) * (uint32_t)Kb + (uint32_t)(slot(row, lane & 7) * 16);
+      const int r = min(row, mrows - 1);
+      const uint32_t src = p.a_rows ? (uint32_t)p.a_rows[row0 + r] : (uint32_t)r;
+      soff[j] = src * (uint32_t)Kb + (uint32_t)(slot(row, lane & 7) * 16);
     }
   } else {
     int bw = wrow0 - kBM;                          // first B row of this wave
@@ -157,7 +166,8 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
   const float* ssrc = nullptr;
   float* bsc = reinterpret_cast<float*>(lds + kStages * STAGE);   // fp8: [2][KB] B block scales
   if constexpr (FP8) {
-    ssrc = p.A_scale + (size_t)(row0 + min((wave & 3) * 64 + lane, mrows - 1)) * KB;
+    const int sr = row0 + min((wave & 3) * 64 + lane, mrows - 1);
+    ssrc = p.A_scale + (size_t)(p.a_rows ? p.a_rows[sr] : sr) * KB;
     const int N128 = N / 128;
     for (int i = tid; i < 2 * KB; i += 64 * NW) {
       const int which = i / KB, kb = i % KB;
@@ -186,13 +196,13 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
   // multiplies every row block (rows past the group's end hold finite copies
   // of its last row and are never stored).
   constexpr bool FULL = FP8;
-  dma_chunk<IPW, FP8>(lds, wbase, soff, wave, ssrc);
+  dma_chunk<IPW, FP8>(lds, wbase, soff, wave, ssrc, nvalid);
   for (int kc = 0; kc < nk; ++kc) {
     wait_vmcnt<0>();        // this wave's share of chunk kc has landed
     lds_barrier();          // every wave's share, and every wave is done with chunk kc - 1
     if (kc + 1 < nk)      // into the stage of chunk kc - 1
       dma_chunk<IPW, FP8>(lds + ((kc + 1) % kStages) * STAGE, wbase + (size_t)(kc + 1) * kRB, soff,
-                          wave, FP8 ? ssrc + kc + 1 : nullptr);
+                          wave, FP8 ? ssrc + kc + 1 : nullptr, nvalid);
     if (!active) continue;
     const uint8_t* As = lds + (kc % kStages) * STAGE;
     const uint8_t* Bs = As + kBM * kRB;

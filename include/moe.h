@@ -175,7 +175,10 @@ int moe_combine(const moe_shape* shape, const void* y_perm, const int32_t* dest,
 /*
  * The whole layer in one call: moe_route -> moe_permute -> moe_grouped_ffn ->
  * moe_combine on `stream`, intermediates in `workspace`
- * (>= moe_forward_workspace_bytes(shape)).  Arguments as above;
+ * (>= moe_forward_workspace_bytes(shape)).  The permuted activation matrix is
+ * never materialised here: the grouped GEMMs gather each row through src_row
+ * from x (bf16) or from x quantised once per token (fp8), which gives the
+ * same operands as moe_permute's x_perm.  Requires T*H*2 < 2^32.  Arguments as above;
  * topk_idx_out / topk_w_out may be NULL (then the routing lives in the
  * workspace only).  out [T, H] bf16.
  */
