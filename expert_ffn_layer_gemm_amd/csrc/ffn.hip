@@ -64,7 +64,7 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ offse
     cls[q] = -1;
     if (m[q] > 0 && m[q] <= kSkinnyMax)
       cls[q] = m[q] <= skinny_class_rows(0) ? 0 : (m[q] <= skinny_class_rows(1) ? 1 : 2);
-    nt[q] = m[q] > kSkinnyMax ? ceil_div(m[q], kTileBM) : 0;
+    nt[q] = m[q] > kSkinnyMax ? ceil_div(m[q], sc.tile_rows) : 0;
   }
 #pragma unroll
   for (int c = 0; c < kSkinnyClasses; ++c) {
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ offse
     const int g = 2 * tid + q;
     for (int i = 0; i < nt[q]; ++i) {
       sc.tiles[2 * nt_pos] = g;
-      sc.tiles[2 * nt_pos + 1] = i * kTileBM;
+      sc.tiles[2 * nt_pos + 1] = i * sc.tile_rows;
       ++nt_pos;
     }
   }
@@ -316,7 +316,7 @@ WsLayout ffn_layout(int T, int H, int E, int k, int I, int n_shared, bool fp8) {
   const long long R = (long long)T * (k + n_shared);
   const int G = E + n_shared;
   const long long big_groups = std::min<long long>(G, R / (kSkinnyMax + 1));
-  L.max_tiles = (int)(R / kTileBM + big_groups + 1);
+  L.max_tiles = (int)(R / tile_rows(fp8) + big_groups + 1);
   size_t off = 0;
   L.h = off;        off += align256((size_t)R * I * (fp8 ? 1 : 2));
   L.h_scale = off;  off += fp8 ? align256((size_t)R * (I / 128) * 4) : 0;
@@ -344,7 +344,8 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
   uint8_t* ws = static_cast<uint8_t*>(f.workspace);
   const int G = f.E + f.n_shared;
   Sched sc{reinterpret_cast<int32_t*>(ws + L.n_skinny), reinterpret_cast<int32_t*>(ws + L.n_tiles),
-           reinterpret_cast<int32_t*>(ws + L.skinny), reinterpret_cast<int32_t*>(ws + L.tiles), G};
+           reinterpret_cast<int32_t*>(ws + L.skinny), reinterpret_cast<int32_t*>(ws + L.tiles), G,
+           tile_rows(f.fp8)};
   const long long R = (long long)f.T * (f.k + f.n_shared);
   MOE_LAUNCH("plan", k_plan, dim3(1), dim3(1024), 0, s, f.offsets, sc);
 

@@ -8,7 +8,8 @@
 namespace moe {
 
 constexpr int kSkinnyMax = 64;      // rows handled by the skinny kernel (4 MFMA row blocks)
-constexpr int kTileBM = 256;        // rows per tile of the tiled kernel
+// Rows per tile of the tiled kernel: 256 for bf16, 128 for fp8.
+__host__ __device__ constexpr int tile_rows(bool fp8) { return fp8 ? 128 : 256; }
 
 // Skinny groups are split into row classes (<= 16, <= 32, <= 64 rows) so each
 // class runs a kernel whose register use matches its row blocks.
@@ -21,6 +22,7 @@ struct Sched {
   int32_t* skinny;    // [kSkinnyClasses][G] group ids
   int32_t* tiles;     // [max_tiles][2] (group, first row)
   int G;
+  int tile_rows;      // rows per tiled-kernel tile
 };
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.f + expf(-g)) * u; }

@@ -1,6 +1,6 @@
 // LDS-pipelined tiled grouped GEMM for groups with more than 64 rows
 // (prefill-sized groups, the shared expert, the hot experts of a skewed
-// routing).  Computes, per (group, 256-row tile, column tile):
+// routing).  Computes, per (group, row tile, column tile):
 //   DUAL:   h = silu(X W_gate^T) * (X W_up^T)    128 h columns (256 B rows)
 //   single: y = h W_down^T                        256 output columns
 // with fp32 accumulation; fp8 layers apply the per-row activation scale and
@@ -11,50 +11,55 @@
 // one workgroup.
 //
 // gfx950 design:
-//   - 256 x 256 tile (A 256 rows, B 256 rows), 4 waves, 64 MFMA 16x16 blocks
-//     (256 fp32 accumulators) per wave.  At 128 FLOP per staged byte (bf16)
-//     the operand stream from L2 / the Infinity Cache stays below what the
-//     MFMA rate needs; smaller tiles were bound by that stream.
-//   - Wave layout WM x WN: 2 x 2 (128 x 128 per wave, fewest LDS reads) for
-//     bf16; 1 x 4 (256 rows x 64 B rows per wave) for fp8, whose groups have
-//     ~128 rows, so that all four SIMDs have rows to multiply.
-//   - K is staged in 128-byte chunks (64 bf16 / 128 e4m3 per row) through a
-//     2-stage LDS ring filled by direct-to-LDS loads (global_load_lds_dwordx4):
-//     the next chunk (64 KB per CU) is in flight while this one is multiplied.
-//   - A direct-to-LDS instruction writes 1 KB contiguously (lane i at +16 i);
-//     each lane fetches global chunk c ^ (row & 7) of its row so row r's
-//     chunk c sits in slot c ^ (r & 7).  Fragment reads (16 lanes on 16
-//     consecutive rows, one chunk) with this slot map measured conflict-free
-//     on gfx950 (the row-XOR variant (r ^ r >> 3) & 7 tried first was not).
+//   - Row tile BM x 256 staged B rows, 8 waves (2 per SIMD) laid out 2 x 4.
+//     bf16 (compute-bound prefill groups): BM = 256, 128 x 64 per wave, at
+//     128 FLOP per staged byte the operand stream from L2 stays below what
+//     the MFMA rate needs.  fp8 (~128-row expert groups, memory-bound):
+//     BM = 128, 64 x 64 per wave.
+//   - K is staged in 128-byte chunks (64 bf16 / 128 e4m3 per row) through an
+//     NS-stage LDS ring filled by direct-to-LDS loads (global_load_lds_dwordx4):
+//     bf16 2 stages (64 KB each), fp8 3 stages (48 KB + scales) so that two
+//     chunks are in flight while one is multiplied.
+//   - A direct-to-LDS instruction writes 1 KB contiguously (lane i at +16 i),
+//     8 staged rows; each block of 8 rows lies in A, B0 or B1 and has its own
+//     wave-uniform base.  Each lane fetches global chunk c ^ (row & 7) of its
+//     row so row r's chunk c sits in slot c ^ (r & 7).  Fragment reads (16
+//     lanes on 16 consecutive rows, one chunk) with this slot map measured
+//     conflict-free on gfx950 (the row-XOR variant (r ^ r >> 3) & 7 tried
+//     first was not).
 //   - Blocks are renumbered so each XCD (own L2) takes a contiguous run of
 //     tiles: the column tiles of one row tile, and the row tiles of one
 //     group, run on the same L2 at the same time and share their operands.
-//   - Rows past the group's end are loaded from its last row (finite values)
-//     and never stored; 16-row blocks wholly past the end skip their MFMAs.
+//   - Rows past the group's end are not fetched (8-row blocks wholly past it)
+//     or re-read its last row; they are never stored, and bf16 skips the MFMAs
+//     of 16-row blocks wholly past the end.
 #include "ffn.hpp"
 
 namespace moe {
 namespace {
 
 constexpr int kRB = 128;                          // bytes of K per staged row and chunk
-constexpr int kStages = 2;
-constexpr int kBM = kTileBM;                      // 256 rows per tile
 constexpr int kBRows = 256;                       // staged B rows per tile
-constexpr int kRows = kBM + kBRows;
-constexpr int kStageData = kRows * kRB;           // 64 KB
 constexpr int kMaxKB = 1024;                      // fp8: K <= 131072 (B scales kept in LDS)
 constexpr int kXcds = 8;
-
-static_assert(kBM == 256, "tile geometry below assumes 256 rows");
 
 // Slot of chunk c of staged row r.
 __device__ __forceinline__ int slot(int r, int c) { return c ^ (r & 7); }
 
-// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+// s_waitcnt vmcnt(v) for a runtime v in [0, VMAX] (the count is an immediate),
+// other counters untouched (gfx9 encoding).
+template <int VMAX>
+__device__ __forceinline__ void wait_vmcnt_le(int v) {
+  static_assert(VMAX >= 0 && VMAX < 64, "vmcnt range");
+  if constexpr (VMAX > 0) {
+    if (v >= VMAX) {
+      __builtin_amdgcn_s_waitcnt((VMAX & 15) | ((VMAX >> 4) << 14) | (7 << 4) | (15 << 8));
+      return;
+    }
+    wait_vmcnt_le<VMAX - 1>(v);
+  } else {
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+  }
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -75,15 +80,16 @@ __device__ __forceinline__ u32x4_t lds_read16(const uint8_t* p) {
 // Direct-to-LDS loads of one K chunk into stage `st`: this wave's IPW
 // 1 KB blocks (wave-uniform base + per-lane offsets) and, for fp8, the row
 // scales of the chunk's K block.
-template <int IPW, bool FP8>
-__device__ __forceinline__ void dma_chunk(uint8_t* st, const uint8_t* kbase, const uint32_t (&soff)[IPW],
-                                          int wave, const float* sptr, int nvalid) {
+template <int IPW, bool FP8, int STAGE_DATA>
+__device__ __forceinline__ void dma_chunk(uint8_t* st, const uint8_t* const (&jb)[IPW],
+                                          const uint32_t (&soff)[IPW], const bool (&jv)[IPW],
+                                          size_t koff, int wave, const float* sptr) {
 #pragma unroll
   for (int j = 0; j < IPW; ++j)
-    if (j < nvalid)
-      __builtin_amdgcn_global_load_lds(kbase + soff[j], (lds_ptr_t)(st + (wave * IPW + j) * 1024), 16, 0, 0);
+    if (jv[j])
+      __builtin_amdgcn_global_load_lds(jb[j] + koff + soff[j], (lds_ptr_t)(st + (wave * IPW + j) * 1024), 16, 0, 0);
   if constexpr (FP8)
-    __builtin_amdgcn_global_load_lds(sptr, (lds_ptr_t)(st + kStageData + wave * 256), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(sptr, (lds_ptr_t)(st + STAGE_DATA + wave * 256), 4, 0, 0);
 }
 
 // Staged B row of 16-column block j (lane row r16) for wave column wn.
@@ -96,14 +102,18 @@ __device__ __forceinline__ int b_row(int j, int wn, int r16) {
 
 }  // namespace
 
-template <bool FP8, bool DUAL, int WM, int WN>
+template <bool FP8, bool DUAL, int WM, int WN, int BM, int NS>
 __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
   // The body is device code only; the host pass needs just the launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int kBM = BM;                         // rows per tile
+  constexpr int kStages = NS;
+  constexpr int kStageData = (kBM + kBRows) * kRB;
   constexpr int NW = WM * WN;                     // waves per workgroup
   constexpr int MB = kBM / WM / 16;               // 16-row blocks per wave
   constexpr int NB = kBRows / WN / 16;            // 16-column blocks per wave
   constexpr int IPW = kStageData / 1024 / NW;     // direct-to-LDS instructions per wave and stage
+  static_assert(IPW * NW * 1024 == kStageData, "stage must split evenly over the waves");
   constexpr int SCALE_BYTES = FP8 ? NW * 256 : 0; // fp8 row scales (waves >= 4 load duplicates)
   constexpr int STAGE = kStageData + SCALE_BYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * STAGE + (FP8 ? 2 * kMaxKB * 4 : 16)];
@@ -130,38 +140,36 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
   const int ncols = DUAL ? 128 : min(256, N - n0);
   const int r16 = lane & 15;
 
-  // Sources of the 16-byte chunks this wave moves per stage: a wave-uniform
-  // base (its rows all lie in A, in B0 or in B1) plus a 32-bit lane offset.
-  const int wrow0 = wave * IPW * 8;                // first staged row of this wave
-  const uint8_t* wbase;
+  // Sources of the 1 KB blocks (8 staged rows each) this wave moves per
+  // stage: block b = wave * IPW + j holds rows 8b .. 8b + 7, all in A, in B0
+  // or in B1, so each has a wave-uniform base plus a 32-bit lane offset.  A
+  // blocks wholly past the group's end are not fetched (their LDS rows keep
+  // stale data from earlier chunks; those outputs are never stored).
+  const uint8_t* jb[IPW];
   uint32_t soff[IPW];
-  // 1 KB instructions of this wave that carry valid rows (A rows past the
-  // group's end are not fetched: those LDS rows keep stale finite data from
-  // earlier chunks and their outputs are never stored).
-  int nvalid = IPW;
-  if (wrow0 < kBM) {
-    nvalid = max(0, min(IPW, ceil_div(mrows - wrow0, 8)));
-    // With a_rows the tile's rows are gathered from the unpermuted matrix.
-    wbase = p.a_rows ? p.A : p.A + (size_t)row0 * Kb;
+  bool jv[IPW];
+  int nv = FP8 ? 1 : 0;                            // vm instructions per chunk of this wave
 #pragma unroll
-    for (int j = 0; j < IPW; ++j) {
-      const int row = wrow0 + j * 8 + (lane >> 3);
+  for (int j = 0; j < IPW; ++j) {
+    const int brow0 = (wave * IPW + j) * 8;        // first staged row of the block
+    const int row = brow0 + (lane >> 3);
+    const uint32_t sl = (uint32_t)(slot(row, lane & 7) * 16);
+    if (brow0 < kBM) {
+      jv[j] = brow0 < mrows;
       const int r = min(row, mrows - 1);
-      const uint32_t src = p.a_rows ? (uint32_t)p.a_rows[row0 + r] : (uint32_t)r;
-      soff[j] = src * (uint32_t)Kb + (uint32_t)(slot(row, lane & 7) * 16);
+      // With a_rows the tile's rows are gathered from the unpermuted matrix.
+      jb[j] = p.a_rows ? p.A : p.A + (size_t)row0 * Kb;
+      soff[j] = (p.a_rows ? (uint32_t)p.a_rows[row0 + r] : (uint32_t)r) * (uint32_t)Kb + sl;
+    } else {
+      int br = brow0 - kBM;
+      const uint8_t* B = p.B0;
+      if (DUAL && br >= 128) { B = p.B1; br -= 128; }
+      jv[j] = true;
+      jb[j] = B + (size_t)g * N * Kb;
+      // Rows past the matrix (ragged last column tile) re-read its last row.
+      soff[j] = (uint32_t)min(n0 + br + (lane >> 3), N - 1) * (uint32_t)Kb + sl;
     }
-  } else {
-    int bw = wrow0 - kBM;                          // first B row of this wave
-    const uint8_t* B = p.B0;
-    if (DUAL && bw >= 128) { B = p.B1; bw -= 128; }
-    // Rows past the matrix (ragged last column tile) re-read its last row.
-    wbase = B + (size_t)g * N * Kb;
-#pragma unroll
-    for (int j = 0; j < IPW; ++j) {
-      const int row = wrow0 + j * 8 + (lane >> 3);
-      const int n = min(n0 + bw + j * 8 + (lane >> 3), N - 1);
-      soff[j] = (uint32_t)n * (uint32_t)Kb + (uint32_t)(slot(row, lane & 7) * 16);
-    }
+    nv += jv[j] ? 1 : 0;
   }
   const float* ssrc = nullptr;
   float* bsc = reinterpret_cast<float*>(lds + kStages * STAGE);   // fp8: [2][KB] B block scales
@@ -196,13 +204,20 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
   // multiplies every row block (rows past the group's end hold finite copies
   // of its last row and are never stored).
   constexpr bool FULL = FP8;
-  dma_chunk<IPW, FP8>(lds, wbase, soff, wave, ssrc, nvalid);
+#pragma unroll
+  for (int c = 0; c < NS - 1; ++c)
+    if (c < nk)
+      dma_chunk<IPW, FP8, kStageData>(lds + c * STAGE, jb, soff, jv, (size_t)c * kRB, wave,
+                                      FP8 ? ssrc + c : nullptr);
   for (int kc = 0; kc < nk; ++kc) {
-    wait_vmcnt<0>();        // this wave's share of chunk kc has landed
+    // Chunks kc + 1 .. kc + NS - 2 may stay in flight (nv instructions each);
+    // chunk kc must have landed.
+    wait_vmcnt_le<(NS - 2) * (IPW + 1)>(min(NS - 2, nk - 1 - kc) * nv);
     lds_barrier();          // every wave's share, and every wave is done with chunk kc - 1
-    if (kc + 1 < nk)      // into the stage of chunk kc - 1
-      dma_chunk<IPW, FP8>(lds + ((kc + 1) % kStages) * STAGE, wbase + (size_t)(kc + 1) * kRB, soff,
-                          wave, FP8 ? ssrc + kc + 1 : nullptr, nvalid);
+    if (kc + NS - 1 < nk)   // into the stage of chunk kc - 1
+      dma_chunk<IPW, FP8, kStageData>(lds + ((kc + NS - 1) % kStages) * STAGE, jb, soff, jv,
+                                      (size_t)(kc + NS - 1) * kRB, wave,
+                                      FP8 ? ssrc + kc + NS - 1 : nullptr);
     if (!active) continue;
     const uint8_t* As = lds + (kc % kStages) * STAGE;
     const uint8_t* Bs = As + kBM * kRB;
@@ -355,10 +370,13 @@ hipError_t launch_tiled(const char* name, bool fp8, bool dual, long long blocks,
   if (blocks <= 0) return hipSuccess;
   // The XCD renumbering needs up to kXcds - 1 blocks past the valid ones.
   const dim3 grid((unsigned)((blocks + 2 * kXcds - 1) / kXcds * kXcds));
-  if (fp8 && dual) MOE_LAUNCH(name, (k_tiled3<true, true, 2, 4>), grid, dim3(512), 0, s, a);
-  else if (fp8) MOE_LAUNCH(name, (k_tiled3<true, false, 2, 4>), grid, dim3(512), 0, s, a);
-  else if (dual) MOE_LAUNCH(name, (k_tiled3<false, true, 2, 4>), grid, dim3(512), 0, s, a);
-  else MOE_LAUNCH(name, (k_tiled3<false, false, 2, 4>), grid, dim3(512), 0, s, a);
+  // bf16 (compute-bound prefill groups): 256-row tiles, 2 stages.  fp8
+  // (memory-bound ~128-row groups): 128-row tiles, 3 stages, two chunks in
+  // flight.  The row counts match tile_rows() used by the schedule.
+  if (fp8 && dual) MOE_LAUNCH(name, (k_tiled3<true, true, 2, 4, 128, 3>), grid, dim3(512), 0, s, a);
+  else if (fp8) MOE_LAUNCH(name, (k_tiled3<true, false, 2, 4, 128, 3>), grid, dim3(512), 0, s, a);
+  else if (dual) MOE_LAUNCH(name, (k_tiled3<false, true, 2, 4, 256, 2>), grid, dim3(512), 0, s, a);
+  else MOE_LAUNCH(name, (k_tiled3<false, false, 2, 4, 256, 2>), grid, dim3(512), 0, s, a);
   return hipSuccess;
 }
 
