@@ -36,9 +36,11 @@ SIGNATURES = {
     "moe_abi_version": (ctypes.c_int, []),
     "moe_forward_workspace_bytes": (_SZ, [_SP]),
     "moe_ffn_workspace_bytes": (_SZ, [_SP]),
-    "moe_route": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_route_workspace_bytes": (_SZ, [_SP]),
+    "moe_route": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_route_from_logits": (ctypes.c_int, [_SP, _P, _P, _P, _P]),
-    "moe_permute": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_permute_workspace_bytes": (_SZ, [_SP]),
+    "moe_permute": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_grouped_ffn": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_combine": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P]),
     "moe_forward": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -84,6 +86,10 @@ def shape_of(cfg) -> MoeShape:
     return make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.n_shared, cfg.wdtype)
 
 
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size() if t is not None else 0
+
+
 def _ptr(t):
     if t is None:
         return None
@@ -122,9 +128,15 @@ def moe_ffn_workspace_bytes(shape: MoeShape) -> int:
     return lib().moe_ffn_workspace_bytes(ctypes.byref(shape))
 
 
-def moe_route(shape, x, w_router, router_bias, logits, topk_idx, topk_w, stream=None):
+def moe_route_workspace_bytes(shape: MoeShape) -> int:
+    return lib().moe_route_workspace_bytes(ctypes.byref(shape))
+
+
+def moe_route(shape, x, w_router, router_bias, logits, topk_idx, topk_w, workspace=None,
+              stream=None):
     _check(lib().moe_route(ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(router_bias),
-                           _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _stream(stream)), "moe_route")
+                           _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(workspace),
+                           _nbytes(workspace), _stream(stream)), "moe_route")
 
 
 def moe_route_from_logits(shape, logits, topk_idx, topk_w, stream=None):
@@ -132,11 +144,16 @@ def moe_route_from_logits(shape, logits, topk_idx, topk_w, stream=None):
                                        _ptr(topk_w), _stream(stream)), "moe_route_from_logits")
 
 
+def moe_permute_workspace_bytes(shape: MoeShape) -> int:
+    return lib().moe_permute_workspace_bytes(ctypes.byref(shape))
+
+
 def moe_permute(shape, topk_idx, x, counts, offsets, dest, src_row, x_perm, x_perm_scale,
-                stream=None):
+                workspace=None, stream=None):
     _check(lib().moe_permute(ctypes.byref(shape), _ptr(topk_idx), _ptr(x), _ptr(counts),
                              _ptr(offsets), _ptr(dest), _ptr(src_row), _ptr(x_perm),
-                             _ptr(x_perm_scale), _stream(stream)), "moe_permute")
+                             _ptr(x_perm_scale), _ptr(workspace), _nbytes(workspace),
+                             _stream(stream)), "moe_permute")
 
 
 def moe_grouped_ffn(shape, offsets, x_perm, x_perm_scale, w_gate, w_up, w_down, s_gate, s_up,

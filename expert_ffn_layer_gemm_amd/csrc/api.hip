@@ -47,8 +47,8 @@ int check_shape(const char* fn, const moe_shape* s, bool need_ffn_dims) {
     return fail(MOE_ERR_UNSUPPORTED, "%s: n_shared=%d not 0 or 1", fn, s->n_shared);
   if ((long long)s->T * (s->k + s->n_shared) >= (1LL << 31))
     return fail(MOE_ERR_UNSUPPORTED, "%s: T*(k+n_shared) >= 2^31", fn);
-  if (s->H < 128 || s->H % 128)
-    return fail(MOE_ERR_UNSUPPORTED, "%s: H=%d not a positive multiple of 128", fn, s->H);
+  if (s->H < 128 || s->H % 128 || s->H > 131072)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: H=%d not a multiple of 128 in [128, 131072]", fn, s->H);
   if (need_ffn_dims && (s->I < 128 || s->I % 128))
     return fail(MOE_ERR_UNSUPPORTED, "%s: I=%d not a positive multiple of 128", fn, s->I);
   // One expert matrix must stay below 4 GB (32-bit in-matrix offsets) and K
@@ -66,7 +66,7 @@ size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 // forward path never builds x_perm: the GEMMs gather their rows through
 // src_row from x (bf16) or from x quantised once per token (fp8: xq, xs).
 struct FwdLayout {
-  size_t logits, idx, w, counts, offsets, dest, src_row, xq, xs, y_perm, ffn, total;
+  size_t logits, rpart, idx, w, counts, offsets, tcnt, dest, src_row, xq, xs, y_perm, ffn, total;
 };
 
 FwdLayout fwd_layout(const moe_shape* s) {
@@ -76,10 +76,12 @@ FwdLayout fwd_layout(const moe_shape* s) {
   FwdLayout L{};
   size_t off = 0;
   L.logits = off;  off += align256(T * E * 4);
+  L.rpart = off;   off += align256(moe::router_workspace_bytes(s->T, s->H, s->E));
   L.idx = off;     off += align256(T * k * 4);
   L.w = off;       off += align256(T * k * 4);
   L.counts = off;  off += align256(G * 4);
   L.offsets = off; off += align256((G + 1) * 4);
+  L.tcnt = off;    off += align256(moe::permute_workspace_bytes(s->T, s->E));
   L.dest = off;    off += align256(T * k * 4);
   L.src_row = off; off += align256(R * 4);
   L.xq = off;      off += fp8 ? align256(T * H) : 0;
@@ -97,7 +99,7 @@ extern "C" {
 
 const char* moe_last_error(void) { return g_err; }
 
-int moe_abi_version(void) { return 1; }
+int moe_abi_version(void) { return 2; }
 
 size_t moe_forward_workspace_bytes(const moe_shape* shape) {
   if (check_shape("moe_forward_workspace_bytes", shape, true) != MOE_OK) return 0;
@@ -110,9 +112,14 @@ size_t moe_ffn_workspace_bytes(const moe_shape* shape) {
                                   shape->n_shared, shape->wdtype == MOE_FP8_E4M3_BLOCK128);
 }
 
+size_t moe_route_workspace_bytes(const moe_shape* shape) {
+  if (check_shape("moe_route_workspace_bytes", shape, false) != MOE_OK) return 0;
+  return moe::router_workspace_bytes(shape->T, shape->H, shape->E);
+}
+
 int moe_route(const moe_shape* shape, const void* x, const float* w_router,
               const float* router_bias, float* logits, int32_t* topk_idx, float* topk_w,
-              void* stream) {
+              void* workspace, size_t ws_bytes, void* stream) {
   const char* fn = "moe_route";
   moe::prof_call_begin();
   if (int rc = check_shape(fn, shape, false)) return rc;
@@ -124,10 +131,18 @@ int moe_route(const moe_shape* shape, const void* x, const float* w_router,
   MOE_NEED_PTR(topk_w);
   if (router_bias && !aligned16(router_bias))
     return fail(MOE_ERR_INVALID_ARG, "%s: router_bias not 16-byte aligned", fn);
-  hipError_t e = moe::launch_router_gemm(static_cast<const uint16_t*>(x), w_router, router_bias,
-                                         logits, shape->T, shape->H, shape->E, as_stream(stream));
+  const size_t need = moe::router_workspace_bytes(shape->T, shape->H, shape->E);
+  if (need > 0 && (workspace == nullptr || ws_bytes < need))
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
+  if (need > 0 && !aligned16(workspace))
+    return fail(MOE_ERR_INVALID_ARG, "%s: workspace not 16-byte aligned", fn);
+  const int ks = moe::router_splits(shape->T, shape->H, shape->E);
+  float* parts = ks > 1 ? static_cast<float*>(workspace) : logits;
+  hipError_t e = moe::launch_router_gemm(static_cast<const uint16_t*>(x), w_router, parts,
+                                         shape->T, shape->H, shape->E, as_stream(stream));
   if (e == hipSuccess)
-    e = moe::launch_topk(logits, topk_idx, topk_w, shape->T, shape->E, shape->k, as_stream(stream));
+    e = moe::launch_topk(parts, ks, router_bias, logits, topk_idx, topk_w, shape->T, shape->E,
+                         shape->k, as_stream(stream));
   return hip_status(e, fn);
 }
 
@@ -144,13 +159,19 @@ int moe_route_from_logits(const moe_shape* shape, const float* logits, int32_t* 
   MOE_NEED_PTR(logits);
   MOE_NEED_PTR(topk_idx);
   MOE_NEED_PTR(topk_w);
-  return hip_status(moe::launch_topk(logits, topk_idx, topk_w, shape->T, shape->E, shape->k,
+  return hip_status(moe::launch_topk(logits, 1, nullptr, nullptr, topk_idx, topk_w, shape->T,
+                                     shape->E, shape->k,
                                      as_stream(stream)), fn);
+}
+
+size_t moe_permute_workspace_bytes(const moe_shape* shape) {
+  if (check_shape("moe_permute_workspace_bytes", shape, false) != MOE_OK) return 0;
+  return moe::permute_workspace_bytes(shape->T, shape->E);
 }
 
 int moe_permute(const moe_shape* shape, const int32_t* topk_idx, const void* x, int32_t* counts,
                 int32_t* offsets, int32_t* dest, int32_t* src_row, void* x_perm,
-                float* x_perm_scale, void* stream) {
+                float* x_perm_scale, void* workspace, size_t ws_bytes, void* stream) {
   const char* fn = "moe_permute";
   moe::prof_call_begin();
   if (int rc = check_shape(fn, shape, false)) return rc;
@@ -165,8 +186,14 @@ int moe_permute(const moe_shape* shape, const int32_t* topk_idx, const void* x, 
     MOE_NEED_PTR(x_perm);
     if (fp8) MOE_NEED_PTR(x_perm_scale);
   }
+  const size_t need = moe::permute_workspace_bytes(shape->T, shape->E);
+  if (need > 0 && (workspace == nullptr || ws_bytes < need))
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
+  if (need > 0 && !aligned16(workspace))
+    return fail(MOE_ERR_INVALID_ARG, "%s: workspace not 16-byte aligned", fn);
   return hip_status(moe::launch_permute(topk_idx, static_cast<const uint16_t*>(x), counts, offsets,
-                                        dest, src_row, x_perm, x_perm_scale, shape->T, shape->H,
+                                        dest, src_row, x_perm, x_perm_scale,
+                                        static_cast<int32_t*>(workspace), shape->T, shape->H,
                                         shape->E, shape->k, shape->n_shared, fp8,
                                         as_stream(stream)), fn);
 }
@@ -267,13 +294,18 @@ int moe_forward(const moe_shape* shape, const void* x, const float* w_router,
   void* y_perm = ws + L.y_perm;
   hipStream_t s = as_stream(stream);
 
-  hipError_t e = moe::launch_router_gemm(static_cast<const uint16_t*>(x), w_router, router_bias,
-                                         logits, shape->T, shape->H, shape->E, s);
-  if (e == hipSuccess) e = moe::launch_topk(logits, idx, w, shape->T, shape->E, shape->k, s);
+  // Router: slice partial sums (or, unsplit, the raw products in the logits
+  // buffer), reduced in slice order by the top-k kernel.
+  const int ks = moe::router_splits(shape->T, shape->H, shape->E);
+  float* parts = ks > 1 ? reinterpret_cast<float*>(ws + L.rpart) : logits;
+  hipError_t e = moe::launch_router_gemm(static_cast<const uint16_t*>(x), w_router, parts,
+                                         shape->T, shape->H, shape->E, s);
+  if (e == hipSuccess)
+    e = moe::launch_topk(parts, ks, router_bias, nullptr, idx, w, shape->T, shape->E, shape->k, s);
   if (e == hipSuccess)   // routing tables only: no row copy
     e = moe::launch_permute(idx, static_cast<const uint16_t*>(x), counts, offsets, dest, src_row,
-                            nullptr, nullptr, shape->T, shape->H, shape->E, shape->k,
-                            shape->n_shared, fp8, s);
+                            nullptr, nullptr, reinterpret_cast<int32_t*>(ws + L.tcnt), shape->T,
+                            shape->H, shape->E, shape->k, shape->n_shared, fp8, s);
   if (e == hipSuccess && fp8)
     e = moe::launch_quantize_rows(static_cast<const uint16_t*>(x), xq, xs, shape->T, shape->H, s);
   if (e == hipSuccess) {

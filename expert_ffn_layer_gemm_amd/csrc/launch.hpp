@@ -22,17 +22,26 @@ void prof_after(hipStream_t s);
   } while (0)
 
 // route.hip
-hipError_t launch_router_gemm(const uint16_t* x, const float* w, const float* bias, float* logits,
-                              int T, int H, int E, hipStream_t s);
-hipError_t launch_topk(const float* logits, int32_t* idx, float* w, int T, int E, int k,
-                       hipStream_t s);
+// The router GEMM splits H into router_splits() slices and writes their
+// partial sums to parts [KS][T][E] (KS == 1: parts may be the logits buffer);
+// router_workspace_bytes() is the size of parts when KS > 1, else 0.
+int router_splits(int T, int H, int E);
+size_t router_workspace_bytes(int T, int H, int E);
+hipError_t launch_router_gemm(const uint16_t* x, const float* w, float* parts, int T, int H, int E,
+                              hipStream_t s);
+// Logits = sum of the KS partial planes in order (+ bias), written to
+// logits_out when non-null (may alias parts when KS == 1), then top-k.
+hipError_t launch_topk(const float* parts, int KS, const float* bias, float* logits_out,
+                       int32_t* idx, float* w, int T, int E, int k, hipStream_t s);
 
 // permute.hip
+// tile_cnt: permute_workspace_bytes(T, E) of device scratch (per-tile counts).
 // x_perm == nullptr skips the row copy (the GEMMs then gather rows through src_row).
+size_t permute_workspace_bytes(int T, int E);
 hipError_t launch_permute(const int32_t* topk_idx, const uint16_t* x, int32_t* counts,
                           int32_t* offsets, int32_t* dest, int32_t* src_row, void* x_perm,
-                          float* x_perm_scale, int T, int H, int E, int k, int n_shared, bool fp8,
-                          hipStream_t s);
+                          float* x_perm_scale, int32_t* tile_cnt, int T, int H, int E, int k,
+                          int n_shared, bool fp8, hipStream_t s);
 // Per-token e4m3 quantisation of x (128-channel groups): the rows the fp8
 // GEMMs gather through src_row.
 hipError_t launch_quantize_rows(const uint16_t* x, uint8_t* xq, float* xs, int T, int H,

@@ -10,29 +10,55 @@
 //     (one bit per token of a 256-token tile per expert) with popcounts, instead
 //     of atomically incremented counters, so dest / src_row / x_perm are
 //     identical from run to run;
-//   - three launches: one workgroup builds counts + offsets (LDS histogram and
-//     a wave-level prefix scan), a tile grid assigns ranks, and a wide grid
-//     gathers rows (x_perm[r] = x[src_row[r]], 16-byte lanes), quantising each
-//     128-channel group to e4m3fn on the way for fp8 layers.
+//   - four launches: per-tile histograms (256-token tiles, LDS atomics), one
+//     workgroup turning them into per-tile bases, counts and offsets (wave-level
+//     prefix scan), a tile grid assigning ranks, and a wide grid gathering rows
+//     (x_perm[r] = x[src_row[r]], 16-byte lanes), quantising each 128-channel
+//     group to e4m3fn on the way for fp8 layers.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace moe {
 
 
-// Counts per group and their exclusive prefix sum; one workgroup of 1024.
-__global__ __launch_bounds__(1024) void k_hist_scan(const int32_t* __restrict__ idx,
-                                                    int32_t* __restrict__ counts,
-                                                    int32_t* __restrict__ offsets, int T, int E,
-                                                    int k, int n_shared) {
+constexpr int kRankTile = 256;   // tokens per tile of the histogram and rank kernels
+
+// Routings per expert inside each 256-token tile: tile_cnt[tile][e].
+__global__ __launch_bounds__(kRankTile) void k_tile_hist(const int32_t* __restrict__ idx,
+                                                         int32_t* __restrict__ tile_cnt, int T,
+                                                         int E, int k) {
+  __shared__ int cnt[1024];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < E; i += kRankTile) cnt[i] = 0;
+  __syncthreads();
+  const int t = blockIdx.x * kRankTile + tid;
+  if (t < T)
+    for (int j = 0; j < k; ++j) atomicAdd(&cnt[idx[(size_t)t * k + j]], 1);
+  __syncthreads();
+  for (int i = tid; i < E; i += kRankTile) tile_cnt[(size_t)blockIdx.x * E + i] = cnt[i];
+}
+
+// One workgroup of 1024: turns tile_cnt into each tile's base row inside
+// every expert's group (routings of that expert in earlier tiles, in place),
+// then counts per group and their exclusive prefix sum.
+__global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ tile_cnt, int n_tiles,
+                                               int32_t* __restrict__ counts,
+                                               int32_t* __restrict__ offsets, int T, int E,
+                                               int n_shared) {
   __shared__ int cnt[2048];
   __shared__ int wave_sum[16];
   const int tid = threadIdx.x, G = E + n_shared;
   for (int i = tid; i < 2048; i += 1024) cnt[i] = 0;
   __syncthreads();
-  const long long n = (long long)T * k;
-  for (long long i = tid; i < n; i += 1024) atomicAdd(&cnt[idx[i]], 1);
-  __syncthreads();
+  if (tid < E) {
+    int run = 0;
+    for (int b = 0; b < n_tiles; ++b) {
+      const int c = tile_cnt[(size_t)b * E + tid];
+      tile_cnt[(size_t)b * E + tid] = run;
+      run += c;
+    }
+    cnt[tid] = run;
+  }
   if (tid == 0 && n_shared) cnt[E] = T;
   __syncthreads();
   // Each thread owns entries 2*tid and 2*tid + 1.
@@ -55,24 +81,20 @@ __global__ __launch_bounds__(1024) void k_hist_scan(const int32_t* __restrict__ 
   if (2 * tid + 1 == G) offsets[G] = excl + a;
 }
 
-// Token-ascending rank of every (t, j) inside its expert's group.
-constexpr int kRankTile = 256;
+// Token-ascending rank of every (t, j) inside its expert's group: the tile's
+// base (k_scan) plus the routings of earlier tokens of the tile, counted from
+// an LDS bit mask per expert (one bit per token of the tile).
 __global__ __launch_bounds__(kRankTile) void k_rank(const int32_t* __restrict__ idx,
                                                     const int32_t* __restrict__ offsets,
+                                                    const int32_t* __restrict__ tile_base,
                                                     int32_t* __restrict__ dest,
                                                     int32_t* __restrict__ src_row, int T, int E,
                                                     int k, int n_shared) {
-  __shared__ int base[1024];
   __shared__ uint32_t mask[1024 * (kRankTile / 32)];
   const int tid = threadIdx.x;
-  const int t0 = blockIdx.x * kRankTile;
-  for (int i = tid; i < E; i += kRankTile) base[i] = 0;
   for (int i = tid; i < E * (kRankTile / 32); i += kRankTile) mask[i] = 0u;
   __syncthreads();
-  // Routings of every token before this tile.
-  const long long before = (long long)t0 * k;
-  for (long long i = tid; i < before; i += kRankTile) atomicAdd(&base[idx[i]], 1);
-  const int t = t0 + tid;
+  const int t = blockIdx.x * kRankTile + tid;
   const bool valid = t < T;
   const int word = tid >> 5;
   const uint32_t bit = 1u << (tid & 31);
@@ -80,6 +102,7 @@ __global__ __launch_bounds__(kRankTile) void k_rank(const int32_t* __restrict__ 
     for (int j = 0; j < k; ++j) atomicOr(&mask[idx[(size_t)t * k + j] * (kRankTile / 32) + word], bit);
   __syncthreads();
   if (!valid) return;
+  const int32_t* base = tile_base + (size_t)blockIdx.x * E;
   for (int j = 0; j < k; ++j) {
     const int e = idx[(size_t)t * k + j];
     const uint32_t* m = mask + e * (kRankTile / 32);
@@ -140,15 +163,23 @@ __global__ __launch_bounds__(256) void k_gather_fp8(const int32_t* __restrict__ 
   }
 }
 
+size_t permute_workspace_bytes(int T, int E) {
+  return (size_t)ceil_div(T, kRankTile) * E * sizeof(int32_t);
+}
+
 hipError_t launch_permute(const int32_t* topk_idx, const uint16_t* x, int32_t* counts,
                           int32_t* offsets, int32_t* dest, int32_t* src_row, void* x_perm,
-                          float* x_perm_scale, int T, int H, int E, int k, int n_shared, bool fp8,
-                          hipStream_t s) {
-  MOE_LAUNCH("hist_scan", k_hist_scan, dim3(1), dim3(1024), 0, s, topk_idx, counts, offsets, T, E, k,
-                     n_shared);
+                          float* x_perm_scale, int32_t* tile_cnt, int T, int H, int E, int k,
+                          int n_shared, bool fp8, hipStream_t s) {
+  const int n_tiles = ceil_div(T, kRankTile);
+  if (T > 0)
+    MOE_LAUNCH("tile_hist", k_tile_hist, dim3(n_tiles), dim3(kRankTile), 0, s, topk_idx, tile_cnt,
+               T, E, k);
+  MOE_LAUNCH("scan", k_scan, dim3(1), dim3(1024), 0, s, tile_cnt, n_tiles, counts, offsets, T, E,
+             n_shared);
   if (T == 0) return hipGetLastError();
-  MOE_LAUNCH("rank", k_rank, dim3(ceil_div(T, kRankTile)), dim3(kRankTile), 0, s, topk_idx, offsets,
-                     dest, src_row, T, E, k, n_shared);
+  MOE_LAUNCH("rank", k_rank, dim3(n_tiles), dim3(kRankTile), 0, s, topk_idx, offsets, tile_cnt,
+             dest, src_row, T, E, k, n_shared);
   if (x_perm == nullptr) return hipGetLastError();
   const int R = T * (k + n_shared);
   const dim3 grid(ceil_div(R, kGatherRows));

@@ -1,0 +1,54 @@
+// Building blocks of the LDS-staged kernels (tiled grouped GEMM, router
+// GEMM): direct-to-LDS loads, explicit vm-counter waits and an LDS-only
+// workgroup barrier.
+#pragma once
+
+#include "common.hpp"
+
+namespace moe {
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Slot of 16-byte chunk c of staged row r, for rows of 8 chunks (128 B) and
+// of 16 chunks (256 B).  A direct-to-LDS instruction writes 1 KB
+// contiguously (lane i at +16 i), so each lane fetches the global chunk that
+// belongs in its slot; fragment reads (16 lanes on 16 consecutive rows, one
+// chunk) then fall on distinct banks.  Measured conflict-free on gfx950.
+__device__ __forceinline__ int slot8(int r, int c) { return c ^ (r & 7); }
+__device__ __forceinline__ int slot16(int r, int c) { return c ^ (r & 15); }
+
+// s_waitcnt vmcnt(v) for a runtime v in [0, VMAX] (the count is an immediate),
+// other counters untouched (gfx9 encoding).
+template <int VMAX>
+__device__ __forceinline__ void wait_vmcnt_le(int v) {
+  static_assert(VMAX >= 0 && VMAX < 64, "vmcnt range");
+  if constexpr (VMAX > 0) {
+    if (v >= VMAX) {
+      __builtin_amdgcn_s_waitcnt((VMAX & 15) | ((VMAX >> 4) << 14) | (7 << 4) | (15 << 8));
+      return;
+    }
+    wait_vmcnt_le<VMAX - 1>(v);
+  } else {
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+  }
+}
+
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() would also
+// wait for every outstanding vector-memory operation, including the
+// direct-to-LDS loads of later chunks, and drain the pipeline; completion of
+// the chunk about to be read is awaited explicitly with wait_vmcnt_le instead.
+// The memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ u32x4_t lds_read16(const uint8_t* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+// One 1 KB direct-to-LDS block: lane i copies 16 bytes from src to dst + 16 i.
+__device__ __forceinline__ void dma16(const void* src, uint8_t* dst_block) {
+  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)dst_block, 16, 0, 0);
+}
+
+}  // namespace moe

@@ -34,6 +34,7 @@
 //     or re-read its last row; they are never stored, and bf16 skips the MFMAs
 //     of 16-row blocks wholly past the end.
 #include "ffn.hpp"
+#include "pipe.hpp"
 
 namespace moe {
 namespace {
@@ -43,39 +44,7 @@ constexpr int kBRows = 256;                       // staged B rows per tile
 constexpr int kMaxKB = 1024;                      // fp8: K <= 131072 (B scales kept in LDS)
 constexpr int kXcds = 8;
 
-// Slot of chunk c of staged row r.
-__device__ __forceinline__ int slot(int r, int c) { return c ^ (r & 7); }
-
-// s_waitcnt vmcnt(v) for a runtime v in [0, VMAX] (the count is an immediate),
-// other counters untouched (gfx9 encoding).
-template <int VMAX>
-__device__ __forceinline__ void wait_vmcnt_le(int v) {
-  static_assert(VMAX >= 0 && VMAX < 64, "vmcnt range");
-  if constexpr (VMAX > 0) {
-    if (v >= VMAX) {
-      __builtin_amdgcn_s_waitcnt((VMAX & 15) | ((VMAX >> 4) << 14) | (7 << 4) | (15 << 8));
-      return;
-    }
-    wait_vmcnt_le<VMAX - 1>(v);
-  } else {
-    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
-  }
-}
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// Workgroup barrier that orders LDS accesses only.  __syncthreads() would also
-// wait for every outstanding vector-memory operation, including the
-// direct-to-LDS loads of the next chunk, and drain the pipeline; completion of
-// the chunk about to be read is awaited explicitly with wait_vmcnt instead.
-// The memory clobber keeps the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-__device__ __forceinline__ u32x4_t lds_read16(const uint8_t* p) {
-  return *reinterpret_cast<const u32x4_t*>(p);
-}
+__device__ __forceinline__ int slot(int r, int c) { return slot8(r, c); }
 
 // Direct-to-LDS loads of one K chunk into stage `st`: this wave's IPW
 // 1 KB blocks (wave-uniform base + per-lane offsets) and, for fp8, the row
@@ -87,7 +56,7 @@ __device__ __forceinline__ void dma_chunk(uint8_t* st, const uint8_t* const (&jb
 #pragma unroll
   for (int j = 0; j < IPW; ++j)
     if (jv[j])
-      __builtin_amdgcn_global_load_lds(jb[j] + koff + soff[j], (lds_ptr_t)(st + (wave * IPW + j) * 1024), 16, 0, 0);
+      dma16(jb[j] + koff + soff[j], st + (wave * IPW + j) * 1024);
   if constexpr (FP8)
     __builtin_amdgcn_global_load_lds(sptr, (lds_ptr_t)(st + STAGE_DATA + wave * 256), 4, 0, 0);
 }

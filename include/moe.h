@@ -90,26 +90,39 @@ size_t moe_forward_workspace_bytes(const moe_shape* shape);
    on-device tile schedule).  Returns 0 for an unsupported shape. */
 size_t moe_ffn_workspace_bytes(const moe_shape* shape);
 
+/* Bytes of device workspace moe_route needs for `shape` (0 when the router
+   GEMM runs unsplit; then workspace may be NULL).  Only T, H and E are read;
+   returns 0 for an unsupported shape as well. */
+size_t moe_route_workspace_bytes(const moe_shape* shape);
+
 /*
  * Router: logits = x W_r^T (+ router_bias), then top-k and renormalised
  * softmax weights (DeepSeek-deployment page, MoE Router).
  *   x           [T, H] bf16
  *   w_router    [E, H] fp32 (torch Linear layout)
  *   router_bias [E] fp32 or NULL (added to every token's logits)
- *   logits      [T, E] fp32, written (required: the top-k reads it back)
+ *   logits      [T, E] fp32, written
  *   topk_idx    [T, k] int32, written: slot j holds the j-th largest logit;
  *               equal logits (+0 == -0) go to the lower expert index
  *   topk_w      [T, k] fp32, written: exp(l_j - l_0) / sum_j' exp(l_j' - l_0)
- * Logits must be finite (a NaN logit gives unspecified routing).
+ *   workspace   >= moe_route_workspace_bytes(shape) bytes of device memory,
+ *               16-byte aligned (partial sums over slices of H); caller-owned
+ * Logits are fp32 sums of exact products, over slices of H added in a fixed
+ * order: the same inputs give the same bits on every call.  Logits must be
+ * finite (a NaN logit gives unspecified routing).  H <= 131072.
  */
 int moe_route(const moe_shape* shape, const void* x, const float* w_router,
               const float* router_bias, float* logits, int32_t* topk_idx,
-              float* topk_w, void* stream);
+              float* topk_w, void* workspace, size_t ws_bytes, void* stream);
 
 /* Top-k + weights alone, from caller-given fp32 logits [T, E] (same rules as
    moe_route).  Only T, E and k of `shape` are read. */
 int moe_route_from_logits(const moe_shape* shape, const float* logits,
                           int32_t* topk_idx, float* topk_w, void* stream);
+
+/* Bytes of device workspace moe_permute needs (ceil(T/256) * E int32).  Only
+   T and E are read; returns 0 for an unsupported shape as well. */
+size_t moe_permute_workspace_bytes(const moe_shape* shape);
 
 /*
  * Dispatch ("CuTeDSL at Perplexity", MoE Dispatch/Combine, local kernel):
@@ -127,12 +140,16 @@ int moe_route_from_logits(const moe_shape* shape, const float* logits,
  *                per 128 channels (scale = amax / 448, 1 for an all-zero group,
  *                codes rounded to nearest even after clamping to +-448)
  *   x_perm_scale [R, H/128] fp32, written for fp8 (NULL for bf16)
- * Routing entries outside [0, E) make the results unspecified.
+ *   workspace    >= moe_permute_workspace_bytes(shape) bytes of device memory,
+ *                16-byte aligned (per-tile expert counts); caller-owned
+ * Ranks come from counts and bit masks, not atomic counters: the same routing
+ * gives the same dest / src_row on every call.  Routing entries outside
+ * [0, E) make the results unspecified.
  */
 int moe_permute(const moe_shape* shape, const int32_t* topk_idx, const void* x,
                 int32_t* counts, int32_t* offsets, int32_t* dest,
                 int32_t* src_row, void* x_perm, float* x_perm_scale,
-                void* stream);
+                void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * Grouped expert FFN over the permuted rows (Qwen3.5-397B on Ironwood, section

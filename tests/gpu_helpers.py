@@ -44,7 +44,8 @@ def run_route(cfg, li):
     logits = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=DEV)
     idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=DEV)
     w = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=DEV)
-    moe.moe_route(sh, li.x, li.w_router, li.router_bias, logits, idx, w)
+    ws = torch.empty(max(moe.moe_route_workspace_bytes(sh), 16), dtype=torch.uint8, device=DEV)
+    moe.moe_route(sh, li.x, li.w_router, li.router_bias, logits, idx, w, ws)
     torch.cuda.synchronize()
     return logits, idx, w
 
@@ -59,7 +60,8 @@ def run_permute(cfg, idx, x):
     src = torch.empty(R, dtype=torch.int32, device=DEV)
     x_perm = torch.empty((R, cfg.H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=DEV)
     x_scale = torch.empty((R, cfg.H // 128), dtype=torch.float32, device=DEV) if fp8 else None
-    moe.moe_permute(sh, idx, x, counts, offsets, dest, src, x_perm, x_scale)
+    ws = torch.empty(max(moe.moe_permute_workspace_bytes(sh), 16), dtype=torch.uint8, device=DEV)
+    moe.moe_permute(sh, idx, x, counts, offsets, dest, src, x_perm, x_scale, ws)
     torch.cuda.synchronize()
     return counts, offsets, dest, src, x_perm, x_scale
 

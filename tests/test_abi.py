@@ -37,7 +37,7 @@ def test_shape_struct_matches_header():
 
 
 def test_abi_version():
-    assert moe.moe_abi_version() == 1
+    assert moe.moe_abi_version() == 2
 
 
 FAKE = 0x10000  # a non-NULL, aligned address; never dereferenced (validation fails first)
@@ -50,6 +50,8 @@ def _call(fn, *args):
 def test_workspace_sizes_and_bad_shapes():
     good = moe.make_shape(64, 4096, 128, 8, 1536)
     assert moe.moe_forward_workspace_bytes(good) > moe.moe_ffn_workspace_bytes(good) > 64 * 8 * 1536 * 2
+    r = moe.moe_route_workspace_bytes(good)          # partial sums [KS][T][E] fp32, or none
+    assert r >= 0 and r % (64 * 128 * 4) == 0
     fp8 = moe.make_shape(4096, 7168, 256, 8, 2048, 1, "fp8")
     assert moe.moe_ffn_workspace_bytes(fp8) >= 4096 * 9 * 2048
     for bad in (moe.make_shape(64, 100, 128, 8, 1536), moe.make_shape(64, 4096, 128, 8, 100),
@@ -64,15 +66,18 @@ def test_error_codes_before_launch():
     sh = moe.make_shape(64, 256, 8, 2, 512)
     P = ctypes.byref
     # NULL shape
-    assert _call("moe_route", None, FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert _call("moe_route", None, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, 0, None) == moe.MOE_ERR_INVALID_ARG
     # NULL / misaligned pointers
-    assert _call("moe_route", P(sh), None, FAKE, None, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert _call("moe_route", P(sh), None, FAKE, None, FAKE, FAKE, FAKE, None, 0, None) == moe.MOE_ERR_INVALID_ARG
     assert "x is NULL" in moe.moe_last_error()
-    assert _call("moe_route", P(sh), FAKE + 2, FAKE, None, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert _call("moe_route", P(sh), FAKE + 2, FAKE, None, FAKE, FAKE, FAKE, None, 0, None) == moe.MOE_ERR_INVALID_ARG
     assert "aligned" in moe.moe_last_error()
+    # router workspace missing when H is split
+    assert moe.moe_route_workspace_bytes(sh) > 0
+    assert _call("moe_route", P(sh), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, 0, None) == moe.MOE_ERR_WORKSPACE
     # unsupported shapes
     bad = moe.make_shape(64, 256, 8, 9, 512)
-    assert _call("moe_route", P(bad), FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert _call("moe_route", P(bad), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, 0, None) == moe.MOE_ERR_UNSUPPORTED
     assert _call("moe_route_from_logits", P(bad), FAKE, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
     bad_dt = moe.MoeShape(64, 256, 8, 2, 512, 0, 3)
     assert _call("moe_combine", P(bad_dt), FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
@@ -90,13 +95,21 @@ def test_error_codes_before_launch():
     assert _call("moe_grouped_ffn", P(s8), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                  FAKE, FAKE, 1 << 30, None) == moe.MOE_ERR_INVALID_ARG
     assert "x_perm_scale" in moe.moe_last_error()
-    assert _call("moe_permute", P(s8), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert _call("moe_permute", P(s8), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 20,
+                 None) == moe.MOE_ERR_INVALID_ARG
+    # permute workspace missing / too small
+    pneed = moe.moe_permute_workspace_bytes(s8)
+    assert pneed == 8 * 4
+    assert _call("moe_permute", P(s8), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,
+                 None) == moe.MOE_ERR_WORKSPACE
+    assert _call("moe_permute", P(s8), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                 pneed - 1, None) == moe.MOE_ERR_WORKSPACE
 
 
 def test_zero_tokens_is_a_no_op():
     sh = moe.make_shape(0, 256, 8, 2, 512)
     P = ctypes.byref
-    assert _call("moe_route", P(sh), None, None, None, None, None, None, None) == moe.MOE_OK
+    assert _call("moe_route", P(sh), None, None, None, None, None, None, None, 0, None) == moe.MOE_OK
     assert _call("moe_combine", P(sh), None, None, None, None, None) == moe.MOE_OK
     assert _call("moe_forward", P(sh), *([None] * 12), None, 0, None) == moe.MOE_OK
 

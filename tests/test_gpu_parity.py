@@ -82,6 +82,30 @@ def test_route_configs(ci):
     assert np.abs(w.cpu().numpy() - w_ref).max() <= 1e-6
 
 
+# Shapes that exercise the router GEMM's edges: token and expert tiles cut
+# short (T, E not multiples of 128), H split into slices of unequal length,
+# one slice (partial sums written in place, bias added there), T = E = 1, and
+# E > 512 for the top-k.
+@pytest.mark.parametrize("T,H,E,k,zipf", [(300, 384, 200, 6, 1.1), (1000, 1280, 256, 8, None),
+                                          (130, 1152, 130, 4, 1.1), (32768, 128, 128, 2, 1.1),
+                                          (1, 256, 1, 1, None), (5, 128, 1000, 16, 1.1)])
+def test_route_ragged_shapes(T, H, E, k, zipf):
+    cfg = MoeConfig(f"route_{T}_{H}_{E}", 11, T=T, H=H, E=E, k=k, I=128, zipf_s=zipf)
+    li = generate_layer(cfg, DEV)
+    logits, idx, w = run_route(cfg, li)
+    inp = _route_inputs(li)
+    x = oracle.bf16_bits_to_f32(inp["x_bf16"])
+    ref = oracle.router_logits(x, inp["w_router"], inp["router_bias"])
+    mag = np.abs(x) @ np.abs(inp["w_router"]).T
+    if inp["router_bias"] is not None:
+        mag = mag + np.abs(inp["router_bias"])[None, :]
+    lg = logits.cpu().numpy()
+    assert np.all(np.abs(lg - ref) <= (cfg.H + 2) * 2.0 ** -24 * mag)
+    idx_ref, w_ref = oracle.topk_softmax(lg, cfg.k)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    assert np.abs(w.cpu().numpy() - w_ref).max() <= 1e-6
+
+
 def test_route_zero_router_weight_ties():
     cfg = MoeConfig("zero_router", 5, T=70, H=512, E=24, k=6, I=128)
     li = generate_layer(cfg, DEV)
@@ -271,6 +295,7 @@ def test_forward_zero_tokens():
     moe.moe_forward(sh, None, None, None, None, None, None, None, None, None, None, None, None, None, 0)
     counts = torch.full((8,), -1, dtype=torch.int32, device=DEV)
     offsets = torch.full((9,), -1, dtype=torch.int32, device=DEV)
+    assert moe.moe_permute_workspace_bytes(sh) == 0
     moe.moe_permute(sh, None, None, counts, offsets, None, None, None, None)
     torch.cuda.synchronize()
     assert counts.cpu().tolist() == [0] * 8 and offsets.cpu().tolist() == [0] * 9
