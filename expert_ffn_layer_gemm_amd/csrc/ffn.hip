@@ -64,7 +64,7 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ offse
     cls[q] = -1;
     if (m[q] > 0 && m[q] <= kSkinnyMax)
       cls[q] = m[q] <= skinny_class_rows(0) ? 0 : (m[q] <= skinny_class_rows(1) ? 1 : 2);
-    nt[q] = m[q] > kSkinnyMax ? ceil_div(m[q], sc.tile_rows) : 0;
+    nt[q] = m[q] > kSkinnyMax ? ceil_div(m[q], group_tile_rows(m[q], sc.tile_rows)) : 0;
   }
 #pragma unroll
   for (int c = 0; c < kSkinnyClasses; ++c) {
@@ -80,9 +80,13 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ offse
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int g = 2 * tid + q;
+    const int first = nt_pos;
     for (int i = 0; i < nt[q]; ++i) {
-      sc.tiles[2 * nt_pos] = g;
-      sc.tiles[2 * nt_pos + 1] = i * sc.tile_rows;
+      const int band = i / kTileBand;
+      sc.tiles[4 * nt_pos] = g;
+      sc.tiles[4 * nt_pos + 1] = i * group_tile_rows(m[q], sc.tile_rows);
+      sc.tiles[4 * nt_pos + 2] = first + band * kTileBand;
+      sc.tiles[4 * nt_pos + 3] = min(kTileBand, nt[q] - band * kTileBand);
       ++nt_pos;
     }
   }
@@ -323,7 +327,7 @@ WsLayout ffn_layout(int T, int H, int E, int k, int I, int n_shared, bool fp8) {
   L.n_skinny = off; off += 256;
   L.n_tiles = off;  off += 256;
   L.skinny = off;   off += align256((size_t)kSkinnyClasses * G * 4);
-  L.tiles = off;    off += align256((size_t)L.max_tiles * 8);
+  L.tiles = off;    off += align256((size_t)L.max_tiles * 16);
   L.total = off;
   return L;
 }

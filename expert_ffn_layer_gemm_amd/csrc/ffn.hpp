@@ -11,6 +11,22 @@ constexpr int kSkinnyMax = 64;      // rows handled by the skinny kernel (4 MFMA
 // Rows per tile of the tiled kernel: 256 for bf16, 128 for fp8.
 __host__ __device__ constexpr int tile_rows(bool fp8) { return fp8 ? 128 : 256; }
 
+// Rows per tile of a group of m rows: the group is cut into ceil(m / bm)
+// tiles of equal height (rounded up to 16), so that the tiles of one group,
+// which stream the same weights, take the same time and stay in step on an
+// XCD's L2.  The last tile may be shorter; none is empty.
+__host__ __device__ inline int group_tile_rows(int m, int bm) {
+  const int n = (m + bm - 1) / bm;
+  return ((m + n - 1) / n + 15) / 16 * 16;
+}
+
+// Consecutive row tiles of a group are taken in bands of up to kTileBand;
+// the tiled kernels walk a band column tile by column tile, row tile fastest,
+// so workgroups that stream the same weight slice are adjacent in dispatch
+// order (and start together on one XCD's L2), and those that share a row
+// tile are at most kTileBand apart.
+constexpr int kTileBand = 8;
+
 // Skinny groups are split into row classes (<= 16, <= 32, <= 64 rows) so each
 // class runs a kernel whose register use matches its row blocks.
 constexpr int kSkinnyClasses = 3;
@@ -20,7 +36,7 @@ struct Sched {
   int32_t* n_skinny;  // [kSkinnyClasses]
   int32_t* n_tiles;
   int32_t* skinny;    // [kSkinnyClasses][G] group ids
-  int32_t* tiles;     // [max_tiles][2] (group, first row)
+  int32_t* tiles;     // [max_tiles][4] (group, first row, band's first tile, band size)
   int G;
   int tile_rows;      // rows per tiled-kernel tile
 };

@@ -16,10 +16,12 @@
 //     128 FLOP per staged byte the operand stream from L2 stays below what
 //     the MFMA rate needs.  fp8 (~128-row expert groups, memory-bound):
 //     BM = 128, 64 x 64 per wave.
-//   - K is staged in 128-byte chunks (64 bf16 / 128 e4m3 per row) through an
-//     NS-stage LDS ring filled by direct-to-LDS loads (global_load_lds_dwordx4):
-//     bf16 2 stages (64 KB each), fp8 3 stages (48 KB + scales) so that two
-//     chunks are in flight while one is multiplied.
+//   - K is staged in 128-byte chunks (64 bf16 / 128 e4m3 per row) by
+//     direct-to-LDS loads (global_load_lds_dwordx4) into two rings: activation
+//     rows and weight rows.  bf16: 2 A stages + 3 B stages of 32 KB (all of
+//     LDS), so two weight chunks are in flight while one is multiplied; fp8:
+//     3 + 3 stages (16 KB + scales, 32 KB).  Measured: the weight stream,
+//     fetched from HBM by the first tile of a band, is the long-latency one.
 //   - A direct-to-LDS instruction writes 1 KB contiguously (lane i at +16 i),
 //     8 staged rows; each block of 8 rows lies in A, B0 or B1 and has its own
 //     wave-uniform base.  Each lane fetches global chunk c ^ (row & 7) of its
@@ -28,8 +30,11 @@
 //     conflict-free on gfx950 (the row-XOR variant (r ^ r >> 3) & 7 tried
 //     first was not).
 //   - Blocks are renumbered so each XCD (own L2) takes a contiguous run of
-//     tiles: the column tiles of one row tile, and the row tiles of one
-//     group, run on the same L2 at the same time and share their operands.
+//     tiles, and within a band of up to 8 row tiles of a group the order is
+//     column tile major, row tile fastest: the workgroups that stream one
+//     weight slice are dispatched back to back and run in step on one L2
+//     (measured: with row tiles 12-16 dispatches apart they drifted out of
+//     step and every row tile re-read the weights from HBM).
 //   - Rows past the group's end are not fetched (8-row blocks wholly past it)
 //     or re-read its last row; they are never stored, and bf16 skips the MFMAs
 //     of 16-row blocks wholly past the end.
@@ -39,26 +44,33 @@
 namespace moe {
 namespace {
 
-constexpr int kRB = 128;                          // bytes of K per staged row and chunk
 constexpr int kBRows = 256;                       // staged B rows per tile
+#ifndef TILED_BF16_RB
+#define TILED_BF16_RB 128
+#define TILED_BF16_NSA 2
+#define TILED_BF16_NSB 2
+#endif
 constexpr int kMaxKB = 1024;                      // fp8: K <= 131072 (B scales kept in LDS)
 constexpr int kXcds = 8;
 
-__device__ __forceinline__ int slot(int r, int c) { return slot8(r, c); }
+// Slot of 16-byte chunk c of staged row r for rows of RB bytes: 128-byte rows
+// c ^ (r & 7), 64-byte rows c ^ ((r >> 1) & 3) (both measured conflict-free
+// for 16 lanes reading one chunk of 16 consecutive rows).
+template <int RB>
+__device__ __forceinline__ int slot(int r, int c) {
+  if constexpr (RB == 128) return slot8(r, c);
+  return c ^ ((r >> 1) & 3);
+}
 
-// Direct-to-LDS loads of one K chunk into stage `st`: this wave's IPW
-// 1 KB blocks (wave-uniform base + per-lane offsets) and, for fp8, the row
-// scales of the chunk's K block.
-template <int IPW, bool FP8, int STAGE_DATA>
-__device__ __forceinline__ void dma_chunk(uint8_t* st, const uint8_t* const (&jb)[IPW],
-                                          const uint32_t (&soff)[IPW], const bool (&jv)[IPW],
-                                          size_t koff, int wave, const float* sptr) {
+// Direct-to-LDS loads of this wave's IPW 1 KB blocks of one K chunk into a
+// ring stage (wave-uniform base + 32-bit lane offset per block).
+template <int IPW>
+__device__ __forceinline__ void dma_blocks(uint8_t* st, const uint8_t* const (&jb)[IPW],
+                                           const uint32_t (&soff)[IPW], const bool (&jv)[IPW],
+                                           size_t koff, int wave) {
 #pragma unroll
   for (int j = 0; j < IPW; ++j)
-    if (jv[j])
-      dma16(jb[j] + koff + soff[j], st + (wave * IPW + j) * 1024);
-  if constexpr (FP8)
-    __builtin_amdgcn_global_load_lds(sptr, (lds_ptr_t)(st + STAGE_DATA + wave * 256), 4, 0, 0);
+    if (jv[j]) dma16(jb[j] + koff + soff[j], st + (wave * IPW + j) * 1024);
 }
 
 // Staged B row of 16-column block j (lane row r16) for wave column wn.
@@ -71,21 +83,34 @@ __device__ __forceinline__ int b_row(int j, int wn, int r16) {
 
 }  // namespace
 
-template <bool FP8, bool DUAL, int WM, int WN, int BM, int NS>
+template <bool FP8, bool DUAL, int WM, int WN, int BM, int NSA, int NSB, int RB>
 __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
   // The body is device code only; the host pass needs just the launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
+  static_assert(RB == 128 || (RB == 64 && !FP8), "fp8 MFMA K step needs 128-byte rows");
+  // A (activation rows) and B (weight rows) have rings of their own: NSA and
+  // NSB stages.  NSB = NSA + 1 keeps one more weight chunk in flight (weights
+  // come from HBM once per band; the activation tile is an L2 hit for all but
+  // the first column tile).  The vm-counter waits below rely on NSB - NSA <= 1
+  // and on A being issued before B in every step.
+  static_assert(NSA >= 2 && (NSB == NSA || NSB == NSA + 1), "ring depths");
+  constexpr int kRB = RB;                         // bytes of K per staged row and chunk
+  constexpr int RPB = 1024 / RB;                  // staged rows per 1 KB DMA block
+  constexpr int LPR = RB / 16;                    // lanes per staged row
   constexpr int kBM = BM;                         // rows per tile
-  constexpr int kStages = NS;
-  constexpr int kStageData = (kBM + kBRows) * kRB;
   constexpr int NW = WM * WN;                     // waves per workgroup
   constexpr int MB = kBM / WM / 16;               // 16-row blocks per wave
   constexpr int NB = kBRows / WN / 16;            // 16-column blocks per wave
-  constexpr int IPW = kStageData / 1024 / NW;     // direct-to-LDS instructions per wave and stage
-  static_assert(IPW * NW * 1024 == kStageData, "stage must split evenly over the waves");
+  constexpr int A_BYTES = kBM * kRB, B_BYTES = kBRows * kRB;
+  constexpr int IPWA = A_BYTES / 1024 / NW;       // direct-to-LDS instructions per wave and chunk
+  constexpr int IPWB = B_BYTES / 1024 / NW;
+  static_assert(IPWA * NW * 1024 == A_BYTES && IPWB * NW * 1024 == B_BYTES,
+                "a chunk must split evenly over the waves");
   constexpr int SCALE_BYTES = FP8 ? NW * 256 : 0; // fp8 row scales (waves >= 4 load duplicates)
-  constexpr int STAGE = kStageData + SCALE_BYTES;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * STAGE + (FP8 ? 2 * kMaxKB * 4 : 16)];
+  constexpr int A_STAGE = A_BYTES + SCALE_BYTES;
+  constexpr int B_RING = NSA * A_STAGE;           // byte offset of the B ring
+  __shared__ __attribute__((aligned(1024)))
+  uint8_t lds[NSA * A_STAGE + NSB * B_BYTES + (FP8 ? 2 * kMaxKB * 4 : 0)];
 
   // XCD-contiguous renumbering of the valid (tile, column tile) pairs.
   const int n_valid = *p.sc.n_tiles * p.n_ntile;
@@ -93,10 +118,15 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
   const int bid = blockIdx.x;
   const int logical = (bid % kXcds) * per_xcd + bid / kXcds;
   if (bid >= kXcds * per_xcd || logical >= n_valid) return;
-  const int tslot = logical / p.n_ntile, nt = logical % p.n_ntile;
-  const int g = p.sc.tiles[2 * tslot], m0 = p.sc.tiles[2 * tslot + 1];
+  // Within a band of row tiles: column tile major, row tile fastest.
+  const int band_first = p.sc.tiles[4 * (logical / p.n_ntile) + 2];
+  const int band_size = p.sc.tiles[4 * (logical / p.n_ntile) + 3];
+  const int local = logical - band_first * p.n_ntile;
+  const int tslot = band_first + local % band_size, nt = local / band_size;
+  const int g = p.sc.tiles[4 * tslot], m0 = p.sc.tiles[4 * tslot + 1];
   const int row0 = p.offsets[g] + m0;
-  const int mrows = min(kBM, p.offsets[g + 1] - row0);
+  const int gm = p.offsets[g + 1] - p.offsets[g];
+  const int mrows = min(group_tile_rows(gm, kBM), gm - m0);
   const int K = p.K, N = p.N;
   const size_t Kb = FP8 ? (size_t)K : 2 * (size_t)K;
   const int nk = (int)(Kb / kRB);
@@ -109,39 +139,46 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
   const int ncols = DUAL ? 128 : min(256, N - n0);
   const int r16 = lane & 15;
 
-  // Sources of the 1 KB blocks (8 staged rows each) this wave moves per
-  // stage: block b = wave * IPW + j holds rows 8b .. 8b + 7, all in A, in B0
-  // or in B1, so each has a wave-uniform base plus a 32-bit lane offset.  A
-  // blocks wholly past the group's end are not fetched (their LDS rows keep
-  // stale data from earlier chunks; those outputs are never stored).
-  const uint8_t* jb[IPW];
-  uint32_t soff[IPW];
-  bool jv[IPW];
-  int nv = FP8 ? 1 : 0;                            // vm instructions per chunk of this wave
+  // Sources of the 1 KB blocks (RPB staged rows each) this wave moves per
+  // chunk: A block a = wave * IPWA + j holds tile rows RPB a .., B block
+  // b = wave * IPWB + j staged B rows RPB b .., all in B0 or all in B1; each
+  // has a wave-uniform base plus a 32-bit lane offset.  A blocks wholly past
+  // the group's end are not fetched (their LDS rows keep stale data from
+  // earlier chunks; those outputs are never stored).
+  const uint8_t* ab[IPWA];
+  uint32_t aoff[IPWA];
+  bool av[IPWA];
+  int nva = FP8 ? 1 : 0;                           // vm instructions per A chunk of this wave
 #pragma unroll
-  for (int j = 0; j < IPW; ++j) {
-    const int brow0 = (wave * IPW + j) * 8;        // first staged row of the block
-    const int row = brow0 + (lane >> 3);
-    const uint32_t sl = (uint32_t)(slot(row, lane & 7) * 16);
-    if (brow0 < kBM) {
-      jv[j] = brow0 < mrows;
-      const int r = min(row, mrows - 1);
-      // With a_rows the tile's rows are gathered from the unpermuted matrix.
-      jb[j] = p.a_rows ? p.A : p.A + (size_t)row0 * Kb;
-      soff[j] = (p.a_rows ? (uint32_t)p.a_rows[row0 + r] : (uint32_t)r) * (uint32_t)Kb + sl;
-    } else {
-      int br = brow0 - kBM;
-      const uint8_t* B = p.B0;
-      if (DUAL && br >= 128) { B = p.B1; br -= 128; }
-      jv[j] = true;
-      jb[j] = B + (size_t)g * N * Kb;
-      // Rows past the matrix (ragged last column tile) re-read its last row.
-      soff[j] = (uint32_t)min(n0 + br + (lane >> 3), N - 1) * (uint32_t)Kb + sl;
-    }
-    nv += jv[j] ? 1 : 0;
+  for (int j = 0; j < IPWA; ++j) {
+    const int brow0 = (wave * IPWA + j) * RPB;
+    const int row = brow0 + lane / LPR;
+    const uint32_t sl = (uint32_t)(slot<RB>(row, lane % LPR) * 16);
+    av[j] = brow0 < mrows;
+    const int r = min(row, mrows - 1);
+    // With a_rows the tile's rows are gathered from the unpermuted matrix.
+    ab[j] = p.a_rows ? p.A : p.A + (size_t)row0 * Kb;
+    aoff[j] = (p.a_rows ? (uint32_t)p.a_rows[row0 + r] : (uint32_t)r) * (uint32_t)Kb + sl;
+    nva += av[j] ? 1 : 0;
   }
+  const uint8_t* bb[IPWB];
+  uint32_t boff[IPWB];
+  bool bv[IPWB];
+#pragma unroll
+  for (int j = 0; j < IPWB; ++j) {
+    int br = (wave * IPWB + j) * RPB;
+    const uint8_t* B = p.B0;
+    if (DUAL && br >= 128) { B = p.B1; br -= 128; }
+    const int row = (wave * IPWB + j) * RPB + lane / LPR;
+    const uint32_t sl = (uint32_t)(slot<RB>(row, lane % LPR) * 16);
+    bv[j] = true;
+    bb[j] = B + (size_t)g * N * Kb;
+    // Rows past the matrix (ragged last column tile) re-read its last row.
+    boff[j] = (uint32_t)min(n0 + br + lane / LPR, N - 1) * (uint32_t)Kb + sl;
+  }
+  constexpr int nvb = IPWB;                        // vm instructions per B chunk of this wave
   const float* ssrc = nullptr;
-  float* bsc = reinterpret_cast<float*>(lds + kStages * STAGE);   // fp8: [2][KB] B block scales
+  float* bsc = reinterpret_cast<float*>(lds + NSA * A_STAGE + NSB * B_BYTES);   // fp8: [2][KB]
   if constexpr (FP8) {
     const int sr = row0 + min((wave & 3) * 64 + lane, mrows - 1);
     ssrc = p.A_scale + (size_t)(p.a_rows ? p.a_rows[sr] : sr) * KB;
@@ -173,39 +210,51 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
   // multiplies every row block (rows past the group's end hold finite copies
   // of its last row and are never stored).
   constexpr bool FULL = FP8;
+  // Prologue: A chunks 0 .. NSA-2 and B chunks 0 .. NSB-2, A before B per chunk.
 #pragma unroll
-  for (int c = 0; c < NS - 1; ++c)
-    if (c < nk)
-      dma_chunk<IPW, FP8, kStageData>(lds + c * STAGE, jb, soff, jv, (size_t)c * kRB, wave,
-                                      FP8 ? ssrc + c : nullptr);
+  for (int c = 0; c < NSB - 1; ++c) {
+    if (c < NSA - 1 && c < nk) {
+      dma_blocks<IPWA>(lds + c * A_STAGE, ab, aoff, av, (size_t)c * kRB, wave);
+      if constexpr (FP8)
+        __builtin_amdgcn_global_load_lds(ssrc + c, (lds_ptr_t)(lds + c * A_STAGE + A_BYTES + wave * 256), 4, 0, 0);
+    }
+    if (c < nk) dma_blocks<IPWB>(lds + B_RING + c * B_BYTES, bb, boff, bv, (size_t)c * kRB, wave);
+  }
   for (int kc = 0; kc < nk; ++kc) {
-    // Chunks kc + 1 .. kc + NS - 2 may stay in flight (nv instructions each);
-    // chunk kc must have landed.
-    wait_vmcnt_le<(NS - 2) * (IPW + 1)>(min(NS - 2, nk - 1 - kc) * nv);
+    // A and B of chunk kc must have landed; the loads issued after them (A of
+    // chunks kc+1 .. kc+NSA-2, B of chunks kc+1 .. kc+NSB-2) may stay in flight.
+    wait_vmcnt_le<(NSA - 2) * (IPWA + 1) + (NSB - 2) * IPWB>(
+        min(NSA - 2, nk - 1 - kc) * nva + max(0, min(NSB - 2, nk - 1 - kc)) * nvb);
     lds_barrier();          // every wave's share, and every wave is done with chunk kc - 1
-    if (kc + NS - 1 < nk)   // into the stage of chunk kc - 1
-      dma_chunk<IPW, FP8, kStageData>(lds + ((kc + NS - 1) % kStages) * STAGE, jb, soff, jv,
-                                      (size_t)(kc + NS - 1) * kRB, wave,
-                                      FP8 ? ssrc + kc + NS - 1 : nullptr);
+    if (kc + NSA - 1 < nk) {   // into the A stage of chunk kc - 1
+      const int c = kc + NSA - 1;
+      dma_blocks<IPWA>(lds + (c % NSA) * A_STAGE, ab, aoff, av, (size_t)c * kRB, wave);
+      if constexpr (FP8)
+        __builtin_amdgcn_global_load_lds(ssrc + c, (lds_ptr_t)(lds + (c % NSA) * A_STAGE + A_BYTES + wave * 256), 4, 0, 0);
+    }
+    if (kc + NSB - 1 < nk) {   // into the B stage of chunk kc - 1
+      const int c = kc + NSB - 1;
+      dma_blocks<IPWB>(lds + B_RING + (c % NSB) * B_BYTES, bb, boff, bv, (size_t)c * kRB, wave);
+    }
     if (!active) continue;
-    const uint8_t* As = lds + (kc % kStages) * STAGE;
-    const uint8_t* Bs = As + kBM * kRB;
+    const uint8_t* As = lds + (kc % NSA) * A_STAGE;
+    const uint8_t* Bs = lds + B_RING + (kc % NSB) * B_BYTES;
     // fp8 (memory-bound) multiplies every row block of an active wave, which
     // keeps its code branch-free; bf16 skips the row blocks past the group's end.
     if constexpr (!FP8) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int ks = 0; ks < RB / 64; ++ks) {
         const int c = ks * 4 + (lane >> 4);
         u32x4_t a[MB], b[NB];
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
           const int br = b_row<DUAL, WN, NB>(j, wn, r16);
-          b[j] = lds_read16(Bs + br * kRB + (slot(br, c) << 4));
+          b[j] = lds_read16(Bs + br * kRB + (slot<RB>(br, c) << 4));
         }
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
           const int r = rbase + i * 16 + r16;
-          a[i] = lds_read16(As + r * kRB + (slot(r, c) << 4));
+          a[i] = lds_read16(As + r * kRB + (slot<RB>(r, c) << 4));
         }
 #pragma unroll
         for (int i = 0; i < MB; ++i)
@@ -223,39 +272,44 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
       for (int j = 0; j < NB; ++j) {
         const int br = b_row<DUAL, WN, NB>(j, wn, r16);
         const uint8_t* rowp = Bs + br * kRB;
-        const u32x4_t lo = lds_read16(rowp + (slot(br, c0) << 4));
-        const u32x4_t hi = lds_read16(rowp + (slot(br, c1) << 4));
+        const u32x4_t lo = lds_read16(rowp + (slot<RB>(br, c0) << 4));
+        const u32x4_t hi = lds_read16(rowp + (slot<RB>(br, c1) << 4));
         b[j] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       }
-      const float* ascale = reinterpret_cast<const float*>(As + kStageData);
+      const float* ascale = reinterpret_cast<const float*>(As + A_BYTES);
       const float sb_lo = DUAL ? bsc[kc] : bsc[(wn * (256 / WN)) / 128 * KB + kc];
       const float sb_hi = DUAL ? bsc[KB + kc] : sb_lo;
-      // One A fragment at a time: the second wave of the SIMD covers its latency.
+      // All fragments first, then the MB x NB MFMAs back to back into
+      // separate partial tiles (no MFMA waits on another's result), then the
+      // per-block scaling: the VALU work of one wave overlaps the MFMAs of the
+      // other wave on the SIMD.
+      i32x8_t a[MB];
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const int r = rbase + i * 16 + r16;
+        const uint8_t* rowp = As + r * kRB;
+        const u32x4_t lo = lds_read16(rowp + (slot<RB>(r, c0) << 4));
+        const u32x4_t hi = lds_read16(rowp + (slot<RB>(r, c1) << 4));
+        a[i] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                       (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
+      f32x4_t pr[MB][NB];
 #pragma unroll
       for (int i = 0; i < MB; ++i)
-        if (FULL || i < nmb) {
-          const int r = rbase + i * 16 + r16;
-          const uint8_t* rowp = As + r * kRB;
-          const u32x4_t lo = lds_read16(rowp + (slot(r, c0) << 4));
-          const u32x4_t hi = lds_read16(rowp + (slot(r, c1) << 4));
-          const i32x8_t a = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                                    (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-          float s_lo[4], s_hi[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float sa = ascale[rbase + i * 16 + (lane >> 4) * 4 + q];
-            s_lo[q] = sa * sb_lo;
-            s_hi[q] = sa * sb_hi;
-          }
+        for (int j = 0; j < NB; ++j)
+          pr[i][j] = mfma_fp8_16x16x128(a[i], b[j], f32x4_t{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-          for (int j = 0; j < NB; ++j) {
-            const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-            const f32x4_t pr = mfma_fp8_16x16x128(a, b[j], z);
+      for (int i = 0; i < MB; ++i) {
+        const f32x4_t sa = *reinterpret_cast<const f32x4_t*>(ascale + rbase + i * 16 + (lane >> 4) * 4);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[i][j][q] += pr[q] * (j < NB / 2 ? s_lo[q] : s_hi[q]);
-          }
+        for (int q = 0; q < 4; ++q) {
+          const float s_lo = sa[q] * sb_lo, s_hi = sa[q] * sb_hi;
+#pragma unroll
+          for (int j = 0; j < NB; ++j) acc[i][j][q] += pr[i][j][q] * (j < NB / 2 ? s_lo : s_hi);
         }
+      }
     }
   }
 
@@ -342,10 +396,10 @@ hipError_t launch_tiled(const char* name, bool fp8, bool dual, long long blocks,
   // bf16 (compute-bound prefill groups): 256-row tiles, 2 stages.  fp8
   // (memory-bound ~128-row groups): 128-row tiles, 3 stages, two chunks in
   // flight.  The row counts match tile_rows() used by the schedule.
-  if (fp8 && dual) MOE_LAUNCH(name, (k_tiled3<true, true, 2, 4, 128, 3>), grid, dim3(512), 0, s, a);
-  else if (fp8) MOE_LAUNCH(name, (k_tiled3<true, false, 2, 4, 128, 3>), grid, dim3(512), 0, s, a);
-  else if (dual) MOE_LAUNCH(name, (k_tiled3<false, true, 2, 4, 256, 2>), grid, dim3(512), 0, s, a);
-  else MOE_LAUNCH(name, (k_tiled3<false, false, 2, 4, 256, 2>), grid, dim3(512), 0, s, a);
+  if (fp8 && dual) MOE_LAUNCH(name, (k_tiled3<true, true, 2, 4, 128, 3, 3, 128>), grid, dim3(512), 0, s, a);
+  else if (fp8) MOE_LAUNCH(name, (k_tiled3<true, false, 2, 4, 128, 3, 3, 128>), grid, dim3(512), 0, s, a);
+  else if (dual) MOE_LAUNCH(name, (k_tiled3<false, true, 2, 4, 256, TILED_BF16_NSA, TILED_BF16_NSB, TILED_BF16_RB>), grid, dim3(512), 0, s, a);
+  else MOE_LAUNCH(name, (k_tiled3<false, false, 2, 4, 256, TILED_BF16_NSA, TILED_BF16_NSB, TILED_BF16_RB>), grid, dim3(512), 0, s, a);
   return hipSuccess;
 }
 
