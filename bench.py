@@ -166,6 +166,15 @@ def main():
         roof.update({"kernel": dom_name, "kernel_ms": kern_s * 1e3,
                      "algorithmic_bytes": work.bytes, "algorithmic_flops": work.flops,
                      "traffic": stored_traffic(cfg.name, dom_name)})
+    # Roofline of every grouped-FFN launch of the untimed profiling step.
+    kernel_roofs = {}
+    for i, (ms, n) in enumerate(launches):
+        if n.startswith(("skinny_", "tiled_")):
+            wk = acc.kernel_work(n, counts, cfg.H, cfg.I, cfg.wdtype)
+            if wk.groups:
+                rf = acc.roofline(wk, ms / 1e3, dtype)
+                kernel_roofs[f"{i}:{n}"] = {"ms": round(ms, 4), "groups": wk.groups,
+                                            "bound": rf["bound"], "frac": round(rf["frac"], 4)}
     layer = acc.layer_work(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.n_shared, cfg.wdtype, counts)
     layer_roof = acc.roofline(layer, ms_per_step / 1e3, dtype)
 
@@ -185,6 +194,7 @@ def main():
         "roofline": roof,
         "layer_roofline": layer_roof,
         "per_kernel_ms": {f"{i}:{n}": round(ms, 4) for i, (ms, n) in enumerate(launches)},
+        "grouped_ffn_rooflines": kernel_roofs,
         "wall_s_timed_region": t_wall,
         "cpu_baseline": cpu,
     }

@@ -20,11 +20,10 @@ import numpy as np
 PEAK_HBM_GBS = 8000.0
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp32": 157.3}
 
-# Row classes of the grouped-FFN schedule; the same thresholds as the C++
-# schedule in csrc/ffn.hip (skinny classes up to 16/32/64 rows, then 128-row
-# tiles).
-SKINNY_CLASS_ROWS = (16, 32, 64)
-TILE_ROWS = 128
+# Split of the grouped-FFN schedule, the same threshold as the C++ schedule
+# (csrc/ffn.hpp kSkinnyMax): groups of up to 64 rows go to the weight-streaming
+# kernels, larger ones to the tiled kernels.
+SKINNY_MAX_ROWS = 64
 
 
 def tokens_per_expert(T: int, k: int, E: int) -> float:
@@ -69,11 +68,9 @@ def kernel_groups(kernel: str, counts: np.ndarray) -> np.ndarray:
     m = np.asarray(counts, dtype=np.int64)
     m = m[m > 0]
     if kernel.startswith("skinny_"):
-        c = int(kernel.rsplit("_r", 1)[1])
-        lo = {16: 0, 32: 16, 64: 32}[c]
-        return m[(m > lo) & (m <= c)]
+        return m[m <= SKINNY_MAX_ROWS]
     if kernel.startswith("tiled_"):
-        return m[m > SKINNY_CLASS_ROWS[-1]]
+        return m[m > SKINNY_MAX_ROWS]
     raise ValueError(f"not a grouped-FFN kernel: {kernel}")
 
 

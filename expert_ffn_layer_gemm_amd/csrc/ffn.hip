@@ -56,25 +56,28 @@ __device__ __forceinline__ void block_scan_pair(int a, int b, int* wave_sum, int
 __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ offsets, Sched sc) {
   __shared__ int wave_sum[16];
   const int tid = threadIdx.x, G = sc.G;
-  int m[2], cls[2], nt[2];
+  int m[2], sl[2], nt[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int g = 2 * tid + q;
     m[q] = g < G ? offsets[g + 1] - offsets[g] : 0;
-    cls[q] = -1;
-    if (m[q] > 0 && m[q] <= kSkinnyMax)
-      cls[q] = m[q] <= skinny_class_rows(0) ? 0 : (m[q] <= skinny_class_rows(1) ? 1 : 2);
+    sl[q] = m[q] > 0 && m[q] <= kSkinnyMax ? ceil_div(m[q], kSliceRows) : 0;
     nt[q] = m[q] > kSkinnyMax ? ceil_div(m[q], group_tile_rows(m[q], sc.tile_rows)) : 0;
   }
+  int sl_pos, sl_total;
+  block_scan_pair(sl[0], sl[1], wave_sum, sl_pos, sl_total);
 #pragma unroll
-  for (int c = 0; c < kSkinnyClasses; ++c) {
-    int pos, total;
-    block_scan_pair(cls[0] == c, cls[1] == c, wave_sum, pos, total);
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-      if (cls[q] == c) sc.skinny[c * G + pos++] = 2 * tid + q;
-    if (tid == 0) sc.n_skinny[c] = total;
+  for (int q = 0; q < 2; ++q) {
+    const int first = sl_pos;
+    for (int i = 0; i < sl[q]; ++i) {
+      sc.skinny[4 * sl_pos] = 2 * tid + q;
+      sc.skinny[4 * sl_pos + 1] = i * kSliceRows;
+      sc.skinny[4 * sl_pos + 2] = first;
+      sc.skinny[4 * sl_pos + 3] = sl[q];
+      ++sl_pos;
+    }
   }
+  if (tid == 0) *sc.n_skinny = sl_total;
   int nt_pos, nt_total;
   block_scan_pair(nt[0], nt[1], wave_sum, nt_pos, nt_total);
 #pragma unroll
@@ -99,11 +102,10 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ offse
 // consecutive k at offset 8*(l/16) of each 32-wide K step.
 template <bool DUAL, int NW, int MB>
 __global__ __launch_bounds__(64 * NW) void k_skinny_bf16(const GemmArgs p) {
-  constexpr int CLS = MB == 1 ? 0 : (MB == 2 ? 1 : 2);
-  const int slot = blockIdx.x / p.n_ntile, nt = blockIdx.x % p.n_ntile;
-  if (slot >= p.sc.n_skinny[CLS]) return;
-  const int g = p.sc.skinny[CLS * p.sc.G + slot];
-  const int row0 = p.offsets[g], m = p.offsets[g + 1] - row0;
+  int slot, nt;
+  if (!band_item(p.sc.skinny, *p.sc.n_skinny, p.n_ntile, slot, nt)) return;
+  const int g = p.sc.skinny[4 * slot], s0 = p.sc.skinny[4 * slot + 1];
+  const int row0 = p.offsets[g] + s0, m = min(16 * MB, p.offsets[g + 1] - row0);
   const int nmb = ceil_div(m, 16);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, kq = (lane >> 4) * 8;
@@ -143,23 +145,24 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_bf16(const GemmArgs p) {
         if (DUAL) nxt1[u] = *reinterpret_cast<const u32x4_t*>(b1 + k0 + 32 * U + u * 32);
       }
     }
-    u32x4_t a[MB][U];
+    // A fragments one 32-wide K step at a time (MB x 4 registers live), so
+    // the 4-block variant keeps enough waves per SIMD to hide the weight
+    // stream's latency.
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-      if (mb < nmb) {
+    for (int u = 0; u < U; ++u) {
+      u32x4_t a[MB];
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-          a[mb][u] = aok[mb] ? *reinterpret_cast<const u32x4_t*>(arow[mb] + k0 + u * 32)
-                             : u32x4_t{0, 0, 0, 0};
-      }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
+      for (int mb = 0; mb < MB; ++mb)
+        if (mb < nmb)
+          a[mb] = aok[mb] ? *reinterpret_cast<const u32x4_t*>(arow[mb] + k0 + u * 32)
+                          : u32x4_t{0, 0, 0, 0};
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
         if (mb < nmb) {
-          acc0[mb] = mfma_bf16_16x16x32(a[mb][u], cur0[u], acc0[mb]);
-          if (DUAL) acc1[mb] = mfma_bf16_16x16x32(a[mb][u], cur1[u], acc1[mb]);
+          acc0[mb] = mfma_bf16_16x16x32(a[mb], cur0[u], acc0[mb]);
+          if (DUAL) acc1[mb] = mfma_bf16_16x16x32(a[mb], cur1[u], acc1[mb]);
         }
+    }
     if (more) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -192,12 +195,11 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_bf16(const GemmArgs p) {
 // row maxima are combined across waves through LDS.
 template <bool DUAL, int NW, int MB>
 __global__ __launch_bounds__(64 * NW) void k_skinny_fp8(const GemmArgs p) {
-  constexpr int CLS = MB == 1 ? 0 : (MB == 2 ? 1 : 2);
   __shared__ float row_amax[NW][16 * MB];
-  const int slot = blockIdx.x / p.n_ntile, nt = blockIdx.x % p.n_ntile;
-  if (slot >= p.sc.n_skinny[CLS]) return;
-  const int g = p.sc.skinny[CLS * p.sc.G + slot];
-  const int row0 = p.offsets[g], m = p.offsets[g + 1] - row0;
+  int slot, nt;
+  if (!band_item(p.sc.skinny, *p.sc.n_skinny, p.n_ntile, slot, nt)) return;
+  const int g = p.sc.skinny[4 * slot], s0 = p.sc.skinny[4 * slot + 1];
+  const int row0 = p.offsets[g] + s0, m = min(16 * MB, p.offsets[g + 1] - row0);
   const int nmb = ceil_div(m, 16);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, kq = (lane >> 4) * 32;
@@ -311,7 +313,7 @@ size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 struct WsLayout {
   size_t h, h_scale, n_skinny, n_tiles, skinny, tiles, total;
-  int max_tiles;
+  int max_tiles, max_slices;
 };
 
 WsLayout ffn_layout(int T, int H, int E, int k, int I, int n_shared, bool fp8) {
@@ -326,7 +328,8 @@ WsLayout ffn_layout(int T, int H, int E, int k, int I, int n_shared, bool fp8) {
   L.h_scale = off;  off += fp8 ? align256((size_t)R * (I / 128) * 4) : 0;
   L.n_skinny = off; off += 256;
   L.n_tiles = off;  off += 256;
-  L.skinny = off;   off += align256((size_t)kSkinnyClasses * G * 4);
+  L.max_slices = (int)std::min<long long>(4LL * G, R / kSliceRows + G);
+  L.skinny = off;   off += align256((size_t)L.max_slices * 16);
   L.tiles = off;    off += align256((size_t)L.max_tiles * 16);
   L.total = off;
   return L;
@@ -355,12 +358,6 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
 
   uint8_t* h = ws + L.h;
   float* h_scale = f.fp8 ? reinterpret_cast<float*>(ws + L.h_scale) : nullptr;
-  // Upper bound on the groups of each skinny class (a class-c group has more
-  // than 16 << (c-1) rows).
-  long long max_cls[kSkinnyClasses];
-  for (int c = 0; c < kSkinnyClasses; ++c)
-    max_cls[c] = std::min<long long>(G, c == 0 ? R : R / (skinny_class_rows(c - 1) + 1));
-
   GemmArgs up{};
   up.sc = sc;
   up.offsets = f.offsets;
@@ -392,14 +389,10 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
   // gate/up + SwiGLU
   if (f.fp8) {
     up.n_ntile = f.I / (16 * 8);
-    launch_gemm("skinny_gateup_fp8_r16", k_skinny_fp8<true, 8, 1>, 512, max_cls[0] * up.n_ntile, up, s);
-    launch_gemm("skinny_gateup_fp8_r32", k_skinny_fp8<true, 8, 2>, 512, max_cls[1] * up.n_ntile, up, s);
-    launch_gemm("skinny_gateup_fp8_r64", k_skinny_fp8<true, 8, 4>, 512, max_cls[2] * up.n_ntile, up, s);
+    launch_gemm("skinny_gateup_fp8", k_skinny_fp8<true, 8, 1>, 512, band_grid(L.max_slices, up.n_ntile), up, s);
   } else {
     up.n_ntile = f.I / (16 * 4);
-    launch_gemm("skinny_gateup_bf16_r16", k_skinny_bf16<true, 4, 1>, 256, max_cls[0] * up.n_ntile, up, s);
-    launch_gemm("skinny_gateup_bf16_r32", k_skinny_bf16<true, 4, 2>, 256, max_cls[1] * up.n_ntile, up, s);
-    launch_gemm("skinny_gateup_bf16_r64", k_skinny_bf16<true, 4, 4>, 256, max_cls[2] * up.n_ntile, up, s);
+    launch_gemm("skinny_gateup_bf16", k_skinny_bf16<true, 4, 1>, 256, band_grid(L.max_slices, up.n_ntile), up, s);
   }
   up.n_ntile = f.I / 128;
   launch_tiled(f.fp8 ? "tiled_gateup_fp8" : "tiled_gateup_bf16", f.fp8, true,
@@ -407,15 +400,10 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
 
   // down
   dn.n_ntile = f.H / (16 * 4);
-  if (f.fp8) {
-    launch_gemm("skinny_down_fp8_r16", k_skinny_fp8<false, 4, 1>, 256, max_cls[0] * dn.n_ntile, dn, s);
-    launch_gemm("skinny_down_fp8_r32", k_skinny_fp8<false, 4, 2>, 256, max_cls[1] * dn.n_ntile, dn, s);
-    launch_gemm("skinny_down_fp8_r64", k_skinny_fp8<false, 4, 4>, 256, max_cls[2] * dn.n_ntile, dn, s);
-  } else {
-    launch_gemm("skinny_down_bf16_r16", k_skinny_bf16<false, 4, 1>, 256, max_cls[0] * dn.n_ntile, dn, s);
-    launch_gemm("skinny_down_bf16_r32", k_skinny_bf16<false, 4, 2>, 256, max_cls[1] * dn.n_ntile, dn, s);
-    launch_gemm("skinny_down_bf16_r64", k_skinny_bf16<false, 4, 4>, 256, max_cls[2] * dn.n_ntile, dn, s);
-  }
+  if (f.fp8)
+    launch_gemm("skinny_down_fp8", k_skinny_fp8<false, 4, 1>, 256, band_grid(L.max_slices, dn.n_ntile), dn, s);
+  else
+    launch_gemm("skinny_down_bf16", k_skinny_bf16<false, 4, 1>, 256, band_grid(L.max_slices, dn.n_ntile), dn, s);
   dn.n_ntile = ceil_div(f.H, 256);
   launch_tiled(f.fp8 ? "tiled_down_fp8" : "tiled_down_bf16", f.fp8, false,
                (long long)L.max_tiles * dn.n_ntile, dn, s);

@@ -27,19 +27,47 @@ __host__ __device__ inline int group_tile_rows(int m, int bm) {
 // tile are at most kTileBand apart.
 constexpr int kTileBand = 8;
 
-// Skinny groups are split into row classes (<= 16, <= 32, <= 64 rows) so each
-// class runs a kernel whose register use matches its row blocks.
-constexpr int kSkinnyClasses = 3;
-__host__ __device__ constexpr int skinny_class_rows(int c) { return 16 << c; }
+// Groups of at most kSkinnyMax rows go to the weight-streaming kernels as
+// 16-row slices (one MFMA row block each), slices of a group adjacent.
+constexpr int kSliceRows = 16;
 
 struct Sched {
-  int32_t* n_skinny;  // [kSkinnyClasses]
+  int32_t* n_skinny;  // number of skinny slices
   int32_t* n_tiles;
-  int32_t* skinny;    // [kSkinnyClasses][G] group ids
+  int32_t* skinny;    // [max_slices][4] (group, first row, group's first slice, its slices)
   int32_t* tiles;     // [max_tiles][4] (group, first row, band's first tile, band size)
   int G;
   int tile_rows;      // rows per tiled-kernel tile
 };
+
+// Work item and column tile of this workgroup.  Blocks are renumbered so each
+// XCD (own L2) takes a contiguous run of (item, column tile) pairs; within a
+// band of items (the slices of a group, or up to kTileBand row tiles) the
+// order is column tile major, item fastest, so workgroups that stream the
+// same weights are dispatched back to back on one L2.  `items` holds 4 ints
+// per item, the last two being the band's first item and its size.  Returns
+// false for blocks past the valid pairs.
+__device__ __forceinline__ bool band_item(const int32_t* items, int n_items, int n_ntile, int& item,
+                                          int& nt) {
+  constexpr int kXcd = 8;
+  const int n_valid = n_items * n_ntile;
+  const int per_xcd = (n_valid + kXcd - 1) / kXcd;
+  const int bid = blockIdx.x;
+  const int logical = (bid % kXcd) * per_xcd + bid / kXcd;
+  if (bid >= kXcd * per_xcd || logical >= n_valid) return false;
+  const int band_first = items[4 * (logical / n_ntile) + 2];
+  const int band_size = items[4 * (logical / n_ntile) + 3];
+  const int local = logical - band_first * n_ntile;
+  item = band_first + local % band_size;
+  nt = local / band_size;
+  return true;
+}
+
+// Grid size for band_item over at most max_items items: the renumbering
+// needs up to 7 blocks past the valid pairs.
+inline long long band_grid(long long max_items, int n_ntile) {
+  return (max_items * n_ntile + 15) / 8 * 8;
+}
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.f + expf(-g)) * u; }
 

@@ -51,7 +51,6 @@ constexpr int kBRows = 256;                       // staged B rows per tile
 #define TILED_BF16_NSB 2
 #endif
 constexpr int kMaxKB = 1024;                      // fp8: K <= 131072 (B scales kept in LDS)
-constexpr int kXcds = 8;
 
 // Slot of 16-byte chunk c of staged row r for rows of RB bytes: 128-byte rows
 // c ^ (r & 7), 64-byte rows c ^ ((r >> 1) & 3) (both measured conflict-free
@@ -112,17 +111,8 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
   __shared__ __attribute__((aligned(1024)))
   uint8_t lds[NSA * A_STAGE + NSB * B_BYTES + (FP8 ? 2 * kMaxKB * 4 : 0)];
 
-  // XCD-contiguous renumbering of the valid (tile, column tile) pairs.
-  const int n_valid = *p.sc.n_tiles * p.n_ntile;
-  const int per_xcd = (n_valid + kXcds - 1) / kXcds;
-  const int bid = blockIdx.x;
-  const int logical = (bid % kXcds) * per_xcd + bid / kXcds;
-  if (bid >= kXcds * per_xcd || logical >= n_valid) return;
-  // Within a band of row tiles: column tile major, row tile fastest.
-  const int band_first = p.sc.tiles[4 * (logical / p.n_ntile) + 2];
-  const int band_size = p.sc.tiles[4 * (logical / p.n_ntile) + 3];
-  const int local = logical - band_first * p.n_ntile;
-  const int tslot = band_first + local % band_size, nt = local / band_size;
+  int tslot, nt;
+  if (!band_item(p.sc.tiles, *p.sc.n_tiles, p.n_ntile, tslot, nt)) return;
   const int g = p.sc.tiles[4 * tslot], m0 = p.sc.tiles[4 * tslot + 1];
   const int row0 = p.offsets[g] + m0;
   const int gm = p.offsets[g + 1] - p.offsets[g];
@@ -391,8 +381,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
 hipError_t launch_tiled(const char* name, bool fp8, bool dual, long long blocks, const GemmArgs& a,
                         hipStream_t s) {
   if (blocks <= 0) return hipSuccess;
-  // The XCD renumbering needs up to kXcds - 1 blocks past the valid ones.
-  const dim3 grid((unsigned)((blocks + 2 * kXcds - 1) / kXcds * kXcds));
+  const dim3 grid((unsigned)band_grid(blocks, 1));
   // bf16 (compute-bound prefill groups): 256-row tiles, 2 stages.  fp8
   // (memory-bound ~128-row groups): 128-row tiles, 3 stages, two chunks in
   // flight.  The row counts match tile_rows() used by the schedule.
