@@ -97,8 +97,8 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ offse
 }
 
 // ---------------------------------------------------------- skinny, bf16 ----
-// Workgroup = NW waves; wave w owns 16 output columns and all (<= 16*MB) rows
-// of the group.  Lane l: row/column l%16 of each 16x16 MFMA block, 8
+// Workgroup = NW waves; wave w owns 16 h columns (DUAL) or 32 output columns and
+// all (<= 16*MB) rows of its slice.  Lane l: row/column l%16 of each 16x16 MFMA block, 8
 // consecutive k at offset 8*(l/16) of each 32-wide K step.
 template <bool DUAL, int NW, int MB>
 __global__ __launch_bounds__(64 * NW) void k_skinny_bf16(const GemmArgs p) {
@@ -110,11 +110,13 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_bf16(const GemmArgs p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, kq = (lane >> 4) * 8;
   const int K = p.K, N = p.N;
-  const int n0 = (nt * NW + wave) * 16;
+  // Two weight streams per wave: gate and up rows of 16 h columns (DUAL), or
+  // the rows of 32 consecutive output columns (16 + 16).
+  const int n0 = (nt * NW + wave) * (DUAL ? 16 : 32);
 
   const uint16_t* b0 = reinterpret_cast<const uint16_t*>(p.B0) + ((size_t)g * N + n0 + r16) * K + kq;
   const uint16_t* b1 = DUAL ? reinterpret_cast<const uint16_t*>(p.B1) + ((size_t)g * N + n0 + r16) * K + kq
-                            : nullptr;
+                            : b0 + (size_t)16 * K;
   const uint16_t* arow[MB];
   bool aok[MB];
 #pragma unroll
@@ -134,7 +136,7 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_bf16(const GemmArgs p) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     cur0[u] = *reinterpret_cast<const u32x4_t*>(b0 + u * 32);
-    if (DUAL) cur1[u] = *reinterpret_cast<const u32x4_t*>(b1 + u * 32);
+    cur1[u] = *reinterpret_cast<const u32x4_t*>(b1 + u * 32);
   }
   for (int k0 = 0; k0 < K; k0 += 32 * U) {
     const bool more = k0 + 32 * U < K;
@@ -142,7 +144,7 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_bf16(const GemmArgs p) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         nxt0[u] = *reinterpret_cast<const u32x4_t*>(b0 + k0 + 32 * U + u * 32);
-        if (DUAL) nxt1[u] = *reinterpret_cast<const u32x4_t*>(b1 + k0 + 32 * U + u * 32);
+        nxt1[u] = *reinterpret_cast<const u32x4_t*>(b1 + k0 + 32 * U + u * 32);
       }
     }
     // A fragments one 32-wide K step at a time (MB x 4 registers live), so
@@ -160,14 +162,14 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_bf16(const GemmArgs p) {
       for (int mb = 0; mb < MB; ++mb)
         if (mb < nmb) {
           acc0[mb] = mfma_bf16_16x16x32(a[mb], cur0[u], acc0[mb]);
-          if (DUAL) acc1[mb] = mfma_bf16_16x16x32(a[mb], cur1[u], acc1[mb]);
+          acc1[mb] = mfma_bf16_16x16x32(a[mb], cur1[u], acc1[mb]);
         }
     }
     if (more) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         cur0[u] = nxt0[u];
-        if (DUAL) cur1[u] = nxt1[u];
+        cur1[u] = nxt1[u];
       }
     }
   }
@@ -180,8 +182,13 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_bf16(const GemmArgs p) {
       for (int q = 0; q < 4; ++q) {
         const int r = mb * 16 + (lane >> 4) * 4 + q;
         if (r < m) {
-          const float v = DUAL ? silu_mul(acc0[mb][q], acc1[mb][q]) : acc0[mb][q];
-          out[(size_t)(row0 + r) * N + n0 + r16] = (uint16_t)f32_to_bf16_bits(v);
+          uint16_t* o = out + (size_t)(row0 + r) * N + n0 + r16;
+          if (DUAL) {
+            o[0] = (uint16_t)f32_to_bf16_bits(silu_mul(acc0[mb][q], acc1[mb][q]));
+          } else {
+            o[0] = (uint16_t)f32_to_bf16_bits(acc0[mb][q]);
+            o[16] = (uint16_t)f32_to_bf16_bits(acc1[mb][q]);
+          }
         }
       }
     }
@@ -399,11 +406,13 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
                (long long)L.max_tiles * up.n_ntile, up, s);
 
   // down
-  dn.n_ntile = f.H / (16 * 4);
-  if (f.fp8)
+  if (f.fp8) {
+    dn.n_ntile = f.H / (16 * 4);
     launch_gemm("skinny_down_fp8", k_skinny_fp8<false, 4, 1>, 256, band_grid(L.max_slices, dn.n_ntile), dn, s);
-  else
+  } else {
+    dn.n_ntile = f.H / (32 * 4);
     launch_gemm("skinny_down_bf16", k_skinny_bf16<false, 4, 1>, 256, band_grid(L.max_slices, dn.n_ntile), dn, s);
+  }
   dn.n_ntile = ceil_div(f.H, 256);
   launch_tiled(f.fp8 ? "tiled_down_fp8" : "tiled_down_bf16", f.fp8, false,
                (long long)L.max_tiles * dn.n_ntile, dn, s);
