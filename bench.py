@@ -83,6 +83,8 @@ def main():
     ap.add_argument("--config", default="qwen3_235b_decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=None)
+    ap.add_argument("--graph-probe", action="store_true",
+                    help="also time K replays of moe_forward captured in a HIP graph (extra field)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (HBM counter calibration)")
     args = ap.parse_args()
@@ -178,6 +180,27 @@ def main():
     layer = acc.layer_work(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.n_shared, cfg.wdtype, counts)
     layer_roof = acc.roofline(layer, ms_per_step / 1e3, dtype)
 
+    graph = None
+    if args.graph_probe:
+        # The same step captured once on a side stream and replayed K times.
+        gs = torch.cuda.Stream()
+        gs.wait_stream(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=gs):
+            moe.moe_forward(shape, li.x, li.w_router, li.router_bias, li.w_gate, li.w_up,
+                            li.w_down, li.s_gate, li.s_up, li.s_down, out, idx, w, ws,
+                            stream=torch.cuda.current_stream())
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(args.steps):
+            g.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph = {"ms_per_step": g0.elapsed_time(g1) / args.steps}
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, li, args.cpu_tokens or CPU_TOKENS.get(cfg.name, 64))
@@ -196,6 +219,7 @@ def main():
         "per_kernel_ms": {f"{i}:{n}": round(ms, 4) for i, (ms, n) in enumerate(launches)},
         "grouped_ffn_rooflines": kernel_roofs,
         "wall_s_timed_region": t_wall,
+        "graph_replay": graph,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res))

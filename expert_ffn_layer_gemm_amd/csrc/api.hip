@@ -227,7 +227,8 @@ int moe_grouped_ffn(const moe_shape* shape, const int32_t* offsets, const void* 
     return fail(MOE_ERR_INVALID_ARG, "%s: workspace not 256-byte aligned", fn);
   moe::FfnArgs a{shape->T, shape->H, shape->E, shape->k, shape->I, shape->n_shared, fp8,
                  offsets, nullptr, x_perm, x_perm_scale, w_gate, w_up, w_down, s_gate, s_up,
-                 s_down, y_perm, workspace};
+                 s_down, y_perm, workspace,
+                 (long long)shape->T * (shape->k + shape->n_shared)};
   return hip_status(moe::launch_grouped_ffn(a, as_stream(stream)), fn);
 }
 
@@ -311,7 +312,7 @@ int moe_forward(const moe_shape* shape, const void* x, const float* w_router,
   if (e == hipSuccess) {
     moe::FfnArgs a{shape->T, shape->H, shape->E, shape->k, shape->I, shape->n_shared, fp8,
                    offsets, src_row, fp8 ? static_cast<const void*>(xq) : x, xs, w_gate, w_up,
-                   w_down, s_gate, s_up, s_down, y_perm, ws + L.ffn};
+                   w_down, s_gate, s_up, s_down, y_perm, ws + L.ffn, (long long)shape->T};
     e = moe::launch_grouped_ffn(a, s);
   }
   if (e == hipSuccess)

@@ -401,9 +401,12 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
     up.n_ntile = f.I / (16 * 4);
     launch_gemm("skinny_gateup_bf16", k_skinny_bf16<true, 4, 1>, 256, band_grid(L.max_slices, up.n_ntile), up, s);
   }
+  // No group above kSkinnyMax rows: no tiled work, skip its launches (decode).
+  const bool tiled = f.max_group_rows > kSkinnyMax;
   up.n_ntile = f.I / 128;
-  launch_tiled(f.fp8 ? "tiled_gateup_fp8" : "tiled_gateup_bf16", f.fp8, true,
-               (long long)L.max_tiles * up.n_ntile, up, s);
+  if (tiled)
+    launch_tiled(f.fp8 ? "tiled_gateup_fp8" : "tiled_gateup_bf16", f.fp8, true,
+                 (long long)L.max_tiles * up.n_ntile, up, s);
 
   // down
   if (f.fp8) {
@@ -414,8 +417,9 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
     launch_gemm("skinny_down_bf16", k_skinny_bf16<false, 4, 1>, 256, band_grid(L.max_slices, dn.n_ntile), dn, s);
   }
   dn.n_ntile = ceil_div(f.H, 256);
-  launch_tiled(f.fp8 ? "tiled_down_fp8" : "tiled_down_bf16", f.fp8, false,
-               (long long)L.max_tiles * dn.n_ntile, dn, s);
+  if (tiled)
+    launch_tiled(f.fp8 ? "tiled_down_fp8" : "tiled_down_bf16", f.fp8, false,
+                 (long long)L.max_tiles * dn.n_ntile, dn, s);
   return hipGetLastError();
 }
 

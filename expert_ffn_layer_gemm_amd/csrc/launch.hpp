@@ -67,6 +67,9 @@ struct FfnArgs {
   const float* s_down;
   void* y_perm;
   void* workspace;
+  // Upper bound on the rows of any group: T when the groups come from a top-k
+  // routing (a token picks an expert once), R for caller-given offsets.
+  long long max_group_rows;
 };
 size_t ffn_workspace_bytes(int T, int H, int E, int k, int I, int n_shared, bool fp8);
 hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s);
