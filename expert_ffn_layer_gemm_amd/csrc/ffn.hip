@@ -347,6 +347,34 @@ size_t ffn_workspace_bytes(int T, int H, int E, int k, int I, int n_shared, bool
   return ffn_layout(T, H, E, k, I, n_shared, fp8).total;
 }
 
+// A second stream per host thread and device, with a fork and a join event:
+// the tiled kernels (groups > kSkinnyMax rows) and the weight-streaming
+// kernels (the other groups) touch disjoint groups, and each down GEMM needs
+// only the gate/up rows of its own groups, so the two chains run concurrently.
+// Created on first use with default priority and kept for the life of the
+// process (host objects only; no device memory).  If creation fails the
+// chains run one after the other on the caller's stream.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool tried = false, ok = false;
+};
+
+SideStream* side_stream() {
+  constexpr int kMaxDev = 16;
+  thread_local SideStream per_dev[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nullptr;
+  SideStream& x = per_dev[dev];
+  if (!x.tried) {
+    x.tried = true;
+    x.ok = hipStreamCreateWithFlags(&x.s, hipStreamNonBlocking) == hipSuccess &&
+           hipEventCreateWithFlags(&x.fork, hipEventDisableTiming) == hipSuccess &&
+           hipEventCreateWithFlags(&x.join, hipEventDisableTiming) == hipSuccess;
+  }
+  return x.ok ? &x : nullptr;
+}
+
 template <typename Kern>
 static void launch_gemm(const char* name, Kern kern, int threads, long long blocks,
                         const GemmArgs& a, hipStream_t s) {
@@ -393,33 +421,45 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
   dn.K = f.I;
   dn.N = f.H;
 
-  // gate/up + SwiGLU
-  if (f.fp8) {
-    up.n_ntile = f.I / (16 * 8);
-    launch_gemm("skinny_gateup_fp8", k_skinny_fp8<true, 8, 1>, 512, band_grid(L.max_slices, up.n_ntile), up, s);
-  } else {
-    up.n_ntile = f.I / (16 * 4);
-    launch_gemm("skinny_gateup_bf16", k_skinny_bf16<true, 4, 1>, 256, band_grid(L.max_slices, up.n_ntile), up, s);
-  }
   // No group above kSkinnyMax rows: no tiled work, skip its launches (decode).
   const bool tiled = f.max_group_rows > kSkinnyMax;
+  SideStream* side = tiled ? side_stream() : nullptr;
+  hipStream_t ts = s;                // stream of the tiled chain
+  if (side) {                        // fork after the plan
+    hipError_t e = hipEventRecord(side->fork, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
+    if (e != hipSuccess) return e;
+    ts = side->s;
+  }
+
+  // The tiled chain is enqueued first: its few large workgroups (one per CU)
+  // start before the weight-streaming workgroups fill the machine.
   up.n_ntile = f.I / 128;
   if (tiled)
     launch_tiled(f.fp8 ? "tiled_gateup_fp8" : "tiled_gateup_bf16", f.fp8, true,
-                 (long long)L.max_tiles * up.n_ntile, up, s);
-
-  // down
-  if (f.fp8) {
-    dn.n_ntile = f.H / (16 * 4);
-    launch_gemm("skinny_down_fp8", k_skinny_fp8<false, 4, 1>, 256, band_grid(L.max_slices, dn.n_ntile), dn, s);
-  } else {
-    dn.n_ntile = f.H / (32 * 4);
-    launch_gemm("skinny_down_bf16", k_skinny_bf16<false, 4, 1>, 256, band_grid(L.max_slices, dn.n_ntile), dn, s);
-  }
+                 (long long)L.max_tiles * up.n_ntile, up, ts);
   dn.n_ntile = ceil_div(f.H, 256);
   if (tiled)
     launch_tiled(f.fp8 ? "tiled_down_fp8" : "tiled_down_bf16", f.fp8, false,
-                 (long long)L.max_tiles * dn.n_ntile, dn, s);
+                 (long long)L.max_tiles * dn.n_ntile, dn, ts);
+
+  // gate/up + SwiGLU, then down, of the groups of at most kSkinnyMax rows
+  if (f.fp8) {
+    up.n_ntile = f.I / (16 * 8);
+    launch_gemm("skinny_gateup_fp8", k_skinny_fp8<true, 8, 1>, 512, band_grid(L.max_slices, up.n_ntile), up, s);
+    dn.n_ntile = f.H / (16 * 4);
+    launch_gemm("skinny_down_fp8", k_skinny_fp8<false, 4, 1>, 256, band_grid(L.max_slices, dn.n_ntile), dn, s);
+  } else {
+    up.n_ntile = f.I / (16 * 4);
+    launch_gemm("skinny_gateup_bf16", k_skinny_bf16<true, 4, 1>, 256, band_grid(L.max_slices, up.n_ntile), up, s);
+    dn.n_ntile = f.H / (32 * 4);
+    launch_gemm("skinny_down_bf16", k_skinny_bf16<false, 4, 1>, 256, band_grid(L.max_slices, dn.n_ntile), dn, s);
+  }
+  if (side) {                        // join: the caller's stream waits for the tiled chain
+    hipError_t e = hipEventRecord(side->join, side->s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, side->join, 0);
+    if (e != hipSuccess) return e;
+  }
   return hipGetLastError();
 }
 

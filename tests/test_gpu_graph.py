@@ -44,6 +44,9 @@ CASES = [
     # the fp8 path with a shared expert
     MoeConfig("graph_bf16", 21, T=640, H=512, E=8, k=2, I=256),
     MoeConfig("graph_fp8", 22, T=384, H=512, E=16, k=4, I=256, n_shared=1, wdtype="fp8"),
+    # skewed routing: groups on both sides of 64 rows, so the tiled chain runs
+    # on the library's second stream, forked and joined inside the capture
+    MoeConfig("graph_mixed", 23, T=512, H=512, E=64, k=4, I=256, zipf_s=1.1),
 ]
 
 
