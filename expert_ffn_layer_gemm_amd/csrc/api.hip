@@ -7,7 +7,7 @@
 #include <algorithm>
 
 #include "../../include/moe.h"
-#include "launch.hpp"
+#include "ffn.hpp"
 
 namespace {
 
@@ -228,7 +228,7 @@ int moe_grouped_ffn(const moe_shape* shape, const int32_t* offsets, const void* 
   moe::FfnArgs a{shape->T, shape->H, shape->E, shape->k, shape->I, shape->n_shared, fp8,
                  offsets, nullptr, x_perm, x_perm_scale, w_gate, w_up, w_down, s_gate, s_up,
                  s_down, y_perm, workspace,
-                 (long long)shape->T * (shape->k + shape->n_shared)};
+                 (long long)shape->T * (shape->k + shape->n_shared), false};
   return hip_status(moe::launch_grouped_ffn(a, as_stream(stream)), fn);
 }
 
@@ -299,22 +299,27 @@ int moe_forward(const moe_shape* shape, const void* x, const float* w_router,
   // buffer), reduced in slice order by the top-k kernel.
   const int ks = moe::router_splits(shape->T, shape->H, shape->E);
   float* parts = ks > 1 ? reinterpret_cast<float*>(ws + L.rpart) : logits;
+  moe::FfnArgs a{shape->T, shape->H, shape->E, shape->k, shape->I, shape->n_shared, fp8,
+                 offsets, src_row, fp8 ? static_cast<const void*>(xq) : x, xs, w_gate, w_up,
+                 w_down, s_gate, s_up, s_down, y_perm, ws + L.ffn, (long long)shape->T, false};
   hipError_t e = moe::launch_router_gemm(static_cast<const uint16_t*>(x), w_router, parts,
                                          shape->T, shape->H, shape->E, s);
   if (e == hipSuccess)
     e = moe::launch_topk(parts, ks, router_bias, nullptr, idx, w, shape->T, shape->E, shape->k, s);
-  if (e == hipSuccess)   // routing tables only: no row copy
+  if (shape->T <= moe::kSmallBatch) {
+    // Small batch: dispatch tables and FFN work lists in one launch.
+    if (e == hipSuccess)
+      e = moe::launch_dispatch_small(idx, counts, offsets, dest, src_row, moe::ffn_schedule(a),
+                                     shape->T, shape->E, shape->k, shape->n_shared, s);
+    a.planned = true;
+  } else if (e == hipSuccess) {   // routing tables only: no row copy
     e = moe::launch_permute(idx, static_cast<const uint16_t*>(x), counts, offsets, dest, src_row,
                             nullptr, nullptr, reinterpret_cast<int32_t*>(ws + L.tcnt), shape->T,
                             shape->H, shape->E, shape->k, shape->n_shared, fp8, s);
+  }
   if (e == hipSuccess && fp8)
     e = moe::launch_quantize_rows(static_cast<const uint16_t*>(x), xq, xs, shape->T, shape->H, s);
-  if (e == hipSuccess) {
-    moe::FfnArgs a{shape->T, shape->H, shape->E, shape->k, shape->I, shape->n_shared, fp8,
-                   offsets, src_row, fp8 ? static_cast<const void*>(xq) : x, xs, w_gate, w_up,
-                   w_down, s_gate, s_up, s_down, y_perm, ws + L.ffn, (long long)shape->T};
-    e = moe::launch_grouped_ffn(a, s);
-  }
+  if (e == hipSuccess) e = moe::launch_grouped_ffn(a, s);
   if (e == hipSuccess)
     e = moe::launch_combine(static_cast<const uint16_t*>(y_perm), dest, w,
                             static_cast<uint16_t*>(out), shape->T, shape->H, shape->k,

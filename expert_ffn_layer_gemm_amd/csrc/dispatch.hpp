@@ -1,0 +1,168 @@
+// Device-side building blocks of routing and dispatch, shared by the
+// separate kernels (route.hip top-k, permute.hip scan, ffn.hip plan) and the
+// single-workgroup routing + dispatch kernel for small batches (small.hip).
+#pragma once
+
+#include "ffn.hpp"
+
+namespace moe {
+
+// Order-preserving integer image of an fp32 value; -0 canonicalised to +0.
+__device__ __forceinline__ uint32_t ordered_key(float v) {
+  uint32_t b = __float_as_uint(v);
+  if ((b & 0x7FFFFFFFu) == 0) b = 0;                 // -0 ties with +0
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_to_value(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+
+// Top-k of token t by one wave (lane = lane index); NPL = logits per lane
+// (E <= 64 NPL).  The logit of expert e is parts[0][t][e] + ... +
+// parts[KS-1][t][e] (+ bias[e]), summed in that order; logits_out (may alias
+// parts when KS == 1) receives it.  Each logit becomes a 64-bit key (ordered
+// value << 32 | ~expert), so a wave max picks the largest logit and the lower
+// expert among equal ones; k rounds of max + removal give the slots best
+// first.  Lane j < k returns slot j's expert and its renormalised weight
+// exp(l_j - l_0) / sum.
+template <int NPL>
+__device__ __forceinline__ void topk_token(const float* parts, int KS, const float* bias,
+                                           float* logits_out, int t, int T, int E, int k,
+                                           int lane, int& out_e, float& out_w) {
+  const size_t plane = (size_t)T * E;
+  uint64_t key[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int e = lane + 64 * i;
+    const size_t o = (size_t)t * E + min(e, E - 1);
+    float v = parts[o];
+    // Loads of 8 planes in flight at a time; the adds stay in plane order.
+#pragma unroll 8
+    for (int s2 = 1; s2 < KS; ++s2) v += parts[s2 * plane + o];
+    if (bias) v += bias[min(e, E - 1)];
+    if (logits_out && e < E) logits_out[o] = v;
+    key[i] = e < E ? ((uint64_t)ordered_key(v) << 32) | (uint32_t)(~e) : 0ull;
+  }
+  int my_e = 0;
+  float my_v = 0.f, top_v = 0.f;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = 0ull;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) best = key[i] > best ? key[i] : best;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      uint32_t lo = __shfl_xor((uint32_t)best, m), hi = __shfl_xor((uint32_t)(best >> 32), m);
+      uint64_t o = ((uint64_t)hi << 32) | lo;
+      best = o > best ? o : best;
+    }
+    // Remove the winner (keys are unique: the expert index is part of them).
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) key[i] = key[i] == best ? 0ull : key[i];
+    const int e = (int)(~(uint32_t)best);
+    const float v = key_to_value((uint32_t)(best >> 32));
+    if (j == 0) top_v = v;
+    if (lane == j) { my_e = e; my_v = v; }
+  }
+  float ex = lane < k ? expf(my_v - top_v) : 0.f;
+  float sum = ex;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) sum += __shfl_xor(sum, m);
+  out_e = my_e;
+  out_w = ex / sum;
+}
+
+// Exclusive position of a + b among all threads of a 1024-thread workgroup
+// (thread order, a before b) and the total.  wave_sum: 16 ints of LDS.
+__device__ __forceinline__ void block_scan_pair(int a, int b, int* wave_sum, int& excl_a,
+                                                int& total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int s = a + b;
+  int incl = s;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wave_sum[wave] = incl;
+  __syncthreads();
+  int before = 0, tot = 0;
+  for (int w = 0; w < 16; ++w) {
+    if (w < wave) before += wave_sum[w];
+    tot += wave_sum[w];
+  }
+  excl_a = before + incl - s;
+  total = tot;
+  __syncthreads();
+}
+
+// counts[g] = cnt[g] and offsets = their exclusive prefix sum, for G <= 2047
+// groups; cnt is 2048 ints (zero past G); 1024-thread workgroup.  The offsets
+// are also left in offs_lds (G + 1 ints) when it is non-null.
+__device__ __forceinline__ void put_group(int g, int G, int c, int o, int32_t* counts,
+                                          int32_t* offsets, int* offs_lds) {
+  if (g < G) counts[g] = c;
+  if (g <= G) {
+    offsets[g] = o;
+    if (offs_lds) offs_lds[g] = o;
+  }
+}
+
+__device__ __forceinline__ void scan_groups(const int* cnt, int G, int32_t* counts,
+                                            int32_t* offsets, int* offs_lds, int* wave_sum) {
+  const int tid = threadIdx.x;
+  const int a = cnt[2 * tid], b = cnt[2 * tid + 1];
+  int excl, total;
+  block_scan_pair(a, b, wave_sum, excl, total);
+  (void)total;
+  put_group(2 * tid, G, a, excl, counts, offsets, offs_lds);
+  put_group(2 * tid + 1, G, b, excl + a, counts, offsets, offs_lds);
+}
+
+// Work lists of the grouped FFN from the group offsets (1024-thread
+// workgroup, G <= 2048): groups of 1 .. kSkinnyMax rows as 16-row slices,
+// larger groups as equal-height row tiles in bands of kTileBand.
+__device__ __forceinline__ void plan_groups(const int32_t* offsets, const Sched& sc,
+                                            int* wave_sum) {
+  const int tid = threadIdx.x, G = sc.G;
+  int m[2], sl[2], nt[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int g = 2 * tid + q;
+    m[q] = g < G ? offsets[g + 1] - offsets[g] : 0;
+    sl[q] = m[q] > 0 && m[q] <= kSkinnyMax ? ceil_div(m[q], kSliceRows) : 0;
+    nt[q] = m[q] > kSkinnyMax ? ceil_div(m[q], group_tile_rows(m[q], sc.tile_rows)) : 0;
+  }
+  int sl_pos, sl_total;
+  block_scan_pair(sl[0], sl[1], wave_sum, sl_pos, sl_total);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int first = sl_pos;
+    for (int i = 0; i < sl[q]; ++i) {
+      sc.skinny[4 * sl_pos] = 2 * tid + q;
+      sc.skinny[4 * sl_pos + 1] = i * kSliceRows;
+      sc.skinny[4 * sl_pos + 2] = first;
+      sc.skinny[4 * sl_pos + 3] = sl[q];
+      ++sl_pos;
+    }
+  }
+  if (tid == 0) *sc.n_skinny = sl_total;
+  int nt_pos, nt_total;
+  block_scan_pair(nt[0], nt[1], wave_sum, nt_pos, nt_total);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int g = 2 * tid + q;
+    const int first = nt_pos;
+    for (int i = 0; i < nt[q]; ++i) {
+      const int band = i / kTileBand;
+      sc.tiles[4 * nt_pos] = g;
+      sc.tiles[4 * nt_pos + 1] = i * group_tile_rows(m[q], sc.tile_rows);
+      sc.tiles[4 * nt_pos + 2] = first + band * kTileBand;
+      sc.tiles[4 * nt_pos + 3] = min(kTileBand, nt[q] - band * kTileBand);
+      ++nt_pos;
+    }
+  }
+  if (tid == 0) *sc.n_tiles = nt_total;
+}
+
+}  // namespace moe

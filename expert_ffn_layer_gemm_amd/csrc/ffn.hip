@@ -26,74 +26,14 @@
 // the device-side list length exit at once.  No host synchronisation.
 #include <algorithm>
 
-#include "ffn.hpp"
+#include "dispatch.hpp"
 
 namespace moe {
 
 // ------------------------------------------------------------------ plan ----
-__device__ __forceinline__ void block_scan_pair(int a, int b, int* wave_sum, int& excl_a,
-                                                int& total) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int s = a + b;
-  int incl = s;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    int o = __shfl_up(incl, d);
-    if (lane >= d) incl += o;
-  }
-  if (lane == 63) wave_sum[wave] = incl;
-  __syncthreads();
-  int before = 0, tot = 0;
-  for (int w = 0; w < 16; ++w) {
-    if (w < wave) before += wave_sum[w];
-    tot += wave_sum[w];
-  }
-  excl_a = before + incl - s;
-  total = tot;
-  __syncthreads();
-}
-
 __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ offsets, Sched sc) {
   __shared__ int wave_sum[16];
-  const int tid = threadIdx.x, G = sc.G;
-  int m[2], sl[2], nt[2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int g = 2 * tid + q;
-    m[q] = g < G ? offsets[g + 1] - offsets[g] : 0;
-    sl[q] = m[q] > 0 && m[q] <= kSkinnyMax ? ceil_div(m[q], kSliceRows) : 0;
-    nt[q] = m[q] > kSkinnyMax ? ceil_div(m[q], group_tile_rows(m[q], sc.tile_rows)) : 0;
-  }
-  int sl_pos, sl_total;
-  block_scan_pair(sl[0], sl[1], wave_sum, sl_pos, sl_total);
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int first = sl_pos;
-    for (int i = 0; i < sl[q]; ++i) {
-      sc.skinny[4 * sl_pos] = 2 * tid + q;
-      sc.skinny[4 * sl_pos + 1] = i * kSliceRows;
-      sc.skinny[4 * sl_pos + 2] = first;
-      sc.skinny[4 * sl_pos + 3] = sl[q];
-      ++sl_pos;
-    }
-  }
-  if (tid == 0) *sc.n_skinny = sl_total;
-  int nt_pos, nt_total;
-  block_scan_pair(nt[0], nt[1], wave_sum, nt_pos, nt_total);
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int g = 2 * tid + q;
-    const int first = nt_pos;
-    for (int i = 0; i < nt[q]; ++i) {
-      const int band = i / kTileBand;
-      sc.tiles[4 * nt_pos] = g;
-      sc.tiles[4 * nt_pos + 1] = i * group_tile_rows(m[q], sc.tile_rows);
-      sc.tiles[4 * nt_pos + 2] = first + band * kTileBand;
-      sc.tiles[4 * nt_pos + 3] = min(kTileBand, nt[q] - band * kTileBand);
-      ++nt_pos;
-    }
-  }
-  if (tid == 0) *sc.n_tiles = nt_total;
+  plan_groups(offsets, sc, wave_sum);
 }
 
 // ---------------------------------------------------------- skinny, bf16 ----
@@ -343,6 +283,14 @@ WsLayout ffn_layout(int T, int H, int E, int k, int I, int n_shared, bool fp8) {
 }
 }  // namespace
 
+Sched ffn_schedule(const FfnArgs& f) {
+  const WsLayout L = ffn_layout(f.T, f.H, f.E, f.k, f.I, f.n_shared, f.fp8);
+  uint8_t* ws = static_cast<uint8_t*>(f.workspace);
+  return Sched{reinterpret_cast<int32_t*>(ws + L.n_skinny), reinterpret_cast<int32_t*>(ws + L.n_tiles),
+               reinterpret_cast<int32_t*>(ws + L.skinny), reinterpret_cast<int32_t*>(ws + L.tiles),
+               f.E + f.n_shared, tile_rows(f.fp8)};
+}
+
 size_t ffn_workspace_bytes(int T, int H, int E, int k, int I, int n_shared, bool fp8) {
   return ffn_layout(T, H, E, k, I, n_shared, fp8).total;
 }
@@ -384,12 +332,9 @@ static void launch_gemm(const char* name, Kern kern, int threads, long long bloc
 hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
   const WsLayout L = ffn_layout(f.T, f.H, f.E, f.k, f.I, f.n_shared, f.fp8);
   uint8_t* ws = static_cast<uint8_t*>(f.workspace);
-  const int G = f.E + f.n_shared;
-  Sched sc{reinterpret_cast<int32_t*>(ws + L.n_skinny), reinterpret_cast<int32_t*>(ws + L.n_tiles),
-           reinterpret_cast<int32_t*>(ws + L.skinny), reinterpret_cast<int32_t*>(ws + L.tiles), G,
-           tile_rows(f.fp8)};
+  const Sched sc = ffn_schedule(f);
   const long long R = (long long)f.T * (f.k + f.n_shared);
-  MOE_LAUNCH("plan", k_plan, dim3(1), dim3(1024), 0, s, f.offsets, sc);
+  if (!f.planned) MOE_LAUNCH("plan", k_plan, dim3(1), dim3(1024), 0, s, f.offsets, sc);
 
   uint8_t* h = ws + L.h;
   float* h_scale = f.fp8 ? reinterpret_cast<float*>(ws + L.h_scale) : nullptr;

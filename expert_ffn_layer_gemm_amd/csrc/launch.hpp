@@ -70,8 +70,20 @@ struct FfnArgs {
   // Upper bound on the rows of any group: T when the groups come from a top-k
   // routing (a token picks an expert once), R for caller-given offsets.
   long long max_group_rows;
+  // The work lists in the workspace were already built (by the small-batch
+  // routing + dispatch kernel); skip the planner.
+  bool planned;
 };
 size_t ffn_workspace_bytes(int T, int H, int E, int k, int I, int n_shared, bool fp8);
 hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s);
+
+// small.hip: histogram, offsets, ranks and the FFN work lists of a batch of
+// at most kSmallBatch tokens (k <= 16) in one single-workgroup launch.
+struct Sched;
+Sched ffn_schedule(const FfnArgs& a);   // the work lists inside a's workspace
+constexpr int kSmallBatch = 256;
+hipError_t launch_dispatch_small(const int32_t* idx, int32_t* counts, int32_t* offsets,
+                                 int32_t* dest, int32_t* src_row, const Sched& sc, int T, int E,
+                                 int k, int n_shared, hipStream_t s);
 
 }  // namespace moe

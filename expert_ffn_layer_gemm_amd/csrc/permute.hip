@@ -15,8 +15,7 @@
 //     prefix scan), a tile grid assigning ranks, and a wide grid gathering rows
 //     (x_perm[r] = x[src_row[r]], 16-byte lanes), quantising each 128-channel
 //     group to e4m3fn on the way for fp8 layers.
-#include "common.hpp"
-#include "launch.hpp"
+#include "dispatch.hpp"
 
 namespace moe {
 
@@ -61,24 +60,7 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ tile_cnt, i
   }
   if (tid == 0 && n_shared) cnt[E] = T;
   __syncthreads();
-  // Each thread owns entries 2*tid and 2*tid + 1.
-  const int a = cnt[2 * tid], b = cnt[2 * tid + 1];
-  int s = a + b, incl = s;
-  const int lane = tid & 63, wave = tid >> 6;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    int o = __shfl_up(incl, d);
-    if (lane >= d) incl += o;
-  }
-  if (lane == 63) wave_sum[wave] = incl;
-  __syncthreads();
-  int before = 0;
-  for (int w = 0; w < wave; ++w) before += wave_sum[w];
-  const int excl = before + incl - s;
-  if (2 * tid < G) { offsets[2 * tid] = excl; counts[2 * tid] = a; }
-  if (2 * tid + 1 < G) { offsets[2 * tid + 1] = excl + a; counts[2 * tid + 1] = b; }
-  if (2 * tid == G) offsets[G] = excl;
-  if (2 * tid + 1 == G) offsets[G] = excl + a;
+  scan_groups(cnt, G, counts, offsets, nullptr, wave_sum);
 }
 
 // Token-ascending rank of every (t, j) inside its expert's group: the tile's

@@ -23,7 +23,7 @@
 // slots best first.  The result does not depend on reduction order.
 #include <algorithm>
 
-#include "launch.hpp"
+#include "dispatch.hpp"
 #include "pipe.hpp"
 
 namespace moe {
@@ -189,19 +189,7 @@ __global__ __launch_bounds__(512) void k_router_tiled(const uint16_t* __restrict
 }
 
 // ------------------------------------------------------------------ top-k ----
-__device__ __forceinline__ uint32_t ordered_key(float v) {
-  uint32_t b = __float_as_uint(v);
-  if ((b & 0x7FFFFFFFu) == 0) b = 0;                 // -0 ties with +0
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-
-__device__ __forceinline__ float key_to_value(uint32_t u) {
-  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
-}
-
-// One wave per token; NPL = logits per lane (E <= 64 NPL).  The logit of
-// expert e is parts[0][t][e] + ... + parts[KS-1][t][e] (+ bias[e]), summed in
-// that order; logits_out (may alias parts when KS == 1) receives it.
+// One wave per token (topk_token); NPL = logits per lane.
 template <int NPL>
 __global__ __launch_bounds__(256) void k_topk(const float* parts, int KS,
                                               const float* __restrict__ bias, float* logits_out,
@@ -210,47 +198,12 @@ __global__ __launch_bounds__(256) void k_topk(const float* parts, int KS,
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const size_t plane = (size_t)T * E;
-  uint64_t key[NPL];
-#pragma unroll
-  for (int i = 0; i < NPL; ++i) {
-    const int e = lane + 64 * i;
-    const size_t o = (size_t)t * E + min(e, E - 1);
-    float v = parts[o];
-    // Loads of 8 planes in flight at a time; the adds stay in plane order.
-#pragma unroll 8
-    for (int s2 = 1; s2 < KS; ++s2) v += parts[s2 * plane + o];
-    if (bias) v += bias[min(e, E - 1)];
-    if (logits_out && e < E) logits_out[o] = v;
-    key[i] = e < E ? ((uint64_t)ordered_key(v) << 32) | (uint32_t)(~e) : 0ull;
-  }
-  int my_e = 0;
-  float my_v = 0.f, top_v = 0.f;
-  for (int j = 0; j < k; ++j) {
-    uint64_t best = 0ull;
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) best = key[i] > best ? key[i] : best;
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      uint32_t lo = __shfl_xor((uint32_t)best, m), hi = __shfl_xor((uint32_t)(best >> 32), m);
-      uint64_t o = ((uint64_t)hi << 32) | lo;
-      best = o > best ? o : best;
-    }
-    // Remove the winner (keys are unique: the expert index is part of them).
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) key[i] = key[i] == best ? 0ull : key[i];
-    const int e = (int)(~(uint32_t)best);
-    const float v = key_to_value((uint32_t)(best >> 32));
-    if (j == 0) top_v = v;
-    if (lane == j) { my_e = e; my_v = v; }
-  }
-  float ex = lane < k ? expf(my_v - top_v) : 0.f;
-  float sum = ex;
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) sum += __shfl_xor(sum, m);
+  int e;
+  float w;
+  topk_token<NPL>(parts, KS, bias, logits_out, t, T, E, k, lane, e, w);
   if (lane < k) {
-    topk_idx[(size_t)t * k + lane] = my_e;
-    topk_w[(size_t)t * k + lane] = ex / sum;
+    topk_idx[(size_t)t * k + lane] = e;
+    topk_w[(size_t)t * k + lane] = w;
   }
 }
 

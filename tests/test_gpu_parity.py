@@ -271,7 +271,10 @@ def test_forward_deterministic(ci):
     assert torch.equal(ia, ib) and torch.equal(wa, wb)
 
 
-@pytest.mark.parametrize("case", ["T1", "T3_ragged", "E1k1", "kE", "one_hot_expert", "fp8_small"])
+# T <= 256 with E <= 256 runs routing and dispatch in one workgroup; the
+# T256/T257 pair straddles that boundary.
+@pytest.mark.parametrize("case", ["T1", "T3_ragged", "E1k1", "kE", "one_hot_expert", "fp8_small",
+                                  "T256_E256", "T257", "k16"])
 def test_forward_edge_cases(case):
     cfgs = {
         "T1": MoeConfig("T1", 30, T=1, H=256, E=8, k=2, I=256),
@@ -280,6 +283,9 @@ def test_forward_edge_cases(case):
         "kE": MoeConfig("kE", 33, T=50, H=256, E=6, k=6, I=256),
         "one_hot_expert": MoeConfig("hot", 34, T=300, H=256, E=8, k=1, I=384),
         "fp8_small": MoeConfig("f8", 35, T=77, H=512, E=12, k=3, I=256, n_shared=1, wdtype="fp8"),
+        "T256_E256": MoeConfig("t256", 36, T=256, H=256, E=256, k=8, I=128, n_shared=1, zipf_s=1.1),
+        "T257": MoeConfig("t257", 37, T=257, H=256, E=256, k=8, I=128, n_shared=1, zipf_s=1.1),
+        "k16": MoeConfig("k16", 38, T=100, H=256, E=64, k=16, I=128),
     }
     cfg = cfgs[case]
     li = generate_layer(cfg, DEV)
