@@ -25,6 +25,8 @@ Readings where the pages are silent (each also listed in the design doc):
   - rows inside an expert group are token-ascending; groups are unpadded.
   - shared expert = group E, rows T*k + t, weight 1, added after the routed sum.
   - fp8 layers: x and h are quantised per row per 128 channels (scale = amax/448).
+  - mxfp8 layers: weights, x and h are MXFP8 (E4M3 elements, one power-of-two
+    E8M0 scale per 32 values along the contraction dimension; oracle/mx.py).
 
 Parity status (pins in tests/test_oracle_*.py):
   router_logits  pinned (exact on small-integer inputs; W_r = 0 special case)
@@ -34,11 +36,14 @@ Parity status (pins in tests/test_oracle_*.py):
   combine        pinned (one-hot routing = inverse permutation, identical experts)
   forward        pinned on tiny and random micro shapes against an fp64
                  per-token brute force; at the large sizes it rests on those pins.
+  mx_*           pinned (closed-form exponents, exhaustive nearest-code search,
+                 exact round trips; tests/test_oracle_mx.py)
 """
 import numpy as np
 
 from .fp8_e4m3 import (quantize_groups_128, dequantize_groups_128,
                        dequantize_blocks_128x128)
+from .mx import mx_quantize_rows, mx_dequantize_rows
 
 F32 = np.float32
 
@@ -123,14 +128,32 @@ def expert_weights_f32(inputs: dict, e: int):
     """fp32 values of expert e's (W_gate [I,H], W_up [I,H], W_down [H,I]).
 
     bf16 weights widen exactly; fp8 weights are code value * block scale
-    (DeepSeek-deployment page, Quantization: one scale per 128x128 block).
+    (DeepSeek-deployment page, Quantization: one scale per 128x128 block);
+    mxfp8 weights are code value * 2^(E8M0 - 127) per 32 values along K.
     """
     if inputs["wdtype"] == "fp8":
         return (dequantize_blocks_128x128(inputs["w_gate"][e], inputs["s_gate"][e]),
                 dequantize_blocks_128x128(inputs["w_up"][e], inputs["s_up"][e]),
                 dequantize_blocks_128x128(inputs["w_down"][e], inputs["s_down"][e]))
+    if inputs["wdtype"] == "mxfp8":   # rows of [N, K], blocks of 32 along K
+        return (mx_dequantize_rows(inputs["w_gate"][e], inputs["s_gate"][e]),
+                mx_dequantize_rows(inputs["w_up"][e], inputs["s_up"][e]),
+                mx_dequantize_rows(inputs["w_down"][e], inputs["s_down"][e]))
     return (bf16_bits_to_f32(inputs["w_gate"][e]), bf16_bits_to_f32(inputs["w_up"][e]),
             bf16_bits_to_f32(inputs["w_down"][e]))
+
+
+def quantize_act(v: np.ndarray, wdtype: str) -> np.ndarray:
+    """Values an activation matrix [rows, C] takes as a GEMM operand.
+
+    bf16: itself.  fp8: quantised per row per 128 channels (DeepSeek-deployment
+    page, Quantization).  mxfp8: MXFP8 per row, blocks of 32 (oracle/mx.py).
+    """
+    if wdtype == "fp8":
+        return dequantize_groups_128(*quantize_groups_128(v))
+    if wdtype == "mxfp8":
+        return mx_dequantize_rows(*mx_quantize_rows(v))
+    return v
 
 
 def silu(z: np.ndarray) -> np.ndarray:
@@ -140,21 +163,21 @@ def silu(z: np.ndarray) -> np.ndarray:
 
 
 def expert_ffn(X: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray,
-               quantize_h: bool = False) -> np.ndarray:
+               quantize_h=False) -> np.ndarray:
     """One expert on its rows: h = silu(X Wg^T) * (X Wu^T); y = h Wd^T (fp32).
 
     SwiGLU as fused into the grouped matmul (Qwen3.5-397B on Ironwood, section
     4.2.2: gate and up projections, then swiglu(gate, up)).  For fp8 layers h
     is quantised per row per 128 channels before the down projection, as the
     DeepSeek-deployment page's SiLU kernel block-quantises its output
-    (Quantization section).
+    (Quantization section); for mxfp8 layers (quantize_h="mxfp8") h is MXFP8
+    per row like every MX GEMM operand.
     """
     G = np.matmul(X, wg.T, dtype=F32)
     U = np.matmul(X, wu.T, dtype=F32)
     h = (silu(G) * U).astype(F32)
-    if quantize_h:
-        codes, scales = quantize_groups_128(h)
-        h = dequantize_groups_128(codes, scales)
+    if quantize_h:   # True (fp8, the historical flag) or a weight dtype name
+        h = quantize_act(h, "fp8" if quantize_h is True else quantize_h)
     return np.matmul(h, wd.T, dtype=F32)
 
 
@@ -169,9 +192,12 @@ def grouped_ffn(x_perm: np.ndarray, offsets: np.ndarray, inputs: dict) -> np.nda
         if hi == lo:
             continue
         wg, wu, wd = expert_weights_f32(inputs, e)
-        y[lo:hi] = expert_ffn(x_perm[lo:hi], wg, wu, wd,
-                              quantize_h=inputs["wdtype"] == "fp8")
+        y[lo:hi] = expert_ffn(x_perm[lo:hi], wg, wu, wd, quantize_h=_h_quant(inputs["wdtype"]))
     return y
+
+
+def _h_quant(wdtype: str):
+    return wdtype if wdtype in ("fp8", "mxfp8") else False
 
 
 # --------------------------------------------------------------- combine ----
@@ -219,6 +245,11 @@ def forward(inputs: dict, logits_override=None) -> OracleResult:
         xc, xs = quantize_groups_128(x)
         x_perm_codes, x_perm_scales = xc[src_row], xs[src_row]
         x_perm = dequantize_groups_128(x_perm_codes, x_perm_scales)
+    elif inputs["wdtype"] == "mxfp8":
+        # MXFP8 activations per token, blocks of 32 channels.
+        xc, xs = mx_quantize_rows(x)
+        x_perm_codes, x_perm_scales = xc[src_row], xs[src_row]
+        x_perm = mx_dequantize_rows(x_perm_codes, x_perm_scales)
     else:
         x_perm_codes = x_perm_scales = None
         x_perm = permute_rows(x, src_row)
@@ -248,17 +279,15 @@ def forward_tokens(inputs: dict, tokens, logits_override=None) -> OracleResult:
     logits = (router_logits(x, inputs["w_router"], inputs.get("router_bias"))
               if logits_override is None else np.asarray(logits_override, dtype=F32))
     idx, w = topk_softmax(logits, k)
-    fp8 = inputs["wdtype"] == "fp8"
-    if fp8:
-        xc, xs = quantize_groups_128(x)
-        x = dequantize_groups_128(xc, xs)
+    hq = _h_quant(inputs["wdtype"])
+    x = quantize_act(x, inputs["wdtype"])
     H = x.shape[1]
     y = np.zeros((n, k + ns, H), dtype=F32)       # expert output of each (token, slot)
     for e in sorted(set(idx.ravel().tolist())):
         rows, slots = np.nonzero(idx == e)
-        y[rows, slots] = expert_ffn(x[rows], *expert_weights_f32(inputs, e), quantize_h=fp8)
+        y[rows, slots] = expert_ffn(x[rows], *expert_weights_f32(inputs, e), quantize_h=hq)
     for s_ in range(ns):
-        y[:, k + s_] = expert_ffn(x, *expert_weights_f32(inputs, E + s_), quantize_h=fp8)
+        y[:, k + s_] = expert_ffn(x, *expert_weights_f32(inputs, E + s_), quantize_h=hq)
     out = np.zeros((n, H), dtype=F32)
     for j in range(k):
         out = (out + (w[:, j:j + 1] * y[:, j]).astype(F32)).astype(F32)

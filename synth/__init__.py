@@ -5,5 +5,5 @@ tests.  It only draws random numbers and casts them to the storage formats the
 layer consumes; it holds none of the layer's arithmetic (no routing, no
 permutation, no GEMM, no activation quantisation).
 """
-from .configs import CONFIGS, MoeConfig, config_by_name  # noqa: F401
+from .configs import CONFIGS, EXTRA_CONFIGS, MoeConfig, config_by_name  # noqa: F401
 from .generate import generate_layer, generate_expert, to_numpy_inputs, LayerInputs  # noqa: F401

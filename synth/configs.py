@@ -26,7 +26,8 @@ class MoeConfig:
     k: int          # experts per token
     I: int          # SwiGLU intermediate size
     n_shared: int = 0           # always-on shared experts (0 or 1)
-    wdtype: str = "bf16"        # "bf16" or "fp8" (e4m3fn codes + fp32 128x128 block scales)
+    wdtype: str = "bf16"        # "bf16", "fp8" (e4m3fn codes + fp32 128x128 block scales) or
+                                # "mxfp8" (e4m3fn codes + E8M0 scales per 32 along K)
     zipf_s: Optional[float] = None  # Zipf exponent of the per-expert router-logit bias
     w_std: float = 0.02
     router_std: float = 0.02
@@ -52,8 +53,18 @@ CONFIGS = [
 ]
 
 
+# Further workloads (not among the five above): the Qwen3-235B-like layer with
+# MXFP8 experts, as "Hosting Qwen on Blackwell" (Quantization) deploys it.
+EXTRA_CONFIGS = [
+    MoeConfig("qwen3_235b_decode_mxfp8", 5, T=64, H=4096, E=128, k=8, I=1536, wdtype="mxfp8",
+              regime="hbm"),
+    MoeConfig("qwen3_235b_prefill_mxfp8", 6, T=8192, H=4096, E=128, k=8, I=1536, wdtype="mxfp8",
+              regime="mfma"),
+]
+
+
 def config_by_name(name: str) -> MoeConfig:
-    for c in CONFIGS:
+    for c in CONFIGS + EXTRA_CONFIGS:
         if c.name == name:
             return c
     raise KeyError(f"unknown config {name!r}; known: {[c.name for c in CONFIGS]}")

@@ -9,8 +9,12 @@ Recipe (per config):
   regenerated): W_gate[e], W_up[e] [I, H] and W_down[e] [H, I] ~ N(0, w_std),
   cast to bf16; or, for "fp8" configs, converted offline to e4m3fn codes with
   one fp32 scale per 128x128 block (scale = block amax / 448, 1 for an all-zero
-  block; codes = torch's e4m3fn cast of the clamped quotient).  This static
-  weight conversion is input preparation: the layer consumes codes + scales.
+  block; codes = torch's e4m3fn cast of the clamped quotient); or, for
+  "mxfp8" configs, to MXFP8: e4m3fn codes with one power-of-two scale per 32
+  values along K (E8M0 byte = floor(log2(amax)) - 8 + 127, 0 for an all-zero
+  block; codes = torch's e4m3fn cast of the quotient clamped to +-448).  This
+  static weight conversion is input preparation: the layer consumes codes +
+  scales.
 
 Every tensor is drawn from its own torch.Generator seeded by
 (config seed, tensor id, expert id); tensor ids: 0 x, 1 W_r, 2 W_gate,
@@ -41,9 +45,9 @@ class LayerInputs:
     w_gate: torch.Tensor                  # [G, I, H] bf16 | uint8 e4m3fn codes
     w_up: torch.Tensor                    # [G, I, H]
     w_down: torch.Tensor                  # [G, H, I]
-    s_gate: Optional[torch.Tensor] = None  # [G, I/128, H/128] fp32
+    s_gate: Optional[torch.Tensor] = None  # fp8: [G, I/128, H/128] fp32; mxfp8: [G, I, H/32] uint8
     s_up: Optional[torch.Tensor] = None
-    s_down: Optional[torch.Tensor] = None  # [G, H/128, I/128] fp32
+    s_down: Optional[torch.Tensor] = None  # fp8: [G, H/128, I/128] fp32; mxfp8: [G, H, I/32] uint8
 
     def to(self, device) -> "LayerInputs":
         f = lambda t: None if t is None else t.to(device)
@@ -61,6 +65,18 @@ def _fp8_blocks(w: torch.Tensor):
     q = (blocks / scale[:, None, :, None]).clamp_(-E4M3_MAX, E4M3_MAX)
     codes = q.reshape(n, k).to(torch.float8_e4m3fn).view(torch.uint8)
     return codes, scale.contiguous()
+
+
+def _mx_rows(w: torch.Tensor):
+    """Static conversion of an fp32 [N, K] matrix to MXFP8: e4m3fn codes + E8M0 per 32 along K."""
+    n, k = w.shape
+    blocks = w.reshape(n, k // 32, 32)
+    amax = blocks.abs().amax(dim=-1)
+    _, ex = torch.frexp(torch.where(amax > 0, amax, torch.ones_like(amax)))
+    e = torch.where(amax > 0, ex - 1 - 8, torch.full_like(ex, -127)).clamp_(-127, 127)
+    q = (blocks * torch.exp2(-e.to(torch.float32))[..., None]).clamp_(-E4M3_MAX, E4M3_MAX)
+    codes = q.reshape(n, k).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, (e + 127).to(torch.uint8)
 
 
 def generate_expert(cfg: MoeConfig, e: int, device="cpu"):
@@ -84,9 +100,10 @@ def generate_layer(cfg: MoeConfig, device="cpu") -> LayerInputs:
         rho = torch.randperm(E, generator=_gen(device, cfg.seed, 5), device=device) + 1
         bias = (-cfg.zipf_s * torch.log(rho.to(torch.float64))).to(torch.float32)
     fp8 = cfg.wdtype == "fp8"
-    if fp8:
-        assert H % 128 == 0 and I % 128 == 0, "fp8 block scaling needs H, I multiples of 128"
-    wdt = torch.uint8 if fp8 else torch.bfloat16
+    mx = cfg.wdtype == "mxfp8"
+    if fp8 or mx:
+        assert H % 128 == 0 and I % 128 == 0, "8-bit weights need H, I multiples of 128"
+    wdt = torch.uint8 if (fp8 or mx) else torch.bfloat16
     w_gate = torch.empty((G, I, H), dtype=wdt, device=device)
     w_up = torch.empty((G, I, H), dtype=wdt, device=device)
     w_down = torch.empty((G, H, I), dtype=wdt, device=device)
@@ -95,12 +112,20 @@ def generate_layer(cfg: MoeConfig, device="cpu") -> LayerInputs:
         s_gate = torch.empty((G, I // 128, H // 128), dtype=torch.float32, device=device)
         s_up = torch.empty_like(s_gate)
         s_down = torch.empty((G, H // 128, I // 128), dtype=torch.float32, device=device)
+    if mx:
+        s_gate = torch.empty((G, I, H // 32), dtype=torch.uint8, device=device)
+        s_up = torch.empty_like(s_gate)
+        s_down = torch.empty((G, H, I // 32), dtype=torch.uint8, device=device)
     for e in range(G):
         wg, wu, wd = generate_expert(cfg, e, device)
         if fp8:
             w_gate[e], s_gate[e] = _fp8_blocks(wg)
             w_up[e], s_up[e] = _fp8_blocks(wu)
             w_down[e], s_down[e] = _fp8_blocks(wd)
+        elif mx:
+            w_gate[e], s_gate[e] = _mx_rows(wg)
+            w_up[e], s_up[e] = _mx_rows(wu)
+            w_down[e], s_down[e] = _mx_rows(wd)
         else:
             w_gate[e] = wg.to(torch.bfloat16)
             w_up[e] = wu.to(torch.bfloat16)

@@ -2,8 +2,9 @@
 
 No permutation, no grouping: for each token, pick its experts by sorting all
 experts with the key (-logit, index), weight them with a float64 softmax over
-the picked logits, and sum w_j * FFN_e(x_t).  FP8 quantisation (fp8 layers only)
-uses torch's e4m3fn cast as the codec, so it shares nothing with the oracle's.
+the picked logits, and sum w_j * FFN_e(x_t).  FP8 quantisation (fp8 and mxfp8
+layers) uses torch's e4m3fn cast as the codec and torch.frexp for the MX
+scale exponent, so it shares nothing with the oracle's.
 """
 import numpy as np
 import torch
@@ -28,7 +29,27 @@ def _quant_dequant_rows_torch(v64):
     return (q * s[..., None].double()).reshape(rows, C).numpy()
 
 
+def _mx_quant_dequant_rows_torch(v64):
+    """Per row, blocks of 32 columns: X = 2^(floor(log2 amax) - 8) (torch.frexp),
+    codes = torch e4m3fn cast of v / X clamped to +-448; returns codes * X."""
+    v = torch.from_numpy(v64.astype(np.float32)).double()
+    rows, C = v.shape
+    g = v.reshape(rows, C // 32, 32)
+    amax = g.abs().amax(-1)
+    _, ex = torch.frexp(torch.where(amax > 0, amax, torch.ones_like(amax)))
+    e = torch.where(amax > 0, ex - 9, torch.full_like(ex, -127)).clamp(-127, 127).double()
+    q = torch.ldexp(g, -e[..., None]).clamp(-448.0, 448.0).float().to(torch.float8_e4m3fn).double()
+    return torch.ldexp(q, e[..., None]).reshape(rows, C).numpy()
+
+
 def _weights64(inp, e):
+    if inp["wdtype"] == "mxfp8":
+        def dqm(c, s):
+            n, k = c.shape
+            return (_e4m3_values(c).reshape(n, k // 32, 32)
+                    * np.exp2(s.astype(np.float64) - 127.0)[..., None]).reshape(n, k)
+        return (dqm(inp["w_gate"][e], inp["s_gate"][e]), dqm(inp["w_up"][e], inp["s_up"][e]),
+                dqm(inp["w_down"][e], inp["s_down"][e]))
     if inp["wdtype"] == "fp8":
         def dq(c, s):
             n, k = c.shape
@@ -46,18 +67,20 @@ def layer_bruteforce(inp):
     Wr = inp["w_router"].astype(np.float64)          # [E, H]
     E = Wr.shape[0]
     k, ns, fp8 = inp["k"], inp["n_shared"], inp["wdtype"] == "fp8"
+    mx = inp["wdtype"] == "mxfp8"
+    quant = _mx_quant_dequant_rows_torch if mx else _quant_dequant_rows_torch
     logits = x @ Wr.T
     if inp.get("router_bias") is not None:
         logits = logits + inp["router_bias"].astype(np.float64)
-    xin = _quant_dequant_rows_torch(x) if fp8 else x
+    xin = quant(x) if (fp8 or mx) else x
     W = [_weights64(inp, e) for e in range(E + ns)]
 
     def ffn(e, xt):
         wg, wu, wd = W[e]
         g, u = wg @ xt, wu @ xt
         h = g / (1.0 + np.exp(-g)) * u
-        if fp8:
-            h = _quant_dequant_rows_torch(h[None, :])[0]
+        if fp8 or mx:
+            h = quant(h[None, :])[0]
         return wd @ h
 
     out = np.zeros((T, H))

@@ -123,3 +123,27 @@ def test_forward_tokens_fp8_shared_vs_bruteforce():
     ok = gap > 1e-5
     assert np.array_equal(part.topk_idx[ok], ref_idx[ok])
     assert _rel_inf(part.out[ok], ref[ok]) <= 2e-2
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_mxfp8_micro_shapes_vs_bruteforce(case):
+    """MXFP8 layers (weights, x and h in MX blocks of 32) against the float64
+    brute force, whose MX codec is torch.frexp + torch's e4m3fn cast."""
+    rng = np.random.default_rng(2000 + case)
+    E = int(rng.integers(1, 10))
+    cfg = MoeConfig(f"mx{case}", 200 + case, T=int(rng.integers(1, 33)),
+                    H=int(rng.choice([128, 256])), E=E, k=int(rng.integers(1, min(E, 4) + 1)),
+                    I=int(rng.choice([128, 256])), n_shared=int(case % 2), wdtype="mxfp8",
+                    zipf_s=1.1 if case % 3 == 1 else None)
+    # as for fp8: h quantised from fp32 vs float64 sums may differ by one code
+    _check_against_bruteforce(cfg, 2e-2)
+
+
+def test_mxfp8_forward_tokens_matches_full_forward():
+    cfg = MoeConfig("mxs", 12, T=24, H=256, E=6, k=2, I=128, n_shared=1, wdtype="mxfp8")
+    inp = to_numpy_inputs(generate_layer(cfg))
+    full = forward(inp)
+    toks = np.array([0, 5, 23, 11])
+    part = oracle.forward_tokens(inp, toks)
+    assert np.array_equal(part.topk_idx, full.topk_idx[toks])
+    assert _rel_inf(part.out, full.out[toks]) <= 1e-5
