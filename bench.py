@@ -72,7 +72,8 @@ def cpu_baseline(cfg, li, n_tokens):
 
 
 CPU_TOKENS = {"tiny": 64, "qwen3_235b_decode": 64, "qwen3_235b_prefill": 256,
-              "qwen35_397b_zipf": 128, "deepseek_v3_fp8": 16}
+              "qwen35_397b_zipf": 128, "deepseek_v3_fp8": 16,
+              "qwen3_235b_decode_mxfp8": 64, "qwen3_235b_prefill_mxfp8": 256}
 
 
 def main():
@@ -157,7 +158,7 @@ def main():
     counts = np.bincount(idx.cpu().numpy().ravel(), minlength=cfg.E)
     if cfg.n_shared:
         counts = np.concatenate([counts, [cfg.T] * cfg.n_shared])
-    dtype = "fp8" if cfg.wdtype == "fp8" else "bf16"
+    dtype = cfg.wdtype if cfg.wdtype in ("fp8", "mxfp8") else "bf16"
     kern_s = float(np.mean(kern_ms)) / 1e3
     if dom_name.startswith(("skinny_", "tiled_")):
         work = acc.kernel_work(dom_name, counts, cfg.H, cfg.I, cfg.wdtype)

@@ -18,6 +18,7 @@ MOE_ERR_WORKSPACE = -3
 MOE_ERR_HIP = -4
 MOE_BF16 = 0
 MOE_FP8_E4M3_BLOCK128 = 1
+MOE_MXFP8 = 2
 
 # Every function include/moe.h declares, with (restype, argtypes).
 _P = ctypes.c_void_p
@@ -78,7 +79,7 @@ def lib() -> ctypes.CDLL:
 
 def make_shape(T, H, E, k, I, n_shared=0, wdtype=MOE_BF16) -> MoeShape:
     if isinstance(wdtype, str):
-        wdtype = {"bf16": MOE_BF16, "fp8": MOE_FP8_E4M3_BLOCK128}[wdtype]
+        wdtype = {"bf16": MOE_BF16, "fp8": MOE_FP8_E4M3_BLOCK128, "mxfp8": MOE_MXFP8}[wdtype]
     return MoeShape(T, H, E, k, I, n_shared, wdtype)
 
 

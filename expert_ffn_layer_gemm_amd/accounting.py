@@ -18,7 +18,7 @@ import numpy as np
 
 # MI355X published peaks (dense, no sparsity).
 PEAK_HBM_GBS = 8000.0
-PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp32": 157.3}
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp8": 5000.0, "fp32": 157.3}
 
 # Split of the grouped-FFN schedule, the same threshold as the C++ schedule
 # (csrc/ffn.hpp kSkinnyMax): groups of up to 64 rows go to the weight-streaming
@@ -60,7 +60,25 @@ class Work:
 
 
 def _elt(wdtype: str) -> int:
-    return 1 if wdtype == "fp8" else 2
+    return 1 if wdtype in ("fp8", "mxfp8") else 2
+
+
+def _scale_bytes(rows: float, cols: int, wdtype: str) -> float:
+    """Scale bytes of a [rows, cols] operand quantised along cols: fp8 one fp32
+    per 128 values of a row; mxfp8 one E8M0 byte per 32."""
+    if wdtype == "fp8":
+        return rows * (cols // 128) * 4
+    if wdtype == "mxfp8":
+        return rows * (cols // 32)
+    return 0.0
+
+
+def _weight_scale_bytes(g: int, n: int, k: int, wdtype: str) -> float:
+    """Scale bytes of g weight matrices [n, k]: fp8 one fp32 per 128 x 128 block,
+    mxfp8 one E8M0 byte per 32 values of a row along k."""
+    if wdtype == "fp8":
+        return g * (n // 128) * (k // 128) * 4
+    return _scale_bytes(g * n, k, wdtype)
 
 
 def kernel_groups(kernel: str, counts: np.ndarray) -> np.ndarray:
@@ -78,17 +96,16 @@ def kernel_work(kernel: str, counts: np.ndarray, H: int, I: int, wdtype: str) ->
     """Algorithmic bytes and FLOPs of one launch of a grouped-FFN kernel."""
     m = kernel_groups(kernel, counts).astype(np.float64)
     e = _elt(wdtype)
-    fp8 = wdtype == "fp8"
     rows = float(m.sum())
     g = len(m)
     if "_gateup_" in kernel:
-        w = g * 2 * I * H * e + (g * 2 * (I // 128) * (H // 128) * 4 if fp8 else 0)
-        a = rows * H * e + (rows * (H // 128) * 4 if fp8 else 0)
-        o = rows * I * e + (rows * (I // 128) * 4 if fp8 else 0)
+        w = g * 2 * I * H * e + 2 * _weight_scale_bytes(g, I, H, wdtype)
+        a = rows * H * e + _scale_bytes(rows, H, wdtype)
+        o = rows * I * e + _scale_bytes(rows, I, wdtype)
         return Work(w + a + o, 4.0 * rows * I * H, g)
     if "_down_" in kernel:
-        w = g * H * I * e + (g * (H // 128) * (I // 128) * 4 if fp8 else 0)
-        a = rows * I * e + (rows * (I // 128) * 4 if fp8 else 0)
+        w = g * H * I * e + _weight_scale_bytes(g, H, I, wdtype)
+        a = rows * I * e + _scale_bytes(rows, I, wdtype)
         o = rows * H * 2
         return Work(w + a + o, 2.0 * rows * H * I, g)
     raise ValueError(f"not a grouped-FFN kernel: {kernel}")
@@ -102,8 +119,7 @@ def layer_work(T: int, H: int, E: int, k: int, I: int, n_shared: int, wdtype: st
     touched = int((m > 0).sum())
     e = _elt(wdtype)
     wbytes = touched * 3 * H * I * e
-    if wdtype == "fp8":
-        wbytes += touched * 3 * (H // 128) * (I // 128) * 4
+    wbytes += 2 * _weight_scale_bytes(touched, I, H, wdtype) + _weight_scale_bytes(touched, H, I, wdtype)
     byts = wbytes + 4 * H * E + T * H * 2 + T * H * 2
     R = T * (k + n_shared)
     flops = 2 * T * H * E + 2 * R * 3 * H * I

@@ -37,7 +37,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Shape checks shared by every entry point.
 int check_shape(const char* fn, const moe_shape* s, bool need_ffn_dims) {
   if (s == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s: shape is NULL", fn);
-  if (s->wdtype != MOE_BF16 && s->wdtype != MOE_FP8_E4M3_BLOCK128)
+  if (s->wdtype != MOE_BF16 && s->wdtype != MOE_FP8_E4M3_BLOCK128 && s->wdtype != MOE_MXFP8)
     return fail(MOE_ERR_INVALID_ARG, "%s: unknown wdtype %d", fn, s->wdtype);
   if (s->T < 0) return fail(MOE_ERR_UNSUPPORTED, "%s: T=%d < 0", fn, s->T);
   if (s->E < 1 || s->E > 1024) return fail(MOE_ERR_UNSUPPORTED, "%s: E=%d not in [1,1024]", fn, s->E);
@@ -60,17 +60,21 @@ int check_shape(const char* fn, const moe_shape* s, bool need_ffn_dims) {
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+// 8-bit codes with scales: per-128 fp32 block scales or MX E8M0 bytes.
+bool is_8bit(const moe_shape* s) { return s->wdtype != MOE_BF16; }
+bool is_mx(const moe_shape* s) { return s->wdtype == MOE_MXFP8; }
+
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 // moe_forward workspace: routing, dispatch and expert intermediates.  The
 // forward path never builds x_perm: the GEMMs gather their rows through
-// src_row from x (bf16) or from x quantised once per token (fp8: xq, xs).
+// src_row from x (bf16) or from x quantised once per token (fp8, mxfp8: xq, xs).
 struct FwdLayout {
   size_t logits, rpart, idx, w, counts, offsets, tcnt, dest, src_row, xq, xs, y_perm, ffn, total;
 };
 
 FwdLayout fwd_layout(const moe_shape* s) {
-  const bool fp8 = s->wdtype == MOE_FP8_E4M3_BLOCK128;
+  const bool fp8 = is_8bit(s), mx = is_mx(s);
   const size_t T = s->T, H = s->H, E = s->E, k = s->k, G = s->E + s->n_shared;
   const size_t R = T * (k + s->n_shared);
   FwdLayout L{};
@@ -85,10 +89,10 @@ FwdLayout fwd_layout(const moe_shape* s) {
   L.dest = off;    off += align256(T * k * 4);
   L.src_row = off; off += align256(R * 4);
   L.xq = off;      off += fp8 ? align256(T * H) : 0;
-  L.xs = off;      off += fp8 ? align256(T * (H / 128) * 4) : 0;
+  L.xs = off;      off += mx ? align256(T * (H / 32)) : fp8 ? align256(T * (H / 128) * 4) : 0;
   L.y_perm = off;  off += align256(R * H * 2);
   L.ffn = off;
-  off += moe::ffn_workspace_bytes(s->T, s->H, s->E, s->k, s->I, s->n_shared, fp8);
+  off += moe::ffn_workspace_bytes(s->T, s->H, s->E, s->k, s->I, s->n_shared, fp8, mx);
   L.total = off;
   return L;
 }
@@ -99,7 +103,7 @@ extern "C" {
 
 const char* moe_last_error(void) { return g_err; }
 
-int moe_abi_version(void) { return 2; }
+int moe_abi_version(void) { return 3; }
 
 size_t moe_forward_workspace_bytes(const moe_shape* shape) {
   if (check_shape("moe_forward_workspace_bytes", shape, true) != MOE_OK) return 0;
@@ -109,7 +113,7 @@ size_t moe_forward_workspace_bytes(const moe_shape* shape) {
 size_t moe_ffn_workspace_bytes(const moe_shape* shape) {
   if (check_shape("moe_ffn_workspace_bytes", shape, true) != MOE_OK) return 0;
   return moe::ffn_workspace_bytes(shape->T, shape->H, shape->E, shape->k, shape->I,
-                                  shape->n_shared, shape->wdtype == MOE_FP8_E4M3_BLOCK128);
+                                  shape->n_shared, is_8bit(shape), is_mx(shape));
 }
 
 size_t moe_route_workspace_bytes(const moe_shape* shape) {
@@ -171,11 +175,11 @@ size_t moe_permute_workspace_bytes(const moe_shape* shape) {
 
 int moe_permute(const moe_shape* shape, const int32_t* topk_idx, const void* x, int32_t* counts,
                 int32_t* offsets, int32_t* dest, int32_t* src_row, void* x_perm,
-                float* x_perm_scale, void* workspace, size_t ws_bytes, void* stream) {
+                void* x_perm_scale, void* workspace, size_t ws_bytes, void* stream) {
   const char* fn = "moe_permute";
   moe::prof_call_begin();
   if (int rc = check_shape(fn, shape, false)) return rc;
-  const bool fp8 = shape->wdtype == MOE_FP8_E4M3_BLOCK128;
+  const bool fp8 = is_8bit(shape), mx = is_mx(shape);
   MOE_NEED_PTR(counts);
   MOE_NEED_PTR(offsets);
   if (shape->T > 0) {
@@ -194,19 +198,19 @@ int moe_permute(const moe_shape* shape, const int32_t* topk_idx, const void* x, 
   return hip_status(moe::launch_permute(topk_idx, static_cast<const uint16_t*>(x), counts, offsets,
                                         dest, src_row, x_perm, x_perm_scale,
                                         static_cast<int32_t*>(workspace), shape->T, shape->H,
-                                        shape->E, shape->k, shape->n_shared, fp8,
+                                        shape->E, shape->k, shape->n_shared, fp8, mx,
                                         as_stream(stream)), fn);
 }
 
 int moe_grouped_ffn(const moe_shape* shape, const int32_t* offsets, const void* x_perm,
-                    const float* x_perm_scale, const void* w_gate, const void* w_up,
-                    const void* w_down, const float* s_gate, const float* s_up,
-                    const float* s_down, void* y_perm, void* workspace, size_t ws_bytes,
+                    const void* x_perm_scale, const void* w_gate, const void* w_up,
+                    const void* w_down, const void* s_gate, const void* s_up,
+                    const void* s_down, void* y_perm, void* workspace, size_t ws_bytes,
                     void* stream) {
   const char* fn = "moe_grouped_ffn";
   moe::prof_call_begin();
   if (int rc = check_shape(fn, shape, true)) return rc;
-  const bool fp8 = shape->wdtype == MOE_FP8_E4M3_BLOCK128;
+  const bool fp8 = is_8bit(shape);
   if (shape->T == 0) return MOE_OK;
   MOE_NEED_PTR(offsets);
   MOE_NEED_PTR(x_perm);
@@ -228,7 +232,7 @@ int moe_grouped_ffn(const moe_shape* shape, const int32_t* offsets, const void* 
   moe::FfnArgs a{shape->T, shape->H, shape->E, shape->k, shape->I, shape->n_shared, fp8,
                  offsets, nullptr, x_perm, x_perm_scale, w_gate, w_up, w_down, s_gate, s_up,
                  s_down, y_perm, workspace,
-                 (long long)shape->T * (shape->k + shape->n_shared), false};
+                 (long long)shape->T * (shape->k + shape->n_shared), false, is_mx(shape)};
   return hip_status(moe::launch_grouped_ffn(a, as_stream(stream)), fn);
 }
 
@@ -249,7 +253,7 @@ int moe_combine(const moe_shape* shape, const void* y_perm, const int32_t* dest,
 
 int moe_forward(const moe_shape* shape, const void* x, const float* w_router,
                 const float* router_bias, const void* w_gate, const void* w_up,
-                const void* w_down, const float* s_gate, const float* s_up, const float* s_down,
+                const void* w_down, const void* s_gate, const void* s_up, const void* s_down,
                 void* out, int32_t* topk_idx_out, float* topk_w_out, void* workspace,
                 size_t ws_bytes, void* stream) {
   const char* fn = "moe_forward";
@@ -257,7 +261,7 @@ int moe_forward(const moe_shape* shape, const void* x, const float* w_router,
   if (int rc = check_shape(fn, shape, true)) return rc;
   if ((long long)shape->T * shape->H * 2 >= (1LL << 32))   // 32-bit row offsets into x
     return fail(MOE_ERR_UNSUPPORTED, "%s: T*H*2 >= 2^32", fn);
-  const bool fp8 = shape->wdtype == MOE_FP8_E4M3_BLOCK128;
+  const bool fp8 = is_8bit(shape), mx = is_mx(shape);
   if (shape->T == 0) return MOE_OK;
   MOE_NEED_PTR(x);
   MOE_NEED_PTR(w_router);
@@ -291,7 +295,7 @@ int moe_forward(const moe_shape* shape, const void* x, const float* w_router,
   int32_t* dest = reinterpret_cast<int32_t*>(ws + L.dest);
   int32_t* src_row = reinterpret_cast<int32_t*>(ws + L.src_row);
   uint8_t* xq = fp8 ? ws + L.xq : nullptr;
-  float* xs = fp8 ? reinterpret_cast<float*>(ws + L.xs) : nullptr;
+  void* xs = fp8 ? static_cast<void*>(ws + L.xs) : nullptr;
   void* y_perm = ws + L.y_perm;
   hipStream_t s = as_stream(stream);
 
@@ -301,7 +305,7 @@ int moe_forward(const moe_shape* shape, const void* x, const float* w_router,
   float* parts = ks > 1 ? reinterpret_cast<float*>(ws + L.rpart) : logits;
   moe::FfnArgs a{shape->T, shape->H, shape->E, shape->k, shape->I, shape->n_shared, fp8,
                  offsets, src_row, fp8 ? static_cast<const void*>(xq) : x, xs, w_gate, w_up,
-                 w_down, s_gate, s_up, s_down, y_perm, ws + L.ffn, (long long)shape->T, false};
+                 w_down, s_gate, s_up, s_down, y_perm, ws + L.ffn, (long long)shape->T, false, mx};
   hipError_t e = moe::launch_router_gemm(static_cast<const uint16_t*>(x), w_router, parts,
                                          shape->T, shape->H, shape->E, s);
   if (e == hipSuccess)
@@ -315,10 +319,10 @@ int moe_forward(const moe_shape* shape, const void* x, const float* w_router,
   } else if (e == hipSuccess) {   // routing tables only: no row copy
     e = moe::launch_permute(idx, static_cast<const uint16_t*>(x), counts, offsets, dest, src_row,
                             nullptr, nullptr, reinterpret_cast<int32_t*>(ws + L.tcnt), shape->T,
-                            shape->H, shape->E, shape->k, shape->n_shared, fp8, s);
+                            shape->H, shape->E, shape->k, shape->n_shared, fp8, mx, s);
   }
   if (e == hipSuccess && fp8)
-    e = moe::launch_quantize_rows(static_cast<const uint16_t*>(x), xq, xs, shape->T, shape->H, s);
+    e = moe::launch_quantize_rows(static_cast<const uint16_t*>(x), xq, xs, shape->T, shape->H, mx, s);
   if (e == hipSuccess) e = moe::launch_grouped_ffn(a, s);
   if (e == hipSuccess)
     e = moe::launch_combine(static_cast<const uint16_t*>(y_perm), dest, w,

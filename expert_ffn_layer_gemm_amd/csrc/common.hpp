@@ -74,6 +74,22 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   return (c & 0x80u) ? -mag : mag;
 }
 
+// ----------------------------------------------------------------- MXFP8 ----
+// E8M0 code of an MX block (32 values) with absolute maximum amax >= 0:
+// floor(log2(amax)) - 8 + 127, clamped at 0 (an all-zero block, and blocks
+// below 2^-118, take 2^-127).  For a normal amax the biased fp32 exponent E
+// is floor(log2(amax)) + 127, so the code is max(E - 8, 0).
+__device__ __forceinline__ uint32_t mx_e8m0(float amax) {
+  const int E = (int)((__float_as_uint(amax) >> 23) & 0xFFu);
+  return (uint32_t)max(E - 8, 0);
+}
+
+// 2^-(code - 127) as fp32 (codes 0 .. 253): the factor that scales a block's
+// values into its e4m3 range, exactly.
+__device__ __forceinline__ float mx_inv_scale(uint32_t code) {
+  return __uint_as_float((254u - code) << 23);
+}
+
 // ----------------------------------------------------------------- MFMA ----
 // D(16x16 fp32) += A(16x32 bf16) * B(32x16 bf16).  Lane l supplies row l%16
 // of A and column l%16 of B, 8 consecutive k each; lane l receives
@@ -90,6 +106,15 @@ __device__ __forceinline__ f32x4_t mfma_fp8_16x16x128(const i32x8_t a, const i32
                                                      f32x4_t c) {
   // cbsz = blgp = 0 selects e4m3 for both operands; scale 127 = 2^0 (e8m0).
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// D += A(16x128 e4m3) * B(128x16 e4m3) with MX block scales: lane l holds
+// row / column l%16, bytes 0..15 at K 16*(l/16) and bytes 16..31 at K
+// 64 + 16*(l/16); its E8M0 scale (bits 7:0 of sa / sb) applies to K block
+// l/16 (K 32*(l/16) .. +32) of its row / column (measured on gfx950).
+__device__ __forceinline__ f32x4_t mfma_mx8_16x16x128(const i32x8_t a, const i32x8_t b, f32x4_t c,
+                                                      uint32_t sa, uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, (int)sa, 0, (int)sb);
 }
 
 // ------------------------------------------------------- wave reductions ----

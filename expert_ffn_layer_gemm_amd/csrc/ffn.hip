@@ -156,8 +156,8 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_fp8(const GemmArgs p) {
 
   const uint8_t* b0 = p.B0 + ((size_t)g * N + n0 + r16) * K + kq;
   const uint8_t* b1 = DUAL ? p.B1 + ((size_t)g * N + n0 + r16) * K + kq : nullptr;
-  const float* sb0 = p.s_B0 + ((size_t)g * (N / 128) + nblk) * KB;
-  const float* sb1 = DUAL ? p.s_B1 + ((size_t)g * (N / 128) + nblk) * KB : nullptr;
+  const float* sb0 = static_cast<const float*>(p.s_B0) + ((size_t)g * (N / 128) + nblk) * KB;
+  const float* sb1 = DUAL ? static_cast<const float*>(p.s_B1) + ((size_t)g * (N / 128) + nblk) * KB : nullptr;
   const uint8_t* arow[MB];
   bool aok[MB];
   const float* srow[MB][4];
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_fp8(const GemmArgs p) {
       const int rr = mb * 16 + (lane >> 4) * 4 + q;
       sok[mb][q] = rr < m;
       const int ps = row0 + (sok[mb][q] ? rr : 0);
-      srow[mb][q] = p.A_scale + (size_t)(p.a_rows ? p.a_rows[ps] : ps) * KB;
+      srow[mb][q] = static_cast<const float*>(p.A_scale) + (size_t)(p.a_rows ? p.a_rows[ps] : ps) * KB;
     }
   }
   f32x4_t acc0[MB], acc1[MB];
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_fp8(const GemmArgs p) {
             const float scale = am == 0.f ? 1.f : am / 448.f;
             const float qv = fminf(fmaxf(hv[mb][q] / scale, -448.f), 448.f);
             p.out[(size_t)(row0 + r) * N + n0 + r16] = (uint8_t)f32_to_e4m3(qv);
-            if (wave == 0 && r16 == 0) p.out_scale[(size_t)(row0 + r) * N128 + gcol] = scale;
+            if (wave == 0 && r16 == 0) static_cast<float*>(p.out_scale)[(size_t)(row0 + r) * N128 + gcol] = scale;
           }
         }
       }
@@ -254,6 +254,107 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_fp8(const GemmArgs p) {
   }
 }
 
+// ----------------------------------------------------------- skinny, mxfp8 ----
+// The 32 codes lane l contributes to an e4m3 MFMA 16x16x128 from a row whose
+// 128-K block starts at ptr - 16*(l/16): 16 bytes at K 16*(l/16) and 16 at
+// K 64 + 16*(l/16).
+__device__ __forceinline__ i32x8_t ld32(const uint8_t* ptr) {
+  const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(ptr);
+  const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(ptr + 64);
+  return i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                 (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+// Weight streaming for MXFP8 layers (16-row slices).  Wave w owns 16 output
+// columns; lane l loads its row's 32 codes of each 128-K block in the MFMA's
+// layout (16 bytes at K 16*(l/16), 16 at K 64 + 16*(l/16)) and the E8M0
+// scale of K block 4*kb + l/16 for its A row and its B row; the scaled MFMA
+// applies both, so the partial sums accumulate directly.  DUAL: h = silu(g) *
+// u is quantised per row in MX blocks of 32 columns (two adjacent waves share
+// a block; their row maxima meet in LDS).
+template <bool DUAL, int NW>
+__global__ __launch_bounds__(64 * NW) void k_skinny_mx(const GemmArgs p) {
+  static_assert(!DUAL || NW % 2 == 0, "an MX block of h spans two waves");
+  __shared__ float row_amax[NW][16];
+  int slot, nt;
+  if (!band_item(p.sc.skinny, *p.sc.n_skinny, p.n_ntile, slot, nt)) return;
+  const int g = p.sc.skinny[4 * slot], s0 = p.sc.skinny[4 * slot + 1];
+  const int row0 = p.offsets[g] + s0, m = min(16, p.offsets[g + 1] - row0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, q4 = lane >> 4;
+  const int K = p.K, N = p.N, KB = K / 128, K32 = K / 32;
+  const int n0 = (nt * NW + wave) * 16;
+
+  const size_t brow = (size_t)g * N + n0 + r16;
+  const uint8_t* b0 = p.B0 + brow * K + 16 * q4;
+  const uint8_t* b1 = DUAL ? p.B1 + brow * K + 16 * q4 : nullptr;
+  const uint8_t* sb0 = static_cast<const uint8_t*>(p.s_B0) + brow * K32;
+  const uint8_t* sb1 = DUAL ? static_cast<const uint8_t*>(p.s_B1) + brow * K32 : nullptr;
+  const bool aok = r16 < m;
+  const int pr = row0 + (aok ? r16 : 0);
+  const size_t arow_i = (size_t)(p.a_rows ? p.a_rows[pr] : pr);
+  const uint8_t* arow = p.A + arow_i * K + 16 * q4;
+  const uint8_t* sarow = static_cast<const uint8_t*>(p.A_scale) + arow_i * K32;
+
+  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  i32x8_t cur0 = ld32(b0), cur1{};
+  uint32_t cs0 = *reinterpret_cast<const uint32_t*>(sb0), cs1 = 0;
+  if (DUAL) { cur1 = ld32(b1); cs1 = *reinterpret_cast<const uint32_t*>(sb1); }
+  for (int kb = 0; kb < KB; ++kb) {
+    const bool more = kb + 1 < KB;
+    i32x8_t nxt0{}, nxt1{};
+    uint32_t ns0 = 0, ns1 = 0;
+    if (more) {
+      nxt0 = ld32(b0 + (kb + 1) * 128);
+      ns0 = *reinterpret_cast<const uint32_t*>(sb0 + 4 * (kb + 1));
+      if (DUAL) {
+        nxt1 = ld32(b1 + (kb + 1) * 128);
+        ns1 = *reinterpret_cast<const uint32_t*>(sb1 + 4 * (kb + 1));
+      }
+    }
+    // Rows past the slice feed zero codes (outputs never stored); the MFMA
+    // itself runs for the whole wave.
+    const i32x8_t a = aok ? ld32(arow + kb * 128) : i32x8_t{};
+    const uint32_t sa =
+        aok ? (*reinterpret_cast<const uint32_t*>(sarow + 4 * kb) >> (8 * q4)) & 0xFFu : 127u;
+    acc0 = mfma_mx8_16x16x128(a, cur0, acc0, sa, (cs0 >> (8 * q4)) & 0xFFu);
+    if (DUAL) acc1 = mfma_mx8_16x16x128(a, cur1, acc1, sa, (cs1 >> (8 * q4)) & 0xFFu);
+    if (more) { cur0 = nxt0; cs0 = ns0; if (DUAL) { cur1 = nxt1; cs1 = ns1; } }
+  }
+
+  if constexpr (DUAL) {
+    float hv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = q4 * 4 + q;
+      hv[q] = r < m ? silu_mul(acc0[q], acc1[q]) : 0.f;
+      const float am = wave_max_xor(fabsf(hv[q]), 16);
+      if (r16 == 0) row_amax[wave][r] = am;
+    }
+    __syncthreads();
+    const int N32 = N / 32;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = q4 * 4 + q;
+      if (r < m) {
+        const float am = fmaxf(row_amax[wave][r], row_amax[wave ^ 1][r]);
+        const uint32_t e8 = mx_e8m0(am);
+        const float qv = fminf(fmaxf(hv[q] * mx_inv_scale(e8), -448.f), 448.f);
+        p.out[(size_t)(row0 + r) * N + n0 + r16] = (uint8_t)f32_to_e4m3(qv);
+        if ((wave & 1) == 0 && r16 == 0)
+          static_cast<uint8_t*>(p.out_scale)[(size_t)(row0 + r) * N32 + n0 / 32] = (uint8_t)e8;
+      }
+    }
+  } else {
+    uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = q4 * 4 + q;
+      if (r < m) out[(size_t)(row0 + r) * N + n0 + r16] = (uint16_t)f32_to_bf16_bits(acc0[q]);
+    }
+  }
+}
+
 // ------------------------------------------------------------------- host ----
 namespace {
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
@@ -263,7 +364,7 @@ struct WsLayout {
   int max_tiles, max_slices;
 };
 
-WsLayout ffn_layout(int T, int H, int E, int k, int I, int n_shared, bool fp8) {
+WsLayout ffn_layout(int T, int H, int E, int k, int I, int n_shared, bool fp8, bool mx) {
   (void)H;
   WsLayout L{};
   const long long R = (long long)T * (k + n_shared);
@@ -272,7 +373,8 @@ WsLayout ffn_layout(int T, int H, int E, int k, int I, int n_shared, bool fp8) {
   L.max_tiles = (int)(R / tile_rows(fp8) + big_groups + 1);
   size_t off = 0;
   L.h = off;        off += align256((size_t)R * I * (fp8 ? 1 : 2));
-  L.h_scale = off;  off += fp8 ? align256((size_t)R * (I / 128) * 4) : 0;
+  // h scales: fp8 one fp32 per 128 channels, mxfp8 one E8M0 byte per 32
+  L.h_scale = off;  off += mx ? align256((size_t)R * (I / 32)) : fp8 ? align256((size_t)R * (I / 128) * 4) : 0;
   L.n_skinny = off; off += 256;
   L.n_tiles = off;  off += 256;
   L.max_slices = (int)std::min<long long>(4LL * G, R / kSliceRows + G);
@@ -284,15 +386,15 @@ WsLayout ffn_layout(int T, int H, int E, int k, int I, int n_shared, bool fp8) {
 }  // namespace
 
 Sched ffn_schedule(const FfnArgs& f) {
-  const WsLayout L = ffn_layout(f.T, f.H, f.E, f.k, f.I, f.n_shared, f.fp8);
+  const WsLayout L = ffn_layout(f.T, f.H, f.E, f.k, f.I, f.n_shared, f.fp8, f.mx);
   uint8_t* ws = static_cast<uint8_t*>(f.workspace);
   return Sched{reinterpret_cast<int32_t*>(ws + L.n_skinny), reinterpret_cast<int32_t*>(ws + L.n_tiles),
                reinterpret_cast<int32_t*>(ws + L.skinny), reinterpret_cast<int32_t*>(ws + L.tiles),
                f.E + f.n_shared, tile_rows(f.fp8)};
 }
 
-size_t ffn_workspace_bytes(int T, int H, int E, int k, int I, int n_shared, bool fp8) {
-  return ffn_layout(T, H, E, k, I, n_shared, fp8).total;
+size_t ffn_workspace_bytes(int T, int H, int E, int k, int I, int n_shared, bool fp8, bool mx) {
+  return ffn_layout(T, H, E, k, I, n_shared, fp8, mx).total;
 }
 
 // A second stream per host thread and device, with a fork and a join event:
@@ -330,14 +432,14 @@ static void launch_gemm(const char* name, Kern kern, int threads, long long bloc
 }
 
 hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
-  const WsLayout L = ffn_layout(f.T, f.H, f.E, f.k, f.I, f.n_shared, f.fp8);
+  const WsLayout L = ffn_layout(f.T, f.H, f.E, f.k, f.I, f.n_shared, f.fp8, f.mx);
   uint8_t* ws = static_cast<uint8_t*>(f.workspace);
   const Sched sc = ffn_schedule(f);
   const long long R = (long long)f.T * (f.k + f.n_shared);
   if (!f.planned) MOE_LAUNCH("plan", k_plan, dim3(1), dim3(1024), 0, s, f.offsets, sc);
 
   uint8_t* h = ws + L.h;
-  float* h_scale = f.fp8 ? reinterpret_cast<float*>(ws + L.h_scale) : nullptr;
+  void* h_scale = f.fp8 ? static_cast<void*>(ws + L.h_scale) : nullptr;
   GemmArgs up{};
   up.sc = sc;
   up.offsets = f.offsets;
@@ -379,17 +481,22 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
 
   // The tiled chain is enqueued first: its few large workgroups (one per CU)
   // start before the weight-streaming workgroups fill the machine.
+  const char* nm_tg = f.mx ? "tiled_gateup_mx" : f.fp8 ? "tiled_gateup_fp8" : "tiled_gateup_bf16";
+  const char* nm_td = f.mx ? "tiled_down_mx" : f.fp8 ? "tiled_down_fp8" : "tiled_down_bf16";
   up.n_ntile = f.I / 128;
   if (tiled)
-    launch_tiled(f.fp8 ? "tiled_gateup_fp8" : "tiled_gateup_bf16", f.fp8, true,
-                 (long long)L.max_tiles * up.n_ntile, up, ts);
+    launch_tiled(nm_tg, f.fp8, f.mx, true, (long long)L.max_tiles * up.n_ntile, up, ts);
   dn.n_ntile = ceil_div(f.H, 256);
   if (tiled)
-    launch_tiled(f.fp8 ? "tiled_down_fp8" : "tiled_down_bf16", f.fp8, false,
-                 (long long)L.max_tiles * dn.n_ntile, dn, ts);
+    launch_tiled(nm_td, f.fp8, f.mx, false, (long long)L.max_tiles * dn.n_ntile, dn, ts);
 
   // gate/up + SwiGLU, then down, of the groups of at most kSkinnyMax rows
-  if (f.fp8) {
+  if (f.mx) {
+    up.n_ntile = f.I / (16 * 8);
+    launch_gemm("skinny_gateup_mx", k_skinny_mx<true, 8>, 512, band_grid(L.max_slices, up.n_ntile), up, s);
+    dn.n_ntile = f.H / (16 * 4);
+    launch_gemm("skinny_down_mx", k_skinny_mx<false, 4>, 256, band_grid(L.max_slices, dn.n_ntile), dn, s);
+  } else if (f.fp8) {
     up.n_ntile = f.I / (16 * 8);
     launch_gemm("skinny_gateup_fp8", k_skinny_fp8<true, 8, 1>, 512, band_grid(L.max_slices, up.n_ntile), up, s);
     dn.n_ntile = f.H / (16 * 4);

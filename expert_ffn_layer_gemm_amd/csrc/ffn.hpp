@@ -78,18 +78,18 @@ struct GemmArgs {
   const int32_t* offsets;
   const int32_t* a_rows;   // optional: A row of permuted row r is a_rows[r] (gather on load)
   const uint8_t* A;
-  const float* A_scale;    // [R, K/128] (fp8)
+  const void* A_scale;     // fp8: [R, K/128] fp32; mxfp8: [R, K/32] E8M0 bytes
   const uint8_t* B0;
   const uint8_t* B1;       // up weights (dual) or unused
-  const float* s_B0;       // [G, N/128, K/128] (fp8)
-  const float* s_B1;
+  const void* s_B0;        // fp8: [G, N/128, K/128] fp32; mxfp8: [G, N, K/32] E8M0 bytes
+  const void* s_B1;
   uint8_t* out;            // bf16 or e4m3 codes
-  float* out_scale;        // [R, N/128] (fp8 dual)
+  void* out_scale;         // dual: fp8 [R, N/128] fp32; mxfp8 [R, N/32] E8M0 bytes
   int K, N, n_ntile;
 };
 
 // Tiled kernel launch (tiled.hip).
-hipError_t launch_tiled(const char* name, bool fp8, bool dual, long long blocks, const GemmArgs& a,
+hipError_t launch_tiled(const char* name, bool fp8, bool mx, bool dual, long long blocks, const GemmArgs& a,
                         hipStream_t s);
 
 }  // namespace moe

@@ -40,11 +40,11 @@ hipError_t launch_topk(const float* parts, int KS, const float* bias, float* log
 size_t permute_workspace_bytes(int T, int E);
 hipError_t launch_permute(const int32_t* topk_idx, const uint16_t* x, int32_t* counts,
                           int32_t* offsets, int32_t* dest, int32_t* src_row, void* x_perm,
-                          float* x_perm_scale, int32_t* tile_cnt, int T, int H, int E, int k,
-                          int n_shared, bool fp8, hipStream_t s);
+                          void* x_perm_scale, int32_t* tile_cnt, int T, int H, int E, int k,
+                          int n_shared, bool fp8, bool mx, hipStream_t s);
 // Per-token e4m3 quantisation of x (128-channel groups): the rows the fp8
 // GEMMs gather through src_row.
-hipError_t launch_quantize_rows(const uint16_t* x, uint8_t* xq, float* xs, int T, int H,
+hipError_t launch_quantize_rows(const uint16_t* x, uint8_t* xq, void* xs, int T, int H, bool mx,
                                 hipStream_t s);
 
 // combine.hip
@@ -58,13 +58,13 @@ struct FfnArgs {
   const int32_t* offsets;
   const int32_t* a_rows;    // nullptr: x_perm holds the permuted rows; else rows of x_perm gathered
   const void* x_perm;
-  const float* x_perm_scale;
+  const void* x_perm_scale;
   const void* w_gate;
   const void* w_up;
   const void* w_down;
-  const float* s_gate;
-  const float* s_up;
-  const float* s_down;
+  const void* s_gate;
+  const void* s_up;
+  const void* s_down;
   void* y_perm;
   void* workspace;
   // Upper bound on the rows of any group: T when the groups come from a top-k
@@ -73,8 +73,10 @@ struct FfnArgs {
   // The work lists in the workspace were already built (by the small-batch
   // routing + dispatch kernel); skip the planner.
   bool planned;
+  // MXFP8 operands (fp8 is then true as well: 8-bit codes).
+  bool mx = false;
 };
-size_t ffn_workspace_bytes(int T, int H, int E, int k, int I, int n_shared, bool fp8);
+size_t ffn_workspace_bytes(int T, int H, int E, int k, int I, int n_shared, bool fp8, bool mx);
 hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s);
 
 // small.hip: histogram, offsets, ranks and the FFN work lists of a batch of

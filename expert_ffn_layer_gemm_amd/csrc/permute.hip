@@ -149,10 +149,44 @@ size_t permute_workspace_bytes(int T, int E) {
   return (size_t)ceil_div(T, kRankTile) * E * sizeof(int32_t);
 }
 
+// x_perm[r] = MXFP8 codes of x[src_row[r]] (x[r] when src_row is null):
+// blocks of 32 channels, 4 lanes of 8 bf16 each; the block maximum is a
+// 4-lane xor reduction, E8M0 = max(biased exponent of amax - 8, 0), codes =
+// e4m3 of v * 2^-(E8M0 - 127) rounded to nearest even, saturated at 448.
+__global__ __launch_bounds__(256) void k_gather_mx(const int32_t* __restrict__ src_row,
+                                                   const uint16_t* __restrict__ x,
+                                                   uint8_t* __restrict__ x_perm,
+                                                   uint8_t* __restrict__ x_scale, int R, int H) {
+  const int chunks = H / 8;
+  for (int rr = 0; rr < kGatherRows; ++rr) {
+    const int r = blockIdx.x * kGatherRows + rr;
+    if (r >= R) return;
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + (size_t)(src_row ? src_row[r] : r) * H);
+    for (int c = threadIdx.x; c < chunks; c += 256) {
+      float v[8];
+      unpack_bf16x8(src[c], v);
+      float amax = 0.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(v[q]));
+      amax = wave_max_xor(amax, 4);
+      const uint32_t e8 = mx_e8m0(amax);
+      const float inv = mx_inv_scale(e8);
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint32_t code = f32_to_e4m3(fminf(fmaxf(v[q] * inv, -448.f), 448.f));
+        if (q < 4) lo |= code << (8 * q); else hi |= code << (8 * (q - 4));
+      }
+      *reinterpret_cast<uint2*>(x_perm + (size_t)r * H + c * 8) = make_uint2(lo, hi);
+      if ((c & 3) == 0) x_scale[(size_t)r * (H / 32) + c / 4] = (uint8_t)e8;
+    }
+  }
+}
+
 hipError_t launch_permute(const int32_t* topk_idx, const uint16_t* x, int32_t* counts,
                           int32_t* offsets, int32_t* dest, int32_t* src_row, void* x_perm,
-                          float* x_perm_scale, int32_t* tile_cnt, int T, int H, int E, int k,
-                          int n_shared, bool fp8, hipStream_t s) {
+                          void* x_perm_scale, int32_t* tile_cnt, int T, int H, int E, int k,
+                          int n_shared, bool fp8, bool mx, hipStream_t s) {
   const int n_tiles = ceil_div(T, kRankTile);
   if (T > 0)
     MOE_LAUNCH("tile_hist", k_tile_hist, dim3(n_tiles), dim3(kRankTile), 0, s, topk_idx, tile_cnt,
@@ -165,20 +199,27 @@ hipError_t launch_permute(const int32_t* topk_idx, const uint16_t* x, int32_t* c
   if (x_perm == nullptr) return hipGetLastError();
   const int R = T * (k + n_shared);
   const dim3 grid(ceil_div(R, kGatherRows));
-  if (fp8)
+  if (mx)
+    MOE_LAUNCH("gather_mx", k_gather_mx, grid, dim3(256), 0, s, src_row, x,
+               static_cast<uint8_t*>(x_perm), static_cast<uint8_t*>(x_perm_scale), R, H);
+  else if (fp8)
     MOE_LAUNCH("gather_fp8", k_gather_fp8, grid, dim3(256), 0, s, src_row, x,
-                       static_cast<uint8_t*>(x_perm), x_perm_scale, R, H);
+               static_cast<uint8_t*>(x_perm), static_cast<float*>(x_perm_scale), R, H);
   else
     MOE_LAUNCH("gather_bf16", k_gather_bf16, grid, dim3(256), 0, s, src_row, x,
-                       static_cast<uint16_t*>(x_perm), R, H);
+               static_cast<uint16_t*>(x_perm), R, H);
   return hipGetLastError();
 }
 
-hipError_t launch_quantize_rows(const uint16_t* x, uint8_t* xq, float* xs, int T, int H,
+hipError_t launch_quantize_rows(const uint16_t* x, uint8_t* xq, void* xs, int T, int H, bool mx,
                                 hipStream_t s) {
   if (T == 0) return hipSuccess;
-  MOE_LAUNCH("quantize_rows_fp8", k_gather_fp8, dim3(ceil_div(T, kGatherRows)), dim3(256), 0, s,
-             static_cast<const int32_t*>(nullptr), x, xq, xs, T, H);
+  if (mx)
+    MOE_LAUNCH("quantize_rows_mx", k_gather_mx, dim3(ceil_div(T, kGatherRows)), dim3(256), 0, s,
+               static_cast<const int32_t*>(nullptr), x, xq, static_cast<uint8_t*>(xs), T, H);
+  else
+    MOE_LAUNCH("quantize_rows_fp8", k_gather_fp8, dim3(ceil_div(T, kGatherRows)), dim3(256), 0, s,
+               static_cast<const int32_t*>(nullptr), x, xq, static_cast<float*>(xs), T, H);
   return hipGetLastError();
 }
 

@@ -82,11 +82,14 @@ __device__ __forceinline__ int b_row(int j, int wn, int r16) {
 
 }  // namespace
 
-template <bool FP8, bool DUAL, int WM, int WN, int BM, int NSA, int NSB, int RB>
+// MX (with FP8): MXFP8 operands; the E8M0 scales of each 32-value block of
+// the A and B rows are staged with the chunk and applied by the MFMA.
+template <bool FP8, bool DUAL, int WM, int WN, int BM, int NSA, int NSB, int RB, bool MX = false>
 __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
   // The body is device code only; the host pass needs just the launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
   static_assert(RB == 128 || (RB == 64 && !FP8), "fp8 MFMA K step needs 128-byte rows");
+  static_assert(!MX || FP8, "MX operands are 8-bit");
   // A (activation rows) and B (weight rows) have rings of their own: NSA and
   // NSB stages.  NSB = NSA + 1 keeps one more weight chunk in flight (weights
   // come from HBM once per band; the activation tile is an L2 hit for all but
@@ -105,11 +108,15 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
   constexpr int IPWB = B_BYTES / 1024 / NW;
   static_assert(IPWA * NW * 1024 == A_BYTES && IPWB * NW * 1024 == B_BYTES,
                 "a chunk must split evenly over the waves");
-  constexpr int SCALE_BYTES = FP8 ? NW * 256 : 0; // fp8 row scales (waves >= 4 load duplicates)
+  // Row scales of a chunk, 4 bytes per row (fp8: the fp32 scale of the row's
+  // 128-K block; MX: its 4 E8M0 bytes), one 4-byte DMA per lane; waves >= 4
+  // load duplicates.  MX also stages the B rows' E8M0 dwords after the B data.
+  constexpr int SCALE_BYTES = FP8 ? NW * 256 : 0;
   constexpr int A_STAGE = A_BYTES + SCALE_BYTES;
+  constexpr int B_STAGE = B_BYTES + (MX ? kBRows * 4 : 0);
   constexpr int B_RING = NSA * A_STAGE;           // byte offset of the B ring
   __shared__ __attribute__((aligned(1024)))
-  uint8_t lds[NSA * A_STAGE + NSB * B_BYTES + (FP8 ? 2 * kMaxKB * 4 : 0)];
+  uint8_t lds[NSA * A_STAGE + NSB * B_STAGE + (FP8 && !MX ? 2 * kMaxKB * 4 : 0)];
 
   int tslot, nt;
   if (!band_item(p.sc.tiles, *p.sc.n_tiles, p.n_ntile, tslot, nt)) return;
@@ -166,18 +173,31 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
     // Rows past the matrix (ragged last column tile) re-read its last row.
     boff[j] = (uint32_t)min(n0 + br + lane / LPR, N - 1) * (uint32_t)Kb + sl;
   }
-  constexpr int nvb = IPWB;                        // vm instructions per B chunk of this wave
-  const float* ssrc = nullptr;
-  float* bsc = reinterpret_cast<float*>(lds + NSA * A_STAGE + NSB * B_BYTES);   // fp8: [2][KB]
-  if constexpr (FP8) {
+  const int nvb = IPWB + ((MX && wave < 4) ? 1 : 0);   // vm instructions per B chunk of this wave
+  const uint8_t* ssrc = nullptr;    // this lane's row scales; chunk c at + 4 c bytes
+  const uint8_t* bssrc = nullptr;   // MX: this lane's B row's E8M0 bytes
+  float* bsc = reinterpret_cast<float*>(lds + NSA * A_STAGE + NSB * B_STAGE);   // fp8: [2][KB]
+  if constexpr (MX) {
     const int sr = row0 + min((wave & 3) * 64 + lane, mrows - 1);
-    ssrc = p.A_scale + (size_t)(p.a_rows ? p.a_rows[sr] : sr) * KB;
+    ssrc = static_cast<const uint8_t*>(p.A_scale) + (size_t)(p.a_rows ? p.a_rows[sr] : sr) * (K / 32);
+    if (wave < 4) {   // staged B row 64 wave + lane
+      int br = wave * 64 + lane;
+      const uint8_t* sB = static_cast<const uint8_t*>(p.s_B0);
+      if (DUAL && br >= 128) { sB = static_cast<const uint8_t*>(p.s_B1); br -= 128; }
+      bssrc = sB + ((size_t)g * N + min(n0 + br, N - 1)) * (K / 32);
+    }
+  } else if constexpr (FP8) {
+    const int sr = row0 + min((wave & 3) * 64 + lane, mrows - 1);
+    ssrc = reinterpret_cast<const uint8_t*>(static_cast<const float*>(p.A_scale) +
+                                            (size_t)(p.a_rows ? p.a_rows[sr] : sr) * KB);
     const int N128 = N / 128;
     for (int i = tid; i < 2 * KB; i += 64 * NW) {
       const int which = i / KB, kb = i % KB;
       float v;
-      if (DUAL) v = (which ? p.s_B1 : p.s_B0)[((size_t)g * N128 + nt) * KB + kb];
-      else v = p.s_B0[((size_t)g * N128 + min(n0 / 128 + which, N128 - 1)) * KB + kb];
+      const float* sB0 = static_cast<const float*>(p.s_B0);
+      const float* sB1 = static_cast<const float*>(p.s_B1);
+      if (DUAL) v = (which ? sB1 : sB0)[((size_t)g * N128 + nt) * KB + kb];
+      else v = sB0[((size_t)g * N128 + min(n0 / 128 + which, N128 - 1)) * KB + kb];
       bsc[i] = v;
     }
   }
@@ -206,29 +226,35 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
     if (c < NSA - 1 && c < nk) {
       dma_blocks<IPWA>(lds + c * A_STAGE, ab, aoff, av, (size_t)c * kRB, wave);
       if constexpr (FP8)
-        __builtin_amdgcn_global_load_lds(ssrc + c, (lds_ptr_t)(lds + c * A_STAGE + A_BYTES + wave * 256), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(ssrc + 4 * c, (lds_ptr_t)(lds + c * A_STAGE + A_BYTES + wave * 256), 4, 0, 0);
     }
-    if (c < nk) dma_blocks<IPWB>(lds + B_RING + c * B_BYTES, bb, boff, bv, (size_t)c * kRB, wave);
+    if (c < nk) {
+      dma_blocks<IPWB>(lds + B_RING + c * B_STAGE, bb, boff, bv, (size_t)c * kRB, wave);
+      if (MX && wave < 4)
+        __builtin_amdgcn_global_load_lds(bssrc + 4 * c, (lds_ptr_t)(lds + B_RING + c * B_STAGE + B_BYTES + wave * 256), 4, 0, 0);
+    }
   }
   for (int kc = 0; kc < nk; ++kc) {
     // A and B of chunk kc must have landed; the loads issued after them (A of
     // chunks kc+1 .. kc+NSA-2, B of chunks kc+1 .. kc+NSB-2) may stay in flight.
-    wait_vmcnt_le<(NSA - 2) * (IPWA + 1) + (NSB - 2) * IPWB>(
+    wait_vmcnt_le<(NSA - 2) * (IPWA + 1) + (NSB - 2) * (IPWB + 1)>(
         min(NSA - 2, nk - 1 - kc) * nva + max(0, min(NSB - 2, nk - 1 - kc)) * nvb);
     lds_barrier();          // every wave's share, and every wave is done with chunk kc - 1
     if (kc + NSA - 1 < nk) {   // into the A stage of chunk kc - 1
       const int c = kc + NSA - 1;
       dma_blocks<IPWA>(lds + (c % NSA) * A_STAGE, ab, aoff, av, (size_t)c * kRB, wave);
       if constexpr (FP8)
-        __builtin_amdgcn_global_load_lds(ssrc + c, (lds_ptr_t)(lds + (c % NSA) * A_STAGE + A_BYTES + wave * 256), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(ssrc + 4 * c, (lds_ptr_t)(lds + (c % NSA) * A_STAGE + A_BYTES + wave * 256), 4, 0, 0);
     }
     if (kc + NSB - 1 < nk) {   // into the B stage of chunk kc - 1
       const int c = kc + NSB - 1;
-      dma_blocks<IPWB>(lds + B_RING + (c % NSB) * B_BYTES, bb, boff, bv, (size_t)c * kRB, wave);
+      dma_blocks<IPWB>(lds + B_RING + (c % NSB) * B_STAGE, bb, boff, bv, (size_t)c * kRB, wave);
+      if (MX && wave < 4)
+        __builtin_amdgcn_global_load_lds(bssrc + 4 * c, (lds_ptr_t)(lds + B_RING + (c % NSB) * B_STAGE + B_BYTES + wave * 256), 4, 0, 0);
     }
     if (!active) continue;
     const uint8_t* As = lds + (kc % NSA) * A_STAGE;
-    const uint8_t* Bs = lds + B_RING + (kc % NSB) * B_BYTES;
+    const uint8_t* Bs = lds + B_RING + (kc % NSB) * B_STAGE;
     // fp8 (memory-bound) multiplies every row block of an active wave, which
     // keeps its code branch-free; bf16 skips the row blocks past the group's end.
     if constexpr (!FP8) {
@@ -267,6 +293,29 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
         b[j] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       }
+      if constexpr (MX) {
+        // E8M0 dwords of the chunk (4 K blocks) per staged A row and B row;
+        // lane l takes byte l/16: the scale of its K block.
+        const uint32_t* asc = reinterpret_cast<const uint32_t*>(As + A_BYTES);
+        const uint32_t* bsw = reinterpret_cast<const uint32_t*>(Bs + B_BYTES);
+        const int sh = 8 * (lane >> 4);
+        uint32_t sbj[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) sbj[j] = (bsw[b_row<DUAL, WN, NB>(j, wn, r16)] >> sh) & 0xFFu;
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+          const int r = rbase + i * 16 + r16;
+          const uint8_t* rowp = As + r * kRB;
+          const u32x4_t lo = lds_read16(rowp + (slot<RB>(r, c0) << 4));
+          const u32x4_t hi = lds_read16(rowp + (slot<RB>(r, c1) << 4));
+          const i32x8_t a = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                    (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+          const uint32_t sa = (asc[r] >> sh) & 0xFFu;
+#pragma unroll
+          for (int j = 0; j < NB; ++j) acc[i][j] = mfma_mx8_16x16x128(a, b[j], acc[i][j], sa, sbj[j]);
+        }
+        continue;
+      }
       const float* ascale = reinterpret_cast<const float*>(As + A_BYTES);
       const float sb_lo = DUAL ? bsc[kc] : bsc[(wn * (256 / WN)) / 128 * KB + kc];
       const float sb_hi = DUAL ? bsc[KB + kc] : sb_lo;
@@ -304,7 +353,37 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
   }
 
   // Epilogue.  Lane holds rows rbase + 16 i + 4 (lane/16) + q of its blocks.
-  if constexpr (FP8 && DUAL) {
+  if constexpr (MX && DUAL) {
+    // The wave's 32 h columns are one MX block of each of its rows: row
+    // maxima by a 16-lane reduction, then E8M0 and codes.
+    constexpr int NH = NB / 2;
+    static_assert(NH * 16 == 32, "one MX block of h per wave");
+    const int N32 = N / 32;
+    const int hc0 = n0 + wn * (128 / WN);
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = rbase + i * 16 + (lane >> 4) * 4 + q;
+        float hv[NH], am = 0.f;
+#pragma unroll
+        for (int j = 0; j < NH; ++j) {
+          hv[j] = silu_mul(acc[i][j][q], acc[i][j + NH][q]);
+          am = fmaxf(am, fabsf(hv[j]));
+        }
+        am = wave_max_xor(am, 16);
+        if (i < nmb && r < mrows) {
+          const uint32_t e8 = mx_e8m0(am);
+          const float inv = mx_inv_scale(e8);
+#pragma unroll
+          for (int j = 0; j < NH; ++j) {
+            const float qv = fminf(fmaxf(hv[j] * inv, -448.f), 448.f);
+            p.out[(size_t)(row0 + r) * N + hc0 + j * 16 + r16] = (uint8_t)f32_to_e4m3(qv);
+          }
+          if (r16 == 0) static_cast<uint8_t*>(p.out_scale)[(size_t)(row0 + r) * N32 + hc0 / 32] = (uint8_t)e8;
+        }
+      }
+  } else if constexpr (FP8 && DUAL) {
     lds_barrier();                                    // stages are free: reuse for row maxima
     float* amax_s = reinterpret_cast<float*>(lds);    // [WN][kBM]
     constexpr int NH = NB / 2;                        // gate (= up) blocks per wave
@@ -342,7 +421,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
               p.out[(size_t)(row0 + r) * N + n0 + wn * (128 / WN) + j * 16 + r16] =
                   (uint8_t)f32_to_e4m3(qv);
             }
-            if (wn == 0 && r16 == 0) p.out_scale[(size_t)(row0 + r) * N128 + nt] = scale;
+            if (wn == 0 && r16 == 0) static_cast<float*>(p.out_scale)[(size_t)(row0 + r) * N128 + nt] = scale;
           }
         }
       }
@@ -378,14 +457,16 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
 #endif
 }
 
-hipError_t launch_tiled(const char* name, bool fp8, bool dual, long long blocks, const GemmArgs& a,
-                        hipStream_t s) {
+hipError_t launch_tiled(const char* name, bool fp8, bool mx, bool dual, long long blocks,
+                        const GemmArgs& a, hipStream_t s) {
   if (blocks <= 0) return hipSuccess;
   const dim3 grid((unsigned)band_grid(blocks, 1));
   // bf16 (compute-bound prefill groups): 256-row tiles, 2 stages.  fp8
   // (memory-bound ~128-row groups): 128-row tiles, 3 stages, two chunks in
   // flight.  The row counts match tile_rows() used by the schedule.
-  if (fp8 && dual) MOE_LAUNCH(name, (k_tiled3<true, true, 2, 4, 128, 3, 3, 128>), grid, dim3(512), 0, s, a);
+  if (mx && dual) MOE_LAUNCH(name, (k_tiled3<true, true, 2, 4, 128, 3, 3, 128, true>), grid, dim3(512), 0, s, a);
+  else if (mx) MOE_LAUNCH(name, (k_tiled3<true, false, 2, 4, 128, 3, 3, 128, true>), grid, dim3(512), 0, s, a);
+  else if (fp8 && dual) MOE_LAUNCH(name, (k_tiled3<true, true, 2, 4, 128, 3, 3, 128>), grid, dim3(512), 0, s, a);
   else if (fp8) MOE_LAUNCH(name, (k_tiled3<true, false, 2, 4, 128, 3, 3, 128>), grid, dim3(512), 0, s, a);
   else if (dual) MOE_LAUNCH(name, (k_tiled3<false, true, 2, 4, 256, TILED_BF16_NSA, TILED_BF16_NSB, TILED_BF16_RB>), grid, dim3(512), 0, s, a);
   else MOE_LAUNCH(name, (k_tiled3<false, false, 2, 4, 256, TILED_BF16_NSA, TILED_BF16_NSB, TILED_BF16_RB>), grid, dim3(512), 0, s, a);

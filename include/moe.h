@@ -60,8 +60,18 @@ typedef enum {
 
 typedef enum {
   MOE_BF16 = 0,              /* bf16 activations and expert weights */
-  MOE_FP8_E4M3_BLOCK128 = 1  /* e4m3fn expert weights + fp32 scale per 128x128
-                                block; x and h quantised per row per 128 channels */
+  MOE_FP8_E4M3_BLOCK128 = 1, /* e4m3fn expert weights + fp32 scale per 128x128
+                                block; x and h quantised per row per 128 channels
+                                ("Lower latency and higher throughput with
+                                multi-node DeepSeek deployment", Quantization) */
+  MOE_MXFP8 = 2              /* MXFP8: e4m3fn codes with one E8M0 (power-of-two)
+                                scale per 32 values along K, for the expert
+                                weights and for x and h per row ("Hosting Qwen
+                                on Blackwell", Quantization; "CuTeDSL at
+                                Perplexity": absolute max over 32 elements).
+                                E8M0 byte = floor(log2(amax)) - 8 + 127, 0 for
+                                an all-zero block; codes = round-to-nearest-even
+                                of v / 2^(byte - 127), saturated at +-448 */
 } moe_wdtype;
 
 /* Shape of one layer call.  G = E + n_shared expert groups; R = T*(k + n_shared)
@@ -138,8 +148,10 @@ size_t moe_permute_workspace_bytes(const moe_shape* shape);
  *   x_perm       [R, H], written: bf16 copy of x[src_row[r]], or for
  *                MOE_FP8_E4M3_BLOCK128 the e4m3fn codes of that row quantised
  *                per 128 channels (scale = amax / 448, 1 for an all-zero group,
- *                codes rounded to nearest even after clamping to +-448)
- *   x_perm_scale [R, H/128] fp32, written for fp8 (NULL for bf16)
+ *                codes rounded to nearest even after clamping to +-448), or for
+ *                MOE_MXFP8 its MXFP8 codes (blocks of 32)
+ *   x_perm_scale written for fp8 ([R, H/128] fp32) and mxfp8 ([R, H/32] uint8
+ *                E8M0); NULL for bf16
  *   workspace    >= moe_permute_workspace_bytes(shape) bytes of device memory,
  *                16-byte aligned (per-tile expert counts); caller-owned
  * Ranks come from counts and bit masks, not atomic counters: the same routing
@@ -148,7 +160,7 @@ size_t moe_permute_workspace_bytes(const moe_shape* shape);
  */
 int moe_permute(const moe_shape* shape, const int32_t* topk_idx, const void* x,
                 int32_t* counts, int32_t* offsets, int32_t* dest,
-                int32_t* src_row, void* x_perm, float* x_perm_scale,
+                int32_t* src_row, void* x_perm, void* x_perm_scale,
                 void* workspace, size_t ws_bytes, void* stream);
 
 /*
@@ -157,22 +169,26 @@ int moe_permute(const moe_shape* shape, const int32_t* topk_idx, const void* x,
  *   h = silu(X W_gate[g]^T) * (X W_up[g]^T)   (fp32 accumulation)
  *   y_perm rows = h W_down[g]^T                (fp32 accumulation, bf16 out)
  * bf16 layers keep h in bf16.  fp8 layers quantise h per row per 128
- * channels like x_perm before the down projection.
+ * channels like x_perm before the down projection; mxfp8 layers quantise h
+ * per row in MX blocks of 32, and the products are the block-scaled ones
+ * (each 32-value block's E8M0 scales applied to its partial sum).
  *   offsets      [G + 1] int32 (device; read only on the device)
- *   x_perm       [R, H] bf16 or e4m3fn codes; x_perm_scale [R, H/128] (fp8)
+ *   x_perm       [R, H] bf16 or e4m3fn codes; x_perm_scale [R, H/128] fp32
+ *                (fp8) or [R, H/32] uint8 E8M0 (mxfp8), NULL for bf16
  *   w_gate, w_up [G, I, H] bf16 or e4m3fn codes
  *   w_down       [G, H, I] bf16 or e4m3fn codes
- *   s_gate, s_up [G, I/128, H/128] fp32 block scales (fp8; NULL for bf16)
- *   s_down       [G, H/128, I/128] fp32 block scales (fp8; NULL for bf16)
+ *   s_gate, s_up fp8: [G, I/128, H/128] fp32 block scales; mxfp8: [G, I, H/32]
+ *                uint8 E8M0; NULL for bf16
+ *   s_down       fp8: [G, H/128, I/128] fp32; mxfp8: [G, H, I/32] uint8 E8M0
  *   y_perm       [R, H] bf16, written (rows of empty groups untouched)
  *   workspace    >= moe_ffn_workspace_bytes(shape) bytes of device memory
  * Groups whose offsets are not non-decreasing within [0, R] give unspecified
  * results.
  */
 int moe_grouped_ffn(const moe_shape* shape, const int32_t* offsets,
-                    const void* x_perm, const float* x_perm_scale,
+                    const void* x_perm, const void* x_perm_scale,
                     const void* w_gate, const void* w_up, const void* w_down,
-                    const float* s_gate, const float* s_up, const float* s_down,
+                    const void* s_gate, const void* s_up, const void* s_down,
                     void* y_perm, void* workspace, size_t ws_bytes,
                     void* stream);
 
@@ -194,15 +210,15 @@ int moe_combine(const moe_shape* shape, const void* y_perm, const int32_t* dest,
  * moe_combine on `stream`, intermediates in `workspace`
  * (>= moe_forward_workspace_bytes(shape)).  The permuted activation matrix is
  * never materialised here: the grouped GEMMs gather each row through src_row
- * from x (bf16) or from x quantised once per token (fp8), which gives the
- * same operands as moe_permute's x_perm.  Requires T*H*2 < 2^32.  Arguments as above;
+ * from x (bf16) or from x quantised once per token (fp8, mxfp8), which gives
+ * the same operands as moe_permute's x_perm.  Requires T*H*2 < 2^32.  Arguments as above;
  * topk_idx_out / topk_w_out may be NULL (then the routing lives in the
  * workspace only).  out [T, H] bf16.
  */
 int moe_forward(const moe_shape* shape, const void* x, const float* w_router,
                 const float* router_bias, const void* w_gate, const void* w_up,
-                const void* w_down, const float* s_gate, const float* s_up,
-                const float* s_down, void* out, int32_t* topk_idx_out,
+                const void* w_down, const void* s_gate, const void* s_up,
+                const void* s_down, void* out, int32_t* topk_idx_out,
                 float* topk_w_out, void* workspace, size_t ws_bytes,
                 void* stream);
 

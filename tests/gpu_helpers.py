@@ -53,13 +53,18 @@ def run_route(cfg, li):
 def run_permute(cfg, idx, x):
     sh = moe.shape_of(cfg)
     G, R = cfg.n_groups, cfg.R
-    fp8 = cfg.wdtype == "fp8"
+    fp8 = cfg.wdtype in ("fp8", "mxfp8")
     counts = torch.empty(G, dtype=torch.int32, device=DEV)
     offsets = torch.empty(G + 1, dtype=torch.int32, device=DEV)
     dest = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=DEV)
     src = torch.empty(R, dtype=torch.int32, device=DEV)
     x_perm = torch.empty((R, cfg.H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=DEV)
-    x_scale = torch.empty((R, cfg.H // 128), dtype=torch.float32, device=DEV) if fp8 else None
+    if cfg.wdtype == "mxfp8":
+        x_scale = torch.empty((R, cfg.H // 32), dtype=torch.uint8, device=DEV)
+    elif fp8:
+        x_scale = torch.empty((R, cfg.H // 128), dtype=torch.float32, device=DEV)
+    else:
+        x_scale = None
     ws = torch.empty(max(moe.moe_permute_workspace_bytes(sh), 16), dtype=torch.uint8, device=DEV)
     moe.moe_permute(sh, idx, x, counts, offsets, dest, src, x_perm, x_scale, ws)
     torch.cuda.synchronize()

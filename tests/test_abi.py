@@ -37,7 +37,7 @@ def test_shape_struct_matches_header():
 
 
 def test_abi_version():
-    assert moe.moe_abi_version() == 2
+    assert moe.moe_abi_version() == 3
 
 
 FAKE = 0x10000  # a non-NULL, aligned address; never dereferenced (validation fails first)

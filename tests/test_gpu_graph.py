@@ -47,6 +47,7 @@ CASES = [
     # skewed routing: groups on both sides of 64 rows, so the tiled chain runs
     # on the library's second stream, forked and joined inside the capture
     MoeConfig("graph_mixed", 23, T=512, H=512, E=64, k=4, I=256, zipf_s=1.1),
+    MoeConfig("graph_mxfp8", 24, T=384, H=512, E=16, k=4, I=256, n_shared=1, wdtype="mxfp8"),
 ]
 
 

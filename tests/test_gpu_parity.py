@@ -1,9 +1,10 @@
 """GPU parity of every C-ABI entry point against the CPU oracle (MI355X).
 
 Bars: routing (top-k indices, counts, offsets, dest, src_row, permuted rows and
-fp8 codes/scales) bit-exact given the same fp32 logits; weights within 1e-6 of
-a float64 evaluation; combine bit-exact given the same y_perm; layer output
-within a per-token infinity-norm relative error of 2e-2 (bf16) / 5e-2 (fp8).
+fp8 / mxfp8 codes and scales) bit-exact given the same fp32 logits; weights
+within 1e-6 of a float64 evaluation; combine bit-exact given the same y_perm;
+layer output within a per-token infinity-norm relative error of 2e-2 (bf16) /
+5e-2 (fp8, mxfp8).
 """
 import numpy as np
 import pytest
@@ -11,12 +12,12 @@ import torch
 
 import expert_ffn_layer_gemm_amd as moe
 import oracle
-from synth import CONFIGS, MoeConfig, generate_layer, to_numpy_inputs
+from synth import CONFIGS, EXTRA_CONFIGS, MoeConfig, generate_layer, to_numpy_inputs
 from tests.gpu_helpers import (DEV, bf16_bits_np, bf16_np, layer, rel_inf, run_ffn, run_forward,
                                run_permute, run_route, to_bf16_rne)
 
 pytestmark = pytest.mark.gpu
-TOL = {"bf16": 2e-2, "fp8": 5e-2}
+TOL = {"bf16": 2e-2, "fp8": 5e-2, "mxfp8": 5e-2}
 
 
 def _route_inputs(li):
@@ -128,6 +129,10 @@ def _check_permute(cfg, li, idx):
         codes, scales = oracle.quantize_groups_128(oracle.bf16_bits_to_f32(xb))
         assert np.array_equal(x_perm.cpu().numpy(), codes[s_ref])
         assert np.array_equal(x_scale.cpu().numpy(), scales[s_ref])
+    elif cfg.wdtype == "mxfp8":
+        codes, e8 = oracle.mx_quantize_rows(oracle.bf16_bits_to_f32(xb))
+        assert np.array_equal(x_perm.cpu().numpy(), codes[s_ref])
+        assert np.array_equal(x_scale.cpu().numpy(), e8[s_ref])
     else:
         assert np.array_equal(bf16_bits_np(x_perm), xb[s_ref])
 
@@ -140,11 +145,11 @@ def test_permute_configs(ci):
     _check_permute(cfg, li, idx)
 
 
-@pytest.mark.parametrize("T,E,k,ns,fp8", [(1, 1, 1, 0, False), (257, 7, 3, 1, True),
-                                          (600, 1024, 16, 0, False), (513, 5, 5, 1, False)])
-def test_permute_ragged_shapes(T, E, k, ns, fp8):
-    cfg = MoeConfig("perm", 9, T=T, H=256, E=E, k=k, I=128, n_shared=ns,
-                    wdtype="fp8" if fp8 else "bf16")
+@pytest.mark.parametrize("T,E,k,ns,wdtype", [(1, 1, 1, 0, "bf16"), (257, 7, 3, 1, "fp8"),
+                                             (600, 1024, 16, 0, "bf16"), (513, 5, 5, 1, "bf16"),
+                                             (300, 9, 2, 1, "mxfp8")])
+def test_permute_ragged_shapes(T, E, k, ns, wdtype):
+    cfg = MoeConfig("perm", 9, T=T, H=256, E=E, k=k, I=128, n_shared=ns, wdtype=wdtype)
     rng = np.random.default_rng(T + E)
     p = 1.0 / np.arange(1, E + 1) ** 1.2
     p /= p.sum()
@@ -169,6 +174,11 @@ def _ffn_case(cfg, sizes, seed):
         x_perm = torch.from_numpy(codes).to(DEV)
         x_scale = torch.from_numpy(scales).to(DEV)
         xo = oracle.fp8_e4m3.dequantize_groups_128(codes, scales)
+    elif cfg.wdtype == "mxfp8":
+        codes, e8 = oracle.mx_quantize_rows(xr)
+        x_perm = torch.from_numpy(codes).to(DEV)
+        x_scale = torch.from_numpy(e8).to(DEV)
+        xo = oracle.mx_dequantize_rows(codes, e8)
     else:
         xt = torch.from_numpy(xr).to(torch.bfloat16)
         x_perm, x_scale = xt.to(DEV), None
@@ -184,7 +194,7 @@ def _ffn_case(cfg, sizes, seed):
     return bf16_np(y)[:R], ref
 
 
-@pytest.mark.parametrize("wdtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8", "mxfp8"])
 def test_grouped_ffn_group_size_boundaries(wdtype):
     # sizes straddle the skinny row classes (16/32/64) and the 128-row tiles
     sizes = [0, 1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 0, 200, 257, 3]
@@ -196,11 +206,25 @@ def test_grouped_ffn_group_size_boundaries(wdtype):
     assert err <= TOL[wdtype]
 
 
-def test_grouped_ffn_fp8_shared_group():
+@pytest.mark.parametrize("wdtype", ["fp8", "mxfp8"])
+def test_grouped_ffn_8bit_shared_group(wdtype):
     sizes = [5, 0, 66, 9, 40]        # routed rows sum to T*k = 80; group 4 = shared expert (T rows)
-    cfg = MoeConfig("ffn_fp8_shared", 22, T=40, H=256, E=4, k=2, I=384, n_shared=1, wdtype="fp8")
+    cfg = MoeConfig("ffn_shared_" + wdtype, 22, T=40, H=256, E=4, k=2, I=384, n_shared=1,
+                    wdtype=wdtype)
     y, ref = _ffn_case(cfg, sizes, 2)
-    assert rel_inf(y, ref) <= TOL["fp8"]
+    assert rel_inf(y, ref) <= TOL[wdtype]
+
+
+# A K extent of 4096 (gate/up) and 1536 (down) walks many MX scale dwords per
+# row; group sizes cover the streaming kernels and ragged 128-row tiles.
+def test_grouped_ffn_mxfp8_deep_k():
+    sizes = [3, 64, 65, 300, 16, 0]
+    cfg = MoeConfig("ffn_mx_deep", 24, T=sum(sizes), H=4096, E=len(sizes), k=1, I=1536,
+                    wdtype="mxfp8")
+    y, ref = _ffn_case(cfg, sizes, 3)
+    err = rel_inf(y, ref)
+    print(f"grouped ffn mxfp8 H=4096: per-row rel err {err:.3e}")
+    assert err <= TOL["mxfp8"]
 
 
 # ----------------------------------------------------------------- combine ----
@@ -261,6 +285,17 @@ def test_forward_configs_sampled(ci):
     _forward_check(cfg, layer(cfg), sample)
 
 
+# MXFP8 layers at the Qwen3-235B shape: decode in full, prefill on sampled tokens.
+@pytest.mark.parametrize("name", [c.name for c in EXTRA_CONFIGS])
+def test_forward_mxfp8_configs(name):
+    cfg = next(c for c in EXTRA_CONFIGS if c.name == name)
+    sample = None
+    if cfg.T > 1024:
+        rng = np.random.default_rng(cfg.seed)
+        sample = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 14, replace=False)]))
+    _forward_check(cfg, layer(cfg), sample)
+
+
 @pytest.mark.parametrize("ci", range(len(CONFIGS)))
 def test_forward_deterministic(ci):
     cfg = CONFIGS[ci]
@@ -274,7 +309,7 @@ def test_forward_deterministic(ci):
 # T <= 256 with E <= 256 runs routing and dispatch in one workgroup; the
 # T256/T257 pair straddles that boundary.
 @pytest.mark.parametrize("case", ["T1", "T3_ragged", "E1k1", "kE", "one_hot_expert", "fp8_small",
-                                  "T256_E256", "T257", "k16"])
+                                  "T256_E256", "T257", "k16", "mx_small", "mx_hot"])
 def test_forward_edge_cases(case):
     cfgs = {
         "T1": MoeConfig("T1", 30, T=1, H=256, E=8, k=2, I=256),
@@ -286,10 +321,12 @@ def test_forward_edge_cases(case):
         "T256_E256": MoeConfig("t256", 36, T=256, H=256, E=256, k=8, I=128, n_shared=1, zipf_s=1.1),
         "T257": MoeConfig("t257", 37, T=257, H=256, E=256, k=8, I=128, n_shared=1, zipf_s=1.1),
         "k16": MoeConfig("k16", 38, T=100, H=256, E=64, k=16, I=128),
+        "mx_small": MoeConfig("mx", 39, T=77, H=512, E=12, k=3, I=256, n_shared=1, wdtype="mxfp8"),
+        "mx_hot": MoeConfig("mxhot", 40, T=300, H=384, E=8, k=1, I=384, wdtype="mxfp8"),
     }
     cfg = cfgs[case]
     li = generate_layer(cfg, DEV)
-    if case == "one_hot_expert":
+    if case in ("one_hot_expert", "mx_hot"):
         li.router_bias = torch.zeros(cfg.E, dtype=torch.float32, device=DEV)
         li.router_bias[3] = 100.0          # every token -> expert 3: 300 rows, ragged tiles
     _forward_check(cfg, li)
