@@ -16,6 +16,12 @@ The layer, as the pages state it:
   4. combine: weighted accumulation of the expert outputs back in token order
      ("CuTeDSL at Perplexity", local combine); a shared expert's output is added
      (DeepSeek-deployment page, Expert parallelism section).
+  5. expert-parallel share ("CuTeDSL at Perplexity", MoE Dispatch/Combine,
+     tensor-parallel deployment; "Hosting Qwen on Blackwell", expert-parallel
+     prefill kernel): with the input replicated on every GPU, a GPU's dispatch
+     keeps only the (token, slot) pairs routed to its own experts and its
+     combine sums those local contributions; the sum over GPUs (an
+     all-reduce) gives the layer's output.
 
 Readings where the pages are silent (each also listed in the design doc):
   - top-k selects on fp32 logits; ties go to the lower expert index; +0 and -0
@@ -23,7 +29,12 @@ Readings where the pages are silent (each also listed in the design doc):
   - weights: softmax over the selected logits (equal to full softmax
     renormalised over the selected experts).
   - rows inside an expert group are token-ascending; groups are unpadded.
-  - shared expert = group E, rows T*k + t, weight 1, added after the routed sum.
+  - shared expert = the group after the routed ones, rows offsets[G-1] + t
+    (T*k + t for the whole layer), weight 1, added after the routed sum.
+  - expert-parallel share of experts [e_first, e_first + e_local): routing over
+    all E experts as usual; group g holds expert e_first + g; pairs routed
+    elsewhere get dest = -1 and add nothing; the shared expert, if the share
+    holds it, comes after the local groups.  Output = the share's partial sum.
   - fp8 layers: x and h are quantised per row per 128 channels (scale = amax/448).
   - mxfp8 layers: weights, x and h are MXFP8 (E4M3 elements, one power-of-two
     E8M0 scale per 32 values along the contraction dimension; oracle/mx.py).
@@ -34,6 +45,9 @@ Parity status (pins in tests/test_oracle_*.py):
   counting_sort  pinned (brute-force loops, bijection / scan invariants)
   expert_ffn     pinned (closed-form SwiGLU values, fp64 brute force per token)
   combine        pinned (one-hot routing = inverse permutation, identical experts)
+  expert shares  pinned (fp64 per-token brute force over local experts; shares
+                 partitioning the experts sum to the whole layer; remote pairs
+                 get dest = -1; tests/test_oracle_ep.py)
   forward        pinned on tiny and random micro shapes against an fp64
                  per-token brute force; at the large sizes it rests on those pins.
   mx_*           pinned (closed-form exponents, exhaustive nearest-code search,
@@ -84,35 +98,46 @@ def topk_softmax(logits: np.ndarray, k: int):
 
 
 # -------------------------------------------------------------- dispatch ----
-def counting_sort(topk_idx: np.ndarray, E: int, n_shared: int = 0):
+def counting_sort(topk_idx: np.ndarray, E: int, n_shared: int = 0, e_first: int = 0,
+                  e_local: int = 0):
     """Per-expert counts, offsets and each (token, slot)'s row in the permuted matrix.
 
     "CuTeDSL at Perplexity", MoE Dispatch/Combine, local kernel: count the
     tokens of each expert, give each token a unique index within its expert,
     then copy.  Unique index = number of earlier tokens routed to the same
-    expert (token-ascending, unpadded groups).  The shared expert is group E
-    holding every token in order.
+    expert (token-ascending, unpadded groups).  The shared expert is the group
+    after the routed ones, holding every token in order.
 
-    Returns counts [E+ns], offsets [E+ns+1], dest [T, k], src_row [R] (int32).
+    Expert-parallel share (same page, tensor-parallel deployment: the local
+    dispatch only selects the tokens assigned to experts of this rank):
+    e_local > 0 keeps the experts [e_first, e_first + e_local) as groups
+    0 .. e_local-1; the pairs routed elsewhere get dest = -1 and no row.
+
+    Returns counts [L+ns], offsets [L+ns+1], dest [T, k], src_row [R] (int32),
+    L = e_local or E, R = offsets[-1].
     """
     T, k = topk_idx.shape
+    L = e_local or E
     flat = topk_idx.reshape(-1).astype(np.int64)
-    counts = np.bincount(flat, minlength=E).astype(np.int64)
-    assert counts.shape[0] == E, "expert index out of range"
+    assert flat.size == 0 or (flat.min() >= 0 and flat.max() < E), "expert index out of range"
+    local = flat - e_first
+    keep = (local >= 0) & (local < L)
+    counts = np.bincount(local[keep], minlength=L).astype(np.int64)
     if n_shared:
         counts = np.concatenate([counts, np.full(n_shared, T, dtype=np.int64)])
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
     # A stable sort by expert keeps (token, slot) order, i.e. token order
     # within each expert since a token picks an expert at most once.
-    order = np.argsort(flat, kind="stable")
-    dest_flat = np.empty(T * k, dtype=np.int64)
-    dest_flat[order] = np.arange(T * k)
+    kept = np.nonzero(keep)[0]                         # flat (token, slot) positions kept
+    order = kept[np.argsort(local[kept], kind="stable")]
+    dest_flat = np.full(T * k, -1, dtype=np.int64)
+    dest_flat[order] = np.arange(order.size)
     dest = dest_flat.reshape(T, k)
     R = int(offsets[-1])
     src_row = np.empty(R, dtype=np.int64)
-    src_row[dest_flat] = np.repeat(np.arange(T), k)
+    src_row[dest_flat[kept]] = kept // k
     for s in range(n_shared):
-        base = int(offsets[E + s])
+        base = int(offsets[L + s])
         src_row[base:base + T] = np.arange(T)
     return (counts.astype(np.int32), offsets.astype(np.int32),
             dest.astype(np.int32), src_row.astype(np.int32))
@@ -201,20 +226,27 @@ def _h_quant(wdtype: str):
 
 
 # --------------------------------------------------------------- combine ----
-def combine(y_perm: np.ndarray, dest: np.ndarray, w: np.ndarray, n_shared: int = 0) -> np.ndarray:
-    """out[t] = sum_{j ascending} w[t,j] * y_perm[dest[t,j]] (+ shared rows), fp32.
+def combine(y_perm: np.ndarray, dest: np.ndarray, w: np.ndarray, n_shared: int = 0,
+            shared_base=None) -> np.ndarray:
+    """out[t] = sum_{j ascending, dest[t,j] >= 0} w[t,j] * y_perm[dest[t,j]] (+ shared rows), fp32.
 
     "CuTeDSL at Perplexity", local combine: weighted accumulation using the
-    offsets dispatch computed.  The shared expert's output (rows T*k + t) is
-    added with weight 1 after the routed sum (DeepSeek-deployment page, Expert
-    parallelism section).  Each step is one fp32 product then one fp32 add.
+    offsets dispatch computed; pairs routed to another GPU's experts (dest < 0)
+    add nothing (same page: the local combine sums the local copies of a token
+    before the all-reduce).  The shared expert's output (rows shared_base + t,
+    by default T*k + t) is added with weight 1 after the routed sum
+    (DeepSeek-deployment page, Expert parallelism section).  Each step is one
+    fp32 product then one fp32 add.
     """
     T, k = dest.shape
+    base = T * k if shared_base is None else int(shared_base)
     out = np.zeros((T, y_perm.shape[1]), dtype=F32)
     for j in range(k):
-        out = (out + (w[:, j:j + 1].astype(F32) * y_perm[dest[:, j]]).astype(F32)).astype(F32)
+        sel = dest[:, j] >= 0
+        term = (w[sel, j:j + 1].astype(F32) * y_perm[dest[sel, j]]).astype(F32)
+        out[sel] = (out[sel] + term).astype(F32)
     for s in range(n_shared):
-        out = (out + y_perm[T * k + s * T + np.arange(T)]).astype(F32)
+        out = (out + y_perm[base + s * T + np.arange(T)]).astype(F32)
     return out
 
 
@@ -230,15 +262,18 @@ def forward(inputs: dict, logits_override=None) -> OracleResult:
     inputs: dict from synth.to_numpy_inputs (bf16 as uint16 bit patterns).
     logits_override: route from these fp32 logits instead of recomputing them
     (used to evaluate the layer under the GPU's own routing at near-ties).
+    inputs["e_first"], inputs["e_local"] (optional): the expert-parallel share
+    (counting_sort); the expert weights then hold the share's groups only.
     """
     x = bf16_bits_to_f32(inputs["x_bf16"])
     T, H = x.shape
     E = inputs["w_router"].shape[0]
     k, ns = inputs["k"], inputs["n_shared"]
+    e_first, e_local = inputs.get("e_first", 0), inputs.get("e_local", 0)
     logits = (router_logits(x, inputs["w_router"], inputs.get("router_bias"))
               if logits_override is None else np.asarray(logits_override, dtype=F32))
     idx, w = topk_softmax(logits, k)
-    counts, offsets, dest, src_row = counting_sort(idx, E, ns)
+    counts, offsets, dest, src_row = counting_sort(idx, E, ns, e_first, e_local)
     if inputs["wdtype"] == "fp8":
         # Activations quantised on the fly per token per 128 channels
         # (DeepSeek-deployment page, Quantization section).
@@ -254,7 +289,7 @@ def forward(inputs: dict, logits_override=None) -> OracleResult:
         x_perm_codes = x_perm_scales = None
         x_perm = permute_rows(x, src_row)
     y_perm = grouped_ffn(x_perm, offsets, inputs)
-    out = combine(y_perm, dest, w, ns)
+    out = combine(y_perm, dest, w, ns, shared_base=offsets[len(offsets) - 1 - ns])
     return OracleResult(logits=logits, topk_idx=idx, topk_w=w, counts=counts, offsets=offsets,
                         dest=dest, src_row=src_row, x_perm=x_perm, x_perm_codes=x_perm_codes,
                         x_perm_scales=x_perm_scales, y_perm=y_perm, out=out)
@@ -276,6 +311,8 @@ def forward_tokens(inputs: dict, tokens, logits_override=None) -> OracleResult:
     x = bf16_bits_to_f32(inputs["x_bf16"][tokens])
     k, ns = inputs["k"], inputs["n_shared"]
     E = inputs["w_router"].shape[0]
+    e_first = inputs.get("e_first", 0)
+    L = inputs.get("e_local", 0) or E               # routed experts of this share
     logits = (router_logits(x, inputs["w_router"], inputs.get("router_bias"))
               if logits_override is None else np.asarray(logits_override, dtype=F32))
     idx, w = topk_softmax(logits, k)
@@ -283,14 +320,16 @@ def forward_tokens(inputs: dict, tokens, logits_override=None) -> OracleResult:
     x = quantize_act(x, inputs["wdtype"])
     H = x.shape[1]
     y = np.zeros((n, k + ns, H), dtype=F32)       # expert output of each (token, slot)
-    for e in sorted(set(idx.ravel().tolist())):
+    local = (idx >= e_first) & (idx < e_first + L)  # pairs routed to this share's experts
+    for e in sorted(set(idx[local].tolist())):
         rows, slots = np.nonzero(idx == e)
-        y[rows, slots] = expert_ffn(x[rows], *expert_weights_f32(inputs, e), quantize_h=hq)
+        y[rows, slots] = expert_ffn(x[rows], *expert_weights_f32(inputs, e - e_first), quantize_h=hq)
     for s_ in range(ns):
-        y[:, k + s_] = expert_ffn(x, *expert_weights_f32(inputs, E + s_), quantize_h=hq)
+        y[:, k + s_] = expert_ffn(x, *expert_weights_f32(inputs, L + s_), quantize_h=hq)
     out = np.zeros((n, H), dtype=F32)
     for j in range(k):
-        out = (out + (w[:, j:j + 1] * y[:, j]).astype(F32)).astype(F32)
+        sel = local[:, j]
+        out[sel] = (out[sel] + (w[sel, j:j + 1] * y[sel, j]).astype(F32)).astype(F32)
     for s_ in range(ns):
         out = (out + y[:, k + s_]).astype(F32)
     return OracleResult(tokens=tokens, logits=logits, topk_idx=idx, topk_w=w, out=out)

@@ -32,15 +32,25 @@ class MoeConfig:
     w_std: float = 0.02
     router_std: float = 0.02
     regime: str = ""            # which roofline binds: "launch", "hbm", "mfma"
+    # Expert-parallel share: this GPU holds routed experts [e_first,
+    # e_first + e_local) of the E (e_local = 0: all of them) and sees every
+    # token (replicated input); its output is the partial sum over its experts.
+    e_first: int = 0
+    e_local: int = 0
 
     @property
     def R(self) -> int:
-        """Rows of the permuted activation matrix (routed + shared)."""
+        """Upper bound on the rows of the permuted activation matrix (routed + shared)."""
         return self.T * self.k + self.T * self.n_shared
 
     @property
+    def E_loc(self) -> int:
+        """Routed experts held by this GPU."""
+        return self.e_local or self.E
+
+    @property
     def n_groups(self) -> int:
-        return self.E + self.n_shared
+        return self.E_loc + self.n_shared
 
 
 CONFIGS = [

@@ -6,7 +6,8 @@ Recipe (per config):
 - optional Zipf(s) popularity term b [E]: b_e = -s * ln(rho_e), rho a seeded
   permutation of 1..E, added to the router logits by the layer.
 - expert weights per expert e (keyed separately so any single expert can be
-  regenerated): W_gate[e], W_up[e] [I, H] and W_down[e] [H, I] ~ N(0, w_std),
+  regenerated, and an expert-parallel share holds the same weights as the
+  whole layer): W_gate[e], W_up[e] [I, H] and W_down[e] [H, I] ~ N(0, w_std),
   cast to bf16; or, for "fp8" configs, converted offline to e4m3fn codes with
   one fp32 scale per 128x128 block (scale = block amax / 448, 1 for an all-zero
   block; codes = torch's e4m3fn cast of the clamped quotient); or, for
@@ -117,7 +118,10 @@ def generate_layer(cfg: MoeConfig, device="cpu") -> LayerInputs:
         s_up = torch.empty_like(s_gate)
         s_down = torch.empty((G, H, I // 32), dtype=torch.uint8, device=device)
     for e in range(G):
-        wg, wu, wd = generate_expert(cfg, e, device)
+        # Local group e holds global expert e_first + e (the shared expert is
+        # global id E): an expert's weights do not depend on the share.
+        gid = cfg.e_first + e if e < cfg.E_loc else cfg.E + (e - cfg.E_loc)
+        wg, wu, wd = generate_expert(cfg, gid, device)
         if fp8:
             w_gate[e], s_gate[e] = _fp8_blocks(wg)
             w_up[e], s_up[e] = _fp8_blocks(wu)
@@ -146,4 +150,5 @@ def to_numpy_inputs(li: LayerInputs) -> dict:
     return dict(x_bf16=bits(li.x), w_router=bits(li.w_router), router_bias=bits(li.router_bias),
                 w_gate=bits(li.w_gate), w_up=bits(li.w_up), w_down=bits(li.w_down),
                 s_gate=bits(li.s_gate), s_up=bits(li.s_up), s_down=bits(li.s_down),
-                k=li.cfg.k, n_shared=li.cfg.n_shared, wdtype=li.cfg.wdtype)
+                k=li.cfg.k, n_shared=li.cfg.n_shared, wdtype=li.cfg.wdtype,
+                e_first=li.cfg.e_first, e_local=li.cfg.e_local)

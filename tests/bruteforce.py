@@ -61,7 +61,12 @@ def _weights64(inp, e):
 
 
 def layer_bruteforce(inp):
-    """Returns (out [T,H] float64, topk_idx [T,k], logits float64, boundary gap per token)."""
+    """Returns (out [T,H] float64, topk_idx [T,k], logits float64, boundary gap per token).
+
+    With inp["e_local"] > 0 (an expert-parallel share) only the picks of
+    experts [e_first, e_first + e_local) contribute, with their full-softmax
+    weights, and the weights arrays hold those experts (then the shared one).
+    """
     x = _bf16_to_f64(inp["x_bf16"])
     T, H = x.shape
     Wr = inp["w_router"].astype(np.float64)          # [E, H]
@@ -73,7 +78,9 @@ def layer_bruteforce(inp):
     if inp.get("router_bias") is not None:
         logits = logits + inp["router_bias"].astype(np.float64)
     xin = quant(x) if (fp8 or mx) else x
-    W = [_weights64(inp, e) for e in range(E + ns)]
+    e_first = inp.get("e_first", 0)
+    L = inp.get("e_local", 0) or E
+    W = [_weights64(inp, e) for e in range(L + ns)]
 
     def ffn(e, xt):
         wg, wu, wd = W[e]
@@ -95,7 +102,8 @@ def layer_bruteforce(inp):
         p = np.exp(sel - sel.max())
         p /= p.sum()
         for j in range(k):
-            out[t] += p[j] * ffn(idx[t, j], xin[t])
+            if e_first <= idx[t, j] < e_first + L:
+                out[t] += p[j] * ffn(idx[t, j] - e_first, xin[t])
         for s in range(ns):
-            out[t] += ffn(E + s, xin[t])
+            out[t] += ffn(L + s, xin[t])
     return out, idx, logits, gap
