@@ -73,7 +73,8 @@ def cpu_baseline(cfg, li, n_tokens):
 
 CPU_TOKENS = {"tiny": 64, "qwen3_235b_decode": 64, "qwen3_235b_prefill": 256,
               "qwen35_397b_zipf": 128, "deepseek_v3_fp8": 16,
-              "qwen3_235b_decode_mxfp8": 64, "qwen3_235b_prefill_mxfp8": 256}
+              "qwen3_235b_decode_mxfp8": 64, "qwen3_235b_prefill_mxfp8": 256,
+              "qwen3_235b_decode_ep8": 64, "qwen3_235b_prefill_ep4": 512}
 
 
 def main():
@@ -156,6 +157,7 @@ def main():
     value = cfg.T * args.steps / (total_ms / 1e3)
 
     counts = np.bincount(idx.cpu().numpy().ravel(), minlength=cfg.E)
+    counts = counts[cfg.e_first:cfg.e_first + cfg.E_loc]      # the experts held here
     if cfg.n_shared:
         counts = np.concatenate([counts, [cfg.T] * cfg.n_shared])
     dtype = cfg.wdtype if cfg.wdtype in ("fp8", "mxfp8") else "bf16"
@@ -213,6 +215,7 @@ def main():
         "data": "synthetic (seeded; random-init weights of the layer's shape)",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k,
                    "I": cfg.I, "n_shared": cfg.n_shared, "weights": cfg.wdtype,
+                   **({"expert_share": [cfg.e_first, cfg.e_first + cfg.E_loc]} if cfg.e_local else {}),
                    "touched_experts": int(layer.groups), "max_group_rows": int(counts.max()),
                    "empty_experts": int((counts[:cfg.E] == 0).sum())},
         "roofline": roof,

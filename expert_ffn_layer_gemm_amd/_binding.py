@@ -28,7 +28,7 @@ _SZ = ctypes.c_size_t
 class MoeShape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("I", ctypes.c_int32), ("n_shared", ctypes.c_int32),
-                ("wdtype", ctypes.c_int32)]
+                ("wdtype", ctypes.c_int32), ("e_first", ctypes.c_int32), ("e_local", ctypes.c_int32)]
 
 
 _SP = ctypes.POINTER(MoeShape)
@@ -43,7 +43,7 @@ SIGNATURES = {
     "moe_permute_workspace_bytes": (_SZ, [_SP]),
     "moe_permute": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_grouped_ffn": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
-    "moe_combine": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P]),
+    "moe_combine": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P]),
     "moe_forward": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_profile_start": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int]),
     "moe_profile_count": (ctypes.c_int, []),
@@ -77,14 +77,15 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
-def make_shape(T, H, E, k, I, n_shared=0, wdtype=MOE_BF16) -> MoeShape:
+def make_shape(T, H, E, k, I, n_shared=0, wdtype=MOE_BF16, e_first=0, e_local=0) -> MoeShape:
     if isinstance(wdtype, str):
         wdtype = {"bf16": MOE_BF16, "fp8": MOE_FP8_E4M3_BLOCK128, "mxfp8": MOE_MXFP8}[wdtype]
-    return MoeShape(T, H, E, k, I, n_shared, wdtype)
+    return MoeShape(T, H, E, k, I, n_shared, wdtype, e_first, e_local)
 
 
 def shape_of(cfg) -> MoeShape:
-    return make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.n_shared, cfg.wdtype)
+    return make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.n_shared, cfg.wdtype,
+                      getattr(cfg, "e_first", 0), getattr(cfg, "e_local", 0))
 
 
 def _nbytes(t) -> int:
@@ -167,9 +168,9 @@ def moe_grouped_ffn(shape, offsets, x_perm, x_perm_scale, w_gate, w_up, w_down, 
                                  _ptr(workspace), ws_bytes, _stream(stream)), "moe_grouped_ffn")
 
 
-def moe_combine(shape, y_perm, dest, topk_w, out, stream=None):
+def moe_combine(shape, y_perm, dest, topk_w, offsets, out, stream=None):
     _check(lib().moe_combine(ctypes.byref(shape), _ptr(y_perm), _ptr(dest), _ptr(topk_w),
-                             _ptr(out), _stream(stream)), "moe_combine")
+                             _ptr(offsets), _ptr(out), _stream(stream)), "moe_combine")
 
 
 def moe_forward(shape, x, w_router, router_bias, w_gate, w_up, w_down, s_gate, s_up, s_down,

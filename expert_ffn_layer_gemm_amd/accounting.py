@@ -114,14 +114,16 @@ def kernel_work(kernel: str, counts: np.ndarray, H: int, I: int, wdtype: str) ->
 def layer_work(T: int, H: int, E: int, k: int, I: int, n_shared: int, wdtype: str,
                counts: np.ndarray) -> Work:
     """Algorithmic bytes / FLOPs of one layer call: weights of touched experts
-    (and their block scales), the router weight, x in and out."""
+    (and their block scales), the router weight, x in and out.  `counts` are
+    the rows of the groups held here (routed, then shared); for an
+    expert-parallel share they cover its experts only."""
     m = np.asarray(counts, dtype=np.int64)
     touched = int((m > 0).sum())
     e = _elt(wdtype)
     wbytes = touched * 3 * H * I * e
     wbytes += 2 * _weight_scale_bytes(touched, I, H, wdtype) + _weight_scale_bytes(touched, H, I, wdtype)
     byts = wbytes + 4 * H * E + T * H * 2 + T * H * 2
-    R = T * (k + n_shared)
+    R = int(m.sum())
     flops = 2 * T * H * E + 2 * R * 3 * H * I
     return Work(float(byts), float(flops), touched)
 

@@ -55,6 +55,10 @@ int check_shape(const char* fn, const moe_shape* s, bool need_ffn_dims) {
   // below 131072 (fp8 block scales of a tile are staged in LDS).
   if (need_ffn_dims && ((long long)s->H * s->I >= (1LL << 31) || s->H > 131072 || s->I > 131072))
     return fail(MOE_ERR_UNSUPPORTED, "%s: H*I=%lld too large", fn, (long long)s->H * s->I);
+  if (s->e_local < 0 || s->e_first < 0 || (s->e_local == 0 && s->e_first != 0) ||
+      (long long)s->e_first + s->e_local > s->E)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: expert share e_first=%d e_local=%d not within E=%d", fn,
+                s->e_first, s->e_local, s->E);
   return MOE_OK;
 }
 
@@ -63,6 +67,10 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 // 8-bit codes with scales: per-128 fp32 block scales or MX E8M0 bytes.
 bool is_8bit(const moe_shape* s) { return s->wdtype != MOE_BF16; }
 bool is_mx(const moe_shape* s) { return s->wdtype == MOE_MXFP8; }
+
+// Routed experts held here (the expert-parallel share, else all E).
+int n_local(const moe_shape* s) { return s->e_local ? s->e_local : s->E; }
+bool is_share(const moe_shape* s) { return s->e_local != 0; }
 
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
@@ -75,7 +83,7 @@ struct FwdLayout {
 
 FwdLayout fwd_layout(const moe_shape* s) {
   const bool fp8 = is_8bit(s), mx = is_mx(s);
-  const size_t T = s->T, H = s->H, E = s->E, k = s->k, G = s->E + s->n_shared;
+  const size_t T = s->T, H = s->H, E = s->E, k = s->k, G = n_local(s) + s->n_shared;
   const size_t R = T * (k + s->n_shared);
   FwdLayout L{};
   size_t off = 0;
@@ -85,14 +93,14 @@ FwdLayout fwd_layout(const moe_shape* s) {
   L.w = off;       off += align256(T * k * 4);
   L.counts = off;  off += align256(G * 4);
   L.offsets = off; off += align256((G + 1) * 4);
-  L.tcnt = off;    off += align256(moe::permute_workspace_bytes(s->T, s->E));
+  L.tcnt = off;    off += align256(moe::permute_workspace_bytes(s->T, n_local(s)));
   L.dest = off;    off += align256(T * k * 4);
   L.src_row = off; off += align256(R * 4);
   L.xq = off;      off += fp8 ? align256(T * H) : 0;
   L.xs = off;      off += mx ? align256(T * (H / 32)) : fp8 ? align256(T * (H / 128) * 4) : 0;
   L.y_perm = off;  off += align256(R * H * 2);
   L.ffn = off;
-  off += moe::ffn_workspace_bytes(s->T, s->H, s->E, s->k, s->I, s->n_shared, fp8, mx);
+  off += moe::ffn_workspace_bytes(s->T, s->H, n_local(s), s->k, s->I, s->n_shared, fp8, mx);
   L.total = off;
   return L;
 }
@@ -103,7 +111,7 @@ extern "C" {
 
 const char* moe_last_error(void) { return g_err; }
 
-int moe_abi_version(void) { return 3; }
+int moe_abi_version(void) { return 4; }
 
 size_t moe_forward_workspace_bytes(const moe_shape* shape) {
   if (check_shape("moe_forward_workspace_bytes", shape, true) != MOE_OK) return 0;
@@ -112,7 +120,7 @@ size_t moe_forward_workspace_bytes(const moe_shape* shape) {
 
 size_t moe_ffn_workspace_bytes(const moe_shape* shape) {
   if (check_shape("moe_ffn_workspace_bytes", shape, true) != MOE_OK) return 0;
-  return moe::ffn_workspace_bytes(shape->T, shape->H, shape->E, shape->k, shape->I,
+  return moe::ffn_workspace_bytes(shape->T, shape->H, n_local(shape), shape->k, shape->I,
                                   shape->n_shared, is_8bit(shape), is_mx(shape));
 }
 
@@ -170,7 +178,7 @@ int moe_route_from_logits(const moe_shape* shape, const float* logits, int32_t* 
 
 size_t moe_permute_workspace_bytes(const moe_shape* shape) {
   if (check_shape("moe_permute_workspace_bytes", shape, false) != MOE_OK) return 0;
-  return moe::permute_workspace_bytes(shape->T, shape->E);
+  return moe::permute_workspace_bytes(shape->T, n_local(shape));
 }
 
 int moe_permute(const moe_shape* shape, const int32_t* topk_idx, const void* x, int32_t* counts,
@@ -190,7 +198,7 @@ int moe_permute(const moe_shape* shape, const int32_t* topk_idx, const void* x, 
     MOE_NEED_PTR(x_perm);
     if (fp8) MOE_NEED_PTR(x_perm_scale);
   }
-  const size_t need = moe::permute_workspace_bytes(shape->T, shape->E);
+  const size_t need = moe::permute_workspace_bytes(shape->T, n_local(shape));
   if (need > 0 && (workspace == nullptr || ws_bytes < need))
     return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
   if (need > 0 && !aligned16(workspace))
@@ -198,8 +206,8 @@ int moe_permute(const moe_shape* shape, const int32_t* topk_idx, const void* x, 
   return hip_status(moe::launch_permute(topk_idx, static_cast<const uint16_t*>(x), counts, offsets,
                                         dest, src_row, x_perm, x_perm_scale,
                                         static_cast<int32_t*>(workspace), shape->T, shape->H,
-                                        shape->E, shape->k, shape->n_shared, fp8, mx,
-                                        as_stream(stream)), fn);
+                                        n_local(shape), shape->k, shape->n_shared, shape->e_first,
+                                        is_share(shape), fp8, mx, as_stream(stream)), fn);
 }
 
 int moe_grouped_ffn(const moe_shape* shape, const int32_t* offsets, const void* x_perm,
@@ -229,7 +237,7 @@ int moe_grouped_ffn(const moe_shape* shape, const int32_t* offsets, const void* 
     return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return fail(MOE_ERR_INVALID_ARG, "%s: workspace not 256-byte aligned", fn);
-  moe::FfnArgs a{shape->T, shape->H, shape->E, shape->k, shape->I, shape->n_shared, fp8,
+  moe::FfnArgs a{shape->T, shape->H, n_local(shape), shape->k, shape->I, shape->n_shared, fp8,
                  offsets, nullptr, x_perm, x_perm_scale, w_gate, w_up, w_down, s_gate, s_up,
                  s_down, y_perm, workspace,
                  (long long)shape->T * (shape->k + shape->n_shared), false, is_mx(shape)};
@@ -237,7 +245,7 @@ int moe_grouped_ffn(const moe_shape* shape, const int32_t* offsets, const void* 
 }
 
 int moe_combine(const moe_shape* shape, const void* y_perm, const int32_t* dest,
-                const float* topk_w, void* out, void* stream) {
+                const float* topk_w, const int32_t* offsets, void* out, void* stream) {
   const char* fn = "moe_combine";
   moe::prof_call_begin();
   if (int rc = check_shape(fn, shape, false)) return rc;
@@ -246,9 +254,12 @@ int moe_combine(const moe_shape* shape, const void* y_perm, const int32_t* dest,
   MOE_NEED_PTR(dest);
   MOE_NEED_PTR(topk_w);
   MOE_NEED_PTR(out);
+  if (shape->n_shared) MOE_NEED_PTR(offsets);
+  const int32_t* shared_base = shape->n_shared ? offsets + n_local(shape) : nullptr;
   return hip_status(moe::launch_combine(static_cast<const uint16_t*>(y_perm), dest, topk_w,
-                                        static_cast<uint16_t*>(out), shape->T, shape->H, shape->k,
-                                        shape->n_shared, as_stream(stream)), fn);
+                                        shared_base, static_cast<uint16_t*>(out), shape->T,
+                                        shape->H, shape->k, shape->n_shared, as_stream(stream)),
+                    fn);
 }
 
 int moe_forward(const moe_shape* shape, const void* x, const float* w_router,
@@ -303,7 +314,8 @@ int moe_forward(const moe_shape* shape, const void* x, const float* w_router,
   // buffer), reduced in slice order by the top-k kernel.
   const int ks = moe::router_splits(shape->T, shape->H, shape->E);
   float* parts = ks > 1 ? reinterpret_cast<float*>(ws + L.rpart) : logits;
-  moe::FfnArgs a{shape->T, shape->H, shape->E, shape->k, shape->I, shape->n_shared, fp8,
+  const int nl = n_local(shape);
+  moe::FfnArgs a{shape->T, shape->H, nl, shape->k, shape->I, shape->n_shared, fp8,
                  offsets, src_row, fp8 ? static_cast<const void*>(xq) : x, xs, w_gate, w_up,
                  w_down, s_gate, s_up, s_down, y_perm, ws + L.ffn, (long long)shape->T, false, mx};
   hipError_t e = moe::launch_router_gemm(static_cast<const uint16_t*>(x), w_router, parts,
@@ -314,18 +326,19 @@ int moe_forward(const moe_shape* shape, const void* x, const float* w_router,
     // Small batch: dispatch tables and FFN work lists in one launch.
     if (e == hipSuccess)
       e = moe::launch_dispatch_small(idx, counts, offsets, dest, src_row, moe::ffn_schedule(a),
-                                     shape->T, shape->E, shape->k, shape->n_shared, s);
+                                     shape->T, nl, shape->k, shape->n_shared, shape->e_first, s);
     a.planned = true;
   } else if (e == hipSuccess) {   // routing tables only: no row copy
     e = moe::launch_permute(idx, static_cast<const uint16_t*>(x), counts, offsets, dest, src_row,
                             nullptr, nullptr, reinterpret_cast<int32_t*>(ws + L.tcnt), shape->T,
-                            shape->H, shape->E, shape->k, shape->n_shared, fp8, mx, s);
+                            shape->H, nl, shape->k, shape->n_shared, shape->e_first,
+                            is_share(shape), fp8, mx, s);
   }
   if (e == hipSuccess && fp8)
     e = moe::launch_quantize_rows(static_cast<const uint16_t*>(x), xq, xs, shape->T, shape->H, mx, s);
   if (e == hipSuccess) e = moe::launch_grouped_ffn(a, s);
   if (e == hipSuccess)
-    e = moe::launch_combine(static_cast<const uint16_t*>(y_perm), dest, w,
+    e = moe::launch_combine(static_cast<const uint16_t*>(y_perm), dest, w, offsets + nl,
                             static_cast<uint16_t*>(out), shape->T, shape->H, shape->k,
                             shape->n_shared, s);
   return hip_status(e, fn);

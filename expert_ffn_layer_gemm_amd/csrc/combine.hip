@@ -1,7 +1,9 @@
-// Combine: out[t] = bf16( sum_j w[t,j] * y_perm[dest[t,j]] (+ y_perm[T*k + t]) )
+// Combine: out[t] = bf16( sum_{j: dest[t,j] >= 0} w[t,j] * y_perm[dest[t,j]]
+//                         (+ y_perm[shared_base + t]) )
 // ("CuTeDSL at Perplexity", local combine: vectorised weighted accumulation in
-// registers from the offsets the dispatch computed; the DeepSeek-deployment
-// page's shared expert is added after the routed sum).
+// registers from the offsets the dispatch computed; an expert-parallel share
+// sums only its local pairs, dest < 0 marking the others; the
+// DeepSeek-deployment page's shared expert is added after the routed sum).
 //
 // A gather, not a scatter: each token reads its k rows, so no atomics are
 // needed and the summation order (slot order, then the shared row) is fixed.
@@ -18,10 +20,12 @@ template <int TPB>
 __global__ __launch_bounds__(TPB) void k_combine(const uint16_t* __restrict__ y_perm,
                                                  const int32_t* __restrict__ dest,
                                                  const float* __restrict__ topk_w,
+                                                 const int32_t* __restrict__ shared_base,
                                                  uint16_t* __restrict__ out, int T, int H, int k,
                                                  int n_shared) {
   const int t = blockIdx.x;
   const int chunks = H / 8;
+  const size_t srow = n_shared ? (size_t)*shared_base + t : 0;
   for (int c = threadIdx.x; c < chunks; c += TPB) {
     float acc[8];
 #pragma unroll
@@ -29,6 +33,7 @@ __global__ __launch_bounds__(TPB) void k_combine(const uint16_t* __restrict__ y_
     for (int j = 0; j < k; ++j) {
       const float w = topk_w[(size_t)t * k + j];
       const int row = dest[(size_t)t * k + j];
+      if (row < 0) continue;                 // held by another share: adds nothing
       float v[8];
       unpack_bf16x8(reinterpret_cast<const u32x4_t*>(y_perm + (size_t)row * H)[c], v);
 #pragma unroll
@@ -36,7 +41,7 @@ __global__ __launch_bounds__(TPB) void k_combine(const uint16_t* __restrict__ y_
     }
     if (n_shared) {
       float v[8];
-      unpack_bf16x8(reinterpret_cast<const u32x4_t*>(y_perm + ((size_t)T * k + t) * H)[c], v);
+      unpack_bf16x8(reinterpret_cast<const u32x4_t*>(y_perm + srow * H)[c], v);
 #pragma unroll
       for (int q = 0; q < 8; ++q) acc[q] = acc[q] + v[q];
     }
@@ -45,13 +50,14 @@ __global__ __launch_bounds__(TPB) void k_combine(const uint16_t* __restrict__ y_
 }
 
 hipError_t launch_combine(const uint16_t* y_perm, const int32_t* dest, const float* topk_w,
-                          uint16_t* out, int T, int H, int k, int n_shared, hipStream_t s) {
+                          const int32_t* shared_base, uint16_t* out, int T, int H, int k,
+                          int n_shared, hipStream_t s) {
   if (H / 8 <= 256)
-    MOE_LAUNCH("combine", (k_combine<64>), dim3(T), dim3(64), 0, s, y_perm, dest, topk_w, out, T, H,
-                       k, n_shared);
+    MOE_LAUNCH("combine", (k_combine<64>), dim3(T), dim3(64), 0, s, y_perm, dest, topk_w,
+               shared_base, out, T, H, k, n_shared);
   else
-    MOE_LAUNCH("combine", (k_combine<256>), dim3(T), dim3(256), 0, s, y_perm, dest, topk_w, out, T, H,
-                       k, n_shared);
+    MOE_LAUNCH("combine", (k_combine<256>), dim3(T), dim3(256), 0, s, y_perm, dest, topk_w,
+               shared_base, out, T, H, k, n_shared);
   return hipGetLastError();
 }
 

@@ -265,16 +265,50 @@ __device__ __forceinline__ i32x8_t ld32(const uint8_t* ptr) {
                  (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
 
-// Weight streaming for MXFP8 layers (16-row slices).  Wave w owns 16 output
-// columns; lane l loads its row's 32 codes of each 128-K block in the MFMA's
-// layout (16 bytes at K 16*(l/16), 16 at K 64 + 16*(l/16)) and the E8M0
-// scale of K block 4*kb + l/16 for its A row and its B row; the scaled MFMA
-// applies both, so the partial sums accumulate directly.  DUAL: h = silu(g) *
-// u is quantised per row in MX blocks of 32 columns (two adjacent waves share
-// a block; their row maxima meet in LDS).
-template <bool DUAL, int NW>
+// Weight streaming for MXFP8 layers (16-row slices).  Wave w owns CB blocks
+// of 16 output columns; lane l loads its row's 32 codes of each 128-K block
+// in the MFMA's layout (16 bytes at K 16*(l/16), 16 at K 64 + 16*(l/16)) and
+// the E8M0 scale of K block 4*kb + l/16 for its A row and its B rows; the
+// scaled MFMA applies both, so the partial sums accumulate directly.  Each A
+// fragment feeds CB (x2 for gate/up) MFMAs.  The operands of U consecutive
+// 128-K blocks sit in a register ring: slot u is refilled with block kb + U
+// right after block kb is multiplied.  DUAL: h = silu(g) * u is quantised
+// per row in MX blocks of 32 columns: within the wave for CB = 2, else two
+// adjacent waves combine their row maxima in LDS.
+template <int NB>
+struct MxSlot {
+  i32x8_t a, b[NB];
+  uint32_t sa, s[NB];
+};
+
+template <int NB>
+__device__ __forceinline__ void mx_fill(MxSlot<NB>& sl, int kb, bool aok, const uint8_t* arow,
+                                        const uint8_t* sarow, const uint8_t* const (&b)[NB],
+                                        const uint8_t* const (&sb)[NB]) {
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    sl.b[j] = ld32(b[j] + (size_t)kb * 128);
+    sl.s[j] = sb[j][4 * kb];
+  }
+  // Rows past the slice feed zero codes with scale 1 (outputs never stored).
+  sl.a = aok ? ld32(arow + (size_t)kb * 128) : i32x8_t{};
+  sl.sa = aok ? (uint32_t)sarow[4 * kb] : 127u;
+}
+
+#ifndef SKINNY_MX_U
+#define SKINNY_MX_NW 4    // gate/up: waves per workgroup
+#define SKINNY_MX_CB 2    //          16-column blocks per wave
+#define SKINNY_MX_U 1     //          ring depth (128-K blocks in flight per stream)
+#define SKINNY_MX_NWD 4   // down
+#define SKINNY_MX_CBD 2
+#define SKINNY_MX_UD 1
+#endif
+
+template <bool DUAL, int NW, int CB, int U>
 __global__ __launch_bounds__(64 * NW) void k_skinny_mx(const GemmArgs p) {
-  static_assert(!DUAL || NW % 2 == 0, "an MX block of h spans two waves");
+  static_assert(!DUAL || CB == 2 || (CB == 1 && NW % 2 == 0), "an MX block of h is 32 columns");
+  constexpr int NM = DUAL ? 2 : 1;          // weight matrices
+  constexpr int NB = NM * CB;               // B streams per lane: [matrix][column block]
   __shared__ float row_amax[NW][16];
   int slot, nt;
   if (!band_item(p.sc.skinny, *p.sc.n_skinny, p.n_ntile, slot, nt)) return;
@@ -283,65 +317,79 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_mx(const GemmArgs p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, q4 = lane >> 4;
   const int K = p.K, N = p.N, KB = K / 128, K32 = K / 32;
-  const int n0 = (nt * NW + wave) * 16;
+  const int n0 = (nt * NW + wave) * 16 * CB;
 
-  const size_t brow = (size_t)g * N + n0 + r16;
-  const uint8_t* b0 = p.B0 + brow * K + 16 * q4;
-  const uint8_t* b1 = DUAL ? p.B1 + brow * K + 16 * q4 : nullptr;
-  const uint8_t* sb0 = static_cast<const uint8_t*>(p.s_B0) + brow * K32;
-  const uint8_t* sb1 = DUAL ? static_cast<const uint8_t*>(p.s_B1) + brow * K32 : nullptr;
+  // Per-lane stream bases: codes at the lane's 16-byte offset, scales at its
+  // 32-block within each 128-K block.
+  const uint8_t* b[NB];
+  const uint8_t* sb[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const size_t brow = (size_t)g * N + n0 + (j % CB) * 16 + r16;
+    b[j] = (j < CB ? p.B0 : p.B1) + brow * K + 16 * q4;
+    sb[j] = static_cast<const uint8_t*>(j < CB ? p.s_B0 : p.s_B1) + brow * K32 + q4;
+  }
   const bool aok = r16 < m;
   const int pr = row0 + (aok ? r16 : 0);
   const size_t arow_i = (size_t)(p.a_rows ? p.a_rows[pr] : pr);
   const uint8_t* arow = p.A + arow_i * K + 16 * q4;
-  const uint8_t* sarow = static_cast<const uint8_t*>(p.A_scale) + arow_i * K32;
+  const uint8_t* sarow = static_cast<const uint8_t*>(p.A_scale) + arow_i * K32 + q4;
 
-  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  i32x8_t cur0 = ld32(b0), cur1{};
-  uint32_t cs0 = *reinterpret_cast<const uint32_t*>(sb0), cs1 = 0;
-  if (DUAL) { cur1 = ld32(b1); cs1 = *reinterpret_cast<const uint32_t*>(sb1); }
-  for (int kb = 0; kb < KB; ++kb) {
-    const bool more = kb + 1 < KB;
-    i32x8_t nxt0{}, nxt1{};
-    uint32_t ns0 = 0, ns1 = 0;
-    if (more) {
-      nxt0 = ld32(b0 + (kb + 1) * 128);
-      ns0 = *reinterpret_cast<const uint32_t*>(sb0 + 4 * (kb + 1));
-      if (DUAL) {
-        nxt1 = ld32(b1 + (kb + 1) * 128);
-        ns1 = *reinterpret_cast<const uint32_t*>(sb1 + 4 * (kb + 1));
-      }
+  f32x4_t acc[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // Fills past the last block reload block KB - 1 (cache hits, never
+  // multiplied), which keeps the ring's loads unconditional.
+  MxSlot<NB> ring[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) mx_fill<NB>(ring[u], min(u, KB - 1), aok, arow, sarow, b, sb);
+  int kb0 = 0;
+  for (; kb0 + U <= KB; kb0 += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        acc[j] = mfma_mx8_16x16x128(ring[u].a, ring[u].b[j], acc[j], ring[u].sa, ring[u].s[j]);
+      mx_fill<NB>(ring[u], min(kb0 + u + U, KB - 1), aok, arow, sarow, b, sb);
     }
-    // Rows past the slice feed zero codes (outputs never stored); the MFMA
-    // itself runs for the whole wave.
-    const i32x8_t a = aok ? ld32(arow + kb * 128) : i32x8_t{};
-    const uint32_t sa =
-        aok ? (*reinterpret_cast<const uint32_t*>(sarow + 4 * kb) >> (8 * q4)) & 0xFFu : 127u;
-    acc0 = mfma_mx8_16x16x128(a, cur0, acc0, sa, (cs0 >> (8 * q4)) & 0xFFu);
-    if (DUAL) acc1 = mfma_mx8_16x16x128(a, cur1, acc1, sa, (cs1 >> (8 * q4)) & 0xFFu);
-    if (more) { cur0 = nxt0; cs0 = ns0; if (DUAL) { cur1 = nxt1; cs1 = ns1; } }
   }
+#pragma unroll
+  for (int u = 0; u < U; ++u)   // the KB % U blocks left sit in slots 0 .. KB % U - 1
+    if (kb0 + u < KB) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        acc[j] = mfma_mx8_16x16x128(ring[u].a, ring[u].b[j], acc[j], ring[u].sa, ring[u].s[j]);
+    }
 
   if constexpr (DUAL) {
-    float hv[4];
+    float hv[4][CB], am[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int r = q4 * 4 + q;
-      hv[q] = r < m ? silu_mul(acc0[q], acc1[q]) : 0.f;
-      const float am = wave_max_xor(fabsf(hv[q]), 16);
-      if (r16 == 0) row_amax[wave][r] = am;
+      am[q] = 0.f;
+#pragma unroll
+      for (int c = 0; c < CB; ++c) {
+        hv[q][c] = r < m ? silu_mul(acc[c][q], acc[CB + c][q]) : 0.f;
+        am[q] = fmaxf(am[q], fabsf(hv[q][c]));
+      }
+      am[q] = wave_max_xor(am[q], 16);
+      if (CB == 1 && r16 == 0) row_amax[wave][r] = am[q];
     }
-    __syncthreads();
+    if (CB == 1) __syncthreads();
     const int N32 = N / 32;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int r = q4 * 4 + q;
       if (r < m) {
-        const float am = fmaxf(row_amax[wave][r], row_amax[wave ^ 1][r]);
-        const uint32_t e8 = mx_e8m0(am);
-        const float qv = fminf(fmaxf(hv[q] * mx_inv_scale(e8), -448.f), 448.f);
-        p.out[(size_t)(row0 + r) * N + n0 + r16] = (uint8_t)f32_to_e4m3(qv);
-        if ((wave & 1) == 0 && r16 == 0)
+        const float a = CB == 1 ? fmaxf(row_amax[wave][r], row_amax[wave ^ 1][r]) : am[q];
+        const uint32_t e8 = mx_e8m0(a);
+        const float inv = mx_inv_scale(e8);
+#pragma unroll
+        for (int c = 0; c < CB; ++c) {
+          const float qv = fminf(fmaxf(hv[q][c] * inv, -448.f), 448.f);
+          p.out[(size_t)(row0 + r) * N + n0 + c * 16 + r16] = (uint8_t)f32_to_e4m3(qv);
+        }
+        if ((CB == 2 || (wave & 1) == 0) && r16 == 0)
           static_cast<uint8_t*>(p.out_scale)[(size_t)(row0 + r) * N32 + n0 / 32] = (uint8_t)e8;
       }
     }
@@ -350,7 +398,11 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_mx(const GemmArgs p) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int r = q4 * 4 + q;
-      if (r < m) out[(size_t)(row0 + r) * N + n0 + r16] = (uint16_t)f32_to_bf16_bits(acc0[q]);
+      if (r < m) {
+#pragma unroll
+        for (int c = 0; c < CB; ++c)
+          out[(size_t)(row0 + r) * N + n0 + c * 16 + r16] = (uint16_t)f32_to_bf16_bits(acc[c][q]);
+      }
     }
   }
 }
@@ -492,10 +544,12 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
 
   // gate/up + SwiGLU, then down, of the groups of at most kSkinnyMax rows
   if (f.mx) {
-    up.n_ntile = f.I / (16 * 8);
-    launch_gemm("skinny_gateup_mx", k_skinny_mx<true, 8>, 512, band_grid(L.max_slices, up.n_ntile), up, s);
-    dn.n_ntile = f.H / (16 * 4);
-    launch_gemm("skinny_down_mx", k_skinny_mx<false, 4>, 256, band_grid(L.max_slices, dn.n_ntile), dn, s);
+    up.n_ntile = f.I / (16 * SKINNY_MX_CB * SKINNY_MX_NW);
+    launch_gemm("skinny_gateup_mx", k_skinny_mx<true, SKINNY_MX_NW, SKINNY_MX_CB, SKINNY_MX_U>,
+                64 * SKINNY_MX_NW, band_grid(L.max_slices, up.n_ntile), up, s);
+    dn.n_ntile = f.H / (16 * SKINNY_MX_CBD * SKINNY_MX_NWD);
+    launch_gemm("skinny_down_mx", k_skinny_mx<false, SKINNY_MX_NWD, SKINNY_MX_CBD, SKINNY_MX_UD>,
+                64 * SKINNY_MX_NWD, band_grid(L.max_slices, dn.n_ntile), dn, s);
   } else if (f.fp8) {
     up.n_ntile = f.I / (16 * 8);
     launch_gemm("skinny_gateup_fp8", k_skinny_fp8<true, 8, 1>, 512, band_grid(L.max_slices, up.n_ntile), up, s);

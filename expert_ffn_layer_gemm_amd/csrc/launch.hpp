@@ -35,21 +35,26 @@ hipError_t launch_topk(const float* parts, int KS, const float* bias, float* log
                        int32_t* idx, float* w, int T, int E, int k, hipStream_t s);
 
 // permute.hip
+// E = the routed experts held here (global ids e_first ..); share: an
+// expert-parallel share (pairs routed elsewhere get dest = -1, rows < R).
 // tile_cnt: permute_workspace_bytes(T, E) of device scratch (per-tile counts).
 // x_perm == nullptr skips the row copy (the GEMMs then gather rows through src_row).
 size_t permute_workspace_bytes(int T, int E);
 hipError_t launch_permute(const int32_t* topk_idx, const uint16_t* x, int32_t* counts,
                           int32_t* offsets, int32_t* dest, int32_t* src_row, void* x_perm,
                           void* x_perm_scale, int32_t* tile_cnt, int T, int H, int E, int k,
-                          int n_shared, bool fp8, bool mx, hipStream_t s);
+                          int n_shared, int e_first, bool share, bool fp8, bool mx,
+                          hipStream_t s);
 // Per-token e4m3 quantisation of x (128-channel groups): the rows the fp8
 // GEMMs gather through src_row.
 hipError_t launch_quantize_rows(const uint16_t* x, uint8_t* xq, void* xs, int T, int H, bool mx,
                                 hipStream_t s);
 
 // combine.hip
+// shared_base: device pointer to the first row of the shared group (n_shared).
 hipError_t launch_combine(const uint16_t* y_perm, const int32_t* dest, const float* topk_w,
-                          uint16_t* out, int T, int H, int k, int n_shared, hipStream_t s);
+                          const int32_t* shared_base, uint16_t* out, int T, int H, int k,
+                          int n_shared, hipStream_t s);
 
 // ffn.hip: the on-device schedule and the grouped GEMMs.
 struct FfnArgs {
@@ -86,6 +91,6 @@ Sched ffn_schedule(const FfnArgs& a);   // the work lists inside a's workspace
 constexpr int kSmallBatch = 256;
 hipError_t launch_dispatch_small(const int32_t* idx, int32_t* counts, int32_t* offsets,
                                  int32_t* dest, int32_t* src_row, const Sched& sc, int T, int E,
-                                 int k, int n_shared, hipStream_t s);
+                                 int k, int n_shared, int e_first, hipStream_t s);
 
 }  // namespace moe

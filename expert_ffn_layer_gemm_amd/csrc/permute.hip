@@ -10,6 +10,10 @@
 //     (one bit per token of a 256-token tile per expert) with popcounts, instead
 //     of atomically incremented counters, so dest / src_row / x_perm are
 //     identical from run to run;
+//   - an expert-parallel share keeps only the pairs routed to its experts
+//     [e_first, e_first + L) (same page, tensor-parallel deployment: the local
+//     dispatch selects the tokens assigned to this rank's experts); the others
+//     get dest = -1, and the row copies stop at the share's row count;
 //   - four launches: per-tile histograms (256-token tiles, LDS atomics), one
 //     workgroup turning them into per-tile bases, counts and offsets (wave-level
 //     prefix scan), a tile grid assigning ranks, and a wide grid gathering rows
@@ -22,17 +26,21 @@ namespace moe {
 
 constexpr int kRankTile = 256;   // tokens per tile of the histogram and rank kernels
 
-// Routings per expert inside each 256-token tile: tile_cnt[tile][e].
+// Routings per local expert inside each 256-token tile: tile_cnt[tile][e]
+// (E = the share's experts, global ids e_first ..).
 __global__ __launch_bounds__(kRankTile) void k_tile_hist(const int32_t* __restrict__ idx,
                                                          int32_t* __restrict__ tile_cnt, int T,
-                                                         int E, int k) {
+                                                         int E, int k, int e_first) {
   __shared__ int cnt[1024];
   const int tid = threadIdx.x;
   for (int i = tid; i < E; i += kRankTile) cnt[i] = 0;
   __syncthreads();
   const int t = blockIdx.x * kRankTile + tid;
   if (t < T)
-    for (int j = 0; j < k; ++j) atomicAdd(&cnt[idx[(size_t)t * k + j]], 1);
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[(size_t)t * k + j] - e_first;
+      if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
+    }
   __syncthreads();
   for (int i = tid; i < E; i += kRankTile) tile_cnt[(size_t)blockIdx.x * E + i] = cnt[i];
 }
@@ -71,7 +79,7 @@ __global__ __launch_bounds__(kRankTile) void k_rank(const int32_t* __restrict__ 
                                                     const int32_t* __restrict__ tile_base,
                                                     int32_t* __restrict__ dest,
                                                     int32_t* __restrict__ src_row, int T, int E,
-                                                    int k, int n_shared) {
+                                                    int k, int n_shared, int e_first) {
   __shared__ uint32_t mask[1024 * (kRankTile / 32)];
   const int tid = threadIdx.x;
   for (int i = tid; i < E * (kRankTile / 32); i += kRankTile) mask[i] = 0u;
@@ -81,12 +89,19 @@ __global__ __launch_bounds__(kRankTile) void k_rank(const int32_t* __restrict__ 
   const int word = tid >> 5;
   const uint32_t bit = 1u << (tid & 31);
   if (valid)
-    for (int j = 0; j < k; ++j) atomicOr(&mask[idx[(size_t)t * k + j] * (kRankTile / 32) + word], bit);
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[(size_t)t * k + j] - e_first;
+      if ((unsigned)e < (unsigned)E) atomicOr(&mask[e * (kRankTile / 32) + word], bit);
+    }
   __syncthreads();
   if (!valid) return;
   const int32_t* base = tile_base + (size_t)blockIdx.x * E;
   for (int j = 0; j < k; ++j) {
-    const int e = idx[(size_t)t * k + j];
+    const int e = idx[(size_t)t * k + j] - e_first;
+    if ((unsigned)e >= (unsigned)E) {   // routed to another share's expert
+      dest[(size_t)t * k + j] = -1;
+      continue;
+    }
     const uint32_t* m = mask + e * (kRankTile / 32);
     int rank = __popc(m[word] & (bit - 1u));
     for (int w = 0; w < word; ++w) rank += __popc(m[w]);
@@ -99,10 +114,18 @@ __global__ __launch_bounds__(kRankTile) void k_rank(const int32_t* __restrict__ 
 
 // x_perm[r] = x[src_row[r]] (bf16), 16 bytes per lane.
 constexpr int kGatherRows = 4;
+// Rows: R, or *n_rows when n_rows is non-null (a share's row count, read on
+// the device).
+__device__ __forceinline__ int gather_rows(int R, const int32_t* n_rows) {
+  return n_rows ? min(R, *n_rows) : R;
+}
+
 __global__ __launch_bounds__(256) void k_gather_bf16(const int32_t* __restrict__ src_row,
                                                      const uint16_t* __restrict__ x,
-                                                     uint16_t* __restrict__ x_perm, int R, int H) {
+                                                     uint16_t* __restrict__ x_perm, int R, int H,
+                                                     const int32_t* __restrict__ n_rows) {
   const int chunks = H / 8;
+  R = gather_rows(R, n_rows);
   for (int rr = 0; rr < kGatherRows; ++rr) {
     const int r = blockIdx.x * kGatherRows + rr;
     if (r >= R) return;
@@ -118,8 +141,10 @@ __global__ __launch_bounds__(256) void k_gather_bf16(const int32_t* __restrict__
 __global__ __launch_bounds__(256) void k_gather_fp8(const int32_t* __restrict__ src_row,
                                                     const uint16_t* __restrict__ x,
                                                     uint8_t* __restrict__ x_perm,
-                                                    float* __restrict__ x_scale, int R, int H) {
+                                                    float* __restrict__ x_scale, int R, int H,
+                                                    const int32_t* __restrict__ n_rows) {
   const int chunks = H / 8;
+  R = gather_rows(R, n_rows);
   for (int rr = 0; rr < kGatherRows; ++rr) {
     const int r = blockIdx.x * kGatherRows + rr;
     if (r >= R) return;
@@ -156,8 +181,10 @@ size_t permute_workspace_bytes(int T, int E) {
 __global__ __launch_bounds__(256) void k_gather_mx(const int32_t* __restrict__ src_row,
                                                    const uint16_t* __restrict__ x,
                                                    uint8_t* __restrict__ x_perm,
-                                                   uint8_t* __restrict__ x_scale, int R, int H) {
+                                                   uint8_t* __restrict__ x_scale, int R, int H,
+                                                   const int32_t* __restrict__ n_rows) {
   const int chunks = H / 8;
+  R = gather_rows(R, n_rows);
   for (int rr = 0; rr < kGatherRows; ++rr) {
     const int r = blockIdx.x * kGatherRows + rr;
     if (r >= R) return;
@@ -186,28 +213,31 @@ __global__ __launch_bounds__(256) void k_gather_mx(const int32_t* __restrict__ s
 hipError_t launch_permute(const int32_t* topk_idx, const uint16_t* x, int32_t* counts,
                           int32_t* offsets, int32_t* dest, int32_t* src_row, void* x_perm,
                           void* x_perm_scale, int32_t* tile_cnt, int T, int H, int E, int k,
-                          int n_shared, bool fp8, bool mx, hipStream_t s) {
+                          int n_shared, int e_first, bool share, bool fp8, bool mx,
+                          hipStream_t s) {
   const int n_tiles = ceil_div(T, kRankTile);
   if (T > 0)
     MOE_LAUNCH("tile_hist", k_tile_hist, dim3(n_tiles), dim3(kRankTile), 0, s, topk_idx, tile_cnt,
-               T, E, k);
+               T, E, k, e_first);
   MOE_LAUNCH("scan", k_scan, dim3(1), dim3(1024), 0, s, tile_cnt, n_tiles, counts, offsets, T, E,
              n_shared);
   if (T == 0) return hipGetLastError();
   MOE_LAUNCH("rank", k_rank, dim3(n_tiles), dim3(kRankTile), 0, s, topk_idx, offsets, tile_cnt,
-             dest, src_row, T, E, k, n_shared);
+             dest, src_row, T, E, k, n_shared, e_first);
   if (x_perm == nullptr) return hipGetLastError();
   const int R = T * (k + n_shared);
+  // A share has fewer rows than R; its count is offsets[G] on the device.
+  const int32_t* n_rows = share ? offsets + E + n_shared : nullptr;
   const dim3 grid(ceil_div(R, kGatherRows));
   if (mx)
     MOE_LAUNCH("gather_mx", k_gather_mx, grid, dim3(256), 0, s, src_row, x,
-               static_cast<uint8_t*>(x_perm), static_cast<uint8_t*>(x_perm_scale), R, H);
+               static_cast<uint8_t*>(x_perm), static_cast<uint8_t*>(x_perm_scale), R, H, n_rows);
   else if (fp8)
     MOE_LAUNCH("gather_fp8", k_gather_fp8, grid, dim3(256), 0, s, src_row, x,
-               static_cast<uint8_t*>(x_perm), static_cast<float*>(x_perm_scale), R, H);
+               static_cast<uint8_t*>(x_perm), static_cast<float*>(x_perm_scale), R, H, n_rows);
   else
     MOE_LAUNCH("gather_bf16", k_gather_bf16, grid, dim3(256), 0, s, src_row, x,
-               static_cast<uint16_t*>(x_perm), R, H);
+               static_cast<uint16_t*>(x_perm), R, H, n_rows);
   return hipGetLastError();
 }
 
@@ -216,10 +246,12 @@ hipError_t launch_quantize_rows(const uint16_t* x, uint8_t* xq, void* xs, int T,
   if (T == 0) return hipSuccess;
   if (mx)
     MOE_LAUNCH("quantize_rows_mx", k_gather_mx, dim3(ceil_div(T, kGatherRows)), dim3(256), 0, s,
-               static_cast<const int32_t*>(nullptr), x, xq, static_cast<uint8_t*>(xs), T, H);
+               static_cast<const int32_t*>(nullptr), x, xq, static_cast<uint8_t*>(xs), T, H,
+               static_cast<const int32_t*>(nullptr));
   else
     MOE_LAUNCH("quantize_rows_fp8", k_gather_fp8, dim3(ceil_div(T, kGatherRows)), dim3(256), 0, s,
-               static_cast<const int32_t*>(nullptr), x, xq, static_cast<float*>(xs), T, H);
+               static_cast<const int32_t*>(nullptr), x, xq, static_cast<float*>(xs), T, H,
+               static_cast<const int32_t*>(nullptr));
   return hipGetLastError();
 }
 

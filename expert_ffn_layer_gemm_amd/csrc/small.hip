@@ -16,7 +16,7 @@ constexpr int kMaxK = 16;
 __global__ __launch_bounds__(1024) void k_dispatch_small(
     const int32_t* __restrict__ topk_idx, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ dest, int32_t* __restrict__ src_row,
-    Sched sc, int T, int E, int k, int n_shared) {
+    Sched sc, int T, int E, int k, int n_shared, int e_first) {
   __shared__ int sidx[kSmallT * kMaxK];                 // expert of every (t, j)
   __shared__ int cnt[2048];
   __shared__ int offs[2049];
@@ -31,12 +31,14 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(
   for (int i = tid; i < E * (kSmallT / 32); i += 1024) mask[i] = 0u;
   __syncthreads();
 
-  // 2. histogram and per-expert token masks (thread t = token t).
+  // 2. histogram and per-expert token masks (thread t = token t) of the
+  //    experts held here (E of them, global ids e_first ..).
   const int word = tid >> 5;
   const uint32_t bit = 1u << (tid & 31);
   if (tid < T)
     for (int j = 0; j < k; ++j) {
-      const int e = sidx[tid * k + j];
+      const int e = sidx[tid * k + j] - e_first;
+      if ((unsigned)e >= (unsigned)E) continue;
       atomicAdd(&cnt[e], 1);
       atomicOr(&mask[e * (kSmallT / 32) + word], bit);
     }
@@ -51,7 +53,11 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(
   // 4. token-ascending ranks inside each group.
   if (tid < T) {
     for (int j = 0; j < k; ++j) {
-      const int e = sidx[tid * k + j];
+      const int e = sidx[tid * k + j] - e_first;
+      if ((unsigned)e >= (unsigned)E) {   // routed to another share's expert
+        dest[tid * k + j] = -1;
+        continue;
+      }
       const uint32_t* m = mask + e * (kSmallT / 32);
       int rank = __popc(m[word] & (bit - 1u));
       for (int w = 0; w < word; ++w) rank += __popc(m[w]);
@@ -69,9 +75,9 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(
 // Requires T <= kSmallBatch, k <= 16 and E <= 1024.
 hipError_t launch_dispatch_small(const int32_t* idx, int32_t* counts, int32_t* offsets,
                                  int32_t* dest, int32_t* src_row, const Sched& sc, int T, int E,
-                                 int k, int n_shared, hipStream_t s) {
+                                 int k, int n_shared, int e_first, hipStream_t s) {
   MOE_LAUNCH("dispatch_small", k_dispatch_small, dim3(1), dim3(1024), 0, s, idx, counts, offsets,
-             dest, src_row, sc, T, E, k, n_shared);
+             dest, src_row, sc, T, E, k, n_shared, e_first);
   return hipGetLastError();
 }
 

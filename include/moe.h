@@ -19,7 +19,13 @@
  *     128-element vector;
  *   - group sizes read on the device, never synchronised back to the host:
  *     DeepSeek-deployment page, Quantization (routing-aware persistent
- *     kernels) and CUDA Graph sections.
+ *     kernels) and CUDA Graph sections;
+ *   - expert-parallel share (moe_shape.e_local > 0): "CuTeDSL at Perplexity",
+ *     MoE Dispatch/Combine, tensor-parallel deployment (input replicated; the
+ *     local dispatch keeps the tokens routed to this rank's experts, the local
+ *     combine sums them, an all-reduce across ranks, not part of this library,
+ *     adds the shares up) and "Hosting Qwen on Blackwell" (expert-parallel
+ *     prefill kernel).
  *
  * Conventions shared by every entry point:
  *   - Every pointer argument is a DEVICE pointer unless stated otherwise; the
@@ -35,7 +41,8 @@
  *     thread-local message.  No exception crosses the ABI.
  *   - Supported shapes: 0 <= T, T*(k+n_shared) < 2^31, 1 <= k <= min(E, 16),
  *     1 <= E <= 1024, n_shared in {0, 1}, H and I positive multiples of 128,
- *     H, I <= 131072 and H*I < 2^31.
+ *     H, I <= 131072 and H*I < 2^31; e_local = 0 and e_first = 0, or
+ *     1 <= e_local and 0 <= e_first <= E - e_local.
  *     T == 0 is a valid no-op.  Other shapes return MOE_ERR_UNSUPPORTED.
  *   - The library keeps no state between calls; calls on different streams
  *     with disjoint buffers may run concurrently.
@@ -74,8 +81,20 @@ typedef enum {
                                 of v / 2^(byte - 127), saturated at +-448 */
 } moe_wdtype;
 
-/* Shape of one layer call.  G = E + n_shared expert groups; R = T*(k + n_shared)
-   rows in the permuted (expert-contiguous) matrices. */
+/* Shape of one layer call.  L = (e_local ? e_local : E) routed experts held
+   here; G = L + n_shared expert groups; R = T*(k + n_shared) rows bound the
+   permuted (expert-contiguous) matrices.
+
+   Expert-parallel share (e_local > 0): this GPU holds routed experts
+   [e_first, e_first + e_local) of the E and sees all T tokens.  Routing is
+   over all E experts; group g < L holds the pairs routed to expert
+   e_first + g, pairs routed to other experts get dest = -1 and no row, the
+   shared expert's group (if n_shared) follows the local groups, and the
+   output is this share's partial sum: summing the outputs of shares that
+   partition the experts (with the shared expert in one of them) gives the
+   whole layer, up to the bf16 rounding of each share.  Expert weight and
+   scale arrays hold the G local groups.  e_local = 0 (with e_first = 0) is
+   the whole layer. */
 typedef struct {
   int32_t T;        /* tokens */
   int32_t H;        /* hidden size */
@@ -84,6 +103,8 @@ typedef struct {
   int32_t I;        /* SwiGLU intermediate size */
   int32_t n_shared; /* always-on shared experts, 0 or 1 (group E) */
   int32_t wdtype;   /* moe_wdtype */
+  int32_t e_first;  /* first routed expert held here (expert-parallel share) */
+  int32_t e_local;  /* routed experts held here; 0 = all E (the whole layer) */
 } moe_shape;
 
 /* Thread-local description of the last non-OK return on this thread. */
@@ -130,8 +151,8 @@ int moe_route(const moe_shape* shape, const void* x, const float* w_router,
 int moe_route_from_logits(const moe_shape* shape, const float* logits,
                           int32_t* topk_idx, float* topk_w, void* stream);
 
-/* Bytes of device workspace moe_permute needs (ceil(T/256) * E int32).  Only
-   T and E are read; returns 0 for an unsupported shape as well. */
+/* Bytes of device workspace moe_permute needs (ceil(T/256) * L int32).  Only
+   T, E and the share are read; returns 0 for an unsupported shape as well. */
 size_t moe_permute_workspace_bytes(const moe_shape* shape);
 
 /*
@@ -140,11 +161,13 @@ size_t moe_permute_workspace_bytes(const moe_shape* shape);
  * expert-contiguous groups, token-ascending within a group, and the row copy.
  *   topk_idx     [T, k] int32 in [0, E) (distinct per token)
  *   x            [T, H] bf16
- *   counts       [G] int32, written: rows per group (group E = shared, = T)
+ *   counts       [G] int32, written: rows per group (group L = shared, = T)
  *   offsets      [G + 1] int32, written: exclusive prefix sum of counts
- *   dest         [T, k] int32, written: row of (t, j) in the permuted matrix
+ *   dest         [T, k] int32, written: row of (t, j) in the permuted matrix,
+ *                -1 when the pair's expert is not held here (share only)
  *   src_row      [R] int32, written: token of each permuted row
- *                (shared group: rows T*k + t hold token t)
+ *                (shared group: rows offsets[L] + t hold token t;
+ *                offsets[L] = T*k for the whole layer)
  *   x_perm       [R, H], written: bf16 copy of x[src_row[r]], or for
  *                MOE_FP8_E4M3_BLOCK128 the e4m3fn codes of that row quantised
  *                per 128 channels (scale = amax / 448, 1 for an all-zero group,
@@ -195,15 +218,18 @@ int moe_grouped_ffn(const moe_shape* shape, const int32_t* offsets,
 /*
  * Combine ("CuTeDSL at Perplexity", local combine; shared expert added as in
  * the DeepSeek-deployment page, Expert parallelism section):
- *   out[t] = bf16( sum_{j = 0..k-1} topk_w[t, j] * y_perm[dest[t, j]]
- *                  + y_perm[T*k + t] if n_shared )
+ *   out[t] = bf16( sum_{j = 0..k-1, dest[t, j] >= 0} topk_w[t, j] * y_perm[dest[t, j]]
+ *                  + y_perm[offsets[L] + t] if n_shared )
  * summed in fp32 in that fixed order, one rounded product and one rounded add
  * per term (no fused multiply-add), one round-to-nearest-even at the end.
+ * Pairs with dest < 0 (experts held by another share) add nothing.
  * Deterministic, no atomics.
  *   y_perm [R, H] bf16; dest [T, k] int32; topk_w [T, k] fp32; out [T, H] bf16
+ *   offsets [G + 1] int32 from moe_permute: read (on the device) only when
+ *           n_shared = 1, for the start of the shared rows; may be NULL otherwise
  */
 int moe_combine(const moe_shape* shape, const void* y_perm, const int32_t* dest,
-                const float* topk_w, void* out, void* stream);
+                const float* topk_w, const int32_t* offsets, void* out, void* stream);
 
 /*
  * The whole layer in one call: moe_route -> moe_permute -> moe_grouped_ffn ->
@@ -213,7 +239,8 @@ int moe_combine(const moe_shape* shape, const void* y_perm, const int32_t* dest,
  * from x (bf16) or from x quantised once per token (fp8, mxfp8), which gives
  * the same operands as moe_permute's x_perm.  Requires T*H*2 < 2^32.  Arguments as above;
  * topk_idx_out / topk_w_out may be NULL (then the routing lives in the
- * workspace only).  out [T, H] bf16.
+ * workspace only).  out [T, H] bf16: the layer's output, or for an
+ * expert-parallel share (e_local > 0) this share's partial sum.
  */
 int moe_forward(const moe_shape* shape, const void* x, const float* w_router,
                 const float* router_bias, const void* w_gate, const void* w_up,

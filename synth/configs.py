@@ -64,12 +64,20 @@ CONFIGS = [
 
 
 # Further workloads (not among the five above): the Qwen3-235B-like layer with
-# MXFP8 experts, as "Hosting Qwen on Blackwell" (Quantization) deploys it.
+# MXFP8 experts, as "Hosting Qwen on Blackwell" (Quantization) deploys it, and
+# expert-parallel shares of the bf16 layer (one GPU's experts, every token:
+# "CuTeDSL at Perplexity", MoE Dispatch/Combine, tensor-parallel deployment):
+# EP8 at the decode batch (16 experts, about 4 rows each) and EP4 at the
+# prefill chunk ("Hosting Qwen on Blackwell" runs its prefill EP on 4 GPUs).
 EXTRA_CONFIGS = [
     MoeConfig("qwen3_235b_decode_mxfp8", 5, T=64, H=4096, E=128, k=8, I=1536, wdtype="mxfp8",
               regime="hbm"),
     MoeConfig("qwen3_235b_prefill_mxfp8", 6, T=8192, H=4096, E=128, k=8, I=1536, wdtype="mxfp8",
               regime="mfma"),
+    MoeConfig("qwen3_235b_decode_ep8", 7, T=64, H=4096, E=128, k=8, I=1536, e_first=16, e_local=16,
+              regime="hbm"),
+    MoeConfig("qwen3_235b_prefill_ep4", 8, T=8192, H=4096, E=128, k=8, I=1536, e_first=32,
+              e_local=32, regime="mfma"),
 ]
 
 

@@ -37,7 +37,7 @@ def test_shape_struct_matches_header():
 
 
 def test_abi_version():
-    assert moe.moe_abi_version() == 3
+    assert moe.moe_abi_version() == 4
 
 
 FAKE = 0x10000  # a non-NULL, aligned address; never dereferenced (validation fails first)
@@ -80,7 +80,11 @@ def test_error_codes_before_launch():
     assert _call("moe_route", P(bad), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, 0, None) == moe.MOE_ERR_UNSUPPORTED
     assert _call("moe_route_from_logits", P(bad), FAKE, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
     bad_dt = moe.MoeShape(64, 256, 8, 2, 512, 0, 3)
-    assert _call("moe_combine", P(bad_dt), FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert _call("moe_combine", P(bad_dt), FAKE, FAKE, FAKE, None, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    # the shared rows' start comes from offsets
+    sh1 = moe.make_shape(64, 256, 8, 2, 512, 1)
+    assert _call("moe_combine", P(sh1), FAKE, FAKE, FAKE, None, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert "offsets is NULL" in moe.moe_last_error()
     # workspace too small / missing
     need = moe.moe_forward_workspace_bytes(sh)
     args = [P(sh), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None, None, FAKE, None, None]
@@ -106,11 +110,28 @@ def test_error_codes_before_launch():
                  pneed - 1, None) == moe.MOE_ERR_WORKSPACE
 
 
+def test_expert_share_shapes():
+    whole = moe.make_shape(64, 4096, 128, 8, 1536)
+    share = moe.make_shape(64, 4096, 128, 8, 1536, 0, "bf16", 16, 16)     # experts 16..31
+    assert 0 < moe.moe_permute_workspace_bytes(share) < moe.moe_permute_workspace_bytes(whole)
+    assert 0 < moe.moe_ffn_workspace_bytes(share) <= moe.moe_ffn_workspace_bytes(whole)
+    assert moe.moe_forward_workspace_bytes(share) > 0
+    last = moe.make_shape(64, 4096, 128, 8, 1536, 1, "bf16", 112, 16)     # experts 112..127 + shared
+    assert moe.moe_forward_workspace_bytes(last) > 0
+    for ef, el in ((0, -1), (-1, 4), (120, 16), (3, 0), (0, 129)):
+        bad = moe.make_shape(64, 4096, 128, 8, 1536, 0, "bf16", ef, el)
+        assert moe.moe_forward_workspace_bytes(bad) == 0
+        assert moe.moe_permute_workspace_bytes(bad) == 0
+    bad = moe.make_shape(64, 256, 8, 2, 512, 0, "bf16", 6, 4)
+    assert _call("moe_combine", ctypes.byref(bad), FAKE, FAKE, FAKE, None, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert "share" in moe.moe_last_error()
+
+
 def test_zero_tokens_is_a_no_op():
     sh = moe.make_shape(0, 256, 8, 2, 512)
     P = ctypes.byref
     assert _call("moe_route", P(sh), None, None, None, None, None, None, None, 0, None) == moe.MOE_OK
-    assert _call("moe_combine", P(sh), None, None, None, None, None) == moe.MOE_OK
+    assert _call("moe_combine", P(sh), None, None, None, None, None, None) == moe.MOE_OK
     assert _call("moe_forward", P(sh), *([None] * 12), None, 0, None) == moe.MOE_OK
 
 

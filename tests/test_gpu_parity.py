@@ -119,22 +119,24 @@ def test_route_zero_router_weight_ties():
 # ---------------------------------------------------------------- permute ----
 def _check_permute(cfg, li, idx):
     counts, offsets, dest, src, x_perm, x_scale = run_permute(cfg, idx, li.x)
-    c_ref, o_ref, d_ref, s_ref = oracle.counting_sort(idx.cpu().numpy(), cfg.E, cfg.n_shared)
+    c_ref, o_ref, d_ref, s_ref = oracle.counting_sort(idx.cpu().numpy(), cfg.E, cfg.n_shared,
+                                                      cfg.e_first, cfg.e_local)
+    R = int(o_ref[-1])                   # rows of the share (R = T*(k + n_shared) for the layer)
     assert np.array_equal(counts.cpu().numpy(), c_ref)
     assert np.array_equal(offsets.cpu().numpy(), o_ref)
     assert np.array_equal(dest.cpu().numpy(), d_ref)
-    assert np.array_equal(src.cpu().numpy(), s_ref)
+    assert np.array_equal(src.cpu().numpy()[:R], s_ref)
     xb = bf16_bits_np(li.x)
     if cfg.wdtype == "fp8":
         codes, scales = oracle.quantize_groups_128(oracle.bf16_bits_to_f32(xb))
-        assert np.array_equal(x_perm.cpu().numpy(), codes[s_ref])
-        assert np.array_equal(x_scale.cpu().numpy(), scales[s_ref])
+        assert np.array_equal(x_perm.cpu().numpy()[:R], codes[s_ref])
+        assert np.array_equal(x_scale.cpu().numpy()[:R], scales[s_ref])
     elif cfg.wdtype == "mxfp8":
         codes, e8 = oracle.mx_quantize_rows(oracle.bf16_bits_to_f32(xb))
-        assert np.array_equal(x_perm.cpu().numpy(), codes[s_ref])
-        assert np.array_equal(x_scale.cpu().numpy(), e8[s_ref])
+        assert np.array_equal(x_perm.cpu().numpy()[:R], codes[s_ref])
+        assert np.array_equal(x_scale.cpu().numpy()[:R], e8[s_ref])
     else:
-        assert np.array_equal(bf16_bits_np(x_perm), xb[s_ref])
+        assert np.array_equal(bf16_bits_np(x_perm)[:R], xb[s_ref])
 
 
 @pytest.mark.parametrize("ci", range(len(CONFIGS)))
@@ -154,6 +156,19 @@ def test_permute_ragged_shapes(T, E, k, ns, wdtype):
     p = 1.0 / np.arange(1, E + 1) ** 1.2
     p /= p.sum()
     idx = np.stack([rng.choice(E, k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    li = generate_layer(cfg, DEV)
+    _check_permute(cfg, li, torch.from_numpy(idx).to(DEV))
+
+
+# Expert-parallel shares: only the pairs routed to experts [e_first,
+# e_first + e_local) get rows; the rest get dest = -1.
+@pytest.mark.parametrize("T,E,k,ns,ef,el,wdtype", [(300, 16, 4, 1, 4, 5, "bf16"), (600, 64, 8, 0, 60, 4, "fp8"),
+                                                   (257, 9, 3, 1, 0, 1, "mxfp8"), (1000, 128, 8, 0, 16, 16, "bf16")])
+def test_permute_share(T, E, k, ns, ef, el, wdtype):
+    cfg = MoeConfig("perm_share", 10, T=T, H=256, E=E, k=k, I=128, n_shared=ns, wdtype=wdtype,
+                    e_first=ef, e_local=el)
+    rng = np.random.default_rng(T + E + ef)
+    idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
     li = generate_layer(cfg, DEV)
     _check_permute(cfg, li, torch.from_numpy(idx).to(DEV))
 
@@ -237,11 +252,36 @@ def test_combine_bitexact(T, H, k, ns):
     dest = perm.reshape(T, k)
     w = rng.random((T, k)).astype(np.float32)
     w /= w.sum(1, keepdims=True)
-    sh = moe.make_shape(T, H, max(k, 2), k, 128, ns)
+    E = max(k, 2)
+    sh = moe.make_shape(T, H, E, k, 128, ns)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
-    moe.moe_combine(sh, y.to(DEV), torch.from_numpy(dest).to(DEV), torch.from_numpy(w).to(DEV), out)
+    offsets = np.zeros(E + ns + 1, np.int32)     # only offsets[E] (start of the shared rows) is read
+    offsets[E:] = T * k
+    moe.moe_combine(sh, y.to(DEV), torch.from_numpy(dest).to(DEV), torch.from_numpy(w).to(DEV),
+                    torch.from_numpy(offsets).to(DEV) if ns else None, out)
     torch.cuda.synchronize()
     ref = oracle.combine(y.float().numpy(), dest, w, ns)
+    assert np.array_equal(bf16_np(out), to_bf16_rne(ref))
+
+
+# An expert-parallel share: pairs of other shares' experts (dest = -1) add
+# nothing, and the shared rows start at offsets[L], below T*k.
+@pytest.mark.parametrize("ns", [0, 1])
+def test_combine_share_bitexact(ns):
+    rng = np.random.default_rng(77 + ns)
+    T, H, k, E, L = 90, 512, 4, 16, 5
+    idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    counts, offsets, dest, src = oracle.counting_sort(idx, E, ns, 3, L)
+    R = int(offsets[-1])
+    y = torch.randn((R, H), generator=torch.Generator().manual_seed(5), dtype=torch.float32).to(torch.bfloat16)
+    w = rng.random((T, k)).astype(np.float32)
+    sh = moe.make_shape(T, H, E, k, 128, ns, "bf16", 3, L)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    moe.moe_combine(sh, y.to(DEV), torch.from_numpy(dest).to(DEV), torch.from_numpy(w).to(DEV),
+                    torch.from_numpy(offsets).to(DEV), out)
+    torch.cuda.synchronize()
+    ref = oracle.combine(y.float().numpy(), dest, w, ns, shared_base=offsets[L])
+    assert (dest < 0).any()
     assert np.array_equal(bf16_np(out), to_bf16_rne(ref))
 
 
@@ -286,7 +326,7 @@ def test_forward_configs_sampled(ci):
 
 
 # MXFP8 layers at the Qwen3-235B shape: decode in full, prefill on sampled tokens.
-@pytest.mark.parametrize("name", [c.name for c in EXTRA_CONFIGS])
+@pytest.mark.parametrize("name", [c.name for c in EXTRA_CONFIGS if c.wdtype == "mxfp8"])
 def test_forward_mxfp8_configs(name):
     cfg = next(c for c in EXTRA_CONFIGS if c.name == name)
     sample = None
@@ -330,6 +370,51 @@ def test_forward_edge_cases(case):
         li.router_bias = torch.zeros(cfg.E, dtype=torch.float32, device=DEV)
         li.router_bias[3] = 100.0          # every token -> expert 3: 300 rows, ragged tiles
     _forward_check(cfg, li)
+
+
+# Expert-parallel shares of the whole layer: small batches (single-workgroup
+# dispatch) and large ones (tile kernels), with and without the shared
+# expert, bf16 / fp8 / mxfp8; the EP8 shares of the Qwen3-235B-like layer.
+SHARES = [
+    MoeConfig("sh_small", 50, T=64, H=512, E=32, k=4, I=256, e_first=8, e_local=8),
+    MoeConfig("sh_small_shared", 51, T=200, H=256, E=12, k=3, I=256, n_shared=1, e_first=9, e_local=3),
+    MoeConfig("sh_large_fp8", 52, T=1500, H=512, E=16, k=4, I=256, n_shared=1, wdtype="fp8",
+              e_first=4, e_local=4),
+    MoeConfig("sh_large_mx", 53, T=700, H=384, E=8, k=2, I=256, wdtype="mxfp8", e_first=0, e_local=2),
+    MoeConfig("sh_one_expert", 54, T=300, H=256, E=8, k=2, I=128, e_first=7, e_local=1),
+]
+
+
+@pytest.mark.parametrize("cfg", SHARES, ids=[c.name for c in SHARES])
+def test_forward_share(cfg):
+    _forward_check(cfg, generate_layer(cfg, DEV))
+
+
+@pytest.mark.parametrize("name", [c.name for c in EXTRA_CONFIGS if c.e_local])
+def test_forward_share_configs(name):
+    cfg = next(c for c in EXTRA_CONFIGS if c.name == name)
+    sample = None
+    if cfg.T > 1024:
+        rng = np.random.default_rng(cfg.seed)
+        sample = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 14, replace=False)]))
+    _forward_check(cfg, layer(cfg), sample)
+
+
+def test_shares_sum_to_the_layer_on_gpu():
+    # Shares partitioning the experts (the shared expert on one of them) add up
+    # to the whole layer: the all-reduce of the expert-parallel deployment.
+    base = dict(T=400, H=512, E=24, k=4, I=256, wdtype="bf16")
+    full_cfg = MoeConfig("sum_full", 55, n_shared=1, **base)
+    full, _, _ = run_forward(full_cfg, generate_layer(full_cfg, DEV))
+    total = torch.zeros((400, 512), dtype=torch.float32, device=DEV)
+    for ef, el, ns in ((0, 10, 1), (10, 4, 0), (14, 10, 0)):
+        c = MoeConfig("sum_share", 55, n_shared=ns, e_first=ef, e_local=el, **base)
+        out, _, _ = run_forward(c, generate_layer(c, DEV))
+        total += out.float()
+    ref = full.float().cpu().numpy().astype(np.float64)
+    err = rel_inf(total.cpu().numpy().astype(np.float64), ref)
+    print(f"sum of shares vs layer: per-token rel err {err:.3e}")
+    assert err <= 1e-2      # each share's output is rounded to bf16 once
 
 
 def test_forward_zero_tokens():
