@@ -40,10 +40,17 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ offse
 // Workgroup = NW waves; wave w owns 16 h columns (DUAL) or 32 output columns and
 // all (<= 16*MB) rows of its slice.  Lane l: row/column l%16 of each 16x16 MFMA block, 8
 // consecutive k at offset 8*(l/16) of each 32-wide K step.
+// Split-K (p.ksplit > 1; "Lower latency and higher throughput with multi-node
+// DeepSeek deployment", GEMM kernels: split-K lowers the latency of some
+// shapes at low batch): when few experts hold rows, K is cut into ksplit
+// ranges, block b taking range b % ksplit of the work item b / ksplit, so
+// ksplit times as many waves stream the weights; each writes its fp32
+// partial sums and k_splitk_reduce adds them in range order.
 template <bool DUAL, int NW, int MB>
 __global__ __launch_bounds__(64 * NW) void k_skinny_bf16(const GemmArgs p) {
   int slot, nt;
-  if (!band_item(p.sc.skinny, *p.sc.n_skinny, p.n_ntile, slot, nt)) return;
+  const int ks = blockIdx.x % p.ksplit;
+  if (!band_item(p.sc.skinny, *p.sc.n_skinny, p.n_ntile, slot, nt, blockIdx.x / p.ksplit)) return;
   const int g = p.sc.skinny[4 * slot], s0 = p.sc.skinny[4 * slot + 1];
   const int row0 = p.offsets[g] + s0, m = min(16 * MB, p.offsets[g + 1] - row0);
   const int nmb = ceil_div(m, 16);
@@ -54,8 +61,10 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_bf16(const GemmArgs p) {
   // the rows of 32 consecutive output columns (16 + 16).
   const int n0 = (nt * NW + wave) * (DUAL ? 16 : 32);
 
-  const uint16_t* b0 = reinterpret_cast<const uint16_t*>(p.B0) + ((size_t)g * N + n0 + r16) * K + kq;
-  const uint16_t* b1 = DUAL ? reinterpret_cast<const uint16_t*>(p.B1) + ((size_t)g * N + n0 + r16) * K + kq
+  // This block's K range [kbeg, kbeg + Kc).
+  const int Kc = K / p.ksplit, kbeg = ks * Kc;
+  const uint16_t* b0 = reinterpret_cast<const uint16_t*>(p.B0) + ((size_t)g * N + n0 + r16) * K + kq + kbeg;
+  const uint16_t* b1 = DUAL ? reinterpret_cast<const uint16_t*>(p.B1) + ((size_t)g * N + n0 + r16) * K + kq + kbeg
                             : b0 + (size_t)16 * K;
   const uint16_t* arow[MB];
   bool aok[MB];
@@ -64,7 +73,7 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_bf16(const GemmArgs p) {
     const int r = mb * 16 + r16;
     aok[mb] = r < m;
     const int pr = row0 + (aok[mb] ? r : 0);
-    arow[mb] = reinterpret_cast<const uint16_t*>(p.A) + (size_t)(p.a_rows ? p.a_rows[pr] : pr) * K + kq;
+    arow[mb] = reinterpret_cast<const uint16_t*>(p.A) + (size_t)(p.a_rows ? p.a_rows[pr] : pr) * K + kq + kbeg;
   }
 
   f32x4_t acc0[MB], acc1[MB];
@@ -78,8 +87,8 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_bf16(const GemmArgs p) {
     cur0[u] = *reinterpret_cast<const u32x4_t*>(b0 + u * 32);
     cur1[u] = *reinterpret_cast<const u32x4_t*>(b1 + u * 32);
   }
-  for (int k0 = 0; k0 < K; k0 += 32 * U) {
-    const bool more = k0 + 32 * U < K;
+  for (int k0 = 0; k0 < Kc; k0 += 32 * U) {
+    const bool more = k0 + 32 * U < Kc;
     if (more) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -114,6 +123,23 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_bf16(const GemmArgs p) {
     }
   }
 
+  if (p.ksplit > 1) {   // fp32 partials of this K range: gate | up, or two column blocks
+    const int NP = DUAL ? 2 * N : N;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      if (mb < nmb) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = mb * 16 + (lane >> 4) * 4 + q;
+          if (r < m) {
+            float* o = p.part + ((size_t)ks * p.R + row0 + r) * NP + n0 + r16;
+            o[0] = acc0[mb][q];
+            o[DUAL ? N : 16] = acc1[mb][q];
+          }
+        }
+      }
+    return;
+  }
   uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
@@ -132,6 +158,38 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_bf16(const GemmArgs p) {
         }
       }
     }
+}
+
+// Sum of the ksplit fp32 partial planes in plane order for rows below
+// *n_rows, then the epilogue: DUAL h = bf16(silu(gate) * up), else bf16(y).
+// 4 columns per thread.
+template <bool DUAL>
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ part, int ksplit,
+                                                       int R, int N, const int32_t* __restrict__ n_rows,
+                                                       uint16_t* __restrict__ out) {
+  const int r = blockIdx.y;
+  if (r >= *n_rows) return;
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (c >= N) return;
+  const int NP = DUAL ? 2 * N : N;
+  float4 a = *reinterpret_cast<const float4*>(part + (size_t)r * NP + c);
+  float4 b = DUAL ? *reinterpret_cast<const float4*>(part + (size_t)r * NP + N + c) : float4{};
+  for (int s = 1; s < ksplit; ++s) {
+    const float* pl = part + ((size_t)s * R + r) * NP;
+    const float4 x = *reinterpret_cast<const float4*>(pl + c);
+    a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+    if (DUAL) {
+      const float4 y = *reinterpret_cast<const float4*>(pl + N + c);
+      b.x += y.x; b.y += y.y; b.z += y.z; b.w += y.w;
+    }
+  }
+  if (DUAL) {
+    a.x = silu_mul(a.x, b.x); a.y = silu_mul(a.y, b.y);
+    a.z = silu_mul(a.z, b.z); a.w = silu_mul(a.w, b.w);
+  }
+  const uint32_t lo = f32_to_bf16_bits(a.x) | (f32_to_bf16_bits(a.y) << 16);
+  const uint32_t hi = f32_to_bf16_bits(a.z) | (f32_to_bf16_bits(a.w) << 16);
+  *reinterpret_cast<uint2*>(out + (size_t)r * N + c) = make_uint2(lo, hi);
 }
 
 // ----------------------------------------------------------- skinny, fp8 ----
@@ -412,9 +470,22 @@ namespace {
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 struct WsLayout {
-  size_t h, h_scale, n_skinny, n_tiles, skinny, tiles, total;
+  size_t h, h_scale, n_skinny, n_tiles, skinny, tiles, part, total;
   int max_tiles, max_slices;
+  int split_up, split_dn;   // split-K factors of the bf16 streaming GEMMs (1 = none)
 };
+
+// Split-K factor of a bf16 streaming GEMM whose at most `items` slices have
+// `waves` waves each and stream [N, K] weights: the smallest power of two up
+// to 8 that gives the chip about 4096 waves (16 per CU), keeping K / S a
+// multiple of 128.  Below 32 MB of weights the launch latency dominates and
+// the extra reduce launch would cost more than it saves: no split.
+int split_factor(long long items, long long waves, int N, int K) {
+  if (items * N * K * 2 < (32LL << 20)) return 1;
+  int S = 1;
+  while (S < 8 && items * waves * S < 4096 && K % (2 * S * 128) == 0) S *= 2;
+  return S;
+}
 
 WsLayout ffn_layout(int T, int H, int E, int k, int I, int n_shared, bool fp8, bool mx) {
   (void)H;
@@ -432,6 +503,17 @@ WsLayout ffn_layout(int T, int H, int E, int k, int I, int n_shared, bool fp8, b
   L.max_slices = (int)std::min<long long>(4LL * G, R / kSliceRows + G);
   L.skinny = off;   off += align256((size_t)L.max_slices * 16);
   L.tiles = off;    off += align256((size_t)L.max_tiles * 16);
+  // Split-K partials: bf16 layers whose groups all stay below kSkinnyMax rows
+  // (T <= kSkinnyMax: no tiled work), when few slices would leave the chip idle.
+  L.split_up = L.split_dn = 1;
+  if (!fp8 && T <= kSkinnyMax) {
+    const long long items = std::min<long long>(G, R);
+    L.split_up = split_factor(items, I / 16, 2 * I, H);
+    L.split_dn = split_factor(items, H / 32, H, I);
+  }
+  L.part = off;
+  if (L.split_up > 1 || L.split_dn > 1)
+    off += align256((size_t)R * 4 * std::max((size_t)L.split_up * 2 * I, (size_t)L.split_dn * H));
   L.total = off;
   return L;
 }
@@ -556,10 +638,29 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
     dn.n_ntile = f.H / (16 * 4);
     launch_gemm("skinny_down_fp8", k_skinny_fp8<false, 4, 1>, 256, band_grid(L.max_slices, dn.n_ntile), dn, s);
   } else {
+    // Split-K only without tiled work (the layout reserved the partials then).
+    const bool split = !tiled && (L.split_up > 1 || L.split_dn > 1);
+    float* part = reinterpret_cast<float*>(ws + L.part);
+    const int32_t* n_rows = f.offsets + (f.E + f.n_shared);
     up.n_ntile = f.I / (16 * 4);
-    launch_gemm("skinny_gateup_bf16", k_skinny_bf16<true, 4, 1>, 256, band_grid(L.max_slices, up.n_ntile), up, s);
+    up.ksplit = split ? L.split_up : 1;
+    up.R = (int)R;
+    up.part = part;
+    launch_gemm("skinny_gateup_bf16", k_skinny_bf16<true, 4, 1>, 256,
+                band_grid(L.max_slices, up.n_ntile) * up.ksplit, up, s);
+    if (up.ksplit > 1)
+      MOE_LAUNCH("splitk_reduce_gateup", k_splitk_reduce<true>, dim3(ceil_div(f.I, 1024), (unsigned)R),
+                 dim3(256), 0, s, part, up.ksplit, (int)R, f.I, n_rows, reinterpret_cast<uint16_t*>(h));
     dn.n_ntile = f.H / (32 * 4);
-    launch_gemm("skinny_down_bf16", k_skinny_bf16<false, 4, 1>, 256, band_grid(L.max_slices, dn.n_ntile), dn, s);
+    dn.ksplit = split ? L.split_dn : 1;
+    dn.R = (int)R;
+    dn.part = part;
+    launch_gemm("skinny_down_bf16", k_skinny_bf16<false, 4, 1>, 256,
+                band_grid(L.max_slices, dn.n_ntile) * dn.ksplit, dn, s);
+    if (dn.ksplit > 1)
+      MOE_LAUNCH("splitk_reduce_down", k_splitk_reduce<false>, dim3(ceil_div(f.H, 1024), (unsigned)R),
+                 dim3(256), 0, s, part, dn.ksplit, (int)R, f.H, n_rows,
+                 static_cast<uint16_t*>(f.y_perm));
   }
   if (side) {                        // join: the caller's stream waits for the tiled chain
     hipError_t e = hipEventRecord(side->join, side->s);

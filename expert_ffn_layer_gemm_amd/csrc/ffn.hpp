@@ -48,11 +48,10 @@ struct Sched {
 // per item, the last two being the band's first item and its size.  Returns
 // false for blocks past the valid pairs.
 __device__ __forceinline__ bool band_item(const int32_t* items, int n_items, int n_ntile, int& item,
-                                          int& nt) {
+                                          int& nt, int bid) {
   constexpr int kXcd = 8;
   const int n_valid = n_items * n_ntile;
   const int per_xcd = (n_valid + kXcd - 1) / kXcd;
-  const int bid = blockIdx.x;
   const int logical = (bid % kXcd) * per_xcd + bid / kXcd;
   if (bid >= kXcd * per_xcd || logical >= n_valid) return false;
   const int band_first = items[4 * (logical / n_ntile) + 2];
@@ -61,6 +60,11 @@ __device__ __forceinline__ bool band_item(const int32_t* items, int n_items, int
   item = band_first + local % band_size;
   nt = local / band_size;
   return true;
+}
+
+__device__ __forceinline__ bool band_item(const int32_t* items, int n_items, int n_ntile, int& item,
+                                          int& nt) {
+  return band_item(items, n_items, n_ntile, item, nt, blockIdx.x);
 }
 
 // Grid size for band_item over at most max_items items: the renumbering
@@ -86,6 +90,12 @@ struct GemmArgs {
   uint8_t* out;            // bf16 or e4m3 codes
   void* out_scale;         // dual: fp8 [R, N/128] fp32; mxfp8 [R, N/32] E8M0 bytes
   int K, N, n_ntile;
+  // Split-K (bf16 streaming kernel): ksplit workgroups per (slice, column
+  // tile) each sum K / ksplit of K into part [ksplit][R][dual ? 2N : N] fp32;
+  // a reduce kernel adds the slices in order and applies the epilogue.
+  int ksplit = 1;
+  int R = 0;
+  float* part = nullptr;
 };
 
 // Tiled kernel launch (tiled.hip).

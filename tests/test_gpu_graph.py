@@ -48,6 +48,8 @@ CASES = [
     # on the library's second stream, forked and joined inside the capture
     MoeConfig("graph_mixed", 23, T=512, H=512, E=64, k=4, I=256, zipf_s=1.1),
     MoeConfig("graph_mxfp8", 24, T=384, H=512, E=16, k=4, I=256, n_shared=1, wdtype="mxfp8"),
+    # an expert-parallel share whose streaming GEMMs take split-K
+    MoeConfig("graph_share_splitk", 25, T=16, H=2048, E=64, k=4, I=1024, e_first=8, e_local=8),
 ]
 
 

@@ -400,6 +400,22 @@ def test_forward_share_configs(name):
     _forward_check(cfg, layer(cfg), sample)
 
 
+# Decode batches whose groups leave the chip idle take split-K in the bf16
+# streaming GEMMs (partials summed in K-range order by a reduce kernel):
+# factors 2 to 8, with and without a shared expert, whole layer and shares.
+SPLITK = [
+    MoeConfig("sk_q235_t4", 60, T=4, H=4096, E=128, k=8, I=1536),
+    MoeConfig("sk_share_s8", 61, T=16, H=2048, E=64, k=4, I=1024, e_first=8, e_local=8),
+    MoeConfig("sk_share_shared", 62, T=8, H=4096, E=16, k=2, I=1024, n_shared=1, e_first=12,
+              e_local=4),
+]
+
+
+@pytest.mark.parametrize("cfg", SPLITK, ids=[c.name for c in SPLITK])
+def test_forward_split_k(cfg):
+    _forward_check(cfg, generate_layer(cfg, DEV))
+
+
 def test_shares_sum_to_the_layer_on_gpu():
     # Shares partitioning the experts (the shared expert on one of them) add up
     # to the whole layer: the all-reduce of the expert-parallel deployment.
