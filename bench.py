@@ -130,7 +130,9 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # One untimed step with events around every launch: find the dominant kernel.
+    # One untimed step with events around every launch: find the dominant kernel
+    # (in this mode the library runs its two FFN kernel chains one after the
+    # other, so each launch is timed alone).
     moe.moe_profile_start(1, 0, 64)
     step()
     launches = [moe.moe_profile_read(i) for i in range(moe.moe_profile_count())]

@@ -604,7 +604,7 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
 
   // No group above kSkinnyMax rows: no tiled work, skip its launches (decode).
   const bool tiled = f.max_group_rows > kSkinnyMax;
-  SideStream* side = tiled ? side_stream() : nullptr;
+  SideStream* side = tiled && !prof_serial() ? side_stream() : nullptr;
   hipStream_t ts = s;                // stream of the tiled chain
   if (side) {                        // fork after the plan
     hipError_t e = hipEventRecord(side->fork, s);

@@ -12,6 +12,8 @@ namespace moe {
 void prof_call_begin();
 void prof_before(const char* name, hipStream_t s);
 void prof_after(hipStream_t s);
+// Per-launch timing is on: run concurrent kernel chains one after the other.
+bool prof_serial();
 
 // Launch a kernel, bracketed by the measurement hook.
 #define MOE_LAUNCH(name, kernel, grid, block, shmem, stream, ...)          \

@@ -31,6 +31,8 @@ void release() {
 
 void prof_call_begin() { g.call_launch = 0; }
 
+bool prof_serial() { return g.mode == 1; }
+
 void prof_before(const char* name, hipStream_t s) {
   if (g.mode == 0) return;
   const bool take = (g.mode == 1 || g.call_launch == g.which) && g.n < g.capacity;

@@ -254,6 +254,9 @@ int moe_forward(const moe_shape* shape, const void* x, const float* w_router,
  * entry-point calls made on this thread record a pair of HIP events on their
  * stream around kernel launches:
  *   mode 1: around every launch, in launch order, up to `capacity` pairs;
+ *           the grouped FFN's two kernel chains (groups above and below 64
+ *           rows) then run one after the other on the caller's stream, so
+ *           each launch is timed alone;
  *   mode 2: around launch number `which` (0-based, counted from the start of
  *           each entry-point call) only, up to `capacity` pairs.
  * The events are created here (host objects; no device memory).
