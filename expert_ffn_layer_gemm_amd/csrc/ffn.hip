@@ -325,44 +325,53 @@ __device__ __forceinline__ i32x8_t ld32(const uint8_t* ptr) {
 
 // Weight streaming for MXFP8 layers (16-row slices).  Wave w owns CB blocks
 // of 16 output columns; lane l loads its row's 32 codes of each 128-K block
-// in the MFMA's layout (16 bytes at K 16*(l/16), 16 at K 64 + 16*(l/16)) and
-// the E8M0 scale of K block 4*kb + l/16 for its A row and its B rows; the
-// scaled MFMA applies both, so the partial sums accumulate directly.  Each A
-// fragment feeds CB (x2 for gate/up) MFMAs.  The operands of U consecutive
-// 128-K blocks sit in a register ring: slot u is refilled with block kb + U
-// right after block kb is multiplied.  DUAL: h = silu(g) * u is quantised
-// per row in MX blocks of 32 columns: within the wave for CB = 2, else two
-// adjacent waves combine their row maxima in LDS.
+// in the MFMA's layout (16 bytes at K 16*(l/16), 16 at K 64 + 16*(l/16)), the
+// next block's codes in flight while the current one is multiplied.  The
+// scaled MFMA applies the E8M0 scales of K block 4*kb + l/16 of the lane's A
+// row and B rows, so the partial sums accumulate directly.  Each A fragment
+// feeds CB (x2 for gate/up) MFMAs.  Scales: one 16-byte load per row and 4 K
+// blocks (the lane picks byte l/16 of each dword); a byte per block and row
+// re-fetched the row's scale line from memory for every block (measured:
+// 0.76 GB of extra HBM reads on the decode workload).  Rows whose scale arrays
+// are not 16-byte aligned (K not a multiple of 512) take the byte loads.
+// DUAL: h = silu(g) * u is quantised per row in MX blocks of 32 columns:
+// within the wave for CB = 2, else two adjacent waves combine their row
+// maxima in LDS.
 template <int NB>
-struct MxSlot {
-  i32x8_t a, b[NB];
-  uint32_t sa, s[NB];
-};
-
-template <int NB>
-__device__ __forceinline__ void mx_fill(MxSlot<NB>& sl, int kb, bool aok, const uint8_t* arow,
-                                        const uint8_t* sarow, const uint8_t* const (&b)[NB],
-                                        const uint8_t* const (&sb)[NB]) {
+__device__ __forceinline__ void mx_load(i32x8_t& a, i32x8_t (&b)[NB], int kb, bool aok,
+                                        const uint8_t* arow, const uint8_t* const (&bp)[NB]) {
 #pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    sl.b[j] = ld32(b[j] + (size_t)kb * 128);
-    sl.s[j] = sb[j][4 * kb];
-  }
-  // Rows past the slice feed zero codes with scale 1 (outputs never stored).
-  sl.a = aok ? ld32(arow + (size_t)kb * 128) : i32x8_t{};
-  sl.sa = aok ? (uint32_t)sarow[4 * kb] : 127u;
+  for (int j = 0; j < NB; ++j) b[j] = ld32(bp[j] + (size_t)kb * 128);
+  // Rows past the slice feed zero codes (outputs never stored).
+  a = aok ? ld32(arow + (size_t)kb * 128) : i32x8_t{};
 }
 
-#ifndef SKINNY_MX_U
+// Scale dwords of K blocks 4 g .. 4 g + 3 of the A row ([NB]) and B rows.
+template <int NB>
+__device__ __forceinline__ void mx_load_scales(u32x4_t (&sv)[NB + 1], int g, const uint8_t* sarow,
+                                               const uint8_t* const (&sbrow)[NB]) {
+#pragma unroll
+  for (int j = 0; j < NB; ++j) sv[j] = *reinterpret_cast<const u32x4_t*>(sbrow[j] + 16 * g);
+  sv[NB] = *reinterpret_cast<const u32x4_t*>(sarow + 16 * g);
+}
+
+#ifndef SKINNY_MX_NW
 #define SKINNY_MX_NW 4    // gate/up: waves per workgroup
 #define SKINNY_MX_CB 2    //          16-column blocks per wave
-#define SKINNY_MX_U 1     //          ring depth (128-K blocks in flight per stream)
 #define SKINNY_MX_NWD 4   // down
 #define SKINNY_MX_CBD 2
-#define SKINNY_MX_UD 1
 #endif
 
-template <bool DUAL, int NW, int CB, int U>
+// Byte q of x.
+__device__ __forceinline__ uint32_t byte_of(uint32_t x, int q) { return (x >> (8 * q)) & 0xFFu; }
+// Element i (0..3, runtime) of a 4-dword vector.
+__device__ __forceinline__ uint32_t dword_of(const u32x4_t v, int i) {
+  return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
+}
+
+// VEC: the scale rows are 16-byte aligned (K a multiple of 512): scales come
+// in one 16-byte load per row and 4 K blocks, else one byte per block.
+template <bool DUAL, int NW, int CB, bool VEC>
 __global__ __launch_bounds__(64 * NW) void k_skinny_mx(const GemmArgs p) {
   static_assert(!DUAL || CB == 2 || (CB == 1 && NW % 2 == 0), "an MX block of h is 32 columns");
   constexpr int NM = DUAL ? 2 : 1;          // weight matrices
@@ -377,47 +386,51 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_mx(const GemmArgs p) {
   const int K = p.K, N = p.N, KB = K / 128, K32 = K / 32;
   const int n0 = (nt * NW + wave) * 16 * CB;
 
-  // Per-lane stream bases: codes at the lane's 16-byte offset, scales at its
-  // 32-block within each 128-K block.
-  const uint8_t* b[NB];
-  const uint8_t* sb[NB];
+  // Per-lane stream bases: codes at the lane's 16-byte offset; scale rows.
+  const uint8_t* bp[NB];
+  const uint8_t* sbrow[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
     const size_t brow = (size_t)g * N + n0 + (j % CB) * 16 + r16;
-    b[j] = (j < CB ? p.B0 : p.B1) + brow * K + 16 * q4;
-    sb[j] = static_cast<const uint8_t*>(j < CB ? p.s_B0 : p.s_B1) + brow * K32 + q4;
+    bp[j] = (j < CB ? p.B0 : p.B1) + brow * K + 16 * q4;
+    sbrow[j] = static_cast<const uint8_t*>(j < CB ? p.s_B0 : p.s_B1) + brow * K32;
   }
   const bool aok = r16 < m;
   const int pr = row0 + (aok ? r16 : 0);
   const size_t arow_i = (size_t)(p.a_rows ? p.a_rows[pr] : pr);
   const uint8_t* arow = p.A + arow_i * K + 16 * q4;
-  const uint8_t* sarow = static_cast<const uint8_t*>(p.A_scale) + arow_i * K32 + q4;
+  const uint8_t* sarow = static_cast<const uint8_t*>(p.A_scale) + arow_i * K32;
 
   f32x4_t acc[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // Fills past the last block reload block KB - 1 (cache hits, never
-  // multiplied), which keeps the ring's loads unconditional.
-  MxSlot<NB> ring[U];
+  // Block kb's codes in (da, db); loads past the last block re-read it
+  // (cache hits, never multiplied), which keeps them unconditional.
+  i32x8_t da, db[NB], xa, xb[NB];
+  mx_load<NB>(da, db, 0, aok, arow, bp);
+  u32x4_t sv[NB + 1];
+  if constexpr (VEC) mx_load_scales<NB>(sv, 0, sarow, sbrow);
+  for (int kb = 0; kb < KB; ++kb) {
+    mx_load<NB>(xa, xb, min(kb + 1, KB - 1), aok, arow, bp);
+    uint32_t sa, sb[NB];
+    if constexpr (VEC) {
+      sa = byte_of(dword_of(sv[NB], kb & 3), q4);
 #pragma unroll
-  for (int u = 0; u < U; ++u) mx_fill<NB>(ring[u], min(u, KB - 1), aok, arow, sarow, b, sb);
-  int kb0 = 0;
-  for (; kb0 + U <= KB; kb0 += U) {
+      for (int j = 0; j < NB; ++j) sb[j] = byte_of(dword_of(sv[j], kb & 3), q4);
+    } else {
+      sa = sarow[4 * kb + q4];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-        acc[j] = mfma_mx8_16x16x128(ring[u].a, ring[u].b[j], acc[j], ring[u].sa, ring[u].s[j]);
-      mx_fill<NB>(ring[u], min(kb0 + u + U, KB - 1), aok, arow, sarow, b, sb);
+      for (int j = 0; j < NB; ++j) sb[j] = sbrow[j][4 * kb + q4];
     }
+    if (!aok) sa = 127u;                    // zero codes with scale 1
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[j] = mfma_mx8_16x16x128(da, db[j], acc[j], sa, sb[j]);
+    // the next 4 blocks' scale dwords, after the last use of these
+    if (VEC && (kb & 3) == 3) mx_load_scales<NB>(sv, min(kb + 1, KB - 4) / 4, sarow, sbrow);
+    da = xa;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) db[j] = xb[j];
   }
-#pragma unroll
-  for (int u = 0; u < U; ++u)   // the KB % U blocks left sit in slots 0 .. KB % U - 1
-    if (kb0 + u < KB) {
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-        acc[j] = mfma_mx8_16x16x128(ring[u].a, ring[u].b[j], acc[j], ring[u].sa, ring[u].s[j]);
-    }
 
   if constexpr (DUAL) {
     float hv[4][CB], am[4];
@@ -626,12 +639,19 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
 
   // gate/up + SwiGLU, then down, of the groups of at most kSkinnyMax rows
   if (f.mx) {
+    // 16-byte scale loads need 16-byte aligned scale rows (K % 512 == 0).
     up.n_ntile = f.I / (16 * SKINNY_MX_CB * SKINNY_MX_NW);
-    launch_gemm("skinny_gateup_mx", k_skinny_mx<true, SKINNY_MX_NW, SKINNY_MX_CB, SKINNY_MX_U>,
-                64 * SKINNY_MX_NW, band_grid(L.max_slices, up.n_ntile), up, s);
+    const long long gu = band_grid(L.max_slices, up.n_ntile);
+    if (f.H % 512 == 0)
+      launch_gemm("skinny_gateup_mx", k_skinny_mx<true, SKINNY_MX_NW, SKINNY_MX_CB, true>, 64 * SKINNY_MX_NW, gu, up, s);
+    else
+      launch_gemm("skinny_gateup_mx", k_skinny_mx<true, SKINNY_MX_NW, SKINNY_MX_CB, false>, 64 * SKINNY_MX_NW, gu, up, s);
     dn.n_ntile = f.H / (16 * SKINNY_MX_CBD * SKINNY_MX_NWD);
-    launch_gemm("skinny_down_mx", k_skinny_mx<false, SKINNY_MX_NWD, SKINNY_MX_CBD, SKINNY_MX_UD>,
-                64 * SKINNY_MX_NWD, band_grid(L.max_slices, dn.n_ntile), dn, s);
+    const long long gd = band_grid(L.max_slices, dn.n_ntile);
+    if (f.I % 512 == 0)
+      launch_gemm("skinny_down_mx", k_skinny_mx<false, SKINNY_MX_NWD, SKINNY_MX_CBD, true>, 64 * SKINNY_MX_NWD, gd, dn, s);
+    else
+      launch_gemm("skinny_down_mx", k_skinny_mx<false, SKINNY_MX_NWD, SKINNY_MX_CBD, false>, 64 * SKINNY_MX_NWD, gd, dn, s);
   } else if (f.fp8) {
     up.n_ntile = f.I / (16 * 8);
     launch_gemm("skinny_gateup_fp8", k_skinny_fp8<true, 8, 1>, 512, band_grid(L.max_slices, up.n_ntile), up, s);
