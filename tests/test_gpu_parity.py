@@ -107,6 +107,21 @@ def test_route_ragged_shapes(T, H, E, k, zipf):
     assert np.abs(w.cpu().numpy() - w_ref).max() <= 1e-6
 
 
+def test_route_max_hidden():
+    # H at the supported maximum: the router splits it into hundreds of slices.
+    cfg = MoeConfig("route_hmax", 12, T=3, H=131072, E=16, k=2, I=128)
+    li = generate_layer(cfg, DEV)
+    logits, idx, w = run_route(cfg, li)
+    inp = _route_inputs(li)
+    x = oracle.bf16_bits_to_f32(inp["x_bf16"])
+    ref = oracle.router_logits(x, inp["w_router"], None)
+    mag = np.abs(x) @ np.abs(inp["w_router"]).T
+    lg = logits.cpu().numpy()
+    assert np.all(np.abs(lg - ref) <= (cfg.H + 2) * 2.0 ** -24 * mag)
+    idx_ref, w_ref = oracle.topk_softmax(lg, cfg.k)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+
+
 def test_route_zero_router_weight_ties():
     cfg = MoeConfig("zero_router", 5, T=70, H=512, E=24, k=6, I=128)
     li = generate_layer(cfg, DEV)
@@ -414,6 +429,26 @@ SPLITK = [
 @pytest.mark.parametrize("cfg", SPLITK, ids=[c.name for c in SPLITK])
 def test_forward_split_k(cfg):
     _forward_check(cfg, generate_layer(cfg, DEV))
+
+
+# Extremes of the supported shapes: 65536 tokens (256 rank tiles, groups of
+# ~8k rows), K = 16384 for fp8 and MXFP8 (128 fp8 scale blocks per row),
+# E = 1024 experts with k = 16.
+EXTREMES = [
+    MoeConfig("x_t64k", 70, T=65536, H=128, E=64, k=8, I=128),
+    MoeConfig("x_h16k_fp8", 71, T=40, H=16384, E=4, k=2, I=256, n_shared=1, wdtype="fp8"),
+    MoeConfig("x_h16k_mx", 73, T=30, H=16384, E=3, k=2, I=128, wdtype="mxfp8"),
+    MoeConfig("x_e1024_k16", 72, T=300, H=256, E=1024, k=16, I=128),
+]
+
+
+@pytest.mark.parametrize("cfg", EXTREMES, ids=[c.name for c in EXTREMES])
+def test_forward_extremes(cfg):
+    sample = None
+    if cfg.T > 4096:
+        rng = np.random.default_rng(cfg.seed)
+        sample = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 30, replace=False)]))
+    _forward_check(cfg, generate_layer(cfg, DEV), sample)
 
 
 def test_shares_sum_to_the_layer_on_gpu():
