@@ -369,10 +369,14 @@ __device__ __forceinline__ uint32_t dword_of(const u32x4_t v, int i) {
   return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
 }
 
-// VEC: the scale rows are 16-byte aligned (K a multiple of 512): scales come
-// in one 16-byte load per row and 4 K blocks, else one byte per block.
-template <bool DUAL, int NW, int CB, bool VEC>
+// Scale modes (SM): 0 one byte per row and block; 1 (rows 16-byte aligned,
+// K a multiple of 512) one 16-byte load per row and 4 K blocks; 2 (also
+// K <= 8192) the workgroup copies the scale rows of its A and B rows into
+// LDS once (dynamic shared memory, rows padded by 16 bytes), so each scale
+// line is read from memory once per workgroup.
+template <bool DUAL, int NW, int CB, int SM>
 __global__ __launch_bounds__(64 * NW) void k_skinny_mx(const GemmArgs p) {
+  constexpr bool VEC = SM == 1;
   static_assert(!DUAL || CB == 2 || (CB == 1 && NW % 2 == 0), "an MX block of h is 32 columns");
   constexpr int NM = DUAL ? 2 : 1;          // weight matrices
   constexpr int NB = NM * CB;               // B streams per lane: [matrix][column block]
@@ -401,6 +405,30 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_mx(const GemmArgs p) {
   const uint8_t* arow = p.A + arow_i * K + 16 * q4;
   const uint8_t* sarow = static_cast<const uint8_t*>(p.A_scale) + arow_i * K32;
 
+  // SM 2: LDS rows 0 .. NW*NB*16-1 hold the B rows (wave, stream, row), then
+  // 16 A rows; row stride K32 + 16.
+  extern __shared__ __attribute__((aligned(16))) uint8_t mxs[];
+  const int RS = K32 + 16;
+  if constexpr (SM == 2) {
+    constexpr int BR = NW * NB * 16;
+    const int c16 = K32 / 16, total = (BR + 16) * c16;
+    for (int idx = threadIdx.x; idx < total; idx += 64 * NW) {
+      const int R = idx / c16, cc = idx % c16;
+      const uint8_t* src;
+      if (R < BR) {
+        const int w = R / (NB * 16), j = (R / 16) % NB, r = R % 16;
+        const size_t br = (size_t)g * N + (nt * NW + w) * 16 * CB + (j % CB) * 16 + r;
+        src = static_cast<const uint8_t*>(j < CB ? p.s_B0 : p.s_B1) + br * K32;
+      } else {
+        const int r = row0 + min(R - BR, m - 1);
+        src = static_cast<const uint8_t*>(p.A_scale) + (size_t)(p.a_rows ? p.a_rows[r] : r) * K32;
+      }
+      *reinterpret_cast<u32x4_t*>(mxs + R * RS + cc * 16) = *reinterpret_cast<const u32x4_t*>(src + cc * 16);
+    }
+    __syncthreads();
+  }
+  const uint8_t* lsa = mxs + (NW * NB * 16 + r16) * RS + q4;   // SM 2: this lane's A scale row
+
   f32x4_t acc[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -413,7 +441,11 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_mx(const GemmArgs p) {
   for (int kb = 0; kb < KB; ++kb) {
     mx_load<NB>(xa, xb, min(kb + 1, KB - 1), aok, arow, bp);
     uint32_t sa, sb[NB];
-    if constexpr (VEC) {
+    if constexpr (SM == 2) {
+      sa = lsa[4 * kb];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) sb[j] = mxs[((wave * NB + j) * 16 + r16) * RS + 4 * kb + q4];
+    } else if constexpr (VEC) {
       sa = byte_of(dword_of(sv[NB], kb & 3), q4);
 #pragma unroll
       for (int j = 0; j < NB; ++j) sb[j] = byte_of(dword_of(sv[j], kb & 3), q4);
@@ -578,6 +610,21 @@ static void launch_gemm(const char* name, Kern kern, int threads, long long bloc
   if (blocks > 0) MOE_LAUNCH(name, kern, dim3((unsigned)blocks), dim3(threads), 0, s, a);
 }
 
+template <bool DUAL, int NW, int CB>
+static void launch_skinny_mx(const char* name, long long blocks, const GemmArgs& a, hipStream_t s) {
+  if (blocks <= 0) return;
+  const int K32 = a.K / 32;
+  if (a.K % 512 == 0 && a.K <= 8192) {
+    constexpr int NB = (DUAL ? 2 : 1) * CB;
+    const size_t shm = (size_t)(NW * NB * 16 + 16) * (K32 + 16);
+    MOE_LAUNCH(name, (k_skinny_mx<DUAL, NW, CB, 2>), dim3((unsigned)blocks), dim3(64 * NW), shm, s, a);
+  } else if (a.K % 512 == 0) {
+    MOE_LAUNCH(name, (k_skinny_mx<DUAL, NW, CB, 1>), dim3((unsigned)blocks), dim3(64 * NW), 0, s, a);
+  } else {
+    MOE_LAUNCH(name, (k_skinny_mx<DUAL, NW, CB, 0>), dim3((unsigned)blocks), dim3(64 * NW), 0, s, a);
+  }
+}
+
 hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
   const WsLayout L = ffn_layout(f.T, f.H, f.E, f.k, f.I, f.n_shared, f.fp8, f.mx);
   uint8_t* ws = static_cast<uint8_t*>(f.workspace);
@@ -639,19 +686,11 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
 
   // gate/up + SwiGLU, then down, of the groups of at most kSkinnyMax rows
   if (f.mx) {
-    // 16-byte scale loads need 16-byte aligned scale rows (K % 512 == 0).
+    // Scale mode by K (16-byte scale loads need 16-byte aligned scale rows).
     up.n_ntile = f.I / (16 * SKINNY_MX_CB * SKINNY_MX_NW);
-    const long long gu = band_grid(L.max_slices, up.n_ntile);
-    if (f.H % 512 == 0)
-      launch_gemm("skinny_gateup_mx", k_skinny_mx<true, SKINNY_MX_NW, SKINNY_MX_CB, true>, 64 * SKINNY_MX_NW, gu, up, s);
-    else
-      launch_gemm("skinny_gateup_mx", k_skinny_mx<true, SKINNY_MX_NW, SKINNY_MX_CB, false>, 64 * SKINNY_MX_NW, gu, up, s);
     dn.n_ntile = f.H / (16 * SKINNY_MX_CBD * SKINNY_MX_NWD);
-    const long long gd = band_grid(L.max_slices, dn.n_ntile);
-    if (f.I % 512 == 0)
-      launch_gemm("skinny_down_mx", k_skinny_mx<false, SKINNY_MX_NWD, SKINNY_MX_CBD, true>, 64 * SKINNY_MX_NWD, gd, dn, s);
-    else
-      launch_gemm("skinny_down_mx", k_skinny_mx<false, SKINNY_MX_NWD, SKINNY_MX_CBD, false>, 64 * SKINNY_MX_NWD, gd, dn, s);
+    launch_skinny_mx<true, SKINNY_MX_NW, SKINNY_MX_CB>("skinny_gateup_mx", band_grid(L.max_slices, up.n_ntile), up, s);
+    launch_skinny_mx<false, SKINNY_MX_NWD, SKINNY_MX_CBD>("skinny_down_mx", band_grid(L.max_slices, dn.n_ntile), dn, s);
   } else if (f.fp8) {
     up.n_ntile = f.I / (16 * 8);
     launch_gemm("skinny_gateup_fp8", k_skinny_fp8<true, 8, 1>, 512, band_grid(L.max_slices, up.n_ntile), up, s);
