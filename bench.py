@@ -50,7 +50,8 @@ def stored_traffic(workload: str, kernel: str):
 
 
 def cpu_baseline(cfg, li, n_tokens):
-    """The oracle, as it stands, on the first n_tokens tokens of the same workload."""
+    """The oracle, as it stands, on the first n_tokens tokens of the same workload.
+    Returns the oracle's result and the timing record."""
     import numpy as np
     import oracle
     from synth import to_numpy_inputs
@@ -63,12 +64,41 @@ def cpu_baseline(cfg, li, n_tokens):
     n = min(n_tokens, cfg.T)
     inp["x_bf16"] = np.ascontiguousarray(inp["x_bf16"][:n])
     t0 = time.perf_counter()
-    oracle.forward(inp)
+    ref = oracle.forward(inp)
     dt = time.perf_counter() - t0
-    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return ref, {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"oracle.forward on the first {n} of {cfg.T} tokens of {cfg.name} "
                       f"(seed {cfg.seed}), {dt:.2f} s, fp32 NumPy, OpenBLAS threads={threads}, "
                       f"os.cpu_count()={os.cpu_count()}"}
+
+
+def routing_stats(counts):
+    """Load balance of the routed experts held here: how many got no row or one
+    row, the largest group, and the spread of group sizes (std / mean)."""
+    import numpy as np
+    c = np.asarray(counts, dtype=np.float64)
+    mean = c.mean() if c.size else 0.0
+    return {"empty_experts": int((c == 0).sum()), "one_row_experts": int((c == 1).sum()),
+            "max_group_rows": int(c.max()) if c.size else 0,
+            "load_std_over_mean": round(float(c.std() / mean), 4) if mean > 0 else None}
+
+
+def sampled_parity(out, idx, ref):
+    """The timed steps' output on the oracle's sample tokens against the oracle
+    (its own router logits, so a near-tie may pick another expert: such tokens
+    are counted, not compared)."""
+    import numpy as np
+    import torch
+    n = ref.out.shape[0]
+    u = out[:n].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    gpu = (u.astype(np.uint32) << 16).view(np.float32)
+    same = (idx[:n].cpu().numpy() == ref.topk_idx).all(axis=1)
+    if not same.any():
+        return {"tokens": n, "routing_differs": int(n), "max_token_rel_err": None}
+    num = np.abs(gpu - ref.out).max(axis=1)
+    den = np.maximum(np.abs(ref.out).max(axis=1), 1e-30)
+    return {"tokens": n, "routing_differs": int((~same).sum()),
+            "max_token_rel_err": float((num / den)[same].max())}
 
 
 CPU_TOKENS = {"tiny": 64, "qwen3_235b_decode": 64, "qwen3_235b_prefill": 256,
@@ -206,9 +236,10 @@ def main():
         torch.cuda.synchronize()
         graph = {"ms_per_step": g0.elapsed_time(g1) / args.steps}
 
-    cpu = None
+    cpu = parity = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, li, args.cpu_tokens or CPU_TOKENS.get(cfg.name, 64))
+        ref, cpu = cpu_baseline(cfg, li, args.cpu_tokens or CPU_TOKENS.get(cfg.name, 64))
+        parity = sampled_parity(out, idx, ref)
 
     res = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
@@ -218,8 +249,8 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k,
                    "I": cfg.I, "n_shared": cfg.n_shared, "weights": cfg.wdtype,
                    **({"expert_share": [cfg.e_first, cfg.e_first + cfg.E_loc]} if cfg.e_local else {}),
-                   "touched_experts": int(layer.groups), "max_group_rows": int(counts.max()),
-                   "empty_experts": int((counts[:cfg.E] == 0).sum())},
+                   "touched_experts": int(layer.groups),
+                   **routing_stats(counts[:cfg.E_loc])},
         "roofline": roof,
         "layer_roofline": layer_roof,
         "per_kernel_ms": {f"{i}:{n}": round(ms, 4) for i, (ms, n) in enumerate(launches)},
@@ -227,6 +258,7 @@ def main():
         "wall_s_timed_region": t_wall,
         "graph_replay": graph,
         "cpu_baseline": cpu,
+        "parity": parity,
     }
     print(json.dumps(res))
 
