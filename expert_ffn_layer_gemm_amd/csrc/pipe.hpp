@@ -51,4 +51,19 @@ __device__ __forceinline__ void dma16(const void* src, uint8_t* dst_block) {
   __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)dst_block, 16, 0, 0);
 }
 
+// The same 1 KB block (lane i copies 16 bytes from base + off_i), issued from
+// inline assembly.  The compiler's wait insertion then does not know of a
+// pending LDS write: with the builtin in flight it waits for EVERY
+// outstanding LDS read before the first use of any (the LDS counter then has
+// two kinds of events), which defeats reads interleaved with MFMAs.  Callers
+// order these loads against LDS reads themselves (wait_vmcnt_le + barrier).
+// base must be wave-uniform; M0 (the LDS address) is written here and is not
+// used by the compiler in kernels that issue no builtin direct-to-LDS loads.
+__device__ __forceinline__ void dma16_untracked(const uint8_t* base, uint32_t off,
+                                                uint8_t* dst_block) {
+  const uint32_t la = (uint32_t)(size_t)(lds_ptr_t)dst_block;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(la), "v"(off), "s"(base) : "memory", "m0");
+}
+
 }  // namespace moe

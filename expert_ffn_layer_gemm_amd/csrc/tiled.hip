@@ -18,10 +18,18 @@
 //     BM = 128, 64 x 64 per wave.
 //   - K is staged in 128-byte chunks (64 bf16 / 128 e4m3 per row) by
 //     direct-to-LDS loads (global_load_lds_dwordx4) into two rings: activation
-//     rows and weight rows.  bf16: 2 A stages + 3 B stages of 32 KB (all of
-//     LDS), so two weight chunks are in flight while one is multiplied; fp8:
-//     3 + 3 stages (16 KB + scales, 32 KB).  Measured: the weight stream,
-//     fetched from HBM by the first tile of a band, is the long-latency one.
+//     rows and weight rows.  bf16: 2 + 2 stages of 32 KB (one chunk in flight
+//     while one is multiplied; 2 + 3 or 3 + 2 stages measured no faster);
+//     fp8: 3 + 3 stages (16 KB + scales, 32 KB).
+//   - bf16 software pipeline: a wave reads the LDS fragments of the next K
+//     step while its MFMAs of the current one run (A row block i right after
+//     the row block's last MFMA), and the chunk barrier sits inside a chunk's
+//     second K step, after the wave's last read of the chunk and before its
+//     first read of the next.  The direct-to-LDS loads of this path are issued
+//     from inline assembly so the compiler keeps exact lgkm-counter waits for
+//     the interleaved reads (it cannot see a pending LDS write).  Measured
+//     7-12 % faster than reading a step's fragments then waiting, with
+//     bit-identical output (same MFMA order per accumulator).
 //   - A direct-to-LDS instruction writes 1 KB contiguously (lane i at +16 i),
 //     8 staged rows; each block of 8 rows lies in A, B0 or B1 and has its own
 //     wave-uniform base.  Each lane fetches global chunk c ^ (row & 7) of its
@@ -45,9 +53,8 @@ namespace moe {
 namespace {
 
 constexpr int kBRows = 256;                       // staged B rows per tile
-#ifndef TILED_BF16_RB
-#define TILED_BF16_RB 128
-#define TILED_BF16_NSA 2
+#ifndef TILED_BF16_NSA
+#define TILED_BF16_NSA 2                          // bf16 A / B ring stages
 #define TILED_BF16_NSB 2
 #endif
 constexpr int kMaxKB = 1024;                      // fp8: K <= 131072 (B scales kept in LDS)
@@ -70,6 +77,17 @@ __device__ __forceinline__ void dma_blocks(uint8_t* st, const uint8_t* const (&j
 #pragma unroll
   for (int j = 0; j < IPW; ++j)
     if (jv[j]) dma16(jb[j] + koff + soff[j], st + (wave * IPW + j) * 1024);
+}
+
+// The same blocks through dma16_untracked (the compiler does not see these
+// LDS writes; the caller orders them with vm-counter waits and barriers).
+template <int IPW>
+__device__ __forceinline__ void dma_blocks_untracked(uint8_t* st, const uint8_t* const (&jb)[IPW],
+                                                     const uint32_t (&soff)[IPW],
+                                                     const bool (&jv)[IPW], size_t koff, int wave) {
+#pragma unroll
+  for (int j = 0; j < IPW; ++j)
+    if (jv[j]) dma16_untracked(jb[j] + koff, soff[j], st + (wave * IPW + j) * 1024);
 }
 
 // Staged B row of 16-column block j (lane row r16) for wave column wn.
@@ -95,7 +113,8 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
   // come from HBM once per band; the activation tile is an L2 hit for all but
   // the first column tile).  The vm-counter waits below rely on NSB - NSA <= 1
   // and on A being issued before B in every step.
-  static_assert(NSA >= 2 && (NSB == NSA || NSB == NSA + 1), "ring depths");
+  static_assert(NSA >= 2 && NSB >= 2 && (NSB == NSA || NSB == NSA + 1 || (!FP8 && NSA == NSB + 1)),
+                "ring depths");
   constexpr int kRB = RB;                         // bytes of K per staged row and chunk
   constexpr int RPB = 1024 / RB;                  // staged rows per 1 KB DMA block
   constexpr int LPR = RB / 16;                    // lanes per staged row
@@ -215,68 +234,174 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Multiply one staged chunk.  bf16: all fragments of a K step are read from
-  // LDS before its MFMAs, so the LDS latency is paid once per step.
-  // Prologue: A chunks 0 .. NSA-2 and B chunks 0 .. NSB-2, A before B per chunk.
+  if constexpr (!FP8) {
+    // bf16: the software-pipelined main loop (file header).  Waves with a
+    // row block past the group's end take the plain loop below, with the
+    // same barriers and loads.
+    static_assert(RB == 128 && MB == 8, "bf16 pipeline layout");
+    // chunk c: A in stage c % NSA of the A ring, B in stage c % NSB of the B ring
+    auto sa = [&](int c) { return lds + (c % NSA) * A_STAGE; };
+    auto sb = [&](int c) { return lds + B_RING + (c % NSB) * B_STAGE; };
+    auto issue_a = [&](int c) { dma_blocks_untracked<IPWA>(sa(c), ab, aoff, av, (size_t)c * kRB, wave); };
+    auto issue_b = [&](int c) { dma_blocks_untracked<IPWB>(sb(c), bb, boff, bv, (size_t)c * kRB, wave); };
+    // Prologue: A chunks 0 .. NSA-1 and B chunks 0 .. NSB-1, A before B per chunk.
 #pragma unroll
-  for (int c = 0; c < NSB - 1; ++c) {
-    if (c < NSA - 1 && c < nk) {
-      dma_blocks<IPWA>(lds + c * A_STAGE, ab, aoff, av, (size_t)c * kRB, wave);
-      if constexpr (FP8)
-        __builtin_amdgcn_global_load_lds(ssrc + 4 * c, (lds_ptr_t)(lds + c * A_STAGE + A_BYTES + wave * 256), 4, 0, 0);
+    for (int c = 0; c < (NSA > NSB ? NSA : NSB); ++c) {
+      if (c < NSA && c < nk) issue_a(c);
+      if (c < NSB && c < nk) issue_b(c);
     }
-    if (c < nk) {
-      dma_blocks<IPWB>(lds + B_RING + c * B_STAGE, bb, boff, bv, (size_t)c * kRB, wave);
-      if (MX && wave < 4)
-        __builtin_amdgcn_global_load_lds(bssrc + 4 * c, (lds_ptr_t)(lds + B_RING + c * B_STAGE + B_BYTES + wave * 256), 4, 0, 0);
-    }
-  }
-  for (int kc = 0; kc < nk; ++kc) {
-    // A and B of chunk kc must have landed; the loads issued after them (A of
-    // chunks kc+1 .. kc+NSA-2, B of chunks kc+1 .. kc+NSB-2) may stay in flight.
-    wait_vmcnt_le<(NSA - 2) * (IPWA + 1) + (NSB - 2) * (IPWB + 1)>(
-        min(NSA - 2, nk - 1 - kc) * nva + max(0, min(NSB - 2, nk - 1 - kc)) * nvb);
-    lds_barrier();          // every wave's share, and every wave is done with chunk kc - 1
-    if (kc + NSA - 1 < nk) {   // into the A stage of chunk kc - 1
-      const int c = kc + NSA - 1;
-      dma_blocks<IPWA>(lds + (c % NSA) * A_STAGE, ab, aoff, av, (size_t)c * kRB, wave);
-      if constexpr (FP8)
-        __builtin_amdgcn_global_load_lds(ssrc + 4 * c, (lds_ptr_t)(lds + (c % NSA) * A_STAGE + A_BYTES + wave * 256), 4, 0, 0);
-    }
-    if (kc + NSB - 1 < nk) {   // into the B stage of chunk kc - 1
-      const int c = kc + NSB - 1;
-      dma_blocks<IPWB>(lds + B_RING + (c % NSB) * B_STAGE, bb, boff, bv, (size_t)c * kRB, wave);
-      if (MX && wave < 4)
-        __builtin_amdgcn_global_load_lds(bssrc + 4 * c, (lds_ptr_t)(lds + B_RING + (c % NSB) * B_STAGE + B_BYTES + wave * 256), 4, 0, 0);
-    }
-    if (!active) continue;
-    const uint8_t* As = lds + (kc % NSA) * A_STAGE;
-    const uint8_t* Bs = lds + B_RING + (kc % NSB) * B_STAGE;
-    // Row blocks past the group's end are neither read nor multiplied (fp8:
-    // measured 4-6 % faster on ~128-row groups split into two tiles).
-    if constexpr (!FP8) {
+    // Chunk c >= 1 is awaited at the boundary of chunk c - 1.  Loads complete
+    // in issue order, so the wave may leave in flight what it issued after the
+    // later of A(c), B(c): with NSB >= NSA that is A(c) (A(c+1 .. c+NSA-2) and
+    // B(c+1 .. c+NSB-2) follow it), with NSA = NSB + 1 it is B(c)
+    // (A(c+2 .. c+NSA-2) and B(c+1 .. c+NSB-2) follow it); chunks past the
+    // last are never issued.
+    constexpr int XA = NSA <= NSB ? NSA - 2 : NSA - 3;
+    constexpr int XB = NSB - 2;
+    auto wait_chunk = [&](int c) {   // A and B of chunk c landed (this wave's share)
+      const int xa = NSA <= NSB ? min(XA, nk - 1 - c) : min(XA, nk - 2 - c);
+      wait_vmcnt_le<XA * IPWA + XB * IPWB>(max(0, xa) * nva + max(0, min(XB, nk - 1 - c)) * IPWB);
+    };
+    // Chunk 0: the prologue issued A(1 .. NSA-1) and B(1 .. NSB-1) after it.
+    wait_vmcnt_le<(NSA - 1) * IPWA + (NSB - 1) * IPWB>(min(NSA - 1, nk - 1) * nva +
+                                                       min(NSB - 1, nk - 1) * IPWB);
+    lds_barrier();
+    const bool full = active && nmb == MB;
+    auto rd_b = [&](const uint8_t* st, int ks, u32x4_t (&b)[NB]) {
+      const int c = ks * 4 + (lane >> 4);
 #pragma unroll
-      for (int ks = 0; ks < RB / 64; ++ks) {
-        const int c = ks * 4 + (lane >> 4);
-        u32x4_t a[MB], b[NB];
+      for (int j = 0; j < NB; ++j) {
+        const int br = b_row<DUAL, WN, NB>(j, wn, r16);
+        b[j] = lds_read16(st + br * kRB + (slot<RB>(br, c) << 4));
+      }
+    };
+    auto rd_a = [&](const uint8_t* st, int ks, int i) {
+      const int c = ks * 4 + (lane >> 4);
+      const int r = rbase + i * 16 + r16;
+      return lds_read16(st + r * kRB + (slot<RB>(r, c) << 4));
+    };
+    auto boundary = [&](int kc) {   // after every wave's last read of chunk kc
+      if (kc + 1 < nk) wait_chunk(kc + 1);
+      lds_barrier();
+      if (kc + NSA < nk) issue_a(kc + NSA);
+      if (kc + NSB < nk) issue_b(kc + NSB);
+    };
+    if (full) {
+      u32x4_t a[MB], bc[NB], bn[NB];
+      rd_b(sb(0), 0, bc);
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          const int br = b_row<DUAL, WN, NB>(j, wn, r16);
-          b[j] = lds_read16(Bs + br * kRB + (slot<RB>(br, c) << 4));
-        }
+      for (int i = 0; i < MB; ++i) a[i] = rd_a(sa(0), 0, i);
+      // sched_barrier(0) keeps the compiler from regrouping the reads and
+      // MFMAs: each read is issued while the MFMA pipe works on the row block
+      // before it.
+      auto chunk = [&](int kc, auto last_c) {
+        constexpr bool last = decltype(last_c)::value;
+        const uint8_t* st = sa(kc);
+        const uint8_t* sn = sa(kc + 1);
+        const uint8_t* bt = sb(kc);
+        const uint8_t* bnx = sb(kc + 1);
+        // K step 0 of chunk kc; reads of step 1.
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
-          const int r = rbase + i * 16 + r16;
-          a[i] = lds_read16(As + r * kRB + (slot<RB>(r, c) << 4));
+#pragma unroll
+          for (int j = 0; j < NB; ++j) acc[i][j] = mfma_bf16_16x16x32(a[i], bc[j], acc[i][j]);
+          if (i < 2) {
+            const int c = 4 + (lane >> 4);
+#pragma unroll
+            for (int j = 2 * i; j < 2 * i + 2; ++j) {
+              const int br = b_row<DUAL, WN, NB>(j, wn, r16);
+              bn[j] = lds_read16(bt + br * kRB + (slot<RB>(br, c) << 4));
+            }
+          }
+          a[i] = rd_a(st, 1, i);
+          __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int i = 0; i < MB; ++i)
-          if (i < nmb) {
+        for (int j = 0; j < NB; ++j) bc[j] = bn[j];
+        // K step 1: first half, the chunk boundary, then the second half with
+        // the reads of the next chunk's step 0.
 #pragma unroll
-            for (int j = 0; j < NB; ++j) acc[i][j] = mfma_bf16_16x16x32(a[i], b[j], acc[i][j]);
-          }
-      }
+        for (int i = 0; i < MB / 2; ++i) {
+#pragma unroll
+          for (int j = 0; j < NB; ++j) acc[i][j] = mfma_bf16_16x16x32(a[i], bc[j], acc[i][j]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        boundary(kc);
+        if constexpr (!last) {
+          rd_b(bnx, 0, bn);
+#pragma unroll
+          for (int i = 0; i < MB / 2; ++i) a[i] = rd_a(sn, 0, i);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = MB / 2; i < MB; ++i) {
+#pragma unroll
+          for (int j = 0; j < NB; ++j) acc[i][j] = mfma_bf16_16x16x32(a[i], bc[j], acc[i][j]);
+          if constexpr (!last) a[i] = rd_a(sn, 0, i);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) bc[j] = bn[j];
+      };
+      for (int kc = 0; kc + 1 < nk; ++kc) chunk(kc, std::false_type{});
+      chunk(nk - 1, std::true_type{});
     } else {
+      for (int kc = 0; kc < nk; ++kc) {
+        if (active) {
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            u32x4_t b[NB], aa[MB];
+            rd_b(sb(kc), ks, b);
+#pragma unroll
+            for (int i = 0; i < MB; ++i) aa[i] = rd_a(sa(kc), ks, i);
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+              if (i < nmb) {
+#pragma unroll
+                for (int j = 0; j < NB; ++j) acc[i][j] = mfma_bf16_16x16x32(aa[i], b[j], acc[i][j]);
+              }
+          }
+        }
+        boundary(kc);
+      }
+    }
+  } else {
+    // fp8 / MXFP8 (memory-bound groups): one barrier per chunk at its start.
+    // Prologue: A chunks 0 .. NSA-2 and B chunks 0 .. NSB-2, A before B per chunk.
+#pragma unroll
+    for (int c = 0; c < NSB - 1; ++c) {
+      if (c < NSA - 1 && c < nk) {
+        dma_blocks<IPWA>(lds + c * A_STAGE, ab, aoff, av, (size_t)c * kRB, wave);
+        __builtin_amdgcn_global_load_lds(ssrc + 4 * c, (lds_ptr_t)(lds + c * A_STAGE + A_BYTES + wave * 256), 4, 0, 0);
+      }
+      if (c < nk) {
+        dma_blocks<IPWB>(lds + B_RING + c * B_STAGE, bb, boff, bv, (size_t)c * kRB, wave);
+        if (MX && wave < 4)
+          __builtin_amdgcn_global_load_lds(bssrc + 4 * c, (lds_ptr_t)(lds + B_RING + c * B_STAGE + B_BYTES + wave * 256), 4, 0, 0);
+      }
+    }
+    for (int kc = 0; kc < nk; ++kc) {
+      // A and B of chunk kc must have landed; the loads issued after them (A of
+      // chunks kc+1 .. kc+NSA-2, B of chunks kc+1 .. kc+NSB-2) may stay in flight.
+      wait_vmcnt_le<(NSA - 2) * (IPWA + 1) + (NSB - 2) * (IPWB + 1)>(
+          min(NSA - 2, nk - 1 - kc) * nva + max(0, min(NSB - 2, nk - 1 - kc)) * nvb);
+      lds_barrier();          // every wave's share, and every wave is done with chunk kc - 1
+      if (kc + NSA - 1 < nk) {   // into the A stage of chunk kc - 1
+        const int c = kc + NSA - 1;
+        dma_blocks<IPWA>(lds + (c % NSA) * A_STAGE, ab, aoff, av, (size_t)c * kRB, wave);
+        __builtin_amdgcn_global_load_lds(ssrc + 4 * c, (lds_ptr_t)(lds + (c % NSA) * A_STAGE + A_BYTES + wave * 256), 4, 0, 0);
+      }
+      if (kc + NSB - 1 < nk) {   // into the B stage of chunk kc - 1
+        const int c = kc + NSB - 1;
+        dma_blocks<IPWB>(lds + B_RING + (c % NSB) * B_STAGE, bb, boff, bv, (size_t)c * kRB, wave);
+        if (MX && wave < 4)
+          __builtin_amdgcn_global_load_lds(bssrc + 4 * c, (lds_ptr_t)(lds + B_RING + (c % NSB) * B_STAGE + B_BYTES + wave * 256), 4, 0, 0);
+      }
+      if (!active) continue;
+      const uint8_t* As = lds + (kc % NSA) * A_STAGE;
+      const uint8_t* Bs = lds + B_RING + (kc % NSB) * B_STAGE;
+      // Row blocks past the group's end are neither read nor multiplied
+      // (measured 4-6 % faster on ~128-row groups split into two tiles).
       // A lane's 32 codes: K positions 16*(lane/16) .. +16 and 64 + 16*(lane/16) .. +16
       // (the same positions for A and B, so the pairing inside the MFMA is right).
       const int c0 = lane >> 4, c1 = 4 + (lane >> 4);
@@ -463,15 +588,15 @@ hipError_t launch_tiled(const char* name, bool fp8, bool mx, bool dual, long lon
                         const GemmArgs& a, hipStream_t s) {
   if (blocks <= 0) return hipSuccess;
   const dim3 grid((unsigned)band_grid(blocks, 1));
-  // bf16 (compute-bound prefill groups): 256-row tiles, 2 stages.  fp8
+  // bf16 (compute-bound prefill groups): 256-row tiles, 2 + 2 stages.  fp8
   // (memory-bound ~128-row groups): 128-row tiles, 3 stages, two chunks in
   // flight.  The row counts match tile_rows() used by the schedule.
   if (mx && dual) MOE_LAUNCH(name, (k_tiled3<true, true, 2, 4, 128, 3, 3, 128, true>), grid, dim3(512), 0, s, a);
   else if (mx) MOE_LAUNCH(name, (k_tiled3<true, false, 2, 4, 128, 3, 3, 128, true>), grid, dim3(512), 0, s, a);
   else if (fp8 && dual) MOE_LAUNCH(name, (k_tiled3<true, true, 2, 4, 128, 3, 3, 128>), grid, dim3(512), 0, s, a);
   else if (fp8) MOE_LAUNCH(name, (k_tiled3<true, false, 2, 4, 128, 3, 3, 128>), grid, dim3(512), 0, s, a);
-  else if (dual) MOE_LAUNCH(name, (k_tiled3<false, true, 2, 4, 256, TILED_BF16_NSA, TILED_BF16_NSB, TILED_BF16_RB>), grid, dim3(512), 0, s, a);
-  else MOE_LAUNCH(name, (k_tiled3<false, false, 2, 4, 256, TILED_BF16_NSA, TILED_BF16_NSB, TILED_BF16_RB>), grid, dim3(512), 0, s, a);
+  else if (dual) MOE_LAUNCH(name, (k_tiled3<false, true, 2, 4, 256, TILED_BF16_NSA, TILED_BF16_NSB, 128>), grid, dim3(512), 0, s, a);
+  else MOE_LAUNCH(name, (k_tiled3<false, false, 2, 4, 256, TILED_BF16_NSA, TILED_BF16_NSB, 128>), grid, dim3(512), 0, s, a);
   return hipSuccess;
 }
 
