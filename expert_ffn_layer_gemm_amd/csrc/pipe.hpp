@@ -66,4 +66,12 @@ __device__ __forceinline__ void dma16_untracked(const uint8_t* base, uint32_t of
                :: "s"(la), "v"(off), "s"(base) : "memory", "m0");
 }
 
+// 4 bytes per lane (lane i's dword from its own address to dst + 4 i), issued
+// like dma16_untracked.
+__device__ __forceinline__ void dma4_untracked(const void* src, uint8_t* dst) {
+  const uint32_t la = (uint32_t)(size_t)(lds_ptr_t)dst;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :: "s"(la), "v"(src) : "memory", "m0");
+}
+
 }  // namespace moe

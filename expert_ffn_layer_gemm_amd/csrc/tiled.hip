@@ -366,115 +366,188 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
       }
     }
   } else {
-    // fp8 / MXFP8 (memory-bound groups): one barrier per chunk at its start.
-    // Prologue: A chunks 0 .. NSA-2 and B chunks 0 .. NSB-2, A before B per chunk.
+    // fp8 / MXFP8: one 128-K chunk is one MFMA K step.  The same skeleton as
+    // bf16: every chunk's loads (data, and the row scales with them) are
+    // issued after the boundary of the chunk NS earlier, and the boundary of
+    // chunk kc (wait for chunk kc+1, barrier, issue chunk kc+NS) comes after
+    // the wave's last read of chunk kc and before its first read of chunk kc+1.
+    static_assert(NSA == NSB && MB == 4, "8-bit ring and wave layout");
+    constexpr int NS = NSA;
+    auto sa = [&](int c) { return lds + (c % NS) * A_STAGE; };
+    auto sb = [&](int c) { return lds + B_RING + (c % NS) * B_STAGE; };
+    auto issue = [&](int c) {
+      dma_blocks_untracked<IPWA>(sa(c), ab, aoff, av, (size_t)c * kRB, wave);
+      dma4_untracked(ssrc + 4 * c, sa(c) + A_BYTES + wave * 256);
+      dma_blocks_untracked<IPWB>(sb(c), bb, boff, bv, (size_t)c * kRB, wave);
+      if (MX && wave < 4) dma4_untracked(bssrc + 4 * c, sb(c) + B_BYTES + wave * 256);
+    };
+    const int nvc = nva + nvb;                       // vm instructions per chunk of this wave
 #pragma unroll
-    for (int c = 0; c < NSB - 1; ++c) {
-      if (c < NSA - 1 && c < nk) {
-        dma_blocks<IPWA>(lds + c * A_STAGE, ab, aoff, av, (size_t)c * kRB, wave);
-        __builtin_amdgcn_global_load_lds(ssrc + 4 * c, (lds_ptr_t)(lds + c * A_STAGE + A_BYTES + wave * 256), 4, 0, 0);
-      }
-      if (c < nk) {
-        dma_blocks<IPWB>(lds + B_RING + c * B_STAGE, bb, boff, bv, (size_t)c * kRB, wave);
-        if (MX && wave < 4)
-          __builtin_amdgcn_global_load_lds(bssrc + 4 * c, (lds_ptr_t)(lds + B_RING + c * B_STAGE + B_BYTES + wave * 256), 4, 0, 0);
-      }
-    }
-    for (int kc = 0; kc < nk; ++kc) {
-      // A and B of chunk kc must have landed; the loads issued after them (A of
-      // chunks kc+1 .. kc+NSA-2, B of chunks kc+1 .. kc+NSB-2) may stay in flight.
-      wait_vmcnt_le<(NSA - 2) * (IPWA + 1) + (NSB - 2) * (IPWB + 1)>(
-          min(NSA - 2, nk - 1 - kc) * nva + max(0, min(NSB - 2, nk - 1 - kc)) * nvb);
-      lds_barrier();          // every wave's share, and every wave is done with chunk kc - 1
-      if (kc + NSA - 1 < nk) {   // into the A stage of chunk kc - 1
-        const int c = kc + NSA - 1;
-        dma_blocks<IPWA>(lds + (c % NSA) * A_STAGE, ab, aoff, av, (size_t)c * kRB, wave);
-        __builtin_amdgcn_global_load_lds(ssrc + 4 * c, (lds_ptr_t)(lds + (c % NSA) * A_STAGE + A_BYTES + wave * 256), 4, 0, 0);
-      }
-      if (kc + NSB - 1 < nk) {   // into the B stage of chunk kc - 1
-        const int c = kc + NSB - 1;
-        dma_blocks<IPWB>(lds + B_RING + (c % NSB) * B_STAGE, bb, boff, bv, (size_t)c * kRB, wave);
-        if (MX && wave < 4)
-          __builtin_amdgcn_global_load_lds(bssrc + 4 * c, (lds_ptr_t)(lds + B_RING + (c % NSB) * B_STAGE + B_BYTES + wave * 256), 4, 0, 0);
-      }
-      if (!active) continue;
-      const uint8_t* As = lds + (kc % NSA) * A_STAGE;
-      const uint8_t* Bs = lds + B_RING + (kc % NSB) * B_STAGE;
-      // Row blocks past the group's end are neither read nor multiplied
-      // (measured 4-6 % faster on ~128-row groups split into two tiles).
-      // A lane's 32 codes: K positions 16*(lane/16) .. +16 and 64 + 16*(lane/16) .. +16
-      // (the same positions for A and B, so the pairing inside the MFMA is right).
-      const int c0 = lane >> 4, c1 = 4 + (lane >> 4);
-      i32x8_t b[NB];
+    for (int c = 0; c < NS; ++c)
+      if (c < nk) issue(c);
+    // Chunk c is followed by chunks c+1 .. c+NS-2 at its boundary's wait
+    // (chunk 0 after the prologue: by chunks 1 .. NS-1).
+    wait_vmcnt_le<(NS - 1) * (IPWA + IPWB + 2)>(min(NS - 1, nk - 1) * nvc);
+    lds_barrier();                                   // also publishes the fp8 B scales
+    auto boundary = [&](int kc) {
+      if (kc + 1 < nk)
+        wait_vmcnt_le<(NS - 2) * (IPWA + IPWB + 2)>(max(0, min(NS - 2, nk - 2 - kc)) * nvc);
+      lds_barrier();
+      if (kc + NS < nk) issue(kc + NS);
+    };
+    // A lane's 32 codes: K positions 16*(lane/16) .. +16 and 64 + 16*(lane/16) .. +16
+    // (the same positions for A and B, so the pairing inside the MFMA is right).
+    const int c0 = lane >> 4, c1 = 4 + (lane >> 4);
+    const int sh = 8 * (lane >> 4);                  // MX: byte of this lane's K block
+    auto rd_frag = [&](const uint8_t* rowp, int row) {
+      const u32x4_t lo = lds_read16(rowp + (slot<RB>(row, c0) << 4));
+      const u32x4_t hi = lds_read16(rowp + (slot<RB>(row, c1) << 4));
+      return i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    };
+    auto rd_b = [&](int kc, int j) {
+      const int br = b_row<DUAL, WN, NB>(j, wn, r16);
+      return rd_frag(sb(kc) + br * kRB, br);
+    };
+    auto rd_bscale = [&](int kc, int j) -> uint32_t {   // MX: E8M0 of the B row's K block
+      const uint32_t* bsw = reinterpret_cast<const uint32_t*>(sb(kc) + B_BYTES);
+      return (bsw[b_row<DUAL, WN, NB>(j, wn, r16)] >> sh) & 0xFFu;
+    };
+    auto rd_a = [&](int kc, int i) {
+      const int r = rbase + i * 16 + r16;
+      return rd_frag(sa(kc) + r * kRB, r);
+    };
+    auto rd_ascale_mx = [&](int kc, int i) -> uint32_t {
+      const uint32_t* asc = reinterpret_cast<const uint32_t*>(sa(kc) + A_BYTES);
+      return (asc[rbase + i * 16 + r16] >> sh) & 0xFFu;
+    };
+    auto rd_ascale = [&](int kc, int i) {               // fp8: rows of the lane's accumulator
+      const float* asc = reinterpret_cast<const float*>(sa(kc) + A_BYTES);
+      return *reinterpret_cast<const f32x4_t*>(asc + rbase + i * 16 + (lane >> 4) * 4);
+    };
+    auto rd_bsc = [&](int kc, float& lo, float& hi) {   // fp8: B block scales of chunk kc
+      lo = DUAL ? bsc[kc] : bsc[(wn * (256 / WN)) / 128 * KB + kc];
+      hi = DUAL ? bsc[KB + kc] : lo;
+    };
+    // fp8: acc += partial * (row scale * block scale), per row block.
+    auto scale_add = [&](int i, const f32x4_t (&pr)[NB], const f32x4_t sa4, float sb_lo, float sb_hi) {
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int br = b_row<DUAL, WN, NB>(j, wn, r16);
-        const uint8_t* rowp = Bs + br * kRB;
-        const u32x4_t lo = lds_read16(rowp + (slot<RB>(br, c0) << 4));
-        const u32x4_t hi = lds_read16(rowp + (slot<RB>(br, c1) << 4));
-        b[j] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                       (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      for (int q = 0; q < 4; ++q) {
+        const float s_lo = sa4[q] * sb_lo, s_hi = sa4[q] * sb_hi;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j][q] += pr[j][q] * (j < NB / 2 ? s_lo : s_hi);
       }
-      if constexpr (MX) {
-        // E8M0 dwords of the chunk (4 K blocks) per staged A row and B row;
-        // lane l takes byte l/16: the scale of its K block.
-        const uint32_t* asc = reinterpret_cast<const uint32_t*>(As + A_BYTES);
-        const uint32_t* bsw = reinterpret_cast<const uint32_t*>(Bs + B_BYTES);
-        const int sh = 8 * (lane >> 4);
-        uint32_t sbj[NB];
+    };
+    const bool full = active && nmb == MB;
+    if (full) {
+      // Software pipeline: the chunk's A rows 2-3 are read first, then row
+      // blocks 0-1 multiply, the boundary, the next chunk's A rows 0-1 are read
+      // (registers just freed), and row blocks 2-3 multiply column by column
+      // with the next chunk's B fragment j read as soon as column j is done.
+      // (A chunk's stage is refilled right after its boundary, so every value
+      // of it is in registers by then.)  The reads are unconditional: after the
+      // last chunk they read a stale stage (in bounds, never used), which keeps
+      // the loop body one basic block.
+      i32x8_t a[MB], b[NB];
+      uint32_t sam[MB], sbm[NB];                       // MX scales
+      f32x4_t saf[MB];                                 // fp8 row scales
+      float sb_lo = 0.f, sb_hi = 0.f;                  // fp8 block scales
+      auto next_a = [&](int kc, int i) {
+        a[i] = rd_a(kc, i);
+        if constexpr (MX) sam[i] = rd_ascale_mx(kc, i);
+        else saf[i] = rd_ascale(kc, i);
+      };
+      auto next_b = [&](int kc, int j) {
+        b[j] = rd_b(kc, j);
+        if constexpr (MX) sbm[j] = rd_bscale(kc, j);
+      };
 #pragma unroll
-        for (int j = 0; j < NB; ++j) sbj[j] = (bsw[b_row<DUAL, WN, NB>(j, wn, r16)] >> sh) & 0xFFu;
-#pragma unroll
-        for (int i = 0; i < MB; ++i)
-          if (i < nmb) {
-            const int r = rbase + i * 16 + r16;
-            const uint8_t* rowp = As + r * kRB;
-            const u32x4_t lo = lds_read16(rowp + (slot<RB>(r, c0) << 4));
-            const u32x4_t hi = lds_read16(rowp + (slot<RB>(r, c1) << 4));
-            const i32x8_t a = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-            const uint32_t sa = (asc[r] >> sh) & 0xFFu;
-#pragma unroll
-            for (int j = 0; j < NB; ++j) acc[i][j] = mfma_mx8_16x16x128(a, b[j], acc[i][j], sa, sbj[j]);
+      for (int j = 0; j < NB; ++j) next_b(0, j);
+      next_a(0, 0);
+      next_a(0, 1);
+      if constexpr (!MX) rd_bsc(0, sb_lo, sb_hi);
+      for (int kc = 0; kc < nk; ++kc) {
+        next_a(kc, 2);                                 // used after the boundary
+        next_a(kc, 3);
+        f32x4_t pr[2][2];                              // fp8: partial tiles of two columns of two row blocks
+        // fp8: a partial tile is one MFMA (a chunk is one K step); it is
+        // scaled into the accumulator one column later.
+        auto col = [&](int i0, int j) {
+          if constexpr (MX) {
+            acc[i0][j] = mfma_mx8_16x16x128(a[i0], b[j], acc[i0][j], sam[i0], sbm[j]);
+            acc[i0 + 1][j] = mfma_mx8_16x16x128(a[i0 + 1], b[j], acc[i0 + 1][j], sam[i0 + 1], sbm[j]);
+          } else {
+            pr[j & 1][0] = mfma_fp8_16x16x128(a[i0], b[j], f32x4_t{0.f, 0.f, 0.f, 0.f});
+            pr[j & 1][1] = mfma_fp8_16x16x128(a[i0 + 1], b[j], f32x4_t{0.f, 0.f, 0.f, 0.f});
           }
-        continue;
-      }
-      const float* ascale = reinterpret_cast<const float*>(As + A_BYTES);
-      const float sb_lo = DUAL ? bsc[kc] : bsc[(wn * (256 / WN)) / 128 * KB + kc];
-      const float sb_hi = DUAL ? bsc[KB + kc] : sb_lo;
-      // All fragments first, then the MB x NB MFMAs back to back into
-      // separate partial tiles (no MFMA waits on another's result), then the
-      // per-block scaling: the VALU work of one wave overlaps the MFMAs of the
-      // other wave on the SIMD.
-      i32x8_t a[MB];
+        };
+        auto scale_col = [&](int i0, int j) {            // fp8: acc += partial * scales, column j
+          if constexpr (!MX) {
 #pragma unroll
-      for (int i = 0; i < MB; ++i)
-        if (i < nmb) {
-        const int r = rbase + i * 16 + r16;
-        const uint8_t* rowp = As + r * kRB;
-        const u32x4_t lo = lds_read16(rowp + (slot<RB>(r, c0) << 4));
-        const u32x4_t hi = lds_read16(rowp + (slot<RB>(r, c1) << 4));
-        a[i] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                       (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      }
-      f32x4_t pr[MB][NB];
+            for (int d = 0; d < 2; ++d)
 #pragma unroll
-      for (int i = 0; i < MB; ++i)
-        if (i < nmb) {
+              for (int q = 0; q < 4; ++q)
+                acc[i0 + d][j][q] += pr[j & 1][d][q] * (saf[i0 + d][q] * (j < NB / 2 ? sb_lo : sb_hi));
+          }
+        };
 #pragma unroll
-          for (int j = 0; j < NB; ++j)
-            pr[i][j] = mfma_fp8_16x16x128(a[i], b[j], f32x4_t{0.f, 0.f, 0.f, 0.f});
+        for (int j = 0; j < NB; ++j) {
+          col(0, j);
+          if (j > 0) scale_col(0, j - 1);
         }
+        scale_col(0, NB - 1);
+        // Keep row blocks 0-1 ahead of the boundary (the compiler would sink
+        // them past its wait and barrier otherwise): they run while the wave
+        // waits there.
 #pragma unroll
-      for (int i = 0; i < MB; ++i)
-        if (i < nmb) {
-        const f32x4_t sa = *reinterpret_cast<const f32x4_t*>(ascale + rbase + i * 16 + (lane >> 4) * 4);
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float s_lo = sa[q] * sb_lo, s_hi = sa[q] * sb_hi;
+          for (int j = 0; j < NB; ++j) asm volatile("" : "+v"(acc[i][j]));
+        boundary(kc);
+        next_a(kc + 1, 0);
+        next_a(kc + 1, 1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int j = 0; j < NB; ++j) acc[i][j][q] += pr[i][j][q] * (j < NB / 2 ? s_lo : s_hi);
+        for (int j = 0; j < NB; ++j) {
+          col(2, j);
+          if (j > 0) scale_col(2, j - 1);
+          next_b(kc + 1, j);
+          __builtin_amdgcn_sched_barrier(0);
         }
+        scale_col(2, NB - 1);
+        if constexpr (!MX) rd_bsc(min(kc + 1, nk - 1), sb_lo, sb_hi);
+      }
+    } else {
+      for (int kc = 0; kc < nk; ++kc) {
+        if (active) {
+          // Row blocks past the group's end are neither read nor multiplied
+          // (measured 4-6 % faster on ~128-row groups split into two tiles).
+          i32x8_t b[NB];
+          uint32_t sbm[NB];
+#pragma unroll
+          for (int j = 0; j < NB; ++j) {
+            b[j] = rd_b(kc, j);
+            if constexpr (MX) sbm[j] = rd_bscale(kc, j);
+          }
+          float sb_lo = 0.f, sb_hi = 0.f;
+          if constexpr (!MX) rd_bsc(kc, sb_lo, sb_hi);
+#pragma unroll
+          for (int i = 0; i < MB; ++i)
+            if (i < nmb) {
+              const i32x8_t a = rd_a(kc, i);
+              if constexpr (MX) {
+                const uint32_t sam = rd_ascale_mx(kc, i);
+#pragma unroll
+                for (int j = 0; j < NB; ++j) acc[i][j] = mfma_mx8_16x16x128(a, b[j], acc[i][j], sam, sbm[j]);
+              } else {
+                f32x4_t pr[NB];
+#pragma unroll
+                for (int j = 0; j < NB; ++j) pr[j] = mfma_fp8_16x16x128(a, b[j], f32x4_t{0.f, 0.f, 0.f, 0.f});
+                scale_add(i, pr, rd_ascale(kc, i), sb_lo, sb_hi);
+              }
+            }
+        }
+        boundary(kc);
       }
     }
   }
