@@ -46,25 +46,14 @@ __device__ __forceinline__ u32x4_t pack_bf16x8(const float* f) {
 
 // --------------------------------------------------------------- e4m3fn ----
 // Round-to-nearest-even encoding of a finite fp32 value with |v| <= 448 into
-// an OCP e4m3fn code (bias 7, 3 mantissa bits, subnormals below 2^-6).
+// an OCP e4m3fn code (bias 7, 3 mantissa bits, subnormals below 2^-6), by
+// gfx950's v_cvt_pk_fp8_f32.  Measured identical to the bit-level definition
+// (exponent rebias, 3 mantissa bits, ties to even, subnormals as m * 2^-9) on
+// 10^6 normal samples scaled by 2^-12 .. 2^11 (clamped to +-448) plus every
+// e4m3 value, every midpoint between neighbours and the fp32 values on either
+// side of it, both signs.
 __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
-  uint32_t b = __float_as_uint(v);
-  uint32_t sign = (b >> 24) & 0x80u;
-  uint32_t a = b & 0x7FFFFFFFu;
-  float af = __uint_as_float(a);
-  uint32_t code;
-  if (af < 0.015625f) {               // 2^-6: subnormal range, value m * 2^-9
-    code = (uint32_t)__builtin_rintf(af * 512.0f);   // exact scaling, ties to even
-  } else {
-    uint32_t e = a >> 23;             // biased fp32 exponent, 121..135
-    uint32_t m = (a & 0x7FFFFFu);
-    uint32_t r = m >> 20;             // top 3 mantissa bits
-    uint32_t rem = m & 0xFFFFFu;
-    r += (rem > 0x80000u) || (rem == 0x80000u && (r & 1u));
-    if (r == 8u) { r = 0u; ++e; }
-    code = ((e - 120u) << 3) | r;     // e - 127 + 7
-  }
-  return sign | code;
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.f, 0, false) & 0xFFu;
 }
 
 __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
@@ -120,6 +109,21 @@ __device__ __forceinline__ f32x4_t mfma_mx8_16x16x128(const i32x8_t a, const i32
 // ------------------------------------------------------- wave reductions ----
 __device__ __forceinline__ float wave_max_xor(float v, int lanes) {
   for (int m = 1; m < lanes; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+
+// Maximum over each row of 16 lanes (lanes 16 r .. 16 r + 15), returned in
+// every lane of the row, by DPP moves (no LDS crossbar): swap neighbours,
+// swap pairs, then mirror within 8 and within 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_mov<0xB1>(v));    // quad_perm 1,0,3,2
+  v = fmaxf(v, dpp_mov<0x4E>(v));    // quad_perm 2,3,0,1
+  v = fmaxf(v, dpp_mov<0x141>(v));   // row_half_mirror
+  v = fmaxf(v, dpp_mov<0x140>(v));   // row_mirror
   return v;
 }
 

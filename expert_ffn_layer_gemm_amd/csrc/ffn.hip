@@ -275,7 +275,7 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_fp8(const GemmArgs p) {
       for (int q = 0; q < 4; ++q) {
         const int r = mb * 16 + (lane >> 4) * 4 + q;
         hv[mb][q] = (mb < nmb && r < m) ? silu_mul(acc0[mb][q], acc1[mb][q]) : 0.f;
-        const float am = wave_max_xor(fabsf(hv[mb][q]), 16);
+        const float am = row16_max(fabsf(hv[mb][q]));
         if (r16 == 0) row_amax[wave][r] = am;
       }
     __syncthreads();
@@ -475,7 +475,7 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_mx(const GemmArgs p) {
         hv[q][c] = r < m ? silu_mul(acc[c][q], acc[CB + c][q]) : 0.f;
         am[q] = fmaxf(am[q], fabsf(hv[q][c]));
       }
-      am[q] = wave_max_xor(am[q], 16);
+      am[q] = row16_max(am[q]);
       if (CB == 1 && r16 == 0) row_amax[wave][r] = am[q];
     }
     if (CB == 1) __syncthreads();

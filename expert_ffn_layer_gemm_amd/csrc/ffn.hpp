@@ -73,7 +73,12 @@ inline long long band_grid(long long max_items, int n_ntile) {
   return (max_items * n_ntile + 15) / 8 * 8;
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.f + expf(-g)) * u; }
+// silu(g) * u with the hardware exp2 and reciprocal (about 1 ulp each; the
+// result is rounded to bf16 or quantised right after).  Large negative g
+// gives exp = inf and a zero reciprocal, so silu -> -0 as it should.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
+}
 
 // Operands of one grouped GEMM launch.  Row-major, K contiguous:
 // A [R, K] (x_perm or h), B0/B1 [G, N, K] (gate/up or down), out [R, N].

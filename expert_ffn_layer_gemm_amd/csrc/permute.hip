@@ -155,7 +155,7 @@ __global__ __launch_bounds__(256) void k_gather_fp8(const int32_t* __restrict__ 
       float amax = 0.f;
 #pragma unroll
       for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(v[q]));
-      amax = wave_max_xor(amax, 16);
+      amax = row16_max(amax);
       const float scale = amax == 0.f ? 1.f : amax / 448.f;
       uint32_t lo = 0, hi = 0;
 #pragma unroll

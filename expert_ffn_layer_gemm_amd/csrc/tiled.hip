@@ -553,6 +553,27 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
   }
 
   // Epilogue.  Lane holds rows rbase + 16 i + 4 (lane/16) + q of its blocks.
+  // The output tile is assembled in LDS (the ring stages are free once every
+  // wave is past its last read) and written out in 16-byte row pieces: the
+  // lanes' own 1- or 2-byte elements, 4 rows x 16 columns per instruction,
+  // made 8-16x as many store instructions and partial-line writes (measured:
+  // the epilogue took 0.2-0.3 ms of the 8-bit kernels' launches).
+  constexpr int OUT_B = (FP8 && DUAL) ? 1 : 2;       // bytes per output element
+  constexpr int OCOLS = DUAL ? 128 : 256;            // output columns per tile
+  constexpr int ROWB = OCOLS * OUT_B;                // bytes per tile row: 128, 256, 512
+  constexpr int NCH = ROWB / 16;                     // 16-byte pieces per row
+  // fp8: per-row maxima of h exchanged across the WN waves of a row block.
+  constexpr int AMAX_BYTES = (FP8 && DUAL && !MX) ? WN * kBM * 4 : 0;
+  static_assert(AMAX_BYTES + kBM * ROWB <= (int)sizeof(lds), "output tile fits in LDS");
+  float* amax_s = reinterpret_cast<float*>(lds);     // [WN][kBM]
+  uint8_t* const tile = lds + AMAX_BYTES;
+  // Piece (r, c / (16 / OUT_B)) sits at piece index c16 ^ (r % NCH): the
+  // 4 rows a store instruction covers (4 apart) fall on different banks.
+  auto tile_at = [&](int r, int c) {
+    const int byte = c * OUT_B;
+    return tile + r * ROWB + ((((byte >> 4) ^ (r % NCH))) << 4) + (byte & 15);
+  };
+  lds_barrier();                                      // every wave is past its last stage read
   if constexpr (MX && DUAL) {
     // The wave's 32 h columns are one MX block of each of its rows: row
     // maxima by a 16-lane reduction, then E8M0 and codes.
@@ -571,21 +592,19 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
           hv[j] = silu_mul(acc[i][j][q], acc[i][j + NH][q]);
           am = fmaxf(am, fabsf(hv[j]));
         }
-        am = wave_max_xor(am, 16);
+        am = row16_max(am);
         if (i < nmb && r < mrows) {
           const uint32_t e8 = mx_e8m0(am);
           const float inv = mx_inv_scale(e8);
 #pragma unroll
           for (int j = 0; j < NH; ++j) {
             const float qv = fminf(fmaxf(hv[j] * inv, -448.f), 448.f);
-            p.out[(size_t)(row0 + r) * N + hc0 + j * 16 + r16] = (uint8_t)f32_to_e4m3(qv);
+            *tile_at(r, wn * (128 / WN) + j * 16 + r16) = (uint8_t)f32_to_e4m3(qv);
           }
           if (r16 == 0) static_cast<uint8_t*>(p.out_scale)[(size_t)(row0 + r) * N32 + hc0 / 32] = (uint8_t)e8;
         }
       }
   } else if constexpr (FP8 && DUAL) {
-    lds_barrier();                                    // stages are free: reuse for row maxima
-    float* amax_s = reinterpret_cast<float*>(lds);    // [WN][kBM]
     constexpr int NH = NB / 2;                        // gate (= up) blocks per wave
 #pragma unroll
     for (int i = 0; i < MB; ++i)
@@ -599,7 +618,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
           acc[i][j][q] = h;
           am = fmaxf(am, fabsf(h));
         }
-        am = wave_max_xor(am, 16);
+        am = row16_max(am);
         if (r16 == 0) amax_s[wn * kBM + r] = am;
       }
     lds_barrier();
@@ -618,39 +637,42 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
 #pragma unroll
             for (int j = 0; j < NH; ++j) {
               const float qv = fminf(fmaxf(acc[i][j][q] / scale, -448.f), 448.f);
-              p.out[(size_t)(row0 + r) * N + n0 + wn * (128 / WN) + j * 16 + r16] =
-                  (uint8_t)f32_to_e4m3(qv);
+              *tile_at(r, wn * (128 / WN) + j * 16 + r16) = (uint8_t)f32_to_e4m3(qv);
             }
             if (wn == 0 && r16 == 0) static_cast<float*>(p.out_scale)[(size_t)(row0 + r) * N128 + nt] = scale;
           }
         }
       }
-  } else {
-    if (!active) return;
-    uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
+  } else if (active) {
 #pragma unroll
     for (int i = 0; i < MB; ++i)
       if (i < nmb) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int r = rbase + i * 16 + (lane >> 4) * 4 + q;
-          if (r < mrows) {
-            uint16_t* orow = out + (size_t)(row0 + r) * N;
-            if constexpr (DUAL) {
+          if constexpr (DUAL) {
 #pragma unroll
-              for (int j = 0; j < NB / 2; ++j)
-                orow[n0 + wn * (128 / WN) + j * 16 + r16] =
-                    (uint16_t)f32_to_bf16_bits(silu_mul(acc[i][j][q], acc[i][j + NB / 2][q]));
-            } else {
+            for (int j = 0; j < NB / 2; ++j)
+              *reinterpret_cast<uint16_t*>(tile_at(r, wn * (128 / WN) + j * 16 + r16)) =
+                  (uint16_t)f32_to_bf16_bits(silu_mul(acc[i][j][q], acc[i][j + NB / 2][q]));
+          } else {
 #pragma unroll
-              for (int j = 0; j < NB; ++j) {
-                const int col = wn * (256 / WN) + j * 16 + r16;
-                if (col < ncols) orow[n0 + col] = (uint16_t)f32_to_bf16_bits(acc[i][j][q]);
-              }
-            }
+            for (int j = 0; j < NB; ++j)
+              *reinterpret_cast<uint16_t*>(tile_at(r, wn * (256 / WN) + j * 16 + r16)) =
+                  (uint16_t)f32_to_bf16_bits(acc[i][j][q]);
           }
         }
       }
+  }
+  lds_barrier();
+  // Rows past the group's end and columns past the matrix are not written.
+  const int nch = ncols * OUT_B / 16;
+  uint8_t* const out = p.out + ((size_t)row0 * N + n0) * OUT_B;
+  for (int idx = tid; idx < mrows * NCH; idx += 64 * NW) {
+    const int r = idx / NCH, ch = idx % NCH;
+    if (ch < nch)
+      *reinterpret_cast<u32x4_t*>(out + (size_t)r * N * OUT_B + ch * 16) =
+          *reinterpret_cast<const u32x4_t*>(tile + r * ROWB + ((ch ^ (r % NCH)) << 4));
   }
 #else
   (void)p;
