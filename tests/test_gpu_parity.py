@@ -364,7 +364,8 @@ def test_forward_deterministic(ci):
 # T <= 256 with E <= 256 runs routing and dispatch in one workgroup; the
 # T256/T257 pair straddles that boundary.
 @pytest.mark.parametrize("case", ["T1", "T3_ragged", "E1k1", "kE", "one_hot_expert", "fp8_small",
-                                  "T256_E256", "T257", "k16", "mx_small", "mx_hot"])
+                                  "T256_E256", "T257", "k16", "mx_small", "mx_hot", "hot_ragged_n",
+                                  "fp8_hot_ragged_n"])
 def test_forward_edge_cases(case):
     cfgs = {
         "T1": MoeConfig("T1", 30, T=1, H=256, E=8, k=2, I=256),
@@ -378,10 +379,14 @@ def test_forward_edge_cases(case):
         "k16": MoeConfig("k16", 38, T=100, H=256, E=64, k=16, I=128),
         "mx_small": MoeConfig("mx", 39, T=77, H=512, E=12, k=3, I=256, n_shared=1, wdtype="mxfp8"),
         "mx_hot": MoeConfig("mxhot", 40, T=300, H=384, E=8, k=1, I=384, wdtype="mxfp8"),
+        # one 600-row group through the tiled kernels with H = 384: the down
+        # GEMM's second column tile holds 128 of its 256 columns
+        "hot_ragged_n": MoeConfig("hotrn", 41, T=600, H=384, E=8, k=1, I=256),
+        "fp8_hot_ragged_n": MoeConfig("f8hotrn", 42, T=600, H=384, E=8, k=1, I=256, wdtype="fp8"),
     }
     cfg = cfgs[case]
     li = generate_layer(cfg, DEV)
-    if case in ("one_hot_expert", "mx_hot"):
+    if case in ("one_hot_expert", "mx_hot", "hot_ragged_n", "fp8_hot_ragged_n"):
         li.router_bias = torch.zeros(cfg.E, dtype=torch.float32, device=DEV)
         li.router_bias[3] = 100.0          # every token -> expert 3: 300 rows, ragged tiles
     _forward_check(cfg, li)
