@@ -195,7 +195,7 @@ def main():
     dtype = cfg.wdtype if cfg.wdtype in ("fp8", "mxfp8") else "bf16"
     kern_s = float(np.mean(kern_ms)) / 1e3
     if dom_name.startswith(("skinny_", "tiled_")):
-        work = acc.kernel_work(dom_name, counts, cfg.H, cfg.I, cfg.wdtype)
+        work = acc.kernel_work(dom_name, counts, cfg.H, cfg.I, cfg.wdtype, acc.skinny_max_rows(cfg.T))
     else:
         work = None
     roof = acc.roofline(work, kern_s, dtype) if work else None
@@ -207,7 +207,7 @@ def main():
     kernel_roofs = {}
     for i, (ms, n) in enumerate(launches):
         if n.startswith(("skinny_", "tiled_")):
-            wk = acc.kernel_work(n, counts, cfg.H, cfg.I, cfg.wdtype)
+            wk = acc.kernel_work(n, counts, cfg.H, cfg.I, cfg.wdtype, acc.skinny_max_rows(cfg.T))
             if wk.groups:
                 rf = acc.roofline(wk, ms / 1e3, dtype)
                 kernel_roofs[f"{i}:{n}"] = {"ms": round(ms, 4), "groups": wk.groups,

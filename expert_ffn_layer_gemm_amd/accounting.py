@@ -20,10 +20,15 @@ import numpy as np
 PEAK_HBM_GBS = 8000.0
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp8": 5000.0, "fp32": 157.3}
 
-# Split of the grouped-FFN schedule, the same threshold as the C++ schedule
-# (csrc/ffn.hpp kSkinnyMax): groups of up to 64 rows go to the weight-streaming
-# kernels, larger ones to the tiled kernels.
+# Split of the grouped-FFN schedule, the same rule as the C++ schedule
+# (csrc/ffn.hpp skinny_max_rows): groups of up to 64 rows go to the
+# weight-streaming kernels when T <= 64 (no group can be larger), else groups of
+# up to 48 rows; larger groups go to the tiled kernels.
 SKINNY_MAX_ROWS = 64
+
+
+def skinny_max_rows(T: int) -> int:
+    return SKINNY_MAX_ROWS if T <= SKINNY_MAX_ROWS else 48
 
 
 def tokens_per_expert(T: int, k: int, E: int) -> float:
@@ -81,20 +86,22 @@ def _weight_scale_bytes(g: int, n: int, k: int, wdtype: str) -> float:
     return _scale_bytes(g * n, k, wdtype)
 
 
-def kernel_groups(kernel: str, counts: np.ndarray) -> np.ndarray:
+def kernel_groups(kernel: str, counts: np.ndarray, skinny_max: int = SKINNY_MAX_ROWS) -> np.ndarray:
     """Group sizes a grouped-FFN launch processes, from its name."""
     m = np.asarray(counts, dtype=np.int64)
     m = m[m > 0]
     if kernel.startswith("skinny_"):
-        return m[m <= SKINNY_MAX_ROWS]
+        return m[m <= skinny_max]
     if kernel.startswith("tiled_"):
-        return m[m > SKINNY_MAX_ROWS]
+        return m[m > skinny_max]
     raise ValueError(f"not a grouped-FFN kernel: {kernel}")
 
 
-def kernel_work(kernel: str, counts: np.ndarray, H: int, I: int, wdtype: str) -> Work:
-    """Algorithmic bytes and FLOPs of one launch of a grouped-FFN kernel."""
-    m = kernel_groups(kernel, counts).astype(np.float64)
+def kernel_work(kernel: str, counts: np.ndarray, H: int, I: int, wdtype: str,
+                skinny_max: int = SKINNY_MAX_ROWS) -> Work:
+    """Algorithmic bytes and FLOPs of one launch of a grouped-FFN kernel
+    (skinny_max: the schedule's split, skinny_max_rows(T))."""
+    m = kernel_groups(kernel, counts, skinny_max).astype(np.float64)
     e = _elt(wdtype)
     rows = float(m.sum())
     g = len(m)

@@ -120,7 +120,7 @@ __device__ __forceinline__ void scan_groups(const int* cnt, int G, int32_t* coun
 }
 
 // Work lists of the grouped FFN from the group offsets (1024-thread
-// workgroup, G <= 2048): groups of 1 .. kSkinnyMax rows as 16-row slices,
+// workgroup, G <= 2048): groups of 1 .. sc.skinny_max rows as 16-row slices,
 // larger groups as equal-height row tiles in bands of kTileBand.
 __device__ __forceinline__ void plan_groups(const int32_t* offsets, const Sched& sc,
                                             int* wave_sum) {
@@ -130,8 +130,8 @@ __device__ __forceinline__ void plan_groups(const int32_t* offsets, const Sched&
   for (int q = 0; q < 2; ++q) {
     const int g = 2 * tid + q;
     m[q] = g < G ? offsets[g + 1] - offsets[g] : 0;
-    sl[q] = m[q] > 0 && m[q] <= kSkinnyMax ? ceil_div(m[q], kSliceRows) : 0;
-    nt[q] = m[q] > kSkinnyMax ? ceil_div(m[q], group_tile_rows(m[q], sc.tile_rows)) : 0;
+    sl[q] = m[q] > 0 && m[q] <= sc.skinny_max ? ceil_div(m[q], kSliceRows) : 0;
+    nt[q] = m[q] > sc.skinny_max ? ceil_div(m[q], group_tile_rows(m[q], sc.tile_rows)) : 0;
   }
   int sl_pos, sl_total;
   block_scan_pair(sl[0], sl[1], wave_sum, sl_pos, sl_total);

@@ -15,7 +15,7 @@
 // sections: kernels read the routed token counts on the device instead of
 // sizing work from the buffer's upper bound).  One small kernel reads
 // `offsets` and writes two work lists into the workspace:
-//   - skinny list: groups with 1..kSkinnyMax rows.  Decode-sized groups are
+//   - skinny list: groups with 1..skinny_max_rows(T) rows.  Decode-sized groups are
 //     bound by streaming their weights from HBM; the skinny kernel keeps the
 //     few activation rows in registers (straight from L2) and streams each
 //     weight byte exactly once, 16 bytes per lane, with the next K block's
@@ -537,7 +537,7 @@ WsLayout ffn_layout(int T, int H, int E, int k, int I, int n_shared, bool fp8, b
   WsLayout L{};
   const long long R = (long long)T * (k + n_shared);
   const int G = E + n_shared;
-  const long long big_groups = std::min<long long>(G, R / (kSkinnyMax + 1));
+  const long long big_groups = std::min<long long>(G, R / (skinny_max_rows(T) + 1));
   L.max_tiles = (int)(R / tile_rows(fp8) + big_groups + 1);
   size_t off = 0;
   L.h = off;        off += align256((size_t)R * I * (fp8 ? 1 : 2));
@@ -569,7 +569,7 @@ Sched ffn_schedule(const FfnArgs& f) {
   uint8_t* ws = static_cast<uint8_t*>(f.workspace);
   return Sched{reinterpret_cast<int32_t*>(ws + L.n_skinny), reinterpret_cast<int32_t*>(ws + L.n_tiles),
                reinterpret_cast<int32_t*>(ws + L.skinny), reinterpret_cast<int32_t*>(ws + L.tiles),
-               f.E + f.n_shared, tile_rows(f.fp8)};
+               f.E + f.n_shared, tile_rows(f.fp8), skinny_max_rows(f.T)};
 }
 
 size_t ffn_workspace_bytes(int T, int H, int E, int k, int I, int n_shared, bool fp8, bool mx) {
@@ -577,7 +577,7 @@ size_t ffn_workspace_bytes(int T, int H, int E, int k, int I, int n_shared, bool
 }
 
 // A second stream per host thread and device, with a fork and a join event:
-// the tiled kernels (groups > kSkinnyMax rows) and the weight-streaming
+// the tiled kernels (groups > skinny_max_rows(T) rows) and the weight-streaming
 // kernels (the other groups) touch disjoint groups, and each down GEMM needs
 // only the gate/up rows of its own groups, so the two chains run concurrently.
 // Created on first use with default priority and kept for the life of the
@@ -662,8 +662,8 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
   dn.K = f.I;
   dn.N = f.H;
 
-  // No group above kSkinnyMax rows: no tiled work, skip its launches (decode).
-  const bool tiled = f.max_group_rows > kSkinnyMax;
+  // No group above the skinny limit: no tiled work, skip its launches (decode).
+  const bool tiled = f.max_group_rows > skinny_max_rows(f.T);
   SideStream* side = tiled && !prof_serial() ? side_stream() : nullptr;
   hipStream_t ts = s;                // stream of the tiled chain
   if (side) {                        // fork after the plan
@@ -684,7 +684,7 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
   if (tiled)
     launch_tiled(nm_td, f.fp8, f.mx, false, (long long)L.max_tiles * dn.n_ntile, dn, ts);
 
-  // gate/up + SwiGLU, then down, of the groups of at most kSkinnyMax rows
+  // gate/up + SwiGLU, then down, of the groups of at most skinny_max_rows(T) rows
   if (f.mx) {
     // Scale mode by K (16-byte scale loads need 16-byte aligned scale rows).
     up.n_ntile = f.I / (16 * SKINNY_MX_CB * SKINNY_MX_NW);

@@ -55,6 +55,17 @@ def test_kernel_work_by_hand():
         acc.kernel_work("combine", counts, H, I, "bf16")
 
 
+def test_skinny_split_follows_the_batch():
+    # T <= 64: no group can exceed 64 rows, all of them stream; larger batches
+    # send groups above 48 rows to the tiled kernels
+    assert acc.skinny_max_rows(1) == acc.skinny_max_rows(64) == 64
+    assert acc.skinny_max_rows(65) == acc.skinny_max_rows(8192) == 48
+    counts = np.array([48, 49, 64, 3])
+    assert list(acc.kernel_groups("skinny_down_bf16", counts, acc.skinny_max_rows(1000))) == [48, 3]
+    assert list(acc.kernel_groups("tiled_down_bf16", counts, acc.skinny_max_rows(1000))) == [49, 64]
+    assert list(acc.kernel_groups("skinny_down_bf16", counts, acc.skinny_max_rows(64))) == [48, 49, 64, 3]
+
+
 def test_layer_work_by_hand():
     T, H, E, k, I = 10, 256, 4, 2, 128
     counts = np.array([7, 0, 13, 0, 10])            # routed (7+13 = 20 = T*k), then a shared expert

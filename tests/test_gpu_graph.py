@@ -40,11 +40,11 @@ def _eager(sh, li, x, cfg):
 
 CASES = [
     config_by_name("qwen3_235b_decode"),
-    # small shapes that still reach the tiled kernels (groups > 64 rows) and
+    # small shapes that still reach the tiled kernels (groups > 48 rows) and
     # the fp8 path with a shared expert
     MoeConfig("graph_bf16", 21, T=640, H=512, E=8, k=2, I=256),
     MoeConfig("graph_fp8", 22, T=384, H=512, E=16, k=4, I=256, n_shared=1, wdtype="fp8"),
-    # skewed routing: groups on both sides of 64 rows, so the tiled chain runs
+    # skewed routing: groups on both sides of 48 rows, so the tiled chain runs
     # on the library's second stream, forked and joined inside the capture
     MoeConfig("graph_mixed", 23, T=512, H=512, E=64, k=4, I=256, zipf_s=1.1),
     MoeConfig("graph_mxfp8", 24, T=384, H=512, E=16, k=4, I=256, n_shared=1, wdtype="mxfp8"),

@@ -226,8 +226,9 @@ def _ffn_case(cfg, sizes, seed):
 
 @pytest.mark.parametrize("wdtype", ["bf16", "fp8", "mxfp8"])
 def test_grouped_ffn_group_size_boundaries(wdtype):
-    # sizes straddle the skinny row classes (16/32/64) and the 128-row tiles
-    sizes = [0, 1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 0, 200, 257, 3]
+    # sizes straddle the 16-row slices, the split between the streaming and
+    # the tiled kernels (48 rows at this batch size) and the 128-row tiles
+    sizes = [0, 1, 15, 16, 17, 31, 32, 33, 47, 48, 49, 63, 64, 65, 127, 128, 129, 0, 200, 257, 3]
     E = len(sizes)
     cfg = MoeConfig("ffn_" + wdtype, 21, T=sum(sizes), H=384, E=E, k=1, I=256, wdtype=wdtype)
     y, ref = _ffn_case(cfg, sizes, 1)
