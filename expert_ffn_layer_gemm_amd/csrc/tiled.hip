@@ -69,18 +69,9 @@ __device__ __forceinline__ int slot(int r, int c) {
 }
 
 // Direct-to-LDS loads of this wave's IPW 1 KB blocks of one K chunk into a
-// ring stage (wave-uniform base + 32-bit lane offset per block).
-template <int IPW>
-__device__ __forceinline__ void dma_blocks(uint8_t* st, const uint8_t* const (&jb)[IPW],
-                                           const uint32_t (&soff)[IPW], const bool (&jv)[IPW],
-                                           size_t koff, int wave) {
-#pragma unroll
-  for (int j = 0; j < IPW; ++j)
-    if (jv[j]) dma16(jb[j] + koff + soff[j], st + (wave * IPW + j) * 1024);
-}
-
-// The same blocks through dma16_untracked (the compiler does not see these
-// LDS writes; the caller orders them with vm-counter waits and barriers).
+// ring stage (wave-uniform base + 32-bit lane offset per block), through
+// dma16_untracked: the compiler does not see these LDS writes, and the caller
+// orders them with vm-counter waits and barriers.
 template <int IPW>
 __device__ __forceinline__ void dma_blocks_untracked(uint8_t* st, const uint8_t* const (&jb)[IPW],
                                                      const uint32_t (&soff)[IPW],
@@ -109,10 +100,8 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
   static_assert(RB == 128 || (RB == 64 && !FP8), "fp8 MFMA K step needs 128-byte rows");
   static_assert(!MX || FP8, "MX operands are 8-bit");
   // A (activation rows) and B (weight rows) have rings of their own: NSA and
-  // NSB stages.  NSB = NSA + 1 keeps one more weight chunk in flight (weights
-  // come from HBM once per band; the activation tile is an L2 hit for all but
-  // the first column tile).  The vm-counter waits below rely on NSB - NSA <= 1
-  // and on A being issued before B in every step.
+  // NSB stages (bf16 2 + 2, 8-bit 3 + 3).  Each path's vm-counter waits follow
+  // from its issue order: at every chunk boundary A is issued before B.
   static_assert(NSA >= 2 && NSB >= 2 && (NSB == NSA || NSB == NSA + 1 || (!FP8 && NSA == NSB + 1)),
                 "ring depths");
   constexpr int kRB = RB;                         // bytes of K per staged row and chunk
