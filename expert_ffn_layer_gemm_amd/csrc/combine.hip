@@ -30,14 +30,29 @@ __global__ __launch_bounds__(TPB) void k_combine(const uint16_t* __restrict__ y_
     float acc[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[q] = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const float w = topk_w[(size_t)t * k + j];
-      const int row = dest[(size_t)t * k + j];
-      if (row < 0) continue;                 // held by another share: adds nothing
-      float v[8];
-      unpack_bf16x8(reinterpret_cast<const u32x4_t*>(y_perm + (size_t)row * H)[c], v);
+    // Slots in groups of 4: the group's row loads are issued before its
+    // adds, which still run in slot order.
+    for (int j0 = 0; j0 < k; j0 += 4) {
+      u32x4_t raw[4];
+      float w[4];
+      bool ok[4];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = acc[q] + w * v[q];
+      for (int u = 0; u < 4; ++u) {
+        const int j = j0 + u;
+        const int row = j < k ? dest[(size_t)t * k + j] : -1;
+        ok[u] = row >= 0;                      // row < 0: held by another share, adds nothing
+        w[u] = ok[u] ? topk_w[(size_t)t * k + j] : 0.f;
+        raw[u] = ok[u] ? reinterpret_cast<const u32x4_t*>(y_perm + (size_t)row * H)[c]
+                       : u32x4_t{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (ok[u]) {
+          float v[8];
+          unpack_bf16x8(raw[u], v);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc[q] = acc[q] + w[u] * v[q];
+        }
     }
     if (n_shared) {
       float v[8];
