@@ -72,6 +72,28 @@ def cpu_baseline(cfg, li, n_tokens):
                       f"os.cpu_count()={os.cpu_count()}"}
 
 
+def device_info(dev):
+    """The GPU the run used (name, compute units, memory) and a plain 1 GiB
+    device-to-device copy's rate, as context for the HBM fractions."""
+    import torch
+    pr = torch.cuda.get_device_properties(dev)
+    a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 5 * 2 * (1 << 30) / (e0.elapsed_time(e1) / 1e3) / 1e9   # read + write bytes
+    del a, b
+    torch.cuda.empty_cache()
+    return {"name": pr.name, "gcn_arch": getattr(pr, "gcnArchName", None),
+            "compute_units": pr.multi_processor_count, "hbm_gib": round(pr.total_memory / 2 ** 30, 1),
+            "copy_1gib_gbs": round(gbs, 1)}
+
+
 def routing_stats(counts):
     """Load balance of the routed experts held here: how many got no row or one
     row, the largest group, and the spread of group sizes (std / mean)."""
@@ -188,6 +210,20 @@ def main():
     ms_per_step = total_ms / args.steps
     value = cfg.T * args.steps / (total_ms / 1e3)
 
+    # After the timed region: the spread of single steps (an event pair
+    # around each of K more steps), and the machine it ran on.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    one = np.array([a.elapsed_time(b) for a, b in evs])
+    spread = {"median_ms": float(np.median(one)), "p90_ms": float(np.percentile(one, 90)),
+              "min_ms": float(one.min()), "steps": int(len(one))}
+    device = device_info(dev)
+
     counts = np.bincount(idx.cpu().numpy().ravel(), minlength=cfg.E)
     counts = counts[cfg.e_first:cfg.e_first + cfg.E_loc]      # the experts held here
     if cfg.n_shared:
@@ -256,6 +292,8 @@ def main():
         "per_kernel_ms": {f"{i}:{n}": round(ms, 4) for i, (ms, n) in enumerate(launches)},
         "grouped_ffn_rooflines": kernel_roofs,
         "wall_s_timed_region": t_wall,
+        "single_steps": spread,
+        "device": device,
         "graph_replay": graph,
         "cpu_baseline": cpu,
         "parity": parity,
