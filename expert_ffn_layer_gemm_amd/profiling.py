@@ -4,13 +4,19 @@
     python -m expert_ffn_layer_gemm_amd.profiling traffic --workload W --bench-kernel NAME \
         --rocprof-kernel SUBSTR --fetch CSV --write CSV --fetch-copy CSV --write-copy CSV \
         --copy-bytes N --cmd-fetch "..." --cmd-write "..." --cmd-copy "..."
+    python -m expert_ffn_layer_gemm_amd.profiling busy --workload W --bench-kernel NAME \
+        --rocprof-kernel SUBSTR --counters CSV --trace CSV --mfma-flop F --peak-tflops P --cmd "..."
 
 `trace` keeps the rows of this library's kernels from a --kernel-trace --stats
 summary.  `traffic` turns two --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per
 dispatch) into HBM bytes per launch of one kernel, each counter scaled by what
 it reads for a plain device copy of known size, and writes
 profiles/traffic_<workload>.json (read by bench.py, tagged with the kernel
-source hash so stale numbers are ignored) plus a text summary.
+source hash so stale numbers are ignored) plus a text summary.  `busy` turns
+one --kernel-trace --pmc run (GRBM_GUI_ACTIVE, SQ_BUSY_CYCLES,
+SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_MFMA) into the kernel's clock (GPU-active
+cycles per XCD over its duration), the fraction of SIMD cycles the matrix
+cores were busy, and the MFMA rate its instruction count implies.
 """
 import argparse
 import collections
@@ -88,6 +94,41 @@ def traffic_summary(a) -> None:
         f"{(fetch_b + write_b) / 1e9:.4f} GB\n")
 
 
+XCDS, SIMDS = 8, 1024          # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
+
+
+def busy_summary(a) -> None:
+    ctr = collections.defaultdict(lambda: collections.defaultdict(float))
+    disp = collections.defaultdict(set)
+    for r in _rows(a.counters):
+        if a.rocprof_kernel in r["Kernel_Name"]:
+            ctr[r["Kernel_Name"]][r["Counter_Name"]] += float(r["Counter_Value"])
+            disp[r["Kernel_Name"]].add(r["Dispatch_Id"])
+    if len(ctr) != 1:
+        raise SystemExit(f"kernel substring {a.rocprof_kernel!r} matches {list(ctr)}")
+    name = next(iter(ctr))
+    nd = len(disp[name])
+    c = {k: v / nd for k, v in ctr[name].items()}          # per dispatch
+    durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in _rows(a.trace)
+            if r["Kernel_Name"] == name]
+    dur_ns = sum(durs) / len(durs)
+    gui = c["GRBM_GUI_ACTIVE"] / XCDS                        # GPU-active cycles of one XCD
+    clock_ghz = gui / dur_ns
+    busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMDS * gui)
+    tflops = c["SQ_INSTS_MFMA"] * a.mfma_flop / (dur_ns * 1e-9) / 1e12
+    txt = os.path.join(ROOT, "profiles", f"{a.bench_kernel}_{a.workload}_mfma_busy.txt")
+    open(txt, "w").write(
+        f"# MFMA activity of {name} on {a.workload} (rocprofv3 --kernel-trace --pmc, one run)\n"
+        f"# command: {a.cmd}\n"
+        f"dispatches: {nd}; average duration {dur_ns / 1e3:.1f} us\n"
+        f"GRBM_GUI_ACTIVE per XCD {gui:.4g} cycles -> clock {clock_ghz:.3f} GHz\n"
+        f"SQ_VALU_MFMA_BUSY_CYCLES {c['SQ_VALU_MFMA_BUSY_CYCLES']:.4g} -> matrix cores busy "
+        f"{100 * busy:.1f} % of SIMD cycles\n"
+        f"SQ_INSTS_MFMA {c['SQ_INSTS_MFMA']:.4g} x {a.mfma_flop:.0f} FLOP -> {tflops:.1f} TFLOP/s, "
+        f"{100 * tflops / a.peak_tflops:.1f} % of the {a.peak_tflops:.0f} TFLOP/s nominal peak\n"
+        f"SQ_BUSY_CYCLES {c['SQ_BUSY_CYCLES']:.4g}\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd_name", required=True)
@@ -100,9 +141,16 @@ def main():
               "write-copy", "cmd-fetch", "cmd-write", "cmd-copy"):
         r.add_argument("--" + n, required=True)
     r.add_argument("--copy-bytes", type=int, required=True)
+    b = sub.add_parser("busy")
+    for n in ("workload", "bench-kernel", "rocprof-kernel", "counters", "trace", "cmd"):
+        b.add_argument("--" + n, required=True)
+    b.add_argument("--mfma-flop", type=float, required=True)
+    b.add_argument("--peak-tflops", type=float, required=True)
     a = ap.parse_args()
     if a.cmd_name == "trace":
         trace_summary(a.stats_csv, a.out_txt, a.cmd)
+    elif a.cmd_name == "busy":
+        busy_summary(a)
     else:
         traffic_summary(a)
 
