@@ -366,7 +366,7 @@ def test_forward_deterministic(ci):
 # T256/T257 pair straddles that boundary.
 @pytest.mark.parametrize("case", ["T1", "T3_ragged", "E1k1", "kE", "one_hot_expert", "fp8_small",
                                   "T256_E256", "T257", "k16", "mx_small", "mx_hot", "hot_ragged_n",
-                                  "fp8_hot_ragged_n"])
+                                  "fp8_hot_ragged_n", "fp8_k512", "fp8_k512_ragged_n"])
 def test_forward_edge_cases(case):
     cfgs = {
         "T1": MoeConfig("T1", 30, T=1, H=256, E=8, k=2, I=256),
@@ -384,6 +384,12 @@ def test_forward_edge_cases(case):
         # GEMM's second column tile holds 128 of its 256 columns
         "hot_ragged_n": MoeConfig("hotrn", 41, T=600, H=384, E=8, k=1, I=256),
         "fp8_hot_ragged_n": MoeConfig("f8hotrn", 42, T=600, H=384, E=8, k=1, I=256, wdtype="fp8"),
+        # K a multiple of 512 in both GEMMs (the fp8 kernel with register-staged
+        # weights): ~150-row groups split into two tiles, a 600-row shared
+        # expert; then H = 640, whose down GEMM has a 128-column last tile.
+        "fp8_k512": MoeConfig("f8k512", 43, T=600, H=1024, E=8, k=2, I=512, n_shared=1, wdtype="fp8"),
+        "fp8_k512_ragged_n": MoeConfig("f8k512rn", 44, T=600, H=640, E=8, k=2, I=512, n_shared=1,
+                                       wdtype="fp8"),
     }
     cfg = cfgs[case]
     li = generate_layer(cfg, DEV)
