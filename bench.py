@@ -15,6 +15,7 @@ during the timed steps.
 """
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -26,14 +27,22 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/sec on 1 MI355X + % of HBM / MFMA roofline"
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and with whitespace runs collapsed."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_hash() -> str:
-    """Hash of the kernel sources, to tell whether stored counter data is stale."""
+    """Hash of the kernel sources' code (comments and layout ignored), to tell
+    whether stored counter data is stale."""
     csrc = os.path.join(ROOT, "expert_ffn_layer_gemm_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".hpp")):
             h.update(f.encode())
-            h.update(open(os.path.join(csrc, f), "rb").read())
+            h.update(_code_only(open(os.path.join(csrc, f), encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -1,6 +1,7 @@
-// LDS-pipelined tiled grouped GEMM for groups with more than 64 rows
-// (prefill-sized groups, the shared expert, the hot experts of a skewed
-// routing).  Computes, per (group, row tile, column tile):
+// LDS-pipelined tiled grouped GEMM for the groups too large for the
+// weight-streaming kernels, more than 48 rows in batches of more than 64
+// tokens (prefill-sized groups, the shared expert, the hot experts of a
+// skewed routing).  Computes, per (group, row tile, column tile):
 //   DUAL:   h = silu(X W_gate^T) * (X W_up^T)    128 h columns (256 B rows)
 //   single: y = h W_down^T                        256 output columns
 // with fp32 accumulation; fp8 layers apply the per-row activation scale and

@@ -45,7 +45,13 @@
  *     1 <= e_local and 0 <= e_first <= E - e_local.
  *     T == 0 is a valid no-op.  Other shapes return MOE_ERR_UNSUPPORTED.
  *   - The library keeps no state between calls; calls on different streams
- *     with disjoint buffers may run concurrently.
+ *     with disjoint buffers may run concurrently.  Its only persistent
+ *     objects are host-side: moe_grouped_ffn and moe_forward fork the tiled
+ *     kernels of large groups onto a second stream of their own (one per
+ *     host thread and device, default priority, created on first use and
+ *     kept for the life of the process) and join it back into `stream`
+ *     with events before returning, so the work stays ordered on `stream`
+ *     and can be captured into a HIP graph.
  */
 #ifndef MOE_H_
 #define MOE_H_
@@ -254,9 +260,9 @@ int moe_forward(const moe_shape* shape, const void* x, const float* w_router,
  * entry-point calls made on this thread record a pair of HIP events on their
  * stream around kernel launches:
  *   mode 1: around every launch, in launch order, up to `capacity` pairs;
- *           the grouped FFN's two kernel chains (groups above and below 64
- *           rows) then run one after the other on the caller's stream, so
- *           each launch is timed alone;
+ *           the grouped FFN's two kernel chains (tiled groups and
+ *           weight-streaming groups) then run one after the other on the
+ *           caller's stream, so each launch is timed alone;
  *   mode 2: around launch number `which` (0-based, counted from the start of
  *           each entry-point call) only, up to `capacity` pairs.
  * The events are created here (host objects; no device memory).

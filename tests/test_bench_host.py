@@ -31,3 +31,11 @@ def test_sampled_parity_skips_rerouted_tokens():
     p = bench.sampled_parity(gpu, idx, ref)
     assert p["tokens"] == 3 and p["routing_differs"] == 1
     assert abs(p["max_token_rel_err"] - 0.0625 / 2) < 1e-7
+
+
+def test_source_hash_ignores_comments_only():
+    """Stored counter data stays valid across comment edits, not code edits."""
+    a = bench._code_only("int f(int x) {  // twice\n  return 2 * x; /* doubled */\n}\n")
+    b = bench._code_only("int f(int x) {\n  return 2 * x;\n}")
+    c = bench._code_only("int f(int x) {\n  return 3 * x;\n}")
+    assert a == b and a != c
