@@ -23,7 +23,7 @@ The layer, as the pages state it:
      combine sums those local contributions; the sum over GPUs (an
      all-reduce) gives the layer's output.
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
   - top-k selects on fp32 logits; ties go to the lower expert index; +0 and -0
     tie; slots are ordered best first.
   - weights: softmax over the selected logits (equal to full softmax

@@ -13,7 +13,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    """Skip GPU tests cleanly when no GPU is visible (they are run with -m gpu on the GPU machine)."""
+    """Skip GPU tests cleanly when no GPU is visible (they run with -m gpu on a machine that has one)."""
     try:
         import torch
         has_gpu = torch.cuda.is_available()
