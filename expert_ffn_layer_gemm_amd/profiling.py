@@ -6,6 +6,8 @@
         --copy-bytes N --cmd-fetch "..." --cmd-write "..." --cmd-copy "..."
     python -m expert_ffn_layer_gemm_amd.profiling busy --workload W --bench-kernel NAME \
         --rocprof-kernel SUBSTR --counters CSV --trace CSV --mfma-flop F --peak-tflops P --cmd "..."
+    python -m expert_ffn_layer_gemm_amd.profiling stalls --workload W --bench-kernel NAME \
+        --rocprof-kernel SUBSTR --counters CSV --cmd "..."
 
 `trace` keeps the rows of this library's kernels from a --kernel-trace --stats
 summary.  `traffic` turns two --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per
@@ -16,7 +18,11 @@ source hash so stale numbers are ignored) plus a text summary.  `busy` turns
 one --kernel-trace --pmc run (GRBM_GUI_ACTIVE, SQ_BUSY_CYCLES,
 SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_MFMA) into the kernel's clock (GPU-active
 cycles per XCD over its duration), the fraction of SIMD cycles the matrix
-cores were busy, and the MFMA rate its instruction count implies.
+cores were busy, and the MFMA rate its instruction count implies.  `stalls`
+turns one --pmc run of wave-state counters (SQ_WAVE_CYCLES, SQ_WAIT_ANY,
+SQ_WAIT_INST_ANY, SQ_WAIT_INST_LDS, SQ_ACTIVE_INST_ANY, SQ_ACTIVE_INST_VALU,
+SQ_ACTIVE_INST_LDS, SQ_LDS_BANK_CONFLICT) into fractions of the kernel's wave
+cycles.
 """
 import argparse
 import collections
@@ -26,6 +32,7 @@ import os
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OUT_DIR = os.path.join(ROOT, "profiles")          # where the summaries are written
 
 
 def _rows(path):
@@ -80,9 +87,9 @@ def traffic_summary(a) -> None:
          "fetch_scale": f_scale, "write_scale": w_scale,
          "traffic_bytes": fetch_b + write_b, "dispatches": [nf, nw],
          "commands": {"fetch": a.cmd_fetch, "write": a.cmd_write, "copy": a.cmd_copy}}
-    out = os.path.join(ROOT, "profiles", f"traffic_{a.workload}.json")
+    out = os.path.join(OUT_DIR, f"traffic_{a.workload}.json")
     json.dump(d, open(out, "w"), indent=1)
-    txt = os.path.join(ROOT, "profiles", f"{a.bench_kernel}_{a.workload}_hbm_traffic.txt")
+    txt = os.path.join(OUT_DIR, f"{a.bench_kernel}_{a.workload}_hbm_traffic.txt")
     open(txt, "w").write(
         f"# HBM traffic of {fk} on {a.workload} (rocprofv3 --pmc, one counter per run)\n"
         f"# commands:\n#   {a.cmd_fetch}\n#   {a.cmd_write}\n#   {a.cmd_copy}  (each counter)\n"
@@ -116,7 +123,7 @@ def busy_summary(a) -> None:
     clock_ghz = gui / dur_ns
     busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMDS * gui)
     tflops = c["SQ_INSTS_MFMA"] * a.mfma_flop / (dur_ns * 1e-9) / 1e12
-    txt = os.path.join(ROOT, "profiles", f"{a.bench_kernel}_{a.workload}_mfma_busy.txt")
+    txt = os.path.join(OUT_DIR, f"{a.bench_kernel}_{a.workload}_mfma_busy.txt")
     open(txt, "w").write(
         f"# MFMA activity of {name} on {a.workload} (rocprofv3 --kernel-trace --pmc, one run)\n"
         f"# command: {a.cmd}\n"
@@ -127,6 +134,46 @@ def busy_summary(a) -> None:
         f"SQ_INSTS_MFMA {c['SQ_INSTS_MFMA']:.4g} x {a.mfma_flop:.0f} FLOP -> {tflops:.1f} TFLOP/s, "
         f"{100 * tflops / a.peak_tflops:.1f} % of the {a.peak_tflops:.0f} TFLOP/s nominal peak\n"
         f"SQ_BUSY_CYCLES {c['SQ_BUSY_CYCLES']:.4g}\n")
+
+
+STALL_COUNTERS = ("SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS",
+                  "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS",
+                  "SQ_LDS_BANK_CONFLICT")
+STALL_MEANING = {
+    "SQ_WAIT_ANY": "waiting at s_waitcnt / barrier",
+    "SQ_WAIT_INST_ANY": "waiting to issue (dependency or busy unit)",
+    "SQ_WAIT_INST_LDS": "waiting to issue an LDS instruction",
+    "SQ_ACTIVE_INST_ANY": "issuing any instruction",
+    "SQ_ACTIVE_INST_VALU": "issuing vector ALU (incl. MFMA issue)",
+    "SQ_ACTIVE_INST_LDS": "issuing LDS instructions",
+    "SQ_LDS_BANK_CONFLICT": "LDS bank-conflict cycles",
+}
+
+
+def stall_summary(a) -> None:
+    ctr = collections.defaultdict(lambda: collections.defaultdict(float))
+    disp = collections.defaultdict(set)
+    for r in _rows(a.counters):
+        if a.rocprof_kernel in r["Kernel_Name"]:
+            ctr[r["Kernel_Name"]][r["Counter_Name"]] += float(r["Counter_Value"])
+            disp[r["Kernel_Name"]].add(r["Dispatch_Id"])
+    if len(ctr) != 1:
+        raise SystemExit(f"kernel substring {a.rocprof_kernel!r} matches {list(ctr)}")
+    name = next(iter(ctr))
+    nd = len(disp[name])
+    c = {k: v / nd for k, v in ctr[name].items()}
+    missing = [k for k in STALL_COUNTERS if k not in c]
+    if missing:
+        raise SystemExit(f"counters missing from {a.counters}: {missing}")
+    wc = c["SQ_WAVE_CYCLES"]
+    lines = [f"# Wave states of {name} on {a.workload} (rocprofv3 --kernel-trace --pmc, one run)",
+             f"# command: {a.cmd}",
+             f"dispatches: {nd}; SQ_WAVE_CYCLES {wc:.4g} per dispatch",
+             "counter | per dispatch | fraction of wave cycles | meaning"]
+    for k in STALL_COUNTERS[1:]:
+        lines.append(f"{k} | {c[k]:.4g} | {c[k] / wc:.3f} | {STALL_MEANING[k]}")
+    txt = os.path.join(OUT_DIR, f"{a.bench_kernel}_{a.workload}_stalls.txt")
+    open(txt, "w").write("\n".join(lines) + "\n")
 
 
 def main():
@@ -146,11 +193,16 @@ def main():
         b.add_argument("--" + n, required=True)
     b.add_argument("--mfma-flop", type=float, required=True)
     b.add_argument("--peak-tflops", type=float, required=True)
+    st = sub.add_parser("stalls")
+    for n in ("workload", "bench-kernel", "rocprof-kernel", "counters", "cmd"):
+        st.add_argument("--" + n, required=True)
     a = ap.parse_args()
     if a.cmd_name == "trace":
         trace_summary(a.stats_csv, a.out_txt, a.cmd)
     elif a.cmd_name == "busy":
         busy_summary(a)
+    elif a.cmd_name == "stalls":
+        stall_summary(a)
     else:
         traffic_summary(a)
 
