@@ -72,13 +72,19 @@ def cpu_baseline(cfg, li, n_tokens):
     inp = to_numpy_inputs(li)
     n = min(n_tokens, cfg.T)
     inp["x_bf16"] = np.ascontiguousarray(inp["x_bf16"][:n])
+    # The same call is repeated until about CPU_MIN_S of work (at most
+    # CPU_MAX_REPS calls), so a short sample still gives a steady rate.
     t0 = time.perf_counter()
     ref = oracle.forward(inp)
+    reps = 1
+    while time.perf_counter() - t0 < CPU_MIN_S and reps < CPU_MAX_REPS:
+        oracle.forward(inp)
+        reps += 1
     dt = time.perf_counter() - t0
-    return ref, {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return ref, {"value": n * reps / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"oracle.forward on the first {n} of {cfg.T} tokens of {cfg.name} "
-                      f"(seed {cfg.seed}), {dt:.2f} s, fp32 NumPy, OpenBLAS threads={threads}, "
-                      f"os.cpu_count()={os.cpu_count()}"}
+                      f"(seed {cfg.seed}), {reps} call(s) in {dt:.2f} s, fp32 NumPy, "
+                      f"OpenBLAS threads={threads}, os.cpu_count()={os.cpu_count()}"}
 
 
 def device_info(dev):
@@ -132,6 +138,7 @@ def sampled_parity(out, idx, ref):
             "max_token_rel_err": float((num / den)[same].max())}
 
 
+CPU_MIN_S, CPU_MAX_REPS = 10.0, 16     # oracle timing: ~10 s of CPU work, bounded
 CPU_TOKENS = {"tiny": 64, "qwen3_235b_decode": 64, "qwen3_235b_prefill": 256,
               "qwen35_397b_zipf": 128, "deepseek_v3_fp8": 16,
               "qwen3_235b_decode_mxfp8": 64, "qwen3_235b_prefill_mxfp8": 256,
