@@ -36,6 +36,7 @@ SIGNATURES = {
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_abi_version": (ctypes.c_int, []),
     "moe_forward_workspace_bytes": (_SZ, [_SP]),
+    "moe_workspace_bytes": (_SZ, [_SP]),
     "moe_ffn_workspace_bytes": (_SZ, [_SP]),
     "moe_route_workspace_bytes": (_SZ, [_SP]),
     "moe_route": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -124,6 +125,10 @@ def moe_abi_version() -> int:
 
 def moe_forward_workspace_bytes(shape: MoeShape) -> int:
     return lib().moe_forward_workspace_bytes(ctypes.byref(shape))
+
+
+def moe_workspace_bytes(shape: MoeShape) -> int:
+    return lib().moe_workspace_bytes(ctypes.byref(shape))
 
 
 def moe_ffn_workspace_bytes(shape: MoeShape) -> int:

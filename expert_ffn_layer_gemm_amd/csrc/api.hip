@@ -118,6 +118,8 @@ size_t moe_forward_workspace_bytes(const moe_shape* shape) {
   return fwd_layout(shape).total;
 }
 
+size_t moe_workspace_bytes(const moe_shape* shape) { return moe_forward_workspace_bytes(shape); }
+
 size_t moe_ffn_workspace_bytes(const moe_shape* shape) {
   if (check_shape("moe_ffn_workspace_bytes", shape, true) != MOE_OK) return 0;
   return moe::ffn_workspace_bytes(shape->T, shape->H, n_local(shape), shape->k, shape->I,

@@ -355,12 +355,10 @@ __device__ __forceinline__ void mx_load_scales(u32x4_t (&sv)[NB + 1], int g, con
   sv[NB] = *reinterpret_cast<const u32x4_t*>(sarow + 16 * g);
 }
 
-#ifndef SKINNY_MX_NW
-#define SKINNY_MX_NW 4    // gate/up: waves per workgroup
-#define SKINNY_MX_CB 2    //          16-column blocks per wave
-#define SKINNY_MX_NWD 4   // down
-#define SKINNY_MX_CBD 2
-#endif
+// MXFP8 streaming shapes: waves per workgroup and 16-column blocks per wave
+// (gate/up, down).
+constexpr int kMxNW = 4, kMxCB = 2;
+constexpr int kMxNWD = 4, kMxCBD = 2;
 
 // Byte q of x.
 __device__ __forceinline__ uint32_t byte_of(uint32_t x, int q) { return (x >> (8 * q)) & 0xFFu; }
@@ -605,14 +603,16 @@ SideStream* side_stream() {
 }
 
 template <typename Kern>
-static void launch_gemm(const char* name, Kern kern, int threads, long long blocks,
-                        const GemmArgs& a, hipStream_t s) {
-  if (blocks > 0) MOE_LAUNCH(name, kern, dim3((unsigned)blocks), dim3(threads), 0, s, a);
+static hipError_t launch_gemm(const char* name, Kern kern, int threads, long long blocks,
+                              const GemmArgs& a, hipStream_t s) {
+  if (blocks <= 0) return hipSuccess;
+  MOE_LAUNCH(name, kern, dim3((unsigned)blocks), dim3(threads), 0, s, a);
+  return hipGetLastError();
 }
 
 template <bool DUAL, int NW, int CB>
-static void launch_skinny_mx(const char* name, long long blocks, const GemmArgs& a, hipStream_t s) {
-  if (blocks <= 0) return;
+static hipError_t launch_skinny_mx(const char* name, long long blocks, const GemmArgs& a, hipStream_t s) {
+  if (blocks <= 0) return hipSuccess;
   const int K32 = a.K / 32;
   if (a.K % 512 == 0 && a.K <= 8192) {
     constexpr int NB = (DUAL ? 2 : 1) * CB;
@@ -623,6 +623,7 @@ static void launch_skinny_mx(const char* name, long long blocks, const GemmArgs&
   } else {
     MOE_LAUNCH(name, (k_skinny_mx<DUAL, NW, CB, 0>), dim3((unsigned)blocks), dim3(64 * NW), 0, s, a);
   }
+  return hipGetLastError();
 }
 
 hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
@@ -630,7 +631,10 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
   uint8_t* ws = static_cast<uint8_t*>(f.workspace);
   const Sched sc = ffn_schedule(f);
   const long long R = (long long)f.T * (f.k + f.n_shared);
-  if (!f.planned) MOE_LAUNCH("plan", k_plan, dim3(1), dim3(1024), 0, s, f.offsets, sc);
+  if (!f.planned) {
+    MOE_LAUNCH("plan", k_plan, dim3(1), dim3(1024), 0, s, f.offsets, sc);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  }
 
   uint8_t* h = ws + L.h;
   void* h_scale = f.fp8 ? static_cast<void*>(ws + L.h_scale) : nullptr;
@@ -673,29 +677,33 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
     ts = side->s;
   }
 
+  // Every launch is checked before the next is enqueued; after a failed one
+  // nothing more is launched, and the side stream is still joined back.
+  hipError_t err = hipSuccess;
+  auto run = [&](hipError_t e) { if (err == hipSuccess) err = e; return err == hipSuccess; };
+
   // The tiled chain is enqueued first: its few large workgroups (one per CU)
   // start before the weight-streaming workgroups fill the machine.
   const char* nm_tg = f.mx ? "tiled_gateup_mx" : f.fp8 ? "tiled_gateup_fp8" : "tiled_gateup_bf16";
   const char* nm_td = f.mx ? "tiled_down_mx" : f.fp8 ? "tiled_down_fp8" : "tiled_down_bf16";
   up.n_ntile = f.I / 128;
-  if (tiled)
-    launch_tiled(nm_tg, f.fp8, f.mx, true, (long long)L.max_tiles * up.n_ntile, up, ts);
   dn.n_ntile = ceil_div(f.H, 256);
-  if (tiled)
-    launch_tiled(nm_td, f.fp8, f.mx, false, (long long)L.max_tiles * dn.n_ntile, dn, ts);
+  if (tiled && run(launch_tiled(nm_tg, f.fp8, f.mx, true, (long long)L.max_tiles * up.n_ntile, up, ts)))
+    run(launch_tiled(nm_td, f.fp8, f.mx, false, (long long)L.max_tiles * dn.n_ntile, dn, ts));
 
   // gate/up + SwiGLU, then down, of the groups of at most skinny_max_rows(T) rows
-  if (f.mx) {
+  if (err != hipSuccess) {
+  } else if (f.mx) {
     // Scale mode by K (16-byte scale loads need 16-byte aligned scale rows).
-    up.n_ntile = f.I / (16 * SKINNY_MX_CB * SKINNY_MX_NW);
-    dn.n_ntile = f.H / (16 * SKINNY_MX_CBD * SKINNY_MX_NWD);
-    launch_skinny_mx<true, SKINNY_MX_NW, SKINNY_MX_CB>("skinny_gateup_mx", band_grid(L.max_slices, up.n_ntile), up, s);
-    launch_skinny_mx<false, SKINNY_MX_NWD, SKINNY_MX_CBD>("skinny_down_mx", band_grid(L.max_slices, dn.n_ntile), dn, s);
+    up.n_ntile = f.I / (16 * kMxCB * kMxNW);
+    dn.n_ntile = f.H / (16 * kMxCBD * kMxNWD);
+    if (run(launch_skinny_mx<true, kMxNW, kMxCB>("skinny_gateup_mx", band_grid(L.max_slices, up.n_ntile), up, s)))
+      run(launch_skinny_mx<false, kMxNWD, kMxCBD>("skinny_down_mx", band_grid(L.max_slices, dn.n_ntile), dn, s));
   } else if (f.fp8) {
     up.n_ntile = f.I / (16 * 8);
-    launch_gemm("skinny_gateup_fp8", k_skinny_fp8<true, 8, 1>, 512, band_grid(L.max_slices, up.n_ntile), up, s);
     dn.n_ntile = f.H / (16 * 4);
-    launch_gemm("skinny_down_fp8", k_skinny_fp8<false, 4, 1>, 256, band_grid(L.max_slices, dn.n_ntile), dn, s);
+    if (run(launch_gemm("skinny_gateup_fp8", k_skinny_fp8<true, 8, 1>, 512, band_grid(L.max_slices, up.n_ntile), up, s)))
+      run(launch_gemm("skinny_down_fp8", k_skinny_fp8<false, 4, 1>, 256, band_grid(L.max_slices, dn.n_ntile), dn, s));
   } else {
     // Split-K only without tiled work (the layout reserved the partials then).
     const bool split = !tiled && (L.split_up > 1 || L.split_dn > 1);
@@ -705,28 +713,31 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
     up.ksplit = split ? L.split_up : 1;
     up.R = (int)R;
     up.part = part;
-    launch_gemm("skinny_gateup_bf16", k_skinny_bf16<true, 4, 1>, 256,
-                band_grid(L.max_slices, up.n_ntile) * up.ksplit, up, s);
-    if (up.ksplit > 1)
-      MOE_LAUNCH("splitk_reduce_gateup", k_splitk_reduce<true>, dim3(ceil_div(f.I, 1024), (unsigned)R),
-                 dim3(256), 0, s, part, up.ksplit, (int)R, f.I, n_rows, reinterpret_cast<uint16_t*>(h));
     dn.n_ntile = f.H / (32 * 4);
     dn.ksplit = split ? L.split_dn : 1;
     dn.R = (int)R;
     dn.part = part;
-    launch_gemm("skinny_down_bf16", k_skinny_bf16<false, 4, 1>, 256,
-                band_grid(L.max_slices, dn.n_ntile) * dn.ksplit, dn, s);
-    if (dn.ksplit > 1)
+    if (run(launch_gemm("skinny_gateup_bf16", k_skinny_bf16<true, 4, 1>, 256,
+                        band_grid(L.max_slices, up.n_ntile) * up.ksplit, up, s)) && up.ksplit > 1) {
+      MOE_LAUNCH("splitk_reduce_gateup", k_splitk_reduce<true>, dim3(ceil_div(f.I, 1024), (unsigned)R),
+                 dim3(256), 0, s, part, up.ksplit, (int)R, f.I, n_rows, reinterpret_cast<uint16_t*>(h));
+      run(hipGetLastError());
+    }
+    if (err == hipSuccess &&
+        run(launch_gemm("skinny_down_bf16", k_skinny_bf16<false, 4, 1>, 256,
+                        band_grid(L.max_slices, dn.n_ntile) * dn.ksplit, dn, s)) && dn.ksplit > 1) {
       MOE_LAUNCH("splitk_reduce_down", k_splitk_reduce<false>, dim3(ceil_div(f.H, 1024), (unsigned)R),
                  dim3(256), 0, s, part, dn.ksplit, (int)R, f.H, n_rows,
                  static_cast<uint16_t*>(f.y_perm));
+      run(hipGetLastError());
+    }
   }
   if (side) {                        // join: the caller's stream waits for the tiled chain
     hipError_t e = hipEventRecord(side->join, side->s);
     if (e == hipSuccess) e = hipStreamWaitEvent(s, side->join, 0);
-    if (e != hipSuccess) return e;
+    run(e);
   }
-  return hipGetLastError();
+  return err;
 }
 
 }  // namespace moe

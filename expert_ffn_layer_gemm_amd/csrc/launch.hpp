@@ -23,6 +23,14 @@ bool prof_serial();
     ::moe::prof_after(stream);                                           \
   } while (0)
 
+// MOE_LAUNCH, then return the launch error (if any) from the enclosing
+// launcher before anything else is enqueued.
+#define MOE_LAUNCH_OR_RETURN(...)                                          \
+  do {                                                                   \
+    MOE_LAUNCH(__VA_ARGS__);                                             \
+    if (hipError_t e_ = hipGetLastError(); e_ != hipSuccess) return e_;  \
+  } while (0)
+
 // route.hip
 // The router GEMM splits H into router_splits() slices and writes their
 // partial sums to parts [KS][T][E] (KS == 1: parts may be the logits buffer);

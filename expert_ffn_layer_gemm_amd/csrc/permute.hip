@@ -217,12 +217,12 @@ hipError_t launch_permute(const int32_t* topk_idx, const uint16_t* x, int32_t* c
                           hipStream_t s) {
   const int n_tiles = ceil_div(T, kRankTile);
   if (T > 0)
-    MOE_LAUNCH("tile_hist", k_tile_hist, dim3(n_tiles), dim3(kRankTile), 0, s, topk_idx, tile_cnt,
+    MOE_LAUNCH_OR_RETURN("tile_hist", k_tile_hist, dim3(n_tiles), dim3(kRankTile), 0, s, topk_idx, tile_cnt,
                T, E, k, e_first);
-  MOE_LAUNCH("scan", k_scan, dim3(1), dim3(1024), 0, s, tile_cnt, n_tiles, counts, offsets, T, E,
+  MOE_LAUNCH_OR_RETURN("scan", k_scan, dim3(1), dim3(1024), 0, s, tile_cnt, n_tiles, counts, offsets, T, E,
              n_shared);
   if (T == 0) return hipGetLastError();
-  MOE_LAUNCH("rank", k_rank, dim3(n_tiles), dim3(kRankTile), 0, s, topk_idx, offsets, tile_cnt,
+  MOE_LAUNCH_OR_RETURN("rank", k_rank, dim3(n_tiles), dim3(kRankTile), 0, s, topk_idx, offsets, tile_cnt,
              dest, src_row, T, E, k, n_shared, e_first);
   if (x_perm == nullptr) return hipGetLastError();
   const int R = T * (k + n_shared);

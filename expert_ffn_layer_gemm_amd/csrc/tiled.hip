@@ -54,10 +54,7 @@ namespace moe {
 namespace {
 
 constexpr int kBRows = 256;                       // staged B rows per tile
-#ifndef TILED_BF16_NSA
-#define TILED_BF16_NSA 2                          // bf16 A / B ring stages
-#define TILED_BF16_NSB 2
-#endif
+constexpr int kBf16NSA = 2, kBf16NSB = 2;        // bf16 A / B ring stages
 constexpr int kMaxKB = 1024;                      // fp8: K <= 131072 (B scales kept in LDS)
 
 // Slot of 16-byte chunk c of staged row r for rows of RB bytes: 128-byte rows
@@ -680,9 +677,9 @@ hipError_t launch_tiled(const char* name, bool fp8, bool mx, bool dual, long lon
   else if (mx) MOE_LAUNCH(name, (k_tiled3<true, false, 2, 4, 128, 3, 3, 128, true>), grid, dim3(512), 0, s, a);
   else if (fp8 && dual) MOE_LAUNCH(name, (k_tiled3<true, true, 2, 4, 128, 3, 3, 128>), grid, dim3(512), 0, s, a);
   else if (fp8) MOE_LAUNCH(name, (k_tiled3<true, false, 2, 4, 128, 3, 3, 128>), grid, dim3(512), 0, s, a);
-  else if (dual) MOE_LAUNCH(name, (k_tiled3<false, true, 2, 4, 256, TILED_BF16_NSA, TILED_BF16_NSB, 128>), grid, dim3(512), 0, s, a);
-  else MOE_LAUNCH(name, (k_tiled3<false, false, 2, 4, 256, TILED_BF16_NSA, TILED_BF16_NSB, 128>), grid, dim3(512), 0, s, a);
-  return hipSuccess;
+  else if (dual) MOE_LAUNCH(name, (k_tiled3<false, true, 2, 4, 256, kBf16NSA, kBf16NSB, 128>), grid, dim3(512), 0, s, a);
+  else MOE_LAUNCH(name, (k_tiled3<false, false, 2, 4, 256, kBf16NSA, kBf16NSB, 128>), grid, dim3(512), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace moe

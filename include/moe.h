@@ -123,6 +123,10 @@ int moe_abi_version(void);
    sub-buffers).  Returns 0 for an unsupported shape. */
 size_t moe_forward_workspace_bytes(const moe_shape* shape);
 
+/* The same value as moe_forward_workspace_bytes, under the name of the
+   layer-level workspace query (the whole layer in one call needs this much). */
+size_t moe_workspace_bytes(const moe_shape* shape);
+
 /* Bytes of device workspace moe_grouped_ffn needs (h, its fp8 scales and the
    on-device tile schedule).  Returns 0 for an unsupported shape. */
 size_t moe_ffn_workspace_bytes(const moe_shape* shape);

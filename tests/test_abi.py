@@ -36,6 +36,14 @@ def test_shape_struct_matches_header():
     assert ctypes.sizeof(moe.MoeShape) == 4 * len(names)
 
 
+def test_workspace_alias():
+    # moe_workspace_bytes is the layer-level name of moe_forward_workspace_bytes
+    for sh in (moe.make_shape(64, 4096, 128, 8, 1536), moe.make_shape(4096, 7168, 256, 8, 2048, 1, "fp8"),
+               moe.make_shape(64, 4096, 128, 8, 1536, 0, "mxfp8", 16, 16), moe.make_shape(64, 100, 8, 2, 128)):
+        assert moe.moe_workspace_bytes(sh) == moe.moe_forward_workspace_bytes(sh)
+    assert moe.moe_workspace_bytes(moe.make_shape(64, 100, 8, 2, 128)) == 0
+
+
 def test_abi_version():
     assert moe.moe_abi_version() == 4
 
