@@ -4,14 +4,20 @@ after the input changes in place, because group sizes, tile lists and row
 maps are rebuilt on the device by every replay (no host round trip).
 
 The kernels are deterministic (fixed summation orders, no atomics on values),
-so eager and replayed results are compared bit for bit.
+so eager and replayed results are compared bit for bit; the first replay's
+output is also checked against the CPU oracle (routing bit-exact given the
+GPU's router logits, output within the layer tolerance).
 """
+import numpy as np
 import pytest
 import torch
 
 import expert_ffn_layer_gemm_amd as moe
-from synth import MoeConfig, config_by_name, generate_layer
-from tests.gpu_helpers import DEV, layer
+import oracle
+from synth import MoeConfig, config_by_name, generate_layer, to_numpy_inputs
+from tests.gpu_helpers import DEV, bf16_np, layer, rel_inf, run_route
+
+TOL = {"bf16": 2e-2, "fp8": 5e-2, "mxfp8": 5e-2}
 
 pytestmark = pytest.mark.gpu
 
@@ -77,6 +83,14 @@ def test_graph_replay_matches_eager(cfg):
         idx.fill_(-1)
         g.replay()
         torch.cuda.synchronize()
+        if rep == 0:
+            # the replayed layer against the oracle, routed on the GPU's logits
+            logits, _, _ = run_route(cfg, li)
+            ref_o = oracle.forward(to_numpy_inputs(li), logits_override=logits.cpu().numpy())
+            assert np.array_equal(idx.cpu().numpy(), ref_o.topk_idx), "replay routing vs oracle"
+            err = rel_inf(bf16_np(out), ref_o.out)
+            print(f"{cfg.name}: replay vs oracle per-token rel err {err:.3e}")
+            assert err <= TOL[cfg.wdtype]
         assert torch.equal(out.view(torch.int16), ref[0].view(torch.int16)), f"replay {rep}: out"
         assert torch.equal(idx, ref[1]), f"replay {rep}: topk_idx"
         assert torch.equal(w, ref[2]), f"replay {rep}: topk_w"

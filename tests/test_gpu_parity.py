@@ -321,35 +321,28 @@ def _forward_check(cfg, li, sample=None):
     own = oracle.topk_softmax(oracle.router_logits(oracle.bf16_bits_to_f32(inp["x_bf16"]),
                                                    inp["w_router"], inp["router_bias"]), cfg.k)[0]
     flips = int((own != idx.cpu().numpy()).any(axis=1).sum())
-    print(f"{cfg.name}: per-token rel err {err:.3e}, routing flips vs oracle logits: {flips}")
+    n_tok = cfg.T if sample is None else len(sample)
+    print(f"{cfg.name}: per-token rel err {err:.3e} over {n_tok} tokens, "
+          f"routing flips vs oracle logits: {flips}")
     assert err <= TOL[cfg.wdtype]
     assert flips <= max(2, cfg.T // 500)
     return out
 
 
-@pytest.mark.parametrize("ci", [0, 1, 3])
+# Every token of every workload at full size against the whole-layer oracle
+# (8192 prefill tokens, 4096 DeepSeek-like tokens through the fp8 tiled
+# kernels at K = 7168, the shared expert's 4096-row group included).
+@pytest.mark.parametrize("ci", range(len(CONFIGS)))
 def test_forward_configs_full(ci):
     cfg = CONFIGS[ci]
     _forward_check(cfg, layer(cfg))
 
 
-@pytest.mark.parametrize("ci", [2, 4])
-def test_forward_configs_sampled(ci):
-    cfg = CONFIGS[ci]
-    rng = np.random.default_rng(ci)
-    sample = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 14, replace=False)]))
-    _forward_check(cfg, layer(cfg), sample)
-
-
-# MXFP8 layers at the Qwen3-235B shape: decode in full, prefill on sampled tokens.
+# MXFP8 layers at the Qwen3-235B shape, decode and prefill, every token.
 @pytest.mark.parametrize("name", [c.name for c in EXTRA_CONFIGS if c.wdtype == "mxfp8"])
 def test_forward_mxfp8_configs(name):
     cfg = next(c for c in EXTRA_CONFIGS if c.name == name)
-    sample = None
-    if cfg.T > 1024:
-        rng = np.random.default_rng(cfg.seed)
-        sample = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 14, replace=False)]))
-    _forward_check(cfg, layer(cfg), sample)
+    _forward_check(cfg, layer(cfg))
 
 
 @pytest.mark.parametrize("ci", range(len(CONFIGS)))
@@ -384,9 +377,9 @@ def test_forward_edge_cases(case):
         # GEMM's second column tile holds 128 of its 256 columns
         "hot_ragged_n": MoeConfig("hotrn", 41, T=600, H=384, E=8, k=1, I=256),
         "fp8_hot_ragged_n": MoeConfig("f8hotrn", 42, T=600, H=384, E=8, k=1, I=256, wdtype="fp8"),
-        # K a multiple of 512 in both GEMMs (the fp8 kernel with register-staged
-        # weights): ~150-row groups split into two tiles, a 600-row shared
-        # expert; then H = 640, whose down GEMM has a 128-column last tile.
+        # ~150-row groups split into two 128-row tiles, a 600-row shared
+        # expert, K a multiple of 512 in both GEMMs; then H = 640, whose down
+        # GEMM has a 128-column last tile.
         "fp8_k512": MoeConfig("f8k512", 43, T=600, H=1024, E=8, k=2, I=512, n_shared=1, wdtype="fp8"),
         "fp8_k512_ragged_n": MoeConfig("f8k512rn", 44, T=600, H=640, E=8, k=2, I=512, n_shared=1,
                                        wdtype="fp8"),
@@ -420,11 +413,7 @@ def test_forward_share(cfg):
 @pytest.mark.parametrize("name", [c.name for c in EXTRA_CONFIGS if c.e_local])
 def test_forward_share_configs(name):
     cfg = next(c for c in EXTRA_CONFIGS if c.name == name)
-    sample = None
-    if cfg.T > 1024:
-        rng = np.random.default_rng(cfg.seed)
-        sample = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 14, replace=False)]))
-    _forward_check(cfg, layer(cfg), sample)
+    _forward_check(cfg, layer(cfg))
 
 
 # Decode batches whose groups leave the chip idle take split-K in the bf16
@@ -456,11 +445,7 @@ EXTREMES = [
 
 @pytest.mark.parametrize("cfg", EXTREMES, ids=[c.name for c in EXTREMES])
 def test_forward_extremes(cfg):
-    sample = None
-    if cfg.T > 4096:
-        rng = np.random.default_rng(cfg.seed)
-        sample = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 30, replace=False)]))
-    _forward_check(cfg, generate_layer(cfg, DEV), sample)
+    _forward_check(cfg, generate_layer(cfg, DEV))
 
 
 def test_shares_sum_to_the_layer_on_gpu():
