@@ -6,12 +6,18 @@ GEMM with SwiGLU, grouped down GEMM, weighted combine.  Inputs and weights are
 resident in HBM before the timed region.  Prints ONE JSON line.
 
     python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
+                    [--no-other-configs]
 
-The default workload is the Qwen3-235B-like decode step (T=64 tokens, hidden
-4096, 128 experts, top-8, intermediate 1536, bf16).  The roofline object is
+The default workload is the largest single-GPU layer: the DeepSeek-V3-like
+layer (T=4096 tokens, hidden 7168, 256 routed experts top-8 + 1 shared
+expert, intermediate 2048, e4m3 weights with 128x128 block scales,
+activations quantised per token per 128 channels).  The `roofline` object is
 for the kernel with the largest share of the step, timed with HIP events
 recorded by the library around that kernel's launch on the caller's stream
-during the timed steps.
+during the timed steps; `layer_roofline` is the whole step's.  The same line
+carries, under `other_configs`, the step time and rooflines of the other four
+layer shapes (Tiny, Qwen3-235B-like decode and prefill, Qwen3.5-397B-like),
+each timed the same way without a CPU baseline.
 """
 import argparse
 import hashlib
@@ -66,9 +72,11 @@ def cpu_baseline(cfg, li, n_tokens):
     from synth import to_numpy_inputs
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        info = threadpool_info()
+        threads = max([p.get("num_threads", 1) for p in info] or [1])
+        blas = ",".join(sorted({p.get("internal_api", "?") for p in info})) or "?"
     except Exception:  # pragma: no cover
-        threads = 1
+        threads, blas = 1, "?"
     inp = to_numpy_inputs(li)
     n = min(n_tokens, cfg.T)
     inp["x_bf16"] = np.ascontiguousarray(inp["x_bf16"][:n])
@@ -81,10 +89,12 @@ def cpu_baseline(cfg, li, n_tokens):
         oracle.forward(inp)
         reps += 1
     dt = time.perf_counter() - t0
+    what = (f"the whole layer ({n} tokens)" if n == cfg.T else f"the first {n} of {cfg.T} tokens")
     return ref, {"value": n * reps / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"oracle.forward on the first {n} of {cfg.T} tokens of {cfg.name} "
-                      f"(seed {cfg.seed}), {reps} call(s) in {dt:.2f} s, fp32 NumPy, "
-                      f"OpenBLAS threads={threads}, os.cpu_count()={os.cpu_count()}"}
+            "sample": f"oracle.forward on {what} of {cfg.name} (seed {cfg.seed}, same inputs as the "
+                      f"GPU steps), {reps} call(s) in {dt:.2f} s, fp32 NumPy; BLAS {blas} with "
+                      f"{threads} threads; {len(os.sched_getaffinity(0))} cores in this process's "
+                      f"affinity, os.cpu_count()={os.cpu_count()}"}
 
 
 def device_info(dev):
@@ -121,9 +131,9 @@ def routing_stats(counts):
 
 
 def sampled_parity(out, idx, ref):
-    """The timed steps' output on the oracle's sample tokens against the oracle
-    (its own router logits, so a near-tie may pick another expert: such tokens
-    are counted, not compared)."""
+    """The timed steps' output on the oracle's tokens (the whole layer by
+    default) against the oracle (its own router logits, so a near-tie may pick
+    another expert: such tokens are counted, not compared)."""
     import numpy as np
     import torch
     n = ref.out.shape[0]
@@ -138,50 +148,30 @@ def sampled_parity(out, idx, ref):
             "max_token_rel_err": float((num / den)[same].max())}
 
 
-CPU_MIN_S, CPU_MAX_REPS = 10.0, 16     # oracle timing: ~10 s of CPU work, bounded
-CPU_TOKENS = {"tiny": 64, "qwen3_235b_decode": 64, "qwen3_235b_prefill": 256,
-              "qwen35_397b_zipf": 128, "deepseek_v3_fp8": 16,
-              "qwen3_235b_decode_mxfp8": 64, "qwen3_235b_prefill_mxfp8": 256,
-              "qwen3_235b_decode_ep8": 64, "qwen3_235b_prefill_ep4": 512}
+CPU_MIN_S, CPU_MAX_REPS = 10.0, 16     # oracle timing: >= ~10 s of CPU work, bounded
+# Tokens the oracle runs on for each workload's CPU baseline: the whole layer
+# (every token) where one oracle call takes well under a minute on the host.
+CPU_TOKENS = {"tiny": 64, "qwen3_235b_decode": 64, "qwen3_235b_prefill": 8192,
+              "qwen35_397b_zipf": 1024, "deepseek_v3_fp8": 4096,
+              "qwen3_235b_decode_mxfp8": 64, "qwen3_235b_prefill_mxfp8": 8192,
+              "qwen3_235b_decode_ep8": 64, "qwen3_235b_prefill_ep4": 8192}
+DEFAULT_CONFIG = "deepseek_v3_fp8"
+OTHER_CONFIGS = ("tiny", "qwen3_235b_decode", "qwen3_235b_prefill", "qwen35_397b_zipf")
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="qwen3_235b_decode")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=None)
-    ap.add_argument("--graph-probe", action="store_true",
-                    help="also time K replays of moe_forward captured in a HIP graph (extra field)")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain 1 GiB device copy 3 times (HBM counter calibration)")
-    args = ap.parse_args()
+def measure(cfg, steps, warmup, graph_probe=False):
+    """Time `steps` moe_forward calls of one workload after `warmup` untimed ones.
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU's share of the MoE layer on one MI355X; "
-              "runs on more than one GPU are not part of this build", file=sys.stderr)
-        sys.exit(2)
-
+    Returns the record fields (timing, rooflines, per-kernel times) and the
+    device buffers the last step wrote (out, idx) plus the generated inputs."""
     import numpy as np
     import torch
 
     import expert_ffn_layer_gemm_amd as moe
     from expert_ffn_layer_gemm_amd import accounting as acc
-    from synth import config_by_name, generate_layer
+    from synth import generate_layer
 
     dev = torch.device("cuda:0")
-    if args.copy_calibration:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes_each_way": 1 << 30, "launches": 3}))
-        return
-
-    cfg = config_by_name(args.config)
     li = generate_layer(cfg, dev)
     shape = moe.shape_of(cfg)
     ws = torch.empty(moe.moe_forward_workspace_bytes(shape), dtype=torch.uint8, device=dev)
@@ -194,7 +184,7 @@ def main():
         moe.moe_forward(shape, li.x, li.w_router, li.router_bias, li.w_gate, li.w_up, li.w_down,
                         li.s_gate, li.s_up, li.s_down, out, idx, w, ws, stream=stream)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
@@ -210,12 +200,12 @@ def main():
 
     # Timed region: K steps; the library records one event pair around the
     # dominant kernel's launch in each step.
-    moe.moe_profile_start(2, dom, args.steps)
+    moe.moe_profile_start(2, dom, steps)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     e0.record(stream)
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     e1.record(stream)
     torch.cuda.synchronize()
@@ -223,13 +213,13 @@ def main():
     total_ms = e0.elapsed_time(e1)
     kern_ms = [moe.moe_profile_read(i)[0] for i in range(moe.moe_profile_count())]
     moe.moe_profile_stop()
-    ms_per_step = total_ms / args.steps
-    value = cfg.T * args.steps / (total_ms / 1e3)
+    ms_per_step = total_ms / steps
+    value = cfg.T * steps / (total_ms / 1e3)
 
     # After the timed region: the spread of single steps (an event pair
-    # around each of K more steps), and the machine it ran on.
+    # around each of K more steps).
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+           for _ in range(steps)]
     for a, b in evs:
         a.record(stream)
         step()
@@ -238,7 +228,6 @@ def main():
     one = np.array([a.elapsed_time(b) for a, b in evs])
     spread = {"median_ms": float(np.median(one)), "p90_ms": float(np.percentile(one, 90)),
               "min_ms": float(one.min()), "steps": int(len(one))}
-    device = device_info(dev)
 
     counts = np.bincount(idx.cpu().numpy().ravel(), minlength=cfg.E)
     counts = counts[cfg.e_first:cfg.e_first + cfg.E_loc]      # the experts held here
@@ -268,7 +257,7 @@ def main():
     layer_roof = acc.roofline(layer, ms_per_step / 1e3, dtype)
 
     graph = None
-    if args.graph_probe:
+    if graph_probe:
         # The same step captured once on a side stream and replayed K times.
         gs = torch.cuda.Stream()
         gs.wait_stream(stream)
@@ -277,42 +266,116 @@ def main():
             moe.moe_forward(shape, li.x, li.w_router, li.router_bias, li.w_gate, li.w_up,
                             li.w_down, li.s_gate, li.s_up, li.s_down, out, idx, w, ws,
                             stream=torch.cuda.current_stream())
-        for _ in range(args.warmup):
+        for _ in range(warmup):
             g.replay()
         torch.cuda.synchronize()
         g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         g0.record()
-        for _ in range(args.steps):
+        for _ in range(steps):
             g.replay()
         g1.record()
         torch.cuda.synchronize()
-        graph = {"ms_per_step": g0.elapsed_time(g1) / args.steps}
+        graph = {"ms_per_step": g0.elapsed_time(g1) / steps}
+
+    config = {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k,
+              "I": cfg.I, "n_shared": cfg.n_shared, "weights": cfg.wdtype,
+              **({"expert_share": [cfg.e_first, cfg.e_first + cfg.E_loc]} if cfg.e_local else {}),
+              "touched_experts": int(layer.groups),
+              **routing_stats(counts[:cfg.E_loc])}
+    rec = {"value": value, "ms_per_step": ms_per_step, "dtype": dtype, "config": config,
+           "roofline": roof, "layer_roofline": layer_roof,
+           "per_kernel_ms": {f"{i}:{n}": round(ms, 4) for i, (ms, n) in enumerate(launches)},
+           "grouped_ffn_rooflines": kernel_roofs, "wall_s_timed_region": t_wall,
+           "single_steps": spread, "graph_replay": graph}
+    return rec, li, out, idx
+
+
+def summary(rec):
+    """The short form of a workload's record carried under other_configs."""
+    r, lr = rec["roofline"], rec["layer_roofline"]
+    return {"tokens_per_s": rec["value"], "ms_per_step": rec["ms_per_step"], "dtype": rec["dtype"],
+            "layer_roofline": {k: lr[k] for k in ("bound", "achieved", "unit", "frac")},
+            "dominant_kernel": None if r is None else
+            {"kernel": r["kernel"], "kernel_ms": r["kernel_ms"], "bound": r["bound"], "frac": r["frac"]},
+            "touched_experts": rec["config"]["touched_experts"],
+            "max_group_rows": rec["config"]["max_group_rows"]}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default=DEFAULT_CONFIG)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="time only --config (no other_configs records)")
+    ap.add_argument("--cpu-tokens", type=int, default=None)
+    ap.add_argument("--graph-probe", action="store_true",
+                    help="also time K replays of moe_forward captured in a HIP graph (extra field)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy 3 times (HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU's share of the MoE layer on one MI355X; "
+              "runs on more than one GPU are not part of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from synth import config_by_name
+
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": 1 << 30, "launches": 3}))
+        return
+
+    cfg = config_by_name(args.config)
+    print(f"bench: timing {cfg.name}", file=sys.stderr, flush=True)
+    rec, li, out, idx = measure(cfg, args.steps, args.warmup, args.graph_probe)
+    device = device_info(dev)
 
     cpu = parity = None
     if not args.no_cpu_baseline:
+        print(f"bench: oracle on the host for {cfg.name}", file=sys.stderr, flush=True)
         ref, cpu = cpu_baseline(cfg, li, args.cpu_tokens or CPU_TOKENS.get(cfg.name, 64))
         parity = sampled_parity(out, idx, ref)
+        del ref
+    del li, out, idx
+    torch.cuda.empty_cache()
+
+    others = None
+    if not args.no_other_configs and args.config == DEFAULT_CONFIG:
+        others = {}
+        for name in OTHER_CONFIGS:
+            print(f"bench: timing {name}", file=sys.stderr, flush=True)
+            r, *_ = measure(config_by_name(name), args.steps, args.warmup)
+            others[name] = summary(r)
+            torch.cuda.empty_cache()
 
     res = {
-        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "metric": METRIC, "value": rec["value"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": rec["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": rec["dtype"],
         "data": "synthetic (seeded; random-init weights of the layer's shape)",
-        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k,
-                   "I": cfg.I, "n_shared": cfg.n_shared, "weights": cfg.wdtype,
-                   **({"expert_share": [cfg.e_first, cfg.e_first + cfg.E_loc]} if cfg.e_local else {}),
-                   "touched_experts": int(layer.groups),
-                   **routing_stats(counts[:cfg.E_loc])},
-        "roofline": roof,
-        "layer_roofline": layer_roof,
-        "per_kernel_ms": {f"{i}:{n}": round(ms, 4) for i, (ms, n) in enumerate(launches)},
-        "grouped_ffn_rooflines": kernel_roofs,
-        "wall_s_timed_region": t_wall,
-        "single_steps": spread,
+        "config": rec["config"],
+        "roofline": rec["roofline"],
+        "layer_roofline": rec["layer_roofline"],
+        "per_kernel_ms": rec["per_kernel_ms"],
+        "grouped_ffn_rooflines": rec["grouped_ffn_rooflines"],
+        "wall_s_timed_region": rec["wall_s_timed_region"],
+        "single_steps": rec["single_steps"],
         "device": device,
-        "graph_replay": graph,
+        "graph_replay": rec["graph_replay"],
         "cpu_baseline": cpu,
         "parity": parity,
+        "other_configs": others,
     }
     print(json.dumps(res))
 
