@@ -309,6 +309,7 @@ def _forward_check(cfg, li, sample=None):
     lg = logits.cpu().numpy()
     inp = to_numpy_inputs(li)
     gpu_out = bf16_np(out)
+    print(f"{cfg.name}: GPU layer done, oracle on the host", flush=True)
     if sample is None:
         ref = oracle.forward(inp, logits_override=lg)
         assert np.array_equal(idx.cpu().numpy(), ref.topk_idx)
