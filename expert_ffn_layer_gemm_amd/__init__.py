@@ -6,5 +6,6 @@ from ._binding import (  # noqa: F401
     moe_ffn_workspace_bytes,
     moe_route_workspace_bytes, moe_route, moe_route_from_logits,
     moe_permute_workspace_bytes, moe_permute, moe_grouped_ffn, moe_combine, moe_forward,
+    moe_forward_noalloc, NOALLOC_SCRATCH_BYTES,
     moe_profile_start, moe_profile_count, moe_profile_read, moe_profile_stop,
 )

@@ -46,6 +46,7 @@ SIGNATURES = {
     "moe_grouped_ffn": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_combine": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P]),
     "moe_forward": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_forward_noalloc": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_profile_start": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int]),
     "moe_profile_count": (ctypes.c_int, []),
     "moe_profile_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_float),
@@ -186,6 +187,18 @@ def moe_forward(shape, x, w_router, router_bias, w_gate, w_up, w_down, s_gate, s
                              _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(s_gate), _ptr(s_up),
                              _ptr(s_down), _ptr(out), _ptr(topk_idx_out), _ptr(topk_w_out),
                              _ptr(workspace), ws_bytes, _stream(stream)), "moe_forward")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES
+
+
+def moe_forward_noalloc(shape, x, w_router, router_bias, w_gate, w_up, w_down, s_gate, s_up,
+                        s_down, out, topk_idx_out, topk_w_out, stream=None):
+    _check(lib().moe_forward_noalloc(ctypes.byref(shape), _ptr(x), _ptr(w_router),
+                                     _ptr(router_bias), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                                     _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(out),
+                                     _ptr(topk_idx_out), _ptr(topk_w_out), _stream(stream)),
+           "moe_forward_noalloc")
 
 
 def moe_profile_start(mode: int, which: int = 0, capacity: int = 64) -> None:

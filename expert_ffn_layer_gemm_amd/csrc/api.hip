@@ -5,6 +5,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "ffn.hpp"
@@ -105,13 +106,133 @@ FwdLayout fwd_layout(const moe_shape* s) {
   return L;
 }
 
+// Argument checks of the whole-layer entry points (everything but the workspace).
+int check_forward_args(const char* fn, const moe_shape* shape, const void* x, const float* w_router,
+                       const float* router_bias, const void* w_gate, const void* w_up,
+                       const void* w_down, const void* s_gate, const void* s_up,
+                       const void* s_down, const void* out, const int32_t* topk_idx_out,
+                       const float* topk_w_out) {
+  if (int rc = check_shape(fn, shape, true)) return rc;
+  if ((long long)shape->T * shape->H * 2 >= (1LL << 32))   // 32-bit row offsets into x
+    return fail(MOE_ERR_UNSUPPORTED, "%s: T*H*2 >= 2^32", fn);
+  if (shape->T == 0) return MOE_OK;
+  MOE_NEED_PTR(x);
+  MOE_NEED_PTR(w_router);
+  MOE_NEED_PTR(w_gate);
+  MOE_NEED_PTR(w_up);
+  MOE_NEED_PTR(w_down);
+  MOE_NEED_PTR(out);
+  if (is_8bit(shape)) {
+    MOE_NEED_PTR(s_gate);
+    MOE_NEED_PTR(s_up);
+    MOE_NEED_PTR(s_down);
+  }
+  if (router_bias && !aligned16(router_bias))
+    return fail(MOE_ERR_INVALID_ARG, "%s: router_bias not 16-byte aligned", fn);
+  if (topk_idx_out && !aligned16(topk_idx_out))
+    return fail(MOE_ERR_INVALID_ARG, "%s: topk_idx_out not 16-byte aligned", fn);
+  if (topk_w_out && !aligned16(topk_w_out))
+    return fail(MOE_ERR_INVALID_ARG, "%s: topk_w_out not 16-byte aligned", fn);
+  return MOE_OK;
+}
+
+// The launch sequence of the whole layer on stream s, intermediates in ws
+// (laid out by L).  one_stream: run the grouped FFN's two kernel chains on s
+// alone (no side stream is created or used).
+hipError_t forward_launch(const moe_shape* shape, const void* x, const float* w_router,
+                          const float* router_bias, const void* w_gate, const void* w_up,
+                          const void* w_down, const void* s_gate, const void* s_up,
+                          const void* s_down, void* out, int32_t* topk_idx_out,
+                          float* topk_w_out, uint8_t* ws, const FwdLayout& L, bool one_stream,
+                          hipStream_t s) {
+  const bool fp8 = is_8bit(shape), mx = is_mx(shape);
+  float* logits = reinterpret_cast<float*>(ws + L.logits);
+  int32_t* idx = topk_idx_out ? topk_idx_out : reinterpret_cast<int32_t*>(ws + L.idx);
+  float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + L.w);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  int32_t* dest = reinterpret_cast<int32_t*>(ws + L.dest);
+  int32_t* src_row = reinterpret_cast<int32_t*>(ws + L.src_row);
+  uint8_t* xq = fp8 ? ws + L.xq : nullptr;
+  void* xs = fp8 ? static_cast<void*>(ws + L.xs) : nullptr;
+  void* y_perm = ws + L.y_perm;
+
+  // Router: slice partial sums (or, unsplit, the raw products in the logits
+  // buffer), reduced in slice order by the top-k kernel.
+  const int ks = moe::router_splits(shape->T, shape->H, shape->E);
+  float* parts = ks > 1 ? reinterpret_cast<float*>(ws + L.rpart) : logits;
+  const int nl = n_local(shape);
+  moe::FfnArgs a{shape->T, shape->H, nl, shape->k, shape->I, shape->n_shared, fp8,
+                 offsets, src_row, fp8 ? static_cast<const void*>(xq) : x, xs, w_gate, w_up,
+                 w_down, s_gate, s_up, s_down, y_perm, ws + L.ffn, (long long)shape->T, false, mx};
+  a.one_stream = one_stream;
+  hipError_t e = moe::launch_router_gemm(static_cast<const uint16_t*>(x), w_router, parts,
+                                         shape->T, shape->H, shape->E, s);
+  if (e == hipSuccess)
+    e = moe::launch_topk(parts, ks, router_bias, nullptr, idx, w, shape->T, shape->E, shape->k, s);
+  if (shape->T <= moe::kSmallBatch) {
+    // Small batch: dispatch tables and FFN work lists in one launch.
+    if (e == hipSuccess)
+      e = moe::launch_dispatch_small(idx, counts, offsets, dest, src_row, moe::ffn_schedule(a),
+                                     shape->T, nl, shape->k, shape->n_shared, shape->e_first, s);
+    a.planned = true;
+  } else if (e == hipSuccess) {   // routing tables only: no row copy
+    e = moe::launch_permute(idx, static_cast<const uint16_t*>(x), counts, offsets, dest, src_row,
+                            nullptr, nullptr, reinterpret_cast<int32_t*>(ws + L.tcnt), shape->T,
+                            shape->H, nl, shape->k, shape->n_shared, shape->e_first,
+                            is_share(shape), fp8, mx, s);
+  }
+  if (e == hipSuccess && fp8)
+    e = moe::launch_quantize_rows(static_cast<const uint16_t*>(x), xq, xs, shape->T, shape->H, mx, s);
+  if (e == hipSuccess) e = moe::launch_grouped_ffn(a, s);
+  if (e == hipSuccess)
+    e = moe::launch_combine(static_cast<const uint16_t*>(y_perm), dest, w, offsets + nl,
+                            static_cast<uint16_t*>(out), shape->T, shape->H, shape->k,
+                            shape->n_shared, s);
+  return e;
+}
+
+// ------------------------------------------------ fixed device scratch ----
+// The intermediates of moe_forward_noalloc live in this array, one copy per
+// GPU, held from module load until the process ends.  Nothing in it has to
+// start at zero: every kernel writes what a later one reads.  Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in for
+// the symbol); it passes the device address hipGetSymbolAddress returns,
+// looked up once per device and kept.
+constexpr size_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_current_device(const char* fn, uint8_t** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, fn);
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: device %d beyond the %d the library tracks", fn, dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (p == nullptr || (reinterpret_cast<uintptr_t>(p) & 255u) != 0)
+      return fail(MOE_ERR_HIP, "%s: scratch symbol address %p unusable", fn, p);
+    g_scratch_ptr[dev] = static_cast<uint8_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
 const char* moe_last_error(void) { return g_err; }
 
-int moe_abi_version(void) { return 4; }
+int moe_abi_version(void) { return 5; }
 
 size_t moe_forward_workspace_bytes(const moe_shape* shape) {
   if (check_shape("moe_forward_workspace_bytes", shape, true) != MOE_OK) return 0;
@@ -271,79 +392,44 @@ int moe_forward(const moe_shape* shape, const void* x, const float* w_router,
                 size_t ws_bytes, void* stream) {
   const char* fn = "moe_forward";
   moe::prof_call_begin();
-  if (int rc = check_shape(fn, shape, true)) return rc;
-  if ((long long)shape->T * shape->H * 2 >= (1LL << 32))   // 32-bit row offsets into x
-    return fail(MOE_ERR_UNSUPPORTED, "%s: T*H*2 >= 2^32", fn);
-  const bool fp8 = is_8bit(shape), mx = is_mx(shape);
+  if (int rc = check_forward_args(fn, shape, x, w_router, router_bias, w_gate, w_up, w_down, s_gate,
+                                  s_up, s_down, out, topk_idx_out, topk_w_out))
+    return rc;
   if (shape->T == 0) return MOE_OK;
-  MOE_NEED_PTR(x);
-  MOE_NEED_PTR(w_router);
-  MOE_NEED_PTR(w_gate);
-  MOE_NEED_PTR(w_up);
-  MOE_NEED_PTR(w_down);
-  MOE_NEED_PTR(out);
-  if (fp8) {
-    MOE_NEED_PTR(s_gate);
-    MOE_NEED_PTR(s_up);
-    MOE_NEED_PTR(s_down);
-  }
-  if (router_bias && !aligned16(router_bias))
-    return fail(MOE_ERR_INVALID_ARG, "%s: router_bias not 16-byte aligned", fn);
-  if (topk_idx_out && !aligned16(topk_idx_out))
-    return fail(MOE_ERR_INVALID_ARG, "%s: topk_idx_out not 16-byte aligned", fn);
-  if (topk_w_out && !aligned16(topk_w_out))
-    return fail(MOE_ERR_INVALID_ARG, "%s: topk_w_out not 16-byte aligned", fn);
   const FwdLayout L = fwd_layout(shape);
   if (workspace == nullptr || ws_bytes < L.total)
     return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, L.total);
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return fail(MOE_ERR_INVALID_ARG, "%s: workspace not 256-byte aligned", fn);
+  return hip_status(forward_launch(shape, x, w_router, router_bias, w_gate, w_up, w_down, s_gate,
+                                   s_up, s_down, out, topk_idx_out, topk_w_out,
+                                   static_cast<uint8_t*>(workspace), L, false, as_stream(stream)),
+                    fn);
+}
 
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  float* logits = reinterpret_cast<float*>(ws + L.logits);
-  int32_t* idx = topk_idx_out ? topk_idx_out : reinterpret_cast<int32_t*>(ws + L.idx);
-  float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + L.w);
-  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
-  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
-  int32_t* dest = reinterpret_cast<int32_t*>(ws + L.dest);
-  int32_t* src_row = reinterpret_cast<int32_t*>(ws + L.src_row);
-  uint8_t* xq = fp8 ? ws + L.xq : nullptr;
-  void* xs = fp8 ? static_cast<void*>(ws + L.xs) : nullptr;
-  void* y_perm = ws + L.y_perm;
-  hipStream_t s = as_stream(stream);
-
-  // Router: slice partial sums (or, unsplit, the raw products in the logits
-  // buffer), reduced in slice order by the top-k kernel.
-  const int ks = moe::router_splits(shape->T, shape->H, shape->E);
-  float* parts = ks > 1 ? reinterpret_cast<float*>(ws + L.rpart) : logits;
-  const int nl = n_local(shape);
-  moe::FfnArgs a{shape->T, shape->H, nl, shape->k, shape->I, shape->n_shared, fp8,
-                 offsets, src_row, fp8 ? static_cast<const void*>(xq) : x, xs, w_gate, w_up,
-                 w_down, s_gate, s_up, s_down, y_perm, ws + L.ffn, (long long)shape->T, false, mx};
-  hipError_t e = moe::launch_router_gemm(static_cast<const uint16_t*>(x), w_router, parts,
-                                         shape->T, shape->H, shape->E, s);
-  if (e == hipSuccess)
-    e = moe::launch_topk(parts, ks, router_bias, nullptr, idx, w, shape->T, shape->E, shape->k, s);
-  if (shape->T <= moe::kSmallBatch) {
-    // Small batch: dispatch tables and FFN work lists in one launch.
-    if (e == hipSuccess)
-      e = moe::launch_dispatch_small(idx, counts, offsets, dest, src_row, moe::ffn_schedule(a),
-                                     shape->T, nl, shape->k, shape->n_shared, shape->e_first, s);
-    a.planned = true;
-  } else if (e == hipSuccess) {   // routing tables only: no row copy
-    e = moe::launch_permute(idx, static_cast<const uint16_t*>(x), counts, offsets, dest, src_row,
-                            nullptr, nullptr, reinterpret_cast<int32_t*>(ws + L.tcnt), shape->T,
-                            shape->H, nl, shape->k, shape->n_shared, shape->e_first,
-                            is_share(shape), fp8, mx, s);
-  }
-  if (e == hipSuccess && fp8)
-    e = moe::launch_quantize_rows(static_cast<const uint16_t*>(x), xq, xs, shape->T, shape->H, mx, s);
-  if (e == hipSuccess) e = moe::launch_grouped_ffn(a, s);
-  if (e == hipSuccess)
-    e = moe::launch_combine(static_cast<const uint16_t*>(y_perm), dest, w, offsets + nl,
-                            static_cast<uint16_t*>(out), shape->T, shape->H, shape->k,
-                            shape->n_shared, s);
-  return hip_status(e, fn);
+int moe_forward_noalloc(const moe_shape* shape, const void* x, const float* w_router,
+                        const float* router_bias, const void* w_gate, const void* w_up,
+                        const void* w_down, const void* s_gate, const void* s_up,
+                        const void* s_down, void* out, int32_t* topk_idx_out, float* topk_w_out,
+                        void* stream) {
+  const char* fn = "moe_forward_noalloc";
+  moe::prof_call_begin();
+  if (int rc = check_forward_args(fn, shape, x, w_router, router_bias, w_gate, w_up, w_down, s_gate,
+                                  s_up, s_down, out, topk_idx_out, topk_w_out))
+    return rc;
+  if (shape->T == 0) return MOE_OK;
+  const FwdLayout L = fwd_layout(shape);
+  if (L.total > kScratchBytes)
+    return fail(MOE_ERR_WORKSPACE,
+                "%s: this shape needs %zu bytes of scratch, more than the library's fixed %zu "
+                "(MOE_NOALLOC_SCRATCH_BYTES); call moe_forward with a workspace instead",
+                fn, L.total, (size_t)kScratchBytes);
+  uint8_t* ws = nullptr;
+  if (int rc = scratch_of_current_device(fn, &ws)) return rc;
+  return hip_status(forward_launch(shape, x, w_router, router_bias, w_gate, w_up, w_down, s_gate,
+                                   s_up, s_down, out, topk_idx_out, topk_w_out, ws, L, true,
+                                   as_stream(stream)),
+                    fn);
 }
 
 }  // extern "C"

@@ -668,7 +668,7 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
 
   // No group above the skinny limit: no tiled work, skip its launches (decode).
   const bool tiled = f.max_group_rows > skinny_max_rows(f.T);
-  SideStream* side = tiled && !prof_serial() ? side_stream() : nullptr;
+  SideStream* side = tiled && !prof_serial() && !f.one_stream ? side_stream() : nullptr;
   hipStream_t ts = s;                // stream of the tiled chain
   if (side) {                        // fork after the plan
     hipError_t e = hipEventRecord(side->fork, s);

@@ -90,6 +90,9 @@ struct FfnArgs {
   bool planned;
   // MXFP8 operands (fp8 is then true as well: 8-bit codes).
   bool mx = false;
+  // Run the tiled and the weight-streaming chains on the caller's stream
+  // only (no side stream is created or used).
+  bool one_stream = false;
 };
 size_t ffn_workspace_bytes(int T, int H, int E, int k, int I, int n_shared, bool fp8, bool mx);
 hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s);

@@ -260,6 +260,30 @@ int moe_forward(const moe_shape* shape, const void* x, const float* w_router,
                 void* stream);
 
 /*
+ * moe_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The intermediates live in a fixed array of
+ * MOE_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU, held from
+ * the library's load on that GPU until the process ends; the call itself
+ * allocates and frees nothing, and runs every kernel on `stream` (the
+ * grouped FFN's two kernel chains one after the other, no side stream).
+ * Arguments, layouts and results are those of moe_forward.
+ *   - A shape whose moe_forward_workspace_bytes exceeds
+ *     MOE_NOALLOC_SCRATCH_BYTES returns MOE_ERR_WORKSPACE (nothing launched);
+ *     decode-sized batches fit (e.g. T = 64 tokens, H = 4096, E = 128, k = 8,
+ *     I = 1536 needs about 8 MB).
+ *   - Every call on one GPU uses that GPU's one array, and its contents are
+ *     whatever the last call left: calls that overlap on one GPU (two streams,
+ *     two host threads) race and give undefined results.  Serialise them.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_forward_noalloc(const moe_shape* shape, const void* x, const float* w_router,
+                        const float* router_bias, const void* w_gate, const void* w_up,
+                        const void* w_down, const void* s_gate, const void* s_up,
+                        const void* s_down, void* out, int32_t* topk_idx_out,
+                        float* topk_w_out, void* stream);
+
+/*
  * Measurement hook (not a step of the layer).  After moe_profile_start, the
  * entry-point calls made on this thread record a pair of HIP events on their
  * stream around kernel launches:

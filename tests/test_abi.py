@@ -45,7 +45,7 @@ def test_workspace_alias():
 
 
 def test_abi_version():
-    assert moe.moe_abi_version() == 4
+    assert moe.moe_abi_version() == 5
 
 
 FAKE = 0x10000  # a non-NULL, aligned address; never dereferenced (validation fails first)
@@ -152,3 +152,19 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(b, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         b.lib()
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch():
+    # Checked on the host before any HIP call: the DeepSeek-like layer needs far
+    # more intermediates than the fixed scratch holds; T = 0 is a no-op.
+    P = ctypes.byref
+    big = moe.make_shape(4096, 7168, 256, 8, 2048, 1, "fp8")
+    assert moe.moe_forward_workspace_bytes(big) > moe.NOALLOC_SCRATCH_BYTES
+    args = [FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None]
+    assert _call("moe_forward_noalloc", P(big), *args) == moe.MOE_ERR_WORKSPACE
+    assert "scratch" in moe.moe_last_error()
+    decode = moe.make_shape(64, 4096, 128, 8, 1536)
+    assert moe.moe_forward_workspace_bytes(decode) <= moe.NOALLOC_SCRATCH_BYTES
+    assert _call("moe_forward_noalloc", P(decode), None, *args[1:]) == moe.MOE_ERR_INVALID_ARG
+    assert _call("moe_forward_noalloc", P(moe.make_shape(0, 256, 8, 2, 512)), *([None] * 13)) == moe.MOE_OK
+
