@@ -536,7 +536,7 @@ WsLayout ffn_layout(int T, int H, int E, int k, int I, int n_shared, bool fp8, b
   const long long R = (long long)T * (k + n_shared);
   const int G = E + n_shared;
   const long long big_groups = std::min<long long>(G, R / (skinny_max_rows(T) + 1));
-  L.max_tiles = (int)(R / tile_rows(fp8) + big_groups + 1);
+  L.max_tiles = (int)(R / tile_rows(fp8, mx) + big_groups + 1);
   size_t off = 0;
   L.h = off;        off += align256((size_t)R * I * (fp8 ? 1 : 2));
   // h scales: fp8 one fp32 per 128 channels, mxfp8 one E8M0 byte per 32
@@ -567,7 +567,7 @@ Sched ffn_schedule(const FfnArgs& f) {
   uint8_t* ws = static_cast<uint8_t*>(f.workspace);
   return Sched{reinterpret_cast<int32_t*>(ws + L.n_skinny), reinterpret_cast<int32_t*>(ws + L.n_tiles),
                reinterpret_cast<int32_t*>(ws + L.skinny), reinterpret_cast<int32_t*>(ws + L.tiles),
-               f.E + f.n_shared, tile_rows(f.fp8), skinny_max_rows(f.T)};
+               f.E + f.n_shared, tile_rows(f.fp8, f.mx), skinny_max_rows(f.T)};
 }
 
 size_t ffn_workspace_bytes(int T, int H, int E, int k, int I, int n_shared, bool fp8, bool mx) {
@@ -688,8 +688,11 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
   const char* nm_td = f.mx ? "tiled_down_mx" : f.fp8 ? "tiled_down_fp8" : "tiled_down_bf16";
   up.n_ntile = f.I / 128;
   dn.n_ntile = ceil_div(f.H, 256);
-  if (tiled && run(launch_tiled(nm_tg, f.fp8, f.mx, true, (long long)L.max_tiles * up.n_ntile, up, ts)))
-    run(launch_tiled(nm_td, f.fp8, f.mx, false, (long long)L.max_tiles * dn.n_ntile, dn, ts));
+  auto tiled_gemm = [&](const char* nm, bool dual, const GemmArgs& g) {
+    const long long blocks = (long long)L.max_tiles * g.n_ntile;
+    return f.fp8 ? launch_tiled8(nm, f.mx, dual, blocks, g, ts) : launch_tiled(nm, dual, blocks, g, ts);
+  };
+  if (tiled && run(tiled_gemm(nm_tg, true, up))) run(tiled_gemm(nm_td, false, dn));
 
   // gate/up + SwiGLU, then down, of the groups of at most skinny_max_rows(T) rows
   if (err != hipSuccess) {

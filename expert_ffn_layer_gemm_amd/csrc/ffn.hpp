@@ -14,8 +14,10 @@ namespace moe {
 // 1.51 -> 1.43 ms per step; DeepSeek-like and decode unchanged).
 constexpr int kSkinnyMax = 64;
 __host__ __device__ constexpr int skinny_max_rows(int T) { return T <= kSkinnyMax ? kSkinnyMax : 48; }
-// Rows per tile of the tiled kernel: 256 for bf16, 128 for fp8.
-__host__ __device__ constexpr int tile_rows(bool fp8) { return fp8 ? 128 : 256; }
+// Rows per tile of the tiled kernels: 256 for bf16; 160 for fp8 (a
+// DeepSeek-like routed group of ~128 rows stays in one tile, so its weights
+// are streamed once); 128 for MXFP8 (its B-row scales need the LDS).
+__host__ __device__ constexpr int tile_rows(bool fp8, bool mx) { return mx ? 128 : fp8 ? 160 : 256; }
 
 // Rows per tile of a group of m rows: the group is cut into ceil(m / bm)
 // tiles of equal height (rounded up to 16), so that the tiles of one group,
@@ -110,8 +112,9 @@ struct GemmArgs {
   float* part = nullptr;
 };
 
-// Tiled kernel launch (tiled.hip).
-hipError_t launch_tiled(const char* name, bool fp8, bool mx, bool dual, long long blocks, const GemmArgs& a,
-                        hipStream_t s);
+// Tiled kernel launches: bf16 (tiled.hip), fp8 and MXFP8 (tiled8.hip).
+hipError_t launch_tiled(const char* name, bool dual, long long blocks, const GemmArgs& a, hipStream_t s);
+hipError_t launch_tiled8(const char* name, bool mx, bool dual, long long blocks, const GemmArgs& a,
+                         hipStream_t s);
 
 }  // namespace moe

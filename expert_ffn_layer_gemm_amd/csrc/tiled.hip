@@ -1,36 +1,30 @@
-// LDS-pipelined tiled grouped GEMM for the groups too large for the
-// weight-streaming kernels, more than 48 rows in batches of more than 64
-// tokens (prefill-sized groups, the shared expert, the hot experts of a
+// LDS-pipelined tiled grouped GEMM for bf16 layers, for the groups too large
+// for the weight-streaming kernels, more than 48 rows in batches of more than
+// 64 tokens (prefill-sized groups, the shared expert, the hot experts of a
 // skewed routing).  Computes, per (group, row tile, column tile):
 //   DUAL:   h = silu(X W_gate^T) * (X W_up^T)    128 h columns (256 B rows)
 //   single: y = h W_down^T                        256 output columns
-// with fp32 accumulation; fp8 layers apply the per-row activation scale and
-// the 128x128 weight-block scale to each 128-wide K block's MFMA partial
-// (DeepSeek-deployment page, Quantization), and the DUAL fp8 epilogue
-// re-quantises h per row per 128 channels.  SwiGLU in the epilogue follows the
-// Ironwood page's GMM v2 (section 4.2.2): gate and up are two B streams of
-// one workgroup.
+// with fp32 accumulation.  SwiGLU in the epilogue follows the Ironwood page's
+// GMM v2 (section 4.2.2): gate and up are two B streams of one workgroup.
+// (8-bit layers have a kernel of their own, tiled8.hip.)
 //
 // gfx950 design:
-//   - Row tile BM x 256 staged B rows, 8 waves (2 per SIMD) laid out 2 x 4.
-//     bf16 (compute-bound prefill groups): BM = 256, 128 x 64 per wave, at
-//     128 FLOP per staged byte the operand stream from L2 stays below what
-//     the MFMA rate needs.  fp8 (~128-row expert groups, memory-bound):
-//     BM = 128, 64 x 64 per wave.
-//   - K is staged in 128-byte chunks (64 bf16 / 128 e4m3 per row) by
-//     direct-to-LDS loads (global_load_lds_dwordx4) into two rings: activation
-//     rows and weight rows.  bf16: 2 + 2 stages of 32 KB (one chunk in flight
-//     while one is multiplied; 2 + 3 or 3 + 2 stages measured no faster);
-//     fp8: 3 + 3 stages (16 KB + scales, 32 KB).
-//   - bf16 software pipeline: a wave reads the LDS fragments of the next K
-//     step while its MFMAs of the current one run (A row block i right after
-//     the row block's last MFMA), and the chunk barrier sits inside a chunk's
+//   - Row tile 256 x 256 staged B rows, 8 waves (2 per SIMD) laid out 2 x 4,
+//     128 x 64 per wave: at 128 FLOP per staged byte the operand stream from
+//     L2 stays below what the MFMA rate needs.
+//   - K is staged in 128-byte chunks (64 bf16 per row) by direct-to-LDS loads
+//     (global_load_lds_dwordx4) into two rings, activation rows and weight
+//     rows, of 2 + 2 stages of 32 KB (one chunk in flight while one is
+//     multiplied; 2 + 3 or 3 + 2 stages measured no faster).
+//   - Software pipeline: a wave reads the LDS fragments of the next K step
+//     while its MFMAs of the current one run (A row block i right after the
+//     row block's last MFMA), and the chunk barrier sits inside a chunk's
 //     second K step, after the wave's last read of the chunk and before its
-//     first read of the next.  The direct-to-LDS loads of this path are issued
-//     from inline assembly so the compiler keeps exact lgkm-counter waits for
-//     the interleaved reads (it cannot see a pending LDS write).  Measured
-//     7-12 % faster than reading a step's fragments then waiting, with
-//     bit-identical output (same MFMA order per accumulator).
+//     first read of the next.  The direct-to-LDS loads are issued from inline
+//     assembly so the compiler keeps exact lgkm-counter waits for the
+//     interleaved reads (it cannot see a pending LDS write).  Measured 7-12 %
+//     faster than reading a step's fragments then waiting, with bit-identical
+//     output (same MFMA order per accumulator).
 //   - A direct-to-LDS instruction writes 1 KB contiguously (lane i at +16 i),
 //     8 staged rows; each block of 8 rows lies in A, B0 or B1 and has its own
 //     wave-uniform base.  Each lane fetches global chunk c ^ (row & 7) of its
@@ -55,7 +49,6 @@ namespace {
 
 constexpr int kBRows = 256;                       // staged B rows per tile
 constexpr int kBf16NSA = 2, kBf16NSB = 2;        // bf16 A / B ring stages
-constexpr int kMaxKB = 1024;                      // fp8: K <= 131072 (B scales kept in LDS)
 
 // Slot of 16-byte chunk c of staged row r for rows of RB bytes: 128-byte rows
 // c ^ (r & 7), 64-byte rows c ^ ((r >> 1) & 3) (both measured conflict-free
@@ -89,19 +82,14 @@ __device__ __forceinline__ int b_row(int j, int wn, int r16) {
 
 }  // namespace
 
-// MX (with FP8): MXFP8 operands; the E8M0 scales of each 32-value block of
-// the A and B rows are staged with the chunk and applied by the MFMA.
-template <bool FP8, bool DUAL, int WM, int WN, int BM, int NSA, int NSB, int RB, bool MX = false>
+template <bool DUAL, int WM, int WN, int BM, int NSA, int NSB, int RB>
 __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
   // The body is device code only; the host pass needs just the launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
-  static_assert(RB == 128 || (RB == 64 && !FP8), "fp8 MFMA K step needs 128-byte rows");
-  static_assert(!MX || FP8, "MX operands are 8-bit");
   // A (activation rows) and B (weight rows) have rings of their own: NSA and
-  // NSB stages (bf16 2 + 2, 8-bit 3 + 3).  Each path's vm-counter waits follow
-  // from its issue order: at every chunk boundary A is issued before B.
-  static_assert(NSA >= 2 && NSB >= 2 && (NSB == NSA || NSB == NSA + 1 || (!FP8 && NSA == NSB + 1)),
-                "ring depths");
+  // NSB stages.  The vm-counter waits follow from the issue order: at every
+  // chunk boundary A is issued before B.
+  static_assert(NSA >= 2 && NSB >= 2 && (NSB == NSA || NSB == NSA + 1 || NSA == NSB + 1), "ring depths");
   constexpr int kRB = RB;                         // bytes of K per staged row and chunk
   constexpr int RPB = 1024 / RB;                  // staged rows per 1 KB DMA block
   constexpr int LPR = RB / 16;                    // lanes per staged row
@@ -114,15 +102,10 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
   constexpr int IPWB = B_BYTES / 1024 / NW;
   static_assert(IPWA * NW * 1024 == A_BYTES && IPWB * NW * 1024 == B_BYTES,
                 "a chunk must split evenly over the waves");
-  // Row scales of a chunk, 4 bytes per row (fp8: the fp32 scale of the row's
-  // 128-K block; MX: its 4 E8M0 bytes), one 4-byte DMA per lane; waves >= 4
-  // load duplicates.  MX also stages the B rows' E8M0 dwords after the B data.
-  constexpr int SCALE_BYTES = FP8 ? NW * 256 : 0;
-  constexpr int A_STAGE = A_BYTES + SCALE_BYTES;
-  constexpr int B_STAGE = B_BYTES + (MX ? kBRows * 4 : 0);
+  constexpr int A_STAGE = A_BYTES;
+  constexpr int B_STAGE = B_BYTES;
   constexpr int B_RING = NSA * A_STAGE;           // byte offset of the B ring
-  __shared__ __attribute__((aligned(1024)))
-  uint8_t lds[NSA * A_STAGE + NSB * B_STAGE + (FP8 && !MX ? 2 * kMaxKB * 4 : 0)];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NSA * A_STAGE + NSB * B_STAGE];
 
   int tslot, nt;
   if (!band_item(p.sc.tiles, *p.sc.n_tiles, p.n_ntile, tslot, nt)) return;
@@ -131,9 +114,8 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
   const int gm = p.offsets[g + 1] - p.offsets[g];
   const int mrows = min(group_tile_rows(gm, kBM), gm - m0);
   const int K = p.K, N = p.N;
-  const size_t Kb = FP8 ? (size_t)K : 2 * (size_t)K;
+  const size_t Kb = 2 * (size_t)K;                 // bytes per row
   const int nk = (int)(Kb / kRB);
-  const int KB = K / 128;
   const int tid = threadIdx.x, lane = tid & 63;
   // Wave index as a scalar: keeps every per-wave condition a scalar branch.
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -151,7 +133,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
   const uint8_t* ab[IPWA];
   uint32_t aoff[IPWA];
   bool av[IPWA];
-  int nva = FP8 ? 1 : 0;                           // vm instructions per A chunk of this wave
+  int nva = 0;                                     // vm instructions per A chunk of this wave
 #pragma unroll
   for (int j = 0; j < IPWA; ++j) {
     const int brow0 = (wave * IPWA + j) * RPB;
@@ -179,35 +161,6 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
     // Rows past the matrix (ragged last column tile) re-read its last row.
     boff[j] = (uint32_t)min(n0 + br + lane / LPR, N - 1) * (uint32_t)Kb + sl;
   }
-  const int nvb = IPWB + ((MX && wave < 4) ? 1 : 0);   // vm instructions per B chunk of this wave
-  const uint8_t* ssrc = nullptr;    // this lane's row scales; chunk c at + 4 c bytes
-  const uint8_t* bssrc = nullptr;   // MX: this lane's B row's E8M0 bytes
-  float* bsc = reinterpret_cast<float*>(lds + NSA * A_STAGE + NSB * B_STAGE);   // fp8: [2][KB]
-  if constexpr (MX) {
-    const int sr = row0 + min((wave & 3) * 64 + lane, mrows - 1);
-    ssrc = static_cast<const uint8_t*>(p.A_scale) + (size_t)(p.a_rows ? p.a_rows[sr] : sr) * (K / 32);
-    if (wave < 4) {   // staged B row 64 wave + lane
-      int br = wave * 64 + lane;
-      const uint8_t* sB = static_cast<const uint8_t*>(p.s_B0);
-      if (DUAL && br >= 128) { sB = static_cast<const uint8_t*>(p.s_B1); br -= 128; }
-      bssrc = sB + ((size_t)g * N + min(n0 + br, N - 1)) * (K / 32);
-    }
-  } else if constexpr (FP8) {
-    const int sr = row0 + min((wave & 3) * 64 + lane, mrows - 1);
-    ssrc = reinterpret_cast<const uint8_t*>(static_cast<const float*>(p.A_scale) +
-                                            (size_t)(p.a_rows ? p.a_rows[sr] : sr) * KB);
-    const int N128 = N / 128;
-    for (int i = tid; i < 2 * KB; i += 64 * NW) {
-      const int which = i / KB, kb = i % KB;
-      float v;
-      const float* sB0 = static_cast<const float*>(p.s_B0);
-      const float* sB1 = static_cast<const float*>(p.s_B1);
-      if (DUAL) v = (which ? sB1 : sB0)[((size_t)g * N128 + nt) * KB + kb];
-      else v = sB0[((size_t)g * N128 + min(n0 / 128 + which, N128 - 1)) * KB + kb];
-      bsc[i] = v;
-    }
-  }
-
 
   // 16-row blocks of the wave holding valid rows.
   const int rbase = wm * (kBM / WM);
@@ -221,339 +174,150 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  if constexpr (!FP8) {
-    // bf16: the software-pipelined main loop (file header).  Waves with a
-    // row block past the group's end take the plain loop below, with the
-    // same barriers and loads.
-    static_assert(RB == 128 && MB == 8, "bf16 pipeline layout");
-    // chunk c: A in stage c % NSA of the A ring, B in stage c % NSB of the B ring
-    auto sa = [&](int c) { return lds + (c % NSA) * A_STAGE; };
-    auto sb = [&](int c) { return lds + B_RING + (c % NSB) * B_STAGE; };
-    auto issue_a = [&](int c) { dma_blocks_untracked<IPWA>(sa(c), ab, aoff, av, (size_t)c * kRB, wave); };
-    auto issue_b = [&](int c) { dma_blocks_untracked<IPWB>(sb(c), bb, boff, bv, (size_t)c * kRB, wave); };
-    // Prologue: A chunks 0 .. NSA-1 and B chunks 0 .. NSB-1, A before B per chunk.
+  {
+  // bf16: the software-pipelined main loop (file header).  Waves with a
+  // row block past the group's end take the plain loop below, with the
+  // same barriers and loads.
+  static_assert(RB == 128 && MB == 8, "bf16 pipeline layout");
+  // chunk c: A in stage c % NSA of the A ring, B in stage c % NSB of the B ring
+  auto sa = [&](int c) { return lds + (c % NSA) * A_STAGE; };
+  auto sb = [&](int c) { return lds + B_RING + (c % NSB) * B_STAGE; };
+  auto issue_a = [&](int c) { dma_blocks_untracked<IPWA>(sa(c), ab, aoff, av, (size_t)c * kRB, wave); };
+  auto issue_b = [&](int c) { dma_blocks_untracked<IPWB>(sb(c), bb, boff, bv, (size_t)c * kRB, wave); };
+  // Prologue: A chunks 0 .. NSA-1 and B chunks 0 .. NSB-1, A before B per chunk.
 #pragma unroll
-    for (int c = 0; c < (NSA > NSB ? NSA : NSB); ++c) {
-      if (c < NSA && c < nk) issue_a(c);
-      if (c < NSB && c < nk) issue_b(c);
-    }
-    // Chunk c >= 1 is awaited at the boundary of chunk c - 1.  Loads complete
-    // in issue order, so the wave may leave in flight what it issued after the
-    // later of A(c), B(c): with NSB >= NSA that is A(c) (A(c+1 .. c+NSA-2) and
-    // B(c+1 .. c+NSB-2) follow it), with NSA = NSB + 1 it is B(c)
-    // (A(c+2 .. c+NSA-2) and B(c+1 .. c+NSB-2) follow it); chunks past the
-    // last are never issued.
-    constexpr int XA = NSA <= NSB ? NSA - 2 : NSA - 3;
-    constexpr int XB = NSB - 2;
-    auto wait_chunk = [&](int c) {   // A and B of chunk c landed (this wave's share)
-      const int xa = NSA <= NSB ? min(XA, nk - 1 - c) : min(XA, nk - 2 - c);
-      wait_vmcnt_le<XA * IPWA + XB * IPWB>(max(0, xa) * nva + max(0, min(XB, nk - 1 - c)) * IPWB);
-    };
-    // Chunk 0: the prologue issued A(1 .. NSA-1) and B(1 .. NSB-1) after it.
-    wait_vmcnt_le<(NSA - 1) * IPWA + (NSB - 1) * IPWB>(min(NSA - 1, nk - 1) * nva +
-                                                       min(NSB - 1, nk - 1) * IPWB);
-    lds_barrier();
-    const bool full = active && nmb == MB;
-    auto rd_b = [&](const uint8_t* st, int ks, u32x4_t (&b)[NB]) {
-      const int c = ks * 4 + (lane >> 4);
+  for (int c = 0; c < (NSA > NSB ? NSA : NSB); ++c) {
+    if (c < NSA && c < nk) issue_a(c);
+    if (c < NSB && c < nk) issue_b(c);
+  }
+  // Chunk c >= 1 is awaited at the boundary of chunk c - 1.  Loads complete
+  // in issue order, so the wave may leave in flight what it issued after the
+  // later of A(c), B(c): with NSB >= NSA that is A(c) (A(c+1 .. c+NSA-2) and
+  // B(c+1 .. c+NSB-2) follow it), with NSA = NSB + 1 it is B(c)
+  // (A(c+2 .. c+NSA-2) and B(c+1 .. c+NSB-2) follow it); chunks past the
+  // last are never issued.
+  constexpr int XA = NSA <= NSB ? NSA - 2 : NSA - 3;
+  constexpr int XB = NSB - 2;
+  auto wait_chunk = [&](int c) {   // A and B of chunk c landed (this wave's share)
+    const int xa = NSA <= NSB ? min(XA, nk - 1 - c) : min(XA, nk - 2 - c);
+    wait_vmcnt_le<XA * IPWA + XB * IPWB>(max(0, xa) * nva + max(0, min(XB, nk - 1 - c)) * IPWB);
+  };
+  // Chunk 0: the prologue issued A(1 .. NSA-1) and B(1 .. NSB-1) after it.
+  wait_vmcnt_le<(NSA - 1) * IPWA + (NSB - 1) * IPWB>(min(NSA - 1, nk - 1) * nva +
+                                                     min(NSB - 1, nk - 1) * IPWB);
+  lds_barrier();
+  const bool full = active && nmb == MB;
+  auto rd_b = [&](const uint8_t* st, int ks, u32x4_t (&b)[NB]) {
+    const int c = ks * 4 + (lane >> 4);
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int br = b_row<DUAL, WN, NB>(j, wn, r16);
-        b[j] = lds_read16(st + br * kRB + (slot<RB>(br, c) << 4));
-      }
-    };
-    auto rd_a = [&](const uint8_t* st, int ks, int i) {
-      const int c = ks * 4 + (lane >> 4);
-      const int r = rbase + i * 16 + r16;
-      return lds_read16(st + r * kRB + (slot<RB>(r, c) << 4));
-    };
-    auto boundary = [&](int kc) {   // after every wave's last read of chunk kc
-      if (kc + 1 < nk) wait_chunk(kc + 1);
-      lds_barrier();
-      if (kc + NSA < nk) issue_a(kc + NSA);
-      if (kc + NSB < nk) issue_b(kc + NSB);
-    };
-    if (full) {
-      u32x4_t a[MB], bc[NB], bn[NB];
-      rd_b(sb(0), 0, bc);
-#pragma unroll
-      for (int i = 0; i < MB; ++i) a[i] = rd_a(sa(0), 0, i);
-      // sched_barrier(0) keeps the compiler from regrouping the reads and
-      // MFMAs: each read is issued while the MFMA pipe works on the row block
-      // before it.
-      auto chunk = [&](int kc, auto last_c) {
-        constexpr bool last = decltype(last_c)::value;
-        const uint8_t* st = sa(kc);
-        const uint8_t* sn = sa(kc + 1);
-        const uint8_t* bt = sb(kc);
-        const uint8_t* bnx = sb(kc + 1);
-        // K step 0 of chunk kc; reads of step 1.
-#pragma unroll
-        for (int i = 0; i < MB; ++i) {
-#pragma unroll
-          for (int j = 0; j < NB; ++j) acc[i][j] = mfma_bf16_16x16x32(a[i], bc[j], acc[i][j]);
-          if (i < 2) {
-            const int c = 4 + (lane >> 4);
-#pragma unroll
-            for (int j = 2 * i; j < 2 * i + 2; ++j) {
-              const int br = b_row<DUAL, WN, NB>(j, wn, r16);
-              bn[j] = lds_read16(bt + br * kRB + (slot<RB>(br, c) << 4));
-            }
-          }
-          a[i] = rd_a(st, 1, i);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int j = 0; j < NB; ++j) bc[j] = bn[j];
-        // K step 1: first half, the chunk boundary, then the second half with
-        // the reads of the next chunk's step 0.
-#pragma unroll
-        for (int i = 0; i < MB / 2; ++i) {
-#pragma unroll
-          for (int j = 0; j < NB; ++j) acc[i][j] = mfma_bf16_16x16x32(a[i], bc[j], acc[i][j]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        boundary(kc);
-        if constexpr (!last) {
-          rd_b(bnx, 0, bn);
-#pragma unroll
-          for (int i = 0; i < MB / 2; ++i) a[i] = rd_a(sn, 0, i);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = MB / 2; i < MB; ++i) {
-#pragma unroll
-          for (int j = 0; j < NB; ++j) acc[i][j] = mfma_bf16_16x16x32(a[i], bc[j], acc[i][j]);
-          if constexpr (!last) a[i] = rd_a(sn, 0, i);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int j = 0; j < NB; ++j) bc[j] = bn[j];
-      };
-      for (int kc = 0; kc + 1 < nk; ++kc) chunk(kc, std::false_type{});
-      chunk(nk - 1, std::true_type{});
-    } else {
-      for (int kc = 0; kc < nk; ++kc) {
-        if (active) {
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            u32x4_t b[NB], aa[MB];
-            rd_b(sb(kc), ks, b);
-#pragma unroll
-            for (int i = 0; i < MB; ++i) aa[i] = rd_a(sa(kc), ks, i);
-#pragma unroll
-            for (int i = 0; i < MB; ++i)
-              if (i < nmb) {
-#pragma unroll
-                for (int j = 0; j < NB; ++j) acc[i][j] = mfma_bf16_16x16x32(aa[i], b[j], acc[i][j]);
-              }
-          }
-        }
-        boundary(kc);
-      }
-    }
-  } else {
-    // fp8 / MXFP8: one 128-K chunk is one MFMA K step.  The same skeleton as
-    // bf16: every chunk's loads (data, and the row scales with them) are
-    // issued after the boundary of the chunk NS earlier, and the boundary of
-    // chunk kc (wait for chunk kc+1, barrier, issue chunk kc+NS) comes after
-    // the wave's last read of chunk kc and before its first read of chunk kc+1.
-    static_assert(NSA == NSB && MB == 4, "8-bit ring and wave layout");
-    constexpr int NS = NSA;
-    auto sa = [&](int c) { return lds + (c % NS) * A_STAGE; };
-    auto sb = [&](int c) { return lds + B_RING + (c % NS) * B_STAGE; };
-    auto issue = [&](int c) {
-      dma_blocks_untracked<IPWA>(sa(c), ab, aoff, av, (size_t)c * kRB, wave);
-      dma4_untracked(ssrc + 4 * c, sa(c) + A_BYTES + wave * 256);
-      dma_blocks_untracked<IPWB>(sb(c), bb, boff, bv, (size_t)c * kRB, wave);
-      if (MX && wave < 4) dma4_untracked(bssrc + 4 * c, sb(c) + B_BYTES + wave * 256);
-    };
-    const int nvc = nva + nvb;                       // vm instructions per chunk of this wave
-#pragma unroll
-    for (int c = 0; c < NS; ++c)
-      if (c < nk) issue(c);
-    // Chunk c is followed by chunks c+1 .. c+NS-2 at its boundary's wait
-    // (chunk 0 after the prologue: by chunks 1 .. NS-1).
-    wait_vmcnt_le<(NS - 1) * (IPWA + IPWB + 2)>(min(NS - 1, nk - 1) * nvc);
-    lds_barrier();                                   // also publishes the fp8 B scales
-    auto boundary = [&](int kc) {
-      if (kc + 1 < nk)
-        wait_vmcnt_le<(NS - 2) * (IPWA + IPWB + 2)>(max(0, min(NS - 2, nk - 2 - kc)) * nvc);
-      lds_barrier();
-      if (kc + NS < nk) issue(kc + NS);
-    };
-    // A lane's 32 codes: K positions 16*(lane/16) .. +16 and 64 + 16*(lane/16) .. +16
-    // (the same positions for A and B, so the pairing inside the MFMA is right).
-    const int c0 = lane >> 4, c1 = 4 + (lane >> 4);
-    const int sh = 8 * (lane >> 4);                  // MX: byte of this lane's K block
-    auto rd_frag = [&](const uint8_t* rowp, int row) {
-      const u32x4_t lo = lds_read16(rowp + (slot<RB>(row, c0) << 4));
-      const u32x4_t hi = lds_read16(rowp + (slot<RB>(row, c1) << 4));
-      return i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-    };
-    auto rd_b = [&](int kc, int j) {
+    for (int j = 0; j < NB; ++j) {
       const int br = b_row<DUAL, WN, NB>(j, wn, r16);
-      return rd_frag(sb(kc) + br * kRB, br);
-    };
-    auto rd_bscale = [&](int kc, int j) -> uint32_t {   // MX: E8M0 of the B row's K block
-      const uint32_t* bsw = reinterpret_cast<const uint32_t*>(sb(kc) + B_BYTES);
-      return (bsw[b_row<DUAL, WN, NB>(j, wn, r16)] >> sh) & 0xFFu;
-    };
-    auto rd_a = [&](int kc, int i) {
-      const int r = rbase + i * 16 + r16;
-      return rd_frag(sa(kc) + r * kRB, r);
-    };
-    auto rd_ascale_mx = [&](int kc, int i) -> uint32_t {
-      const uint32_t* asc = reinterpret_cast<const uint32_t*>(sa(kc) + A_BYTES);
-      return (asc[rbase + i * 16 + r16] >> sh) & 0xFFu;
-    };
-    auto rd_ascale = [&](int kc, int i) {               // fp8: rows of the lane's accumulator
-      const float* asc = reinterpret_cast<const float*>(sa(kc) + A_BYTES);
-      return *reinterpret_cast<const f32x4_t*>(asc + rbase + i * 16 + (lane >> 4) * 4);
-    };
-    auto rd_bsc = [&](int kc, float& lo, float& hi) {   // fp8: B block scales of chunk kc
-      lo = DUAL ? bsc[kc] : bsc[(wn * (256 / WN)) / 128 * KB + kc];
-      hi = DUAL ? bsc[KB + kc] : lo;
-    };
-    // fp8: acc += partial * (row scale * block scale), per row block.
-    auto scale_add = [&](int i, const f32x4_t (&pr)[NB], const f32x4_t sa4, float sb_lo, float sb_hi) {
+      b[j] = lds_read16(st + br * kRB + (slot<RB>(br, c) << 4));
+    }
+  };
+  auto rd_a = [&](const uint8_t* st, int ks, int i) {
+    const int c = ks * 4 + (lane >> 4);
+    const int r = rbase + i * 16 + r16;
+    return lds_read16(st + r * kRB + (slot<RB>(r, c) << 4));
+  };
+  auto boundary = [&](int kc) {   // after every wave's last read of chunk kc
+    if (kc + 1 < nk) wait_chunk(kc + 1);
+    lds_barrier();
+    if (kc + NSA < nk) issue_a(kc + NSA);
+    if (kc + NSB < nk) issue_b(kc + NSB);
+  };
+  if (full) {
+    u32x4_t a[MB], bc[NB], bn[NB];
+    rd_b(sb(0), 0, bc);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float s_lo = sa4[q] * sb_lo, s_hi = sa4[q] * sb_hi;
+    for (int i = 0; i < MB; ++i) a[i] = rd_a(sa(0), 0, i);
+    // sched_barrier(0) keeps the compiler from regrouping the reads and
+    // MFMAs: each read is issued while the MFMA pipe works on the row block
+    // before it.
+    auto chunk = [&](int kc, auto last_c) {
+      constexpr bool last = decltype(last_c)::value;
+      const uint8_t* st = sa(kc);
+      const uint8_t* sn = sa(kc + 1);
+      const uint8_t* bt = sb(kc);
+      const uint8_t* bnx = sb(kc + 1);
+      // K step 0 of chunk kc; reads of step 1.
 #pragma unroll
-        for (int j = 0; j < NB; ++j) acc[i][j][q] += pr[j][q] * (j < NB / 2 ? s_lo : s_hi);
-      }
-    };
-    const bool full = active && nmb == MB;
-    if (full) {
-      // Software pipeline: the chunk's A rows 2-3 are read first, then row
-      // blocks 0-1 multiply, the boundary, the next chunk's A rows 0-1 are read
-      // (registers just freed), and row blocks 2-3 multiply column by column
-      // with the next chunk's B fragment j read as soon as column j is done.
-      // (A chunk's stage is refilled right after its boundary, so every value
-      // of it is in registers by then.)  The reads are unconditional: after the
-      // last chunk they read a stale stage (in bounds, never used), which keeps
-      // the loop body one basic block.
-      i32x8_t a[MB], b[NB];
-      uint32_t sam[MB], sbm[NB];                       // MX scales
-      f32x4_t saf[MB];                                 // fp8 row scales
-      float sb_lo = 0.f, sb_hi = 0.f;                  // fp8 block scales
-      auto next_a = [&](int kc, int i) {
-        a[i] = rd_a(kc, i);
-        if constexpr (MX) sam[i] = rd_ascale_mx(kc, i);
-        else saf[i] = rd_ascale(kc, i);
-      };
-      auto next_b = [&](int kc, int j) {
-        b[j] = rd_b(kc, j);
-        if constexpr (MX) sbm[j] = rd_bscale(kc, j);
-      };
+      for (int i = 0; i < MB; ++i) {
 #pragma unroll
-      for (int j = 0; j < NB; ++j) next_b(0, j);
-      next_a(0, 0);
-      next_a(0, 1);
-      if constexpr (!MX) rd_bsc(0, sb_lo, sb_hi);
-      for (int kc = 0; kc < nk; ++kc) {
-        next_a(kc, 2);                                 // used after the boundary
-        next_a(kc, 3);
-        f32x4_t pr[2][2];                              // fp8: partial tiles of two columns of two row blocks
-        // fp8: a partial tile is one MFMA (a chunk is one K step); it is
-        // scaled into the accumulator one column later.
-        auto col = [&](int i0, int j) {
-          if constexpr (MX) {
-            acc[i0][j] = mfma_mx8_16x16x128(a[i0], b[j], acc[i0][j], sam[i0], sbm[j]);
-            acc[i0 + 1][j] = mfma_mx8_16x16x128(a[i0 + 1], b[j], acc[i0 + 1][j], sam[i0 + 1], sbm[j]);
-          } else {
-            pr[j & 1][0] = mfma_fp8_16x16x128(a[i0], b[j], f32x4_t{0.f, 0.f, 0.f, 0.f});
-            pr[j & 1][1] = mfma_fp8_16x16x128(a[i0 + 1], b[j], f32x4_t{0.f, 0.f, 0.f, 0.f});
+        for (int j = 0; j < NB; ++j) acc[i][j] = mfma_bf16_16x16x32(a[i], bc[j], acc[i][j]);
+        if (i < 2) {
+          const int c = 4 + (lane >> 4);
+#pragma unroll
+          for (int j = 2 * i; j < 2 * i + 2; ++j) {
+            const int br = b_row<DUAL, WN, NB>(j, wn, r16);
+            bn[j] = lds_read16(bt + br * kRB + (slot<RB>(br, c) << 4));
           }
-        };
-        auto scale_col = [&](int i0, int j) {            // fp8: acc += partial * scales, column j
-          if constexpr (!MX) {
-#pragma unroll
-            for (int d = 0; d < 2; ++d)
-#pragma unroll
-              for (int q = 0; q < 4; ++q)
-                acc[i0 + d][j][q] += pr[j & 1][d][q] * (saf[i0 + d][q] * (j < NB / 2 ? sb_lo : sb_hi));
-          }
-        };
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          col(0, j);
-          if (j > 0) scale_col(0, j - 1);
         }
-        scale_col(0, NB - 1);
-        // Keep row blocks 0-1 ahead of the boundary (the compiler would sink
-        // them past its wait and barrier otherwise): they run while the wave
-        // waits there.
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < NB; ++j) asm volatile("" : "+v"(acc[i][j]));
-        boundary(kc);
-        next_a(kc + 1, 0);
-        next_a(kc + 1, 1);
+        a[i] = rd_a(st, 1, i);
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          col(2, j);
-          if (j > 0) scale_col(2, j - 1);
-          next_b(kc + 1, j);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        scale_col(2, NB - 1);
-        if constexpr (!MX) rd_bsc(min(kc + 1, nk - 1), sb_lo, sb_hi);
       }
-    } else {
-      for (int kc = 0; kc < nk; ++kc) {
-        if (active) {
-          // Row blocks past the group's end are neither read nor multiplied
-          // (measured 4-6 % faster on ~128-row groups split into two tiles).
-          i32x8_t b[NB];
-          uint32_t sbm[NB];
 #pragma unroll
-          for (int j = 0; j < NB; ++j) {
-            b[j] = rd_b(kc, j);
-            if constexpr (MX) sbm[j] = rd_bscale(kc, j);
-          }
-          float sb_lo = 0.f, sb_hi = 0.f;
-          if constexpr (!MX) rd_bsc(kc, sb_lo, sb_hi);
+      for (int j = 0; j < NB; ++j) bc[j] = bn[j];
+      // K step 1: first half, the chunk boundary, then the second half with
+      // the reads of the next chunk's step 0.
+#pragma unroll
+      for (int i = 0; i < MB / 2; ++i) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = mfma_bf16_16x16x32(a[i], bc[j], acc[i][j]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      boundary(kc);
+      if constexpr (!last) {
+        rd_b(bnx, 0, bn);
+#pragma unroll
+        for (int i = 0; i < MB / 2; ++i) a[i] = rd_a(sn, 0, i);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = MB / 2; i < MB; ++i) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = mfma_bf16_16x16x32(a[i], bc[j], acc[i][j]);
+        if constexpr (!last) a[i] = rd_a(sn, 0, i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) bc[j] = bn[j];
+    };
+    for (int kc = 0; kc + 1 < nk; ++kc) chunk(kc, std::false_type{});
+    chunk(nk - 1, std::true_type{});
+  } else {
+    for (int kc = 0; kc < nk; ++kc) {
+      if (active) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          u32x4_t b[NB], aa[MB];
+          rd_b(sb(kc), ks, b);
+#pragma unroll
+          for (int i = 0; i < MB; ++i) aa[i] = rd_a(sa(kc), ks, i);
 #pragma unroll
           for (int i = 0; i < MB; ++i)
             if (i < nmb) {
-              const i32x8_t a = rd_a(kc, i);
-              if constexpr (MX) {
-                const uint32_t sam = rd_ascale_mx(kc, i);
 #pragma unroll
-                for (int j = 0; j < NB; ++j) acc[i][j] = mfma_mx8_16x16x128(a, b[j], acc[i][j], sam, sbm[j]);
-              } else {
-                f32x4_t pr[NB];
-#pragma unroll
-                for (int j = 0; j < NB; ++j) pr[j] = mfma_fp8_16x16x128(a, b[j], f32x4_t{0.f, 0.f, 0.f, 0.f});
-                scale_add(i, pr, rd_ascale(kc, i), sb_lo, sb_hi);
-              }
+              for (int j = 0; j < NB; ++j) acc[i][j] = mfma_bf16_16x16x32(aa[i], b[j], acc[i][j]);
             }
         }
-        boundary(kc);
       }
+      boundary(kc);
     }
+  }
   }
 
   // Epilogue.  Lane holds rows rbase + 16 i + 4 (lane/16) + q of its blocks.
   // The output tile is assembled in LDS (the ring stages are free once every
-  // wave is past its last read) and written out in 16-byte row pieces: the
-  // lanes' own 1- or 2-byte elements, 4 rows x 16 columns per instruction,
-  // made 8-16x as many store instructions and partial-line writes (measured:
-  // the epilogue took 0.2-0.3 ms of the 8-bit kernels' launches).
-  constexpr int OUT_B = (FP8 && DUAL) ? 1 : 2;       // bytes per output element
+  // wave is past its last read) and written out in 16-byte row pieces rather
+  // than the lanes' own 2-byte elements (8x fewer store instructions, no
+  // partial-line writes).
+  constexpr int OUT_B = 2;                           // bytes per output element (bf16)
   constexpr int OCOLS = DUAL ? 128 : 256;            // output columns per tile
-  constexpr int ROWB = OCOLS * OUT_B;                // bytes per tile row: 128, 256, 512
+  constexpr int ROWB = OCOLS * OUT_B;                // bytes per tile row: 256 or 512
   constexpr int NCH = ROWB / 16;                     // 16-byte pieces per row
-  // fp8: per-row maxima of h exchanged across the WN waves of a row block.
-  constexpr int AMAX_BYTES = (FP8 && DUAL && !MX) ? WN * kBM * 4 : 0;
-  static_assert(AMAX_BYTES + kBM * ROWB <= (int)sizeof(lds), "output tile fits in LDS");
-  float* amax_s = reinterpret_cast<float*>(lds);     // [WN][kBM]
-  uint8_t* const tile = lds + AMAX_BYTES;
+  static_assert(kBM * ROWB <= (int)sizeof(lds), "output tile fits in LDS");
+  uint8_t* const tile = lds;
   // Piece (r, c / (16 / OUT_B)) sits at piece index c16 ^ (r % NCH): the
   // 4 rows a store instruction covers (4 apart) fall on different banks.
   auto tile_at = [&](int r, int c) {
@@ -561,76 +325,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
     return tile + r * ROWB + ((((byte >> 4) ^ (r % NCH))) << 4) + (byte & 15);
   };
   lds_barrier();                                      // every wave is past its last stage read
-  if constexpr (MX && DUAL) {
-    // The wave's 32 h columns are one MX block of each of its rows: row
-    // maxima by a 16-lane reduction, then E8M0 and codes.
-    constexpr int NH = NB / 2;
-    static_assert(NH * 16 == 32, "one MX block of h per wave");
-    const int N32 = N / 32;
-    const int hc0 = n0 + wn * (128 / WN);
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = rbase + i * 16 + (lane >> 4) * 4 + q;
-        float hv[NH], am = 0.f;
-#pragma unroll
-        for (int j = 0; j < NH; ++j) {
-          hv[j] = silu_mul(acc[i][j][q], acc[i][j + NH][q]);
-          am = fmaxf(am, fabsf(hv[j]));
-        }
-        am = row16_max(am);
-        if (i < nmb && r < mrows) {
-          const uint32_t e8 = mx_e8m0(am);
-          const float inv = mx_inv_scale(e8);
-#pragma unroll
-          for (int j = 0; j < NH; ++j) {
-            const float qv = fminf(fmaxf(hv[j] * inv, -448.f), 448.f);
-            *tile_at(r, wn * (128 / WN) + j * 16 + r16) = (uint8_t)f32_to_e4m3(qv);
-          }
-          if (r16 == 0) static_cast<uint8_t*>(p.out_scale)[(size_t)(row0 + r) * N32 + hc0 / 32] = (uint8_t)e8;
-        }
-      }
-  } else if constexpr (FP8 && DUAL) {
-    constexpr int NH = NB / 2;                        // gate (= up) blocks per wave
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = rbase + i * 16 + (lane >> 4) * 4 + q;
-        float am = 0.f;
-#pragma unroll
-        for (int j = 0; j < NH; ++j) {
-          const float h = (i < nmb && r < mrows) ? silu_mul(acc[i][j][q], acc[i][j + NH][q]) : 0.f;
-          acc[i][j][q] = h;
-          am = fmaxf(am, fabsf(h));
-        }
-        am = row16_max(am);
-        if (r16 == 0) amax_s[wn * kBM + r] = am;
-      }
-    lds_barrier();
-    const int N128 = N / 128;
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-      if (i < nmb) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r = rbase + i * 16 + (lane >> 4) * 4 + q;
-          if (r < mrows) {
-            float am = 0.f;
-#pragma unroll
-            for (int w = 0; w < WN; ++w) am = fmaxf(am, amax_s[w * kBM + r]);
-            const float scale = am == 0.f ? 1.f : am / 448.f;
-#pragma unroll
-            for (int j = 0; j < NH; ++j) {
-              const float qv = fminf(fmaxf(acc[i][j][q] / scale, -448.f), 448.f);
-              *tile_at(r, wn * (128 / WN) + j * 16 + r16) = (uint8_t)f32_to_e4m3(qv);
-            }
-            if (wn == 0 && r16 == 0) static_cast<float*>(p.out_scale)[(size_t)(row0 + r) * N128 + nt] = scale;
-          }
-        }
-      }
-  } else if (active) {
+  if (active) {
 #pragma unroll
     for (int i = 0; i < MB; ++i)
       if (i < nmb) {
@@ -666,19 +361,14 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
 #endif
 }
 
-hipError_t launch_tiled(const char* name, bool fp8, bool mx, bool dual, long long blocks,
-                        const GemmArgs& a, hipStream_t s) {
+hipError_t launch_tiled(const char* name, bool dual, long long blocks, const GemmArgs& a, hipStream_t s) {
   if (blocks <= 0) return hipSuccess;
   const dim3 grid((unsigned)band_grid(blocks, 1));
-  // bf16 (compute-bound prefill groups): 256-row tiles, 2 + 2 stages.  fp8
-  // (memory-bound ~128-row groups): 128-row tiles, 3 stages, two chunks in
-  // flight.  The row counts match tile_rows() used by the schedule.
-  if (mx && dual) MOE_LAUNCH(name, (k_tiled3<true, true, 2, 4, 128, 3, 3, 128, true>), grid, dim3(512), 0, s, a);
-  else if (mx) MOE_LAUNCH(name, (k_tiled3<true, false, 2, 4, 128, 3, 3, 128, true>), grid, dim3(512), 0, s, a);
-  else if (fp8 && dual) MOE_LAUNCH(name, (k_tiled3<true, true, 2, 4, 128, 3, 3, 128>), grid, dim3(512), 0, s, a);
-  else if (fp8) MOE_LAUNCH(name, (k_tiled3<true, false, 2, 4, 128, 3, 3, 128>), grid, dim3(512), 0, s, a);
-  else if (dual) MOE_LAUNCH(name, (k_tiled3<false, true, 2, 4, 256, kBf16NSA, kBf16NSB, 128>), grid, dim3(512), 0, s, a);
-  else MOE_LAUNCH(name, (k_tiled3<false, false, 2, 4, 256, kBf16NSA, kBf16NSB, 128>), grid, dim3(512), 0, s, a);
+  // 256-row tiles (compute-bound prefill groups), 2 + 2 stages.  The row
+  // count matches tile_rows() used by the schedule.
+  static_assert(tile_rows(false, false) == 256, "bf16 tile height");
+  if (dual) MOE_LAUNCH(name, (k_tiled3<true, 2, 4, 256, kBf16NSA, kBf16NSB, 128>), grid, dim3(512), 0, s, a);
+  else MOE_LAUNCH(name, (k_tiled3<false, 2, 4, 256, kBf16NSA, kBf16NSB, 128>), grid, dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

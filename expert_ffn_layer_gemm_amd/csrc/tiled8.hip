@@ -1,0 +1,507 @@
+// LDS-pipelined tiled grouped GEMM for 8-bit layers (e4m3 codes with fp32
+// 128 x 128 block scales, or MXFP8 with E8M0 scales per 32 values), for the
+// groups too large for the weight-streaming kernels.  Per (group, row tile,
+// column tile) it computes
+//   DUAL:   h = silu(X W_gate^T) * (X W_up^T)    128 h columns, re-quantised
+//   single: y = h W_down^T                        256 output columns, bf16
+// with fp32 accumulation.  fp8: each 128-wide K block's MFMA partial is scaled
+// by the row's activation scale times the weight block's scale ("Lower latency
+// and higher throughput with multi-node DeepSeek deployment", Quantization);
+// MXFP8: the E8M0 scales ride the scaled MFMA ("Hosting Qwen on Blackwell",
+// Quantization).  SwiGLU in the epilogue follows the Ironwood page's GMM v2
+// (section 4.2.2): gate and up are two B streams of one workgroup.
+//
+// gfx950 design.  These layers are memory-bound (a ~128-row expert group
+// reads 29 MB of weights for 7.5 GFLOP), and what bounds them is the number of
+// L1 -> L2 requests a CU has in flight (rocprofv3 on the DeepSeek-like layer:
+// about 80 outstanding requests per CU, whatever the bytes per request), so
+// the kernel is built to issue few, full-line requests:
+//   - Row tile BM (128 or 160) x 256 staged B rows, 8 waves (2 per SIMD) laid
+//     out 2 x 4; K staged in 128-byte chunks (one 16x16x128 MFMA step) by
+//     direct-to-LDS loads of whole 128-byte row pieces into a 3-stage A ring
+//     and a 3-stage B ring (two chunks in flight while one is multiplied).
+//     A 160-row tile keeps a DeepSeek-like routed group (mean 128 rows) in
+//     one tile, so its weights are streamed once.
+//   - Scales travel in groups of SG chunks: every SG-th chunk, the first
+//     waves load, per A row (and per B row for MX, or the two weight-block
+//     scale rows for fp8), the scales of the next SG chunks with one 16-byte
+//     request (SG = 4) instead of one 4-byte request per row and chunk; a
+//     scale stage is reused SG chunks later, so NSS = ceil((NS + SG - 1) / SG)
+//     stages suffice.
+//   - Chunk c's loads are issued after the boundary of chunk c - NS (the
+//     workgroup barrier that ends every wave's reads of those stages), one
+//     part between each two columns of the second half's MFMAs; each wave
+//     waits with explicit vm-counter counts (its own loads land in issue
+//     order), then an LDS-only barrier publishes the chunk.
+//   - Software pipeline: a wave reads the A fragments of the second half of
+//     its row blocks before the boundary, multiplies the first half, passes
+//     the boundary, reads the next chunk's A fragments of the first half, and
+//     multiplies the second half column by column, reading the next chunk's B
+//     fragment j as soon as column j is done.  Row blocks past the group's end
+//     are neither read nor multiplied (uniform branches).
+//   - A direct-to-LDS instruction writes 1 KB (8 staged rows of 128 B; lane i
+//     at +16 i); row r's 16-byte piece c sits in slot c ^ (r & 7), which makes
+//     the fragment reads (16 lanes on 16 rows, one piece) conflict-free.
+//   - XCD-contiguous block numbering and band order as in the bf16 kernel.
+#include "ffn.hpp"
+#include "pipe.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int k8BRows = 256;   // staged B rows per tile
+constexpr int k8NS = 3;        // ring stages of A and of B
+
+// Direct-to-LDS load of `BYTES` (4 or 16) bytes per lane from the lane's own
+// address: lane i writes dst + BYTES * i.  Issued from inline assembly, like
+// dma16_untracked (the caller orders it with vm-counter waits and barriers).
+template <int BYTES>
+__device__ __forceinline__ void dma_addr_untracked(const void* src, uint8_t* dst) {
+  const uint32_t la = (uint32_t)(size_t)(lds_ptr_t)dst;
+  if constexpr (BYTES == 16)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(la), "v"(src) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                 :: "s"(la), "v"(src) : "memory", "m0");
+}
+
+// Staged B row of 16-column block j (lane row r16) for wave column wn
+// (4 wave columns, 4 blocks each).
+template <bool DUAL>
+__device__ __forceinline__ int b8_row(int j, int wn, int r16) {
+  if constexpr (DUAL) return (j < 2 ? wn * 32 + j * 16 : 128 + wn * 32 + (j - 2) * 16) + r16;
+  return wn * 64 + j * 16 + r16;
+}
+
+}  // namespace
+
+// LDS bytes of one configuration (static: checked against the 160 KB limit).
+template <bool MX, int BM, int SG>
+struct Tiled8Lds {
+  static constexpr int A_BYTES = BM * 128;
+  static constexpr int B_BYTES = k8BRows * 128;
+  static constexpr int SROWS = MX ? BM + k8BRows : BM + 2;   // scale rows of a stage
+  static constexpr int SB = 4 * SG;                           // bytes per scale row and stage
+  static constexpr int SSTAGE = (SROWS * SB + 255) / 256 * 256;
+  static constexpr int NSS = (k8NS + SG - 1 + SG - 1) / SG;  // scale stages
+  static constexpr int TOTAL = k8NS * A_BYTES + k8NS * B_BYTES + NSS * SSTAGE;
+};
+
+template <bool MX, bool DUAL, int BM, int SG>
+__global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using L = Tiled8Lds<MX, BM, SG>;
+  static_assert(L::TOTAL <= 160 * 1024, "LDS budget");
+  static_assert(SG == 1 || SG == 4, "16-byte or 4-byte scale loads");
+  constexpr int NS = k8NS;
+  constexpr int NW = 8, WN = 4;
+  constexpr int MB = BM / 32;                       // 16-row blocks per wave (2 wave rows)
+  constexpr int NB = 4;                             // 16-column blocks per wave
+  constexpr int HA = MB / 2;                        // row blocks multiplied before the boundary
+  constexpr int A_BLK = BM / 8;                     // 1 KB DMA blocks of an A chunk
+  constexpr int IPWA = (A_BLK + NW - 1) / NW;
+  constexpr int IPWB = L::B_BYTES / 1024 / NW;
+  constexpr int NSC = (L::SROWS + 63) / 64;         // waves that load scales
+  static_assert(NSC <= NW, "scale rows");
+  static_assert(IPWB == NB && IPWA <= NB, "one load part per column");
+  constexpr int B_RING = NS * L::A_BYTES;
+  constexpr int S_RING = B_RING + NS * L::B_BYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[L::TOTAL];
+
+  int tslot, nt;
+  if (!band_item(p.sc.tiles, *p.sc.n_tiles, p.n_ntile, tslot, nt)) return;
+  const int g = p.sc.tiles[4 * tslot], m0 = p.sc.tiles[4 * tslot + 1];
+  const int row0 = p.offsets[g] + m0;
+  const int gm = p.offsets[g + 1] - p.offsets[g];
+  const int mrows = min(group_tile_rows(gm, BM), gm - m0);
+  const int K = p.K, N = p.N;
+  const int nk = K / 128;
+  const int KB = K / 128;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int n0 = nt * (DUAL ? 128 : 256);
+  const int ncols = DUAL ? 128 : min(256, N - n0);
+  const int r16 = lane & 15;
+
+  // A DMA blocks of this wave: block a = wave * IPWA + j holds tile rows
+  // 8a .. 8a+7; blocks past the tile or wholly past the group's end are not
+  // fetched (their rows are never stored).
+  const uint8_t* ab[IPWA];
+  uint32_t aoff[IPWA];
+  bool av[IPWA];
+  int nva = 0;
+#pragma unroll
+  for (int j = 0; j < IPWA; ++j) {
+    const int blk = wave * IPWA + j;
+    const int row = blk * 8 + lane / 8;
+    const uint32_t sl = (uint32_t)(slot8(row, lane % 8) * 16);
+    av[j] = blk < A_BLK && blk * 8 < mrows;
+    const int r = min(row, mrows - 1);
+    ab[j] = p.a_rows ? p.A : p.A + (size_t)row0 * K;
+    aoff[j] = (p.a_rows ? (uint32_t)p.a_rows[row0 + r] : (uint32_t)r) * (uint32_t)K + sl;
+    nva += av[j] ? 1 : 0;
+  }
+  const uint8_t* bb[IPWB];
+  uint32_t boff[IPWB];
+#pragma unroll
+  for (int j = 0; j < IPWB; ++j) {
+    int br = (wave * IPWB + j) * 8;
+    const uint8_t* B = p.B0;
+    if (DUAL && br >= 128) { B = p.B1; br -= 128; }
+    const int row = (wave * IPWB + j) * 8 + lane / 8;
+    const uint32_t sl = (uint32_t)(slot8(row, lane % 8) * 16);
+    bb[j] = B + (size_t)g * N * K;
+    // Rows past the matrix (ragged last column tile) re-read its last row.
+    boff[j] = (uint32_t)min(n0 + br + lane / 8, N - 1) * (uint32_t)K + sl;
+  }
+
+  // Scale row of this lane (waves < NSC): srow < BM the A row's scales;
+  // fp8: srow = BM, BM+1 the two weight-block scale rows of the tile (DUAL:
+  // gate, up; single: the tile's two 128-column blocks); MX: srow = BM + b
+  // the E8M0 row of staged B row b.  A stage holds SB bytes per scale row:
+  // chunks SG*q .. SG*q+SG-1 of the row's scales (4 bytes per chunk).
+  const int srow = wave * 64 + lane;
+  const bool s_lane = wave < NSC && srow < L::SROWS;
+  const uint8_t* ssrc = nullptr;
+  if (s_lane) {
+    const int N128 = N / 128;
+    if (srow < BM) {
+      const int r = row0 + min(srow, mrows - 1);
+      const size_t ar = (size_t)(p.a_rows ? p.a_rows[r] : r);
+      ssrc = static_cast<const uint8_t*>(p.A_scale) + ar * (size_t)(4 * KB);
+    } else if constexpr (MX) {
+      int br = srow - BM;
+      const uint8_t* sB = static_cast<const uint8_t*>(p.s_B0);
+      if (DUAL && br >= 128) { sB = static_cast<const uint8_t*>(p.s_B1); br -= 128; }
+      ssrc = sB + ((size_t)g * N + min(n0 + br, N - 1)) * (size_t)(K / 32);
+    } else {
+      const int which = srow - BM;
+      if (DUAL)
+        ssrc = static_cast<const uint8_t*>(which ? p.s_B1 : p.s_B0) +
+               ((size_t)g * N128 + nt) * (size_t)(4 * KB);
+      else
+        ssrc = static_cast<const uint8_t*>(p.s_B0) +
+               ((size_t)g * N128 + min(n0 / 128 + which, N128 - 1)) * (size_t)(4 * KB);
+    }
+  }
+
+  auto sa = [&](int c) { return lds + (c % NS) * L::A_BYTES; };
+  auto sbs = [&](int c) { return lds + B_RING + (c % NS) * L::B_BYTES; };
+  auto ss = [&](int c) { return lds + S_RING + ((c / SG) % L::NSS) * L::SSTAGE; };
+  const bool scale_wave = wave < NSC;
+  // vm instructions this wave issues for chunk c
+  auto ops = [&](int c) { return nva + IPWB + ((scale_wave && c % SG == 0) ? 1 : 0); };
+  auto issue = [&](int c) {
+    if (scale_wave && c % SG == 0) {
+      if (s_lane) dma_addr_untracked<4 * SG>(ssrc + (size_t)c * 4, ss(c) + wave * 64 * L::SB);
+    }
+#pragma unroll
+    for (int j = 0; j < IPWA; ++j)
+      if (av[j]) dma16_untracked(ab[j] + (size_t)c * 128, aoff[j], sa(c) + (wave * IPWA + j) * 1024);
+#pragma unroll
+    for (int j = 0; j < IPWB; ++j)
+      dma16_untracked(bb[j] + (size_t)c * 128, boff[j], sbs(c) + (wave * IPWB + j) * 1024);
+  };
+  constexpr int OPS_MAX = IPWA + IPWB + 1;
+#pragma unroll
+  for (int c = 0; c < NS; ++c)
+    if (c < nk) issue(c);
+  {
+    int later = 0;   // issued after chunk 0
+#pragma unroll
+    for (int c = 1; c < NS; ++c)
+      if (c < nk) later += ops(c);
+    wait_vmcnt_le<(NS - 1) * OPS_MAX>(later);
+  }
+  lds_barrier();
+  // Boundary of chunk kc (after this wave's last read of it): wait for chunk
+  // kc+1 (loads issued after it: chunks kc+2 .. kc+NS-1), barrier, then
+  // issue chunk kc+NS into the stages chunk kc used.
+  auto boundary = [&](int kc) {
+    if (kc + 1 < nk) {
+      int later = 0;
+#pragma unroll
+      for (int c = kc + 2; c < kc + NS; ++c)
+        if (c < nk) later += ops(c);
+      wait_vmcnt_le<(NS - 2) * OPS_MAX>(later);
+    }
+    lds_barrier();
+  };
+  // Part j (of NB) of chunk c's loads: the scale load with part 0, A block j
+  // (if any), B block j.  Chunk kc+NS's parts are issued between the columns
+  // of chunk kc's second half (after its boundary, so its stages are free):
+  // spread out, not as one burst after the barrier (measured 5 % faster on
+  // the DeepSeek-like layer, same output bits).
+  auto issue_part = [&](int c, int j) {
+    if (j == 0 && scale_wave && c % SG == 0) {
+      if (s_lane) dma_addr_untracked<4 * SG>(ssrc + (size_t)c * 4, ss(c) + wave * 64 * L::SB);
+    }
+    if (j < IPWA) {
+      const int ja = j < IPWA ? j : 0;
+      if (av[ja]) dma16_untracked(ab[ja] + (size_t)c * 128, aoff[ja], sa(c) + (wave * IPWA + ja) * 1024);
+    }
+    dma16_untracked(bb[j] + (size_t)c * 128, boff[j], sbs(c) + (wave * IPWB + j) * 1024);
+  };
+
+  // Valid 16-row blocks of this wave (0 for a wave without columns).
+  const int rbase = wm * (BM / 2);
+  const bool has_cols = DUAL || wn * 64 < ncols;
+  const int nmb = has_cols ? max(0, min(MB, ceil_div(mrows - rbase, 16))) : 0;
+
+  f32x4_t acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // A lane's 32 codes: K bytes 16*(lane/16) .. +16 and 64 + 16*(lane/16) .. +16
+  // (the same positions for A and B, so the pairing inside the MFMA is right).
+  const int c0 = lane >> 4, c1 = 4 + (lane >> 4);
+  const int sh = 8 * (lane >> 4);                  // MX: byte of this lane's K block
+  auto rd_frag = [&](const uint8_t* rowp, int row) {
+    const u32x4_t lo = lds_read16(rowp + (slot8(row, c0) << 4));
+    const u32x4_t hi = lds_read16(rowp + (slot8(row, c1) << 4));
+    return i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                   (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+  auto sword = [&](int kc, int r) {                  // scale dword of scale row r, chunk kc
+    return *reinterpret_cast<const uint32_t*>(ss(kc) + r * L::SB + (kc % SG) * 4);
+  };
+
+  i32x8_t a[MB], b[NB];
+  uint32_t sam[MB], sbm[NB];                       // MX: E8M0 bytes
+  f32x4_t saf[MB];                                 // fp8: activation scales of the lane's 4 rows
+  float sb_lo = 0.f, sb_hi = 0.f;                  // fp8: weight block scales
+  auto next_a = [&](int kc, int i) {
+    const int r = rbase + i * 16 + r16;
+    a[i] = rd_frag(sa(kc) + r * 128, r);
+    if constexpr (MX) {
+      sam[i] = (sword(kc, r) >> sh) & 0xFFu;
+    } else {
+      const int rr = rbase + i * 16 + (lane >> 4) * 4;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) saf[i][q] = __uint_as_float(sword(kc, rr + q));
+    }
+  };
+  auto next_b = [&](int kc, int j) {
+    const int br = b8_row<DUAL>(j, wn, r16);
+    b[j] = rd_frag(sbs(kc) + br * 128, br);
+    if constexpr (MX) sbm[j] = (sword(kc, BM + br) >> sh) & 0xFFu;
+  };
+  auto rd_bsc = [&](int kc) {
+    if constexpr (!MX) {
+      const float s0 = __uint_as_float(sword(kc, BM)), s1 = __uint_as_float(sword(kc, BM + 1));
+      sb_lo = DUAL ? s0 : (wn < 2 ? s0 : s1);
+      sb_hi = DUAL ? s1 : sb_lo;
+    }
+  };
+
+  // Partial tiles of the current column for the row blocks of one half.
+  constexpr int HMAX = MB - HA;
+  f32x4_t pr[2][HMAX];
+  auto col = [&](int i0, int i1, int j) {          // MFMAs of row blocks [i0, i1) with B block j
+#pragma unroll
+    for (int i = i0; i < i1; ++i)
+      if (i < nmb) {
+        if constexpr (MX) acc[i][j] = mfma_mx8_16x16x128(a[i], b[j], acc[i][j], sam[i], sbm[j]);
+        else pr[j & 1][i - i0] = mfma_fp8_16x16x128(a[i], b[j], f32x4_t{0.f, 0.f, 0.f, 0.f});
+      }
+  };
+  auto scale_col = [&](int i0, int i1, int j) {    // fp8: acc += partial * (row scale * block scale)
+    if constexpr (!MX) {
+      const float sbv = j < NB / 2 ? sb_lo : sb_hi;
+#pragma unroll
+      for (int i = i0; i < i1; ++i)
+        if (i < nmb) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[i][j][q] += pr[j & 1][i - i0][q] * (saf[i][q] * sbv);
+        }
+    }
+  };
+
+  // Prologue reads: chunk 0's B fragments, A of the first half, block scales.
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+    if (nmb > 0) next_b(0, j);
+#pragma unroll
+  for (int i = 0; i < HA; ++i)
+    if (i < nmb) next_a(0, i);
+  rd_bsc(0);
+  for (int kc = 0; kc < nk; ++kc) {
+    // A fragments of the second half (the stage is refilled at the boundary).
+#pragma unroll
+    for (int i = HA; i < MB; ++i)
+      if (i < nmb) next_a(kc, i);
+    // First half: row blocks [0, HA), column by column; a column's partials
+    // are scaled into the accumulators one column later.
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      col(0, HA, j);
+      if (j > 0) scale_col(0, HA, j - 1);
+    }
+    scale_col(0, HA, NB - 1);
+    // Keep the first half ahead of the boundary (the compiler would sink it
+    // past the wait and barrier otherwise): it runs while the wave waits.
+#pragma unroll
+    for (int i = 0; i < HA; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) asm volatile("" : "+v"(acc[i][j]));
+    boundary(kc);
+    const bool more = kc + 1 < nk;
+    // The next chunk's A fragments of the first half (registers just freed).
+#pragma unroll
+    for (int i = 0; i < HA; ++i)
+      if (more && i < nmb) next_a(kc + 1, i);
+    __builtin_amdgcn_sched_barrier(0);
+    // Second half, column by column; B fragment j of the next chunk is read
+    // as soon as column j is done.
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      col(HA, MB, j);
+      if (kc + NS < nk) issue_part(kc + NS, j);
+      if (j > 0) scale_col(HA, MB, j - 1);
+      if (more && nmb > 0) next_b(kc + 1, j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    scale_col(HA, MB, NB - 1);
+    if (more) rd_bsc(kc + 1);
+  }
+
+  // Epilogue.  Lane holds rows rbase + 16 i + 4 (lane/16) + q of its blocks.
+  // The output tile is assembled in LDS (the ring stages are free once every
+  // wave is past its last read) and written out in 16-byte row pieces.
+  constexpr int OUT_B = DUAL ? 1 : 2;                // bytes per output element
+  constexpr int OCOLS = DUAL ? 128 : 256;            // output columns per tile
+  constexpr int ROWB = OCOLS * OUT_B;                // bytes per tile row: 128 or 512
+  constexpr int NCH = ROWB / 16;                     // 16-byte pieces per row
+  constexpr int AMAX_BYTES = (DUAL && !MX) ? WN * BM * 4 : 0;
+  static_assert(AMAX_BYTES + BM * ROWB <= L::TOTAL, "output tile fits in LDS");
+  float* amax_s = reinterpret_cast<float*>(lds);     // [WN][BM]
+  uint8_t* const tile = lds + AMAX_BYTES;
+  auto tile_at = [&](int r, int c) {
+    const int byte = c * OUT_B;
+    return tile + r * ROWB + ((((byte >> 4) ^ (r % NCH))) << 4) + (byte & 15);
+  };
+  lds_barrier();                                      // every wave is past its last stage read
+  if constexpr (MX && DUAL) {
+    // The wave's 32 h columns are one MX block of each of its rows.
+    const int N32 = N / 32;
+    const int hc0 = n0 + wn * 32;
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = rbase + i * 16 + (lane >> 4) * 4 + q;
+        float hv[2], am = 0.f;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          hv[j] = silu_mul(acc[i][j][q], acc[i][j + 2][q]);
+          am = fmaxf(am, fabsf(hv[j]));
+        }
+        am = row16_max(am);
+        if (i < nmb && r < mrows) {
+          const uint32_t e8 = mx_e8m0(am);
+          const float inv = mx_inv_scale(e8);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const float qv = fminf(fmaxf(hv[j] * inv, -448.f), 448.f);
+            *tile_at(r, wn * 32 + j * 16 + r16) = (uint8_t)f32_to_e4m3(qv);
+          }
+          if (r16 == 0) static_cast<uint8_t*>(p.out_scale)[(size_t)(row0 + r) * N32 + hc0 / 32] = (uint8_t)e8;
+        }
+      }
+  } else if constexpr (DUAL) {
+    // h = silu(g) * u; per-row maxima over the tile's 128 columns (4 waves).
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = rbase + i * 16 + (lane >> 4) * 4 + q;
+        float am = 0.f;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const float h = (i < nmb && r < mrows) ? silu_mul(acc[i][j][q], acc[i][j + 2][q]) : 0.f;
+          acc[i][j][q] = h;
+          am = fmaxf(am, fabsf(h));
+        }
+        am = row16_max(am);
+        if (r16 == 0) amax_s[wn * BM + r] = am;
+      }
+    lds_barrier();
+    const int N128 = N / 128;
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+      if (i < nmb) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = rbase + i * 16 + (lane >> 4) * 4 + q;
+          if (r < mrows) {
+            float am = 0.f;
+#pragma unroll
+            for (int w = 0; w < WN; ++w) am = fmaxf(am, amax_s[w * BM + r]);
+            const float scale = am == 0.f ? 1.f : am / 448.f;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const float qv = fminf(fmaxf(acc[i][j][q] / scale, -448.f), 448.f);
+              *tile_at(r, wn * 32 + j * 16 + r16) = (uint8_t)f32_to_e4m3(qv);
+            }
+            if (wn == 0 && r16 == 0) static_cast<float*>(p.out_scale)[(size_t)(row0 + r) * N128 + nt] = scale;
+          }
+        }
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+      if (i < nmb) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = rbase + i * 16 + (lane >> 4) * 4 + q;
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+            *reinterpret_cast<uint16_t*>(tile_at(r, wn * 64 + j * 16 + r16)) =
+                (uint16_t)f32_to_bf16_bits(acc[i][j][q]);
+        }
+      }
+  }
+  lds_barrier();
+  // Rows past the group's end and columns past the matrix are not written.
+  const int nch = ncols * OUT_B / 16;
+  uint8_t* const out = p.out + ((size_t)row0 * N + n0) * OUT_B;
+  for (int idx = tid; idx < mrows * NCH; idx += 64 * NW) {
+    const int r = idx / NCH, ch = idx % NCH;
+    if (ch < nch)
+      *reinterpret_cast<u32x4_t*>(out + (size_t)r * N * OUT_B + ch * 16) =
+          *reinterpret_cast<const u32x4_t*>(tile + r * ROWB + ((ch ^ (r % NCH)) << 4));
+  }
+#else
+  (void)p;
+#endif
+}
+
+hipError_t launch_tiled8(const char* name, bool mx, bool dual, long long blocks, const GemmArgs& a,
+                         hipStream_t s) {
+  if (blocks <= 0) return hipSuccess;
+  const dim3 grid((unsigned)band_grid(blocks, 1));
+  // Scales in groups of 4 chunks when a row's scale array splits into 16-byte
+  // pieces (K a multiple of 512), else one 4-byte load per chunk.
+  const bool g4 = a.K % 512 == 0;
+  if (mx) {
+    static_assert(tile_rows(true, true) == 128, "MXFP8 tile height");
+    if (dual) {
+      if (g4) MOE_LAUNCH(name, (k_tiled8<true, true, 128, 4>), grid, dim3(512), 0, s, a);
+      else MOE_LAUNCH(name, (k_tiled8<true, true, 128, 1>), grid, dim3(512), 0, s, a);
+    } else {
+      if (g4) MOE_LAUNCH(name, (k_tiled8<true, false, 128, 4>), grid, dim3(512), 0, s, a);
+      else MOE_LAUNCH(name, (k_tiled8<true, false, 128, 1>), grid, dim3(512), 0, s, a);
+    }
+  } else {
+    static_assert(tile_rows(true, false) == 160, "fp8 tile height");
+    if (dual) MOE_LAUNCH(name, (k_tiled8<false, true, 160, 1>), grid, dim3(512), 0, s, a);
+    else MOE_LAUNCH(name, (k_tiled8<false, false, 160, 1>), grid, dim3(512), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -3,9 +3,9 @@
 
 The tiled kernels issue their direct-to-LDS loads from inline assembly that
 writes M0 (the LDS destination) itself; the compiler is told M0 is clobbered
-but may not save a live M0 value around it.  This test compiles tiled.hip for
-gfx950 and checks that in every tiled kernel M0 is written only by those
-sequences (s_mov_b32 m0, s_nop 0, a direct-to-LDS load) and read only by the
+but may not save a live M0 value around it.  This test compiles tiled.hip and
+tiled8.hip for gfx950 and checks that in every tiled kernel M0 is written only
+by those sequences (s_mov_b32 m0, s_nop 0, a direct-to-LDS load) and read only by the
 direct-to-LDS load that follows each write."""
 import os
 import re
@@ -20,15 +20,17 @@ HIPCC = shutil.which("hipcc") or ("/opt/rocm/bin/hipcc" if os.path.exists("/opt/
 
 
 @pytest.mark.skipif(HIPCC is None, reason="hipcc not available")
-def test_tiled_kernels_use_m0_only_for_their_direct_to_lds_loads(tmp_path):
-    out = tmp_path / "tiled.s"
+@pytest.mark.parametrize("src,pattern,n_min", [("tiled.hip", r"_ZN3moe8k_tiled3\w+", 2),
+                                               ("tiled8.hip", r"_ZN3moe8k_tiled8\w+", 6)])
+def test_tiled_kernels_use_m0_only_for_their_direct_to_lds_loads(tmp_path, src, pattern, n_min):
+    out = tmp_path / (src + ".s")
     cmd = [HIPCC, *build.HIPCC_FLAGS, "--cuda-device-only", "-S",
-           os.path.join(build.CSRC, "tiled.hip"), "-o", str(out)]
+           os.path.join(build.CSRC, src), "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     asm = out.read_text()
-    kernels = re.findall(r"^(_ZN3moe8k_tiled3\w+):", asm, flags=re.M)
-    assert len(kernels) >= 6
+    kernels = re.findall(r"^(" + pattern + r"):", asm, flags=re.M)
+    assert len(kernels) >= n_min
     for name in kernels:
         body = asm[asm.index(name + ":"):]
         body = body[:body.index(".Lfunc_end")]
