@@ -79,7 +79,7 @@ size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 // forward path never builds x_perm: the GEMMs gather their rows through
 // src_row from x (bf16) or from x quantised once per token (fp8, mxfp8: xq, xs).
 struct FwdLayout {
-  size_t logits, rpart, idx, w, counts, offsets, tcnt, dest, src_row, xq, xs, y_perm, ffn, total;
+  size_t logits, rpart, idx, w, counts, offsets, tcnt, tick, dest, src_row, xq, xs, y_perm, ffn, total;
 };
 
 FwdLayout fwd_layout(const moe_shape* s) {
@@ -95,6 +95,7 @@ FwdLayout fwd_layout(const moe_shape* s) {
   L.counts = off;  off += align256(G * 4);
   L.offsets = off; off += align256((G + 1) * 4);
   L.tcnt = off;    off += align256(moe::permute_workspace_bytes(s->T, n_local(s)));
+  L.tick = off;    off += 256;          // ticket counter of the small-batch routing + dispatch
   L.dest = off;    off += align256(T * k * 4);
   L.src_row = off; off += align256(R * 4);
   L.xq = off;      off += fp8 ? align256(T * H) : 0;
@@ -166,23 +167,30 @@ hipError_t forward_launch(const moe_shape* shape, const void* x, const float* w_
                  offsets, src_row, fp8 ? static_cast<const void*>(xq) : x, xs, w_gate, w_up,
                  w_down, s_gate, s_up, s_down, y_perm, ws + L.ffn, (long long)shape->T, false, mx};
   a.one_stream = one_stream;
+  const bool small = shape->T <= moe::kSmallBatch;
+  int32_t* tick = reinterpret_cast<int32_t*>(ws + L.tick);
   hipError_t e = moe::launch_router_gemm(static_cast<const uint16_t*>(x), w_router, parts,
-                                         shape->T, shape->H, shape->E, s);
-  if (e == hipSuccess)
-    e = moe::launch_topk(parts, ks, router_bias, nullptr, idx, w, shape->T, shape->E, shape->k, s);
-  if (shape->T <= moe::kSmallBatch) {
-    // Small batch: dispatch tables and FFN work lists in one launch.
+                                         shape->T, shape->H, shape->E, s, small ? tick : nullptr);
+  if (small) {
+    // Small batch: top-k, dispatch tables and FFN work lists in one launch.
     if (e == hipSuccess)
-      e = moe::launch_dispatch_small(idx, counts, offsets, dest, src_row, moe::ffn_schedule(a),
-                                     shape->T, nl, shape->k, shape->n_shared, shape->e_first, s);
+      e = moe::launch_route_dispatch_small(parts, ks, router_bias, idx, w, counts, offsets, dest,
+                                           src_row, moe::ffn_schedule(a), shape->T, shape->E,
+                                           shape->k, nl, shape->n_shared, shape->e_first, tick,
+                                           static_cast<const uint16_t*>(x), xq, xs, shape->H, fp8,
+                                           mx, s);
     a.planned = true;
-  } else if (e == hipSuccess) {   // routing tables only: no row copy
-    e = moe::launch_permute(idx, static_cast<const uint16_t*>(x), counts, offsets, dest, src_row,
-                            nullptr, nullptr, reinterpret_cast<int32_t*>(ws + L.tcnt), shape->T,
-                            shape->H, nl, shape->k, shape->n_shared, shape->e_first,
-                            is_share(shape), fp8, mx, s);
+  } else {
+    if (e == hipSuccess)
+      e = moe::launch_topk(parts, ks, router_bias, nullptr, idx, w, shape->T, shape->E, shape->k, s);
+    // Routing tables only: no row copy.
+    if (e == hipSuccess)
+      e = moe::launch_permute(idx, static_cast<const uint16_t*>(x), counts, offsets, dest, src_row,
+                              nullptr, nullptr, reinterpret_cast<int32_t*>(ws + L.tcnt), shape->T,
+                              shape->H, nl, shape->k, shape->n_shared, shape->e_first,
+                              is_share(shape), fp8, mx, s);
   }
-  if (e == hipSuccess && fp8)
+  if (e == hipSuccess && fp8 && !small)   // (small batches: quantised in the routing launch)
     e = moe::launch_quantize_rows(static_cast<const uint16_t*>(x), xq, xs, shape->T, shape->H, mx, s);
   if (e == hipSuccess) e = moe::launch_grouped_ffn(a, s);
   if (e == hipSuccess)

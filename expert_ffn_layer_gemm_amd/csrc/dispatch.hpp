@@ -165,4 +165,51 @@ __device__ __forceinline__ void plan_groups(const int32_t* offsets, const Sched&
   if (tid == 0) *sc.n_tiles = nt_total;
 }
 
+// Quantisation of one bf16 row of H channels (src) into e4m3 codes (dst) by
+// the threads tid = 0 .. nthreads-1 (nthreads a multiple of 64, consecutive
+// lanes of whole waves), 8 channels per thread and step.
+//   fp8 (MX = false): per 128-channel group, scale = amax / 448 (1 for an
+//     all-zero group) into scale_row[group] (float); 16 lanes cover a group,
+//     the group maximum is a 16-lane DPP reduction;
+//   MXFP8 (MX = true): per 32-channel block, E8M0 = max(biased exponent of
+//     amax - 8, 0) into scale_row[block] (byte), codes of v * 2^-(E8M0 - 127);
+//     4 lanes cover a block.
+// Codes round to nearest even after clamping to +-448.
+template <bool MX>
+__device__ __forceinline__ void quantize_row(const uint16_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                             void* __restrict__ scale_row, int H, int tid, int nthreads) {
+  const int chunks = H / 8;
+  const u32x4_t* s8 = reinterpret_cast<const u32x4_t*>(src);
+  for (int c = tid; c < chunks; c += nthreads) {
+    float v[8];
+    unpack_bf16x8(s8[c], v);
+    float amax = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(v[q]));
+    uint32_t lo = 0, hi = 0;
+    if constexpr (MX) {
+      amax = wave_max_xor(amax, 4);
+      const uint32_t e8 = mx_e8m0(amax);
+      const float inv = mx_inv_scale(e8);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint32_t code = f32_to_e4m3(fminf(fmaxf(v[q] * inv, -448.f), 448.f));
+        if (q < 4) lo |= code << (8 * q); else hi |= code << (8 * (q - 4));
+      }
+      if ((c & 3) == 0) static_cast<uint8_t*>(scale_row)[c / 4] = (uint8_t)e8;
+    } else {
+      amax = row16_max(amax);
+      const float scale = amax == 0.f ? 1.f : amax / 448.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float qv = fminf(fmaxf(v[q] / scale, -448.f), 448.f);
+        const uint32_t code = f32_to_e4m3(qv);
+        if (q < 4) lo |= code << (8 * q); else hi |= code << (8 * (q - 4));
+      }
+      if ((c & 15) == 0) static_cast<float*>(scale_row)[c / 16] = scale;
+    }
+    *reinterpret_cast<uint2*>(dst + c * 8) = make_uint2(lo, hi);
+  }
+}
+
 }  // namespace moe

@@ -37,8 +37,10 @@ bool prof_serial();
 // router_workspace_bytes() is the size of parts when KS > 1, else 0.
 int router_splits(int T, int H, int E);
 size_t router_workspace_bytes(int T, int H, int E);
+// zero_ctr (optional): a counter the kernel sets to 0 (read by the next
+// launch on the stream, the small-batch routing + dispatch kernel).
 hipError_t launch_router_gemm(const uint16_t* x, const float* w, float* parts, int T, int H, int E,
-                              hipStream_t s);
+                              hipStream_t s, int32_t* zero_ctr = nullptr);
 // Logits = sum of the KS partial planes in order (+ bias), written to
 // logits_out when non-null (may alias parts when KS == 1), then top-k.
 hipError_t launch_topk(const float* parts, int KS, const float* bias, float* logits_out,
@@ -97,13 +99,19 @@ struct FfnArgs {
 size_t ffn_workspace_bytes(int T, int H, int E, int k, int I, int n_shared, bool fp8, bool mx);
 hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s);
 
-// small.hip: histogram, offsets, ranks and the FFN work lists of a batch of
-// at most kSmallBatch tokens (k <= 16) in one single-workgroup launch.
+// small.hip: top-k of a batch of at most kSmallBatch tokens (k <= 16) from the
+// router's slice partials (8-bit layers: and x quantised per token into xq,
+// xs), then histogram, offsets, ranks and the FFN work lists, in one launch (tickets: a counter zeroed by the preceding router
+// GEMM on the same stream).  E_all: experts scored; E: routed experts held
+// here (global ids e_first ..).
 struct Sched;
 Sched ffn_schedule(const FfnArgs& a);   // the work lists inside a's workspace
 constexpr int kSmallBatch = 256;
-hipError_t launch_dispatch_small(const int32_t* idx, int32_t* counts, int32_t* offsets,
-                                 int32_t* dest, int32_t* src_row, const Sched& sc, int T, int E,
-                                 int k, int n_shared, int e_first, hipStream_t s);
+hipError_t launch_route_dispatch_small(const float* parts, int KS, const float* bias, int32_t* idx,
+                                       float* w, int32_t* counts, int32_t* offsets, int32_t* dest,
+                                       int32_t* src_row, const Sched& sc, int T, int E_all, int k,
+                                       int E, int n_shared, int e_first, int32_t* tickets,
+                                       const uint16_t* x, uint8_t* xq, void* xs, int H, bool fp8,
+                                       bool mx, hipStream_t s);
 
 }  // namespace moe

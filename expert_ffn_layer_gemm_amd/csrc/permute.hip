@@ -136,37 +136,18 @@ __global__ __launch_bounds__(256) void k_gather_bf16(const int32_t* __restrict__
 }
 
 // x_perm[r] = e4m3 codes of x[src_row[r]] (x[r] when src_row is null) per
-// 128-channel group, scale = amax/448.  16 lanes cover one group (8 bf16
-// each); the group max is a 16-lane xor reduction.
+// 128-channel group, scale = amax/448 (quantize_row<false>).
 __global__ __launch_bounds__(256) void k_gather_fp8(const int32_t* __restrict__ src_row,
                                                     const uint16_t* __restrict__ x,
                                                     uint8_t* __restrict__ x_perm,
                                                     float* __restrict__ x_scale, int R, int H,
                                                     const int32_t* __restrict__ n_rows) {
-  const int chunks = H / 8;
   R = gather_rows(R, n_rows);
   for (int rr = 0; rr < kGatherRows; ++rr) {
     const int r = blockIdx.x * kGatherRows + rr;
     if (r >= R) return;
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + (size_t)(src_row ? src_row[r] : r) * H);
-    for (int c = threadIdx.x; c < chunks; c += 256) {
-      float v[8];
-      unpack_bf16x8(src[c], v);
-      float amax = 0.f;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(v[q]));
-      amax = row16_max(amax);
-      const float scale = amax == 0.f ? 1.f : amax / 448.f;
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float qv = fminf(fmaxf(v[q] / scale, -448.f), 448.f);
-        const uint32_t code = f32_to_e4m3(qv);
-        if (q < 4) lo |= code << (8 * q); else hi |= code << (8 * (q - 4));
-      }
-      *reinterpret_cast<uint2*>(x_perm + (size_t)r * H + c * 8) = make_uint2(lo, hi);
-      if ((c & 15) == 0) x_scale[(size_t)r * (H / 128) + c / 16] = scale;
-    }
+    quantize_row<false>(x + (size_t)(src_row ? src_row[r] : r) * H, x_perm + (size_t)r * H,
+                        x_scale + (size_t)r * (H / 128), H, threadIdx.x, 256);
   }
 }
 
@@ -175,38 +156,18 @@ size_t permute_workspace_bytes(int T, int E) {
 }
 
 // x_perm[r] = MXFP8 codes of x[src_row[r]] (x[r] when src_row is null):
-// blocks of 32 channels, 4 lanes of 8 bf16 each; the block maximum is a
-// 4-lane xor reduction, E8M0 = max(biased exponent of amax - 8, 0), codes =
-// e4m3 of v * 2^-(E8M0 - 127) rounded to nearest even, saturated at 448.
+// blocks of 32 channels (quantize_row<true>).
 __global__ __launch_bounds__(256) void k_gather_mx(const int32_t* __restrict__ src_row,
                                                    const uint16_t* __restrict__ x,
                                                    uint8_t* __restrict__ x_perm,
                                                    uint8_t* __restrict__ x_scale, int R, int H,
                                                    const int32_t* __restrict__ n_rows) {
-  const int chunks = H / 8;
   R = gather_rows(R, n_rows);
   for (int rr = 0; rr < kGatherRows; ++rr) {
     const int r = blockIdx.x * kGatherRows + rr;
     if (r >= R) return;
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + (size_t)(src_row ? src_row[r] : r) * H);
-    for (int c = threadIdx.x; c < chunks; c += 256) {
-      float v[8];
-      unpack_bf16x8(src[c], v);
-      float amax = 0.f;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(v[q]));
-      amax = wave_max_xor(amax, 4);
-      const uint32_t e8 = mx_e8m0(amax);
-      const float inv = mx_inv_scale(e8);
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const uint32_t code = f32_to_e4m3(fminf(fmaxf(v[q] * inv, -448.f), 448.f));
-        if (q < 4) lo |= code << (8 * q); else hi |= code << (8 * (q - 4));
-      }
-      *reinterpret_cast<uint2*>(x_perm + (size_t)r * H + c * 8) = make_uint2(lo, hi);
-      if ((c & 3) == 0) x_scale[(size_t)r * (H / 32) + c / 4] = (uint8_t)e8;
-    }
+    quantize_row<true>(x + (size_t)(src_row ? src_row[r] : r) * H, x_perm + (size_t)r * H,
+                       x_scale + (size_t)r * (H / 32), H, threadIdx.x, 256);
   }
 }
 

@@ -73,8 +73,9 @@ __device__ __forceinline__ void rt_dma(uint8_t* lds, int c, const uint8_t* const
 __global__ __launch_bounds__(512) void k_router_tiled(const uint16_t* __restrict__ x,
                                                       const float* __restrict__ w,
                                                       float* __restrict__ parts, int T, int H,
-                                                      int E, int KS) {
+                                                      int E, int KS, int32_t* zero_ctr) {
 #if defined(__HIP_DEVICE_COMPILE__)
+  if (zero_ctr && threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) *zero_ctr = 0;
   constexpr int WN = 4, MB = kRtTM / 2 / 16, NB = kRtTE / WN / 16;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kRtNS * kRtStage];
   const int t0 = blockIdx.x * kRtTM, e0 = blockIdx.y * kRtTE, ks = blockIdx.z;
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(512) void k_router_tiled(const uint16_t* __restrict
         if (t < T && e < E) out[(size_t)t * E + e] = acc[i][j][q];
       }
 #else
-  (void)x; (void)w; (void)parts; (void)T; (void)H; (void)E; (void)KS;
+  (void)x; (void)w; (void)parts; (void)T; (void)H; (void)E; (void)KS; (void)zero_ctr;
 #endif
 }
 
@@ -220,10 +221,11 @@ size_t router_workspace_bytes(int T, int H, int E) {
 }
 
 hipError_t launch_router_gemm(const uint16_t* x, const float* w, float* parts, int T, int H, int E,
-                              hipStream_t s) {
+                              hipStream_t s, int32_t* zero_ctr) {
   const int ks = router_splits(T, H, E);
   dim3 grid(ceil_div(T, kRtTM), ceil_div(E, kRtTE), ks);
-  MOE_LAUNCH("router_gemm", k_router_tiled, grid, dim3(64 * kRtWaves), 0, s, x, w, parts, T, H, E, ks);
+  MOE_LAUNCH("router_gemm", k_router_tiled, grid, dim3(64 * kRtWaves), 0, s, x, w, parts, T, H, E, ks,
+             zero_ctr);
   return hipGetLastError();
 }
 
