@@ -154,7 +154,8 @@ CPU_MIN_S, CPU_MAX_REPS = 10.0, 16     # oracle timing: >= ~10 s of CPU work, bo
 CPU_TOKENS = {"tiny": 64, "qwen3_235b_decode": 64, "qwen3_235b_prefill": 8192,
               "qwen35_397b_zipf": 1024, "deepseek_v3_fp8": 4096,
               "qwen3_235b_decode_mxfp8": 64, "qwen3_235b_prefill_mxfp8": 8192,
-              "qwen3_235b_decode_ep8": 64, "qwen3_235b_prefill_ep4": 8192}
+              "qwen3_235b_decode_ep8": 64, "qwen3_235b_prefill_ep4": 8192,
+              "deepseek_v3_decode_ep16": 64, "qwen3_235b_decode_mxfp8_ep8": 64}
 DEFAULT_CONFIG = "deepseek_v3_fp8"
 OTHER_CONFIGS = ("tiny", "qwen3_235b_decode", "qwen3_235b_prefill", "qwen35_397b_zipf")
 

@@ -192,6 +192,49 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
   *reinterpret_cast<uint2*>(out + (size_t)r * N + c) = make_uint2(lo, hi);
 }
 
+// Split-K reduce of an 8-bit gate/up GEMM: h = silu(sum of gate planes) *
+// (sum of up planes), planes added in order, then h quantised per row like
+// the one-pass epilogue: fp8 (MX = false) per 128 columns (scale = amax /
+// 448, 32 threads of 4 columns per group), MXFP8 per 32 columns (E8M0, 8
+// threads per block).  Rows below *n_rows; 4 columns per thread.
+template <bool MX>
+__global__ __launch_bounds__(256) void k_splitk_reduce_q8(const float* __restrict__ part, int ksplit,
+                                                          int R, int N, const int32_t* __restrict__ n_rows,
+                                                          uint8_t* __restrict__ out, void* __restrict__ out_scale) {
+  const int r = blockIdx.y;
+  if (r >= *n_rows) return;
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 4;   // N is a multiple of 128: whole groups per block
+  if (c >= N) return;
+  const int NP = 2 * N;
+  float4 a = *reinterpret_cast<const float4*>(part + (size_t)r * NP + c);
+  float4 b = *reinterpret_cast<const float4*>(part + (size_t)r * NP + N + c);
+  for (int s2 = 1; s2 < ksplit; ++s2) {
+    const float* pl = part + ((size_t)s2 * R + r) * NP;
+    const float4 x = *reinterpret_cast<const float4*>(pl + c);
+    const float4 y = *reinterpret_cast<const float4*>(pl + N + c);
+    a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+    b.x += y.x; b.y += y.y; b.z += y.z; b.w += y.w;
+  }
+  float h[4] = {silu_mul(a.x, b.x), silu_mul(a.y, b.y), silu_mul(a.z, b.z), silu_mul(a.w, b.w)};
+  float am = fmaxf(fmaxf(fabsf(h[0]), fabsf(h[1])), fmaxf(fabsf(h[2]), fabsf(h[3])));
+  uint32_t word = 0;
+  if constexpr (MX) {
+    am = wave_max_xor(am, 8);
+    const uint32_t e8 = mx_e8m0(am);
+    const float inv = mx_inv_scale(e8);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) word |= f32_to_e4m3(fminf(fmaxf(h[q] * inv, -448.f), 448.f)) << (8 * q);
+    if ((c & 31) == 0) static_cast<uint8_t*>(out_scale)[(size_t)r * (N / 32) + c / 32] = (uint8_t)e8;
+  } else {
+    am = wave_max_xor(am, 32);
+    const float scale = am == 0.f ? 1.f : am / 448.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) word |= f32_to_e4m3(fminf(fmaxf(h[q] / scale, -448.f), 448.f)) << (8 * q);
+    if ((c & 127) == 0) static_cast<float*>(out_scale)[(size_t)r * (N / 128) + c / 128] = scale;
+  }
+  *reinterpret_cast<uint32_t*>(out + (size_t)r * N + c) = word;
+}
+
 // ----------------------------------------------------------- skinny, fp8 ----
 // Same scheme with the e4m3 16x16x128 MFMA: one MFMA per 128-wide K block;
 // lane l supplies 32 codes at K offset 32*(l/16).  The block partial is scaled
@@ -202,7 +245,10 @@ template <bool DUAL, int NW, int MB>
 __global__ __launch_bounds__(64 * NW) void k_skinny_fp8(const GemmArgs p) {
   __shared__ float row_amax[NW][16 * MB];
   int slot, nt;
-  if (!band_item(p.sc.skinny, *p.sc.n_skinny, p.n_ntile, slot, nt)) return;
+  // Split-K as in the bf16 kernel: block b sums K range b % ksplit of work
+  // item b / ksplit (whole 128-K scale blocks) into fp32 partials.
+  const int ks = blockIdx.x % p.ksplit;
+  if (!band_item(p.sc.skinny, *p.sc.n_skinny, p.n_ntile, slot, nt, blockIdx.x / p.ksplit)) return;
   const int g = p.sc.skinny[4 * slot], s0 = p.sc.skinny[4 * slot + 1];
   const int row0 = p.offsets[g] + s0, m = min(16 * MB, p.offsets[g + 1] - row0);
   const int nmb = ceil_div(m, 16);
@@ -211,6 +257,7 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_fp8(const GemmArgs p) {
   const int K = p.K, N = p.N, KB = K / 128;
   const int n0 = (nt * NW + wave) * 16;
   const int nblk = n0 / 128;
+  const int KBc = KB / p.ksplit, kb0 = ks * KBc;   // this block's 128-K blocks
 
   const uint8_t* b0 = p.B0 + ((size_t)g * N + n0 + r16) * K + kq;
   const uint8_t* b1 = DUAL ? p.B1 + ((size_t)g * N + n0 + r16) * K + kq : nullptr;
@@ -238,10 +285,10 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_fp8(const GemmArgs p) {
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc0[mb] = acc1[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  i32x8_t cur0 = *reinterpret_cast<const i32x8_t*>(b0), cur1{};
-  if (DUAL) cur1 = *reinterpret_cast<const i32x8_t*>(b1);
-  for (int kb = 0; kb < KB; ++kb) {
-    const bool more = kb + 1 < KB;
+  i32x8_t cur0 = *reinterpret_cast<const i32x8_t*>(b0 + kb0 * 128), cur1{};
+  if (DUAL) cur1 = *reinterpret_cast<const i32x8_t*>(b1 + kb0 * 128);
+  for (int kb = kb0; kb < kb0 + KBc; ++kb) {
+    const bool more = kb + 1 < kb0 + KBc;
     i32x8_t nxt0{}, nxt1{};
     if (more) {
       nxt0 = *reinterpret_cast<const i32x8_t*>(b0 + (kb + 1) * 128);
@@ -264,6 +311,24 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_fp8(const GemmArgs p) {
         }
       }
     if (more) { cur0 = nxt0; if (DUAL) cur1 = nxt1; }
+  }
+
+  if (p.ksplit > 1) {   // fp32 partials of this K range: gate | up, or the columns
+    const int NP = DUAL ? 2 * N : N;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      if (mb < nmb) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = mb * 16 + (lane >> 4) * 4 + q;
+          if (r < m) {
+            float* o = p.part + ((size_t)ks * p.R + row0 + r) * NP + n0 + r16;
+            o[0] = acc0[mb][q];
+            if (DUAL) o[N] = acc1[mb][q];
+          }
+        }
+      }
+    return;
   }
 
   if constexpr (DUAL) {
@@ -380,13 +445,17 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_mx(const GemmArgs p) {
   constexpr int NB = NM * CB;               // B streams per lane: [matrix][column block]
   __shared__ float row_amax[NW][16];
   int slot, nt;
-  if (!band_item(p.sc.skinny, *p.sc.n_skinny, p.n_ntile, slot, nt)) return;
+  // Split-K: block b sums 128-K blocks [kb0, kb0 + KBc) of work item
+  // b / ksplit (kb0 a multiple of 4, so the 16-byte scale loads stay aligned).
+  const int ks = blockIdx.x % p.ksplit;
+  if (!band_item(p.sc.skinny, *p.sc.n_skinny, p.n_ntile, slot, nt, blockIdx.x / p.ksplit)) return;
   const int g = p.sc.skinny[4 * slot], s0 = p.sc.skinny[4 * slot + 1];
   const int row0 = p.offsets[g] + s0, m = min(16, p.offsets[g + 1] - row0);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, q4 = lane >> 4;
   const int K = p.K, N = p.N, KB = K / 128, K32 = K / 32;
   const int n0 = (nt * NW + wave) * 16 * CB;
+  const int KBc = KB / p.ksplit, kb0 = ks * KBc;
 
   // Per-lane stream bases: codes at the lane's 16-byte offset; scale rows.
   const uint8_t* bp[NB];
@@ -408,10 +477,11 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_mx(const GemmArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t mxs[];
   const int RS = K32 + 16;
   if constexpr (SM == 2) {
+    // Only the 16-byte pieces of this block's K range (4 K blocks each).
     constexpr int BR = NW * NB * 16;
-    const int c16 = K32 / 16, total = (BR + 16) * c16;
+    const int c_lo = kb0 / 4, c16 = KBc / 4, total = (BR + 16) * c16;
     for (int idx = threadIdx.x; idx < total; idx += 64 * NW) {
-      const int R = idx / c16, cc = idx % c16;
+      const int R = idx / c16, cc = c_lo + idx % c16;
       const uint8_t* src;
       if (R < BR) {
         const int w = R / (NB * 16), j = (R / 16) % NB, r = R % 16;
@@ -433,11 +503,12 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_mx(const GemmArgs p) {
   // Block kb's codes in (da, db); loads past the last block re-read it
   // (cache hits, never multiplied), which keeps them unconditional.
   i32x8_t da, db[NB], xa, xb[NB];
-  mx_load<NB>(da, db, 0, aok, arow, bp);
+  const int kb1 = kb0 + KBc;                // end of this block's K range
+  mx_load<NB>(da, db, kb0, aok, arow, bp);
   u32x4_t sv[NB + 1];
-  if constexpr (VEC) mx_load_scales<NB>(sv, 0, sarow, sbrow);
-  for (int kb = 0; kb < KB; ++kb) {
-    mx_load<NB>(xa, xb, min(kb + 1, KB - 1), aok, arow, bp);
+  if constexpr (VEC) mx_load_scales<NB>(sv, kb0 / 4, sarow, sbrow);
+  for (int kb = kb0; kb < kb1; ++kb) {
+    mx_load<NB>(xa, xb, min(kb + 1, kb1 - 1), aok, arow, bp);
     uint32_t sa, sb[NB];
     if constexpr (SM == 2) {
       sa = lsa[4 * kb];
@@ -456,10 +527,24 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_mx(const GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[j] = mfma_mx8_16x16x128(da, db[j], acc[j], sa, sb[j]);
     // the next 4 blocks' scale dwords, after the last use of these
-    if (VEC && (kb & 3) == 3) mx_load_scales<NB>(sv, min(kb + 1, KB - 4) / 4, sarow, sbrow);
+    if (VEC && (kb & 3) == 3) mx_load_scales<NB>(sv, min(kb + 1, kb1 - 4) / 4, sarow, sbrow);
     da = xa;
 #pragma unroll
     for (int j = 0; j < NB; ++j) db[j] = xb[j];
+  }
+
+  if (p.ksplit > 1) {   // fp32 partials of this K range: gate | up, or the columns
+    const int NP = DUAL ? 2 * N : N;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = q4 * 4 + q;
+      if (r < m) {
+        float* o = p.part + ((size_t)ks * p.R + row0 + r) * NP + n0 + r16;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) o[(j / CB) * N + (j % CB) * 16] = acc[j][q];
+      }
+    }
+    return;
   }
 
   if constexpr (DUAL) {
@@ -523,10 +608,13 @@ struct WsLayout {
 // to 8 that gives the chip about 4096 waves (16 per CU), keeping K / S a
 // multiple of 128.  Below 32 MB of weights the launch latency dominates and
 // the extra reduce launch would cost more than it saves: no split.
-int split_factor(long long items, long long waves, int N, int K) {
-  if (items * N * K * 2 < (32LL << 20)) return 1;
+// elt: bytes per weight; kalign: each K range a multiple of kalign (128 for
+// bf16 and fp8; 1024 for MXFP8: its scales come 4 K blocks at a time, and
+// ranges of 512 measured slower than no split on an EP8 decode share).
+int split_factor(long long items, long long waves, int N, int K, int elt, int kalign) {
+  if (items * N * K * elt < (32LL << 20)) return 1;
   int S = 1;
-  while (S < 8 && items * waves * S < 4096 && K % (2 * S * 128) == 0) S *= 2;
+  while (S < 8 && items * waves * S < 4096 && K % (2 * S * kalign) == 0) S *= 2;
   return S;
 }
 
@@ -546,13 +634,16 @@ WsLayout ffn_layout(int T, int H, int E, int k, int I, int n_shared, bool fp8, b
   L.max_slices = (int)std::min<long long>(4LL * G, R / kSliceRows + G);
   L.skinny = off;   off += align256((size_t)L.max_slices * 16);
   L.tiles = off;    off += align256((size_t)L.max_tiles * 16);
-  // Split-K partials: bf16 layers whose groups all stay below kSkinnyMax rows
-  // (T <= kSkinnyMax: no tiled work), when few slices would leave the chip idle.
+  // Split-K partials: layers whose groups all stay below kSkinnyMax rows
+  // (T <= kSkinnyMax: no tiled work), when few slices would leave the chip
+  // idle.  Waves per slice: bf16 gate/up I/16, down H/32; fp8 I/16, H/16;
+  // MXFP8 I/32, H/32.
   L.split_up = L.split_dn = 1;
-  if (!fp8 && T <= kSkinnyMax) {
+  if (T <= kSkinnyMax) {
     const long long items = std::min<long long>(G, R);
-    L.split_up = split_factor(items, I / 16, 2 * I, H);
-    L.split_dn = split_factor(items, H / 32, H, I);
+    const int elt = fp8 ? 1 : 2, ka = mx ? 1024 : 128;
+    L.split_up = split_factor(items, mx ? I / 32 : I / 16, 2 * I, H, elt, ka);
+    L.split_dn = split_factor(items, (fp8 && !mx) ? H / 16 : H / 32, H, I, elt, ka);
   }
   L.part = off;
   if (L.split_up > 1 || L.split_dn > 1)
@@ -696,17 +787,48 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
 
   // gate/up + SwiGLU, then down, of the groups of at most skinny_max_rows(T) rows
   if (err != hipSuccess) {
-  } else if (f.mx) {
-    // Scale mode by K (16-byte scale loads need 16-byte aligned scale rows).
-    up.n_ntile = f.I / (16 * kMxCB * kMxNW);
-    dn.n_ntile = f.H / (16 * kMxCBD * kMxNWD);
-    if (run(launch_skinny_mx<true, kMxNW, kMxCB>("skinny_gateup_mx", band_grid(L.max_slices, up.n_ntile), up, s)))
-      run(launch_skinny_mx<false, kMxNWD, kMxCBD>("skinny_down_mx", band_grid(L.max_slices, dn.n_ntile), dn, s));
   } else if (f.fp8) {
-    up.n_ntile = f.I / (16 * 8);
-    dn.n_ntile = f.H / (16 * 4);
-    if (run(launch_gemm("skinny_gateup_fp8", k_skinny_fp8<true, 8, 1>, 512, band_grid(L.max_slices, up.n_ntile), up, s)))
-      run(launch_gemm("skinny_down_fp8", k_skinny_fp8<false, 4, 1>, 256, band_grid(L.max_slices, dn.n_ntile), dn, s));
+    // Split-K only without tiled work (the layout reserved the partials then).
+    const bool split = !tiled && (L.split_up > 1 || L.split_dn > 1);
+    float* part = reinterpret_cast<float*>(ws + L.part);
+    const int32_t* n_rows = f.offsets + (f.E + f.n_shared);
+    up.ksplit = split ? L.split_up : 1;
+    dn.ksplit = split ? L.split_dn : 1;
+    up.R = dn.R = (int)R;
+    up.part = dn.part = part;
+    if (f.mx) {
+      up.n_ntile = f.I / (16 * kMxCB * kMxNW);
+      dn.n_ntile = f.H / (16 * kMxCBD * kMxNWD);
+      run(launch_skinny_mx<true, kMxNW, kMxCB>("skinny_gateup_mx",
+                                               band_grid(L.max_slices, up.n_ntile) * up.ksplit, up, s));
+    } else {
+      up.n_ntile = f.I / (16 * 8);
+      dn.n_ntile = f.H / (16 * 4);
+      run(launch_gemm("skinny_gateup_fp8", k_skinny_fp8<true, 8, 1>, 512,
+                      band_grid(L.max_slices, up.n_ntile) * up.ksplit, up, s));
+    }
+    if (err == hipSuccess && up.ksplit > 1) {
+      if (f.mx)
+        MOE_LAUNCH("splitk_reduce_gateup", k_splitk_reduce_q8<true>, dim3(ceil_div(f.I, 1024), (unsigned)R),
+                   dim3(256), 0, s, part, up.ksplit, (int)R, f.I, n_rows, h, h_scale);
+      else
+        MOE_LAUNCH("splitk_reduce_gateup", k_splitk_reduce_q8<false>, dim3(ceil_div(f.I, 1024), (unsigned)R),
+                   dim3(256), 0, s, part, up.ksplit, (int)R, f.I, n_rows, h, h_scale);
+      run(hipGetLastError());
+    }
+    if (err == hipSuccess) {
+      if (f.mx)
+        run(launch_skinny_mx<false, kMxNWD, kMxCBD>("skinny_down_mx",
+                                                    band_grid(L.max_slices, dn.n_ntile) * dn.ksplit, dn, s));
+      else
+        run(launch_gemm("skinny_down_fp8", k_skinny_fp8<false, 4, 1>, 256,
+                        band_grid(L.max_slices, dn.n_ntile) * dn.ksplit, dn, s));
+    }
+    if (err == hipSuccess && dn.ksplit > 1) {
+      MOE_LAUNCH("splitk_reduce_down", k_splitk_reduce<false>, dim3(ceil_div(f.H, 1024), (unsigned)R),
+                 dim3(256), 0, s, part, dn.ksplit, (int)R, f.H, n_rows, static_cast<uint16_t*>(f.y_perm));
+      run(hipGetLastError());
+    }
   } else {
     // Split-K only without tiled work (the layout reserved the partials then).
     const bool split = !tiled && (L.split_up > 1 || L.split_dn > 1);

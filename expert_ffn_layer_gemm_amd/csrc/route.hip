@@ -209,10 +209,13 @@ __global__ __launch_bounds__(256) void k_topk(const float* parts, int KS,
 }
 
 // ---------------------------------------------------------------- launchers ----
+// Slices of H: about one workgroup per CU, each slice at least 4 K chunks
+// (256 of H) long, so the top-k's sum over slice partials stays short (a
+// 64-token decode batch with H = 7168 and 256 experts: 28 slices, not 112).
 int router_splits(int T, int H, int E) {
   const long long tiles = (long long)ceil_div(T, kRtTM) * ceil_div(E, kRtTE);
   const long long want = (256 + tiles - 1) / tiles;    // one workgroup per CU
-  return (int)std::max(1LL, std::min(want, (long long)(H / 64)));
+  return (int)std::max(1LL, std::min(want, (long long)(H / 256)));
 }
 
 size_t router_workspace_bytes(int T, int H, int E) {

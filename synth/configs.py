@@ -65,7 +65,7 @@ CONFIGS = [
 
 # Further workloads (not among the five above): the Qwen3-235B-like layer with
 # MXFP8 experts, as "Hosting Qwen on Blackwell" (Quantization) deploys it, and
-# expert-parallel shares of the bf16 layer (one GPU's experts, every token:
+# expert-parallel shares (one GPU's experts, every token:
 # "CuTeDSL at Perplexity", MoE Dispatch/Combine, tensor-parallel deployment):
 # EP8 at the decode batch (16 experts, about 4 rows each) and EP4 at the
 # prefill chunk ("Hosting Qwen on Blackwell" runs its prefill EP on 4 GPUs).
@@ -78,6 +78,13 @@ EXTRA_CONFIGS = [
               regime="hbm"),
     MoeConfig("qwen3_235b_prefill_ep4", 8, T=8192, H=4096, E=128, k=8, I=1536, e_first=32,
               e_local=32, regime="mfma"),
+    # 8-bit decode shares: the DeepSeek-like layer's 16 routed experts of an
+    # EP16 deployment at a 64-token decode batch (fp8), and the MXFP8
+    # Qwen3-235B-like layer's EP8 share.
+    MoeConfig("deepseek_v3_decode_ep16", 9, T=64, H=7168, E=256, k=8, I=2048, wdtype="fp8",
+              e_first=32, e_local=16, regime="hbm"),
+    MoeConfig("qwen3_235b_decode_mxfp8_ep8", 10, T=64, H=4096, E=128, k=8, I=1536, wdtype="mxfp8",
+              e_first=16, e_local=16, regime="hbm"),
 ]
 
 

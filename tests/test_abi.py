@@ -80,9 +80,11 @@ def test_error_codes_before_launch():
     assert "x is NULL" in moe.moe_last_error()
     assert _call("moe_route", P(sh), FAKE + 2, FAKE, None, FAKE, FAKE, FAKE, None, 0, None) == moe.MOE_ERR_INVALID_ARG
     assert "aligned" in moe.moe_last_error()
-    # router workspace missing when H is split
-    assert moe.moe_route_workspace_bytes(sh) > 0
-    assert _call("moe_route", P(sh), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, 0, None) == moe.MOE_ERR_WORKSPACE
+    # router workspace missing when H is split (slices of at least 256 channels)
+    assert moe.moe_route_workspace_bytes(sh) == 0
+    sh_split = moe.make_shape(64, 1024, 8, 2, 512)
+    assert moe.moe_route_workspace_bytes(sh_split) == 4 * 64 * 8 * 4
+    assert _call("moe_route", P(sh_split), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, 0, None) == moe.MOE_ERR_WORKSPACE
     # unsupported shapes
     bad = moe.make_shape(64, 256, 8, 9, 512)
     assert _call("moe_route", P(bad), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, 0, None) == moe.MOE_ERR_UNSUPPORTED

@@ -417,14 +417,25 @@ def test_forward_share_configs(name):
     _forward_check(cfg, layer(cfg))
 
 
-# Decode batches whose groups leave the chip idle take split-K in the bf16
+# Decode batches whose groups leave the chip idle take split-K in the
 # streaming GEMMs (partials summed in K-range order by a reduce kernel):
-# factors 2 to 8, with and without a shared expert, whole layer and shares.
+# factors 2 to 8, with and without a shared expert, whole layer and shares,
+# bf16, fp8 and MXFP8.
 SPLITK = [
     MoeConfig("sk_q235_t4", 60, T=4, H=4096, E=128, k=8, I=1536),
     MoeConfig("sk_share_s8", 61, T=16, H=2048, E=64, k=4, I=1024, e_first=8, e_local=8),
     MoeConfig("sk_share_shared", 62, T=8, H=4096, E=16, k=2, I=1024, n_shared=1, e_first=12,
               e_local=4),
+    # 8-bit streaming kernels with split-K: fp8 gate/up split 2 (a
+    # DeepSeek-shaped share of 16 experts), fp8 down split 4, MXFP8 gate/up
+    # split 4, MXFP8 down split 4 (gate/up partials re-quantised per 128 / 32
+    # columns by the reduce)
+    MoeConfig("sk_fp8_share", 63, T=16, H=7168, E=256, k=8, I=2048, wdtype="fp8", e_first=16,
+              e_local=16),
+    MoeConfig("sk_fp8_down", 64, T=8, H=1024, E=16, k=2, I=4096, n_shared=1, wdtype="fp8"),
+    MoeConfig("sk_mx_share", 65, T=16, H=4096, E=128, k=8, I=1536, wdtype="mxfp8", e_first=16,
+              e_local=16),
+    MoeConfig("sk_mx_both", 66, T=8, H=1024, E=16, k=2, I=4096, n_shared=1, wdtype="mxfp8"),
 ]
 
 
