@@ -12,11 +12,11 @@
 // (section 4.2.2): gate and up are two B streams of one workgroup.
 //
 // gfx950 design.  These layers are memory-bound (a ~128-row expert group
-// reads 29 MB of weights for 7.5 GFLOP), and what bounds them is the number of
-// L1 -> L2 requests a CU has in flight (rocprofv3 on the DeepSeek-like layer:
-// about 80 outstanding requests per CU, whatever the bytes per request), so
-// the kernel is built to issue few, full-line requests:
-//   - Row tile BM (128 or 160) x 256 staged B rows, 8 waves (2 per SIMD) laid
+// reads 29 MB of weights for 7.5 GFLOP, about 256 FLOP per byte against the
+// 625 of fp8's ridge), so the kernel is a load pipeline that keeps two
+// chunks of whole 128-byte row pieces in flight per CU with the MFMAs, the
+// per-block scaling and the epilogue overlapped as far as its LDS allows:
+//   - Row tile BM (MXFP8 128, fp8 160) x 256 staged B rows, 8 waves (2 per SIMD) laid
 //     out 2 x 4; K staged in 128-byte chunks (one 16x16x128 MFMA step) by
 //     direct-to-LDS loads of whole 128-byte row pieces into a 3-stage A ring
 //     and a 3-stage B ring (two chunks in flight while one is multiplied).
@@ -24,10 +24,11 @@
 //     one tile, so its weights are streamed once.
 //   - Scales travel in groups of SG chunks: every SG-th chunk, the first
 //     waves load, per A row (and per B row for MX, or the two weight-block
-//     scale rows for fp8), the scales of the next SG chunks with one 16-byte
-//     request (SG = 4) instead of one 4-byte request per row and chunk; a
-//     scale stage is reused SG chunks later, so NSS = ceil((NS + SG - 1) / SG)
-//     stages suffice.
+//     scale rows for fp8), the scales of the next SG chunks.  MXFP8 with K a
+//     multiple of 512 uses SG = 4 (one 16-byte request per row per 4 chunks
+//     instead of four 4-byte ones); fp8 uses SG = 1, since 160-row tiles
+//     leave no LDS for 4-chunk scale stages.  A scale stage is reused SG
+//     chunks later, so NSS = ceil((NS + SG - 1) / SG) stages suffice.
 //   - Chunk c's loads are issued after the boundary of chunk c - NS (the
 //     workgroup barrier that ends every wave's reads of those stages), one
 //     part between each two columns of the second half's MFMAs; each wave
