@@ -3,6 +3,8 @@
 // workgroup barrier.
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace moe {
@@ -72,6 +74,30 @@ __device__ __forceinline__ void dma4_untracked(const void* src, uint8_t* dst) {
   const uint32_t la = (uint32_t)(size_t)(lds_ptr_t)dst;
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
                :: "s"(la), "v"(src) : "memory", "m0");
+}
+
+// Calls f(std::integral_constant<int, n>) for a runtime n in [0, N]: a tiled
+// kernel's main loop is compiled once per count of valid row blocks, so its
+// row-block checks are resolved at compile time instead of being one scalar
+// branch per block and column.
+template <int N, class F>
+__device__ __forceinline__ void with_count(int n, F&& f) {
+  if constexpr (N > 0) {
+    if (n >= N) {
+      f(std::integral_constant<int, N>{});
+      return;
+    }
+    with_count<N - 1>(n, f);
+  } else {
+    f(std::integral_constant<int, 0>{});
+  }
+}
+
+// The count a with_count callee was given, or a plain runtime count.
+template <class T>
+__device__ __forceinline__ constexpr int count_value(T n) {
+  if constexpr (std::is_integral_v<T>) return n;
+  else return T::value;
 }
 
 }  // namespace moe

@@ -175,9 +175,8 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
     for (int j = 0; j < NB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   {
-  // bf16: the software-pipelined main loop (file header).  Waves with a
-  // row block past the group's end take the plain loop below, with the
-  // same barriers and loads.
+  // bf16: the software-pipelined main loop (file header), for the wave's
+  // valid row blocks only.
   static_assert(RB == 128 && MB == 8, "bf16 pipeline layout");
   // chunk c: A in stage c % NSA of the A ring, B in stage c % NSB of the B ring
   auto sa = [&](int c) { return lds + (c % NSA) * A_STAGE; };
@@ -206,7 +205,6 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
   wait_vmcnt_le<(NSA - 1) * IPWA + (NSB - 1) * IPWB>(min(NSA - 1, nk - 1) * nva +
                                                      min(NSB - 1, nk - 1) * IPWB);
   lds_barrier();
-  const bool full = active && nmb == MB;
   auto rd_b = [&](const uint8_t* st, int ks, u32x4_t (&b)[NB]) {
     const int c = ks * 4 + (lane >> 4);
 #pragma unroll
@@ -226,85 +224,77 @@ __global__ __launch_bounds__(64 * WM * WN) void k_tiled3(const GemmArgs p) {
     if (kc + NSA < nk) issue_a(kc + NSA);
     if (kc + NSB < nk) issue_b(kc + NSB);
   };
-  if (full) {
-    u32x4_t a[MB], bc[NB], bn[NB];
-    rd_b(sb(0), 0, bc);
+  // The main loop, compiled once per count NMB of valid row blocks of the
+  // wave (0: the wave only takes part in the loads and barriers).
+  auto main_loop = [&](auto nm) {
+    constexpr int NMB = decltype(nm)::value;
+    if constexpr (NMB == 0) {
+      for (int kc = 0; kc < nk; ++kc) boundary(kc);
+    } else {
+      constexpr int H = NMB / 2;   // row blocks of K step 1 multiplied before the boundary
+      u32x4_t a[MB], bc[NB], bn[NB];
+      rd_b(sb(0), 0, bc);
 #pragma unroll
-    for (int i = 0; i < MB; ++i) a[i] = rd_a(sa(0), 0, i);
-    // sched_barrier(0) keeps the compiler from regrouping the reads and
-    // MFMAs: each read is issued while the MFMA pipe works on the row block
-    // before it.
-    auto chunk = [&](int kc, auto last_c) {
-      constexpr bool last = decltype(last_c)::value;
-      const uint8_t* st = sa(kc);
-      const uint8_t* sn = sa(kc + 1);
-      const uint8_t* bt = sb(kc);
-      const uint8_t* bnx = sb(kc + 1);
-      // K step 0 of chunk kc; reads of step 1.
+      for (int i = 0; i < NMB; ++i) a[i] = rd_a(sa(0), 0, i);
+      // sched_barrier(0) keeps the compiler from regrouping the reads and
+      // MFMAs: each read is issued while the MFMA pipe works on the row block
+      // before it.
+      auto chunk = [&](int kc, auto last_c) {
+        constexpr bool last = decltype(last_c)::value;
+        const uint8_t* st = sa(kc);
+        const uint8_t* sn = sa(kc + 1);
+        const uint8_t* bt = sb(kc);
+        const uint8_t* bnx = sb(kc + 1);
+        // K step 0 of chunk kc; reads of step 1 (B over the first two row
+        // blocks, or all of it after the first when there is one).
 #pragma unroll
-      for (int i = 0; i < MB; ++i) {
+        for (int i = 0; i < NMB; ++i) {
 #pragma unroll
-        for (int j = 0; j < NB; ++j) acc[i][j] = mfma_bf16_16x16x32(a[i], bc[j], acc[i][j]);
-        if (i < 2) {
-          const int c = 4 + (lane >> 4);
+          for (int j = 0; j < NB; ++j) acc[i][j] = mfma_bf16_16x16x32(a[i], bc[j], acc[i][j]);
+          if (i < 2) {
+            const int c = 4 + (lane >> 4);
+            constexpr int JB = NMB >= 2 ? NB / 2 : NB;
 #pragma unroll
-          for (int j = 2 * i; j < 2 * i + 2; ++j) {
-            const int br = b_row<DUAL, WN, NB>(j, wn, r16);
-            bn[j] = lds_read16(bt + br * kRB + (slot<RB>(br, c) << 4));
-          }
-        }
-        a[i] = rd_a(st, 1, i);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int j = 0; j < NB; ++j) bc[j] = bn[j];
-      // K step 1: first half, the chunk boundary, then the second half with
-      // the reads of the next chunk's step 0.
-#pragma unroll
-      for (int i = 0; i < MB / 2; ++i) {
-#pragma unroll
-        for (int j = 0; j < NB; ++j) acc[i][j] = mfma_bf16_16x16x32(a[i], bc[j], acc[i][j]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      boundary(kc);
-      if constexpr (!last) {
-        rd_b(bnx, 0, bn);
-#pragma unroll
-        for (int i = 0; i < MB / 2; ++i) a[i] = rd_a(sn, 0, i);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = MB / 2; i < MB; ++i) {
-#pragma unroll
-        for (int j = 0; j < NB; ++j) acc[i][j] = mfma_bf16_16x16x32(a[i], bc[j], acc[i][j]);
-        if constexpr (!last) a[i] = rd_a(sn, 0, i);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int j = 0; j < NB; ++j) bc[j] = bn[j];
-    };
-    for (int kc = 0; kc + 1 < nk; ++kc) chunk(kc, std::false_type{});
-    chunk(nk - 1, std::true_type{});
-  } else {
-    for (int kc = 0; kc < nk; ++kc) {
-      if (active) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          u32x4_t b[NB], aa[MB];
-          rd_b(sb(kc), ks, b);
-#pragma unroll
-          for (int i = 0; i < MB; ++i) aa[i] = rd_a(sa(kc), ks, i);
-#pragma unroll
-          for (int i = 0; i < MB; ++i)
-            if (i < nmb) {
-#pragma unroll
-              for (int j = 0; j < NB; ++j) acc[i][j] = mfma_bf16_16x16x32(aa[i], b[j], acc[i][j]);
+            for (int j = JB * i; j < JB * i + JB; ++j) {
+              const int br = b_row<DUAL, WN, NB>(j, wn, r16);
+              bn[j] = lds_read16(bt + br * kRB + (slot<RB>(br, c) << 4));
             }
+          }
+          a[i] = rd_a(st, 1, i);
+          __builtin_amdgcn_sched_barrier(0);
         }
-      }
-      boundary(kc);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) bc[j] = bn[j];
+        // K step 1: first half, the chunk boundary, then the second half with
+        // the reads of the next chunk's step 0.
+#pragma unroll
+        for (int i = 0; i < H; ++i) {
+#pragma unroll
+          for (int j = 0; j < NB; ++j) acc[i][j] = mfma_bf16_16x16x32(a[i], bc[j], acc[i][j]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        boundary(kc);
+        if constexpr (!last) {
+          rd_b(bnx, 0, bn);
+#pragma unroll
+          for (int i = 0; i < H; ++i) a[i] = rd_a(sn, 0, i);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = H; i < NMB; ++i) {
+#pragma unroll
+          for (int j = 0; j < NB; ++j) acc[i][j] = mfma_bf16_16x16x32(a[i], bc[j], acc[i][j]);
+          if constexpr (!last) a[i] = rd_a(sn, 0, i);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) bc[j] = bn[j];
+      };
+      for (int kc = 0; kc + 1 < nk; ++kc) chunk(kc, std::false_type{});
+      chunk(nk - 1, std::true_type{});
     }
-  }
+  };
+  with_count<MB>(active ? nmb : 0, main_loop);
   }
 
   // Epilogue.  Lane holds rows rbase + 16 i + 4 (lane/16) + q of its blocks.

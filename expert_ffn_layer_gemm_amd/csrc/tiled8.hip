@@ -302,47 +302,51 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
   // Partial tiles of the current column for the row blocks of one half.
   constexpr int HMAX = MB - HA;
   f32x4_t pr[2][HMAX];
-  auto col = [&](int i0, int i1, int j) {          // MFMAs of row blocks [i0, i1) with B block j
+  // MFMAs of row blocks [i0, i1) with B block j (blocks below the count nm)
+  auto col = [&](int i0, int i1, int j, auto nm) {
 #pragma unroll
     for (int i = i0; i < i1; ++i)
-      if (i < nmb) {
+      if (i < count_value(nm)) {
         if constexpr (MX) acc[i][j] = mfma_mx8_16x16x128(a[i], b[j], acc[i][j], sam[i], sbm[j]);
         else pr[j & 1][i - i0] = mfma_fp8_16x16x128(a[i], b[j], f32x4_t{0.f, 0.f, 0.f, 0.f});
       }
   };
-  auto scale_col = [&](int i0, int i1, int j) {    // fp8: acc += partial * (row scale * block scale)
+  // fp8: acc += partial * (row scale * block scale)
+  auto scale_col = [&](int i0, int i1, int j, auto nm) {
     if constexpr (!MX) {
       const float sbv = j < NB / 2 ? sb_lo : sb_hi;
 #pragma unroll
       for (int i = i0; i < i1; ++i)
-        if (i < nmb) {
+        if (i < count_value(nm)) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) acc[i][j][q] += pr[j & 1][i - i0][q] * (saf[i][q] * sbv);
         }
     }
   };
 
+  auto main_loop = [&](auto nm) {
+  const int NMB = count_value(nm);
   // Prologue reads: chunk 0's B fragments, A of the first half, block scales.
 #pragma unroll
   for (int j = 0; j < NB; ++j)
-    if (nmb > 0) next_b(0, j);
+    if (NMB > 0) next_b(0, j);
 #pragma unroll
   for (int i = 0; i < HA; ++i)
-    if (i < nmb) next_a(0, i);
+    if (i < NMB) next_a(0, i);
   rd_bsc(0);
   for (int kc = 0; kc < nk; ++kc) {
     // A fragments of the second half (the stage is refilled at the boundary).
 #pragma unroll
     for (int i = HA; i < MB; ++i)
-      if (i < nmb) next_a(kc, i);
+      if (i < NMB) next_a(kc, i);
     // First half: row blocks [0, HA), column by column; a column's partials
     // are scaled into the accumulators one column later.
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      col(0, HA, j);
-      if (j > 0) scale_col(0, HA, j - 1);
+      col(0, HA, j, nm);
+      if (j > 0) scale_col(0, HA, j - 1, nm);
     }
-    scale_col(0, HA, NB - 1);
+    scale_col(0, HA, NB - 1, nm);
     // Keep the first half ahead of the boundary (the compiler would sink it
     // past the wait and barrier otherwise): it runs while the wave waits.
 #pragma unroll
@@ -354,21 +358,28 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
     // The next chunk's A fragments of the first half (registers just freed).
 #pragma unroll
     for (int i = 0; i < HA; ++i)
-      if (more && i < nmb) next_a(kc + 1, i);
+      if (more && i < NMB) next_a(kc + 1, i);
     __builtin_amdgcn_sched_barrier(0);
     // Second half, column by column; B fragment j of the next chunk is read
     // as soon as column j is done.
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      col(HA, MB, j);
+      col(HA, MB, j, nm);
       if (kc + NS < nk) issue_part(kc + NS, j);
-      if (j > 0) scale_col(HA, MB, j - 1);
-      if (more && nmb > 0) next_b(kc + 1, j);
+      if (j > 0) scale_col(HA, MB, j - 1, nm);
+      if (more && NMB > 0) next_b(kc + 1, j);
       __builtin_amdgcn_sched_barrier(0);
     }
-    scale_col(HA, MB, NB - 1);
+    scale_col(HA, MB, NB - 1, nm);
     if (more) rd_bsc(kc + 1);
   }
+  };
+  // MXFP8: one copy of the loop per count of valid row blocks (2 % faster on
+  // the MXFP8 prefill layer); fp8: one loop with runtime checks (the
+  // specialised copies were 3 % slower on the DeepSeek-like layer, whose two
+  // wave rows usually hold different counts and so run different copies).
+  if constexpr (MX) with_count<MB>(nmb, main_loop);
+  else main_loop(nmb);
 
   // Epilogue.  Lane holds rows rbase + 16 i + 4 (lane/16) + q of its blocks.
   // The output tile is assembled in LDS (the ring stages are free once every
