@@ -77,7 +77,10 @@ size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 // moe_forward workspace: routing, dispatch and expert intermediates.  The
 // forward path never builds x_perm: the GEMMs gather their rows through
-// src_row from x (bf16) or from x quantised once per token (fp8, mxfp8: xq, xs).
+// src_row from x (bf16) or from x quantised once per token (fp8, mxfp8: xq,
+// xs).  fp8 scales are K-block-major: per permuted row ([H/128][R], R slots
+// per block) for large batches, per token ([H/128][T]) for small ones, whose
+// routing launch quantises before the rows are known.
 struct FwdLayout {
   size_t logits, rpart, idx, w, counts, offsets, tcnt, tick, dest, src_row, xq, xs, y_perm, ffn, total;
 };
@@ -99,7 +102,7 @@ FwdLayout fwd_layout(const moe_shape* s) {
   L.dest = off;    off += align256(T * k * 4);
   L.src_row = off; off += align256(R * 4);
   L.xq = off;      off += fp8 ? align256(T * H) : 0;
-  L.xs = off;      off += mx ? align256(T * (H / 32)) : fp8 ? align256(T * (H / 128) * 4) : 0;
+  L.xs = off;      off += mx ? align256(T * (H / 32)) : fp8 ? align256(R * (H / 128) * 4) : 0;
   L.y_perm = off;  off += align256(R * H * 2);
   L.ffn = off;
   off += moe::ffn_workspace_bytes(s->T, s->H, n_local(s), s->k, s->I, s->n_shared, fp8, mx);
@@ -168,6 +171,10 @@ hipError_t forward_launch(const moe_shape* shape, const void* x, const float* w_
                  w_down, s_gate, s_up, s_down, y_perm, ws + L.ffn, (long long)shape->T, false, mx};
   a.one_stream = one_stream;
   const bool small = shape->T <= moe::kSmallBatch;
+  if (small) {                       // fp8 scales per token: rows map to tokens
+    a.s_rows = src_row;
+    a.s_ld = shape->T;
+  }
   int32_t* tick = reinterpret_cast<int32_t*>(ws + L.tick);
   hipError_t e = moe::launch_router_gemm(static_cast<const uint16_t*>(x), w_router, parts,
                                          shape->T, shape->H, shape->E, s, small ? tick : nullptr);
@@ -191,7 +198,9 @@ hipError_t forward_launch(const moe_shape* shape, const void* x, const float* w_
                               is_share(shape), fp8, mx, s);
   }
   if (e == hipSuccess && fp8 && !small)   // (small batches: quantised in the routing launch)
-    e = moe::launch_quantize_rows(static_cast<const uint16_t*>(x), xq, xs, shape->T, shape->H, mx, s);
+    e = moe::launch_quantize_rows(static_cast<const uint16_t*>(x), xq, xs, shape->T, shape->H, mx,
+                                  dest, shape->k, shape->n_shared ? offsets + nl : nullptr,
+                                  shape->T * (shape->k + shape->n_shared), s);
   if (e == hipSuccess) e = moe::launch_grouped_ffn(a, s);
   if (e == hipSuccess)
     e = moe::launch_combine(static_cast<const uint16_t*>(y_perm), dest, w, offsets + nl,

@@ -169,15 +169,17 @@ __device__ __forceinline__ void plan_groups(const int32_t* offsets, const Sched&
 // the threads tid = 0 .. nthreads-1 (nthreads a multiple of 64, consecutive
 // lanes of whole waves), 8 channels per thread and step.
 //   fp8 (MX = false): per 128-channel group, scale = amax / 448 (1 for an
-//     all-zero group) into scale_row[group] (float); 16 lanes cover a group,
-//     the group maximum is a 16-lane DPP reduction;
+//     all-zero group); 16 lanes cover a group, the group maximum is a 16-lane
+//     DPP reduction that leaves it in all 16;
 //   MXFP8 (MX = true): per 32-channel block, E8M0 = max(biased exponent of
-//     amax - 8, 0) into scale_row[block] (byte), codes of v * 2^-(E8M0 - 127);
-//     4 lanes cover a block.
-// Codes round to nearest even after clamping to +-448.
-template <bool MX>
+//     amax - 8, 0), codes of v * 2^-(E8M0 - 127); 4 lanes cover a block.
+// Codes round to nearest even after clamping to +-448.  Every lane of a group
+// calls put_scale(group, scale, its lane within the group) (fp8: float scale,
+// lanes 0..15; MXFP8: E8M0 byte, lanes 0..3), so the caller decides where, and
+// by how many lanes, the scale is stored.
+template <bool MX, typename PutScale>
 __device__ __forceinline__ void quantize_row(const uint16_t* __restrict__ src, uint8_t* __restrict__ dst,
-                                             void* __restrict__ scale_row, int H, int tid, int nthreads) {
+                                             PutScale put_scale, int H, int tid, int nthreads) {
   const int chunks = H / 8;
   const u32x4_t* s8 = reinterpret_cast<const u32x4_t*>(src);
   for (int c = tid; c < chunks; c += nthreads) {
@@ -196,7 +198,7 @@ __device__ __forceinline__ void quantize_row(const uint16_t* __restrict__ src, u
         const uint32_t code = f32_to_e4m3(fminf(fmaxf(v[q] * inv, -448.f), 448.f));
         if (q < 4) lo |= code << (8 * q); else hi |= code << (8 * (q - 4));
       }
-      if ((c & 3) == 0) static_cast<uint8_t*>(scale_row)[c / 4] = (uint8_t)e8;
+      put_scale(c / 4, e8, c & 3);
     } else {
       amax = row16_max(amax);
       const float scale = amax == 0.f ? 1.f : amax / 448.f;
@@ -206,7 +208,7 @@ __device__ __forceinline__ void quantize_row(const uint16_t* __restrict__ src, u
         const uint32_t code = f32_to_e4m3(qv);
         if (q < 4) lo |= code << (8 * q); else hi |= code << (8 * (q - 4));
       }
-      if ((c & 15) == 0) static_cast<float*>(scale_row)[c / 16] = scale;
+      put_scale(c / 16, scale, c & 15);
     }
     *reinterpret_cast<uint2*>(dst + c * 8) = make_uint2(lo, hi);
   }

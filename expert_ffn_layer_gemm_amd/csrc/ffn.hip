@@ -195,8 +195,9 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
 // Split-K reduce of an 8-bit gate/up GEMM: h = silu(sum of gate planes) *
 // (sum of up planes), planes added in order, then h quantised per row like
 // the one-pass epilogue: fp8 (MX = false) per 128 columns (scale = amax /
-// 448, 32 threads of 4 columns per group), MXFP8 per 32 columns (E8M0, 8
-// threads per block).  Rows below *n_rows; 4 columns per thread.
+// 448, 32 threads of 4 columns per group; scales [N/128][R]), MXFP8 per 32
+// columns (E8M0, 8 threads per block; [R][N/32]).  Rows below *n_rows; 4
+// columns per thread.
 template <bool MX>
 __global__ __launch_bounds__(256) void k_splitk_reduce_q8(const float* __restrict__ part, int ksplit,
                                                           int R, int N, const int32_t* __restrict__ n_rows,
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce_q8(const float* __restric
     const float scale = am == 0.f ? 1.f : am / 448.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) word |= f32_to_e4m3(fminf(fmaxf(h[q] / scale, -448.f), 448.f)) << (8 * q);
-    if ((c & 127) == 0) static_cast<float*>(out_scale)[(size_t)r * (N / 128) + c / 128] = scale;
+    if ((c & 127) == 0) static_cast<float*>(out_scale)[(size_t)(c / 128) * R + r] = scale;
   }
   *reinterpret_cast<uint32_t*>(out + (size_t)r * N + c) = word;
 }
@@ -278,7 +279,7 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_fp8(const GemmArgs p) {
       const int rr = mb * 16 + (lane >> 4) * 4 + q;
       sok[mb][q] = rr < m;
       const int ps = row0 + (sok[mb][q] ? rr : 0);
-      srow[mb][q] = static_cast<const float*>(p.A_scale) + (size_t)(p.a_rows ? p.a_rows[ps] : ps) * KB;
+      srow[mb][q] = static_cast<const float*>(p.A_scale) + (p.s_rows ? p.s_rows[ps] : ps);
     }
   }
   f32x4_t acc0[MB], acc1[MB];
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_fp8(const GemmArgs p) {
         if (DUAL) p1 = mfma_fp8_16x16x128(a, cur1, z);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float sa = sok[mb][q] ? srow[mb][q][kb] : 0.f;
+          const float sa = sok[mb][q] ? srow[mb][q][(size_t)kb * p.s_ld] : 0.f;
           acc0[mb][q] += p0[q] * (sa * s0);
           if (DUAL) acc1[mb][q] += p1[q] * (sa * s1);
         }
@@ -344,7 +345,6 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_fp8(const GemmArgs p) {
         if (r16 == 0) row_amax[wave][r] = am;
       }
     __syncthreads();
-    const int N128 = N / 128;
     const int gcol = (nt * NW * 16) / 128;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -359,7 +359,7 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_fp8(const GemmArgs p) {
             const float scale = am == 0.f ? 1.f : am / 448.f;
             const float qv = fminf(fmaxf(hv[mb][q] / scale, -448.f), 448.f);
             p.out[(size_t)(row0 + r) * N + n0 + r16] = (uint8_t)f32_to_e4m3(qv);
-            if (wave == 0 && r16 == 0) static_cast<float*>(p.out_scale)[(size_t)(row0 + r) * N128 + gcol] = scale;
+            if (wave == 0 && r16 == 0) static_cast<float*>(p.out_scale)[(size_t)gcol * p.R + row0 + r] = scale;
           }
         }
       }
@@ -743,9 +743,14 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
   up.out_scale = h_scale;
   up.K = f.H;
   up.N = f.I;
+  up.R = (int)R;
+  up.s_rows = f.s_rows;           // fp8 activation scales, K-block-major
+  up.s_ld = f.s_ld ? f.s_ld : (int)R;
 
   GemmArgs dn = up;
-  dn.a_rows = nullptr;            // h is written in permuted row order
+  dn.a_rows = nullptr;            // h (and its scales, [I/128][R]) in permuted row order
+  dn.s_rows = nullptr;
+  dn.s_ld = (int)R;
   dn.A = h;
   dn.A_scale = h_scale;
   dn.B0 = static_cast<const uint8_t*>(f.w_down);

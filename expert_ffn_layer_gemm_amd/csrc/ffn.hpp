@@ -96,19 +96,26 @@ struct GemmArgs {
   const int32_t* offsets;
   const int32_t* a_rows;   // optional: A row of permuted row r is a_rows[r] (gather on load)
   const uint8_t* A;
-  const void* A_scale;     // fp8: [R, K/128] fp32; mxfp8: [R, K/32] E8M0 bytes
+  // fp8: fp32 activation scales stored K-block-major, the scale of A row a
+  // for K block kb at A_scale[kb * s_ld + a], a = s_rows ? s_rows[r] : r for
+  // permuted row r (the scales one K step of a row tile needs are then
+  // adjacent); mxfp8: [R, K/32] E8M0 bytes of row a_rows ? a_rows[r] : r.
+  const void* A_scale;
   const uint8_t* B0;
   const uint8_t* B1;       // up weights (dual) or unused
   const void* s_B0;        // fp8: [G, N/128, K/128] fp32; mxfp8: [G, N, K/32] E8M0 bytes
   const void* s_B1;
   uint8_t* out;            // bf16 or e4m3 codes
-  void* out_scale;         // dual: fp8 [R, N/128] fp32; mxfp8 [R, N/32] E8M0 bytes
+  void* out_scale;         // dual: fp8 [N/128][R] fp32 (K-block-major for the next GEMM);
+                           // mxfp8 [R, N/32] E8M0 bytes
   int K, N, n_ntile;
   // Split-K (bf16 streaming kernel): ksplit workgroups per (slice, column
   // tile) each sum K / ksplit of K into part [ksplit][R][dual ? 2N : N] fp32;
   // a reduce kernel adds the slices in order and applies the epilogue.
   int ksplit = 1;
-  int R = 0;
+  int R = 0;               // rows of the permuted matrix: stride of out_scale and of part
+  const int32_t* s_rows = nullptr;
+  int s_ld = 0;
   float* part = nullptr;
 };
 

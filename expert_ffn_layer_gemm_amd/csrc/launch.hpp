@@ -57,9 +57,14 @@ hipError_t launch_permute(const int32_t* topk_idx, const uint16_t* x, int32_t* c
                           void* x_perm_scale, int32_t* tile_cnt, int T, int H, int E, int k,
                           int n_shared, int e_first, bool share, bool fp8, bool mx,
                           hipStream_t s);
-// Per-token e4m3 quantisation of x (128-channel groups): the rows the fp8
-// GEMMs gather through src_row.
+// Per-token quantisation of x (fp8: 128-channel groups; mxfp8: blocks of
+// 32): the rows the 8-bit GEMMs gather through src_row.  fp8 scales go to the
+// permuted rows that read them, K-block-major: xs[b * R + dest[t, j]] for
+// every held pair (t, j), and xs[b * R + *shared_base + t] for the shared
+// group (shared_base null without one); mxfp8 scales stay per token,
+// xs[t * H/32 + b].
 hipError_t launch_quantize_rows(const uint16_t* x, uint8_t* xq, void* xs, int T, int H, bool mx,
+                                const int32_t* dest, int k, const int32_t* shared_base, int R,
                                 hipStream_t s);
 
 // combine.hip
@@ -95,6 +100,11 @@ struct FfnArgs {
   // Run the tiled and the weight-streaming chains on the caller's stream
   // only (no side stream is created or used).
   bool one_stream = false;
+  // fp8 activation scales, K-block-major: block kb of permuted row r at
+  // x_perm_scale[kb * s_ld + (s_rows ? s_rows[r] : r)]; s_ld = 0 means R
+  // (one scale per permuted row, the layout moe_grouped_ffn takes).
+  const int32_t* s_rows = nullptr;
+  int s_ld = 0;
 };
 size_t ffn_workspace_bytes(int T, int H, int E, int k, int I, int n_shared, bool fp8, bool mx);
 hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s);

@@ -135,19 +135,47 @@ __global__ __launch_bounds__(256) void k_gather_bf16(const int32_t* __restrict__
   }
 }
 
-// x_perm[r] = e4m3 codes of x[src_row[r]] (x[r] when src_row is null) per
-// 128-channel group, scale = amax/448 (quantize_row<false>).
+// x_perm[r] = e4m3 codes of x[src_row[r]] per 128-channel group, scale =
+// amax/448 (quantize_row<false>), scales K-block-major: x_scale[b * ld + r].
 __global__ __launch_bounds__(256) void k_gather_fp8(const int32_t* __restrict__ src_row,
                                                     const uint16_t* __restrict__ x,
                                                     uint8_t* __restrict__ x_perm,
-                                                    float* __restrict__ x_scale, int R, int H,
+                                                    float* __restrict__ x_scale, int R, int H, int ld,
                                                     const int32_t* __restrict__ n_rows) {
   R = gather_rows(R, n_rows);
   for (int rr = 0; rr < kGatherRows; ++rr) {
     const int r = blockIdx.x * kGatherRows + rr;
     if (r >= R) return;
-    quantize_row<false>(x + (size_t)(src_row ? src_row[r] : r) * H, x_perm + (size_t)r * H,
-                        x_scale + (size_t)r * (H / 128), H, threadIdx.x, 256);
+    quantize_row<false>(x + (size_t)src_row[r] * H, x_perm + (size_t)r * H,
+                        [&](int b, float sc, int li) { if (li == 0) x_scale[(size_t)b * ld + r] = sc; },
+                        H, threadIdx.x, 256);
+  }
+}
+
+// Per-token e4m3 codes of x (xq[t] = codes of x[t]); each 128-channel scale
+// is stored once per permuted row that reads token t: xs[b * R + dest[t, j]]
+// for the pairs held here (dest >= 0), and xs[b * R + *shared_base + t] for
+// the shared group.  The 16 lanes of a group share these stores.
+__global__ __launch_bounds__(256) void k_quantize_tokens_fp8(const uint16_t* __restrict__ x,
+                                                             uint8_t* __restrict__ xq,
+                                                             float* __restrict__ xs, int T, int H,
+                                                             const int32_t* __restrict__ dest, int k,
+                                                             const int32_t* __restrict__ shared_base,
+                                                             int R) {
+  const int ns = shared_base ? 1 : 0;
+  const int sb = shared_base ? *shared_base : 0;
+  for (int tt = 0; tt < kGatherRows; ++tt) {
+    const int t = blockIdx.x * kGatherRows + tt;
+    if (t >= T) return;
+    const int32_t* dt = dest + (size_t)t * k;
+    quantize_row<false>(x + (size_t)t * H, xq + (size_t)t * H,
+                        [&](int b, float sc, int li) {
+                          for (int j = li; j < k + ns; j += 16) {
+                            const int d = j < k ? dt[j] : sb + t;
+                            if (d >= 0) xs[(size_t)b * R + d] = sc;
+                          }
+                        },
+                        H, threadIdx.x, 256);
   }
 }
 
@@ -156,7 +184,7 @@ size_t permute_workspace_bytes(int T, int E) {
 }
 
 // x_perm[r] = MXFP8 codes of x[src_row[r]] (x[r] when src_row is null):
-// blocks of 32 channels (quantize_row<true>).
+// blocks of 32 channels (quantize_row<true>), E8M0 scales x_scale[r][b].
 __global__ __launch_bounds__(256) void k_gather_mx(const int32_t* __restrict__ src_row,
                                                    const uint16_t* __restrict__ x,
                                                    uint8_t* __restrict__ x_perm,
@@ -166,8 +194,10 @@ __global__ __launch_bounds__(256) void k_gather_mx(const int32_t* __restrict__ s
   for (int rr = 0; rr < kGatherRows; ++rr) {
     const int r = blockIdx.x * kGatherRows + rr;
     if (r >= R) return;
+    uint8_t* srow = x_scale + (size_t)r * (H / 32);
     quantize_row<true>(x + (size_t)(src_row ? src_row[r] : r) * H, x_perm + (size_t)r * H,
-                       x_scale + (size_t)r * (H / 32), H, threadIdx.x, 256);
+                       [&](int b, uint32_t e8, int li) { if (li == 0) srow[b] = (uint8_t)e8; },
+                       H, threadIdx.x, 256);
   }
 }
 
@@ -195,7 +225,7 @@ hipError_t launch_permute(const int32_t* topk_idx, const uint16_t* x, int32_t* c
                static_cast<uint8_t*>(x_perm), static_cast<uint8_t*>(x_perm_scale), R, H, n_rows);
   else if (fp8)
     MOE_LAUNCH("gather_fp8", k_gather_fp8, grid, dim3(256), 0, s, src_row, x,
-               static_cast<uint8_t*>(x_perm), static_cast<float*>(x_perm_scale), R, H, n_rows);
+               static_cast<uint8_t*>(x_perm), static_cast<float*>(x_perm_scale), R, H, R, n_rows);
   else
     MOE_LAUNCH("gather_bf16", k_gather_bf16, grid, dim3(256), 0, s, src_row, x,
                static_cast<uint16_t*>(x_perm), R, H, n_rows);
@@ -203,6 +233,7 @@ hipError_t launch_permute(const int32_t* topk_idx, const uint16_t* x, int32_t* c
 }
 
 hipError_t launch_quantize_rows(const uint16_t* x, uint8_t* xq, void* xs, int T, int H, bool mx,
+                                const int32_t* dest, int k, const int32_t* shared_base, int R,
                                 hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (mx)
@@ -210,9 +241,8 @@ hipError_t launch_quantize_rows(const uint16_t* x, uint8_t* xq, void* xs, int T,
                static_cast<const int32_t*>(nullptr), x, xq, static_cast<uint8_t*>(xs), T, H,
                static_cast<const int32_t*>(nullptr));
   else
-    MOE_LAUNCH("quantize_rows_fp8", k_gather_fp8, dim3(ceil_div(T, kGatherRows)), dim3(256), 0, s,
-               static_cast<const int32_t*>(nullptr), x, xq, static_cast<float*>(xs), T, H,
-               static_cast<const int32_t*>(nullptr));
+    MOE_LAUNCH("quantize_rows_fp8", k_quantize_tokens_fp8, dim3(ceil_div(T, kGatherRows)), dim3(256),
+               0, s, x, xq, static_cast<float*>(xs), T, H, dest, k, shared_base, R);
   return hipGetLastError();
 }
 

@@ -90,7 +90,8 @@ __device__ __forceinline__ void dispatch_small(const int32_t* topk_idx, int32_t*
 // E_all: experts the router scores; E: the routed experts held here.
 // QM: 0 bf16 layer; 1 fp8 and 2 MXFP8 layers, whose GEMMs gather rows of x
 // quantised per token: the workgroup's other waves quantise its tokens' rows
-// of x into xq / xs meanwhile.
+// of x into xq / xs meanwhile (fp8 scales K-block-major, xs[b * T + t];
+// MXFP8 per token, xs[t * H/32 + b]).
 template <int NPL, int QM>
 __global__ __launch_bounds__(1024) void k_route_dispatch_small(
     const float* parts, int KS, const float* __restrict__ bias, int32_t* topk_idx, float* topk_w,
@@ -116,12 +117,17 @@ __global__ __launch_bounds__(1024) void k_route_dispatch_small(
     for (int j = 0; j < kTokPerWg; ++j) {
       const int tt = blockIdx.x * kTokPerWg + j;
       if (tt >= T) break;
-      if constexpr (QM == 2)
+      if constexpr (QM == 2) {
+        uint8_t* srow = static_cast<uint8_t*>(xs) + (size_t)tt * (H / 32);
         quantize_row<true>(x + (size_t)tt * H, xq + (size_t)tt * H,
-                           static_cast<uint8_t*>(xs) + (size_t)tt * (H / 32), H, qt, nq);
-      else
+                           [&](int b, uint32_t e8, int li) { if (li == 0) srow[b] = (uint8_t)e8; },
+                           H, qt, nq);
+      } else {
+        float* xsf = static_cast<float*>(xs);
         quantize_row<false>(x + (size_t)tt * H, xq + (size_t)tt * H,
-                            static_cast<float*>(xs) + (size_t)tt * (H / 128), H, qt, nq);
+                            [&](int b, float sc, int li) { if (li == 0) xsf[(size_t)b * T + tt] = sc; },
+                            H, qt, nq);
+      }
     }
   }
   // Publish this workgroup's routing, then draw a ticket (vector atomic).

@@ -24,7 +24,10 @@
 //     one tile, so its weights are streamed once.
 //   - Scales travel in groups of SG chunks: every SG-th chunk, the first
 //     waves load, per A row (and per B row for MX, or the two weight-block
-//     scale rows for fp8), the scales of the next SG chunks.  MXFP8 with K a
+//     scale rows for fp8), the scales of the next SG chunks.  fp8 activation
+//     scales are stored K-block-major (one K block's scales of consecutive
+//     rows adjacent), so a chunk's row scales are a few whole cache lines
+//     instead of one line per row (3 % per DeepSeek-like layer).  MXFP8 with K a
 //     multiple of 512 uses SG = 4 (one 16-byte request per row per 4 chunks
 //     instead of four 4-byte ones); fp8 uses SG = 1, since 160-row tiles
 //     leave no LDS for 4-chunk scale stages.  A scale stage is reused SG
@@ -171,12 +174,19 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
   const int srow = wave * 64 + lane;
   const bool s_lane = wave < NSC && srow < L::SROWS;
   const uint8_t* ssrc = nullptr;
+  uint32_t sstep = 4;                                // bytes from one chunk's scale to the next
   if (s_lane) {
     const int N128 = N / 128;
     if (srow < BM) {
       const int r = row0 + min(srow, mrows - 1);
-      const size_t ar = (size_t)(p.a_rows ? p.a_rows[r] : r);
-      ssrc = static_cast<const uint8_t*>(p.A_scale) + ar * (size_t)(4 * KB);
+      if constexpr (MX) {
+        const size_t ar = (size_t)(p.a_rows ? p.a_rows[r] : r);
+        ssrc = static_cast<const uint8_t*>(p.A_scale) + ar * (size_t)(4 * KB);
+      } else {                                       // K-block-major: a chunk's row scales adjacent
+        const size_t ar = (size_t)(p.s_rows ? p.s_rows[r] : r);
+        ssrc = static_cast<const uint8_t*>(p.A_scale) + ar * 4;
+        sstep = 4u * (uint32_t)p.s_ld;
+      }
     } else if constexpr (MX) {
       int br = srow - BM;
       const uint8_t* sB = static_cast<const uint8_t*>(p.s_B0);
@@ -201,7 +211,7 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
   auto ops = [&](int c) { return nva + IPWB + ((scale_wave && c % SG == 0) ? 1 : 0); };
   auto issue = [&](int c) {
     if (scale_wave && c % SG == 0) {
-      if (s_lane) dma_addr_untracked<4 * SG>(ssrc + (size_t)c * 4, ss(c) + wave * 64 * L::SB);
+      if (s_lane) dma_addr_untracked<4 * SG>(ssrc + (size_t)c * sstep, ss(c) + wave * 64 * L::SB);
     }
 #pragma unroll
     for (int j = 0; j < IPWA; ++j)
@@ -242,7 +252,7 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
   // the DeepSeek-like layer, same output bits).
   auto issue_part = [&](int c, int j) {
     if (j == 0 && scale_wave && c % SG == 0) {
-      if (s_lane) dma_addr_untracked<4 * SG>(ssrc + (size_t)c * 4, ss(c) + wave * 64 * L::SB);
+      if (s_lane) dma_addr_untracked<4 * SG>(ssrc + (size_t)c * sstep, ss(c) + wave * 64 * L::SB);
     }
     if (j < IPWA) {
       const int ja = j < IPWA ? j : 0;
@@ -453,7 +463,6 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
       if (lane < 16) amax_s[wn * BM + m] = am;
     }
     lds_barrier();
-    const int N128 = N / 128;
 #pragma unroll
     for (int i = 0; i < MB; ++i)
       if (i < nmb) {
@@ -473,7 +482,7 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
             w4 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[2], qv[3], w4, true);
             *reinterpret_cast<uint32_t*>(tile_at(m, wn * 32 + j * 16 + 4 * (lane >> 4))) = (uint32_t)w4;
           }
-          if (wn == 0 && lane < 16) static_cast<float*>(p.out_scale)[(size_t)(row0 + m) * N128 + nt] = scale;
+          if (wn == 0 && lane < 16) static_cast<float*>(p.out_scale)[(size_t)nt * p.R + row0 + m] = scale;
         }
       }
   } else if constexpr (MX) {

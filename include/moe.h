@@ -183,8 +183,10 @@ size_t moe_permute_workspace_bytes(const moe_shape* shape);
  *                per 128 channels (scale = amax / 448, 1 for an all-zero group,
  *                codes rounded to nearest even after clamping to +-448), or for
  *                MOE_MXFP8 its MXFP8 codes (blocks of 32)
- *   x_perm_scale written for fp8 ([R, H/128] fp32) and mxfp8 ([R, H/32] uint8
- *                E8M0); NULL for bf16
+ *   x_perm_scale written for fp8: [H/128, R] fp32, K-block-major (the scale
+ *                of row r, channels 128 b .. 128 b + 127, at b * R + r, so
+ *                one block's scales of consecutive rows are adjacent); for
+ *                mxfp8: [R, H/32] uint8 E8M0; NULL for bf16
  *   workspace    >= moe_permute_workspace_bytes(shape) bytes of device memory,
  *                16-byte aligned (per-tile expert counts); caller-owned
  * Ranks come from counts and bit masks, not atomic counters: the same routing
@@ -206,8 +208,10 @@ int moe_permute(const moe_shape* shape, const int32_t* topk_idx, const void* x,
  * per row in MX blocks of 32, and the products are the block-scaled ones
  * (each 32-value block's E8M0 scales applied to its partial sum).
  *   offsets      [G + 1] int32 (device; read only on the device)
- *   x_perm       [R, H] bf16 or e4m3fn codes; x_perm_scale [R, H/128] fp32
- *                (fp8) or [R, H/32] uint8 E8M0 (mxfp8), NULL for bf16
+ *   x_perm       [R, H] bf16 or e4m3fn codes; x_perm_scale [H/128, R] fp32
+ *                (fp8, K-block-major as moe_permute writes it, R = T*(k +
+ *                n_shared) slots per block) or [R, H/32] uint8 E8M0 (mxfp8),
+ *                NULL for bf16
  *   w_gate, w_up [G, I, H] bf16 or e4m3fn codes
  *   w_down       [G, H, I] bf16 or e4m3fn codes
  *   s_gate, s_up fp8: [G, I/128, H/128] fp32 block scales; mxfp8: [G, I, H/32]

@@ -62,7 +62,8 @@ def run_permute(cfg, idx, x):
     if cfg.wdtype == "mxfp8":
         x_scale = torch.empty((R, cfg.H // 32), dtype=torch.uint8, device=DEV)
     elif fp8:
-        x_scale = torch.empty((R, cfg.H // 128), dtype=torch.float32, device=DEV)
+        # K-block-major: the R row scales of each 128-channel block are adjacent
+        x_scale = torch.empty((cfg.H // 128, R), dtype=torch.float32, device=DEV)
     else:
         x_scale = None
     ws = torch.empty(max(moe.moe_permute_workspace_bytes(sh), 16), dtype=torch.uint8, device=DEV)

@@ -145,7 +145,7 @@ def _check_permute(cfg, li, idx):
     if cfg.wdtype == "fp8":
         codes, scales = oracle.quantize_groups_128(oracle.bf16_bits_to_f32(xb))
         assert np.array_equal(x_perm.cpu().numpy()[:R], codes[s_ref])
-        assert np.array_equal(x_scale.cpu().numpy()[:R], scales[s_ref])
+        assert np.array_equal(x_scale.cpu().numpy()[:, :R].T, scales[s_ref])   # [H/128, R] layout
     elif cfg.wdtype == "mxfp8":
         codes, e8 = oracle.mx_quantize_rows(oracle.bf16_bits_to_f32(xb))
         assert np.array_equal(x_perm.cpu().numpy()[:R], codes[s_ref])
@@ -202,7 +202,10 @@ def _ffn_case(cfg, sizes, seed):
     if cfg.wdtype == "fp8":
         codes, scales = oracle.quantize_groups_128(xr)
         x_perm = torch.from_numpy(codes).to(DEV)
-        x_scale = torch.from_numpy(scales).to(DEV)
+        # the library takes fp8 activation scales K-block-major, [H/128, T*(k+n_shared)]
+        xs = np.zeros((cfg.H // 128, cfg.R), dtype=np.float32)
+        xs[:, :R] = scales.T
+        x_scale = torch.from_numpy(xs).to(DEV)
         xo = oracle.fp8_e4m3.dequantize_groups_128(codes, scales)
     elif cfg.wdtype == "mxfp8":
         codes, e8 = oracle.mx_quantize_rows(xr)
