@@ -35,6 +35,13 @@ __device__ __forceinline__ void wait_vmcnt_le(int v) {
   }
 }
 
+// s_waitcnt vmcnt(V) for a compile-time V, other counters untouched.
+template <int V>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(V >= 0 && V < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() would also
 // wait for every outstanding vector-memory operation, including the
 // direct-to-LDS loads of later chunks, and drain the pipeline; completion of

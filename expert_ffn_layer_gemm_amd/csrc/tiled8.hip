@@ -37,6 +37,14 @@
 //     part between each two columns of the second half's MFMAs; each wave
 //     waits with explicit vm-counter counts (its own loads land in issue
 //     order), then an LDS-only barrier publishes the chunk.
+//   - Every wave issues the same number of loads for every chunk index: A
+//     blocks past the tile and the scale loads of waves (or chunks) without
+//     one go to a 1 KB LDS sink, and the chunks after the last re-read the
+//     last one.  All waits are then compile-time counts, and the loop carries
+//     no per-wave or per-chunk bookkeeping (a scalar branch tree per wait,
+//     stage indices by division, masked scale loads): with one loop copy per
+//     count of valid row blocks it runs about 40 % fewer instructions per
+//     chunk, which is what the waves' issue slots were spent on.
 //   - fp8 computes D = B A^T (weights times activations): a lane's four
 //     outputs of a 16 x 16 block are then four consecutive columns of one
 //     row, so one activation scale times one weight-block scale rescales them
@@ -47,7 +55,8 @@
 //     the boundary, reads the next chunk's A fragments of the first half, and
 //     multiplies the second half column by column, reading the next chunk's B
 //     fragment j as soon as column j is done.  Row blocks past the group's end
-//     are neither read nor multiplied (uniform branches).
+//     are not multiplied: the loop is compiled once per count of valid row
+//     blocks.
 //   - A direct-to-LDS instruction writes 1 KB (8 staged rows of 128 B; lane i
 //     at +16 i); row r's 16-byte piece c sits in slot c ^ (r & 7), which makes
 //     the fragment reads (16 lanes on 16 rows, one piece) conflict-free.
@@ -92,9 +101,14 @@ struct Tiled8Lds {
   static constexpr int B_BYTES = k8BRows * 128;
   static constexpr int SROWS = MX ? BM + k8BRows : BM + 2;   // scale rows of a stage
   static constexpr int SB = 4 * SG;                           // bytes per scale row and stage
-  static constexpr int SSTAGE = (SROWS * SB + 255) / 256 * 256;
+  static constexpr int NSC = (SROWS + 63) / 64;               // waves that load scales
+  // A scale stage has a slot for every lane of those waves (lanes past the
+  // scale rows load a duplicate into their own slot, so no lane is masked).
+  static constexpr int SSTAGE = (NSC * 64 * SB + 255) / 256 * 256;
   static constexpr int NSS = (k8NS + SG - 1 + SG - 1) / SG;  // scale stages
-  static constexpr int TOTAL = k8NS * A_BYTES + k8NS * B_BYTES + NSS * SSTAGE;
+  // 1 KB sink for the loads that only keep every wave's load count equal.
+  static constexpr int SINK = k8NS * A_BYTES + k8NS * B_BYTES + NSS * SSTAGE;
+  static constexpr int TOTAL = SINK + 1024;
 };
 
 template <bool MX, bool DUAL, int BM, int SG>
@@ -102,21 +116,27 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using L = Tiled8Lds<MX, BM, SG>;
   static_assert(L::TOTAL <= 160 * 1024, "LDS budget");
-  static_assert(SG == 1 || SG == 4, "16-byte or 4-byte scale loads");
+  static_assert(SG == 1 || (SG == 4 && L::NSS == 2), "4-byte scale loads, or 16-byte ones in 2 stages");
   constexpr int NS = k8NS;
   constexpr int NW = 8, WN = 4;
   constexpr int MB = BM / 32;                       // 16-row blocks per wave (2 wave rows)
   constexpr int NB = 4;                             // 16-column blocks per wave
   constexpr int HA = MB / 2;                        // row blocks multiplied before the boundary
   constexpr int A_BLK = BM / 8;                     // 1 KB DMA blocks of an A chunk
-  constexpr int IPWA = (A_BLK + NW - 1) / NW;
+  constexpr int IPWA = (A_BLK + NW - 1) / NW;       // A blocks per wave (block j * NW + wave)
   constexpr int IPWB = L::B_BYTES / 1024 / NW;
-  constexpr int NSC = (L::SROWS + 63) / 64;         // waves that load scales
+  constexpr int NSC = L::NSC;
   static_assert(NSC <= NW, "scale rows");
   static_assert(IPWB == NB && IPWA <= NB, "one load part per column");
+  // Every wave issues exactly OPS loads for every chunk index: A blocks past
+  // the tile and scale loads of waves or chunks without one go to the sink,
+  // chunks past the end re-read the last chunk.  Every vm-counter wait is then
+  // a compile-time count (no per-wave or per-chunk bookkeeping in the loop).
+  constexpr int OPS = IPWA + IPWB + 1;
   constexpr int B_RING = NS * L::A_BYTES;
   constexpr int S_RING = B_RING + NS * L::B_BYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[L::TOTAL];
+  uint8_t* const sink = lds + L::SINK;
 
   int tslot, nt;
   if (!band_item(p.sc.tiles, *p.sc.n_tiles, p.n_ntile, tslot, nt)) return;
@@ -134,51 +154,55 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
   const int ncols = DUAL ? 128 : min(256, N - n0);
   const int r16 = lane & 15;
 
-  // A DMA blocks of this wave: block a = wave * IPWA + j holds tile rows
-  // 8a .. 8a+7; blocks past the tile or wholly past the group's end are not
-  // fetched (their rows are never stored).
-  const uint8_t* ab[IPWA];
+  // A DMA blocks of this wave: block a = j * NW + wave holds tile rows
+  // 8a .. 8a+7; rows past the group's end re-read its last row (never
+  // stored), blocks past the tile load into the sink.
+  const uint8_t* const ab = p.a_rows ? p.A : p.A + (size_t)row0 * K;
   uint32_t aoff[IPWA];
-  bool av[IPWA];
-  int nva = 0;
+  bool ain[IPWA];
 #pragma unroll
   for (int j = 0; j < IPWA; ++j) {
-    const int blk = wave * IPWA + j;
+    const int blk = j * NW + wave;
     const int row = blk * 8 + lane / 8;
     const uint32_t sl = (uint32_t)(slot8(row, lane % 8) * 16);
-    av[j] = blk < A_BLK && blk * 8 < mrows;
+    ain[j] = blk < A_BLK;
     const int r = min(row, mrows - 1);
-    ab[j] = p.a_rows ? p.A : p.A + (size_t)row0 * K;
     aoff[j] = (p.a_rows ? (uint32_t)p.a_rows[row0 + r] : (uint32_t)r) * (uint32_t)K + sl;
-    nva += av[j] ? 1 : 0;
   }
-  const uint8_t* bb[IPWB];
+  // B: this wave's 32 staged rows come from one matrix (DUAL: waves 0-3 the
+  // gate rows, 4-7 the up rows).
+  const uint8_t* bb;
   uint32_t boff[IPWB];
-#pragma unroll
-  for (int j = 0; j < IPWB; ++j) {
-    int br = (wave * IPWB + j) * 8;
+  {
+    int br0 = wave * IPWB * 8;
     const uint8_t* B = p.B0;
-    if (DUAL && br >= 128) { B = p.B1; br -= 128; }
-    const int row = (wave * IPWB + j) * 8 + lane / 8;
-    const uint32_t sl = (uint32_t)(slot8(row, lane % 8) * 16);
-    bb[j] = B + (size_t)g * N * K;
-    // Rows past the matrix (ragged last column tile) re-read its last row.
-    boff[j] = (uint32_t)min(n0 + br + lane / 8, N - 1) * (uint32_t)K + sl;
+    if (DUAL && br0 >= 128) { B = p.B1; br0 -= 128; }
+    bb = B + (size_t)g * N * K;
+#pragma unroll
+    for (int j = 0; j < IPWB; ++j) {
+      const int row = (wave * IPWB + j) * 8 + lane / 8;
+      const uint32_t sl = (uint32_t)(slot8(row, lane % 8) * 16);
+      // Rows past the matrix (ragged last column tile) re-read its last row.
+      boff[j] = (uint32_t)min(n0 + br0 + j * 8 + lane / 8, N - 1) * (uint32_t)K + sl;
+    }
   }
 
-  // Scale row of this lane (waves < NSC): srow < BM the A row's scales;
-  // fp8: srow = BM, BM+1 the two weight-block scale rows of the tile (DUAL:
-  // gate, up; single: the tile's two 128-column blocks); MX: srow = BM + b
-  // the E8M0 row of staged B row b.  A stage holds SB bytes per scale row:
-  // chunks SG*q .. SG*q+SG-1 of the row's scales (4 bytes per chunk).
+  // Scale row of this lane (waves < NSC; sr = srow clamped to the rows
+  // there are): sr < BM the A row's scales; fp8: sr = BM, BM+1 the two
+  // weight-block scale rows of the tile (DUAL: gate, up; single: the tile's
+  // two 128-column blocks); MX: sr = BM + b the E8M0 row of staged B row b.
+  // A stage holds SB bytes per lane: chunks SG*q .. SG*q+SG-1 of the row's
+  // scales (4 bytes per chunk).  Waves >= NSC compute a valid address too
+  // (their loads go to the sink).
   const int srow = wave * 64 + lane;
-  const bool s_lane = wave < NSC && srow < L::SROWS;
-  const uint8_t* ssrc = nullptr;
+  const int sr = min(srow, L::SROWS - 1);
+  const bool swave = wave < NSC;
+  const uint8_t* ssrc;
   uint32_t sstep = 4;                                // bytes from one chunk's scale to the next
-  if (s_lane) {
+  {
     const int N128 = N / 128;
-    if (srow < BM) {
-      const int r = row0 + min(srow, mrows - 1);
+    if (sr < BM) {
+      const int r = row0 + min(sr, mrows - 1);
       if constexpr (MX) {
         const size_t ar = (size_t)(p.a_rows ? p.a_rows[r] : r);
         ssrc = static_cast<const uint8_t*>(p.A_scale) + ar * (size_t)(4 * KB);
@@ -188,12 +212,12 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
         sstep = 4u * (uint32_t)p.s_ld;
       }
     } else if constexpr (MX) {
-      int br = srow - BM;
+      int br = sr - BM;
       const uint8_t* sB = static_cast<const uint8_t*>(p.s_B0);
       if (DUAL && br >= 128) { sB = static_cast<const uint8_t*>(p.s_B1); br -= 128; }
       ssrc = sB + ((size_t)g * N + min(n0 + br, N - 1)) * (size_t)(K / 32);
     } else {
-      const int which = srow - BM;
+      const int which = sr - BM;
       if (DUAL)
         ssrc = static_cast<const uint8_t*>(which ? p.s_B1 : p.s_B0) +
                ((size_t)g * N128 + nt) * (size_t)(4 * KB);
@@ -203,63 +227,38 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
     }
   }
 
-  auto sa = [&](int c) { return lds + (c % NS) * L::A_BYTES; };
-  auto sbs = [&](int c) { return lds + B_RING + (c % NS) * L::B_BYTES; };
-  auto ss = [&](int c) { return lds + S_RING + ((c / SG) % L::NSS) * L::SSTAGE; };
-  const bool scale_wave = wave < NSC;
-  // vm instructions this wave issues for chunk c
-  auto ops = [&](int c) { return nva + IPWB + ((scale_wave && c % SG == 0) ? 1 : 0); };
-  auto issue = [&](int c) {
-    if (scale_wave && c % SG == 0) {
-      if (s_lane) dma_addr_untracked<4 * SG>(ssrc + (size_t)c * sstep, ss(c) + wave * 64 * L::SB);
-    }
-#pragma unroll
-    for (int j = 0; j < IPWA; ++j)
-      if (av[j]) dma16_untracked(ab[j] + (size_t)c * 128, aoff[j], sa(c) + (wave * IPWA + j) * 1024);
-#pragma unroll
-    for (int j = 0; j < IPWB; ++j)
-      dma16_untracked(bb[j] + (size_t)c * 128, boff[j], sbs(c) + (wave * IPWB + j) * 1024);
+  // Ring positions: chunk c sits in A and B stage c % NS (kept as a running
+  // stage index, not recomputed) and in scale stage (c / SG) % NSS.
+  auto a_st = [&](int st) { return lds + st * L::A_BYTES; };
+  auto b_st = [&](int st) { return lds + B_RING + st * L::B_BYTES; };
+  auto s_st = [&](int c, int st) {
+    const int ss = SG == 1 ? st : ((c >> 2) & 1);
+    return lds + S_RING + ss * L::SSTAGE;
   };
-  constexpr int OPS_MAX = IPWA + IPWB + 1;
-#pragma unroll
-  for (int c = 0; c < NS; ++c)
-    if (c < nk) issue(c);
-  {
-    int later = 0;   // issued after chunk 0
-#pragma unroll
-    for (int c = 1; c < NS; ++c)
-      if (c < nk) later += ops(c);
-    wait_vmcnt_le<(NS - 1) * OPS_MAX>(later);
-  }
-  lds_barrier();
-  // Boundary of chunk kc (after this wave's last read of it): wait for chunk
-  // kc+1 (loads issued after it: chunks kc+2 .. kc+NS-1), barrier, then
-  // issue chunk kc+NS into the stages chunk kc used.
-  auto boundary = [&](int kc) {
-    if (kc + 1 < nk) {
-      int later = 0;
-#pragma unroll
-      for (int c = kc + 2; c < kc + NS; ++c)
-        if (c < nk) later += ops(c);
-      wait_vmcnt_le<(NS - 2) * OPS_MAX>(later);
-    }
-    lds_barrier();
-  };
-  // Part j (of NB) of chunk c's loads: the scale load with part 0, A block j
-  // (if any), B block j.  Chunk kc+NS's parts are issued between the columns
-  // of chunk kc's second half (after its boundary, so its stages are free):
-  // spread out, not as one burst after the barrier (measured 5 % faster on
-  // the DeepSeek-like layer, same output bits).
-  auto issue_part = [&](int c, int j) {
-    if (j == 0 && scale_wave && c % SG == 0) {
-      if (s_lane) dma_addr_untracked<4 * SG>(ssrc + (size_t)c * sstep, ss(c) + wave * 64 * L::SB);
+  // Part j (of NB) of chunk c's loads into stage st: the scale load with part
+  // 0, A block j (if any), B block j.  Chunk kc+NS's parts are issued between
+  // the columns of chunk kc's second half (after its boundary, so its stages
+  // are free): spread out, not as one burst after the barrier (measured 5 %
+  // faster on the DeepSeek-like layer, same output bits).
+  auto issue_part = [&](int c, int st, int j) {
+    const int cc = min(c, nk - 1);
+    if (j == 0) {
+      uint8_t* const dst = (swave && c % SG == 0) ? s_st(c, st) + wave * 64 * L::SB : sink;
+      dma_addr_untracked<L::SB>(ssrc + (size_t)(cc - cc % SG) * sstep, dst);
     }
     if (j < IPWA) {
       const int ja = j < IPWA ? j : 0;
-      if (av[ja]) dma16_untracked(ab[ja] + (size_t)c * 128, aoff[ja], sa(c) + (wave * IPWA + ja) * 1024);
+      uint8_t* const dst = ain[ja] ? a_st(st) + (ja * NW + wave) * 1024 : sink;
+      dma16_untracked(ab + (size_t)cc * 128, aoff[ja], dst);
     }
-    dma16_untracked(bb[j] + (size_t)c * 128, boff[j], sbs(c) + (wave * IPWB + j) * 1024);
+    dma16_untracked(bb + (size_t)cc * 128, boff[j], b_st(st) + (wave * IPWB + j) * 1024);
   };
+#pragma unroll
+  for (int c = 0; c < NS; ++c)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) issue_part(c, c, j);
+  wait_vmcnt<(NS - 1) * OPS>();                      // chunk 0 is in
+  lds_barrier();
 
   // Valid 16-row blocks of this wave (0 for a wave without columns).
   const int rbase = wm * (BM / 2);
@@ -282,8 +281,9 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
     return i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                    (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   };
-  auto sword = [&](int kc, int r) {                  // scale dword of scale row r, chunk kc
-    return *reinterpret_cast<const uint32_t*>(ss(kc) + r * L::SB + (kc % SG) * 4);
+  // scale dword of scale row r for chunk c (scale stage base sb)
+  auto sword = [&](const uint8_t* sb, int c, int r) {
+    return *reinterpret_cast<const uint32_t*>(sb + r * L::SB + (c % SG) * 4);
   };
 
   i32x8_t a[MB], b[NB];
@@ -293,23 +293,26 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
   // scale cover them); MXFP8 activations by weights.
   float saf[MB];                                   // fp8: activation scale of the lane's row
   float sb_lo = 0.f, sb_hi = 0.f;                  // fp8: weight block scales
-  auto next_a = [&](int kc, int i) {
+  // Fragment reads of chunk c from stage st (read unconditionally, also for
+  // the chunk after the last: in-bounds LDS, never used).
+  auto next_a = [&](int c, int st, int i) {
     const int r = rbase + i * 16 + r16;
-    a[i] = rd_frag(sa(kc) + r * 128, r);
+    a[i] = rd_frag(a_st(st) + r * 128, r);
     if constexpr (MX) {
-      sam[i] = (sword(kc, r) >> sh) & 0xFFu;
+      sam[i] = (sword(s_st(c, st), c, r) >> sh) & 0xFFu;
     } else {
-      saf[i] = __uint_as_float(sword(kc, r));
+      saf[i] = __uint_as_float(sword(s_st(c, st), c, r));
     }
   };
-  auto next_b = [&](int kc, int j) {
+  auto next_b = [&](int c, int st, int j) {
     const int br = b8_row<DUAL>(j, wn, r16);
-    b[j] = rd_frag(sbs(kc) + br * 128, br);
-    if constexpr (MX) sbm[j] = (sword(kc, BM + br) >> sh) & 0xFFu;
+    b[j] = rd_frag(b_st(st) + br * 128, br);
+    if constexpr (MX) sbm[j] = (sword(s_st(c, st), c, BM + br) >> sh) & 0xFFu;
   };
-  auto rd_bsc = [&](int kc) {
+  auto rd_bsc = [&](int c, int st) {
     if constexpr (!MX) {
-      const float s0 = __uint_as_float(sword(kc, BM)), s1 = __uint_as_float(sword(kc, BM + 1));
+      const uint8_t* sb = s_st(c, st);
+      const float s0 = __uint_as_float(sword(sb, c, BM)), s1 = __uint_as_float(sword(sb, c, BM + 1));
       sb_lo = DUAL ? s0 : (wn < 2 ? s0 : s1);
       sb_hi = DUAL ? s1 : sb_lo;
     }
@@ -341,20 +344,18 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
   };
 
   auto main_loop = [&](auto nm) {
-  const int NMB = count_value(nm);
   // Prologue reads: chunk 0's B fragments, A of the first half, block scales.
 #pragma unroll
-  for (int j = 0; j < NB; ++j)
-    if (NMB > 0) next_b(0, j);
+  for (int j = 0; j < NB; ++j) next_b(0, 0, j);
 #pragma unroll
-  for (int i = 0; i < HA; ++i)
-    if (i < NMB) next_a(0, i);
-  rd_bsc(0);
+  for (int i = 0; i < HA; ++i) next_a(0, 0, i);
+  rd_bsc(0, 0);
+  int st = 0;                                      // stage of chunk kc
   for (int kc = 0; kc < nk; ++kc) {
+    const int sn = st == NS - 1 ? 0 : st + 1;      // stage of chunk kc + 1
     // A fragments of the second half (the stage is refilled at the boundary).
 #pragma unroll
-    for (int i = HA; i < MB; ++i)
-      if (i < NMB) next_a(kc, i);
+    for (int i = HA; i < MB; ++i) next_a(kc, st, i);
     // First half: row blocks [0, HA), column by column; a column's partials
     // are scaled into the accumulators one column later.
 #pragma unroll
@@ -369,33 +370,37 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
     for (int i = 0; i < HA; ++i)
 #pragma unroll
       for (int j = 0; j < NB; ++j) asm volatile("" : "+v"(acc[i][j]));
-    boundary(kc);
-    const bool more = kc + 1 < nk;
+    // Boundary of chunk kc: wait for chunk kc+1 (chunk kc+2's loads may be
+    // in flight), barrier; then chunk kc+NS goes into the stages chunk kc used.
+    wait_vmcnt<(NS - 2) * OPS>();
+    lds_barrier();
     // The next chunk's A fragments of the first half (registers just freed).
 #pragma unroll
-    for (int i = 0; i < HA; ++i)
-      if (more && i < NMB) next_a(kc + 1, i);
+    for (int i = 0; i < HA; ++i) next_a(kc + 1, sn, i);
     __builtin_amdgcn_sched_barrier(0);
     // Second half, column by column; B fragment j of the next chunk is read
     // as soon as column j is done.
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       col(HA, MB, j, nm);
-      if (kc + NS < nk) issue_part(kc + NS, j);
+      issue_part(kc + NS, st, j);
       if (j > 0) scale_col(HA, MB, j - 1, nm);
-      if (more && NMB > 0) next_b(kc + 1, j);
+      next_b(kc + 1, sn, j);
       __builtin_amdgcn_sched_barrier(0);
     }
     scale_col(HA, MB, NB - 1, nm);
-    if (more) rd_bsc(kc + 1);
+    rd_bsc(kc + 1, sn);
+    st = sn;
   }
   };
-  // MXFP8: one copy of the loop per count of valid row blocks (2 % faster on
-  // the MXFP8 prefill layer); fp8: one loop with runtime checks (the
-  // specialised copies were 3 % slower on the DeepSeek-like layer, whose two
-  // wave rows usually hold different counts and so run different copies).
-  if constexpr (MX) with_count<MB>(nmb, main_loop);
-  else main_loop(nmb);
+  // One copy of the loop per count of valid row blocks: no row-block branch
+  // inside (with the uniform load counts, the DeepSeek-like layer went from
+  // 3.20 to 2.87 ms; runtime checks there cost a scalar branch per block and
+  // column).
+  with_count<MB>(nmb, main_loop);
+  // The loads of the chunks past the end (re-reads into the ring and the
+  // sink) land before the epilogue reuses the ring.
+  wait_vmcnt<0>();
 
   // Epilogue.  MXFP8: the lane holds rows rbase + 16 i + 4 (lane/16) + q of
   // its blocks, column lane % 16; fp8: see below.
