@@ -273,18 +273,32 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
 
   // A lane's 32 codes: K bytes 16*(lane/16) .. +16 and 64 + 16*(lane/16) .. +16
   // (the same positions for A and B, so the pairing inside the MFMA is right).
+  // Every 16-row block starts at a multiple of 8 rows, so the slot map of the
+  // lane's row depends on r16 only: a fragment read is a per-stage base (one
+  // add per stage and ring) plus a compile-time offset per block.
   const int c0 = lane >> 4, c1 = 4 + (lane >> 4);
   const int sh = 8 * (lane >> 4);                  // MX: byte of this lane's K block
-  auto rd_frag = [&](const uint8_t* rowp, int row) {
-    const u32x4_t lo = lds_read16(rowp + (slot8(row, c0) << 4));
-    const u32x4_t hi = lds_read16(rowp + (slot8(row, c1) << 4));
-    return i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                   (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  const uint32_t a_lo0 = (uint32_t)((rbase + r16) * 128 + (slot8(r16, c0) << 4));
+  const uint32_t a_hi0 = (uint32_t)((rbase + r16) * 128 + (slot8(r16, c1) << 4));
+  const int brow0 = b8_row<DUAL>(0, wn, r16);
+  const uint32_t b_lo0 = (uint32_t)(B_RING + brow0 * 128 + (slot8(r16, c0) << 4));
+  const uint32_t b_hi0 = (uint32_t)(B_RING + brow0 * 128 + (slot8(r16, c1) << 4));
+  const uint32_t s_a0 = (uint32_t)(S_RING + (rbase + r16) * L::SB);   // A row scales
+  const uint32_t s_b0 = (uint32_t)(S_RING + (BM + brow0) * L::SB);    // MX: B row scales
+  // opaque to the compiler, so the per-block offsets stay immediates
+  auto opq = [](uint32_t v) { asm volatile("" : "+v"(v)); return v; };
+  auto frag_at = [&](uint32_t lo, uint32_t hi) {
+    const u32x4_t x = lds_read16(lds + lo), y = lds_read16(lds + hi);
+    return i32x8_t{(int)x[0], (int)x[1], (int)x[2], (int)x[3],
+                   (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
   };
-  // scale dword of scale row r for chunk c (scale stage base sb)
-  auto sword = [&](const uint8_t* sb, int c, int r) {
-    return *reinterpret_cast<const uint32_t*>(sb + r * L::SB + (c % SG) * 4);
+  // LDS byte offset of scale stage of chunk c (ring stage st) plus the chunk's
+  // dword inside a scale slot
+  auto s_off = [&](int c, int st) {
+    const int ss = SG == 1 ? st : ((c >> 2) & 1);
+    return (uint32_t)(ss * L::SSTAGE + (c % SG) * 4);
   };
+  auto ld32 = [&](uint32_t off) { return *reinterpret_cast<const uint32_t*>(lds + off); };
 
   i32x8_t a[MB], b[NB];
   uint32_t sam[MB], sbm[NB];                       // MX: E8M0 bytes
@@ -293,26 +307,30 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
   // scale cover them); MXFP8 activations by weights.
   float saf[MB];                                   // fp8: activation scale of the lane's row
   float sb_lo = 0.f, sb_hi = 0.f;                  // fp8: weight block scales
-  // Fragment reads of chunk c from stage st (read unconditionally, also for
-  // the chunk after the last: in-bounds LDS, never used).
-  auto next_a = [&](int c, int st, int i) {
-    const int r = rbase + i * 16 + r16;
-    a[i] = rd_frag(a_st(st) + r * 128, r);
-    if constexpr (MX) {
-      sam[i] = (sword(s_st(c, st), c, r) >> sh) & 0xFFu;
-    } else {
-      saf[i] = __uint_as_float(sword(s_st(c, st), c, r));
-    }
+  // Per-stage read bases of chunk c in ring stage st.
+  struct Bases { uint32_t alo, ahi, blo, bhi, sa, sb; };
+  auto bases = [&](int c, int st) {
+    const uint32_t so = s_off(c, st);
+    return Bases{opq(a_lo0 + st * L::A_BYTES), opq(a_hi0 + st * L::A_BYTES),
+                 opq(b_lo0 + st * L::B_BYTES), opq(b_hi0 + st * L::B_BYTES),
+                 opq(s_a0 + so), MX ? opq(s_b0 + so) : 0u};
   };
-  auto next_b = [&](int c, int st, int j) {
-    const int br = b8_row<DUAL>(j, wn, r16);
-    b[j] = rd_frag(b_st(st) + br * 128, br);
-    if constexpr (MX) sbm[j] = (sword(s_st(c, st), c, BM + br) >> sh) & 0xFFu;
+  // Fragment reads (read unconditionally, also for the chunk after the last:
+  // in-bounds LDS, never used).
+  auto next_a = [&](const Bases& q, int i) {
+    a[i] = frag_at(q.alo + i * 2048, q.ahi + i * 2048);
+    if constexpr (MX) sam[i] = (ld32(q.sa + i * 16 * L::SB) >> sh) & 0xFFu;
+    else saf[i] = __uint_as_float(ld32(q.sa + i * 16 * L::SB));
+  };
+  auto next_b = [&](const Bases& q, int j) {
+    const int dr = b8_row<DUAL>(j, 0, 0);          // row offset of block j
+    b[j] = frag_at(q.blo + dr * 128, q.bhi + dr * 128);
+    if constexpr (MX) sbm[j] = (ld32(q.sb + dr * L::SB) >> sh) & 0xFFu;
   };
   auto rd_bsc = [&](int c, int st) {
     if constexpr (!MX) {
-      const uint8_t* sb = s_st(c, st);
-      const float s0 = __uint_as_float(sword(sb, c, BM)), s1 = __uint_as_float(sword(sb, c, BM + 1));
+      const uint32_t o = S_RING + s_off(c, st) + BM * L::SB;
+      const float s0 = __uint_as_float(ld32(o)), s1 = __uint_as_float(ld32(o + L::SB));
       sb_lo = DUAL ? s0 : (wn < 2 ? s0 : s1);
       sb_hi = DUAL ? s1 : sb_lo;
     }
@@ -345,17 +363,23 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
 
   auto main_loop = [&](auto nm) {
   // Prologue reads: chunk 0's B fragments, A of the first half, block scales.
+  {
+    const Bases q0 = bases(0, 0);
 #pragma unroll
-  for (int j = 0; j < NB; ++j) next_b(0, 0, j);
+    for (int j = 0; j < NB; ++j) next_b(q0, j);
 #pragma unroll
-  for (int i = 0; i < HA; ++i) next_a(0, 0, i);
+    for (int i = 0; i < HA; ++i) next_a(q0, i);
+  }
   rd_bsc(0, 0);
   int st = 0;                                      // stage of chunk kc
   for (int kc = 0; kc < nk; ++kc) {
     const int sn = st == NS - 1 ? 0 : st + 1;      // stage of chunk kc + 1
     // A fragments of the second half (the stage is refilled at the boundary).
+    {
+      const Bases qk = bases(kc, st);
 #pragma unroll
-    for (int i = HA; i < MB; ++i) next_a(kc, st, i);
+      for (int i = HA; i < MB; ++i) next_a(qk, i);
+    }
     // First half: row blocks [0, HA), column by column; a column's partials
     // are scaled into the accumulators one column later.
 #pragma unroll
@@ -375,8 +399,9 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
     wait_vmcnt<(NS - 2) * OPS>();
     lds_barrier();
     // The next chunk's A fragments of the first half (registers just freed).
+    const Bases qn = bases(kc + 1, sn);
 #pragma unroll
-    for (int i = 0; i < HA; ++i) next_a(kc + 1, sn, i);
+    for (int i = 0; i < HA; ++i) next_a(qn, i);
     __builtin_amdgcn_sched_barrier(0);
     // Second half, column by column; B fragment j of the next chunk is read
     // as soon as column j is done.
@@ -385,7 +410,7 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
       col(HA, MB, j, nm);
       issue_part(kc + NS, st, j);
       if (j > 0) scale_col(HA, MB, j - 1, nm);
-      next_b(kc + 1, sn, j);
+      next_b(qn, j);
       __builtin_amdgcn_sched_barrier(0);
     }
     scale_col(HA, MB, NB - 1, nm);
