@@ -764,7 +764,16 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
 
   // No group above the skinny limit: no tiled work, skip its launches (decode).
   const bool tiled = f.max_group_rows > skinny_max_rows(f.T);
-  SideStream* side = tiled && !prof_serial() && !f.one_stream ? side_stream() : nullptr;
+  // The streaming chain gets a stream of its own only when the routing is
+  // expected to leave real work for it next to the tiled one (mean rows per
+  // group at most twice the skinny limit, e.g. the Zipf-routed Qwen3.5-like
+  // layer: 20); with larger groups nearly every group is tiled, and the
+  // mostly empty streaming launches then cost more concurrently than after
+  // the tiled chain on one stream (DeepSeek-like layer 2.86 -> 2.83 ms,
+  // Qwen3-like prefill 2.66 -> 2.645; the Zipf layer 1.41 -> 1.44 on one).
+  const long long mean_rows = (long long)f.T * f.k / std::max(1, f.E);
+  const bool mixed = mean_rows <= 2LL * skinny_max_rows(f.T);
+  SideStream* side = tiled && mixed && !prof_serial() && !f.one_stream ? side_stream() : nullptr;
   hipStream_t ks = s;                // stream of the streaming chain
   if (side) {                        // fork after the plan
     hipError_t e = hipEventRecord(side->fork, s);
