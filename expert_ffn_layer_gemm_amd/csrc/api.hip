@@ -79,10 +79,12 @@ size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 // forward path never builds x_perm: the GEMMs gather their rows through
 // src_row from x (bf16) or from x quantised once per token (fp8, mxfp8: xq,
 // xs).  fp8 scales are K-block-major: per permuted row ([H/128][R], R slots
-// per block) for large batches, per token ([H/128][T]) for small ones, whose
-// routing launch quantises before the rows are known.
+// per block) for large batches (quantised per token into xs_tok, then moved
+// to the rows once the ranks are known), per token ([H/128][T]) for small
+// ones, whose routing launch quantises before the rows are known.
 struct FwdLayout {
-  size_t logits, rpart, idx, w, counts, offsets, tcnt, tick, dest, src_row, xq, xs, y_perm, ffn, total;
+  size_t logits, rpart, idx, w, counts, offsets, tcnt, tick, dest, src_row, xq, xs, xs_tok, y_perm, ffn,
+      total;
 };
 
 FwdLayout fwd_layout(const moe_shape* s) {
@@ -103,6 +105,7 @@ FwdLayout fwd_layout(const moe_shape* s) {
   L.src_row = off; off += align256(R * 4);
   L.xq = off;      off += fp8 ? align256(T * H) : 0;
   L.xs = off;      off += mx ? align256(T * (H / 32)) : fp8 ? align256(R * (H / 128) * 4) : 0;
+  L.xs_tok = off;  off += (fp8 && !mx) ? align256(T * (H / 128) * 4) : 0;
   L.y_perm = off;  off += align256(R * H * 2);
   L.ffn = off;
   off += moe::ffn_workspace_bytes(s->T, s->H, n_local(s), s->k, s->I, s->n_shared, fp8, mx);
@@ -159,6 +162,7 @@ hipError_t forward_launch(const moe_shape* shape, const void* x, const float* w_
   int32_t* src_row = reinterpret_cast<int32_t*>(ws + L.src_row);
   uint8_t* xq = fp8 ? ws + L.xq : nullptr;
   void* xs = fp8 ? static_cast<void*>(ws + L.xs) : nullptr;
+  float* xs_tok = (fp8 && !mx) ? reinterpret_cast<float*>(ws + L.xs_tok) : nullptr;
   void* y_perm = ws + L.y_perm;
 
   // Router: slice partial sums (or, unsplit, the raw products in the logits
@@ -176,7 +180,24 @@ hipError_t forward_launch(const moe_shape* shape, const void* x, const float* w_
     a.s_ld = shape->T;
   }
   int32_t* tick = reinterpret_cast<int32_t*>(ws + L.tick);
-  hipError_t e = moe::launch_router_gemm(static_cast<const uint16_t*>(x), w_router, parts,
+  hipError_t e = hipSuccess;
+  // Large 8-bit batches: the per-token quantisation of x needs no routing, so
+  // it runs on a side stream beside the router GEMM, top-k and ranks (forked
+  // after everything already on s, so an earlier call's GEMMs are done with
+  // the buffers) and is joined before the FFN.
+  void* xs_q = mx ? xs : static_cast<void*>(xs_tok);
+  moe::SideStream* qs = nullptr;
+  if (fp8 && !small && !one_stream && !moe::prof_serial()) qs = moe::side_stream(1);
+  if (qs) {
+    e = hipEventRecord(qs->fork, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(qs->s, qs->fork, 0);
+    if (e == hipSuccess)
+      e = moe::launch_quantize_rows(static_cast<const uint16_t*>(x), xq, xs_q, shape->T, shape->H,
+                                    mx, qs->s);
+    if (e == hipSuccess) e = hipEventRecord(qs->join, qs->s);
+    if (e != hipSuccess) return e;
+  }
+  e = moe::launch_router_gemm(static_cast<const uint16_t*>(x), w_router, parts,
                                          shape->T, shape->H, shape->E, s, small ? tick : nullptr);
   if (small) {
     // Small batch: top-k, dispatch tables and FFN work lists in one launch.
@@ -197,10 +218,18 @@ hipError_t forward_launch(const moe_shape* shape, const void* x, const float* w_
                               shape->H, nl, shape->k, shape->n_shared, shape->e_first,
                               is_share(shape), fp8, mx, s);
   }
-  if (e == hipSuccess && fp8 && !small)   // (small batches: quantised in the routing launch)
-    e = moe::launch_quantize_rows(static_cast<const uint16_t*>(x), xq, xs, shape->T, shape->H, mx,
-                                  dest, shape->k, shape->n_shared ? offsets + nl : nullptr,
-                                  shape->T * (shape->k + shape->n_shared), s);
+  if (e == hipSuccess && fp8 && !small) {   // (small batches: quantised in the routing launch)
+    if (qs)
+      e = hipStreamWaitEvent(s, qs->join, 0);
+    else
+      e = moe::launch_quantize_rows(static_cast<const uint16_t*>(x), xq, xs_q, shape->T, shape->H,
+                                    mx, s);
+    // fp8: the token scales moved to the permuted rows (of this share: offsets[G] rows)
+    if (e == hipSuccess && !mx)
+      e = moe::launch_permute_scales(xs_tok, src_row, offsets + nl + shape->n_shared,
+                                     static_cast<float*>(xs), shape->T,
+                                     shape->T * (shape->k + shape->n_shared), shape->H / 128, s);
+  }
   if (e == hipSuccess) e = moe::launch_grouped_ffn(a, s);
   if (e == hipSuccess)
     e = moe::launch_combine(static_cast<const uint16_t*>(y_perm), dest, w, offsets + nl,

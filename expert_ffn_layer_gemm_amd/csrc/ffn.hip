@@ -672,18 +672,13 @@ size_t ffn_workspace_bytes(int T, int H, int E, int k, int I, int n_shared, bool
 // Created on first use with default priority and kept for the life of the
 // process (host objects only; no device memory).  If creation fails the
 // chains run one after the other on the caller's stream.
-struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  bool tried = false, ok = false;
-};
-
-SideStream* side_stream() {
+SideStream* side_stream(int slot) {
   constexpr int kMaxDev = 16;
-  thread_local SideStream per_dev[kMaxDev];
+  thread_local SideStream per_dev[kMaxDev][kSideSlots];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nullptr;
-  SideStream& x = per_dev[dev];
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev || slot < 0 || slot >= kSideSlots)
+    return nullptr;
+  SideStream& x = per_dev[dev][slot];
   if (!x.tried) {
     x.tried = true;
     x.ok = hipStreamCreateWithFlags(&x.s, hipStreamNonBlocking) == hipSuccess &&
@@ -773,7 +768,7 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
   // Qwen3-like prefill 2.66 -> 2.645; the Zipf layer 1.41 -> 1.44 on one).
   const long long mean_rows = (long long)f.T * f.k / std::max(1, f.E);
   const bool mixed = mean_rows <= 2LL * skinny_max_rows(f.T);
-  SideStream* side = tiled && mixed && !prof_serial() && !f.one_stream ? side_stream() : nullptr;
+  SideStream* side = tiled && mixed && !prof_serial() && !f.one_stream ? side_stream(0) : nullptr;
   hipStream_t ks = s;                // stream of the streaming chain
   if (side) {                        // fork after the plan
     hipError_t e = hipEventRecord(side->fork, s);

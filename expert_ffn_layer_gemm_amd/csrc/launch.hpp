@@ -57,15 +57,17 @@ hipError_t launch_permute(const int32_t* topk_idx, const uint16_t* x, int32_t* c
                           void* x_perm_scale, int32_t* tile_cnt, int T, int H, int E, int k,
                           int n_shared, int e_first, bool share, bool fp8, bool mx,
                           hipStream_t s);
-// Per-token quantisation of x (fp8: 128-channel groups; mxfp8: blocks of
-// 32): the rows the 8-bit GEMMs gather through src_row.  fp8 scales go to the
-// permuted rows that read them, K-block-major: xs[b * R + dest[t, j]] for
-// every held pair (t, j), and xs[b * R + *shared_base + t] for the shared
-// group (shared_base null without one); mxfp8 scales stay per token,
-// xs[t * H/32 + b].
+// Per-token quantisation of x (fp8: 128-channel groups, scales K-block-major
+// per token, xs[b * T + t]; mxfp8: blocks of 32, xs[t * H/32 + b]): the rows
+// the 8-bit GEMMs gather through src_row.
 hipError_t launch_quantize_rows(const uint16_t* x, uint8_t* xq, void* xs, int T, int H, bool mx,
-                                const int32_t* dest, int k, const int32_t* shared_base, int R,
                                 hipStream_t s);
+// fp8 activation scales of the permuted rows from the per-token ones:
+// xs_perm[b * R + r] = xs_tok[b * T + src_row[r]] for r < *n_rows (K-block-
+// major both, so the GEMMs read one K block's scales of consecutive rows
+// adjacent).
+hipError_t launch_permute_scales(const float* xs_tok, const int32_t* src_row, const int32_t* n_rows,
+                                 float* xs_perm, int T, int R, int KB, hipStream_t s);
 
 // combine.hip
 // shared_base: device pointer to the first row of the shared group (n_shared).
@@ -108,6 +110,18 @@ struct FfnArgs {
 };
 size_t ffn_workspace_bytes(int T, int H, int E, int k, int I, int n_shared, bool fp8, bool mx);
 hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s);
+
+// A second stream per device and slot (default priority, non-blocking) with
+// a fork and a join event, created on first use; null if it cannot be made.
+// Slot 0: the grouped FFN's streaming chain; slot 1: the layer's per-token
+// quantisation, run beside the router.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool tried = false, ok = false;
+};
+constexpr int kSideSlots = 2;
+SideStream* side_stream(int slot);
 
 // small.hip: top-k of a batch of at most kSmallBatch tokens (k <= 16) from the
 // router's slice partials (8-bit layers: and x quantised per token into xq,

@@ -152,31 +152,35 @@ __global__ __launch_bounds__(256) void k_gather_fp8(const int32_t* __restrict__ 
   }
 }
 
-// Per-token e4m3 codes of x (xq[t] = codes of x[t]); each 128-channel scale
-// is stored once per permuted row that reads token t: xs[b * R + dest[t, j]]
-// for the pairs held here (dest >= 0), and xs[b * R + *shared_base + t] for
-// the shared group.  The 16 lanes of a group share these stores.
+// Per-token e4m3 codes of x (xq[t] = codes of x[t]) and their 128-channel
+// scales, K-block-major per token: xs[b * T + t].
 __global__ __launch_bounds__(256) void k_quantize_tokens_fp8(const uint16_t* __restrict__ x,
                                                              uint8_t* __restrict__ xq,
-                                                             float* __restrict__ xs, int T, int H,
-                                                             const int32_t* __restrict__ dest, int k,
-                                                             const int32_t* __restrict__ shared_base,
-                                                             int R) {
-  const int ns = shared_base ? 1 : 0;
-  const int sb = shared_base ? *shared_base : 0;
+                                                             float* __restrict__ xs, int T, int H) {
   for (int tt = 0; tt < kGatherRows; ++tt) {
     const int t = blockIdx.x * kGatherRows + tt;
     if (t >= T) return;
-    const int32_t* dt = dest + (size_t)t * k;
     quantize_row<false>(x + (size_t)t * H, xq + (size_t)t * H,
-                        [&](int b, float sc, int li) {
-                          for (int j = li; j < k + ns; j += 16) {
-                            const int d = j < k ? dt[j] : sb + t;
-                            if (d >= 0) xs[(size_t)b * R + d] = sc;
-                          }
-                        },
+                        [&](int b, float sc, int li) { if (li == 0) xs[(size_t)b * T + t] = sc; },
                         H, threadIdx.x, 256);
   }
+}
+
+// xs_perm[b * R + r] = xs_tok[b * T + src_row[r]] for the rows r < *n_rows:
+// thread r of block (x, y) handles blocks 8 y .. 8 y + 7 of its row (stores
+// of consecutive rows adjacent; the gathers stay inside one block's T scales).
+constexpr int kScaleBlocksPerThread = 8;
+__global__ __launch_bounds__(256) void k_permute_scales(const float* __restrict__ xs_tok,
+                                                        const int32_t* __restrict__ src_row,
+                                                        const int32_t* __restrict__ n_rows,
+                                                        float* __restrict__ xs_perm, int T, int R,
+                                                        int KB) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= min(R, *n_rows)) return;
+  const int t = src_row[r];
+  const int b0 = blockIdx.y * kScaleBlocksPerThread;
+  const int b1 = min(KB, b0 + kScaleBlocksPerThread);
+  for (int b = b0; b < b1; ++b) xs_perm[(size_t)b * R + r] = xs_tok[(size_t)b * T + t];
 }
 
 size_t permute_workspace_bytes(int T, int E) {
@@ -233,7 +237,6 @@ hipError_t launch_permute(const int32_t* topk_idx, const uint16_t* x, int32_t* c
 }
 
 hipError_t launch_quantize_rows(const uint16_t* x, uint8_t* xq, void* xs, int T, int H, bool mx,
-                                const int32_t* dest, int k, const int32_t* shared_base, int R,
                                 hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (mx)
@@ -242,7 +245,16 @@ hipError_t launch_quantize_rows(const uint16_t* x, uint8_t* xq, void* xs, int T,
                static_cast<const int32_t*>(nullptr));
   else
     MOE_LAUNCH("quantize_rows_fp8", k_quantize_tokens_fp8, dim3(ceil_div(T, kGatherRows)), dim3(256),
-               0, s, x, xq, static_cast<float*>(xs), T, H, dest, k, shared_base, R);
+               0, s, x, xq, static_cast<float*>(xs), T, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_scales(const float* xs_tok, const int32_t* src_row, const int32_t* n_rows,
+                                 float* xs_perm, int T, int R, int KB, hipStream_t s) {
+  if (R == 0 || KB == 0) return hipSuccess;
+  const dim3 grid(ceil_div(R, 256), ceil_div(KB, kScaleBlocksPerThread));
+  MOE_LAUNCH("permute_scales", k_permute_scales, grid, dim3(256), 0, s, xs_tok, src_row, n_rows,
+             xs_perm, T, R, KB);
   return hipGetLastError();
 }
 
