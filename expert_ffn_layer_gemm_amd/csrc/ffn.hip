@@ -37,6 +37,12 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ offse
 }
 
 // ---------------------------------------------------------- skinny, bf16 ----
+// Whether streaming work item b (split factor p.ksplit) exists.
+__device__ __forceinline__ bool skinny_live(const GemmArgs& p, int b) {
+  int slot, nt;
+  return band_item(p.sc.skinny, *p.sc.n_skinny, p.n_ntile, slot, nt, b / p.ksplit);
+}
+
 // Workgroup = NW waves; wave w owns 16 h columns (DUAL) or 32 output columns and
 // all (<= 16*MB) rows of its slice.  Lane l: row/column l%16 of each 16x16 MFMA block, 8
 // consecutive k at offset 8*(l/16) of each 32-wide K step.
@@ -47,14 +53,14 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ offse
 // ksplit times as many waves stream the weights; each writes its fp32
 // partial sums and k_splitk_reduce adds them in range order.
 template <bool DUAL, int NW, int MB>
-__global__ __launch_bounds__(64 * NW) void k_skinny_bf16(const GemmArgs p) {
+__device__ __forceinline__ void skinny_bf16_item(const GemmArgs& p, const int bid, const int tid_) {
   int slot, nt;
-  const int ks = blockIdx.x % p.ksplit;
-  if (!band_item(p.sc.skinny, *p.sc.n_skinny, p.n_ntile, slot, nt, blockIdx.x / p.ksplit)) return;
+  const int ks = bid % p.ksplit;
+  if (!band_item(p.sc.skinny, *p.sc.n_skinny, p.n_ntile, slot, nt, bid / p.ksplit)) return;
   const int g = p.sc.skinny[4 * slot], s0 = p.sc.skinny[4 * slot + 1];
   const int row0 = p.offsets[g] + s0, m = min(16 * MB, p.offsets[g + 1] - row0);
   const int nmb = ceil_div(m, 16);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = tid_ & 63, wave = tid_ >> 6;
   const int r16 = lane & 15, kq = (lane >> 4) * 8;
   const int K = p.K, N = p.N;
   // Two weight streams per wave: gate and up rows of 16 h columns (DUAL), or
@@ -160,6 +166,25 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_bf16(const GemmArgs p) {
     }
 }
 
+// WALK = false: one workgroup per work item.  WALK = true (grid capped at
+// kSkinnyGrid workgroups): each walks items b, b + grid, ... (same XCD: the
+// grid is a multiple of 8 times the split factor) and stops at the first index
+// past the list; the thread index is laundered per item so nothing derived
+// from it is hoisted out of the walk into long-lived registers.
+template <bool DUAL, int NW, int MB, bool WALK>
+__global__ __launch_bounds__(64 * NW) void k_skinny_bf16(const GemmArgs p) {
+  if constexpr (!WALK) {
+    skinny_bf16_item<DUAL, NW, MB>(p, blockIdx.x, (int)threadIdx.x);
+  } else {
+    for (int b = blockIdx.x; skinny_live(p, b); b += (int)gridDim.x) {
+      int tid = (int)threadIdx.x;
+      asm volatile("" : "+v"(tid));
+      skinny_bf16_item<DUAL, NW, MB>(p, b, tid);
+      __syncthreads();                     // LDS of this item is read before the next one writes it
+    }
+  }
+}
+
 // Sum of the ksplit fp32 partial planes in plane order for rows below
 // *n_rows, then the epilogue: DUAL h = bf16(silu(gate) * up), else bf16(y).
 // 4 columns per thread.
@@ -243,17 +268,17 @@ __global__ __launch_bounds__(256) void k_splitk_reduce_q8(const float* __restric
 // DUAL needs NW = 8 so a workgroup covers one 128-column group of h, whose
 // row maxima are combined across waves through LDS.
 template <bool DUAL, int NW, int MB>
-__global__ __launch_bounds__(64 * NW) void k_skinny_fp8(const GemmArgs p) {
+__device__ __forceinline__ void skinny_fp8_item(const GemmArgs& p, const int bid, const int tid_) {
   __shared__ float row_amax[NW][16 * MB];
   int slot, nt;
   // Split-K as in the bf16 kernel: block b sums K range b % ksplit of work
   // item b / ksplit (whole 128-K scale blocks) into fp32 partials.
-  const int ks = blockIdx.x % p.ksplit;
-  if (!band_item(p.sc.skinny, *p.sc.n_skinny, p.n_ntile, slot, nt, blockIdx.x / p.ksplit)) return;
+  const int ks = bid % p.ksplit;
+  if (!band_item(p.sc.skinny, *p.sc.n_skinny, p.n_ntile, slot, nt, bid / p.ksplit)) return;
   const int g = p.sc.skinny[4 * slot], s0 = p.sc.skinny[4 * slot + 1];
   const int row0 = p.offsets[g] + s0, m = min(16 * MB, p.offsets[g + 1] - row0);
   const int nmb = ceil_div(m, 16);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = tid_ & 63, wave = tid_ >> 6;
   const int r16 = lane & 15, kq = (lane >> 4) * 32;
   const int K = p.K, N = p.N, KB = K / 128;
   const int n0 = (nt * NW + wave) * 16;
@@ -377,6 +402,25 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_fp8(const GemmArgs p) {
   }
 }
 
+// WALK = false: one workgroup per work item.  WALK = true (grid capped at
+// kSkinnyGrid workgroups): each walks items b, b + grid, ... (same XCD: the
+// grid is a multiple of 8 times the split factor) and stops at the first index
+// past the list; the thread index is laundered per item so nothing derived
+// from it is hoisted out of the walk into long-lived registers.
+template <bool DUAL, int NW, int MB, bool WALK>
+__global__ __launch_bounds__(64 * NW) void k_skinny_fp8(const GemmArgs p) {
+  if constexpr (!WALK) {
+    skinny_fp8_item<DUAL, NW, MB>(p, blockIdx.x, (int)threadIdx.x);
+  } else {
+    for (int b = blockIdx.x; skinny_live(p, b); b += (int)gridDim.x) {
+      int tid = (int)threadIdx.x;
+      asm volatile("" : "+v"(tid));
+      skinny_fp8_item<DUAL, NW, MB>(p, b, tid);
+      __syncthreads();                     // LDS of this item is read before the next one writes it
+    }
+  }
+}
+
 // ----------------------------------------------------------- skinny, mxfp8 ----
 // The 32 codes lane l contributes to an e4m3 MFMA 16x16x128 from a row whose
 // 128-K block starts at ptr - 16*(l/16): 16 bytes at K 16*(l/16) and 16 at
@@ -438,7 +482,7 @@ __device__ __forceinline__ uint32_t dword_of(const u32x4_t v, int i) {
 // LDS once (dynamic shared memory, rows padded by 16 bytes), so each scale
 // line is read from memory once per workgroup.
 template <bool DUAL, int NW, int CB, int SM>
-__global__ __launch_bounds__(64 * NW) void k_skinny_mx(const GemmArgs p) {
+__device__ __forceinline__ void skinny_mx_item(const GemmArgs& p, const int bid, const int tid_) {
   constexpr bool VEC = SM == 1;
   static_assert(!DUAL || CB == 2 || (CB == 1 && NW % 2 == 0), "an MX block of h is 32 columns");
   constexpr int NM = DUAL ? 2 : 1;          // weight matrices
@@ -447,11 +491,11 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_mx(const GemmArgs p) {
   int slot, nt;
   // Split-K: block b sums 128-K blocks [kb0, kb0 + KBc) of work item
   // b / ksplit (kb0 a multiple of 4, so the 16-byte scale loads stay aligned).
-  const int ks = blockIdx.x % p.ksplit;
-  if (!band_item(p.sc.skinny, *p.sc.n_skinny, p.n_ntile, slot, nt, blockIdx.x / p.ksplit)) return;
+  const int ks = bid % p.ksplit;
+  if (!band_item(p.sc.skinny, *p.sc.n_skinny, p.n_ntile, slot, nt, bid / p.ksplit)) return;
   const int g = p.sc.skinny[4 * slot], s0 = p.sc.skinny[4 * slot + 1];
   const int row0 = p.offsets[g] + s0, m = min(16, p.offsets[g + 1] - row0);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = tid_ & 63, wave = tid_ >> 6;
   const int r16 = lane & 15, q4 = lane >> 4;
   const int K = p.K, N = p.N, KB = K / 128, K32 = K / 32;
   const int n0 = (nt * NW + wave) * 16 * CB;
@@ -480,7 +524,7 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_mx(const GemmArgs p) {
     // Only the 16-byte pieces of this block's K range (4 K blocks each).
     constexpr int BR = NW * NB * 16;
     const int c_lo = kb0 / 4, c16 = KBc / 4, total = (BR + 16) * c16;
-    for (int idx = threadIdx.x; idx < total; idx += 64 * NW) {
+    for (int idx = tid_; idx < total; idx += 64 * NW) {
       const int R = idx / c16, cc = c_lo + idx % c16;
       const uint8_t* src;
       if (R < BR) {
@@ -593,6 +637,25 @@ __global__ __launch_bounds__(64 * NW) void k_skinny_mx(const GemmArgs p) {
   }
 }
 
+// WALK = false: one workgroup per work item.  WALK = true (grid capped at
+// kSkinnyGrid workgroups): each walks items b, b + grid, ... (same XCD: the
+// grid is a multiple of 8 times the split factor) and stops at the first index
+// past the list; the thread index is laundered per item so nothing derived
+// from it is hoisted out of the walk into long-lived registers.
+template <bool DUAL, int NW, int CB, int SM, bool WALK>
+__global__ __launch_bounds__(64 * NW) void k_skinny_mx(const GemmArgs p) {
+  if constexpr (!WALK) {
+    skinny_mx_item<DUAL, NW, CB, SM>(p, blockIdx.x, (int)threadIdx.x);
+  } else {
+    for (int b = blockIdx.x; skinny_live(p, b); b += (int)gridDim.x) {
+      int tid = (int)threadIdx.x;
+      asm volatile("" : "+v"(tid));
+      skinny_mx_item<DUAL, NW, CB, SM>(p, b, tid);
+      __syncthreads();                     // LDS of this item is read before the next one writes it
+    }
+  }
+}
+
 // ------------------------------------------------------------------- host ----
 namespace {
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
@@ -688,27 +751,49 @@ SideStream* side_stream(int slot) {
   return x.ok ? &x : nullptr;
 }
 
-template <typename Kern>
-static hipError_t launch_gemm(const char* name, Kern kern, int threads, long long blocks,
-                              const GemmArgs& a, hipStream_t s) {
+// When (nearly) every group is tiled, the streaming kernels' grid is capped
+// at kSkinnyGrid workgroups (16 per CU; a multiple of 8 times every split
+// factor) that walk the work list: the host-side bound on the items is loose
+// (every group might be small), and a grid of that bound whose workgroups
+// nearly all find nothing cost up to ~40 us of dispatch after the tiled chain
+// of the DeepSeek-like layer.  With real streaming work (decode, skewed
+// routing) each workgroup keeps one item: walking measured 2-3 % slower there.
+constexpr long long kSkinnyGrid = 4096;
+
+template <typename Kern1, typename KernW>
+static hipError_t launch_gemm(const char* name, Kern1 one, KernW walk_kern, int threads,
+                              long long blocks, bool walk, const GemmArgs& a, hipStream_t s) {
   if (blocks <= 0) return hipSuccess;
-  MOE_LAUNCH(name, kern, dim3((unsigned)blocks), dim3(threads), 0, s, a);
+  if (walk && blocks > kSkinnyGrid) {
+    MOE_LAUNCH(name, walk_kern, dim3((unsigned)kSkinnyGrid), dim3(threads), 0, s, a);
+  } else {
+    MOE_LAUNCH(name, one, dim3((unsigned)blocks), dim3(threads), 0, s, a);
+  }
   return hipGetLastError();
 }
 
 template <bool DUAL, int NW, int CB>
-static hipError_t launch_skinny_mx(const char* name, long long blocks, const GemmArgs& a, hipStream_t s) {
+static hipError_t launch_skinny_mx(const char* name, long long blocks, bool walk, const GemmArgs& a,
+                                   hipStream_t s) {
   if (blocks <= 0) return hipSuccess;
+  const bool w = walk && blocks > kSkinnyGrid;
+  const dim3 grid((unsigned)(w ? kSkinnyGrid : blocks));
   const int K32 = a.K / 32;
+#define MOE_SKMX(SM, SHM)                                                                          \
+  {                                                                                                \
+    if (w) MOE_LAUNCH(name, (k_skinny_mx<DUAL, NW, CB, SM, true>), grid, dim3(64 * NW), SHM, s, a); \
+    else MOE_LAUNCH(name, (k_skinny_mx<DUAL, NW, CB, SM, false>), grid, dim3(64 * NW), SHM, s, a); \
+  }
   if (a.K % 512 == 0 && a.K <= 8192) {
     constexpr int NB = (DUAL ? 2 : 1) * CB;
     const size_t shm = (size_t)(NW * NB * 16 + 16) * (K32 + 16);
-    MOE_LAUNCH(name, (k_skinny_mx<DUAL, NW, CB, 2>), dim3((unsigned)blocks), dim3(64 * NW), shm, s, a);
+    MOE_SKMX(2, shm)
   } else if (a.K % 512 == 0) {
-    MOE_LAUNCH(name, (k_skinny_mx<DUAL, NW, CB, 1>), dim3((unsigned)blocks), dim3(64 * NW), 0, s, a);
+    MOE_SKMX(1, 0)
   } else {
-    MOE_LAUNCH(name, (k_skinny_mx<DUAL, NW, CB, 0>), dim3((unsigned)blocks), dim3(64 * NW), 0, s, a);
+    MOE_SKMX(0, 0)
   }
+#undef MOE_SKMX
   return hipGetLastError();
 }
 
@@ -769,6 +854,7 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
   const long long mean_rows = (long long)f.T * f.k / std::max(1, f.E);
   const bool mixed = mean_rows <= 2LL * skinny_max_rows(f.T);
   SideStream* side = tiled && mixed && !prof_serial() && !f.one_stream ? side_stream(0) : nullptr;
+  const bool walk = tiled && !mixed;   // streaming grids capped and walked (see kSkinnyGrid)
   hipStream_t ks = s;                // stream of the streaming chain
   if (side) {                        // fork after the plan
     hipError_t e = hipEventRecord(side->fork, s);
@@ -812,12 +898,12 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
       up.n_ntile = f.I / (16 * kMxCB * kMxNW);
       dn.n_ntile = f.H / (16 * kMxCBD * kMxNWD);
       run(launch_skinny_mx<true, kMxNW, kMxCB>("skinny_gateup_mx",
-                                               band_grid(L.max_slices, up.n_ntile) * up.ksplit, up, ks));
+                                               band_grid(L.max_slices, up.n_ntile) * up.ksplit, walk, up, ks));
     } else {
       up.n_ntile = f.I / (16 * 8);
       dn.n_ntile = f.H / (16 * 4);
-      run(launch_gemm("skinny_gateup_fp8", k_skinny_fp8<true, 8, 1>, 512,
-                      band_grid(L.max_slices, up.n_ntile) * up.ksplit, up, ks));
+      run(launch_gemm("skinny_gateup_fp8", k_skinny_fp8<true, 8, 1, false>, k_skinny_fp8<true, 8, 1, true>,
+                      512, band_grid(L.max_slices, up.n_ntile) * up.ksplit, walk, up, ks));
     }
     if (err == hipSuccess && up.ksplit > 1) {
       if (f.mx)
@@ -831,10 +917,10 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
     if (err == hipSuccess) {
       if (f.mx)
         run(launch_skinny_mx<false, kMxNWD, kMxCBD>("skinny_down_mx",
-                                                    band_grid(L.max_slices, dn.n_ntile) * dn.ksplit, dn, ks));
+                                                    band_grid(L.max_slices, dn.n_ntile) * dn.ksplit, walk, dn, ks));
       else
-        run(launch_gemm("skinny_down_fp8", k_skinny_fp8<false, 4, 1>, 256,
-                        band_grid(L.max_slices, dn.n_ntile) * dn.ksplit, dn, ks));
+        run(launch_gemm("skinny_down_fp8", k_skinny_fp8<false, 4, 1, false>, k_skinny_fp8<false, 4, 1, true>,
+                        256, band_grid(L.max_slices, dn.n_ntile) * dn.ksplit, walk, dn, ks));
     }
     if (err == hipSuccess && dn.ksplit > 1) {
       MOE_LAUNCH("splitk_reduce_down", k_splitk_reduce<false>, dim3(ceil_div(f.H, 1024), (unsigned)R),
@@ -854,15 +940,17 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
     dn.ksplit = split ? L.split_dn : 1;
     dn.R = (int)R;
     dn.part = part;
-    if (run(launch_gemm("skinny_gateup_bf16", k_skinny_bf16<true, 4, 1>, 256,
-                        band_grid(L.max_slices, up.n_ntile) * up.ksplit, up, ks)) && up.ksplit > 1) {
+    if (run(launch_gemm("skinny_gateup_bf16", k_skinny_bf16<true, 4, 1, false>,
+                        k_skinny_bf16<true, 4, 1, true>, 256,
+                        band_grid(L.max_slices, up.n_ntile) * up.ksplit, walk, up, ks)) && up.ksplit > 1) {
       MOE_LAUNCH("splitk_reduce_gateup", k_splitk_reduce<true>, dim3(ceil_div(f.I, 1024), (unsigned)R),
                  dim3(256), 0, ks, part, up.ksplit, (int)R, f.I, n_rows, reinterpret_cast<uint16_t*>(h));
       run(hipGetLastError());
     }
     if (err == hipSuccess &&
-        run(launch_gemm("skinny_down_bf16", k_skinny_bf16<false, 4, 1>, 256,
-                        band_grid(L.max_slices, dn.n_ntile) * dn.ksplit, dn, ks)) && dn.ksplit > 1) {
+        run(launch_gemm("skinny_down_bf16", k_skinny_bf16<false, 4, 1, false>,
+                        k_skinny_bf16<false, 4, 1, true>, 256,
+                        band_grid(L.max_slices, dn.n_ntile) * dn.ksplit, walk, dn, ks)) && dn.ksplit > 1) {
       MOE_LAUNCH("splitk_reduce_down", k_splitk_reduce<false>, dim3(ceil_div(f.H, 1024), (unsigned)R),
                  dim3(256), 0, ks, part, dn.ksplit, (int)R, f.H, n_rows,
                  static_cast<uint16_t*>(f.y_perm));

@@ -396,6 +396,20 @@ def test_forward_edge_cases(case):
     _forward_check(cfg, li)
 
 
+# Layers whose mean group is large run the streaming kernels with a capped
+# grid whose workgroups walk the work list (each several items here: up to
+# 8192 items for 4096 workgroups); Zipf-skewed routing leaves real small
+# groups for them next to the tiled ones.
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8", "mxfp8"])
+def test_forward_streaming_walk(wdtype):
+    cfg = MoeConfig("walk_" + wdtype, 57, T=4096, H=512, E=64, k=2, I=2048, zipf_s=1.1, wdtype=wdtype)
+    li = generate_layer(cfg, DEV)
+    _, idx, _ = run_route(cfg, li)
+    sizes = np.bincount(idx.cpu().numpy().ravel(), minlength=cfg.E)
+    assert (sizes <= 48).sum() >= 4 and sizes.mean() > 96   # small groups beside large ones
+    _forward_check(cfg, li)
+
+
 # Expert-parallel shares of the whole layer: small batches (single-workgroup
 # dispatch) and large ones (tile kernels), with and without the shared
 # expert, bf16 / fp8 / mxfp8; the EP8 shares of the Qwen3-235B-like layer.
