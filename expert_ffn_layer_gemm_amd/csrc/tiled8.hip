@@ -70,6 +70,7 @@ namespace {
 
 constexpr int k8BRows = 256;   // staged B rows per tile
 constexpr int k8NS = 3;        // ring stages of A and of B
+constexpr int kPersistGrid = 256;   // persistent fp8 kernel: one workgroup per CU
 
 // Direct-to-LDS load of `BYTES` (4 or 16) bytes per lane from the lane's own
 // address: lane i writes dst + BYTES * i.  Issued from inline assembly, like
@@ -569,6 +570,452 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
 #endif
 }
 
+// Persistent form of the fp8 kernel for large launches (the DeepSeek-like
+// layer's gate/up and down GEMMs).  Per item the plain kernel spends about
+// 4 us before its first MFMA (the chain tile count -> band entry -> tile entry
+// -> group offsets -> A rows, then the first chunk) and 3-5 us in the
+// epilogue, with a workgroup launch in between: 12 % of a gate/up item and
+// a quarter of a down item (16 chunks).  Here one workgroup per CU walks its
+// items (blockIdx.x + k * gridDim.x, the same XCD-contiguous band order):
+//   - the lanes of every wave look up the workgroup's items once, in
+//     parallel (lane l: item l, at most 64), and keep them in registers;
+//   - the last NS iterations of an item's K loop load the next item's first
+//     chunks into the ring, so the next item starts on data already in LDS;
+//   - the epilogue writes from registers (no staging tile).  The next item's
+//     third chunk is held back until after the stores (the last iteration's
+//     loads go to the sink instead, keeping the counts): gate/up passes the
+//     per-row maxima of four waves through the stage the last chunk freed,
+//     and the wait for the next item's first chunk then retires neither the
+//     stores nor that chunk;
+//   - gathered A rows (gate/up) are looked up two items ahead, right after
+//     an epilogue, when only loads issued long before are in flight.
+// Same arithmetic and bits as k_tiled8<false, DUAL, 160, 1>.
+template <bool DUAL>
+__global__ __launch_bounds__(512) void k_tiled8p(const GemmArgs p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr bool MX = false;
+  constexpr int BM = 160, SG = 1;
+  using L = Tiled8Lds<MX, BM, SG>;
+  static_assert(L::TOTAL <= 160 * 1024, "LDS budget");
+  constexpr int NS = k8NS;
+  constexpr int NW = 8, WN = 4;
+  constexpr int MB = BM / 32;
+  constexpr int NB = 4;
+  constexpr int HA = MB / 2;
+  constexpr int A_BLK = BM / 8;
+  constexpr int IPWA = (A_BLK + NW - 1) / NW;
+  constexpr int IPWB = L::B_BYTES / 1024 / NW;
+  constexpr int NSC = L::NSC;
+  static_assert(NSC <= NW && IPWB == NB && IPWA <= NB, "load parts");
+  constexpr int OPS = IPWA + IPWB + 1;
+  constexpr int B_RING = NS * L::A_BYTES;
+  constexpr int S_RING = B_RING + NS * L::B_BYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[L::TOTAL];
+  uint8_t* const sink = lds + L::SINK;
+
+  const int K = p.K, N = p.N;
+  const int nk = K / 128, KB = K / 128;
+  const int N128 = N / 128;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int r16 = lane & 15;
+
+  // Items of this workgroup (blockIdx.x + k * gridDim.x, k < 64; the host
+  // sizes the grid for that): lane k holds item k as (group | rows << 16,
+  // first row | column tile << 24).
+  uint32_t mw0, mw1;
+  int n_items;
+  {
+    int tslot = 0, ntv = 0;
+    const bool ok = band_item(p.sc.tiles, *p.sc.n_tiles, p.n_ntile, tslot, ntv,
+                              (int)blockIdx.x + lane * (int)gridDim.x);
+    uint32_t w0 = 0, w1 = 0;
+    if (ok) {
+      const int g = p.sc.tiles[4 * tslot], m0 = p.sc.tiles[4 * tslot + 1];
+      const int o0 = p.offsets[g], gm = p.offsets[g + 1] - o0;
+      const int mr = min(group_tile_rows(gm, BM), gm - m0);
+      w0 = (uint32_t)g | ((uint32_t)mr << 16);
+      w1 = (uint32_t)(o0 + m0) | ((uint32_t)ntv << 24);
+    }
+    mw0 = w0;
+    mw1 = w1;
+    // band_item is monotone in k: the valid items are a prefix.
+    n_items = __builtin_amdgcn_readfirstlane(__popcll(__ballot(ok)));
+  }
+  if (n_items == 0) return;
+  struct Item { int g, row0, mrows, nt; };
+  auto item = [&](int i) {
+    const uint32_t w0 = (uint32_t)__builtin_amdgcn_readlane((int)mw0, i);
+    const uint32_t w1 = (uint32_t)__builtin_amdgcn_readlane((int)mw1, i);
+    return Item{(int)(w0 & 0xFFFFu), (int)(w1 & 0xFFFFFFu), (int)(w0 >> 16), (int)(w1 >> 24)};
+  };
+
+  // Per-lane load geometry (item independent).  A block j * NW + wave holds
+  // tile rows 8 (j * NW + wave) .. +7 (blocks past the tile go to the sink);
+  // B: this wave's 32 staged rows from one matrix (DUAL: waves 0-3 gate,
+  // 4-7 up); scales: lane row sr as in the plain kernel.
+  bool ain[IPWA];
+  int arow[IPWA];
+  uint32_t asl[IPWA];
+#pragma unroll
+  for (int j = 0; j < IPWA; ++j) {
+    const int blk = j * NW + wave;
+    arow[j] = blk * 8 + lane / 8;
+    asl[j] = (uint32_t)(slot8(arow[j], lane % 8) * 16);
+    ain[j] = blk < A_BLK;
+  }
+  int br0 = wave * IPWB * 8;
+  const uint8_t* Bm = p.B0;
+  if (DUAL && br0 >= 128) { Bm = p.B1; br0 -= 128; }
+  uint32_t bsl[IPWB];
+#pragma unroll
+  for (int j = 0; j < IPWB; ++j)
+    bsl[j] = (uint32_t)(slot8((wave * IPWB + j) * 8 + lane / 8, lane % 8) * 16);
+  const int srow = wave * 64 + lane;
+  const int sr = min(srow, L::SROWS - 1);
+  const bool swave = wave < NSC;
+  const uint32_t sstep = sr < BM ? 4u * (uint32_t)p.s_ld : 4u;
+
+  // Load sources of one item.
+  struct Src {
+    const uint8_t* ab;
+    const uint8_t* bb;
+    const uint8_t* ssrc;
+    uint32_t aoff[IPWA];
+    uint32_t boff[IPWB];
+  };
+  // A offsets of an item (the gathered row, if any, times K plus the slot).
+  auto a_offsets = [&](const Item& it, uint32_t (&ao)[IPWA]) {
+#pragma unroll
+    for (int j = 0; j < IPWA; ++j) {
+      const int r = min(arow[j], it.mrows - 1);
+      ao[j] = (p.a_rows ? (uint32_t)p.a_rows[it.row0 + r] : (uint32_t)r) * (uint32_t)K + asl[j];
+    }
+  };
+  auto make_src = [&](const Item& it, const uint32_t (&ao)[IPWA]) {
+    Src s;
+    s.ab = p.a_rows ? p.A : p.A + (size_t)it.row0 * K;
+#pragma unroll
+    for (int j = 0; j < IPWA; ++j) s.aoff[j] = ao[j];
+    s.bb = Bm + (size_t)it.g * N * K;
+    const int n0 = it.nt * (DUAL ? 128 : 256);
+#pragma unroll
+    for (int j = 0; j < IPWB; ++j)
+      s.boff[j] = (uint32_t)min(n0 + br0 + j * 8 + lane / 8, N - 1) * (uint32_t)K + bsl[j];
+    if (sr < BM) {
+      s.ssrc = static_cast<const uint8_t*>(p.A_scale) + (size_t)(it.row0 + min(sr, it.mrows - 1)) * 4;
+    } else {
+      const int which = sr - BM;
+      if (DUAL)
+        s.ssrc = static_cast<const uint8_t*>(which ? p.s_B1 : p.s_B0) +
+                 ((size_t)it.g * N128 + it.nt) * (size_t)(4 * KB);
+      else
+        s.ssrc = static_cast<const uint8_t*>(p.s_B0) +
+                 ((size_t)it.g * N128 + min(n0 / 128 + which, N128 - 1)) * (size_t)(4 * KB);
+    }
+    return s;
+  };
+
+  auto a_st = [&](int st) { return lds + st * L::A_BYTES; };
+  auto b_st = [&](int st) { return lds + B_RING + st * L::B_BYTES; };
+  auto s_st = [&](int st) { return lds + S_RING + st * L::SSTAGE; };
+  // Part j of chunk c of source s into stage st (to_sink: every load of the
+  // part goes to the sink; it only keeps the counts).
+  auto issue_part = [&](const Src& s, int c, int st, int j, bool to_sink) {
+    const int cc = min(c, nk - 1);
+    if (j == 0) {
+      uint8_t* const dst = (swave && !to_sink) ? s_st(st) + wave * 64 * L::SB : sink;
+      dma_addr_untracked<L::SB>(s.ssrc + (size_t)cc * sstep, dst);
+    }
+    if (j < IPWA) {
+      const int ja = j < IPWA ? j : 0;
+      uint8_t* const dst = (ain[ja] && !to_sink) ? a_st(st) + (ja * NW + wave) * 1024 : sink;
+      dma16_untracked(s.ab + (size_t)cc * 128, s.aoff[ja], dst);
+    }
+    uint8_t* const dst = to_sink ? sink : b_st(st) + (wave * IPWB + j) * 1024;
+    dma16_untracked(s.bb + (size_t)cc * 128, s.boff[j], dst);
+  };
+
+  // First items: sources of items 0 and 1, A offsets of item 2, then the
+  // first NS chunks of item 0.
+  Src cur, nxt;
+  uint32_t ao2[IPWA];
+  {
+    uint32_t ao[IPWA];
+    const Item i0 = item(0);
+    a_offsets(i0, ao);
+    cur = make_src(i0, ao);
+    if (n_items > 1) {
+      const Item i1 = item(1);
+      a_offsets(i1, ao);
+      nxt = make_src(i1, ao);
+    } else {
+      nxt = cur;
+    }
+    if (n_items > 2) a_offsets(item(2), ao2);
+#pragma unroll
+    for (int j = 0; j < IPWA; ++j) ao2[j] = n_items > 2 ? ao2[j] : cur.aoff[j];
+  }
+#pragma unroll
+  for (int c = 0; c < NS; ++c)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) issue_part(cur, c, c, j, false);
+  wait_vmcnt<(NS - 1) * OPS>();
+  lds_barrier();
+
+  // Fragment reads and MFMAs, as in the plain kernel.
+  const int rbase = wm * (BM / 2);
+  // Epilogue column of a lane after the pair exchange: c even starts at 4c
+  // of its first block, c odd at 4 (c - 1) of the next (c = lane / 16).
+  const bool ceven = ((lane >> 4) & 1) == 0;
+  const int pcol = ceven ? 4 * (lane >> 4) : 16 + 4 * ((lane >> 4) - 1);
+  const int c0 = lane >> 4, c1 = 4 + (lane >> 4);
+  const uint32_t a_lo0 = (uint32_t)((rbase + r16) * 128 + (slot8(r16, c0) << 4));
+  const uint32_t a_hi0 = (uint32_t)((rbase + r16) * 128 + (slot8(r16, c1) << 4));
+  const int brow0 = b8_row<DUAL>(0, wn, r16);
+  const uint32_t b_lo0 = (uint32_t)(B_RING + brow0 * 128 + (slot8(r16, c0) << 4));
+  const uint32_t b_hi0 = (uint32_t)(B_RING + brow0 * 128 + (slot8(r16, c1) << 4));
+  const uint32_t s_a0 = (uint32_t)(S_RING + (rbase + r16) * L::SB);
+  auto opq = [](uint32_t v) { asm volatile("" : "+v"(v)); return v; };
+  auto frag_at = [&](uint32_t lo, uint32_t hi) {
+    const u32x4_t x = lds_read16(lds + lo), y = lds_read16(lds + hi);
+    return i32x8_t{(int)x[0], (int)x[1], (int)x[2], (int)x[3],
+                   (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
+  };
+  auto ld32 = [&](uint32_t off) { return *reinterpret_cast<const uint32_t*>(lds + off); };
+
+  f32x4_t acc[MB][NB];
+  i32x8_t a[MB], b[NB];
+  float saf[MB];
+  float sb_lo = 0.f, sb_hi = 0.f;
+  struct Bases { uint32_t alo, ahi, blo, bhi, sa; };
+  auto bases = [&](int st) {
+    const uint32_t so = (uint32_t)(st * L::SSTAGE);
+    return Bases{opq(a_lo0 + st * L::A_BYTES), opq(a_hi0 + st * L::A_BYTES),
+                 opq(b_lo0 + st * L::B_BYTES), opq(b_hi0 + st * L::B_BYTES), opq(s_a0 + so)};
+  };
+  auto next_a = [&](const Bases& q, int i) {
+    a[i] = frag_at(q.alo + i * 2048, q.ahi + i * 2048);
+    saf[i] = __uint_as_float(ld32(q.sa + i * 16 * L::SB));
+  };
+  auto next_b = [&](const Bases& q, int j) {
+    const int dr = b8_row<DUAL>(j, 0, 0);
+    b[j] = frag_at(q.blo + dr * 128, q.bhi + dr * 128);
+  };
+  auto rd_bsc = [&](int st) {
+    const uint32_t o = S_RING + (uint32_t)(st * L::SSTAGE) + BM * L::SB;
+    const float s0 = __uint_as_float(ld32(o)), s1 = __uint_as_float(ld32(o + L::SB));
+    sb_lo = DUAL ? s0 : (wn < 2 ? s0 : s1);
+    sb_hi = DUAL ? s1 : sb_lo;
+  };
+  constexpr int HMAX = MB - HA;
+  f32x4_t pr[2][HMAX];
+  auto col = [&](int i0, int i1, int j, auto nm) {
+#pragma unroll
+    for (int i = i0; i < i1; ++i)
+      if (i < count_value(nm))
+        pr[j & 1][i - i0] = mfma_fp8_16x16x128(b[j], a[i], f32x4_t{0.f, 0.f, 0.f, 0.f});
+  };
+  auto scale_col = [&](int i0, int i1, int j, auto nm) {
+    const float sbv = j < NB / 2 ? sb_lo : sb_hi;
+#pragma unroll
+    for (int i = i0; i < i1; ++i)
+      if (i < count_value(nm)) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[i][j][q] += pr[j & 1][i - i0][q] * (saf[i] * sbv);
+      }
+  };
+
+  int st = 0;                                        // ring stage of the current chunk
+  for (int it_i = 0;; ++it_i) {
+    const Item it = item(it_i);
+    const bool has_next = it_i + 1 < n_items;
+    const int n0 = it.nt * (DUAL ? 128 : 256);
+    const int ncols = DUAL ? 128 : min(256, N - n0);
+    const bool has_cols = DUAL || wn * 64 < ncols;
+    const int nmb = has_cols ? max(0, min(MB, ceil_div(it.mrows - rbase, 16))) : 0;
+    // The tail's loads: the next item's chunks 0 .. NS-1, or re-reads of
+    // this item's last chunk after the last item.
+    Src tsrc;
+    tsrc.ab = has_next ? nxt.ab : cur.ab;
+    tsrc.bb = has_next ? nxt.bb : cur.bb;
+    tsrc.ssrc = has_next ? nxt.ssrc : cur.ssrc;
+#pragma unroll
+    for (int j = 0; j < IPWA; ++j) tsrc.aoff[j] = has_next ? nxt.aoff[j] : cur.aoff[j];
+#pragma unroll
+    for (int j = 0; j < IPWB; ++j) tsrc.boff[j] = has_next ? nxt.boff[j] : cur.boff[j];
+    const int tshift = has_next ? nk : 0;
+
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto main_loop = [&](auto nm) {
+      {
+        const Bases q0 = bases(st);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) next_b(q0, j);
+#pragma unroll
+        for (int i = 0; i < HA; ++i) next_a(q0, i);
+      }
+      rd_bsc(st);
+      // One chunk: its loads are issued by issue(j) between the second
+      // half's columns.
+      auto step = [&](auto&& issue) {
+        const int sn = st == NS - 1 ? 0 : st + 1;
+        {
+          const Bases qk = bases(st);
+#pragma unroll
+          for (int i = HA; i < MB; ++i) next_a(qk, i);
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          col(0, HA, j, nm);
+          if (j > 0) scale_col(0, HA, j - 1, nm);
+        }
+        scale_col(0, HA, NB - 1, nm);
+#pragma unroll
+        for (int i = 0; i < HA; ++i)
+#pragma unroll
+          for (int j = 0; j < NB; ++j) asm volatile("" : "+v"(acc[i][j]));
+        wait_vmcnt<(NS - 2) * OPS>();
+        lds_barrier();
+        const Bases qn = bases(sn);
+#pragma unroll
+        for (int i = 0; i < HA; ++i) next_a(qn, i);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          col(HA, MB, j, nm);
+          issue(j);
+          if (j > 0) scale_col(HA, MB, j - 1, nm);
+          next_b(qn, j);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        scale_col(HA, MB, NB - 1, nm);
+        rd_bsc(sn);
+        st = sn;
+      };
+      for (int kc = 0; kc < nk - NS; ++kc)
+        step([&](int j) { issue_part(cur, kc + NS, st, j, false); });
+      for (int kc = nk - NS; kc < nk; ++kc) {
+        // The next item's chunk NS-1 is held back (see below).
+        const bool to_sink = has_next && kc == nk - 1;
+        step([&](int j) { issue_part(tsrc, kc + NS - tshift, st, j, to_sink); });
+      }
+    };
+    with_count<MB>(nmb, main_loop);
+    // st is now the stage of the next item's chunk 0; the last chunk's
+    // stage (free: every wave is past the last boundary) is st_last.
+    const int st_last = st == 0 ? NS - 1 : st - 1;
+    if (!has_next) wait_vmcnt<0>();                  // the tail's re-reads land before the exit
+
+    if constexpr (DUAL) {
+      // h = silu(g) * u; per-row maxima over the tile's 128 columns (the
+      // lane's 8 values, the 4 lanes of the row, the 4 waves of the row
+      // through the free stage), e4m3 codes with scale amax / 448.
+      float* amax_s = reinterpret_cast<float*>(b_st(st_last));   // [WN][BM]
+      lds_barrier();
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const int m = rbase + i * 16 + r16;
+        float am = 0.f;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float h = (i < nmb && m < it.mrows) ? silu_mul(acc[i][j][q], acc[i][j + 2][q]) : 0.f;
+            acc[i][j][q] = h;
+            am = fmaxf(am, fabsf(h));
+          }
+        am = fmaxf(am, __shfl_xor(am, 16));
+        am = fmaxf(am, __shfl_xor(am, 32));
+        if (lane < 16) amax_s[wn * BM + m] = am;
+      }
+      lds_barrier();
+      uint32_t w4[MB][2];
+      float scl[MB];
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const int m = rbase + i * 16 + r16;
+        float am = 0.f;
+#pragma unroll
+        for (int w = 0; w < WN; ++w) am = fmaxf(am, amax_s[w * BM + m]);
+        const float scale = am == 0.f ? 1.f : am / 448.f;
+        scl[i] = scale;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          float qv[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) qv[q] = fminf(fmaxf(acc[i][j][q] / scale, -448.f), 448.f);
+          int v = __builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[1], 0, false);
+          v = __builtin_amdgcn_cvt_pk_fp8_f32(qv[2], qv[3], v, true);
+          w4[i][j] = (uint32_t)v;
+        }
+      }
+      if (has_next && it_i + 2 < n_items) a_offsets(item(it_i + 2), ao2);
+      // Lanes c and c ^ 1 (c = lane / 16) trade codes so that each holds
+      // eight consecutive columns of its row (c even of block 0, c odd of
+      // block 1): one 8-byte store per lane and row block.
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+        if (i < nmb) {
+          const int m = rbase + i * 16 + r16;
+          const uint32_t got = (uint32_t)__shfl_xor((int)(ceven ? w4[i][1] : w4[i][0]), 16);
+          if (m < it.mrows) {
+            const u32x2_t o = ceven ? u32x2_t{w4[i][0], got} : u32x2_t{got, w4[i][1]};
+            *reinterpret_cast<u32x2_t*>(p.out + (size_t)(it.row0 + m) * N + n0 + wn * 32 + pcol) = o;
+            if (wn == 0 && lane < 16)
+              static_cast<float*>(p.out_scale)[(size_t)it.nt * p.R + it.row0 + m] = scl[i];
+          }
+        }
+      if (has_next) lds_barrier();                   // the maxima are read: the stage is free
+    } else {
+      if (has_next && it_i + 2 < n_items) a_offsets(item(it_i + 2), ao2);
+      // A lane holds four consecutive bf16 columns of row m per block; lanes
+      // c and c ^ 1 trade halves so that each holds eight (c even of block j,
+      // c odd of block j + 1): one 16-byte store per lane and block pair.
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+        if (i < nmb) {
+          const int m = rbase + i * 16 + r16;
+          uint8_t* const orow = p.out + ((size_t)(it.row0 + m) * N + n0 + wn * 64) * 2;
+#pragma unroll
+          for (int jp = 0; jp < NB; jp += 2) {
+            uint32_t v[2][2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              v[t][0] = f32_to_bf16_bits(acc[i][jp + t][0]) | (f32_to_bf16_bits(acc[i][jp + t][1]) << 16);
+              v[t][1] = f32_to_bf16_bits(acc[i][jp + t][2]) | (f32_to_bf16_bits(acc[i][jp + t][3]) << 16);
+            }
+            const uint32_t g0 = (uint32_t)__shfl_xor((int)(ceven ? v[1][0] : v[0][0]), 16);
+            const uint32_t g1 = (uint32_t)__shfl_xor((int)(ceven ? v[1][1] : v[0][1]), 16);
+            const int cidx = jp * 16 + pcol;
+            if (m < it.mrows && wn * 64 + cidx < ncols)
+              *reinterpret_cast<u32x4_t*>(orow + (size_t)cidx * 2) =
+                  ceven ? u32x4_t{v[0][0], v[0][1], g0, g1} : u32x4_t{g0, g1, v[1][0], v[1][1]};
+          }
+        }
+    }
+    if (!has_next) break;
+    // The next item's chunk NS-1 into the free stage, after the stores: the
+    // vm counter retires in issue order, so the wait for the next item's
+    // chunk 0 (chunks 1, the sink loads and NS-1 came later) need not wait
+    // for the stores, nor for this last chunk.
+#pragma unroll
+    for (int j = 0; j < NB; ++j) issue_part(nxt, NS - 1, st_last, j, false);
+    cur = nxt;
+    if (it_i + 2 < n_items) nxt = make_src(item(it_i + 2), ao2);
+    wait_vmcnt<NS * OPS>();                          // the new item's chunk 0 is in
+    lds_barrier();
+  }
+#else
+  (void)p;
+#endif
+}
+
 hipError_t launch_tiled8(const char* name, bool mx, bool dual, long long blocks, const GemmArgs& a,
                          hipStream_t s) {
   if (blocks <= 0) return hipSuccess;
@@ -587,6 +1034,21 @@ hipError_t launch_tiled8(const char* name, bool mx, bool dual, long long blocks,
     }
   } else {
     static_assert(tile_rows(true, false) == 160, "fp8 tile height");
+    // Persistent walk for large launches: one workgroup per CU (more when a
+    // workgroup would exceed the 64 items its lanes hold), a multiple of 8 so
+    // that every workgroup stays on one XCD's band run.  Needs K of at
+    // least NS chunks, no ragged column tile, ungathered activation scales
+    // and the packed item fields (rows < 2^24, column tiles < 256).
+    const long long pairs = (long long)band_grid(blocks, 1);
+    const int ncw = dual ? 128 : 256;
+    if (pairs >= 4 * kPersistGrid && a.s_rows == nullptr && a.K >= 128 * k8NS && a.N % ncw == 0 &&
+        a.n_ntile < 256 && a.R < (1 << 24)) {
+      const long long need = (pairs + 8 + 63) / 64;
+      const dim3 pgrid((unsigned)(((need > kPersistGrid ? need : kPersistGrid) + 7) / 8 * 8));
+      if (dual) MOE_LAUNCH(name, (k_tiled8p<true>), pgrid, dim3(512), 0, s, a);
+      else MOE_LAUNCH(name, (k_tiled8p<false>), pgrid, dim3(512), 0, s, a);
+      return hipGetLastError();
+    }
     if (dual) MOE_LAUNCH(name, (k_tiled8<false, true, 160, 1>), grid, dim3(512), 0, s, a);
     else MOE_LAUNCH(name, (k_tiled8<false, false, 160, 1>), grid, dim3(512), 0, s, a);
   }

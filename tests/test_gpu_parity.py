@@ -410,6 +410,22 @@ def test_forward_streaming_walk(wdtype):
     _forward_check(cfg, li)
 
 
+# Large fp8 launches run the persistent tiled kernel (one workgroup per CU
+# walking its tiles, the next tile's first chunks loaded during the current
+# tile's last ones, the epilogue stored from registers).  DeepSeek-like
+# routing at 1024 tokens leaves the tiles of the 1024-row shared expert and
+# a few routed groups (most workgroups get no tile or one); 1536 and 2048
+# tokens give about 4 and 8 tiles per workgroup (the full layer: 17 to 32).
+@pytest.mark.parametrize("T", [1024, 1536, 2048])
+def test_forward_fp8_persistent_walk(T):
+    cfg = MoeConfig(f"pers_{T}", 58, T=T, H=2048, E=256, k=8, I=1024, n_shared=1, wdtype="fp8")
+    li = generate_layer(cfg, DEV)
+    _, idx, _ = run_route(cfg, li)
+    tiled = np.bincount(idx.cpu().numpy().ravel(), minlength=cfg.E) > 48
+    assert (tiled.sum() < 16) if T == 1024 else (tiled.sum() > 64)
+    _forward_check(cfg, li)
+
+
 # Expert-parallel shares of the whole layer: small batches (single-workgroup
 # dispatch) and large ones (tile kernels), with and without the shared
 # expert, bf16 / fp8 / mxfp8; the EP8 shares of the Qwen3-235B-like layer.
