@@ -687,7 +687,7 @@ WsLayout ffn_layout(int T, int H, int E, int k, int I, int n_shared, bool fp8, b
   const long long R = (long long)T * (k + n_shared);
   const int G = E + n_shared;
   const long long big_groups = std::min<long long>(G, R / (skinny_max_rows(T) + 1));
-  L.max_tiles = (int)(R / tile_rows(fp8, mx) + big_groups + 1);
+  L.max_tiles = (int)(R / tile_rows(fp8, mx, bf16_stream_tiles(T, k, E, fp8)) + big_groups + 1);
   size_t off = 0;
   L.h = off;        off += align256((size_t)R * I * (fp8 ? 1 : 2));
   // h scales: fp8 one fp32 per 128 channels, mxfp8 one E8M0 byte per 32
@@ -721,7 +721,8 @@ Sched ffn_schedule(const FfnArgs& f) {
   uint8_t* ws = static_cast<uint8_t*>(f.workspace);
   return Sched{reinterpret_cast<int32_t*>(ws + L.n_skinny), reinterpret_cast<int32_t*>(ws + L.n_tiles),
                reinterpret_cast<int32_t*>(ws + L.skinny), reinterpret_cast<int32_t*>(ws + L.tiles),
-               f.E + f.n_shared, tile_rows(f.fp8, f.mx), skinny_max_rows(f.T)};
+               f.E + f.n_shared, tile_rows(f.fp8, f.mx, bf16_stream_tiles(f.T, f.k, f.E, f.fp8)),
+               skinny_max_rows(f.T)};
 }
 
 size_t ffn_workspace_bytes(int T, int H, int E, int k, int I, int n_shared, bool fp8, bool mx) {
@@ -877,9 +878,15 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, hipStream_t s) {
   const char* nm_td = f.mx ? "tiled_down_mx" : f.fp8 ? "tiled_down_fp8" : "tiled_down_bf16";
   up.n_ntile = f.I / 128;
   dn.n_ntile = ceil_div(f.H, 256);
+  // bf16 layers with small mean groups: the few tiled groups are
+  // weight-streaming-bound and take the 3-stage 160-row kernel in bf16 (the
+  // Qwen3.5-like layer 1.40 -> 1.36 ms, same bits); larger groups the
+  // 256-row bf16 kernel.
+  const bool bfs = bf16_stream_tiles(f.T, f.k, f.E, f.fp8);
   auto tiled_gemm = [&](const char* nm, bool dual, const GemmArgs& g) {
     const long long blocks = (long long)L.max_tiles * g.n_ntile;
-    return f.fp8 ? launch_tiled8(nm, f.mx, dual, blocks, g, s) : launch_tiled(nm, dual, blocks, g, s);
+    return f.fp8 ? launch_tiled8(nm, f.mx, dual, blocks, g, s)
+                 : bfs ? launch_tiled8_bf16(nm, dual, blocks, g, s) : launch_tiled(nm, dual, blocks, g, s);
   };
   if (tiled && run(tiled_gemm(nm_tg, true, up))) run(tiled_gemm(nm_td, false, dn));
 

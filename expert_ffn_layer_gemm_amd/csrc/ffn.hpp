@@ -16,8 +16,18 @@ constexpr int kSkinnyMax = 64;
 __host__ __device__ constexpr int skinny_max_rows(int T) { return T <= kSkinnyMax ? kSkinnyMax : 48; }
 // Rows per tile of the tiled kernels: 256 for bf16; 160 for fp8 (a
 // DeepSeek-like routed group of ~128 rows stays in one tile, so its weights
-// are streamed once); 128 for MXFP8 (its B-row scales need the LDS).
-__host__ __device__ constexpr int tile_rows(bool fp8, bool mx) { return mx ? 128 : fp8 ? 160 : 256; }
+// are streamed once) and for bf16 layers with small mean groups (bf_stream:
+// their few tiled groups are weight-streaming-bound and run the fp8 kernel's
+// 3-stage form in bf16); 128 for MXFP8 (its B-row scales need the LDS).
+__host__ __device__ constexpr int tile_rows(bool fp8, bool mx, bool bf_stream = false) {
+  return mx ? 128 : fp8 ? 160 : bf_stream ? 160 : 256;
+}
+
+// bf16 layers whose mean group (T k / E rows) is at most twice the streaming
+// kernels' row limit: most groups stream, the tiled ones are few.
+__host__ __device__ constexpr bool bf16_stream_tiles(int T, int k, int E, bool fp8) {
+  return !fp8 && (long long)T * k / (E > 0 ? E : 1) <= 2LL * skinny_max_rows(T);
+}
 
 // Rows per tile of a group of m rows: the group is cut into ceil(m / bm)
 // tiles of equal height (rounded up to 16), so that the tiles of one group,
@@ -121,6 +131,8 @@ struct GemmArgs {
 
 // Tiled kernel launches: bf16 (tiled.hip), fp8 and MXFP8 (tiled8.hip).
 hipError_t launch_tiled(const char* name, bool dual, long long blocks, const GemmArgs& a, hipStream_t s);
+hipError_t launch_tiled8_bf16(const char* name, bool dual, long long blocks, const GemmArgs& a,
+                              hipStream_t s);
 hipError_t launch_tiled8(const char* name, bool mx, bool dual, long long blocks, const GemmArgs& a,
                          hipStream_t s);
 

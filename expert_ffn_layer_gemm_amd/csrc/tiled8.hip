@@ -113,7 +113,7 @@ struct Tiled8Lds {
   static constexpr int TOTAL = SINK + 1024;
 };
 
-template <bool MX, bool DUAL, int BM, int SG>
+template <bool MX, bool DUAL, int BM, int SG, bool BF = false>
 __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using L = Tiled8Lds<MX, BM, SG>;
@@ -134,7 +134,8 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
   // the tile and scale loads of waves or chunks without one go to the sink,
   // chunks past the end re-read the last chunk.  Every vm-counter wait is then
   // a compile-time count (no per-wave or per-chunk bookkeeping in the loop).
-  constexpr int OPS = IPWA + IPWB + 1;
+  static_assert(!(BF && MX), "bf16 operands carry no scales");
+  constexpr int OPS = IPWA + IPWB + (BF ? 0 : 1);
   constexpr int B_RING = NS * L::A_BYTES;
   constexpr int S_RING = B_RING + NS * L::B_BYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[L::TOTAL];
@@ -147,7 +148,8 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
   const int gm = p.offsets[g + 1] - p.offsets[g];
   const int mrows = min(group_tile_rows(gm, BM), gm - m0);
   const int K = p.K, N = p.N;
-  const int nk = K / 128;
+  const int KBY = BF ? 2 * K : K;                   // bytes per operand row
+  const int nk = KBY / 128;
   const int KB = K / 128;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -159,7 +161,7 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
   // A DMA blocks of this wave: block a = j * NW + wave holds tile rows
   // 8a .. 8a+7; rows past the group's end re-read its last row (never
   // stored), blocks past the tile load into the sink.
-  const uint8_t* const ab = p.a_rows ? p.A : p.A + (size_t)row0 * K;
+  const uint8_t* const ab = p.a_rows ? p.A : p.A + (size_t)row0 * KBY;
   uint32_t aoff[IPWA];
   bool ain[IPWA];
 #pragma unroll
@@ -169,7 +171,7 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
     const uint32_t sl = (uint32_t)(slot8(row, lane % 8) * 16);
     ain[j] = blk < A_BLK;
     const int r = min(row, mrows - 1);
-    aoff[j] = (p.a_rows ? (uint32_t)p.a_rows[row0 + r] : (uint32_t)r) * (uint32_t)K + sl;
+    aoff[j] = (p.a_rows ? (uint32_t)p.a_rows[row0 + r] : (uint32_t)r) * (uint32_t)KBY + sl;
   }
   // B: this wave's 32 staged rows come from one matrix (DUAL: waves 0-3 the
   // gate rows, 4-7 the up rows).
@@ -179,13 +181,13 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
     int br0 = wave * IPWB * 8;
     const uint8_t* B = p.B0;
     if (DUAL && br0 >= 128) { B = p.B1; br0 -= 128; }
-    bb = B + (size_t)g * N * K;
+    bb = B + (size_t)g * N * KBY;
 #pragma unroll
     for (int j = 0; j < IPWB; ++j) {
       const int row = (wave * IPWB + j) * 8 + lane / 8;
       const uint32_t sl = (uint32_t)(slot8(row, lane % 8) * 16);
       // Rows past the matrix (ragged last column tile) re-read its last row.
-      boff[j] = (uint32_t)min(n0 + br0 + j * 8 + lane / 8, N - 1) * (uint32_t)K + sl;
+      boff[j] = (uint32_t)min(n0 + br0 + j * 8 + lane / 8, N - 1) * (uint32_t)KBY + sl;
     }
   }
 
@@ -199,9 +201,9 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
   const int srow = wave * 64 + lane;
   const int sr = min(srow, L::SROWS - 1);
   const bool swave = wave < NSC;
-  const uint8_t* ssrc;
+  const uint8_t* ssrc = nullptr;
   uint32_t sstep = 4;                                // bytes from one chunk's scale to the next
-  {
+  if constexpr (!BF) {
     const int N128 = N / 128;
     if (sr < BM) {
       const int r = row0 + min(sr, mrows - 1);
@@ -253,7 +255,7 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
       (uint32_t)__builtin_amdgcn_readlane((int)reinterpret_cast<uint64_t>(ssrc), 63));
   auto issue_part = [&](int c, int st, int j) {
     const int cc = min(c, nk - 1);
-    if (j == 0) {
+    if (!BF && j == 0) {
       const bool real = swave && c % SG == 0;
       uint8_t* const dst = real ? s_st(c, st) + wave * 64 * L::SB : sink;
       const size_t sk = (size_t)(cc - cc % SG);
@@ -333,7 +335,7 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
   auto next_a = [&](const Bases& q, int i) {
     a[i] = frag_at(q.alo + i * 2048, q.ahi + i * 2048);
     if constexpr (MX) sam[i] = (ld32(q.sa + i * 16 * L::SB) >> sh) & 0xFFu;
-    else saf[i] = __uint_as_float(ld32(q.sa + i * 16 * L::SB));
+    else if constexpr (!BF) saf[i] = __uint_as_float(ld32(q.sa + i * 16 * L::SB));
   };
   auto next_b = [&](const Bases& q, int j) {
     const int dr = b8_row<DUAL>(j, 0, 0);          // row offset of block j
@@ -341,7 +343,7 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
     if constexpr (MX) sbm[j] = (ld32(q.sb + dr * L::SB) >> sh) & 0xFFu;
   };
   auto rd_bsc = [&](int c, int st) {
-    if constexpr (!MX) {
+    if constexpr (!MX && !BF) {
       const uint32_t o = S_RING + s_off(c, st) + BM * L::SB;
       const float s0 = __uint_as_float(ld32(o)), s1 = __uint_as_float(ld32(o + L::SB));
       sb_lo = DUAL ? s0 : (wn < 2 ? s0 : s1);
@@ -357,13 +359,26 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
 #pragma unroll
     for (int i = i0; i < i1; ++i)
       if (i < count_value(nm)) {
-        if constexpr (MX) acc[i][j] = mfma_mx8_16x16x128(a[i], b[j], acc[i][j], sam[i], sbm[j]);
-        else pr[j & 1][i - i0] = mfma_fp8_16x16x128(b[j], a[i], f32x4_t{0.f, 0.f, 0.f, 0.f});
+        if constexpr (MX) {
+          acc[i][j] = mfma_mx8_16x16x128(a[i], b[j], acc[i][j], sam[i], sbm[j]);
+        } else if constexpr (BF) {
+          // The chunk's 64 bf16 values as two K = 32 steps: the lane's low 16
+          // bytes are elements 8 (lane/16) .. +8, its high ones 32 + the same.
+          const i32x8_t x = a[i], y = b[j];
+          acc[i][j] = mfma_bf16_16x16x32(u32x4_t{(uint32_t)x[0], (uint32_t)x[1], (uint32_t)x[2], (uint32_t)x[3]},
+                                         u32x4_t{(uint32_t)y[0], (uint32_t)y[1], (uint32_t)y[2], (uint32_t)y[3]},
+                                         acc[i][j]);
+          acc[i][j] = mfma_bf16_16x16x32(u32x4_t{(uint32_t)x[4], (uint32_t)x[5], (uint32_t)x[6], (uint32_t)x[7]},
+                                         u32x4_t{(uint32_t)y[4], (uint32_t)y[5], (uint32_t)y[6], (uint32_t)y[7]},
+                                         acc[i][j]);
+        } else {
+          pr[j & 1][i - i0] = mfma_fp8_16x16x128(b[j], a[i], f32x4_t{0.f, 0.f, 0.f, 0.f});
+        }
       }
   };
   // fp8: acc += partial * (row scale * block scale)
   auto scale_col = [&](int i0, int i1, int j, auto nm) {
-    if constexpr (!MX) {
+    if constexpr (!MX && !BF) {
       const float sbv = j < NB / 2 ? sb_lo : sb_hi;
 #pragma unroll
       for (int i = i0; i < i1; ++i)
@@ -444,11 +459,11 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
   // its blocks, column lane % 16; fp8: see below.
   // The output tile is assembled in LDS (the ring stages are free once every
   // wave is past its last read) and written out in 16-byte row pieces.
-  constexpr int OUT_B = DUAL ? 1 : 2;                // bytes per output element
+  constexpr int OUT_B = (DUAL && !BF) ? 1 : 2;       // bytes per output element
   constexpr int OCOLS = DUAL ? 128 : 256;            // output columns per tile
   constexpr int ROWB = OCOLS * OUT_B;                // bytes per tile row: 128 or 512
   constexpr int NCH = ROWB / 16;                     // 16-byte pieces per row
-  constexpr int AMAX_BYTES = (DUAL && !MX) ? WN * BM * 4 : 0;
+  constexpr int AMAX_BYTES = (DUAL && !MX && !BF) ? WN * BM * 4 : 0;
   static_assert(AMAX_BYTES + BM * ROWB <= L::TOTAL, "output tile fits in LDS");
   float* amax_s = reinterpret_cast<float*>(lds);     // [WN][BM]
   uint8_t* const tile = lds + AMAX_BYTES;
@@ -482,6 +497,21 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
             *tile_at(r, wn * 32 + j * 16 + r16) = (uint8_t)f32_to_e4m3(qv);
           }
           if (r16 == 0) static_cast<uint8_t*>(p.out_scale)[(size_t)(row0 + r) * N32 + hc0 / 32] = (uint8_t)e8;
+        }
+      }
+  } else if constexpr (DUAL && BF) {
+    // bf16: the lane holds rows rbase + 16 i + 4 (lane/16) + q of its blocks,
+    // column lane % 16; h = silu(g) * u rounded to bf16.
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+      if (i < nmb) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = rbase + i * 16 + (lane >> 4) * 4 + q;
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            *reinterpret_cast<uint16_t*>(tile_at(r, wn * 32 + j * 16 + r16)) =
+                (uint16_t)f32_to_bf16_bits(silu_mul(acc[i][j][q], acc[i][j + 2][q]));
         }
       }
   } else if constexpr (DUAL) {
@@ -528,7 +558,7 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
           if (wn == 0 && lane < 16) static_cast<float*>(p.out_scale)[(size_t)nt * p.R + row0 + m] = scale;
         }
       }
-  } else if constexpr (MX) {
+  } else if constexpr (MX || BF) {
 #pragma unroll
     for (int i = 0; i < MB; ++i)
       if (i < nmb) {
@@ -1014,6 +1044,16 @@ __global__ __launch_bounds__(512) void k_tiled8p(const GemmArgs p) {
 #else
   (void)p;
 #endif
+}
+
+hipError_t launch_tiled8_bf16(const char* name, bool dual, long long blocks, const GemmArgs& a,
+                              hipStream_t s) {
+  if (blocks <= 0) return hipSuccess;
+  const dim3 grid((unsigned)band_grid(blocks, 1));
+  static_assert(tile_rows(false, false, true) == 160, "bf16 streaming tile height");
+  if (dual) MOE_LAUNCH(name, (k_tiled8<false, true, 160, 1, true>), grid, dim3(512), 0, s, a);
+  else MOE_LAUNCH(name, (k_tiled8<false, false, 160, 1, true>), grid, dim3(512), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_tiled8(const char* name, bool mx, bool dual, long long blocks, const GemmArgs& a,
