@@ -64,7 +64,10 @@ int moe_profile_start(int mode, int which, int capacity) {
   moe::g.stop.resize(capacity);
   moe::g.name.assign(capacity, nullptr);
   for (int i = 0; i < capacity; ++i) {
-    if (hipEventCreate(&moe::g.start[i]) != hipSuccess || hipEventCreate(&moe::g.stop[i]) != hipSuccess) {
+    // Timing-only events: no system-scope fence (its cache write-back and
+    // invalidation would slow the launches that follow each record).
+    if (hipEventCreateWithFlags(&moe::g.start[i], hipEventDisableSystemFence) != hipSuccess ||
+        hipEventCreateWithFlags(&moe::g.stop[i], hipEventDisableSystemFence) != hipSuccess) {
       moe::g.start.resize(i);
       moe::g.stop.resize(i);
       moe::release();
