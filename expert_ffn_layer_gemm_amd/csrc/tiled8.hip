@@ -600,33 +600,41 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
 #endif
 }
 
-// Persistent form of the fp8 kernel for large launches (the DeepSeek-like
-// layer's gate/up and down GEMMs).  Per item the plain kernel spends about
-// 4 us before its first MFMA (the chain tile count -> band entry -> tile entry
-// -> group offsets -> A rows, then the first chunk) and 3-5 us in the
-// epilogue, with a workgroup launch in between: 12 % of a gate/up item and
-// a quarter of a down item (16 chunks).  Here one workgroup per CU walks its
-// items (blockIdx.x + k * gridDim.x, the same XCD-contiguous band order):
+// Persistent form of the 8-bit kernel for large launches (the DeepSeek-like
+// layer's fp8 GEMMs, the Qwen3-like MXFP8 prefill).  Per item the plain
+// kernel spends 3.5-4.5 us before its first MFMA (the chain tile count ->
+// band entry -> tile entry -> group offsets -> A rows, then the first chunk)
+// and 2.5-5 us in the epilogue, with a workgroup launch in between: 12 % of
+// a DeepSeek-like gate/up item, a quarter of its down item (16 chunks), a
+// fifth and a third of the MXFP8 prefill's.  Here one workgroup per CU walks
+// its items (blockIdx.x + k * gridDim.x, the same XCD-contiguous band order):
 //   - the lanes of every wave look up the workgroup's items once, in
 //     parallel (lane l: item l, at most 64), and keep them in registers;
 //   - the last NS iterations of an item's K loop load the next item's first
 //     chunks into the ring, so the next item starts on data already in LDS;
-//   - the epilogue writes from registers (no staging tile).  The next item's
-//     third chunk is held back until after the stores (the last iteration's
-//     loads go to the sink instead, keeping the counts): gate/up passes the
-//     per-row maxima of four waves through the stage the last chunk freed,
-//     and the wait for the next item's first chunk then retires neither the
-//     stores nor that chunk;
-//   - gathered A rows (gate/up) are looked up two items ahead, right after
-//     an epilogue, when only loads issued long before are in flight.
-// Same arithmetic and bits as k_tiled8<false, DUAL, 160, 1>.
-template <bool DUAL>
+//   - the epilogue writes from registers (no staging tile): MXFP8 multiplies
+//     with the operands swapped (D = B A^T, as fp8), so a lane holds four
+//     consecutive columns of one row and a 32-column E8M0 block of h is one
+//     wave's, reduced across its lanes.  The next item's third chunk is held
+//     back until after the stores (the last iteration's loads go to the sink
+//     instead, keeping the counts): fp8 gate/up passes the per-row maxima of
+//     four waves through the stage the last chunk freed, and the wait for
+//     the next item's first chunk then retires neither the stores nor that
+//     chunk;
+//   - gathered A rows (gate/up; MXFP8 also their scale rows) are looked up
+//     two items ahead, right after an epilogue, when only loads issued long
+//     before are in flight;
+//   - MXFP8 scale stages alternate per 4-chunk group across items (a
+//     running parity), as within one.
+// fp8: same arithmetic and bits as k_tiled8<false, DUAL, 160, 1>; MXFP8: the
+// same products as k_tiled8<true, DUAL, 128, 4>, taken transposed.
+template <bool MX, bool DUAL>
 __global__ __launch_bounds__(512) void k_tiled8p(const GemmArgs p) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  constexpr bool MX = false;
-  constexpr int BM = 160, SG = 1;
+  constexpr int BM = MX ? 128 : 160, SG = MX ? 4 : 1;
   using L = Tiled8Lds<MX, BM, SG>;
   static_assert(L::TOTAL <= 160 * 1024, "LDS budget");
+  static_assert(SG == 1 || L::NSS == 2, "MXFP8: two 4-chunk scale stages");
   constexpr int NS = k8NS;
   constexpr int NW = 8, WN = 4;
   constexpr int MB = BM / 32;
@@ -705,58 +713,89 @@ __global__ __launch_bounds__(512) void k_tiled8p(const GemmArgs p) {
   const int srow = wave * 64 + lane;
   const int sr = min(srow, L::SROWS - 1);
   const bool swave = wave < NSC;
-  const uint32_t sstep = sr < BM ? 4u * (uint32_t)p.s_ld : 4u;
+  const uint32_t sstep = (!MX && sr < BM) ? 4u * (uint32_t)p.s_ld : 4u;
 
-  // Load sources of one item.
+  // Load sources of one item.  spad (MXFP8): what lane 63 reads, for the
+  // scale loads that only keep the counts (one line instead of 64).
   struct Src {
     const uint8_t* ab;
     const uint8_t* bb;
     const uint8_t* ssrc;
+    const uint8_t* spad;
     uint32_t aoff[IPWA];
     uint32_t boff[IPWB];
   };
-  // A offsets of an item (the gathered row, if any, times K plus the slot).
-  auto a_offsets = [&](const Item& it, uint32_t (&ao)[IPWA]) {
+  // A rows of an item (the gathered ones, if any) as offsets, and for MXFP8
+  // the lane's activation scale row.
+  struct ARows { uint32_t off[IPWA]; uint32_t srow; };
+  auto a_rows_of = [&](const Item& it) {
+    ARows ar;
 #pragma unroll
     for (int j = 0; j < IPWA; ++j) {
       const int r = min(arow[j], it.mrows - 1);
-      ao[j] = (p.a_rows ? (uint32_t)p.a_rows[it.row0 + r] : (uint32_t)r) * (uint32_t)K + asl[j];
+      ar.off[j] = (p.a_rows ? (uint32_t)p.a_rows[it.row0 + r] : (uint32_t)r) * (uint32_t)K + asl[j];
     }
+    ar.srow = 0;
+    if constexpr (MX) {
+      const int r = it.row0 + min(sr, it.mrows - 1);
+      ar.srow = (uint32_t)((p.a_rows && sr < BM) ? p.a_rows[r] : r);
+    }
+    return ar;
   };
-  auto make_src = [&](const Item& it, const uint32_t (&ao)[IPWA]) {
+  auto make_src = [&](const Item& it, const ARows& ar) {
     Src s;
     s.ab = p.a_rows ? p.A : p.A + (size_t)it.row0 * K;
 #pragma unroll
-    for (int j = 0; j < IPWA; ++j) s.aoff[j] = ao[j];
+    for (int j = 0; j < IPWA; ++j) s.aoff[j] = ar.off[j];
     s.bb = Bm + (size_t)it.g * N * K;
     const int n0 = it.nt * (DUAL ? 128 : 256);
 #pragma unroll
     for (int j = 0; j < IPWB; ++j)
       s.boff[j] = (uint32_t)min(n0 + br0 + j * 8 + lane / 8, N - 1) * (uint32_t)K + bsl[j];
-    if (sr < BM) {
-      s.ssrc = static_cast<const uint8_t*>(p.A_scale) + (size_t)(it.row0 + min(sr, it.mrows - 1)) * 4;
+    if constexpr (MX) {
+      if (sr < BM) {
+        s.ssrc = static_cast<const uint8_t*>(p.A_scale) + (size_t)ar.srow * (size_t)(4 * KB);
+      } else {
+        int br = sr - BM;
+        const uint8_t* sB = static_cast<const uint8_t*>(p.s_B0);
+        if (DUAL && br >= 128) { sB = static_cast<const uint8_t*>(p.s_B1); br -= 128; }
+        s.ssrc = sB + ((size_t)it.g * N + min(n0 + br, N - 1)) * (size_t)(K / 32);
+      }
+      s.spad = reinterpret_cast<const uint8_t*>(
+          ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(reinterpret_cast<uint64_t>(s.ssrc) >> 32), 63) << 32) |
+          (uint32_t)__builtin_amdgcn_readlane((int)reinterpret_cast<uint64_t>(s.ssrc), 63));
     } else {
-      const int which = sr - BM;
-      if (DUAL)
-        s.ssrc = static_cast<const uint8_t*>(which ? p.s_B1 : p.s_B0) +
-                 ((size_t)it.g * N128 + it.nt) * (size_t)(4 * KB);
-      else
-        s.ssrc = static_cast<const uint8_t*>(p.s_B0) +
-                 ((size_t)it.g * N128 + min(n0 / 128 + which, N128 - 1)) * (size_t)(4 * KB);
+      if (sr < BM) {
+        s.ssrc = static_cast<const uint8_t*>(p.A_scale) + (size_t)(it.row0 + min(sr, it.mrows - 1)) * 4;
+      } else {
+        const int which = sr - BM;
+        if (DUAL)
+          s.ssrc = static_cast<const uint8_t*>(which ? p.s_B1 : p.s_B0) +
+                   ((size_t)it.g * N128 + it.nt) * (size_t)(4 * KB);
+        else
+          s.ssrc = static_cast<const uint8_t*>(p.s_B0) +
+                   ((size_t)it.g * N128 + min(n0 / 128 + which, N128 - 1)) * (size_t)(4 * KB);
+      }
+      s.spad = s.ssrc;
     }
     return s;
   };
 
   auto a_st = [&](int st) { return lds + st * L::A_BYTES; };
   auto b_st = [&](int st) { return lds + B_RING + st * L::B_BYTES; };
-  auto s_st = [&](int st) { return lds + S_RING + st * L::SSTAGE; };
+  // Scale stage of chunk c in ring stage st: fp8 the ring stage; MXFP8 the
+  // parity of the chunk's 4-chunk group counted from the walk's start (sgo:
+  // the item's first group's parity).
+  auto s_stage = [&](int c, int st, int sgo) { return MX ? (((c >> 2) + sgo) & 1) : st; };
   // Part j of chunk c of source s into stage st (to_sink: every load of the
   // part goes to the sink; it only keeps the counts).
-  auto issue_part = [&](const Src& s, int c, int st, int j, bool to_sink) {
+  auto issue_part = [&](const Src& s, int c, int st, int sgo, int j, bool to_sink) {
     const int cc = min(c, nk - 1);
     if (j == 0) {
-      uint8_t* const dst = (swave && !to_sink) ? s_st(st) + wave * 64 * L::SB : sink;
-      dma_addr_untracked<L::SB>(s.ssrc + (size_t)cc * sstep, dst);
+      const bool real = swave && c % SG == 0 && !to_sink;
+      uint8_t* const dst = real ? lds + S_RING + s_stage(c, st, sgo) * L::SSTAGE + wave * 64 * L::SB : sink;
+      const size_t sk = (size_t)(cc - cc % SG);
+      dma_addr_untracked<L::SB>((real || !MX ? s.ssrc : s.spad) + sk * sstep, dst);
     }
     if (j < IPWA) {
       const int ja = j < IPWA ? j : 0;
@@ -767,30 +806,27 @@ __global__ __launch_bounds__(512) void k_tiled8p(const GemmArgs p) {
     dma16_untracked(s.bb + (size_t)cc * 128, s.boff[j], dst);
   };
 
-  // First items: sources of items 0 and 1, A offsets of item 2, then the
-  // first NS chunks of item 0.
+  // First items: sources of items 0 and 1, A rows of item 2, then the first
+  // NS chunks of item 0.
   Src cur, nxt;
-  uint32_t ao2[IPWA];
+  ARows ar2;
   {
-    uint32_t ao[IPWA];
     const Item i0 = item(0);
-    a_offsets(i0, ao);
-    cur = make_src(i0, ao);
+    cur = make_src(i0, a_rows_of(i0));
     if (n_items > 1) {
       const Item i1 = item(1);
-      a_offsets(i1, ao);
-      nxt = make_src(i1, ao);
+      nxt = make_src(i1, a_rows_of(i1));
     } else {
       nxt = cur;
     }
-    if (n_items > 2) a_offsets(item(2), ao2);
-#pragma unroll
-    for (int j = 0; j < IPWA; ++j) ao2[j] = n_items > 2 ? ao2[j] : cur.aoff[j];
+    ar2 = a_rows_of(item(n_items > 2 ? 2 : 0));
   }
+  int sgo = 0;                                       // MXFP8: scale-group parity of the item's chunk 0
+  const int sgo_step = (nk / 4) & 1;
 #pragma unroll
   for (int c = 0; c < NS; ++c)
 #pragma unroll
-    for (int j = 0; j < NB; ++j) issue_part(cur, c, c, j, false);
+    for (int j = 0; j < NB; ++j) issue_part(cur, c, c, 0, j, false);
   wait_vmcnt<(NS - 1) * OPS>();
   lds_barrier();
 
@@ -801,12 +837,14 @@ __global__ __launch_bounds__(512) void k_tiled8p(const GemmArgs p) {
   const bool ceven = ((lane >> 4) & 1) == 0;
   const int pcol = ceven ? 4 * (lane >> 4) : 16 + 4 * ((lane >> 4) - 1);
   const int c0 = lane >> 4, c1 = 4 + (lane >> 4);
+  const int sh = 8 * (lane >> 4);                    // MXFP8: byte of this lane's K block
   const uint32_t a_lo0 = (uint32_t)((rbase + r16) * 128 + (slot8(r16, c0) << 4));
   const uint32_t a_hi0 = (uint32_t)((rbase + r16) * 128 + (slot8(r16, c1) << 4));
   const int brow0 = b8_row<DUAL>(0, wn, r16);
   const uint32_t b_lo0 = (uint32_t)(B_RING + brow0 * 128 + (slot8(r16, c0) << 4));
   const uint32_t b_hi0 = (uint32_t)(B_RING + brow0 * 128 + (slot8(r16, c1) << 4));
   const uint32_t s_a0 = (uint32_t)(S_RING + (rbase + r16) * L::SB);
+  const uint32_t s_b0 = (uint32_t)(S_RING + (BM + brow0) * L::SB);   // MXFP8: B row scales
   auto opq = [](uint32_t v) { asm volatile("" : "+v"(v)); return v; };
   auto frag_at = [&](uint32_t lo, uint32_t hi) {
     const u32x4_t x = lds_read16(lds + lo), y = lds_read16(lds + hi);
@@ -817,44 +855,54 @@ __global__ __launch_bounds__(512) void k_tiled8p(const GemmArgs p) {
 
   f32x4_t acc[MB][NB];
   i32x8_t a[MB], b[NB];
-  float saf[MB];
+  float saf[MB];                                     // fp8: activation scale of the lane's row
+  uint32_t sam[MB], sbm[NB];                         // MXFP8: E8M0 bytes
   float sb_lo = 0.f, sb_hi = 0.f;
-  struct Bases { uint32_t alo, ahi, blo, bhi, sa; };
-  auto bases = [&](int st) {
-    const uint32_t so = (uint32_t)(st * L::SSTAGE);
+  struct Bases { uint32_t alo, ahi, blo, bhi, sa, sb; };
+  auto bases = [&](int c, int st, int sgo_) {
+    const uint32_t so = (uint32_t)(s_stage(c, st, sgo_) * L::SSTAGE + (MX ? (c & 3) * 4 : 0));
     return Bases{opq(a_lo0 + st * L::A_BYTES), opq(a_hi0 + st * L::A_BYTES),
-                 opq(b_lo0 + st * L::B_BYTES), opq(b_hi0 + st * L::B_BYTES), opq(s_a0 + so)};
+                 opq(b_lo0 + st * L::B_BYTES), opq(b_hi0 + st * L::B_BYTES), opq(s_a0 + so),
+                 MX ? opq(s_b0 + so) : 0u};
   };
   auto next_a = [&](const Bases& q, int i) {
     a[i] = frag_at(q.alo + i * 2048, q.ahi + i * 2048);
-    saf[i] = __uint_as_float(ld32(q.sa + i * 16 * L::SB));
+    if constexpr (MX) sam[i] = (ld32(q.sa + i * 16 * L::SB) >> sh) & 0xFFu;
+    else saf[i] = __uint_as_float(ld32(q.sa + i * 16 * L::SB));
   };
   auto next_b = [&](const Bases& q, int j) {
     const int dr = b8_row<DUAL>(j, 0, 0);
     b[j] = frag_at(q.blo + dr * 128, q.bhi + dr * 128);
+    if constexpr (MX) sbm[j] = (ld32(q.sb + dr * L::SB) >> sh) & 0xFFu;
   };
   auto rd_bsc = [&](int st) {
-    const uint32_t o = S_RING + (uint32_t)(st * L::SSTAGE) + BM * L::SB;
-    const float s0 = __uint_as_float(ld32(o)), s1 = __uint_as_float(ld32(o + L::SB));
-    sb_lo = DUAL ? s0 : (wn < 2 ? s0 : s1);
-    sb_hi = DUAL ? s1 : sb_lo;
+    if constexpr (!MX) {
+      const uint32_t o = S_RING + (uint32_t)(st * L::SSTAGE) + BM * L::SB;
+      const float s0 = __uint_as_float(ld32(o)), s1 = __uint_as_float(ld32(o + L::SB));
+      sb_lo = DUAL ? s0 : (wn < 2 ? s0 : s1);
+      sb_hi = DUAL ? s1 : sb_lo;
+    }
   };
   constexpr int HMAX = MB - HA;
   f32x4_t pr[2][HMAX];
   auto col = [&](int i0, int i1, int j, auto nm) {
 #pragma unroll
     for (int i = i0; i < i1; ++i)
-      if (i < count_value(nm))
-        pr[j & 1][i - i0] = mfma_fp8_16x16x128(b[j], a[i], f32x4_t{0.f, 0.f, 0.f, 0.f});
+      if (i < count_value(nm)) {
+        if constexpr (MX) acc[i][j] = mfma_mx8_16x16x128(b[j], a[i], acc[i][j], sbm[j], sam[i]);
+        else pr[j & 1][i - i0] = mfma_fp8_16x16x128(b[j], a[i], f32x4_t{0.f, 0.f, 0.f, 0.f});
+      }
   };
   auto scale_col = [&](int i0, int i1, int j, auto nm) {
-    const float sbv = j < NB / 2 ? sb_lo : sb_hi;
+    if constexpr (!MX) {
+      const float sbv = j < NB / 2 ? sb_lo : sb_hi;
 #pragma unroll
-    for (int i = i0; i < i1; ++i)
-      if (i < count_value(nm)) {
+      for (int i = i0; i < i1; ++i)
+        if (i < count_value(nm)) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[i][j][q] += pr[j & 1][i - i0][q] * (saf[i] * sbv);
-      }
+          for (int q = 0; q < 4; ++q) acc[i][j][q] += pr[j & 1][i - i0][q] * (saf[i] * sbv);
+        }
+    }
   };
 
   int st = 0;                                        // ring stage of the current chunk
@@ -871,11 +919,14 @@ __global__ __launch_bounds__(512) void k_tiled8p(const GemmArgs p) {
     tsrc.ab = has_next ? nxt.ab : cur.ab;
     tsrc.bb = has_next ? nxt.bb : cur.bb;
     tsrc.ssrc = has_next ? nxt.ssrc : cur.ssrc;
+    tsrc.spad = has_next ? nxt.spad : cur.spad;
 #pragma unroll
     for (int j = 0; j < IPWA; ++j) tsrc.aoff[j] = has_next ? nxt.aoff[j] : cur.aoff[j];
 #pragma unroll
     for (int j = 0; j < IPWB; ++j) tsrc.boff[j] = has_next ? nxt.boff[j] : cur.boff[j];
     const int tshift = has_next ? nk : 0;
+    const int sgo_n = (sgo + sgo_step) & 1;          // MXFP8: the next item's
+    const int tsgo = has_next ? sgo_n : sgo;
 
 #pragma unroll
     for (int i = 0; i < MB; ++i)
@@ -884,7 +935,7 @@ __global__ __launch_bounds__(512) void k_tiled8p(const GemmArgs p) {
 
     auto main_loop = [&](auto nm) {
       {
-        const Bases q0 = bases(st);
+        const Bases q0 = bases(0, st, sgo);
 #pragma unroll
         for (int j = 0; j < NB; ++j) next_b(q0, j);
 #pragma unroll
@@ -893,10 +944,10 @@ __global__ __launch_bounds__(512) void k_tiled8p(const GemmArgs p) {
       rd_bsc(st);
       // One chunk: its loads are issued by issue(j) between the second
       // half's columns.
-      auto step = [&](auto&& issue) {
+      auto step = [&](int kc, auto&& issue) {
         const int sn = st == NS - 1 ? 0 : st + 1;
         {
-          const Bases qk = bases(st);
+          const Bases qk = bases(kc, st, sgo);
 #pragma unroll
           for (int i = HA; i < MB; ++i) next_a(qk, i);
         }
@@ -912,7 +963,8 @@ __global__ __launch_bounds__(512) void k_tiled8p(const GemmArgs p) {
           for (int j = 0; j < NB; ++j) asm volatile("" : "+v"(acc[i][j]));
         wait_vmcnt<(NS - 2) * OPS>();
         lds_barrier();
-        const Bases qn = bases(sn);
+        // (After the last chunk these read the next item's chunk 0, unused.)
+        const Bases qn = bases(kc + 1, sn, sgo);
 #pragma unroll
         for (int i = 0; i < HA; ++i) next_a(qn, i);
         __builtin_amdgcn_sched_barrier(0);
@@ -929,11 +981,11 @@ __global__ __launch_bounds__(512) void k_tiled8p(const GemmArgs p) {
         st = sn;
       };
       for (int kc = 0; kc < nk - NS; ++kc)
-        step([&](int j) { issue_part(cur, kc + NS, st, j, false); });
+        step(kc, [&](int j) { issue_part(cur, kc + NS, st, sgo, j, false); });
       for (int kc = nk - NS; kc < nk; ++kc) {
         // The next item's chunk NS-1 is held back (see below).
         const bool to_sink = has_next && kc == nk - 1;
-        step([&](int j) { issue_part(tsrc, kc + NS - tshift, st, j, to_sink); });
+        step(kc, [&](int j) { issue_part(tsrc, kc + NS - tshift, st, tsgo, j, to_sink); });
       }
     };
     with_count<MB>(nmb, main_loop);
@@ -943,11 +995,15 @@ __global__ __launch_bounds__(512) void k_tiled8p(const GemmArgs p) {
     if (!has_next) wait_vmcnt<0>();                  // the tail's re-reads land before the exit
 
     if constexpr (DUAL) {
-      // h = silu(g) * u; per-row maxima over the tile's 128 columns (the
-      // lane's 8 values, the 4 lanes of the row, the 4 waves of the row
-      // through the free stage), e4m3 codes with scale amax / 448.
-      float* amax_s = reinterpret_cast<float*>(b_st(st_last));   // [WN][BM]
-      lds_barrier();
+      // h = silu(g) * u per lane: row m, columns 4 c + q of blocks 0 and 1
+      // (c = lane / 16).  MXFP8: one E8M0 scale per row and 32 columns (the
+      // wave's); fp8: per 128 columns (four waves, through the free stage),
+      // scale amax / 448.
+      uint32_t w4[MB][2];
+      float scl[MB];
+      uint32_t e8s[MB];
+      float* amax_s = reinterpret_cast<float*>(b_st(st_last));   // fp8: [WN][BM]
+      if constexpr (!MX) lds_barrier();
 #pragma unroll
       for (int i = 0; i < MB; ++i) {
         const int m = rbase + i * 16 + r16;
@@ -956,39 +1012,55 @@ __global__ __launch_bounds__(512) void k_tiled8p(const GemmArgs p) {
         for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float h = (i < nmb && m < it.mrows) ? silu_mul(acc[i][j][q], acc[i][j + 2][q]) : 0.f;
+            float h;
+            if constexpr (MX) h = silu_mul(acc[i][j][q], acc[i][j + 2][q]);
+            else h = (i < nmb && m < it.mrows) ? silu_mul(acc[i][j][q], acc[i][j + 2][q]) : 0.f;
             acc[i][j][q] = h;
             am = fmaxf(am, fabsf(h));
           }
         am = fmaxf(am, __shfl_xor(am, 16));
         am = fmaxf(am, __shfl_xor(am, 32));
-        if (lane < 16) amax_s[wn * BM + m] = am;
-      }
-      lds_barrier();
-      uint32_t w4[MB][2];
-      float scl[MB];
+        if constexpr (MX) {
+          const uint32_t e8 = mx_e8m0(am);
+          const float inv = mx_inv_scale(e8);
+          e8s[i] = e8;
 #pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        const int m = rbase + i * 16 + r16;
-        float am = 0.f;
+          for (int j = 0; j < 2; ++j) {
+            uint32_t v = 0;
 #pragma unroll
-        for (int w = 0; w < WN; ++w) am = fmaxf(am, amax_s[w * BM + m]);
-        const float scale = am == 0.f ? 1.f : am / 448.f;
-        scl[i] = scale;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          float qv[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) qv[q] = fminf(fmaxf(acc[i][j][q] / scale, -448.f), 448.f);
-          int v = __builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[1], 0, false);
-          v = __builtin_amdgcn_cvt_pk_fp8_f32(qv[2], qv[3], v, true);
-          w4[i][j] = (uint32_t)v;
+            for (int q = 0; q < 4; ++q)
+              v |= ((uint32_t)f32_to_e4m3(fminf(fmaxf(acc[i][j][q] * inv, -448.f), 448.f)) & 0xFFu) << (8 * q);
+            w4[i][j] = v;
+          }
+        } else {
+          if (lane < 16) amax_s[wn * BM + m] = am;
         }
       }
-      if (has_next && it_i + 2 < n_items) a_offsets(item(it_i + 2), ao2);
-      // Lanes c and c ^ 1 (c = lane / 16) trade codes so that each holds
-      // eight consecutive columns of its row (c even of block 0, c odd of
-      // block 1): one 8-byte store per lane and row block.
+      if constexpr (!MX) {
+        lds_barrier();
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+          const int m = rbase + i * 16 + r16;
+          float am = 0.f;
+#pragma unroll
+          for (int w = 0; w < WN; ++w) am = fmaxf(am, amax_s[w * BM + m]);
+          const float scale = am == 0.f ? 1.f : am / 448.f;
+          scl[i] = scale;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            float qv[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) qv[q] = fminf(fmaxf(acc[i][j][q] / scale, -448.f), 448.f);
+            int v = __builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[1], 0, false);
+            v = __builtin_amdgcn_cvt_pk_fp8_f32(qv[2], qv[3], v, true);
+            w4[i][j] = (uint32_t)v;
+          }
+        }
+      }
+      if (has_next && it_i + 2 < n_items) ar2 = a_rows_of(item(it_i + 2));
+      // Lanes c and c ^ 1 trade codes so that each holds eight consecutive
+      // columns of its row (c even of block 0, c odd of block 1): one 8-byte
+      // store per lane and row block.
 #pragma unroll
       for (int i = 0; i < MB; ++i)
         if (i < nmb) {
@@ -997,13 +1069,19 @@ __global__ __launch_bounds__(512) void k_tiled8p(const GemmArgs p) {
           if (m < it.mrows) {
             const u32x2_t o = ceven ? u32x2_t{w4[i][0], got} : u32x2_t{got, w4[i][1]};
             *reinterpret_cast<u32x2_t*>(p.out + (size_t)(it.row0 + m) * N + n0 + wn * 32 + pcol) = o;
-            if (wn == 0 && lane < 16)
-              static_cast<float*>(p.out_scale)[(size_t)it.nt * p.R + it.row0 + m] = scl[i];
+            if constexpr (MX) {
+              if (lane < 16)
+                static_cast<uint8_t*>(p.out_scale)[(size_t)(it.row0 + m) * (N / 32) + (n0 + wn * 32) / 32] =
+                    (uint8_t)e8s[i];
+            } else {
+              if (wn == 0 && lane < 16)
+                static_cast<float*>(p.out_scale)[(size_t)it.nt * p.R + it.row0 + m] = scl[i];
+            }
           }
         }
-      if (has_next) lds_barrier();                   // the maxima are read: the stage is free
+      if (!MX && has_next) lds_barrier();            // the maxima are read: the stage is free
     } else {
-      if (has_next && it_i + 2 < n_items) a_offsets(item(it_i + 2), ao2);
+      if (has_next && it_i + 2 < n_items) ar2 = a_rows_of(item(it_i + 2));
       // A lane holds four consecutive bf16 columns of row m per block; lanes
       // c and c ^ 1 trade halves so that each holds eight (c even of block j,
       // c odd of block j + 1): one 16-byte store per lane and block pair.
@@ -1035,9 +1113,10 @@ __global__ __launch_bounds__(512) void k_tiled8p(const GemmArgs p) {
     // chunk 0 (chunks 1, the sink loads and NS-1 came later) need not wait
     // for the stores, nor for this last chunk.
 #pragma unroll
-    for (int j = 0; j < NB; ++j) issue_part(nxt, NS - 1, st_last, j, false);
+    for (int j = 0; j < NB; ++j) issue_part(nxt, NS - 1, st_last, sgo_n, j, false);
     cur = nxt;
-    if (it_i + 2 < n_items) nxt = make_src(item(it_i + 2), ao2);
+    if (it_i + 2 < n_items) nxt = make_src(item(it_i + 2), ar2);
+    sgo = sgo_n;
     wait_vmcnt<NS * OPS>();                          // the new item's chunk 0 is in
     lds_barrier();
   }
@@ -1063,8 +1142,30 @@ hipError_t launch_tiled8(const char* name, bool mx, bool dual, long long blocks,
   // Scales in groups of 4 chunks when a row's scale array splits into 16-byte
   // pieces (K a multiple of 512), else one 4-byte load per chunk.
   const bool g4 = a.K % 512 == 0;
+  static_assert(tile_rows(true, true) == 128, "MXFP8 tile height");
+  static_assert(tile_rows(true, false) == 160, "fp8 tile height");
+  // Persistent walk for large launches: one workgroup per CU (more when a
+  // workgroup would exceed the 64 items its lanes hold), a multiple of 8 so
+  // that every workgroup stays on one XCD's band run.  Needs K of at least
+  // NS chunks, no ragged column tile, the packed item fields (rows < 2^24,
+  // column tiles < 256), and fp8 ungathered activation scales, MXFP8 scales
+  // in 4-chunk groups.
+  const long long pairs = (long long)band_grid(blocks, 1);
+  const int ncw = dual ? 128 : 256;
+  if (pairs >= 4 * kPersistGrid && a.K >= 128 * k8NS && a.N % ncw == 0 && a.n_ntile < 256 &&
+      a.R < (1 << 24) && (mx ? g4 : a.s_rows == nullptr)) {
+    const long long need = (pairs + 8 + 63) / 64;
+    const dim3 pgrid((unsigned)(((need > kPersistGrid ? need : kPersistGrid) + 7) / 8 * 8));
+    if (mx) {
+      if (dual) MOE_LAUNCH(name, (k_tiled8p<true, true>), pgrid, dim3(512), 0, s, a);
+      else MOE_LAUNCH(name, (k_tiled8p<true, false>), pgrid, dim3(512), 0, s, a);
+    } else {
+      if (dual) MOE_LAUNCH(name, (k_tiled8p<false, true>), pgrid, dim3(512), 0, s, a);
+      else MOE_LAUNCH(name, (k_tiled8p<false, false>), pgrid, dim3(512), 0, s, a);
+    }
+    return hipGetLastError();
+  }
   if (mx) {
-    static_assert(tile_rows(true, true) == 128, "MXFP8 tile height");
     if (dual) {
       if (g4) MOE_LAUNCH(name, (k_tiled8<true, true, 128, 4>), grid, dim3(512), 0, s, a);
       else MOE_LAUNCH(name, (k_tiled8<true, true, 128, 1>), grid, dim3(512), 0, s, a);
@@ -1073,22 +1174,6 @@ hipError_t launch_tiled8(const char* name, bool mx, bool dual, long long blocks,
       else MOE_LAUNCH(name, (k_tiled8<true, false, 128, 1>), grid, dim3(512), 0, s, a);
     }
   } else {
-    static_assert(tile_rows(true, false) == 160, "fp8 tile height");
-    // Persistent walk for large launches: one workgroup per CU (more when a
-    // workgroup would exceed the 64 items its lanes hold), a multiple of 8 so
-    // that every workgroup stays on one XCD's band run.  Needs K of at
-    // least NS chunks, no ragged column tile, ungathered activation scales
-    // and the packed item fields (rows < 2^24, column tiles < 256).
-    const long long pairs = (long long)band_grid(blocks, 1);
-    const int ncw = dual ? 128 : 256;
-    if (pairs >= 4 * kPersistGrid && a.s_rows == nullptr && a.K >= 128 * k8NS && a.N % ncw == 0 &&
-        a.n_ntile < 256 && a.R < (1 << 24)) {
-      const long long need = (pairs + 8 + 63) / 64;
-      const dim3 pgrid((unsigned)(((need > kPersistGrid ? need : kPersistGrid) + 7) / 8 * 8));
-      if (dual) MOE_LAUNCH(name, (k_tiled8p<true>), pgrid, dim3(512), 0, s, a);
-      else MOE_LAUNCH(name, (k_tiled8p<false>), pgrid, dim3(512), 0, s, a);
-      return hipGetLastError();
-    }
     if (dual) MOE_LAUNCH(name, (k_tiled8<false, true, 160, 1>), grid, dim3(512), 0, s, a);
     else MOE_LAUNCH(name, (k_tiled8<false, false, 160, 1>), grid, dim3(512), 0, s, a);
   }

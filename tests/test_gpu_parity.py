@@ -410,15 +410,17 @@ def test_forward_streaming_walk(wdtype):
     _forward_check(cfg, li)
 
 
-# Large fp8 launches run the persistent tiled kernel (one workgroup per CU
+# Large 8-bit launches run the persistent tiled kernel (one workgroup per CU
 # walking its tiles, the next tile's first chunks loaded during the current
-# tile's last ones, the epilogue stored from registers).  DeepSeek-like
-# routing at 1024 tokens leaves the tiles of the 1024-row shared expert and
-# a few routed groups (most workgroups get no tile or one); 1536 and 2048
-# tokens give about 4 and 8 tiles per workgroup (the full layer: 17 to 32).
+# tile's last ones, the epilogue stored from registers; MXFP8 with its scale
+# stages alternating across tiles).  DeepSeek-like routing at 1024 tokens
+# leaves the tiles of the 1024-row shared expert and a few routed groups
+# (most workgroups get no tile or one); 1536 and 2048 tokens give about 4
+# and 8 tiles per workgroup (the full layers: 17 to 37).
+@pytest.mark.parametrize("wdtype", ["fp8", "mxfp8"])
 @pytest.mark.parametrize("T", [1024, 1536, 2048])
-def test_forward_fp8_persistent_walk(T):
-    cfg = MoeConfig(f"pers_{T}", 58, T=T, H=2048, E=256, k=8, I=1024, n_shared=1, wdtype="fp8")
+def test_forward_8bit_persistent_walk(T, wdtype):
+    cfg = MoeConfig(f"pers_{T}_{wdtype}", 58, T=T, H=2048, E=256, k=8, I=1024, n_shared=1, wdtype=wdtype)
     li = generate_layer(cfg, DEV)
     _, idx, _ = run_route(cfg, li)
     tiled = np.bincount(idx.cpu().numpy().ravel(), minlength=cfg.E) > 48
