@@ -26,6 +26,42 @@ __device__ __forceinline__ float key_to_value(uint32_t u) {
 // expert among equal ones; k rounds of max + removal give the slots best
 // first.  Lane j < k returns slot j's expert and its renormalised weight
 // exp(l_j - l_0) / sum.
+// One 64-bit key per lane through a DPP permutation (both halves).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)v, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(v >> 32), (int)(uint32_t)(v >> 32),
+                                                            CTRL, 0xF, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Maximum of a 64-bit key over the 64 lanes of a wave, in every lane (all
+// lanes active): DPP quad swaps and row mirrors within each row of 16, then
+// gfx950's row swaps (v_permlane16_swap / v_permlane32_swap return both
+// members of the lane ^ 16 and lane ^ 32 pairs).  Register moves instead of
+// six LDS-crossbar round trips per reduction.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = max_u64(v, dpp_u64<0xB1>(v));                 // quad_perm [1,0,3,2]: lane ^ 1
+  v = max_u64(v, dpp_u64<0x4E>(v));                 // quad_perm [2,3,0,1]: lane ^ 2
+  v = max_u64(v, dpp_u64<0x141>(v));                // row_half_mirror: the other quad of 8
+  v = max_u64(v, dpp_u64<0x140>(v));                // row_mirror: the other half of 16
+  {
+    const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    const auto l = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto h = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    v = max_u64(((uint64_t)h[0] << 32) | l[0], ((uint64_t)h[1] << 32) | l[1]);
+  }
+  {
+    const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    const auto l = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto h = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    v = max_u64(((uint64_t)h[0] << 32) | l[0], ((uint64_t)h[1] << 32) | l[1]);
+  }
+  return v;
+}
+
 template <int NPL>
 __device__ __forceinline__ void topk_token(const float* parts, int KS, const float* bias,
                                            float* logits_out, int t, int T, int E, int k,
@@ -50,12 +86,7 @@ __device__ __forceinline__ void topk_token(const float* parts, int KS, const flo
     uint64_t best = 0ull;
 #pragma unroll
     for (int i = 0; i < NPL; ++i) best = key[i] > best ? key[i] : best;
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      uint32_t lo = __shfl_xor((uint32_t)best, m), hi = __shfl_xor((uint32_t)(best >> 32), m);
-      uint64_t o = ((uint64_t)hi << 32) | lo;
-      best = o > best ? o : best;
-    }
+    best = wave_max_u64(best);
     // Remove the winner (keys are unique: the expert index is part of them).
 #pragma unroll
     for (int i = 0; i < NPL; ++i) key[i] = key[i] == best ? 0ull : key[i];
