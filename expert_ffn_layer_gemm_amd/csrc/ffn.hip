@@ -753,13 +753,15 @@ SideStream* side_stream(int slot) {
 }
 
 // When (nearly) every group is tiled, the streaming kernels' grid is capped
-// at kSkinnyGrid workgroups (16 per CU; a multiple of 8 times every split
+// at kSkinnyGrid workgroups (4 per CU; a multiple of 8 times every split
 // factor) that walk the work list: the host-side bound on the items is loose
 // (every group might be small), and a grid of that bound whose workgroups
 // nearly all find nothing cost up to ~40 us of dispatch after the tiled chain
-// of the DeepSeek-like layer.  With real streaming work (decode, skewed
-// routing) each workgroup keeps one item: walking measured 2-3 % slower there.
-constexpr long long kSkinnyGrid = 4096;
+// of the DeepSeek-like layer (4096 walkers still 15 us, 1024 about a third of
+// that: the DeepSeek-like layer and both prefills -0.3 to -0.6 %).  With real
+// streaming work (decode, skewed routing) each workgroup keeps one item:
+// walking measured 2-3 % slower there.
+constexpr long long kSkinnyGrid = 1024;
 
 template <typename Kern1, typename KernW>
 static hipError_t launch_gemm(const char* name, Kern1 one, KernW walk_kern, int threads,

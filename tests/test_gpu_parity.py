@@ -398,7 +398,7 @@ def test_forward_edge_cases(case):
 
 # Layers whose mean group is large run the streaming kernels with a capped
 # grid whose workgroups walk the work list (each several items here: up to
-# 8192 items for 4096 workgroups); Zipf-skewed routing leaves real small
+# 8192 items for 1024 workgroups); Zipf-skewed routing leaves real small
 # groups for them next to the tiled ones.
 @pytest.mark.parametrize("wdtype", ["bf16", "fp8", "mxfp8"])
 def test_forward_streaming_walk(wdtype):
