@@ -67,18 +67,32 @@ __device__ __forceinline__ void topk_token(const float* parts, int KS, const flo
                                            float* logits_out, int t, int T, int E, int k,
                                            int lane, int& out_e, float& out_w) {
   const size_t plane = (size_t)T * E;
+  const size_t row = (size_t)t * E;
+  // Every lane's sums first, the logit stores after them: logits_out may alias
+  // parts, so a store between two lanes' worth of loads would hold the later
+  // loads back until it is done.  The adds stay in plane order.
+  float v[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) v[i] = parts[row + min(lane + 64 * i, E - 1)];
+#pragma unroll 4
+  for (int s2 = 1; s2 < KS; ++s2) {
+    float p[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) p[i] = parts[s2 * plane + row + min(lane + 64 * i, E - 1)];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) v[i] += p[i];
+  }
   uint64_t key[NPL];
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int e = lane + 64 * i;
-    const size_t o = (size_t)t * E + min(e, E - 1);
-    float v = parts[o];
-    // Loads of 8 planes in flight at a time; the adds stay in plane order.
-#pragma unroll 8
-    for (int s2 = 1; s2 < KS; ++s2) v += parts[s2 * plane + o];
-    if (bias) v += bias[min(e, E - 1)];
-    if (logits_out && e < E) logits_out[o] = v;
-    key[i] = e < E ? ((uint64_t)ordered_key(v) << 32) | (uint32_t)(~e) : 0ull;
+    if (bias) v[i] += bias[min(e, E - 1)];
+    key[i] = e < E ? ((uint64_t)ordered_key(v[i]) << 32) | (uint32_t)(~e) : 0ull;
+  }
+  if (logits_out) {
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      if (lane + 64 * i < E) logits_out[row + lane + 64 * i] = v[i];
   }
   int my_e = 0;
   float my_v = 0.f, top_v = 0.f;

@@ -25,6 +25,7 @@ namespace moe {
 
 
 constexpr int kRankTile = 256;   // tokens per tile of the histogram and rank kernels
+constexpr int kMaxTopK = 16;     // slots per token at most (the C ABI rejects k > 16)
 
 // Routings per local expert inside each 256-token tile: tile_cnt[tile][e]
 // (E = the share's experts, global ids e_first ..).
@@ -58,11 +59,19 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ tile_cnt, i
   for (int i = tid; i < 2048; i += 1024) cnt[i] = 0;
   __syncthreads();
   if (tid < E) {
+    // 16 tiles' counts loaded at a time before their bases are stored (a load
+    // after a store to the same array would wait for it).
     int run = 0;
-    for (int b = 0; b < n_tiles; ++b) {
-      const int c = tile_cnt[(size_t)b * E + tid];
-      tile_cnt[(size_t)b * E + tid] = run;
-      run += c;
+    for (int b0 = 0; b0 < n_tiles; b0 += 16) {
+      int c[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) c[q] = b0 + q < n_tiles ? tile_cnt[(size_t)(b0 + q) * E + tid] : 0;
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        if (b0 + q < n_tiles) {
+          tile_cnt[(size_t)(b0 + q) * E + tid] = run;
+          run += c[q];
+        }
     }
     cnt[tid] = run;
   }
@@ -73,7 +82,10 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ tile_cnt, i
 
 // Token-ascending rank of every (t, j) inside its expert's group: the tile's
 // base (k_scan) plus the routings of earlier tokens of the tile, counted from
-// an LDS bit mask per expert (one bit per token of the tile).
+// an LDS bit mask per expert (one bit per token of the tile).  A thread's k
+// expert ids are loaded once, and each expert's first row (offsets[e] + the
+// tile's base) is staged in LDS beside the masks, so the per-slot lookups are
+// LDS reads instead of k rounds of dependent global loads.
 __global__ __launch_bounds__(kRankTile) void k_rank(const int32_t* __restrict__ idx,
                                                     const int32_t* __restrict__ offsets,
                                                     const int32_t* __restrict__ tile_base,
@@ -81,23 +93,28 @@ __global__ __launch_bounds__(kRankTile) void k_rank(const int32_t* __restrict__ 
                                                     int32_t* __restrict__ src_row, int T, int E,
                                                     int k, int n_shared, int e_first) {
   __shared__ uint32_t mask[1024 * (kRankTile / 32)];
+  __shared__ int first_row[1024];
   const int tid = threadIdx.x;
+  const int32_t* base = tile_base + (size_t)blockIdx.x * E;
+  for (int i = tid; i < E; i += kRankTile) first_row[i] = offsets[i] + base[i];
   for (int i = tid; i < E * (kRankTile / 32); i += kRankTile) mask[i] = 0u;
-  __syncthreads();
   const int t = blockIdx.x * kRankTile + tid;
   const bool valid = t < T;
+  int ev[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) ev[j] = valid && j < k ? idx[(size_t)t * k + j] - e_first : -1;
+  __syncthreads();
   const int word = tid >> 5;
   const uint32_t bit = 1u << (tid & 31);
-  if (valid)
-    for (int j = 0; j < k; ++j) {
-      const int e = idx[(size_t)t * k + j] - e_first;
-      if ((unsigned)e < (unsigned)E) atomicOr(&mask[e * (kRankTile / 32) + word], bit);
-    }
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j)
+    if ((unsigned)ev[j] < (unsigned)E) atomicOr(&mask[ev[j] * (kRankTile / 32) + word], bit);
   __syncthreads();
   if (!valid) return;
-  const int32_t* base = tile_base + (size_t)blockIdx.x * E;
-  for (int j = 0; j < k; ++j) {
-    const int e = idx[(size_t)t * k + j] - e_first;
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    if (j >= k) break;
+    const int e = ev[j];
     if ((unsigned)e >= (unsigned)E) {   // routed to another share's expert
       dest[(size_t)t * k + j] = -1;
       continue;
@@ -105,7 +122,7 @@ __global__ __launch_bounds__(kRankTile) void k_rank(const int32_t* __restrict__ 
     const uint32_t* m = mask + e * (kRankTile / 32);
     int rank = __popc(m[word] & (bit - 1u));
     for (int w = 0; w < word; ++w) rank += __popc(m[w]);
-    const int d = offsets[e] + base[e] + rank;
+    const int d = first_row[e] + rank;
     dest[(size_t)t * k + j] = d;
     src_row[d] = t;
   }
