@@ -33,7 +33,7 @@ constexpr int kRtTM = 128, kRtTE = 128, kRtNS = 3;
 constexpr int kRtXB = kRtTM * 128;          // x bytes per stage (64 bf16 per row)
 constexpr int kRtWB = kRtTE * 256;          // W bytes per stage (64 fp32 per row)
 constexpr int kRtStage = kRtXB + kRtWB;     // 48 KB
-constexpr int kRtWaves = 8;                 // 2 (tokens) x 4 (experts)
+constexpr int kRtWaves = 8;                 // 1 (tokens) x 8 (experts)
 constexpr int kRtIPW = kRtStage / 1024 / kRtWaves;
 static_assert(kRtIPW * kRtWaves * 1024 == kRtStage, "stage must split evenly over the waves");
 
@@ -76,7 +76,11 @@ __global__ __launch_bounds__(512) void k_router_tiled(const uint16_t* __restrict
                                                       int E, int KS, int32_t* zero_ctr) {
 #if defined(__HIP_DEVICE_COMPILE__)
   if (zero_ctr && threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) *zero_ctr = 0;
-  constexpr int WN = 4, MB = kRtTM / 2 / 16, NB = kRtTE / WN / 16;
+  // Waves 1 (tokens) x 8 (experts): each wave multiplies all 128 token rows
+  // with its own 16 experts, so every W_r value of the stage is split into
+  // its three bf16 terms by one wave only (with 2 x 4 waves each split was
+  // done twice, and the split's vector ops outweighed the MFMAs).
+  constexpr int WM = 1, WN = 8, MB = kRtTM / WM / 16, NB = kRtTE / WN / 16;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kRtNS * kRtStage];
   const int t0 = blockIdx.x * kRtTM, e0 = blockIdx.y * kRtTE, ks = blockIdx.z;
   const int nch = H / 64;
@@ -113,7 +117,7 @@ __global__ __launch_bounds__(512) void k_router_tiled(const uint16_t* __restrict
     nv += jv[j] ? 1 : 0;
   }
 
-  const int rbase = wm * (kRtTM / 2), cbase = wn * (kRtTE / WN);
+  const int rbase = wm * (kRtTM / WM), cbase = wn * (kRtTE / WN);
   const int nmb = max(0, min(MB, ceil_div(mrows - rbase, 16)));
   const int ncb = max(0, min(NB, ceil_div(ncols - cbase, 16)));
 
@@ -148,27 +152,19 @@ __global__ __launch_bounds__(512) void k_router_tiled(const uint16_t* __restrict
         const u32x4_t w1 = lds_read16(Ws + e * 256 + (slot16(e, c0 + 1) << 4));
         split3(w0, w1, bh[j], bm[j], bl[j]);
       }
-      // Small terms first; the 3 x MB x NB MFMAs interleave independent accumulators.
+      // Small terms first (lo, mid, hi into each accumulator in turn).  With
+      // the three sweeps over all blocks of the 1 x 8 layout the compiler
+      // spilled; an accumulator's three MFMAs issue back to back instead.
 #pragma unroll
       for (int i = 0; i < MB; ++i)
         if (i < nmb) {
 #pragma unroll
           for (int j = 0; j < NB; ++j)
-            if (j < ncb) acc[i][j] = mfma_bf16_16x16x32(a[i], bl[j], acc[i][j]);
-        }
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-        if (i < nmb) {
-#pragma unroll
-          for (int j = 0; j < NB; ++j)
-            if (j < ncb) acc[i][j] = mfma_bf16_16x16x32(a[i], bm[j], acc[i][j]);
-        }
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-        if (i < nmb) {
-#pragma unroll
-          for (int j = 0; j < NB; ++j)
-            if (j < ncb) acc[i][j] = mfma_bf16_16x16x32(a[i], bh[j], acc[i][j]);
+            if (j < ncb) {
+              acc[i][j] = mfma_bf16_16x16x32(a[i], bl[j], acc[i][j]);
+              acc[i][j] = mfma_bf16_16x16x32(a[i], bm[j], acc[i][j]);
+              acc[i][j] = mfma_bf16_16x16x32(a[i], bh[j], acc[i][j]);
+            }
         }
     }
   }
