@@ -57,6 +57,24 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.f, 0, false) & 0xFFu;
 }
 
+// a / s rounded to nearest even, from y = 1 / s (itself rounded to nearest),
+// for scales s >= kDivFastMin; callers divide outright below that.  The
+// product |a| y is within 2 ulps of |a| / s; each step q += (|a| - q s) y takes
+// the exact FMA residual, and the second starts within 1 ulp and so rounds
+// correctly (Markstein's theorem for FMA division).  The residuals are exact
+// while s >= kDivFastMin and |a| / s >= 2^-10 (half the smallest e4m3 step);
+// below that the quotient may be off by an ulp, but every such value maps to
+// the e4m3 code 0 either way.  The sign is restored last, so -0 stays -0.
+// Four FMA-rate operations per value instead of a full-precision division.
+constexpr float kDivFastMin = 0x1p-64f;
+__device__ __forceinline__ float div_rn_by(float a, float s, float y) {
+  const float m = fabsf(a);
+  float q = m * y;
+  q = __builtin_fmaf(__builtin_fmaf(-q, s, m), y, q);
+  q = __builtin_fmaf(__builtin_fmaf(-q, s, m), y, q);
+  return __builtin_copysignf(q, a);
+}
+
 __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   uint32_t ef = (c >> 3) & 0xFu, mf = c & 7u;
   float mag = ef == 0 ? (float)mf * 0.001953125f

@@ -545,11 +545,24 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
 #pragma unroll
           for (int w = 0; w < WN; ++w) am = fmaxf(am, amax_s[w * BM + m]);
           const float scale = am == 0.f ? 1.f : am / 448.f;
+          float qd[2][4];
+          if (scale >= kDivFastMin) {       // the row's eight quotients from one reciprocal
+            const float y = 1.f / scale;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) qd[j][q] = div_rn_by(acc[i][j][q], scale, y);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) qd[j][q] = acc[i][j][q] / scale;
+          }
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             float qv[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) qv[q] = fminf(fmaxf(acc[i][j][q] / scale, -448.f), 448.f);
+            for (int q = 0; q < 4; ++q) qv[q] = fminf(fmaxf(qd[j][q], -448.f), 448.f);
             // four e4m3 codes, columns 4 (lane / 16) .. +3 of block j
             int w4 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[1], 0, false);
             w4 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[2], qv[3], w4, true);
@@ -1046,11 +1059,24 @@ __global__ __launch_bounds__(512) void k_tiled8p(const GemmArgs p) {
           for (int w = 0; w < WN; ++w) am = fmaxf(am, amax_s[w * BM + m]);
           const float scale = am == 0.f ? 1.f : am / 448.f;
           scl[i] = scale;
+          float qd[2][4];
+          if (scale >= kDivFastMin) {       // the row's eight quotients from one reciprocal
+            const float y = 1.f / scale;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) qd[j][q] = div_rn_by(acc[i][j][q], scale, y);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) qd[j][q] = acc[i][j][q] / scale;
+          }
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             float qv[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) qv[q] = fminf(fmaxf(acc[i][j][q] / scale, -448.f), 448.f);
+            for (int q = 0; q < 4; ++q) qv[q] = fminf(fmaxf(qd[j][q], -448.f), 448.f);
             int v = __builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[1], 0, false);
             v = __builtin_amdgcn_cvt_pk_fp8_f32(qv[2], qv[3], v, true);
             w4[i][j] = (uint32_t)v;
