@@ -247,9 +247,18 @@ __device__ __forceinline__ void quantize_row(const uint16_t* __restrict__ src, u
     } else {
       amax = row16_max(amax);
       const float scale = amax == 0.f ? 1.f : amax / 448.f;
+      float d[8];
+      if (scale >= kDivFastMin) {         // eight quotients from one reciprocal (bit-identical)
+        const float y = 1.f / scale;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) d[q] = div_rn_by(v[q], scale, y);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) d[q] = v[q] / scale;
+      }
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        const float qv = fminf(fmaxf(v[q] / scale, -448.f), 448.f);
+        const float qv = fminf(fmaxf(d[q], -448.f), 448.f);
         const uint32_t code = f32_to_e4m3(qv);
         if (q < 4) lo |= code << (8 * q); else hi |= code << (8 * (q - 4));
       }
