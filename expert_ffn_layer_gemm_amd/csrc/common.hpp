@@ -21,11 +21,18 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
   return __uint_as_float(b << 16);
 }
 
-// Round-to-nearest-even fp32 -> bf16 bits (inputs are finite here).
+// Round-to-nearest-even fp32 -> bf16 bits (inputs are finite here), by
+// gfx950's v_cvt_pk_bf16_f32 (fp32 denormals are kept in these kernels, so
+// it rounds every finite value as the bit-level rule u + 0x7FFF + lsb, >> 16,
+// does); pack_bf16x2 rounds two values into one word with one instruction.
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 // Unpack 8 bf16 values held in a 16-byte word.
@@ -41,7 +48,7 @@ __device__ __forceinline__ u32x4_t pack_bf16x8(const float* f) {
   u32x4_t r;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    r[i] = f32_to_bf16_bits(f[2 * i]) | (f32_to_bf16_bits(f[2 * i + 1]) << 16);
+    r[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
   return r;
 }
 

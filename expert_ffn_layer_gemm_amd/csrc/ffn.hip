@@ -212,8 +212,8 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
     a.x = silu_mul(a.x, b.x); a.y = silu_mul(a.y, b.y);
     a.z = silu_mul(a.z, b.z); a.w = silu_mul(a.w, b.w);
   }
-  const uint32_t lo = f32_to_bf16_bits(a.x) | (f32_to_bf16_bits(a.y) << 16);
-  const uint32_t hi = f32_to_bf16_bits(a.z) | (f32_to_bf16_bits(a.w) << 16);
+  const uint32_t lo = pack_bf16x2(a.x, a.y);
+  const uint32_t hi = pack_bf16x2(a.z, a.w);
   *reinterpret_cast<uint2*>(out + (size_t)r * N + c) = make_uint2(lo, hi);
 }
 

@@ -592,8 +592,8 @@ __global__ __launch_bounds__(512) void k_tiled8(const GemmArgs p) {
         const int m = rbase + i * 16 + r16;
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-          const uint32_t lo = f32_to_bf16_bits(acc[i][j][0]) | (f32_to_bf16_bits(acc[i][j][1]) << 16);
-          const uint32_t hi = f32_to_bf16_bits(acc[i][j][2]) | (f32_to_bf16_bits(acc[i][j][3]) << 16);
+          const uint32_t lo = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+          const uint32_t hi = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
           *reinterpret_cast<u32x2_t*>(tile_at(m, wn * 64 + j * 16 + 4 * (lane >> 4))) = u32x2_t{lo, hi};
         }
       }
@@ -1121,8 +1121,8 @@ __global__ __launch_bounds__(512) void k_tiled8p(const GemmArgs p) {
             uint32_t v[2][2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-              v[t][0] = f32_to_bf16_bits(acc[i][jp + t][0]) | (f32_to_bf16_bits(acc[i][jp + t][1]) << 16);
-              v[t][1] = f32_to_bf16_bits(acc[i][jp + t][2]) | (f32_to_bf16_bits(acc[i][jp + t][3]) << 16);
+              v[t][0] = pack_bf16x2(acc[i][jp + t][0], acc[i][jp + t][1]);
+              v[t][1] = pack_bf16x2(acc[i][jp + t][2], acc[i][jp + t][3]);
             }
             const uint32_t g0 = (uint32_t)__shfl_xor((int)(ceven ? v[1][0] : v[0][0]), 16);
             const uint32_t g1 = (uint32_t)__shfl_xor((int)(ceven ? v[1][1] : v[0][1]), 16);
